@@ -1,0 +1,97 @@
+"""fp64 decode attention: the plain definition, no tiling, no online softmax.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed (the pages' statement of the decode step):
+
+* One new query token per sequence attends over every cached K/V row of that
+  sequence plus its own newly appended row: append first, then attend
+  ("苦猿的大模型日记 · Day45 · 大模型推理加速", PART 02, the ``torch.cat`` of the new
+  K/V onto the cache followed by ``attention(new_q, k_cache, v_cache)``;
+  "大模型推理加速——KV Cache篇" §2.2, K_cur/V_cur concatenated onto the cached
+  K_last/V_last).
+* Per head, scores = q . K^T, weights = softmax(scores * scale), output =
+  weights . V ("LLM推理优化实战：从KV-Cache到Continuous Batching…" §1.1
+  ``attention_step``; "苦猿的大模型日记" PART 02, softmax(QK^T/sqrt(d))V).  The
+  scale is passed in explicitly (the kernel's fp32 value) so both sides use the
+  same number.
+* GQA: the query heads are split into contiguous groups, each sharing one KV
+  head, so query head h reads KV head h // (Hq / Hkv)
+  ("大模型推理加速核心KV Cache 复用机制与内存布局优化" §二; "大模型推理加速——KV Cache篇"
+  §6.2).  Hkv == Hq is MHA, Hkv == 1 is MQA.
+* Decode needs no causal mask: with one query row at the last position every
+  cached column is visible (the mask of "苦猿的大模型日记" PART 04's
+  ``naive_attention`` keeps all kv_len columns for q_len = 1; the LLaMA code in
+  "大模型推理加速——KV Cache篇" §3 builds a mask only when seqlen > 1).
+
+``causal_attention`` is the full-recompute definition (page 5's
+``naive_attention`` with ``tril(diagonal = kv_len - q_len)``), written here
+without torch, used to pin ``decode_attention`` by brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decode_attention(q, k, v, scale):
+    """Decode attention of one query token over a contiguous history.
+
+    q: [Hq, D]   query of the new token (any real dtype; upcast to fp64)
+    k, v: [n, Hkv, D]  the sequence's K/V rows in position order, the newly
+        appended token last (n >= 1)
+    scale: float, the softmax scale (e.g. fp32(1/sqrt(D)))
+    returns: [Hq, D] fp64
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    hq, d = q.shape
+    n, hkv, dk = k.shape
+    if n < 1:
+        raise ValueError("decode attention needs at least one key (the new token)")
+    if dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if hq % hkv != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    group = hq // hkv
+    scale = float(scale)
+    out = np.empty((hq, d), dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        scores = scale * (k[:, g, :] @ q[h])          # [n]
+        w = np.exp(scores - scores.max())             # softmax numerator
+        out[h] = (w @ v[:, g, :]) / w.sum()
+    return out
+
+
+def decode_attention_batch(q, k_list, v_list, scale):
+    """Apply ``decode_attention`` sequence by sequence.
+
+    q: [B, Hq, D]; k_list[b], v_list[b]: [n_b, Hkv, D].  Returns [B, Hq, D].
+    """
+    q = np.asarray(q)
+    out = np.empty(q.shape, dtype=np.float64)
+    for b in range(q.shape[0]):
+        out[b] = decode_attention(q[b], k_list[b], v_list[b], scale)
+    return out
+
+
+def causal_attention(q, k, v, scale):
+    """Full causal attention for one head: q [nq, D], k/v [nk, D], nk >= nq.
+
+    Row i may see key columns j <= i + (nk - nq) (the lower triangle shifted
+    so the last query row sees every key), scores are scaled, softmax'd along
+    the key axis with masked entries excluded, then multiplied by V.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nq, nk = q.shape[0], k.shape[0]
+    out = np.empty((nq, v.shape[1]), dtype=np.float64)
+    for i in range(nq):
+        visible = i + (nk - nq) + 1                    # columns 0 .. visible-1
+        scores = np.array([scale * float(q[i] @ k[j]) for j in range(visible)])
+        w = np.exp(scores - scores.max())
+        w = w / w.sum()
+        out[i] = sum(w[j] * v[j] for j in range(visible))
+    return out

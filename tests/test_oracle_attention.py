@@ -1,0 +1,181 @@
+"""Pins for the fp64 attention oracle (CPU only).
+
+Each pin ties the oracle to something other than itself: the pages' worked
+example (inputs printed on "大模型推理加速——KV Cache篇" §2.1), closed forms,
+brute-force full recomputation, and torch's own scaled_dot_product_attention
+and softmax run in fp64 on the CPU (independent library routines).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import attention
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+@pytest.fixture
+def worked(golden_dir):
+    g = _load(golden_dir, "worked_example.json")
+    X1, X2 = np.array(g["X_step1"]), np.array(g["X_step2"])
+    WQ, WK, WV = np.array(g["W_Q"]), np.array(g["W_K"]), np.array(g["W_V"])
+    return dict(g=g, X1=X1, X2=X2, WQ=WQ, WK=WK, WV=WV, scale=1.0 / g["score_divisor"])
+
+
+def test_worked_example_first_row_is_first_value(worked):
+    # Closed form: a query that sees a single key returns that key's value row.
+    X2, WQ, WK, WV = worked["X2"], worked["WQ"], worked["WK"], worked["WV"]
+    Q, K, V = X2 @ WQ, X2 @ WK, X2 @ WV
+    out = attention.decode_attention(Q[:1], K[:1, None, :], V[:1, None, :], worked["scale"])
+    assert np.array_equal(out[0], V[0])
+    full = attention.causal_attention(Q, K, V, worked["scale"])
+    assert np.array_equal(full[0], V[0])
+
+
+def test_worked_example_matches_page_procedure_in_torch(worked):
+    # The page's own procedure (scores / 2 + printed mask, F.softmax, matmul),
+    # evaluated by torch in fp64, against the oracle's causal and decode forms.
+    g = worked["g"]
+    for X, mask in ((worked["X1"], g["mask_step1"]), (worked["X2"], g["mask_step2"])):
+        Xt = torch.tensor(X, dtype=torch.float64)
+        Q = Xt @ torch.tensor(g["W_Q"], dtype=torch.float64)
+        K = Xt @ torch.tensor(g["W_K"], dtype=torch.float64)
+        V = Xt @ torch.tensor(g["W_V"], dtype=torch.float64)
+        m = torch.tensor([[float(x) for x in row] for row in mask], dtype=torch.float64)
+        ref = F.softmax(Q @ K.T / g["score_divisor"] + m, dim=-1) @ V
+        ours = attention.causal_attention(Q.numpy(), K.numpy(), V.numpy(), worked["scale"])
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=0, atol=1e-15)
+        # every row i is also a decode step over keys 0..i
+        for i in range(X.shape[0]):
+            dec = attention.decode_attention(Q[i:i + 1].numpy(), K[:i + 1, None].numpy(),
+                                             V[:i + 1, None].numpy(), worked["scale"])
+            np.testing.assert_allclose(dec[0], ref[i].numpy(), rtol=0, atol=1e-15)
+
+
+def test_worked_example_cache_reuse(worked):
+    # Step 1 rows equal step 2's first two rows (history does not change when a
+    # token is appended), and the cached decode of the third token equals the
+    # full recomputation's last row (the page's claim in §2.2).
+    X1, X2, WQ, WK, WV, s = (worked[k] for k in ("X1", "X2", "WQ", "WK", "WV", "scale"))
+    full1 = attention.causal_attention(X1 @ WQ, X1 @ WK, X1 @ WV, s)
+    full2 = attention.causal_attention(X2 @ WQ, X2 @ WK, X2 @ WV, s)
+    np.testing.assert_allclose(full1, full2[:2], rtol=0, atol=1e-16)
+    K_cached, V_cached = X1 @ WK, X1 @ WV                   # K_last, V_last
+    x_new = X2[2:3]
+    K_all = np.concatenate([K_cached, x_new @ WK])[:, None, :]
+    V_all = np.concatenate([V_cached, x_new @ WV])[:, None, :]
+    dec = attention.decode_attention(x_new @ WQ, K_all, V_all, s)
+    np.testing.assert_allclose(dec[0], full2[2], rtol=0, atol=1e-16)
+
+
+@pytest.mark.parametrize("hq,hkv,d,n", [(1, 1, 4, 1), (4, 4, 8, 9), (8, 2, 64, 33), (8, 1, 16, 17),
+                                        (6, 3, 8, 40), (16, 2, 128, 64)])
+def test_decode_equals_last_row_of_full_recompute(hq, hkv, d, n):
+    rng = np.random.default_rng(hq * 1000 + n)
+    Q = rng.standard_normal((n, hq, d))
+    K = rng.standard_normal((n, hkv, d))
+    V = rng.standard_normal((n, hkv, d))
+    s = 1.0 / math.sqrt(d)
+    dec = attention.decode_attention(Q[-1], K, V, s)
+    G = hq // hkv
+    for h in range(hq):
+        full = attention.causal_attention(Q[:, h], K[:, h // G], V[:, h // G], s)
+        np.testing.assert_allclose(dec[h], full[-1], rtol=1e-12, atol=1e-14)
+
+
+def _sdpa_reference(q, K, V, scale):
+    # torch's SDPA in fp64 on the CPU; enable_gqa groups query heads contiguously.
+    qt = torch.tensor(q, dtype=torch.float64)[None, :, None, :]          # [1, Hq, 1, D]
+    kt = torch.tensor(K, dtype=torch.float64).permute(1, 0, 2)[None]      # [1, Hkv, n, D]
+    vt = torch.tensor(V, dtype=torch.float64).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(), scale=scale,
+                                       enable_gqa=True)
+    return o[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (8, 1), (64, 8), (32, 8)])
+def test_decode_matches_torch_sdpa_fp64(hq, hkv):
+    rng = np.random.default_rng(hq + 7 * hkv)
+    d, n = 128, 50
+    q = rng.standard_normal((hq, d))
+    K = rng.standard_normal((n, hkv, d))
+    V = rng.standard_normal((n, hkv, d))
+    s = float(np.float32(1 / math.sqrt(d)))
+    np.testing.assert_allclose(attention.decode_attention(q, K, V, s), _sdpa_reference(q, K, V, s),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_planted_head_mapping_mistake_is_caught():
+    # A plausible slip -- interleaved groups (h % Hkv) instead of contiguous
+    # ones -- must fail the SDPA pin, so the pin has teeth.
+    def wrong(q, K, V, scale):
+        hq, hkv = q.shape[0], K.shape[1]
+        out = np.empty_like(q)
+        for h in range(hq):
+            g = h % hkv
+            sc = scale * (K[:, g] @ q[h])
+            w = np.exp(sc - sc.max())
+            out[h] = w @ V[:, g] / w.sum()
+        return out
+    rng = np.random.default_rng(5)
+    q, K, V = rng.standard_normal((8, 16)), rng.standard_normal((20, 2, 16)), rng.standard_normal((20, 2, 16))
+    ref = _sdpa_reference(q, K, V, 0.25)
+    assert not np.allclose(wrong(q, K, V, 0.25), ref, atol=1e-6)
+    assert np.allclose(attention.decode_attention(q, K, V, 0.25), ref, atol=1e-12)
+
+
+def test_closed_forms():
+    rng = np.random.default_rng(11)
+    d = 64
+    # single token: output is that token's value row for every head of the group
+    q = rng.standard_normal((8, d))
+    K = rng.standard_normal((1, 2, d))
+    V = rng.standard_normal((1, 2, d))
+    out = attention.decode_attention(q, K, V, 0.125)
+    for h in range(8):
+        assert np.array_equal(out[h], V[0, h // 4])
+    # identical keys: uniform weights -> mean of the values
+    n = 37
+    K = np.repeat(rng.standard_normal((1, 2, d)), n, axis=0)
+    V = rng.standard_normal((n, 2, d))
+    out = attention.decode_attention(q, K, V, 0.125)
+    for h in range(8):
+        np.testing.assert_allclose(out[h], V[:, h // 4].mean(axis=0), rtol=0, atol=1e-14)
+    # constant values: output is that constant whatever the scores
+    K = rng.standard_normal((n, 2, d)) * 5
+    V = np.broadcast_to(rng.standard_normal((1, 2, d)), (n, 2, d))
+    out = attention.decode_attention(q, K, V, 0.125)
+    for h in range(8):
+        np.testing.assert_allclose(out[h], V[0, h // 4], rtol=1e-15, atol=1e-15)
+    # scale 0: plain mean of the values
+    V = rng.standard_normal((n, 2, d))
+    out = attention.decode_attention(q, K, V, 0.0)
+    np.testing.assert_allclose(out[0], V[:, 0].mean(axis=0), atol=1e-14)
+
+
+def test_outputs_lie_in_the_convex_hull():
+    rng = np.random.default_rng(3)
+    q, K, V = rng.standard_normal((8, 32)) * 3, rng.standard_normal((100, 4, 32)), rng.standard_normal((100, 4, 32))
+    out = attention.decode_attention(q, K, V, 1.0)
+    for h in range(8):
+        g = h // 2
+        assert np.all(out[h] <= V[:, g].max(axis=0) + 1e-12)
+        assert np.all(out[h] >= V[:, g].min(axis=0) - 1e-12)
+
+
+def test_batch_wrapper_is_per_sequence():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((3, 4, 8))
+    ks = [rng.standard_normal((n, 2, 8)) for n in (1, 5, 17)]
+    vs = [rng.standard_normal((n, 2, 8)) for n in (1, 5, 17)]
+    out = attention.decode_attention_batch(q, ks, vs, 0.3)
+    for b in range(3):
+        np.testing.assert_array_equal(out[b], attention.decode_attention(q[b], ks[b], vs[b], 0.3))

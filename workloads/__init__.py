@@ -1,0 +1,10 @@
+"""Seeded synthetic workloads for paged GQA decode attention.
+
+This package only draws inputs: shapes, context lengths, the physical-block
+placement permutation, the order of the setup operations, and N(0, 1) tensor
+values rounded to the storage dtype.  It holds none of the method's
+arithmetic, and both the HIP path's callers and the oracle's callers take
+their inputs from it.
+"""
+from .configs import (CONFIGS, SMALL, Workload, custom_workload, make_values,  # noqa: F401
+                      make_workload, setup_ops)

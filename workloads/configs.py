@@ -1,0 +1,212 @@
+"""The five decode workloads (and scaled-down variants) as seeded synthetic inputs.
+
+Shapes follow the pages' workloads: a LLaMA2-7B-shaped MHA layer (32/32 heads,
+head_dim 128, fp16, 2048 context), a 70B-shaped GQA layer (64 query / 8 KV
+heads) at page 5's 4096-token inputs, a 32K context with a shared system-prompt
+prefix forked copy-on-write, and an fp8 (E4M3) KV cache over a mixed batch of
+up to 16K tokens.  Every config has one layer and 16-token blocks.
+
+Draw order (fixed): context lengths, placement permutation (numpy
+``default_rng(seed)``), then the tensors K history, V history, q, k_new,
+v_new (torch generator seeded with ``seed`` on the device they are made on),
+each drawn as float32 N(0, 1) and rounded to nearest-even into its storage
+dtype.  The placement permutation is the initial free-list order handed to the
+allocator; blocks are then popped from its end in logical order.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+TORCH_DTYPE_NAMES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+@dataclass
+class Workload:
+    name: str
+    batch: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    q_dtype: str            # dtype of q and of the output
+    kv_dtype: str           # storage dtype of the cache: f32 / f16 / bf16 / fp8
+    new_dtype: str          # dtype of the appended k_new / v_new rows
+    context_lens: np.ndarray  # [B] tokens already cached before the step (L_b)
+    shared_prefix: int      # tokens of sequence 0 shared by every sequence via fork (0 = none)
+    num_blocks: int
+    free_order: np.ndarray  # [num_blocks] int32 permutation
+    seed: int
+    num_layers: int = 1
+    block_size: int = BLOCK_SIZE
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(head_dim), as the fp32 value passed to the kernel."""
+        return float(np.float32(1.0 / math.sqrt(self.head_dim)))
+
+    @property
+    def attend_lens(self) -> np.ndarray:
+        """Tokens each sequence attends in the step: L_b + 1 (the appended one)."""
+        return self.context_lens + 1
+
+    @property
+    def history_rows(self) -> int:
+        """Rows of K/V history written during setup (a shared prefix counts once)."""
+        if self.shared_prefix:
+            return int(self.shared_prefix + np.sum(self.context_lens - self.shared_prefix))
+        return int(np.sum(self.context_lens))
+
+    @property
+    def max_context_len(self) -> int:
+        return int(np.max(self.attend_lens))
+
+
+def _blocks(n: int) -> int:
+    return (n + BLOCK_SIZE - 1) // BLOCK_SIZE
+
+
+def _exact_pool(lens, shared_prefix: int) -> int:
+    lens = np.asarray(lens)
+    if shared_prefix:
+        return _blocks(shared_prefix) + int(np.sum([_blocks(l + 1) - _blocks(shared_prefix) for l in lens]))
+    return int(np.sum([_blocks(l + 1) for l in lens]))
+
+
+def _lengths(cid: int, rng, p) -> np.ndarray:
+    kind = p["lens"]
+    if kind[0] == "fixed":
+        return np.asarray(kind[1], dtype=np.int64)
+    if kind[0] == "const":
+        return np.full(p["batch"], kind[1], dtype=np.int64)
+    if kind[0] == "lognormal":
+        _, median, sigma, lo, hi = kind
+        x = rng.lognormal(mean=math.log(median), sigma=sigma, size=p["batch"])
+        return np.clip(np.rint(x), lo, hi).astype(np.int64)
+    if kind[0] == "uniform":
+        _, lo, hi = kind
+        return rng.integers(lo, hi, size=p["batch"], endpoint=True).astype(np.int64)
+    raise ValueError(kind)
+
+
+# Full-size configs (the measured workloads) and scaled-down twins with the
+# same structure that the oracle finishes in seconds.
+CONFIGS = {
+    1: dict(name="tiny paged decode, fp32, B4, 8/2 heads, D64, L{17,33,100,256}",
+            batch=4, num_heads=8, num_kv_heads=2, head_dim=64, q_dtype="f32", kv_dtype="f32",
+            lens=("fixed", [17, 33, 100, 256]), shared_prefix=0, pool=128),
+    2: dict(name="LLaMA2-7B-shaped MHA layer, fp16, B32, 32/32 heads, D128, L2048",
+            batch=32, num_heads=32, num_kv_heads=32, head_dim=128, q_dtype="f16", kv_dtype="f16",
+            lens=("const", 2048), shared_prefix=0, pool=None),
+    3: dict(name="70B-shaped GQA layer, bf16, B64, 64/8 heads, D128, L lognormal(median 4096) in [128, 8192]",
+            batch=64, num_heads=64, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16",
+            lens=("lognormal", 4096, 1.0, 128, 8192), shared_prefix=0, pool=None),
+    4: dict(name="long-context GQA with 4096-token shared prefix, bf16, B16, 32/8 heads, D128, L32768",
+            batch=16, num_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16",
+            lens=("const", 32768), shared_prefix=4096, pool=None),
+    5: dict(name="fp8 E4M3 KV mixed batch, bf16 q, B128, 64/8 heads, D128, L uniform 256..16384",
+            batch=128, num_heads=64, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="fp8",
+            lens=("uniform", 256, 16384), shared_prefix=0, pool=None),
+}
+
+SMALL = {
+    1: dict(CONFIGS[1]),
+    2: dict(CONFIGS[2], name="MHA fp16 (scaled down), B4, 32/32 heads, D128, L300",
+            batch=4, lens=("const", 300)),
+    3: dict(CONFIGS[3], name="GQA bf16 (scaled down), B8, 64/8 heads, D128, L lognormal(median 300) in [1, 1200]",
+            batch=8, lens=("lognormal", 300, 1.0, 1, 1200)),
+    4: dict(CONFIGS[4], name="shared-prefix GQA bf16 (scaled down), B4, 32/8 heads, D128, L700, prefix 256",
+            batch=4, lens=("const", 700), shared_prefix=256),
+    5: dict(CONFIGS[5], name="fp8 KV (scaled down), B8, 64/8 heads, D128, L uniform 1..1000",
+            batch=8, lens=("uniform", 1, 1000)),
+}
+
+
+def make_workload(cid: int, seed: int | None = None, small: bool = False, **override) -> Workload:
+    """Build config ``cid`` (1..5).  ``seed`` defaults to the config number."""
+    p = dict((SMALL if small else CONFIGS)[cid])
+    p.update(override)
+    seed = cid if seed is None else seed
+    rng = np.random.default_rng(seed)
+    lens = _lengths(cid, rng, p)
+    pool = p["pool"] or _exact_pool(lens, p["shared_prefix"])
+    free_order = rng.permutation(pool).astype(np.int32)
+    kv = p["kv_dtype"]
+    return Workload(name=p["name"], batch=p["batch"], num_heads=p["num_heads"],
+                    num_kv_heads=p["num_kv_heads"], head_dim=p["head_dim"],
+                    q_dtype=p["q_dtype"], kv_dtype=kv,
+                    new_dtype=("bf16" if kv == "fp8" else kv),
+                    context_lens=lens, shared_prefix=int(p["shared_prefix"]),
+                    num_blocks=int(pool), free_order=free_order, seed=seed)
+
+
+def custom_workload(batch, num_heads, num_kv_heads, head_dim, kv_dtype, context_lens,
+                    q_dtype=None, num_blocks=None, seed=0, shared_prefix=0, name="custom") -> Workload:
+    """A workload of any shape (used by edge-case and sweep tests)."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    pool = num_blocks or _exact_pool(lens, shared_prefix)
+    free_order = rng.permutation(pool).astype(np.int32)
+    q_dtype = q_dtype or ("bf16" if kv_dtype == "fp8" else kv_dtype)
+    return Workload(name=name, batch=batch, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                    head_dim=head_dim, q_dtype=q_dtype, kv_dtype=kv_dtype,
+                    new_dtype=("bf16" if kv_dtype == "fp8" else kv_dtype),
+                    context_lens=lens, shared_prefix=int(shared_prefix), num_blocks=int(pool),
+                    free_order=free_order, seed=seed)
+
+
+def setup_ops(wl: Workload):
+    """The operations that build the cached history, in order.
+
+    ("add", seq, 0)            create an empty sequence
+    ("append", seqs, n_new)    append n_new[i] history rows to seqs[i]; rows are
+                               taken in order from the K/V history tensors
+    ("fork", parent, child)    share the parent's blocks copy-on-write
+    """
+    ops = []
+    B = wl.batch
+    if wl.shared_prefix:
+        ops.append(("add", 0, 0))
+        ops.append(("append", [0], [wl.shared_prefix]))
+        for b in range(1, B):
+            ops.append(("fork", 0, b))
+        ops.append(("append", list(range(B)), [int(l) - wl.shared_prefix for l in wl.context_lens]))
+    else:
+        for b in range(B):
+            ops.append(("add", b, 0))
+        ops.append(("append", list(range(B)), [int(l) for l in wl.context_lens]))
+    return ops
+
+
+def _randn(shape, dtype_name, gen, device):
+    import torch
+    tdt = getattr(torch, TORCH_DTYPE_NAMES[dtype_name])
+    out = torch.empty(shape, dtype=tdt, device=device)
+    flat = out.view(-1)
+    chunk = 1 << 26
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        flat[i:i + n] = torch.randn(n, generator=gen, dtype=torch.float32, device=device).to(tdt)
+    return out
+
+
+def make_values(wl: Workload, device="cpu"):
+    """Tensors of the workload, drawn on ``device`` (torch generator seeded with wl.seed).
+
+    k_hist, v_hist: [layers, history_rows, Hkv, D] (new_dtype), rows in setup-op order
+    q: [B, Hq, D] (q_dtype); k_new, v_new: [layers, B, Hkv, D] (new_dtype)
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(wl.seed))
+    L, T, H, D = wl.num_layers, wl.history_rows, wl.num_kv_heads, wl.head_dim
+    k_hist = _randn((L, T, H, D), wl.new_dtype, gen, device)
+    v_hist = _randn((L, T, H, D), wl.new_dtype, gen, device)
+    q = _randn((wl.batch, wl.num_heads, D), wl.q_dtype, gen, device)
+    k_new = _randn((L, wl.batch, H, D), wl.new_dtype, gen, device)
+    v_new = _randn((L, wl.batch, H, D), wl.new_dtype, gen, device)
+    return dict(k_hist=k_hist, v_hist=v_hist, q=q, k_new=k_new, v_new=v_new)
