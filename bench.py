@@ -1,0 +1,215 @@
+"""Benchmark one paged GQA decode step on one MI355X.
+
+A step is the whole hot path over one batch: kvc_append of every sequence's
+new K/V row (slot reservation on the host, upload of the write plan, the
+append kernel), then kvc_decode_attention (split-K kernel + merge kernel).
+The step is made repeatable by truncating each sequence back to its history
+length afterwards (host bookkeeping only), so every step appends into the
+same slots.
+
+Prints ONE JSON line: value = KV-read GB/s (distinct K/V bytes the step
+attends / step time), plus us_per_step, the split kernel's roofline (HIP
+events on the launch stream) and the fp64 CPU oracle timed on a sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged GQA decode attn: µs/step, KV-read HBM GB/s and % of MI355X peak"
+PEAK_HBM_GBS = 8000.0
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 70B-shaped GQA layer)")
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--kernel", type=int, default=0, help="0 auto, 1 fp32 FMA, 2 MFMA")
+    p.add_argument("--partition-tokens", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate", action="store_true", help="also time the plain copy kernel (2 GiB)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(wl):
+    """Bytes the decode must move, per step (what the method reads and writes)."""
+    eb = ELEM_BYTES[wl.kv_dtype]
+    tokens = wl.history_rows + wl.batch            # distinct rows attended (shared prefix once)
+    kv = 2 * tokens * wl.num_kv_heads * wl.head_dim * eb
+    blocks_distinct = wl.num_blocks
+    scales = 2 * 4 * blocks_distinct * wl.num_kv_heads if wl.kv_dtype == "fp8" else 0
+    qb = ELEM_BYTES[wl.q_dtype]
+    q = wl.batch * wl.num_heads * wl.head_dim * qb
+    out = q
+    tables = 4 * sum((int(n) + 15) // 16 for n in wl.attend_lens) + 4 * wl.batch
+    append = 2 * wl.batch * wl.num_kv_heads * wl.head_dim * eb
+    return dict(kv=kv, scales=scales, q=q, out=out, tables=tables, append=append,
+                split_kernel=kv + scales + q + tables)
+
+
+def cpu_baseline(wl, values, budget_s):
+    """Time the fp64 oracle on a sample of the same workload (sequences in order
+    until the budget is spent); report GB/s of KV it processed and the cores it
+    kept busy (process CPU time / wall time)."""
+    import numpy as np
+    import torch
+    from oracle.attention import decode_attention
+    lens = [int(x) for x in wl.context_lens]
+    p = wl.shared_prefix
+    q = values["q"].to(torch.float64).cpu().numpy()
+    kh, vh = values["k_hist"], values["v_hist"]
+    done_bytes, n_seq, wall, cpu = 0, 0, 0.0, 0.0
+    start_row = p if p else 0
+    for b in range(wl.batch):
+        rows = (torch.cat([torch.arange(0, p), torch.arange(start_row, start_row + lens[b] - p)]) if p
+                else torch.arange(start_row, start_row + lens[b]))
+        start_row += lens[b] - p
+        k = torch.cat([kh[0, rows.to(kh.device)], values["k_new"][0, b:b + 1]]).cpu()
+        v = torch.cat([vh[0, rows.to(vh.device)], values["v_new"][0, b:b + 1]]).cpu()
+        if wl.kv_dtype == "fp8":
+            pass  # the oracle is timed on the unquantised rows (same arithmetic, same sizes)
+        t0, c0 = time.perf_counter(), time.process_time()
+        decode_attention(q[b], k.to(torch.float64).numpy(), v.to(torch.float64).numpy(), wl.scale)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        n_seq += 1
+        done_bytes += 2 * (lens[b] + 1) * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
+        if wall > budget_s:
+            break
+    return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {wl.batch} sequences of the same workload ({done_bytes / 1e9:.3f} GB of KV, "
+                      f"fp64 NumPy, {wall:.1f} s wall), one decode step each; "
+                      f"os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode path here is single-GPU by design "
+              f"(--gpus {args.gpus} requested); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_split_amd as kvc
+    from workloads import make_values, make_workload, setup_ops
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    wl = make_workload(args.config, seed=args.seed)
+    print(f"[bench] config {args.config}: {wl.name}; blocks {wl.num_blocks}, attended tokens "
+          f"{int(wl.attend_lens.sum())}", file=sys.stderr, flush=True)
+    values = make_values(wl, dev)
+    cache = kvc.KVCache(wl.num_layers, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.kv_dtype, device=dev,
+                        free_order=wl.free_order)
+    row = 0
+    for op in setup_ops(wl):
+        if op[0] == "add":
+            cache.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            cache.fork(op[1], op[2])
+        else:
+            t = int(sum(op[2]))
+            cache.append(op[1], values["k_hist"][:, row:row + t].contiguous(),
+                         values["v_hist"][:, row:row + t].contiguous(), n_new=op[2])
+            row += t
+    seqs = list(range(wl.batch))
+    hist_len = [int(x) for x in wl.context_lens]
+    k_new, v_new, q = values["k_new"].contiguous(), values["v_new"].contiguous(), values["q"].contiguous()
+    # tables as they are after the step's append (the decode reads L+1 tokens)
+    cache.append(seqs, k_new, v_new)
+    bt, cl = cache.export_tables(seqs)
+    for s, L in zip(seqs, hist_len):
+        cache.truncate(s, L)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, kvc.decode_workspace_bytes(wl.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
+                                                         wl.max_context_len, args.partition_tokens, args.kernel)),
+                     dtype=torch.uint8, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:          # materialise the events before handing them to the library
+        a.record()
+        b.record()
+
+    def step(events=None):
+        cache.append(seqs, k_new, v_new)
+        cache.decode(q, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws, kernel=args.kernel,
+                     partition_tokens=args.partition_tokens, split_events=events)
+        for s, L in zip(seqs, hist_len):
+            cache.truncate(s, L)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    split_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    split_avg_ms = sum(split_ms) / len(split_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    ab = algorithmic_bytes(wl)
+    kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
+    achieved = ab["split_kernel"] / (split_avg_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak_hbm": round(100.0 * kv_gbs / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype if wl.kv_dtype != "fp8" else "fp8-e4m3 kv / bf16 q",
+        "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block placement)",
+        "config": {"workload": wl.name, "config_id": args.config, "batch": wl.batch, "num_heads": wl.num_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "attended_tokens": int(wl.attend_lens.sum()), "kv_bytes": ab["kv"],
+                   "kernel": ["auto", "fma", "mfma"][args.kernel], "partition_tokens": args.partition_tokens or "auto",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode split-K kernel", "avg_launch_us": round(split_avg_ms * 1e3, 2),
+                     "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
+                     "algorithmic_bytes_per_launch": ab["split_kernel"]},
+    }
+    if args.calibrate:
+        n = 1 << 31
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        kvc.stream_copy(dst, src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            kvc.stream_copy(dst, src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        result["calibration"] = {"copy_bytes": n, "copy_read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+        del src, dst
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, values, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

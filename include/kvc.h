@@ -1,0 +1,253 @@
+/*
+ * kvc.h -- paged KV cache and split-K paged GQA decode attention for MI355X (gfx950).
+ *
+ * C ABI of libkvc.  Plain pointers and sizes only.  Device pointers are
+ * borrowed: the library never allocates, frees or retains device memory that
+ * is passed in, and the caller keeps it alive until the work queued on the
+ * given stream has completed.  Host arrays are read (or written) before the
+ * call returns.  Every call returns a kvc_status; on failure nothing has
+ * changed (no allocator state, no queued device work) and kvc_last_error()
+ * returns a message for the calling thread.
+ *
+ * The method (pages cited by title and section):
+ *  - Decode: one new query token per sequence attends over that sequence's
+ *    cached K/V plus its own appended row, softmax(q K^T * scale) V per query
+ *    head ("LLM推理优化实战：从KV-Cache到Continuous Batching…" §1.1
+ *    attention_step; "苦猿的大模型日记 · Day45 · 大模型推理加速" PART 02).
+ *  - GQA: query head h reads KV head h / (num_heads / num_kv_heads)
+ *    ("大模型推理加速核心KV Cache 复用机制与内存布局优化" §二; "大模型推理加速——KV Cache篇" §6.2).
+ *  - Paging: fixed-size blocks of block_size tokens, reached through a
+ *    per-sequence block table; the physical blocks need not be contiguous
+ *    ("大模型推理加速核心KV Cache 复用机制与内存布局优化" §三 BlockTable;
+ *    "LLM推理优化实战…" §2.2 PageAttentionBlock / RequestBlockTable;
+ *    "大模型推理加速——KV Cache篇" §6.1).
+ *  - Copy-on-write prefix sharing through refcounted fork (same passages).
+ *  - Split-K over KV partitions with an exact merge of the per-partition
+ *    (max, sum, acc) triples: the online-softmax recurrence of
+ *    "LLM推理优化实战…" §3.2 and the "merge between blocks" a paged kernel needs
+ *    ("大模型推理加速核心KV Cache 复用机制与内存布局优化" §四); decode is KV-read bound
+ *    ("苦猿的大模型日记" PART 03, Flash-Decoding).
+ *
+ * ---------------------------------------------------------------------------
+ * Pool layout (device memory the caller allocates; sizes from kvc_pool_bytes)
+ * ---------------------------------------------------------------------------
+ *  Let E = element bytes of the KV dtype (4 f32, 2 f16/bf16, 1 fp8) and
+ *  x = 16 / E elements per 16-byte chunk.  A block id names the same block in
+ *  every layer and in both pools.
+ *    K pool: [num_layers][num_blocks][num_kv_heads][head_dim / x][block_size][x]
+ *            (a (block, head) tile is head_dim/x rows of block_size 16-byte chunks)
+ *    V pool: [num_layers][num_blocks][num_kv_heads][head_dim][block_size]
+ *            (a (block, head) tile is V transposed: token index fastest)
+ *    fp8 only: k_scale, v_scale float32 [num_layers][num_blocks][num_kv_heads];
+ *            the value of a stored code c is e4m3(c) * scale.
+ *  Token position p of a sequence lives in block table[p / block_size] at
+ *  slot p % block_size.
+ *
+ * fp8 (E4M3) storage: OCP E4M3 "FN" (bias 7, max 448, S.1111.111 = NaN).
+ *  For each write of c new rows into one (layer, block, KV head) that already
+ *  holds n0 rows with scale s: s_old = (n0 > 0 ? s : 0);
+ *  s_new = max(s_old, amax(new rows) / 448) in IEEE float32; if s_new > s_old
+ *  and n0 > 0 the held codes are re-encoded as enc((dec(c) * s_old) / s_new);
+ *  new values are stored as enc(x / s_new) (enc(x) when s_new == 0).  enc is
+ *  round-to-nearest-even with saturation at +-448.  The pages name E4M3 KV but
+ *  give no scale rule; this is the plainest rule that never saturates a
+ *  block's largest element.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t as an opaque pointer (0 = the default stream). */
+typedef void* kvc_stream_t;
+/* hipEvent_t as an opaque pointer. */
+typedef void* kvc_event_t;
+
+typedef enum kvc_status {
+  KVC_OK = 0,
+  KVC_E_INVALID = 1,      /* bad argument, shape or state; see kvc_last_error() */
+  KVC_E_UNSUPPORTED = 2,  /* valid but not implemented (dtype combination, head_dim, block_size) */
+  KVC_E_NO_BLOCKS = 3,    /* free list too short: nothing was taken (the caller may preempt and retry) */
+  KVC_E_NO_SEQ = 4,       /* unknown sequence id */
+  KVC_E_SEQ_EXISTS = 5,   /* sequence id already in use */
+  KVC_E_HIP = 6,          /* a HIP runtime call failed */
+  KVC_E_WORKSPACE = 7     /* device scratch or workspace smaller than required */
+} kvc_status;
+
+typedef enum kvc_dtype {
+  KVC_F32 = 0,
+  KVC_F16 = 1,
+  KVC_BF16 = 2,
+  KVC_FP8_E4M3 = 3
+} kvc_dtype;
+
+typedef struct kvc_config {
+  int32_t num_layers;     /* >= 1 */
+  int32_t num_kv_heads;   /* >= 1 */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t block_size;     /* tokens per block; device work needs 16, bookkeeping accepts 1..256 */
+  int32_t num_blocks;     /* physical blocks in the pool, >= 1 */
+  kvc_dtype kv_dtype;     /* storage dtype of the pools */
+  void* k_pool;           /* device, kvc_pool_bytes() bytes; may be NULL for bookkeeping-only use */
+  void* v_pool;           /* device, same size as k_pool */
+  float* k_scale;         /* device, fp8 only: kvc_scale_bytes() bytes */
+  float* v_scale;         /* device, fp8 only */
+  void* dev_scratch;      /* device, >= kvc_scratch_bytes(max batch, max tokens per append) bytes */
+  size_t dev_scratch_bytes;
+  const int32_t* free_order; /* host, optional: initial free list (a permutation of
+                                0..num_blocks-1); blocks are taken from its END.
+                                NULL = 0..num_blocks-1.  Copied at create. */
+} kvc_config;
+
+typedef struct kvc_stats_t {
+  int64_t total_blocks;
+  int64_t free_blocks;
+  int64_t used_blocks;      /* blocks with refcount >= 1 */
+  int64_t shared_blocks;    /* blocks with refcount >= 2 */
+  int64_t peak_used_blocks;
+  int64_t cow_copies;       /* block copies issued by copy-on-write */
+  int64_t num_seqs;
+} kvc_stats_t;
+
+typedef struct kvc_cache kvc_cache;
+
+/* ---- sizing (pure functions) ------------------------------------------- */
+
+/* KV bytes per token: 2 x num_layers x num_kv_heads x head_dim x dtype bytes
+ * ("苦猿的大模型日记 · Day45" PART 02).  fp8 scales are not included. */
+size_t kvc_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim, kvc_dtype dtype);
+/* Bytes of ONE pool (K or V) for the layout above. */
+size_t kvc_pool_bytes(int32_t num_layers, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, kvc_dtype dtype);
+/* Bytes of ONE fp8 scale array (K or V): 4 x layers x blocks x kv_heads. */
+size_t kvc_scale_bytes(int32_t num_layers, int32_t num_blocks, int32_t num_kv_heads);
+/* Device scratch an append of max_tokens new rows over max_batch sequences
+ * that each receive at least one row needs (its write plan and copy-on-write
+ * list); sequences listed with n_new = 0 do not count. */
+size_t kvc_scratch_bytes(int32_t max_batch, int64_t max_tokens);
+
+/* ---- handle --------------------------------------------------------------- */
+
+/* Validates cfg and builds the host bookkeeping (free list, refcounts 0).
+ * No device work.  *out is owned by the caller; release with kvc_destroy. */
+kvc_status kvc_create(const kvc_config* cfg, kvc_cache** out);
+void kvc_destroy(kvc_cache* cache);
+
+/* Replace the device scratch kvc_append uses (for instance with a larger one).
+ * The caller keeps the old buffer alive until work queued on it has finished. */
+kvc_status kvc_set_scratch(kvc_cache* cache, void* dev_scratch, size_t dev_scratch_bytes);
+
+/* ---- bookkeeping (host only, no device work) ------------------------------ */
+
+/* Page 2 allocate: a new sequence with ceil(num_tokens / block_size) blocks
+ * reserved (refcount 1 each) and length 0; appends fill reserved blocks first.
+ * KVC_E_NO_BLOCKS takes nothing. */
+kvc_status kvc_add_seq(kvc_cache* cache, int64_t seq_id, int32_t num_tokens);
+/* Page 2 fork: child shares every block of parent (refcount + 1) and its length. */
+kvc_status kvc_fork(kvc_cache* cache, int64_t parent_id, int64_t child_id);
+/* Page 2 free: every block loses one reference; at 0 it returns to the free list. */
+kvc_status kvc_free_seq(kvc_cache* cache, int64_t seq_id);
+/* Drop tokens past num_tokens (<= length); blocks past ceil(num_tokens/bs) are
+ * released last-first, so re-appending takes the same blocks back. */
+kvc_status kvc_truncate(kvc_cache* cache, int64_t seq_id, int32_t num_tokens);
+
+/* Reserve slots for n_new[i] new tokens of seq_ids[i] (n_new NULL = 1 each)
+ * without moving data: the bookkeeping half of kvc_append.  Sequences are
+ * served in call order, positions ascending; a position past the table takes a
+ * fresh block, a write into a block with refcount > 1 first takes a private
+ * block (copy-on-write; a copy pair is reported when the sequence already has
+ * rows in that block).  Ids must be distinct.  On KVC_E_NO_BLOCKS nothing is
+ * taken.  slots_out (host, sum(n_new) entries, optional) receives
+ * block * block_size + offset per new token in that order; cow_src / cow_dst
+ * (host, optional, cow_capacity entries each) receive the copy pairs in the
+ * order issued and *num_cow (optional) their count.  There is at most one pair
+ * per block written, so batch + sum(n_new) / block_size + 1 entries always
+ * suffice; with fewer, a call that needs more fails with KVC_E_INVALID and
+ * takes nothing. */
+kvc_status kvc_reserve_host(kvc_cache* cache, int32_t batch, const int64_t* seq_ids, const int32_t* n_new,
+                            int32_t* slots_out, int32_t* cow_src, int32_t* cow_dst, int32_t cow_capacity,
+                            int32_t* num_cow);
+
+/* Host copy of one sequence's table: up to max_blocks ids into blocks_out,
+ * *num_blocks = table length, *length = tokens written. */
+kvc_status kvc_get_table(const kvc_cache* cache, int64_t seq_id, int32_t* blocks_out, int32_t max_blocks,
+                         int32_t* num_blocks, int32_t* length);
+kvc_status kvc_stats(const kvc_cache* cache, kvc_stats_t* out);
+
+/* ---- device work (asynchronous on `stream`) ------------------------------ */
+
+/* Reserve (as kvc_reserve_host) and write: copies every copy-on-write block
+ * (all layers, K and V, fp8 scales) then stores the new rows of every layer in
+ * their slots.  k_new / v_new: device [num_layers][T][num_kv_heads][head_dim]
+ * in in_dtype, T = sum(n_new), rows sequence by sequence in call order,
+ * positions ascending.  in_dtype must equal kv_dtype, except that an fp8 cache
+ * takes f32, f16 or bf16 rows and quantises them (rule above).  Requires
+ * block_size 16, non-NULL pools (and scales for fp8) and dev_scratch of at
+ * least kvc_scratch_bytes(batch, T).  Calls on one handle must use one stream
+ * (or the caller orders them): the device scratch is reused call to call. */
+kvc_status kvc_append(kvc_cache* cache, int32_t batch, const int64_t* seq_ids, const int32_t* n_new,
+                      const void* k_new, const void* v_new, kvc_dtype in_dtype, kvc_stream_t stream);
+
+/* Write the block-table rows and lengths of `batch` sequences into device
+ * arrays: block_table [batch][max_blocks] int32 padded with -1, context_lens
+ * [batch] int32 = tokens written (after an append, that count includes the
+ * new token).  KVC_E_INVALID if a table is longer than max_blocks. */
+kvc_status kvc_export_tables(kvc_cache* cache, int32_t batch, const int64_t* seq_ids, int32_t* block_table,
+                             int32_t max_blocks, int32_t* context_lens, kvc_stream_t stream);
+
+/* Decode options; pass NULL for the defaults. */
+typedef struct kvc_decode_opts {
+  int32_t partition_tokens; /* tokens per KV partition (multiple of block_size); 0 = chosen from the shape */
+  int32_t kernel;           /* 0 = auto, 1 = fp32 FMA (VALU) kernel, 2 = MFMA kernel (16-bit and fp8 KV) */
+  kvc_event_t split_start;  /* optional events recorded on `stream` around the split-K kernel */
+  kvc_event_t split_end;
+} kvc_decode_opts;
+
+/* Workspace bytes kvc_decode_attention needs for this shape (partials of the
+ * split-K kernel; 0 when every sequence fits one partition). */
+size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_context_len, const kvc_decode_opts* opts);
+
+/* Decode attention for one layer.
+ *  q:            device [batch][num_heads][head_dim], q_dtype (f32 for an f32 cache,
+ *                f16 / bf16 for 16-bit caches of the same dtype, bf16 for fp8)
+ *  block_table:  device int32 [batch][max_blocks_per_seq], physical block ids
+ *  context_lens: device int32 [batch], tokens to attend per sequence, >= 1,
+ *                including the appended token (what kvc_export_tables writes)
+ *  max_context_len: host upper bound of context_lens (sizes the grid)
+ *  scale:        softmax scale (normally 1/sqrt(head_dim))
+ *  out:          device [batch][num_heads][head_dim], q_dtype (rounded to nearest even)
+ *  workspace:    device, kvc_decode_workspace_bytes() bytes
+ * Checks: num_heads % num_kv_heads == 0 and num_heads / num_kv_heads <= 16,
+ * num_kv_heads / head_dim / block_size equal the cache's, block_size 16.
+ * Device-side values are clamped so every access stays inside the arrays the
+ * arguments describe: a length above max_context_len or max_blocks_per_seq *
+ * block_size is cut to it, a block id outside [0, num_blocks) reads block 0
+ * (the result for that sequence is then meaningless, but nothing faults). */
+kvc_status kvc_decode_attention(kvc_cache* cache, int32_t layer, const void* q, kvc_dtype q_dtype,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                float scale, void* out, void* workspace, size_t workspace_bytes,
+                                const kvc_decode_opts* opts, kvc_stream_t stream);
+
+/* ---- measurement helper ---------------------------------------------------- */
+
+/* Streaming copy of `bytes` (multiple of 16) from src to dst on `stream`: a
+ * plain copy kernel of known size, used to calibrate HBM byte counters and
+ * achievable bandwidth.  Not part of the method. */
+kvc_status kvc_stream_copy(void* dst, const void* src, size_t bytes, kvc_stream_t stream);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* kvc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

@@ -1,0 +1,318 @@
+"""ctypes binding of libkvc (include/kvc.h).
+
+Argument marshalling only: every step of the decode path runs in libkvc's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library has not been built this module raises ImportError -- there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libkvc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libkvc.so not found at {LIB_PATH}; build it with `python paged_kv_cache_split_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# status codes (kvc_status)
+OK, E_INVALID, E_UNSUPPORTED, E_NO_BLOCKS, E_NO_SEQ, E_SEQ_EXISTS, E_HIP, E_WORKSPACE = range(8)
+STATUS_NAMES = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_NO_BLOCKS", 4: "E_NO_SEQ",
+                5: "E_SEQ_EXISTS", 6: "E_HIP", 7: "E_WORKSPACE"}
+# dtypes (kvc_dtype)
+F32, F16, BF16, FP8 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8}
+
+SYMBOLS = [
+    "kvc_bytes_per_token", "kvc_pool_bytes", "kvc_scale_bytes", "kvc_scratch_bytes", "kvc_create", "kvc_destroy",
+    "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_reserve_host",
+    "kvc_get_table", "kvc_stats", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
+    "kvc_decode_attention", "kvc_stream_copy", "kvc_last_error",
+]
+
+
+class KvcConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32), ("kv_dtype", ctypes.c_int),
+        ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("dev_scratch", ctypes.c_void_p), ("dev_scratch_bytes", ctypes.c_size_t),
+        ("free_order", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+class KvcStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("total_blocks", "free_blocks", "used_blocks", "shared_blocks",
+                                               "peak_used_blocks", "cow_copies", "num_seqs")]
+
+
+class KvcDecodeOpts(ctypes.Structure):
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p)]
+
+
+_i32, _i64, _sz, _vp, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_P32, _P64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+
+_sig = {
+    "kvc_bytes_per_token": (_sz, [_i32, _i32, _i32, ctypes.c_int]),
+    "kvc_pool_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, ctypes.c_int]),
+    "kvc_scale_bytes": (_sz, [_i32, _i32, _i32]),
+    "kvc_scratch_bytes": (_sz, [_i32, _i64]),
+    "kvc_create": (ctypes.c_int, [ctypes.POINTER(KvcConfig), ctypes.POINTER(_vp)]),
+    "kvc_destroy": (None, [_vp]),
+    "kvc_set_scratch": (ctypes.c_int, [_vp, _vp, _sz]),
+    "kvc_add_seq": (ctypes.c_int, [_vp, _i64, _i32]),
+    "kvc_fork": (ctypes.c_int, [_vp, _i64, _i64]),
+    "kvc_free_seq": (ctypes.c_int, [_vp, _i64]),
+    "kvc_truncate": (ctypes.c_int, [_vp, _i64, _i32]),
+    "kvc_reserve_host": (ctypes.c_int, [_vp, _i32, _P64, _P32, _P32, _P32, _P32, _i32, _P32]),
+    "kvc_get_table": (ctypes.c_int, [_vp, _i64, _P32, _i32, _P32, _P32]),
+    "kvc_stats": (ctypes.c_int, [_vp, ctypes.POINTER(KvcStats)]),
+    "kvc_append": (ctypes.c_int, [_vp, _i32, _P64, _P32, _vp, _vp, ctypes.c_int, _vp]),
+    "kvc_export_tables": (ctypes.c_int, [_vp, _i32, _P64, _vp, _i32, _vp, _vp]),
+    "kvc_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
+    "kvc_decode_attention": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _f, _vp, _vp, _sz, ctypes.POINTER(KvcDecodeOpts), _vp]),
+    "kvc_stream_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+    "kvc_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.kvc_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise KvcError(status, where)
+
+
+def lib():
+    return _lib
+
+
+def _i64_array(xs):
+    a = np.ascontiguousarray(np.asarray(xs, dtype=np.int64))
+    return a, a.ctypes.data_as(_P64)
+
+
+def _i32_array(xs):
+    a = np.ascontiguousarray(np.asarray(xs, dtype=np.int32))
+    return a, a.ctypes.data_as(_P32)
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    if isinstance(t, str):
+        return DTYPE_CODES[t]
+    import torch
+    return {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}[t]
+
+
+# -- sizing -----------------------------------------------------------------
+
+def bytes_per_token(num_layers, num_kv_heads, head_dim, dtype) -> int:
+    return _lib.kvc_bytes_per_token(num_layers, num_kv_heads, head_dim, DTYPE_CODES[dtype])
+
+
+def pool_bytes(num_layers, num_blocks, num_kv_heads, head_dim, block_size, dtype) -> int:
+    return _lib.kvc_pool_bytes(num_layers, num_blocks, num_kv_heads, head_dim, block_size, DTYPE_CODES[dtype])
+
+
+def scale_bytes(num_layers, num_blocks, num_kv_heads) -> int:
+    return _lib.kvc_scale_bytes(num_layers, num_blocks, num_kv_heads)
+
+
+def scratch_bytes(max_batch, max_tokens) -> int:
+    return _lib.kvc_scratch_bytes(max_batch, max_tokens)
+
+
+def decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len, partition_tokens=0,
+                           kernel=0) -> int:
+    opts = KvcDecodeOpts(partition_tokens, kernel, None, None)
+    return _lib.kvc_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len,
+                                           ctypes.byref(opts))
+
+
+def stream_copy(dst, src, nbytes=None, stream=None):
+    """Plain device copy of ``nbytes`` (default: all of src) -- the calibration kernel."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(_lib.kvc_stream_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), nbytes,
+                                _stream_ptr(stream)), "kvc_stream_copy")
+
+
+# -- the cache ----------------------------------------------------------------
+
+class KVCache:
+    """A paged KV cache: host bookkeeping in libkvc, pools in torch device memory.
+
+    ``device=None`` builds a bookkeeping-only cache (no pools, no device work).
+    """
+
+    def __init__(self, num_layers, num_kv_heads, head_dim, num_blocks, kv_dtype, block_size=16,
+                 device="cuda", free_order=None):
+        self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
+        self.num_blocks, self.block_size, self.kv_dtype = num_blocks, block_size, kv_dtype
+        self.device = device
+        self.k_pool = self.v_pool = self.k_scale = self.v_scale = self.scratch = None
+        cfg = KvcConfig()
+        cfg.num_layers, cfg.num_kv_heads, cfg.head_dim = num_layers, num_kv_heads, head_dim
+        cfg.block_size, cfg.num_blocks, cfg.kv_dtype = block_size, num_blocks, DTYPE_CODES[kv_dtype]
+        if device is not None:
+            import torch
+            nbytes = pool_bytes(num_layers, num_blocks, num_kv_heads, head_dim, block_size, kv_dtype)
+            self.k_pool = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            self.v_pool = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            cfg.k_pool, cfg.v_pool = self.k_pool.data_ptr(), self.v_pool.data_ptr()
+            if kv_dtype == "fp8":
+                n = scale_bytes(num_layers, num_blocks, num_kv_heads) // 4
+                self.k_scale = torch.zeros(n, dtype=torch.float32, device=device)
+                self.v_scale = torch.zeros(n, dtype=torch.float32, device=device)
+                cfg.k_scale, cfg.v_scale = self.k_scale.data_ptr(), self.v_scale.data_ptr()
+        self._order = None
+        if free_order is not None:
+            self._order, cfg.free_order = _i32_array(free_order)
+        handle = ctypes.c_void_p()
+        _check(_lib.kvc_create(ctypes.byref(cfg), ctypes.byref(handle)), "kvc_create")
+        self._h = handle
+        self._order = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.kvc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    # bookkeeping
+    def add_seq(self, seq_id, num_tokens=0):
+        _check(_lib.kvc_add_seq(self._h, int(seq_id), int(num_tokens)), "kvc_add_seq")
+
+    def fork(self, parent_id, child_id):
+        _check(_lib.kvc_fork(self._h, int(parent_id), int(child_id)), "kvc_fork")
+
+    def free_seq(self, seq_id):
+        _check(_lib.kvc_free_seq(self._h, int(seq_id)), "kvc_free_seq")
+
+    def truncate(self, seq_id, num_tokens):
+        _check(_lib.kvc_truncate(self._h, int(seq_id), int(num_tokens)), "kvc_truncate")
+
+    def reserve_host(self, seq_ids, n_new=None):
+        ids, pids = _i64_array(seq_ids)
+        nn, pnn = (None, None) if n_new is None else _i32_array(n_new)
+        total = len(ids) if n_new is None else int(np.sum(nn))
+        slots = np.zeros(max(total, 1), dtype=np.int32)
+        cap = len(ids) + total // max(self.block_size, 1) + 1
+        src = np.zeros(cap, dtype=np.int32)
+        dst = np.zeros(cap, dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(_lib.kvc_reserve_host(self._h, len(ids), pids, pnn, slots.ctypes.data_as(_P32),
+                                     src.ctypes.data_as(_P32), dst.ctypes.data_as(_P32), cap,
+                                     ctypes.byref(ncow)), "kvc_reserve_host")
+        n = ncow.value
+        return slots[:total].tolist(), list(zip(src[:n].tolist(), dst[:n].tolist()))
+
+    def get_table(self, seq_id):
+        nb, ln = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(_lib.kvc_get_table(self._h, int(seq_id), None, 0, ctypes.byref(nb), ctypes.byref(ln)),
+               "kvc_get_table")
+        out = np.zeros(max(nb.value, 1), dtype=np.int32)
+        _check(_lib.kvc_get_table(self._h, int(seq_id), out.ctypes.data_as(_P32), nb.value, ctypes.byref(nb),
+                                  ctypes.byref(ln)), "kvc_get_table")
+        return out[:nb.value].tolist(), ln.value
+
+    def stats(self) -> dict:
+        st = KvcStats()
+        _check(_lib.kvc_stats(self._h, ctypes.byref(st)), "kvc_stats")
+        return {n: getattr(st, n) for n, _ in KvcStats._fields_}
+
+    # device work
+    def _ensure_scratch(self, active, total):
+        import torch
+        need = scratch_bytes(active, total)
+        if self.scratch is None or self.scratch.numel() < need:
+            self.scratch = torch.empty(max(need, 4096), dtype=torch.uint8, device=self.device)
+            _check(_lib.kvc_set_scratch(self._h, ctypes.c_void_p(self.scratch.data_ptr()), self.scratch.numel()),
+                   "kvc_set_scratch")
+
+    def append(self, seq_ids, k_new, v_new, n_new=None, stream=None):
+        """k_new / v_new: device tensors [num_layers, T, Hkv, D] (or [T, Hkv, D] for one layer)."""
+        ids, pids = _i64_array(seq_ids)
+        nn, pnn = (None, None) if n_new is None else _i32_array(n_new)
+        total = len(ids) if n_new is None else int(np.sum(nn))
+        active = len(ids) if n_new is None else int(np.count_nonzero(nn))
+        for t in (k_new, v_new):
+            expect = self.num_layers * total * self.num_kv_heads * self.head_dim
+            if not t.is_contiguous() or t.numel() != expect or not t.is_cuda:
+                raise ValueError(f"append rows must be contiguous device tensors of {expect} elements")
+        self._ensure_scratch(active, total)
+        _check(_lib.kvc_append(self._h, len(ids), pids, pnn, ctypes.c_void_p(k_new.data_ptr()),
+                               ctypes.c_void_p(v_new.data_ptr()), _dtype_code(k_new.dtype), _stream_ptr(stream)),
+               "kvc_append")
+
+    def export_tables(self, seq_ids, max_blocks=None, block_table=None, context_lens=None, stream=None):
+        import torch
+        ids, pids = _i64_array(seq_ids)
+        if max_blocks is None:
+            max_blocks = max(1, max(len(self.get_table(s)[0]) for s in ids))
+        if block_table is None:
+            block_table = torch.empty((len(ids), max_blocks), dtype=torch.int32, device=self.device)
+        if context_lens is None:
+            context_lens = torch.empty((len(ids),), dtype=torch.int32, device=self.device)
+        _check(_lib.kvc_export_tables(self._h, len(ids), pids, ctypes.c_void_p(block_table.data_ptr()),
+                                      int(max_blocks), ctypes.c_void_p(context_lens.data_ptr()),
+                                      _stream_ptr(stream)), "kvc_export_tables")
+        return block_table, context_lens
+
+    def decode(self, q, block_table, context_lens, max_context_len, scale, layer=0, out=None, workspace=None,
+               partition_tokens=0, kernel=0, split_events=None, stream=None):
+        """Decode attention for one layer.  q: [B, Hq, D] device tensor."""
+        import torch
+        B, Hq, D = q.shape
+        if not q.is_contiguous():
+            raise ValueError("q must be contiguous")
+        opts = KvcDecodeOpts(int(partition_tokens), int(kernel), None, None)
+        if split_events is not None:
+            opts.split_start = split_events[0].cuda_event
+            opts.split_end = split_events[1].cuda_event
+        ws_need = _lib.kvc_decode_workspace_bytes(B, Hq, self.num_kv_heads, D, int(max_context_len),
+                                                  ctypes.byref(opts))
+        if workspace is None or workspace.numel() < ws_need:
+            workspace = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty_like(q)
+        _check(_lib.kvc_decode_attention(
+            self._h, int(layer), ctypes.c_void_p(q.data_ptr()), _dtype_code(q.dtype),
+            ctypes.c_void_p(block_table.data_ptr()), int(block_table.shape[1]),
+            ctypes.c_void_p(context_lens.data_ptr()), int(max_context_len), B, Hq, self.num_kv_heads, D,
+            self.block_size, float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+            workspace.numel(), ctypes.byref(opts), _stream_ptr(stream)), "kvc_decode_attention")
+        return out

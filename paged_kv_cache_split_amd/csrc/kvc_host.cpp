@@ -1,0 +1,630 @@
+// Host half of libkvc: configuration, validation, the block allocator
+// (free list, per-sequence block tables, refcounts, copy-on-write), append
+// planning, device uploads and kernel dispatch.
+//
+// Allocator semantics follow the BlockTable class of
+// "大模型推理加速核心KV Cache 复用机制与内存布局优化" §三 (allocate / fork / free with
+// refcounts; allocation fails as a whole when the free list is short, which
+// is where a scheduler would preempt) and the RequestBlockTable of
+// "LLM推理优化实战：从KV-Cache到Continuous Batching的技术演进与代码实现" §2.2 (position p
+// lives in logical block p / block_size).  Copy-on-write on the first write
+// into a shared block follows the same pages and "大模型推理加速——KV Cache篇" §6.1.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "kvc_internal.h"
+
+using kvc::AppendSegment;
+using kvc::CowPair;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvc_status fail(kvc_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kvc_status fail(kvc_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kvc_status ok() {
+  g_last_error.clear();
+  return KVC_OK;
+}
+
+bool valid_dtype(int t) { return t >= KVC_F32 && t <= KVC_FP8_E4M3; }
+
+constexpr int kDeviceBlockSize = 16;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Upper bound on the segments (and copy pairs) an append of `tokens` rows over
+// `batch` sequences produces with 16-token blocks: each sequence's run of n
+// rows touches at most n / 16 + 2 blocks.
+int64_t max_segments(int64_t batch, int64_t tokens) { return tokens / kDeviceBlockSize + 2 * batch + 1; }
+
+}  // namespace
+
+struct kvc_cache {
+  kvc_config cfg;
+  std::mutex mu;
+
+  struct Seq {
+    std::vector<int32_t> blocks;
+    int32_t len = 0;
+  };
+  std::vector<int32_t> free_list;  // blocks are taken from the back
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t used = 0;
+  int64_t peak_used = 0;
+  int64_t cow_copies = 0;
+
+  // Pinned staging for host->device uploads; `staging_free` is recorded
+  // after the last copy that reads it.
+  void* staging = nullptr;
+  size_t staging_bytes = 0;
+  hipEvent_t staging_free = nullptr;
+
+  kvc::PoolDesc pool() const {
+    kvc::PoolDesc p;
+    p.k = static_cast<char*>(cfg.k_pool);
+    p.v = static_cast<char*>(cfg.v_pool);
+    p.k_scale = cfg.k_scale;
+    p.v_scale = cfg.v_scale;
+    p.num_layers = cfg.num_layers;
+    p.num_blocks = cfg.num_blocks;
+    p.num_kv_heads = cfg.num_kv_heads;
+    p.head_dim = cfg.head_dim;
+    p.block_size = cfg.block_size;
+    p.dtype = cfg.kv_dtype;
+    return p;
+  }
+
+  int32_t pop_block() {
+    int32_t b = free_list.back();
+    free_list.pop_back();
+    ref[b] = 1;
+    ++used;
+    peak_used = std::max(peak_used, used);
+    return b;
+  }
+
+  void release(int32_t b) {
+    if (--ref[b] == 0) {
+      free_list.push_back(b);
+      --used;
+    }
+  }
+};
+
+namespace {
+
+// Waits until the previous upload has consumed the staging buffer, then
+// makes it at least `bytes` long.
+kvc_status staging_acquire(kvc_cache* c, size_t bytes) {
+  if (c->staging_free) {
+    hipError_t e = hipEventSynchronize(c->staging_free);
+    if (e != hipSuccess) return fail(KVC_E_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+  } else {
+    hipError_t e = hipEventCreateWithFlags(&c->staging_free, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      c->staging_free = nullptr;
+      return fail(KVC_E_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  if (c->staging_bytes < bytes) {
+    if (c->staging) (void)hipHostFree(c->staging);
+    c->staging = nullptr;
+    c->staging_bytes = 0;
+    size_t want = std::max(bytes, size_t(1) << 16);
+    hipError_t e = hipHostMalloc(&c->staging, want, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      c->staging = nullptr;
+      return fail(KVC_E_HIP, "hipHostMalloc(%zu): %s", want, hipGetErrorString(e));
+    }
+    c->staging_bytes = want;
+  }
+  return KVC_OK;
+}
+
+kvc_status staging_upload(kvc_cache* c, void* dst_dev, size_t bytes, hipStream_t s) {
+  hipError_t e = hipMemcpyAsync(dst_dev, c->staging, bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return fail(KVC_E_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  e = hipEventRecord(c->staging_free, s);
+  if (e != hipSuccess) return fail(KVC_E_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  return KVC_OK;
+}
+
+struct AppendPlan {
+  std::vector<int32_t> slots;
+  std::vector<CowPair> cow;
+  std::vector<AppendSegment> segs;
+};
+
+// The bookkeeping of an append.  Validates, counts the blocks it needs
+// (fresh blocks past a table's end plus private copies of shared blocks), and
+// only then takes them, so a failing call changes nothing.
+kvc_status plan_append(kvc_cache* c, int32_t batch, const int64_t* ids, const int32_t* n_new, bool want_slots,
+                       int64_t cow_capacity, AppendPlan* plan) {
+  if (batch < 0) return fail(KVC_E_INVALID, "batch must be >= 0");
+  if (batch > 0 && !ids) return fail(KVC_E_INVALID, "seq_ids is NULL");
+  const int32_t bs = c->cfg.block_size;
+  std::vector<kvc_cache::Seq*> seqs(batch);
+  {
+    std::unordered_set<int64_t> seen;
+    seen.reserve(batch * 2 + 1);
+    for (int32_t i = 0; i < batch; ++i) {
+      if (!seen.insert(ids[i]).second) return fail(KVC_E_INVALID, "sequence %lld listed twice", (long long)ids[i]);
+      auto it = c->seqs.find(ids[i]);
+      if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)ids[i]);
+      seqs[i] = &it->second;
+      int32_t n = n_new ? n_new[i] : 1;
+      if (n < 0) return fail(KVC_E_INVALID, "n_new[%d] < 0", i);
+      if ((int64_t)seqs[i]->len + n > (int64_t)INT32_MAX - bs)
+        return fail(KVC_E_INVALID, "sequence %lld would exceed the maximum length", (long long)ids[i]);
+    }
+  }
+  // Dry run: how many blocks will be popped, and how many copy pairs issued.
+  int64_t need = 0, pairs = 0;
+  std::unordered_map<int32_t, int32_t> drop;  // references a copy-on-write already released, per block
+  for (int32_t i = 0; i < batch; ++i) {
+    const kvc_cache::Seq& s = *seqs[i];
+    int32_t n = n_new ? n_new[i] : 1;
+    if (n == 0) continue;
+    int64_t first = s.len / bs, last = ((int64_t)s.len + n - 1) / bs;
+    for (int64_t idx = first; idx <= last; ++idx) {
+      if (idx >= (int64_t)s.blocks.size()) {
+        ++need;
+      } else {
+        int32_t b = s.blocks[idx];
+        int32_t r = c->ref[b] - drop[b];
+        if (r > 1) {
+          ++need;
+          ++drop[b];
+          int64_t first_pos = std::max<int64_t>(s.len, idx * bs);
+          if (first_pos % bs != 0) ++pairs;
+        }
+      }
+    }
+  }
+  if (need > (int64_t)c->free_list.size())
+    return fail(KVC_E_NO_BLOCKS, "append needs %lld free blocks, %zu available", (long long)need,
+                c->free_list.size());
+  if (pairs > cow_capacity)
+    return fail(KVC_E_INVALID, "append needs %lld copy pairs, capacity %lld", (long long)pairs,
+                (long long)cow_capacity);
+  // Commit, in the same order as the dry run.
+  int64_t total = 0;
+  for (int32_t i = 0; i < batch; ++i) total += n_new ? n_new[i] : 1;
+  if (want_slots) plan->slots.reserve(total);
+  int32_t row = 0;
+  for (int32_t i = 0; i < batch; ++i) {
+    kvc_cache::Seq& s = *seqs[i];
+    int32_t n = n_new ? n_new[i] : 1;
+    int32_t p = s.len, end = s.len + n;
+    while (p < end) {
+      int32_t idx = p / bs, off = p % bs;
+      int32_t run = std::min(end - p, bs - off);
+      if (idx == (int32_t)s.blocks.size()) {
+        s.blocks.push_back(c->pop_block());
+      } else if (c->ref[s.blocks[idx]] > 1) {
+        int32_t old = s.blocks[idx];
+        int32_t fresh = c->pop_block();
+        c->release(old);
+        s.blocks[idx] = fresh;
+        if (off > 0) {
+          plan->cow.push_back({old, fresh});
+          ++c->cow_copies;
+        }
+      }
+      int32_t blk = s.blocks[idx];
+      plan->segs.push_back({blk, off, run, row});
+      if (want_slots)
+        for (int32_t k = 0; k < run; ++k) plan->slots.push_back(blk * bs + off + k);
+      row += run;
+      p += run;
+    }
+    s.len = end;
+  }
+  return KVC_OK;
+}
+
+kvc_status check_device_ready(const kvc_cache* c) {
+  const kvc_config& f = c->cfg;
+  if (f.block_size != kDeviceBlockSize)
+    return fail(KVC_E_UNSUPPORTED, "device work needs block_size 16 (cache has %d)", f.block_size);
+  if (!f.k_pool || !f.v_pool) return fail(KVC_E_INVALID, "pools are NULL (bookkeeping-only cache)");
+  if (f.kv_dtype == KVC_FP8_E4M3 && (!f.k_scale || !f.v_scale))
+    return fail(KVC_E_INVALID, "fp8 cache needs k_scale and v_scale");
+  return KVC_OK;
+}
+
+int32_t auto_partition_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len) {
+  // Enough partitions to give the chip many waves, few enough to keep the
+  // merge small: start at 256 tokens and grow while there are over ~8 waves
+  // per CU-SIMD slot's worth of work items (2048 slots on 256 CUs).
+  int64_t pt = 256;
+  while (pt < 1024) {
+    int64_t parts = (max_context_len + pt - 1) / pt;
+    if ((int64_t)batch * num_kv_heads * parts <= 16384) break;
+    pt *= 2;
+  }
+  return (int32_t)pt;
+}
+
+bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, const kvc_decode_opts* opts,
+                 kvc::DecodePlan* plan) {
+  int32_t pt = (opts && opts->partition_tokens > 0) ? opts->partition_tokens
+                                                    : auto_partition_tokens(batch, num_kv_heads, max_context_len);
+  if (pt % kDeviceBlockSize != 0 || pt > 1024) return false;
+  plan->partition_tokens = pt;
+  plan->num_partitions = std::max(1, (max_context_len + pt - 1) / pt);
+  plan->kernel = opts ? opts->kernel : 0;
+  return true;
+}
+
+size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t head_dim, const kvc::DecodePlan& p) {
+  if (p.num_partitions <= 1) return 0;
+  size_t rows = (size_t)batch * num_heads * p.num_partitions;
+  return align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvc_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim, kvc_dtype dtype) {
+  if (num_layers < 0 || num_kv_heads < 0 || head_dim < 0 || !valid_dtype(dtype)) return 0;
+  return (size_t)2 * num_layers * num_kv_heads * head_dim * kvc::dtype_bytes(dtype);
+}
+
+size_t kvc_pool_bytes(int32_t num_layers, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, kvc_dtype dtype) {
+  if (num_layers < 0 || num_blocks < 0 || num_kv_heads < 0 || head_dim < 0 || block_size < 0 || !valid_dtype(dtype))
+    return 0;
+  return (size_t)num_layers * num_blocks * num_kv_heads * block_size * head_dim * kvc::dtype_bytes(dtype);
+}
+
+size_t kvc_scale_bytes(int32_t num_layers, int32_t num_blocks, int32_t num_kv_heads) {
+  if (num_layers < 0 || num_blocks < 0 || num_kv_heads < 0) return 0;
+  return (size_t)num_layers * num_blocks * num_kv_heads * sizeof(float);
+}
+
+size_t kvc_scratch_bytes(int32_t max_batch, int64_t max_tokens) {
+  if (max_batch < 0 || max_tokens < 0) return 0;
+  int64_t s = max_segments(max_batch, max_tokens);
+  return align256((size_t)s * sizeof(AppendSegment)) + align256((size_t)s * sizeof(CowPair));
+}
+
+kvc_status kvc_create(const kvc_config* cfg, kvc_cache** out) {
+  if (!cfg || !out) return fail(KVC_E_INVALID, "cfg and out must be non-NULL");
+  *out = nullptr;
+  if (cfg->num_layers < 1) return fail(KVC_E_INVALID, "num_layers must be >= 1");
+  if (cfg->num_kv_heads < 1) return fail(KVC_E_INVALID, "num_kv_heads must be >= 1");
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return fail(KVC_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (cfg->block_size < 1 || cfg->block_size > 256) return fail(KVC_E_INVALID, "block_size must be in 1..256");
+  if (cfg->num_blocks < 1) return fail(KVC_E_INVALID, "num_blocks must be >= 1");
+  if (!valid_dtype(cfg->kv_dtype)) return fail(KVC_E_INVALID, "unknown kv_dtype %d", (int)cfg->kv_dtype);
+  if ((int64_t)cfg->num_blocks * cfg->block_size > INT32_MAX)
+    return fail(KVC_E_INVALID, "num_blocks * block_size must fit int32 slot numbers");
+  kvc_cache* c = new (std::nothrow) kvc_cache();
+  if (!c) return fail(KVC_E_INVALID, "out of host memory");
+  c->cfg = *cfg;
+  c->cfg.free_order = nullptr;
+  c->ref.assign(cfg->num_blocks, 0);
+  c->free_list.resize(cfg->num_blocks);
+  if (cfg->free_order) {
+    std::vector<char> seen(cfg->num_blocks, 0);
+    for (int32_t i = 0; i < cfg->num_blocks; ++i) {
+      int32_t b = cfg->free_order[i];
+      if (b < 0 || b >= cfg->num_blocks || seen[b]) {
+        delete c;
+        return fail(KVC_E_INVALID, "free_order is not a permutation of 0..num_blocks-1");
+      }
+      seen[b] = 1;
+      c->free_list[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < cfg->num_blocks; ++i) c->free_list[i] = i;
+  }
+  *out = c;
+  return ok();
+}
+
+void kvc_destroy(kvc_cache* c) {
+  if (!c) return;
+  if (c->staging_free) {
+    (void)hipEventSynchronize(c->staging_free);
+    (void)hipEventDestroy(c->staging_free);
+  }
+  if (c->staging) (void)hipHostFree(c->staging);
+  delete c;
+}
+
+kvc_status kvc_set_scratch(kvc_cache* c, void* dev_scratch, size_t dev_scratch_bytes) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  c->cfg.dev_scratch = dev_scratch;
+  c->cfg.dev_scratch_bytes = dev_scratch ? dev_scratch_bytes : 0;
+  return ok();
+}
+
+kvc_status kvc_add_seq(kvc_cache* c, int64_t seq_id, int32_t num_tokens) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  if (num_tokens < 0) return fail(KVC_E_INVALID, "num_tokens must be >= 0");
+  if (c->seqs.count(seq_id)) return fail(KVC_E_SEQ_EXISTS, "sequence %lld exists", (long long)seq_id);
+  int64_t needed = ((int64_t)num_tokens + c->cfg.block_size - 1) / c->cfg.block_size;
+  if (needed > (int64_t)c->free_list.size())
+    return fail(KVC_E_NO_BLOCKS, "need %lld blocks, %zu free", (long long)needed, c->free_list.size());
+  kvc_cache::Seq s;
+  s.blocks.reserve(needed);
+  for (int64_t i = 0; i < needed; ++i) s.blocks.push_back(c->pop_block());
+  c->seqs.emplace(seq_id, std::move(s));
+  return ok();
+}
+
+kvc_status kvc_fork(kvc_cache* c, int64_t parent_id, int64_t child_id) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  auto it = c->seqs.find(parent_id);
+  if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown parent %lld", (long long)parent_id);
+  if (c->seqs.count(child_id)) return fail(KVC_E_SEQ_EXISTS, "sequence %lld exists", (long long)child_id);
+  kvc_cache::Seq child = it->second;
+  for (int32_t b : child.blocks) ++c->ref[b];
+  c->seqs.emplace(child_id, std::move(child));
+  return ok();
+}
+
+kvc_status kvc_free_seq(kvc_cache* c, int64_t seq_id) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  auto it = c->seqs.find(seq_id);
+  if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)seq_id);
+  for (int32_t b : it->second.blocks) c->release(b);
+  c->seqs.erase(it);
+  return ok();
+}
+
+kvc_status kvc_truncate(kvc_cache* c, int64_t seq_id, int32_t num_tokens) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  auto it = c->seqs.find(seq_id);
+  if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)seq_id);
+  kvc_cache::Seq& s = it->second;
+  if (num_tokens < 0 || num_tokens > s.len)
+    return fail(KVC_E_INVALID, "truncate to %d outside 0..%d", num_tokens, s.len);
+  size_t keep = ((int64_t)num_tokens + c->cfg.block_size - 1) / c->cfg.block_size;
+  while (s.blocks.size() > keep) {
+    c->release(s.blocks.back());
+    s.blocks.pop_back();
+  }
+  s.len = num_tokens;
+  return ok();
+}
+
+kvc_status kvc_reserve_host(kvc_cache* c, int32_t batch, const int64_t* seq_ids, const int32_t* n_new,
+                            int32_t* slots_out, int32_t* cow_src, int32_t* cow_dst, int32_t cow_capacity,
+                            int32_t* num_cow) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  AppendPlan plan;
+  int64_t cap = (cow_src && cow_dst) ? std::max(cow_capacity, 0) : INT64_MAX;
+  kvc_status st = plan_append(c, batch, seq_ids, n_new, slots_out != nullptr, cap, &plan);
+  if (st != KVC_OK) return st;
+  if (slots_out) std::copy(plan.slots.begin(), plan.slots.end(), slots_out);
+  if (cow_src && cow_dst)
+    for (size_t i = 0; i < plan.cow.size(); ++i) {
+      cow_src[i] = plan.cow[i].src;
+      cow_dst[i] = plan.cow[i].dst;
+    }
+  if (num_cow) *num_cow = (int32_t)plan.cow.size();
+  return ok();
+}
+
+kvc_status kvc_get_table(const kvc_cache* cc, int64_t seq_id, int32_t* blocks_out, int32_t max_blocks,
+                         int32_t* num_blocks, int32_t* length) {
+  kvc_cache* c = const_cast<kvc_cache*>(cc);
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  auto it = c->seqs.find(seq_id);
+  if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)seq_id);
+  const auto& s = it->second;
+  if (blocks_out) {
+    int32_t n = std::min<int32_t>(max_blocks, (int32_t)s.blocks.size());
+    std::copy(s.blocks.begin(), s.blocks.begin() + std::max(n, 0), blocks_out);
+  }
+  if (num_blocks) *num_blocks = (int32_t)s.blocks.size();
+  if (length) *length = s.len;
+  return ok();
+}
+
+kvc_status kvc_stats(const kvc_cache* cc, kvc_stats_t* out) {
+  kvc_cache* c = const_cast<kvc_cache*>(cc);
+  if (!c || !out) return fail(KVC_E_INVALID, "cache and out must be non-NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  out->total_blocks = c->cfg.num_blocks;
+  out->free_blocks = (int64_t)c->free_list.size();
+  out->used_blocks = c->used;
+  int64_t shared = 0;
+  for (int32_t r : c->ref) shared += (r >= 2);
+  out->shared_blocks = shared;
+  out->peak_used_blocks = c->peak_used;
+  out->cow_copies = c->cow_copies;
+  out->num_seqs = (int64_t)c->seqs.size();
+  return ok();
+}
+
+kvc_status kvc_append(kvc_cache* c, int32_t batch, const int64_t* seq_ids, const int32_t* n_new,
+                      const void* k_new, const void* v_new, kvc_dtype in_dtype, kvc_stream_t stream) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  kvc_status st = check_device_ready(c);
+  if (st != KVC_OK) return st;
+  const kvc_dtype kv = c->cfg.kv_dtype;
+  if (!valid_dtype(in_dtype)) return fail(KVC_E_INVALID, "unknown in_dtype");
+  if (kv == KVC_FP8_E4M3 ? in_dtype == KVC_FP8_E4M3 : in_dtype != kv)
+    return fail(KVC_E_UNSUPPORTED, "append rows of dtype %d into a cache of dtype %d", (int)in_dtype, (int)kv);
+  if (batch < 0) return fail(KVC_E_INVALID, "batch must be >= 0");
+  int64_t total = 0;
+  int32_t active = 0;
+  for (int32_t i = 0; i < batch; ++i) {
+    int32_t n = n_new ? n_new[i] : 1;
+    if (n < 0) return fail(KVC_E_INVALID, "n_new[%d] < 0", i);
+    total += n;
+    active += (n > 0);
+  }
+  if (total > 0 && (!k_new || !v_new)) return fail(KVC_E_INVALID, "k_new / v_new are NULL");
+  if (total > INT32_MAX) return fail(KVC_E_INVALID, "too many rows in one append");
+  size_t need = kvc_scratch_bytes(active, total);
+  if (!c->cfg.dev_scratch || c->cfg.dev_scratch_bytes < need)
+    return fail(KVC_E_WORKSPACE, "dev_scratch has %zu bytes, this append needs %zu", c->cfg.dev_scratch_bytes, need);
+  // Get the staging buffer before touching the bookkeeping so that a HIP
+  // failure here leaves the allocator unchanged.
+  const int64_t smax = max_segments(active, total);
+  const size_t seg_bytes = align256((size_t)smax * sizeof(AppendSegment));
+  st = staging_acquire(c, need);
+  if (st != KVC_OK) return st;
+  AppendPlan plan;
+  st = plan_append(c, batch, seq_ids, n_new, false, INT64_MAX, &plan);
+  if (st != KVC_OK) return st;
+  if (plan.segs.empty()) return ok();
+  char* stg = static_cast<char*>(c->staging);
+  std::memcpy(stg, plan.segs.data(), plan.segs.size() * sizeof(AppendSegment));
+  if (!plan.cow.empty()) std::memcpy(stg + seg_bytes, plan.cow.data(), plan.cow.size() * sizeof(CowPair));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  size_t upload = plan.cow.empty() ? plan.segs.size() * sizeof(AppendSegment)
+                                   : seg_bytes + plan.cow.size() * sizeof(CowPair);
+  // The bookkeeping is committed at this point; device failures below are
+  // reported but the blocks stay reserved (the caller frees the sequences).
+  st = staging_upload(c, c->cfg.dev_scratch, upload, s);
+  if (st != KVC_OK) return st;
+  const kvc::PoolDesc pool = c->pool();
+  char* scratch = static_cast<char*>(c->cfg.dev_scratch);
+  if (!plan.cow.empty()) {
+    hipError_t e = kvc::launch_copy_blocks(pool, reinterpret_cast<const CowPair*>(scratch + seg_bytes),
+                                           (int32_t)plan.cow.size(), s);
+    if (e != hipSuccess) return fail(KVC_E_HIP, "copy-on-write launch: %s", hipGetErrorString(e));
+  }
+  hipError_t e = kvc::launch_append(pool, reinterpret_cast<const AppendSegment*>(scratch), (int32_t)plan.segs.size(),
+                                    k_new, v_new, in_dtype, total, s);
+  if (e != hipSuccess) return fail(KVC_E_HIP, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvc_status kvc_export_tables(kvc_cache* c, int32_t batch, const int64_t* seq_ids, int32_t* block_table,
+                             int32_t max_blocks, int32_t* context_lens, kvc_stream_t stream) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  if (batch < 0 || max_blocks < 1) return fail(KVC_E_INVALID, "batch must be >= 0 and max_blocks >= 1");
+  if (batch == 0) return ok();
+  if (!seq_ids || !block_table || !context_lens) return fail(KVC_E_INVALID, "NULL argument");
+  std::vector<const kvc_cache::Seq*> rows(batch);
+  for (int32_t i = 0; i < batch; ++i) {
+    auto it = c->seqs.find(seq_ids[i]);
+    if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if ((int64_t)it->second.blocks.size() > max_blocks)
+      return fail(KVC_E_INVALID, "sequence %lld has %zu blocks > max_blocks %d", (long long)seq_ids[i],
+                  it->second.blocks.size(), max_blocks);
+    rows[i] = &it->second;
+  }
+  size_t table_bytes = (size_t)batch * max_blocks * sizeof(int32_t);
+  size_t lens_off = align256(table_bytes);
+  kvc_status st = staging_acquire(c, lens_off + (size_t)batch * sizeof(int32_t));
+  if (st != KVC_OK) return st;
+  int32_t* t = static_cast<int32_t*>(c->staging);
+  int32_t* l = reinterpret_cast<int32_t*>(static_cast<char*>(c->staging) + lens_off);
+  for (int32_t i = 0; i < batch; ++i) {
+    const auto& b = rows[i]->blocks;
+    std::copy(b.begin(), b.end(), t + (size_t)i * max_blocks);
+    std::fill(t + (size_t)i * max_blocks + b.size(), t + (size_t)(i + 1) * max_blocks, -1);
+    l[i] = rows[i]->len;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(block_table, t, table_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(context_lens, l, batch * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipEventRecord(c->staging_free, s);
+  if (e != hipSuccess) return fail(KVC_E_HIP, "table upload: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_context_len, const kvc_decode_opts* opts) {
+  if (batch < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_context_len < 1) return 0;
+  kvc::DecodePlan p;
+  if (!plan_decode(batch, num_kv_heads, max_context_len, opts, &p)) return 0;
+  return workspace_bytes_for(batch, num_heads, head_dim, p);
+}
+
+kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_dtype q_dtype,
+                                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, float scale, void* out, void* workspace,
+                                size_t workspace_bytes, const kvc_decode_opts* opts, kvc_stream_t stream) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  kvc_status st = check_device_ready(c);
+  if (st != KVC_OK) return st;
+  const kvc_config& f = c->cfg;
+  if (layer < 0 || layer >= f.num_layers) return fail(KVC_E_INVALID, "layer %d outside 0..%d", layer, f.num_layers - 1);
+  if (batch < 0) return fail(KVC_E_INVALID, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (num_kv_heads != f.num_kv_heads) return fail(KVC_E_INVALID, "num_kv_heads %d != cache's %d", num_kv_heads, f.num_kv_heads);
+  if (head_dim != f.head_dim) return fail(KVC_E_INVALID, "head_dim %d != cache's %d", head_dim, f.head_dim);
+  if (block_size != f.block_size) return fail(KVC_E_INVALID, "block_size %d != cache's %d", block_size, f.block_size);
+  if (num_heads < 1 || num_heads % num_kv_heads != 0)
+    return fail(KVC_E_INVALID, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
+  if (num_heads / num_kv_heads > 16) return fail(KVC_E_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (!q || !block_table || !context_lens || !out) return fail(KVC_E_INVALID, "NULL device argument");
+  if (max_blocks_per_seq < 1) return fail(KVC_E_INVALID, "max_blocks_per_seq must be >= 1");
+  if (max_context_len < 1) return fail(KVC_E_INVALID, "max_context_len must be >= 1");
+  const kvc_dtype kv = f.kv_dtype;
+  bool dt_ok = (kv == KVC_FP8_E4M3) ? (q_dtype == KVC_BF16) : (q_dtype == kv);
+  if (!dt_ok) return fail(KVC_E_UNSUPPORTED, "q dtype %d with a cache of dtype %d", (int)q_dtype, (int)kv);
+  if (!(scale == scale)) return fail(KVC_E_INVALID, "scale is NaN");
+  kvc::DecodePlan plan;
+  if (!plan_decode(batch, num_kv_heads, std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size),
+                   opts, &plan))
+    return fail(KVC_E_INVALID, "partition_tokens must be a multiple of 16 and at most 1024");
+  if (plan.kernel == 0) plan.kernel = (kv == KVC_F32) ? 1 : 2;
+  if (plan.kernel == 2 && kv == KVC_F32) return fail(KVC_E_UNSUPPORTED, "the MFMA kernel needs a 16-bit or fp8 cache");
+  if (plan.kernel != 1 && plan.kernel != 2) return fail(KVC_E_INVALID, "unknown kernel %d", plan.kernel);
+  size_t need = workspace_bytes_for(batch, num_heads, head_dim, plan);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  hipError_t e = kvc::launch_decode(c->pool(), layer, plan, q, q_dtype, block_table, max_blocks_per_seq, context_lens,
+                                    max_context_len, batch, num_heads, scale, out, workspace,
+                                    opts ? static_cast<hipEvent_t>(opts->split_start) : nullptr,
+                                    opts ? static_cast<hipEvent_t>(opts->split_end) : nullptr,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVC_E_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvc_status kvc_stream_copy(void* dst, const void* src, size_t bytes, kvc_stream_t stream) {
+  if (!dst || !src) return fail(KVC_E_INVALID, "NULL pointer");
+  if (bytes % 16 != 0) return fail(KVC_E_INVALID, "bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  hipError_t e = kvc::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVC_E_HIP, "copy launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

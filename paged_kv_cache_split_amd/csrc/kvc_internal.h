@@ -1,0 +1,76 @@
+// Internal interface between the host half of libkvc (kvc_host.cpp) and its
+// HIP kernels (kvc_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+// One contiguous run of new rows that lands in one physical block:
+// rows [row, row + count) of the append input go to slots
+// [offset, offset + count) of `block`.  `offset` rows were already valid.
+struct AppendSegment {
+  int32_t block;
+  int32_t offset;
+  int32_t count;
+  int32_t row;
+};
+
+struct CowPair {
+  int32_t src;
+  int32_t dst;
+};
+
+// Device pool description for one cache.
+struct PoolDesc {
+  char* k;
+  char* v;
+  float* k_scale;
+  float* v_scale;
+  int32_t num_layers;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  kvc_dtype dtype;
+};
+
+__host__ __device__ inline int dtype_bytes(kvc_dtype t) {
+  switch (t) {
+    case KVC_F32: return 4;
+    case KVC_F16: return 2;
+    case KVC_BF16: return 2;
+    case KVC_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+// Bytes of one (block, head) tile of one pool.
+__host__ __device__ inline int64_t tile_bytes(const PoolDesc& p) {
+  return (int64_t)p.head_dim * p.block_size * dtype_bytes(p.dtype);
+}
+
+struct DecodePlan {
+  int32_t partition_tokens;
+  int32_t num_partitions;  // max over the batch: ceil(max_context_len / partition_tokens)
+  int32_t kernel;          // 1 = FMA, 2 = MFMA
+};
+
+// Launchers (kvc_kernels.hip).  They only launch; arguments are validated by
+// the caller.  Return hipSuccess or the launch error.
+hipError_t launch_copy_blocks(const PoolDesc& pool, const CowPair* pairs_dev, int32_t num_pairs,
+                              hipStream_t stream);
+hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, int32_t num_segments,
+                         const void* k_new, const void* v_new, kvc_dtype in_dtype, int64_t total_rows,
+                         hipStream_t stream);
+hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q,
+                         kvc_dtype q_dtype, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* context_lens, int32_t max_context_len, int32_t batch, int32_t num_heads,
+                         float scale, void* out, void* workspace, hipEvent_t ev_start, hipEvent_t ev_end,
+                         hipStream_t stream);
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace kvc

@@ -1,0 +1,867 @@
+// HIP kernels of libkvc for CDNA4 (gfx950): append into the paged pool
+// (with fp8 quantisation), copy-on-write block copies, the split-K paged
+// decode kernels (fp32 FMA and MFMA variants), the partial merge, and a plain
+// streaming copy used for bandwidth calibration.
+//
+// Pool layout (one (block, KV head) tile of block_size = 16 tokens):
+//   K tile: [head_dim / X][16][X] elements, X = 16 bytes / element size, so
+//           a 16-byte chunk holds X consecutive dims of one token and the 16
+//           tokens' chunk c are 256 contiguous bytes;
+//   V tile: [head_dim][16], V transposed (token index fastest).
+// Block ids index the same tile position in every layer and both pools.
+//
+// What the decode computes (pages cited by title and section): per query
+// head, softmax(q K^T * scale) V over the sequence's cached rows including
+// the one just appended ("LLM推理优化实战：从KV-Cache到Continuous Batching…" §1.1;
+// "苦猿的大模型日记 · Day45 · 大模型推理加速" PART 02); query head h reads KV head
+// h / G ("大模型推理加速核心KV Cache 复用机制与内存布局优化" §二); rows are reached
+// through a per-sequence block table (same page §三).  Each work-group covers
+// one (KV partition, KV head, sequence); inside it the rows are consumed 16
+// at a time with the online-softmax recurrence (running max m, sum l and
+// accumulator rescaled by exp(m_old - m_new), "LLM推理优化实战…" §3.2), and the
+// per-partition (m, l, acc) triples are merged exactly by a second kernel
+// (the "merge between blocks" of "大模型推理加速核心KV Cache…" §四).  Scores are
+// kept in the base-2 domain (scale * log2(e) folded in), which leaves the
+// softmax unchanged.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBS = 16;                       // tokens per block (device work)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------------------
+// Scalar conversions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+  return (float)h;
+}
+
+// float -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// OCP E4M3 ("FN") code -> float, from the format definition: bias 7,
+// exponent field 0 subnormal (m/8 * 2^-6).  Used where the value must be exact
+// and independent of hardware conversion modes (re-encoding held codes).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  float mag = (e == 0) ? (float)m * 0.001953125f                       // m * 2^-9
+                       : __uint_as_float(((e + 120u) << 23) | (m << 20));  // 2^(e-7) * (1 + m/8)
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// float -> E4M3 code, round to nearest even, saturating at +-448 (never NaN).
+// Signed zero is kept.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = __builtin_fabsf(x);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {                          // below 2^-6: subnormal grid m * 2^-9
+    float q = __builtin_rintf(a * 512.0f);      // exact scaling, then round half to even
+    return sign | (uint32_t)q;                  // q == 8 is the smallest normal code 0x08
+  }
+  uint32_t au = __float_as_uint(a);
+  uint32_t e = (au >> 23) - 127u + 7u;          // biased E4M3 exponent, 1..15
+  uint32_t mant = au & 0x7FFFFFu;
+  uint32_t r = mant >> 20, rem = mant & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  if (r == 8u) { r = 0; ++e; }
+  uint32_t code = (e << 3) | r;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+template <kvc_dtype T>
+__device__ __forceinline__ float load_elem(const void* base, int64_t i) {
+  if constexpr (T == KVC_F32) return static_cast<const float*>(base)[i];
+  else if constexpr (T == KVC_F16) return f16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+  else return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int clamp_block(int b, int num_blocks) {
+  return (b < 0 || b >= num_blocks) ? 0 : b;
+}
+
+// Tokens to attend for sequence b, clamped so every access stays in bounds.
+__device__ __forceinline__ int attend_len(const int32_t* context_lens, int b, int max_ctx, int max_blocks) {
+  int n = context_lens[b];
+  n = n < max_ctx ? n : max_ctx;
+  int cap = max_blocks * kBS;
+  return n < cap ? n : cap;
+}
+
+// ---------------------------------------------------------------------------
+// Copy-on-write: copy whole blocks (every layer, head, K and V, fp8 scales).
+// grid (num_pairs, num_layers), 256 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void copy_blocks_kernel(PoolDesc p, const CowPair* pairs) {
+  const CowPair pr = pairs[blockIdx.x];
+  const int layer = blockIdx.y;
+  const int64_t block_bytes = (int64_t)p.num_kv_heads * tile_bytes(p);
+  const int64_t layer_bytes = (int64_t)p.num_blocks * block_bytes;
+  const int64_t src = layer * layer_bytes + (int64_t)pr.src * block_bytes;
+  const int64_t dst = layer * layer_bytes + (int64_t)pr.dst * block_bytes;
+  for (int64_t i = threadIdx.x * 16; i < block_bytes; i += 256 * 16) {
+    *reinterpret_cast<u32x4*>(p.k + dst + i) = *reinterpret_cast<const u32x4*>(p.k + src + i);
+    *reinterpret_cast<u32x4*>(p.v + dst + i) = *reinterpret_cast<const u32x4*>(p.v + src + i);
+  }
+  if (p.dtype == KVC_FP8_E4M3) {
+    const int64_t so = ((int64_t)layer * p.num_blocks + pr.src) * p.num_kv_heads;
+    const int64_t dof = ((int64_t)layer * p.num_blocks + pr.dst) * p.num_kv_heads;
+    for (int h = threadIdx.x; h < p.num_kv_heads; h += 256) {
+      p.k_scale[dof + h] = p.k_scale[so + h];
+      p.v_scale[dof + h] = p.v_scale[so + h];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append (reshape-and-cache) for f32 / f16 / bf16 caches: a plain copy of
+// every new row into its slot.  grid (num_segments, num_kv_heads, num_layers),
+// 64 threads.
+// ---------------------------------------------------------------------------
+template <int EBYTES>
+__global__ __launch_bounds__(64) void append_copy_kernel(PoolDesc p, const AppendSegment* segs, const char* k_new,
+                                                         const char* v_new, int64_t total_rows) {
+  const AppendSegment sg = segs[blockIdx.x];
+  const int h = blockIdx.y, layer = blockIdx.z;
+  const int D = p.head_dim, H = p.num_kv_heads;
+  constexpr int X = 16 / EBYTES;
+  const int nch = D / X;
+  const int64_t tb = tile_bytes(p);
+  const int64_t tile_off = ((int64_t)layer * p.num_blocks + sg.block) * H * tb + (int64_t)h * tb;
+  char* kt = p.k + tile_off;
+  char* vt = p.v + tile_off;
+  const int64_t row_bytes = (int64_t)H * D * EBYTES;
+  const char* ksrc = k_new + ((int64_t)layer * total_rows + sg.row) * row_bytes + (int64_t)h * D * EBYTES;
+  const char* vsrc = v_new + ((int64_t)layer * total_rows + sg.row) * row_bytes + (int64_t)h * D * EBYTES;
+  // K: 16-byte chunks, chunk c of row r -> tile[c][offset + r][:]
+  for (int i = threadIdx.x; i < sg.count * nch; i += 64) {
+    int r = i / nch, c = i % nch;
+    u32x4 val = *reinterpret_cast<const u32x4*>(ksrc + r * row_bytes + c * 16);
+    *reinterpret_cast<u32x4*>(kt + ((int64_t)c * kBS + sg.offset + r) * 16) = val;
+  }
+  // V: element (r, d) -> tile[d][offset + r]
+  for (int i = threadIdx.x; i < sg.count * D; i += 64) {
+    int r = i / D, d = i % D;
+    const char* s = vsrc + r * row_bytes + (int64_t)d * EBYTES;
+    char* t = vt + ((int64_t)d * kBS + sg.offset + r) * EBYTES;
+    if constexpr (EBYTES == 4) *reinterpret_cast<uint32_t*>(t) = *reinterpret_cast<const uint32_t*>(s);
+    else *reinterpret_cast<uint16_t*>(t) = *reinterpret_cast<const uint16_t*>(s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append into an fp8 (E4M3) cache: per (segment, KV head, K or V) apply the
+// scale rule -- s_new = max(s_old, amax/448); re-encode held codes when the
+// scale grows; encode the new rows with s_new.  grid (num_segments,
+// num_kv_heads, 2 * num_layers), 64 threads (one wave).
+// ---------------------------------------------------------------------------
+template <kvc_dtype IN>
+__global__ __launch_bounds__(64) void append_fp8_kernel(PoolDesc p, const AppendSegment* segs, const void* k_new,
+                                                        const void* v_new, int64_t total_rows) {
+  const AppendSegment sg = segs[blockIdx.x];
+  const int h = blockIdx.y;
+  const int layer = blockIdx.z >> 1;
+  const bool is_v = blockIdx.z & 1;
+  const int D = p.head_dim, H = p.num_kv_heads;
+  const int lane = threadIdx.x;
+  const int64_t tb = tile_bytes(p);  // D * 16 bytes
+  uint8_t* tile = reinterpret_cast<uint8_t*>((is_v ? p.v : p.k) + ((int64_t)layer * p.num_blocks + sg.block) * H * tb +
+                                             (int64_t)h * tb);
+  float* scale_ptr = (is_v ? p.v_scale : p.k_scale) + ((int64_t)layer * p.num_blocks + sg.block) * H + h;
+  const void* src = is_v ? v_new : k_new;
+  const int64_t src_row0 = ((int64_t)layer * total_rows + sg.row) * H * D + (int64_t)h * D;
+  // Position of element (slot, d) inside the tile.
+  auto at = [&](int slot, int d) -> int64_t {
+    return is_v ? (int64_t)d * kBS + slot : ((int64_t)(d >> 4) * kBS + slot) * 16 + (d & 15);
+  };
+  float amax = 0.0f;
+  for (int i = lane; i < sg.count * D; i += 64) {
+    int r = i / D, d = i % D;
+    amax = fmaxf(amax, __builtin_fabsf(load_elem<IN>(src, src_row0 + (int64_t)r * H * D + d)));
+  }
+  amax = wave_max(amax);
+  const float s_old = sg.offset > 0 ? *scale_ptr : 0.0f;
+  const float s_new = fmaxf(s_old, amax / 448.0f);
+  if (s_new > s_old && sg.offset > 0) {
+    for (int i = lane; i < sg.offset * D; i += 64) {
+      int r = i / D, d = i % D;
+      int64_t o = at(r, d);
+      float x = e4m3_decode(tile[o]) * s_old;
+      tile[o] = (uint8_t)e4m3_encode(x / s_new);
+    }
+  }
+  for (int i = lane; i < sg.count * D; i += 64) {
+    int r = i / D, d = i % D;
+    float x = load_elem<IN>(src, src_row0 + (int64_t)r * H * D + d);
+    tile[at(sg.offset + r, d)] = (uint8_t)e4m3_encode(s_new > 0.0f ? x / s_new : x);
+  }
+  if (lane == 0) *scale_ptr = s_new;
+}
+
+// ---------------------------------------------------------------------------
+// Decode arguments (one layer).
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+  const void* q;
+  void* out;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* ws_acc;   // [B][Hq][NP][D]
+  float* ws_m;     // [B][Hq][NP]
+  float* ws_l;     // [B][Hq][NP]
+  const char* k;   // layer base of the K pool
+  const char* v;   // layer base of the V pool
+  const float* k_scale;  // layer base (fp8)
+  const float* v_scale;
+  int64_t tile_bytes;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t part_tokens;
+  int32_t num_parts;
+  float qk_scale;  // softmax scale * log2(e)
+};
+
+template <kvc_dtype QT>
+__device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
+  if constexpr (QT == KVC_F32) static_cast<float*>(out)[i] = v;
+  else if constexpr (QT == KVC_F16) static_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_f16_bits(v);
+  else static_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K decode, fp32 FMA (VALU) variant.  One wave per (partition, KV head,
+// sequence).  Scores: lane = (token t = lane / 4, quarter j = lane % 4), each
+// lane dots a quarter of head_dim against the group's queries held in LDS,
+// then a quad reduction.  Values: lane owns head_dim / 64 dims and sums the
+// 16 tokens' weighted rows, weights broadcast from LDS.
+// ---------------------------------------------------------------------------
+template <kvc_dtype KV, kvc_dtype QT, int D, int GMAX>
+__global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
+  const int t0 = part * a.part_tokens;
+  if (t0 >= n) return;
+  const int t1 = min(n, t0 + a.part_tokens);
+  const int G = a.group;
+  constexpr int EB = (KV == KVC_F32) ? 4 : (KV == KVC_FP8_E4M3 ? 1 : 2);
+  constexpr int X = 16 / EB;
+  constexpr int NCH = D / X;        // 16-byte chunks per token row
+  constexpr int CPL = NCH / 4;      // chunks per lane
+  constexpr int DPL = D / 64;       // output dims per lane
+
+  __shared__ float q_s[GMAX][D];
+  __shared__ float p_s[GMAX][kBS];
+  for (int i = lane; i < GMAX * D; i += 64) {
+    int hh = i / D, d = i % D;
+    float qv = 0.0f;
+    if (hh < G) qv = load_elem<QT>(a.q, ((int64_t)b * a.num_heads + g * G + hh) * D + d) * a.qk_scale;
+    q_s[hh][d] = qv;
+  }
+  __syncthreads();
+
+  const int t = lane >> 2, j = lane & 3;
+  float m[GMAX], l[GMAX], acc[GMAX][DPL];
+#pragma unroll
+  for (int hh = 0; hh < GMAX; ++hh) {
+    m[hh] = kNegInf;
+    l[hh] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[hh][i] = 0.0f;
+  }
+  const int32_t* row = a.block_table + (int64_t)b * a.max_blocks;
+  for (int kb = t0 / kBS; kb * kBS < t1; ++kb) {
+    const int phys = clamp_block(row[kb], a.num_blocks);
+    const int64_t toff = ((int64_t)phys * a.num_kv_heads + g) * a.tile_bytes;
+    const char* kt = a.k + toff;
+    const char* vt = a.v + toff;
+    float ksc = 1.0f, vsc = 1.0f;
+    if constexpr (KV == KVC_FP8_E4M3) {
+      ksc = a.k_scale[(int64_t)phys * a.num_kv_heads + g];
+      vsc = a.v_scale[(int64_t)phys * a.num_kv_heads + g];
+    }
+    float s[GMAX];
+#pragma unroll
+    for (int hh = 0; hh < GMAX; ++hh) s[hh] = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+      const int c = cc * 4 + j;
+      u32x4 raw = *reinterpret_cast<const u32x4*>(kt + ((int64_t)c * kBS + t) * 16);
+      float kx[X];
+      if constexpr (KV == KVC_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kx[e] = __uint_as_float(raw[e]);
+      } else if constexpr (KV == KVC_FP8_E4M3) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) kx[e] = e4m3_decode((raw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t bits = (raw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          kx[e] = (KV == KVC_F16) ? f16_bits_to_f32(bits) : bf16_bits_to_f32(bits);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < GMAX; ++hh) {
+        if (hh < G) {
+#pragma unroll
+          for (int e = 0; e < X; ++e) s[hh] = fmaf(q_s[hh][c * X + e], kx[e], s[hh]);
+        }
+      }
+    }
+    const bool valid = kb * kBS + t < t1;
+    float alpha[GMAX];
+#pragma unroll
+    for (int hh = 0; hh < GMAX; ++hh) {
+      float v = s[hh];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v = valid ? v * ksc : kNegInf;
+      float mx = v;
+      mx = fmaxf(mx, __shfl_xor(mx, 4));
+      mx = fmaxf(mx, __shfl_xor(mx, 8));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[hh], mx);
+      alpha[hh] = __builtin_amdgcn_exp2f(m[hh] - mnew);
+      const float pv = __builtin_amdgcn_exp2f(v - mnew);
+      l[hh] = l[hh] * alpha[hh] + (j == 0 ? pv : 0.0f);
+      m[hh] = mnew;
+      if (j == 0 && hh < G) p_s[hh][t] = pv * vsc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int d = lane + 64 * i;
+      float vx[kBS];
+      const char* vrow = vt + (int64_t)d * kBS * EB;
+      if constexpr (KV == KVC_F32) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x4 r = *reinterpret_cast<const u32x4*>(vrow + q4 * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vx[q4 * 4 + e] = __uint_as_float(r[e]);
+        }
+      } else if constexpr (KV == KVC_FP8_E4M3) {
+        u32x4 r = *reinterpret_cast<const u32x4*>(vrow);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vx[e] = e4m3_decode((r[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      } else {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u32x4 r = *reinterpret_cast<const u32x4*>(vrow + h2 * 16);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint32_t bits = (r[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            vx[h2 * 8 + e] = (KV == KVC_F16) ? f16_bits_to_f32(bits) : bf16_bits_to_f32(bits);
+          }
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < GMAX; ++hh) {
+        if (hh < G) {
+          float acc_h = acc[hh][i] * alpha[hh];
+#pragma unroll
+          for (int tt = 0; tt < kBS; ++tt) acc_h = fmaf(p_s[hh][tt], vx[tt], acc_h);
+          acc[hh][i] = acc_h;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const int parts_b = (n + a.part_tokens - 1) / a.part_tokens;
+#pragma unroll
+  for (int hh = 0; hh < GMAX; ++hh) {
+    if (hh >= G) continue;
+    const float lt = wave_sum(l[hh]);
+    const int h = g * G + hh;
+    if (parts_b == 1) {
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) store_out<QT>(a.out, ((int64_t)b * a.num_heads + h) * D + lane + 64 * i, acc[hh][i] * inv);
+    } else {
+      const int64_t r = ((int64_t)b * a.num_heads + h) * a.num_parts + part;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) a.ws_acc[r * D + lane + 64 * i] = acc[hh][i];
+      if (lane == 0) {
+        a.ws_m[r] = m[hh];
+        a.ws_l[r] = lt;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K decode, MFMA variant (16-bit and fp8 caches).  One wave per
+// (partition, KV head, sequence); the group's G <= 16 query heads are the 16
+// columns of the matrix-core tiles (zero-padded).
+//   scores^T [16 tokens x 16 heads] = K_tile [16 x D] * Q^T [D x 16 heads]
+//       with v_mfma_f32_16x16x32_{bf16,f16}: lane (row = lane % 16, group
+//       r = lane / 16) feeds the 16-byte K chunk (4 kk + r) of token lane % 16
+//       straight from memory, and the same dims of query head lane % 16;
+//   out^T [16 dims x 16 heads] += V^T_tile [16 dims x 16 tokens] * P^T
+//       with v_mfma_f32_16x16x16: the score tile's lane layout (tokens
+//       4r..4r+3 of head lane % 16) is exactly the P^T operand, and V^T rows
+//       give each lane its 4 tokens as one 8-byte load.
+// Softmax runs on the score tile: a lane's 4 values plus two cross-group
+// shuffles give the per-head block max.
+// ---------------------------------------------------------------------------
+template <kvc_dtype KV>
+__device__ __forceinline__ floatx4 mfma_qk(const u32x4& a, const u32x4& b, floatx4 c) {
+  if constexpr (KV == KVC_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                   0);
+}
+
+template <kvc_dtype KV>
+__device__ __forceinline__ floatx4 mfma_pv(const u32x2& a, const u32x2& b, floatx4 c) {
+  if constexpr (KV == KVC_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c, 0, 0,
+                                                     0);
+}
+
+// Two E4M3 codes (bytes 2*sel, 2*sel+1 of w) -> two bf16 packed in a dword.
+// E4M3 values are exact in bf16 (3-bit mantissa, exponents 2^-9 .. 2^8).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  floatx2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+template <kvc_dtype KV, int D>
+struct KvBlock {
+  static constexpr int NK = (KV == KVC_FP8_E4M3) ? D / 64 : D / 32;  // 16-byte K loads per lane
+  static constexpr int NV = D / 16;                                   // V^T loads per lane
+  u32x4 k[NK];
+  typename std::conditional<KV == KVC_FP8_E4M3, uint32_t, u32x2>::type v[NV];
+};
+
+template <kvc_dtype KV, int D>
+__device__ __forceinline__ void load_block(KvBlock<KV, D>& blk, const char* kt, const char* vt, int nn, int r) {
+  if constexpr (KV == KVC_FP8_E4M3) {
+    // K tile [D/16][16][16]: lane loads chunks r and r + 4 (16 dims each) of token nn.
+#pragma unroll
+    for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2)
+      blk.k[c2] = *reinterpret_cast<const u32x4*>(kt + ((int64_t)(r + 4 * c2) * kBS + nn) * 16);
+    // V^T tile [D][16] bytes: tokens 4r..4r+3 of dim 16*dd + nn.
+#pragma unroll
+    for (int dd = 0; dd < KvBlock<KV, D>::NV; ++dd)
+      blk.v[dd] = *reinterpret_cast<const uint32_t*>(vt + (int64_t)(16 * dd + nn) * kBS + 4 * r);
+  } else {
+    // K tile [D/8][16][8]: chunk 4*kk + r of token nn.
+#pragma unroll
+    for (int kk = 0; kk < KvBlock<KV, D>::NK; ++kk)
+      blk.k[kk] = *reinterpret_cast<const u32x4*>(kt + ((int64_t)(4 * kk + r) * kBS + nn) * 16);
+#pragma unroll
+    for (int dd = 0; dd < KvBlock<KV, D>::NV; ++dd)
+      blk.v[dd] = *reinterpret_cast<const u32x2*>(vt + ((int64_t)(16 * dd + nn) * kBS + 4 * r) * 2);
+  }
+}
+
+template <kvc_dtype KV, int D>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
+  const int t0 = part * a.part_tokens;
+  if (t0 >= n) return;
+  const int t1 = min(n, t0 + a.part_tokens);
+  const int nn = lane & 15, r = lane >> 4;
+  const int G = a.group;
+  const bool head_ok = nn < G;
+  const int h = g * G + nn;
+  constexpr int NQK = D / 32;   // QK matrix-core steps (32 dims each)
+  constexpr int NDD = D / 16;   // output dim tiles
+
+  // Query operand: for step kk the lane holds 8 dims of head nn, the same dims
+  // its K operand holds for token nn.
+  u32x4 qv[NQK];
+  {
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_heads + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < NQK; ++kk) {
+      int d0;
+      if constexpr (KV == KVC_FP8_E4M3) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
+      else d0 = (4 * kk + r) * 8;
+      qv[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
+    }
+  }
+  floatx4 acc[NDD];
+#pragma unroll
+  for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.0f;
+
+  const int kb0 = t0 / kBS;
+  const int nblk = (t1 + kBS - 1) / kBS - kb0;   // <= 64 (partition <= 1024 tokens)
+  const int32_t* row = a.block_table + (int64_t)b * a.max_blocks + kb0;
+  const int my_id = lane < nblk ? clamp_block(row[lane], a.num_blocks) : 0;
+  const int64_t head_off = (int64_t)g * a.tile_bytes;
+
+  KvBlock<KV, D> cur, nxt;
+  {
+    const int phys = __builtin_amdgcn_readfirstlane(my_id);
+    const int64_t toff = (int64_t)phys * a.num_kv_heads * a.tile_bytes + head_off;
+    load_block<KV, D>(cur, a.k + toff, a.v + toff, nn, r);
+  }
+  for (int i = 0; i < nblk; ++i) {
+    const int phys = __builtin_amdgcn_readlane(my_id, i);
+    if (i + 1 < nblk) {
+      const int pn = __builtin_amdgcn_readlane(my_id, i + 1);
+      const int64_t toff = (int64_t)pn * a.num_kv_heads * a.tile_bytes + head_off;
+      load_block<KV, D>(nxt, a.k + toff, a.v + toff, nn, r);
+    }
+    // scores^T for the 16 tokens of this block
+    floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+    float qk = a.qk_scale;
+    float vsc = 1.0f;
+    if constexpr (KV == KVC_FP8_E4M3) {
+      qk *= a.k_scale[(int64_t)phys * a.num_kv_heads + g];
+      vsc = a.v_scale[(int64_t)phys * a.num_kv_heads + g];
+#pragma unroll
+      for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
+        u32x4 lo, hi;
+        lo[0] = fp8x2_to_bf16x2<false>(cur.k[c2][0]);
+        lo[1] = fp8x2_to_bf16x2<true>(cur.k[c2][0]);
+        lo[2] = fp8x2_to_bf16x2<false>(cur.k[c2][1]);
+        lo[3] = fp8x2_to_bf16x2<true>(cur.k[c2][1]);
+        hi[0] = fp8x2_to_bf16x2<false>(cur.k[c2][2]);
+        hi[1] = fp8x2_to_bf16x2<true>(cur.k[c2][2]);
+        hi[2] = fp8x2_to_bf16x2<false>(cur.k[c2][3]);
+        hi[3] = fp8x2_to_bf16x2<true>(cur.k[c2][3]);
+        s = mfma_qk<KV>(lo, qv[2 * c2], s);
+        s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
+    }
+    const int tbase = (kb0 + i) * kBS + 4 * r;
+    float sv[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = (tbase + e < t1) ? s[e] * qk : kNegInf;
+      mx = fmaxf(mx, sv[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    float pv[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
+      psum += pv[e];
+    }
+    l = l * alpha + psum;
+    m = mnew;
+    u32x2 pb;
+    if constexpr (KV == KVC_F16) {
+      pb[0] = f32_to_f16_bits(pv[0]) | (f32_to_f16_bits(pv[1]) << 16);
+      pb[1] = f32_to_f16_bits(pv[2]) | (f32_to_f16_bits(pv[3]) << 16);
+    } else {
+      pb[0] = f32_to_bf16_bits(pv[0] * vsc) | (f32_to_bf16_bits(pv[1] * vsc) << 16);
+      pb[1] = f32_to_bf16_bits(pv[2] * vsc) | (f32_to_bf16_bits(pv[3] * vsc) << 16);
+    }
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) {
+      acc[dd] *= alpha;
+      u32x2 va;
+      if constexpr (KV == KVC_FP8_E4M3) {
+        va[0] = fp8x2_to_bf16x2<false>(cur.v[dd]);
+        va[1] = fp8x2_to_bf16x2<true>(cur.v[dd]);
+      } else {
+        va = cur.v[dd];
+      }
+      acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
+    }
+    if (i + 1 < nblk) cur = nxt;
+  }
+  // l over the head's 16 tokens-per-block lanes
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!head_ok) return;
+  const int parts_b = (n + a.part_tokens - 1) / a.part_tokens;
+  // lane holds out^T[d = 16*dd + 4r + e][head nn]
+  if (parts_b == 1) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) {
+      const int64_t o = ((int64_t)b * a.num_heads + h) * D + 16 * dd + 4 * r;
+      u32x2 w;
+      if constexpr (KV == KVC_F16) {
+        w[0] = f32_to_f16_bits(acc[dd][0] * inv) | (f32_to_f16_bits(acc[dd][1] * inv) << 16);
+        w[1] = f32_to_f16_bits(acc[dd][2] * inv) | (f32_to_f16_bits(acc[dd][3] * inv) << 16);
+      } else {
+        w[0] = f32_to_bf16_bits(acc[dd][0] * inv) | (f32_to_bf16_bits(acc[dd][1] * inv) << 16);
+        w[1] = f32_to_bf16_bits(acc[dd][2] * inv) | (f32_to_bf16_bits(acc[dd][3] * inv) << 16);
+      }
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = w;
+    }
+  } else {
+    const int64_t rr = ((int64_t)b * a.num_heads + h) * a.num_parts + part;
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd)
+      *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[dd];
+    if (r == 0) {
+      a.ws_m[rr] = m;
+      a.ws_l[rr] = l;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the per-partition triples: M = max_p m_p; out = sum_p acc_p 2^(m_p - M)
+// / sum_p l_p 2^(m_p - M).  One work-group of 256 threads per (head, sequence);
+// D/4 threads cover one partition row with 16-byte loads, the rest stride over
+// partitions, and the rows are combined through LDS.
+// ---------------------------------------------------------------------------
+template <kvc_dtype QT, int D>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
+  const int np = (n + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;
+  constexpr int TPR = D / 4;          // threads per partition row
+  constexpr int ROWS = 256 / TPR;     // partition rows in flight
+  __shared__ float red[256];
+  __shared__ floatx4 part_acc[ROWS][TPR];
+  __shared__ float part_l[ROWS];
+  const int64_t base = ((int64_t)b * a.num_heads + h) * a.num_parts;
+  float mx = kNegInf;
+  for (int p = tid; p < np; p += 256) mx = fmaxf(mx, a.ws_m[base + p]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  const int prow = tid / TPR, c = tid % TPR;
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.0f;
+#pragma unroll 4
+  for (int p = prow; p < np; p += ROWS) {
+    const float w = __builtin_amdgcn_exp2f(a.ws_m[base + p] - M);
+    const floatx4 v = *reinterpret_cast<const floatx4*>(a.ws_acc + (base + p) * D + 4 * c);
+    acc += v * w;
+    L += w * a.ws_l[base + p];
+  }
+  part_acc[prow][c] = acc;
+  if (c == 0) part_l[prow] = L;
+  __syncthreads();
+  if (tid < TPR) {
+    floatx4 tot = part_acc[0][tid];
+    float lt = part_l[0];
+#pragma unroll
+    for (int rr = 1; rr < ROWS; ++rr) {
+      tot += part_acc[rr][tid];
+      lt += part_l[rr];
+    }
+    const float inv = 1.0f / lt;
+    const int64_t o = ((int64_t)b * a.num_heads + h) * D + 4 * tid;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, tot[e] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Plain streaming copy (calibration).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stream_copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                          int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+template <kvc_dtype KV, kvc_dtype QT, int D>
+hipError_t launch_fma(const DecodeArgs& a, int G, dim3 grid, hipStream_t s) {
+  if (G <= 1) hipLaunchKernelGGL((decode_fma_kernel<KV, QT, D, 1>), grid, dim3(64), 0, s, a);
+  else if (G <= 2) hipLaunchKernelGGL((decode_fma_kernel<KV, QT, D, 2>), grid, dim3(64), 0, s, a);
+  else if (G <= 4) hipLaunchKernelGGL((decode_fma_kernel<KV, QT, D, 4>), grid, dim3(64), 0, s, a);
+  else if (G <= 8) hipLaunchKernelGGL((decode_fma_kernel<KV, QT, D, 8>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_fma_kernel<KV, QT, D, 16>), grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <kvc_dtype KV, kvc_dtype QT>
+hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, dim3 grid, dim3 mgrid, bool merge,
+                               hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+  if (kernel == 1) {
+    e = (D == 64) ? launch_fma<KV, QT, 64>(a, a.group, grid, s) : launch_fma<KV, QT, 128>(a, a.group, grid, s);
+  } else {
+    if constexpr (KV != KVC_F32) {
+      if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128>), grid, dim3(64), 0, s, a);
+      e = hipGetLastError();
+    } else {
+      e = hipErrorInvalidValue;
+    }
+  }
+  if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+  if (merge) {
+    if (D == 64) hipLaunchKernelGGL((merge_kernel<QT, 64>), mgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((merge_kernel<QT, 128>), mgrid, dim3(256), 0, s, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const PoolDesc& pool, const CowPair* pairs_dev, int32_t num_pairs, hipStream_t stream) {
+  if (num_pairs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, pool.num_layers), dim3(256), 0, stream, pool, pairs_dev);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, int32_t num_segments, const void* k_new,
+                         const void* v_new, kvc_dtype in_dtype, int64_t total_rows, hipStream_t stream) {
+  if (num_segments <= 0) return hipSuccess;
+  const char* kn = static_cast<const char*>(k_new);
+  const char* vn = static_cast<const char*>(v_new);
+  switch (pool.dtype) {
+    case KVC_F32:
+      hipLaunchKernelGGL(append_copy_kernel<4>, dim3(num_segments, pool.num_kv_heads, pool.num_layers), dim3(64), 0,
+                         stream, pool, segs_dev, kn, vn, total_rows);
+      break;
+    case KVC_F16:
+    case KVC_BF16:
+      hipLaunchKernelGGL(append_copy_kernel<2>, dim3(num_segments, pool.num_kv_heads, pool.num_layers), dim3(64), 0,
+                         stream, pool, segs_dev, kn, vn, total_rows);
+      break;
+    case KVC_FP8_E4M3: {
+      dim3 grid(num_segments, pool.num_kv_heads, 2 * pool.num_layers);
+      if (in_dtype == KVC_F32)
+        hipLaunchKernelGGL(append_fp8_kernel<KVC_F32>, grid, dim3(64), 0, stream, pool, segs_dev, k_new, v_new, total_rows);
+      else if (in_dtype == KVC_F16)
+        hipLaunchKernelGGL(append_fp8_kernel<KVC_F16>, grid, dim3(64), 0, stream, pool, segs_dev, k_new, v_new, total_rows);
+      else
+        hipLaunchKernelGGL(append_fp8_kernel<KVC_BF16>, grid, dim3(64), 0, stream, pool, segs_dev, k_new, v_new, total_rows);
+      break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q, kvc_dtype q_dtype,
+                         const int32_t* block_table, int32_t max_blocks, const int32_t* context_lens,
+                         int32_t max_context_len, int32_t batch, int32_t num_heads, float scale, void* out,
+                         void* workspace, hipEvent_t ev_start, hipEvent_t ev_end, hipStream_t stream) {
+  DecodeArgs a;
+  const int64_t tb = tile_bytes(pool);
+  const int64_t layer_bytes = (int64_t)pool.num_blocks * pool.num_kv_heads * tb;
+  a.q = q;
+  a.out = out;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.k = pool.k + layer * layer_bytes;
+  a.v = pool.v + layer * layer_bytes;
+  a.k_scale = pool.k_scale ? pool.k_scale + (int64_t)layer * pool.num_blocks * pool.num_kv_heads : nullptr;
+  a.v_scale = pool.v_scale ? pool.v_scale + (int64_t)layer * pool.num_blocks * pool.num_kv_heads : nullptr;
+  a.tile_bytes = tb;
+  a.num_blocks = pool.num_blocks;
+  a.max_blocks = max_blocks;
+  a.max_ctx = max_context_len;
+  a.num_heads = num_heads;
+  a.num_kv_heads = pool.num_kv_heads;
+  a.group = num_heads / pool.num_kv_heads;
+  a.part_tokens = plan.partition_tokens;
+  a.num_parts = plan.num_partitions;
+  a.qk_scale = scale * kLog2e;
+  const bool merge = plan.num_partitions > 1;
+  if (merge) {
+    const size_t rows = (size_t)batch * num_heads * plan.num_partitions;
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    char* w = static_cast<char*>(workspace);
+    a.ws_acc = reinterpret_cast<float*>(w);
+    a.ws_m = reinterpret_cast<float*>(w + al(rows * pool.head_dim * sizeof(float)));
+    a.ws_l = reinterpret_cast<float*>(w + al(rows * pool.head_dim * sizeof(float)) + al(rows * sizeof(float)));
+  } else {
+    a.ws_acc = a.ws_m = a.ws_l = nullptr;
+  }
+  dim3 grid(plan.num_partitions, pool.num_kv_heads, batch);
+  dim3 mgrid(num_heads, batch);
+  const int D = pool.head_dim;
+  switch (pool.dtype) {
+    case KVC_F32:
+      return launch_decode_typed<KVC_F32, KVC_F32>(a, D, plan.kernel, grid, mgrid, merge, ev_start, ev_end, stream);
+    case KVC_F16:
+      return launch_decode_typed<KVC_F16, KVC_F16>(a, D, plan.kernel, grid, mgrid, merge, ev_start, ev_end, stream);
+    case KVC_BF16:
+      return launch_decode_typed<KVC_BF16, KVC_BF16>(a, D, plan.kernel, grid, mgrid, merge, ev_start, ev_end, stream);
+    case KVC_FP8_E4M3:
+      return launch_decode_typed<KVC_FP8_E4M3, KVC_BF16>(a, D, plan.kernel, grid, mgrid, merge, ev_start, ev_end,
+                                                         stream);
+  }
+  (void)q_dtype;
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<u32x4*>(dst),
+                     static_cast<const u32x4*>(src), n16);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

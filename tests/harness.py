@@ -1,0 +1,166 @@
+"""Drive one workload through the HIP library and through the oracle.
+
+The two sides share only the workload (``workloads``): the GPU side runs the
+setup operations through libkvc, the oracle side through ``oracle.kvstore``.
+``pool_layout`` reads device pools back into (block, layer, head, slot, dim)
+order following the layout documented in include/kvc.h.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from workloads import make_values, setup_ops
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+BITS_TORCH = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
+BITS_NP = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+
+
+def to_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Raw storage bits of a tensor of the given dtype, as an unsigned numpy array."""
+    t = t.detach().cpu().contiguous()
+    if dtype == "fp8":
+        return t.view(torch.uint8).numpy()
+    return t.view(BITS_TORCH[dtype]).numpy().view(BITS_NP[dtype])
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+# -- pool layout (include/kvc.h) ------------------------------------------------
+
+def read_pools(cache):
+    """Pools of a KVCache as raw bits [N, L, H, block_size, D] (and fp8 scales [N, L, H]).
+
+    K pool [L][N][H][D/x][bs][x], V pool [L][N][H][D][bs], x = 16 / element bytes.
+    """
+    L, N, H, D, bs, dt = (cache.num_layers, cache.num_blocks, cache.num_kv_heads, cache.head_dim,
+                          cache.block_size, cache.kv_dtype)
+    x = 16 // ELEM_BYTES[dt]
+    k = cache.k_pool.detach().cpu().numpy().view(BITS_NP[dt]).reshape(L, N, H, D // x, bs, x)
+    k = k.transpose(1, 0, 2, 4, 3, 5).reshape(N, L, H, bs, D)
+    v = cache.v_pool.detach().cpu().numpy().view(BITS_NP[dt]).reshape(L, N, H, D, bs)
+    v = v.transpose(1, 0, 2, 4, 3)
+    out = dict(k=np.ascontiguousarray(k), v=np.ascontiguousarray(v))
+    if dt == "fp8":
+        out["k_scale"] = cache.k_scale.cpu().numpy().reshape(L, N, H).transpose(1, 0, 2).copy()
+        out["v_scale"] = cache.v_scale.cpu().numpy().reshape(L, N, H).transpose(1, 0, 2).copy()
+    return out
+
+
+# -- GPU side -------------------------------------------------------------------
+
+def gpu_setup(wl, values, device="cuda"):
+    """Build the cache and the history through libkvc; returns the KVCache."""
+    from paged_kv_cache_split_amd import KVCache
+    cache = KVCache(wl.num_layers, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.kv_dtype,
+                    block_size=wl.block_size, device=device, free_order=wl.free_order)
+    k_hist = values["k_hist"].to(device)
+    v_hist = values["v_hist"].to(device)
+    row = 0
+    for op in setup_ops(wl):
+        if op[0] == "add":
+            cache.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            cache.fork(op[1], op[2])
+        elif op[0] == "append":
+            seqs, n_new = op[1], op[2]
+            t = int(sum(n_new))
+            if t:
+                cache.append(seqs, k_hist[:, row:row + t].contiguous(), v_hist[:, row:row + t].contiguous(),
+                             n_new=n_new)
+            row += t
+    return cache
+
+
+def gpu_step(cache, wl, values, kernel=0, partition_tokens=0, device="cuda", out=None):
+    """The decode step: append each sequence's new token, export tables, decode."""
+    seqs = list(range(wl.batch))
+    cache.append(seqs, values["k_new"].to(device).contiguous(), values["v_new"].to(device).contiguous())
+    bt, cl = cache.export_tables(seqs)
+    q = values["q"].to(device).contiguous()
+    o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
+                     out=out)
+    return o, bt, cl
+
+
+def gpu_decode_again(cache, wl, values, bt, cl, kernel=0, partition_tokens=0, device="cuda"):
+    q = values["q"].to(device).contiguous()
+    return cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens)
+
+
+# -- oracle side ------------------------------------------------------------------
+
+def oracle_run(wl, values):
+    """Execute the setup and the step's append on the oracle's store; return it."""
+    from oracle.kvstore import KVStoreModel
+    st = KVStoreModel(wl.num_layers, wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.kv_dtype,
+                      free_order=wl.free_order, in_dtype=wl.new_dtype)
+    kb = to_bits(values["k_hist"], wl.new_dtype)
+    vb = to_bits(values["v_hist"], wl.new_dtype)
+    row = 0
+    for op in setup_ops(wl):
+        if op[0] == "add":
+            assert st.allocate(op[1], op[2]) == 0
+        elif op[0] == "fork":
+            assert st.fork(op[1], op[2]) == 0
+        elif op[0] == "append":
+            t = int(sum(op[2]))
+            status, _, _ = st.append(op[1], op[2], kb[:, row:row + t], vb[:, row:row + t])
+            assert status == 0
+            row += t
+    seqs = list(range(wl.batch))
+    status, slots, cow = st.append(seqs, [1] * wl.batch, to_bits(values["k_new"], wl.new_dtype),
+                                   to_bits(values["v_new"], wl.new_dtype))
+    assert status == 0
+    return st
+
+
+def oracle_decode(st, wl, values, seqs=None, layer=0):
+    """fp64 decode outputs [len(seqs), Hq, D] from the oracle store's stored values."""
+    from oracle.attention import decode_attention
+    q = to_f64(values["q"])
+    seqs = list(range(wl.batch)) if seqs is None else list(seqs)
+    out = np.empty((len(seqs), wl.num_heads, wl.head_dim))
+    for i, b in enumerate(seqs):
+        k, v = st.gather(b, layer)
+        out[i] = decode_attention(q[b], k, v, wl.scale)
+    return out
+
+
+def logical_history(wl, values, b, layer=0):
+    """The unquantised K/V rows of sequence b in position order (history + new
+    token), as fp64, straight from the workload tensors."""
+    k_hist, v_hist = values["k_hist"], values["v_hist"]
+    rows = _history_rows(wl, b)
+    k = torch.cat([k_hist[layer, rows], values["k_new"][layer, b:b + 1]]).to(torch.float64).cpu().numpy()
+    v = torch.cat([v_hist[layer, rows], values["v_new"][layer, b:b + 1]]).to(torch.float64).cpu().numpy()
+    return k, v
+
+
+def _history_rows(wl, b):
+    lens = [int(x) for x in wl.context_lens]
+    if wl.shared_prefix:
+        p = wl.shared_prefix
+        start = p + sum(l - p for l in lens[:b])
+        return torch.cat([torch.arange(0, p), torch.arange(start, start + lens[b] - p)])
+    start = sum(lens[:b])
+    return torch.arange(start, start + lens[b])
+
+
+def check_close(gpu: np.ndarray, ref: np.ndarray, atol: float, rtol: float, what: str):
+    """Per element |gpu - ref| <= atol + rtol * |ref|; returns (max_abs, max_rel)."""
+    d = np.abs(gpu - ref)
+    bad = d > atol + rtol * np.abs(ref)
+    max_abs = float(d.max()) if d.size else 0.0
+    big = np.abs(ref) > 1e-3
+    max_rel = float((d[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance "
+                             f"(atol {atol}, rtol {rtol}); first at {tuple(idx)}: gpu {gpu[tuple(idx)]!r} "
+                             f"ref {ref[tuple(idx)]!r}; max_abs {max_abs:.3e} max_rel {max_rel:.3e}")
+    return max_abs, max_rel

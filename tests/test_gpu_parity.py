@@ -1,0 +1,154 @@
+"""GPU parity: libkvc's HIP path against the oracle (needs an MI355X).
+
+* append: the whole pool (and fp8 scales) bit-exact against the oracle's store,
+  block tables and lengths bit-exact against the oracle's allocator model;
+* decode: per element |gpu - ref| <= atol + rtol * |ref| with (2e-3, 1e-2) for
+  f32 / f16 / bf16 caches and for fp8 against the oracle fed the stored
+  (dequantised) values, and (5e-2, 1e-2) for fp8 against the unquantised rows;
+* placement invariance and run-to-run determinism bitwise; partition-boundary
+  sweeps; both decode kernels (fp32 FMA and MFMA).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+from harness import (check_close, gpu_decode_again, gpu_setup, gpu_step, logical_history, oracle_decode, oracle_run,
+                     read_pools, to_f64)
+from workloads import custom_workload, make_values, make_workload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+TOL = {"f32": (2e-3, 1e-2), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2), "fp8": (2e-3, 1e-2)}
+FP8_UNQUANT_TOL = (5e-2, 1e-2)
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _kernels_for(wl):
+    return [1] if wl.kv_dtype == "f32" else [1, 2]
+
+
+def _check_append(cache, st, wl, bt, cl):
+    pools = read_pools(cache)
+    assert np.array_equal(pools["k"], st.k), "K pool differs from the oracle's store"
+    assert np.array_equal(pools["v"], st.v), "V pool differs from the oracle's store"
+    if wl.kv_dtype == "fp8":
+        assert np.array_equal(pools["k_scale"].view(np.uint32), st.k_scale.view(np.uint32))
+        assert np.array_equal(pools["v_scale"].view(np.uint32), st.v_scale.view(np.uint32))
+    rows, lens = st.tables.export(list(range(wl.batch)), bt.shape[1])
+    assert np.array_equal(bt.cpu().numpy(), np.array(rows, dtype=np.int32))
+    assert np.array_equal(cl.cpu().numpy(), np.array(lens, dtype=np.int32))
+    assert np.array_equal(cl.cpu().numpy(), wl.attend_lens)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_small_configs_append_and_decode(cid):
+    wl = make_workload(cid, small=True)
+    _say(f"[parity] config {cid} (small): {wl.name}")
+    values = make_values(wl, "cpu")
+    st = oracle_run(wl, values)
+    cache = gpu_setup(wl, values)
+    out, bt, cl = gpu_step(cache, wl, values)
+    torch.cuda.synchronize()
+    _check_append(cache, st, wl, bt, cl)
+    ref = oracle_decode(st, wl, values)
+    atol, rtol = TOL[wl.kv_dtype]
+    for kernel in _kernels_for(wl):
+        o = out if kernel == _kernels_for(wl)[-1] else gpu_decode_again(cache, wl, values, bt, cl, kernel=kernel)
+        got = to_f64(o)
+        ma, mr = check_close(got, ref, atol, rtol, f"config {cid} kernel {kernel}")
+        _say(f"  kernel {kernel}: max_abs {ma:.2e} max_rel {mr:.2e}")
+    if wl.kv_dtype == "fp8":
+        from oracle.attention import decode_attention
+        q = to_f64(values["q"])
+        for b in range(wl.batch):
+            k, v = logical_history(wl, values, b)
+            r = decode_attention(q[b], k, v, wl.scale)
+            check_close(to_f64(out[b]), r, *FP8_UNQUANT_TOL, f"config 5 seq {b} vs unquantised rows")
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "fp8"])
+@pytest.mark.parametrize("pt", [16, 64])
+def test_partition_boundaries(kv, pt):
+    lens = [0, 14, 15, 16, pt - 2, pt - 1, pt, pt + 15, 2 * pt, 3 * pt + 5]
+    wl = custom_workload(len(lens), 8, 2, 64 if kv == "f32" else 128, kv, lens, seed=11, name=f"boundary {kv} {pt}")
+    _say(f"[parity] partition boundaries kv={kv} partition_tokens={pt}")
+    values = make_values(wl, "cpu")
+    st = oracle_run(wl, values)
+    cache = gpu_setup(wl, values)
+    out, bt, cl = gpu_step(cache, wl, values, partition_tokens=pt)
+    torch.cuda.synchronize()
+    _check_append(cache, st, wl, bt, cl)
+    ref = oracle_decode(st, wl, values)
+    for kernel in _kernels_for(wl):
+        o = gpu_decode_again(cache, wl, values, bt, cl, kernel=kernel, partition_tokens=pt)
+        check_close(to_f64(o), ref, *TOL[kv], f"{kv} P={pt} kernel {kernel}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (8, 4, 128), (16, 4, 64), (16, 1, 128), (32, 2, 128), (12, 3, 64)])
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8"])
+def test_head_groupings(hq, hkv, d, kv):
+    lens = [5, 40, 300, 129]
+    wl = custom_workload(len(lens), hq, hkv, d, kv, lens, seed=hq * 7 + hkv, name="groupings")
+    _say(f"[parity] heads {hq}/{hkv} D={d} kv={kv}")
+    values = make_values(wl, "cpu")
+    st = oracle_run(wl, values)
+    cache = gpu_setup(wl, values)
+    out, bt, cl = gpu_step(cache, wl, values, partition_tokens=128)
+    torch.cuda.synchronize()
+    ref = oracle_decode(st, wl, values)
+    for kernel in (1, 2):
+        o = gpu_decode_again(cache, wl, values, bt, cl, kernel=kernel, partition_tokens=128)
+        check_close(to_f64(o), ref, *TOL[kv], f"{hq}/{hkv} D{d} {kv} kernel {kernel}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_placement_invariance_and_determinism(kv):
+    lens = [100, 33, 257, 1]
+    outs = []
+    for seed_order in (None, 5):
+        wl = custom_workload(len(lens), 16, 4, 128, kv, lens, seed=3, name="placement")
+        if seed_order is None:
+            wl.free_order = np.arange(wl.num_blocks, dtype=np.int32)[::-1].copy()   # pops 0, 1, 2, ...: contiguous
+        else:
+            wl.free_order = np.random.default_rng(seed_order).permutation(wl.num_blocks).astype(np.int32)
+        values = make_values(wl, "cpu")
+        cache = gpu_setup(wl, values)
+        out, bt, cl = gpu_step(cache, wl, values, partition_tokens=64)
+        again = gpu_decode_again(cache, wl, values, bt, cl, partition_tokens=64)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "decode not deterministic"
+        outs.append(out.cpu())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "result depends on placement"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_fork_mid_block_copy_on_write(kv):
+    # prefix of 21 tokens (block 1 half full) shared by 3 sequences; each then
+    # appends its own rows: the first write into the shared half block copies it.
+    wl = custom_workload(3, 8, 2, 128, kv, [21 + 9, 21 + 2, 21 + 30], seed=4, shared_prefix=21, name="cow")
+    wl.num_blocks += 4
+    wl.free_order = np.random.default_rng(1).permutation(wl.num_blocks).astype(np.int32)
+    values = make_values(wl, "cpu")
+    st = oracle_run(wl, values)
+    cache = gpu_setup(wl, values)
+    out, bt, cl = gpu_step(cache, wl, values, partition_tokens=32)
+    torch.cuda.synchronize()
+    assert cache.stats()["cow_copies"] == st.tables.cow_copies >= 2
+    _check_append(cache, st, wl, bt, cl)
+    ref = oracle_decode(st, wl, values)
+    check_close(to_f64(out), ref, *TOL[kv], f"cow {kv}")
+
+
+def test_stream_copy_calibration_kernel():
+    from paged_kv_cache_split_amd import stream_copy
+    src = torch.randint(0, 2 ** 31 - 1, (1 << 20,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    stream_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)

@@ -1,0 +1,220 @@
+"""CPU tests of libkvc: exports, sizing, and the host allocator against the
+oracle's block-table model (bit-exact tables, slots and copy pairs).  No
+device work is issued: caches here are bookkeeping-only (no pools)."""
+import ctypes
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_split_amd as kvc
+from paged_kv_cache_split_amd import _binding as B
+from oracle import blocktable, sizing
+from oracle.blocktable import BlockTableModel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(kvc.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kvc.SYMBOLS)
+
+
+@pytest.mark.parametrize("layers,heads,dim,dt", [(36, 8, 128, "f16"), (80, 64, 128, "f16"), (1, 8, 128, "fp8"),
+                                                 (32, 32, 128, "bf16"), (1, 2, 64, "f32")])
+def test_sizing_matches_oracle(layers, heads, dim, dt):
+    assert kvc.bytes_per_token(layers, heads, dim, dt) == sizing.kv_bytes_per_token(layers, heads, dim, dt)
+    assert kvc.pool_bytes(layers, 100, heads, dim, 16, dt) == sizing.pool_bytes(layers, 100, heads, dim, 16, dt)
+    assert kvc.scale_bytes(layers, 100, heads) == sizing.scale_bytes(layers, 100, heads)
+    assert kvc.bytes_per_token(36, 8, 128, "f16") == 147456
+
+
+def _host_cache(num_blocks, block_size=16, order=None, dim=64):
+    return kvc.KVCache(1, 2, dim, num_blocks, "f16", block_size=block_size, device=None, free_order=order)
+
+
+def _same_state(c, m, seqs):
+    for s in seqs:
+        t, ln = c.get_table(s)
+        assert t == m.tables[s], (s, t, m.tables[s])
+        assert ln == m.lens[s]
+    st = c.stats()
+    assert st["free_blocks"] == len(m.free)
+    assert st["used_blocks"] == sum(1 for r in m.ref if r > 0)
+    assert st["shared_blocks"] == sum(1 for r in m.ref if r > 1)
+    assert st["cow_copies"] == m.cow_copies
+    assert st["num_seqs"] == len(m.tables)
+
+
+def test_figures_through_the_library():
+    # block_size 4: 10 tokens -> 3 blocks; fork at 6 tokens -> CoW of the half-full block
+    order = [5, 1, 7, 0, 3, 6, 2, 4]
+    c, m = _host_cache(8, 4, order), BlockTableModel(8, 4, order)
+    c.add_seq(0, 0)
+    m.allocate(0, 0)
+    slots, cow = c.reserve_host([0], [10])
+    st, ms, mc = m.append([0], [10])
+    assert slots == ms and cow == mc == []
+    c.truncate(0, 6)
+    m.truncate(0, 6)
+    c.fork(0, 1)
+    m.fork(0, 1)
+    slots, cow = c.reserve_host([0, 1], [1, 1])
+    st, ms, mc = m.append([0, 1], [1, 1])
+    assert (slots, cow) == (ms, mc) and len(cow) == 1
+    _same_state(c, m, [0, 1])
+
+
+def test_randomised_against_oracle_model():
+    rng = random.Random(7)
+    for trial in range(25):
+        bs = rng.choice([1, 4, 16])
+        nb = rng.randint(1, 60)
+        order = list(np.random.default_rng(trial).permutation(nb)) if trial % 3 else None
+        c, m = _host_cache(nb, bs, order), BlockTableModel(nb, bs, order)
+        live, nxt = [], 0
+        for _ in range(150):
+            op = rng.random()
+            if op < 0.2 or not live:
+                n = rng.randint(0, 50)
+                expect = m.allocate(nxt, n)
+                try:
+                    c.add_seq(nxt, n)
+                    got = 0
+                except kvc.KvcError as e:
+                    got = e.status
+                assert got == expect
+                if expect == 0:
+                    live.append(nxt)
+                nxt += 1
+            elif op < 0.32:
+                p = rng.choice(live)
+                c.fork(p, nxt)
+                m.fork(p, nxt)
+                live.append(nxt)
+                nxt += 1
+            elif op < 0.45:
+                s = rng.choice(live)
+                c.free_seq(s)
+                m.free_seq(s)
+                live.remove(s)
+            elif op < 0.55:
+                s = rng.choice(live)
+                n = rng.randint(0, m.lens[s])
+                c.truncate(s, n)
+                m.truncate(s, n)
+            else:
+                seqs = rng.sample(live, rng.randint(1, len(live)))
+                n_new = [rng.randint(0, 3 * bs) for _ in seqs]
+                expect, ms, mc = m.append(seqs, n_new)
+                try:
+                    slots, cow = c.reserve_host(seqs, n_new)
+                    got = 0
+                except kvc.KvcError as e:
+                    got, slots, cow = e.status, [], []
+                assert got == expect
+                assert slots == ms and cow == mc
+            _same_state(c, m, live)
+
+
+def test_status_codes():
+    c = _host_cache(4)
+    c.add_seq(1, 40)
+    with pytest.raises(kvc.KvcError) as e:
+        c.add_seq(1, 0)
+    assert e.value.status == B.E_SEQ_EXISTS
+    with pytest.raises(kvc.KvcError) as e:
+        c.add_seq(2, 17)                       # needs 2 blocks, 1 free
+    assert e.value.status == B.E_NO_BLOCKS
+    assert c.stats()["num_seqs"] == 1 and c.stats()["free_blocks"] == 1
+    with pytest.raises(kvc.KvcError) as e:
+        c.fork(9, 10)
+    assert e.value.status == B.E_NO_SEQ
+    with pytest.raises(kvc.KvcError) as e:
+        c.reserve_host([1, 1], [1, 1])
+    assert e.value.status == B.E_INVALID
+    with pytest.raises(kvc.KvcError) as e:
+        c.truncate(1, 1)                       # length is 0
+    assert e.value.status == B.E_INVALID
+    c.free_seq(1)
+    with pytest.raises(kvc.KvcError) as e:
+        c.free_seq(1)
+    assert e.value.status == B.E_NO_SEQ
+
+
+def test_reserve_oom_is_atomic_across_the_batch():
+    c, m = _host_cache(3, 4), BlockTableModel(3, 4)
+    for s in (0, 1):
+        c.add_seq(s, 0)
+        m.allocate(s, 0)
+    c.reserve_host([0, 1], [4, 4])
+    m.append([0, 1], [4, 4])
+    with pytest.raises(kvc.KvcError) as e:
+        c.reserve_host([0, 1], [1, 1])
+    assert e.value.status == B.E_NO_BLOCKS
+    _same_state(c, m, [0, 1])
+    slots, _ = c.reserve_host([0], [1])        # exactly exhausts the pool
+    assert c.stats()["free_blocks"] == 0
+
+
+def _cfg(**kw):
+    cfg = B.KvcConfig()
+    cfg.num_layers, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, cfg.num_blocks, cfg.kv_dtype = 1, 2, 64, 16, 8, 1
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+@pytest.mark.parametrize("field,value,status", [("head_dim", 96, B.E_UNSUPPORTED), ("num_layers", 0, B.E_INVALID),
+                                                ("num_kv_heads", 0, B.E_INVALID), ("block_size", 0, B.E_INVALID),
+                                                ("num_blocks", 0, B.E_INVALID), ("kv_dtype", 9, B.E_INVALID)])
+def test_create_rejects_bad_configs(field, value, status):
+    h = ctypes.c_void_p()
+    cfg = _cfg(**{field: value})
+    assert B.lib().kvc_create(ctypes.byref(cfg), ctypes.byref(h)) == status
+    assert not h.value
+    assert len(B.lib().kvc_last_error()) > 0
+
+
+def test_create_rejects_bad_free_order():
+    h = ctypes.c_void_p()
+    order = (ctypes.c_int32 * 8)(0, 1, 2, 3, 4, 5, 6, 6)
+    cfg = _cfg(free_order=ctypes.cast(order, ctypes.POINTER(ctypes.c_int32)))
+    assert B.lib().kvc_create(ctypes.byref(cfg), ctypes.byref(h)) == B.E_INVALID
+
+
+def test_device_calls_on_bookkeeping_only_cache_fail_cleanly():
+    c = _host_cache(8)
+    c.add_seq(0, 0)
+    lib = B.lib()
+    ids = (ctypes.c_int64 * 1)(0)
+    st = lib.kvc_append(c.handle, 1, ids, None, None, None, B.F16, None)
+    assert st == B.E_INVALID
+    assert c.get_table(0) == ([], 0)           # nothing reserved
+    c16 = _host_cache(8, block_size=4)
+    c16.add_seq(0, 0)
+    assert lib.kvc_append(c16.handle, 1, ids, None, None, None, B.F16, None) == B.E_UNSUPPORTED
+    st = lib.kvc_decode_attention(c.handle, 0, None, B.F16, None, 1, None, 1, 1, 4, 2, 64, 16, 0.1, None, None, 0,
+                                  None, None)
+    assert st == B.E_INVALID
+
+
+def test_workspace_sizes():
+    # one partition: no workspace; otherwise rows * (D + 2) floats, 256-byte aligned pieces
+    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, partition_tokens=256) == 0
+    ws = kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=256)
+    rows = 4 * 8 * 2
+    assert ws >= rows * (64 + 2) * 4
+    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=100) == 0   # invalid partition
