@@ -69,6 +69,25 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed 16-bit pair (element a in the low half), nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2_t v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t packed) { return (float)__builtin_bit_cast(f16x2_t, packed)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t packed) { return (float)__builtin_bit_cast(f16x2_t, packed)[1]; }
+
 // OCP E4M3 ("FN") code -> float, from the format definition: bias 7,
 // exponent field 0 subnormal (m/8 * 2^-6).  Used where the value must be exact
 // and independent of hardware conversion modes (re-encoding held codes).
@@ -607,13 +626,22 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     }
     l = l * alpha + psum;
     m = mnew;
-    u32x2 pb;
+    // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
+    // ~2^-17 relative), so rounding the weights to 16 bits costs no accuracy
+    // when the weighted values cancel.
+    u32x2 pb, pl;
     if constexpr (KV == KVC_F16) {
-      pb[0] = f32_to_f16_bits(pv[0]) | (f32_to_f16_bits(pv[1]) << 16);
-      pb[1] = f32_to_f16_bits(pv[2]) | (f32_to_f16_bits(pv[3]) << 16);
+      pb[0] = pack_f16x2(pv[0], pv[1]);
+      pb[1] = pack_f16x2(pv[2], pv[3]);
+      pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
+      pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
     } else {
-      pb[0] = f32_to_bf16_bits(pv[0] * vsc) | (f32_to_bf16_bits(pv[1] * vsc) << 16);
-      pb[1] = f32_to_bf16_bits(pv[2] * vsc) | (f32_to_bf16_bits(pv[3] * vsc) << 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+      pb[0] = pack_bf16x2(pv[0], pv[1]);
+      pb[1] = pack_bf16x2(pv[2], pv[3]);
+      pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
+      pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
     }
 #pragma unroll
     for (int dd = 0; dd < NDD; ++dd) {
@@ -626,6 +654,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         va = cur.v[dd];
       }
       acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
+      acc[dd] = mfma_pv<KV>(va, pl, acc[dd]);
     }
     if (i + 1 < nblk) cur = nxt;
   }

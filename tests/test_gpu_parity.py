@@ -64,12 +64,17 @@ def test_small_configs_append_and_decode(cid):
         ma, mr = check_close(got, ref, atol, rtol, f"config {cid} kernel {kernel}")
         _say(f"  kernel {kernel}: max_abs {ma:.2e} max_rel {mr:.2e}")
     if wl.kv_dtype == "fp8":
+        # end to end, quantisation error included: against the unquantised rows
+        # (the lengths here start at 256, as in the full fp8 workload)
         from oracle.attention import decode_attention
         q = to_f64(values["q"])
+        worst = 0.0
         for b in range(wl.batch):
             k, v = logical_history(wl, values, b)
             r = decode_attention(q[b], k, v, wl.scale)
-            check_close(to_f64(out[b]), r, *FP8_UNQUANT_TOL, f"config 5 seq {b} vs unquantised rows")
+            ma, _ = check_close(to_f64(out[b]), r, *FP8_UNQUANT_TOL, f"config 5 seq {b} vs unquantised rows")
+            worst = max(worst, ma)
+        _say(f"  fp8 vs unquantised rows: max_abs {worst:.2e}")
 
 
 @pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "fp8"])

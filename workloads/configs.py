@@ -121,8 +121,8 @@ SMALL = {
             batch=8, lens=("lognormal", 300, 1.0, 1, 1200)),
     4: dict(CONFIGS[4], name="shared-prefix GQA bf16 (scaled down), B4, 32/8 heads, D128, L700, prefix 256",
             batch=4, lens=("const", 700), shared_prefix=256),
-    5: dict(CONFIGS[5], name="fp8 KV (scaled down), B8, 64/8 heads, D128, L uniform 1..1000",
-            batch=8, lens=("uniform", 1, 1000)),
+    5: dict(CONFIGS[5], name="fp8 KV (scaled down), B8, 64/8 heads, D128, L uniform 256..1000",
+            batch=8, lens=("uniform", 256, 1000)),
 }
 
 
