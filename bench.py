@@ -35,7 +35,8 @@ def parse():
     p.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 70B-shaped GQA layer)")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--kernel", type=int, default=0, help="0 auto, 1 fp32 FMA, 2 MFMA")
-    p.add_argument("--partition-tokens", type=int, default=0)
+    p.add_argument("--partition-tokens", type=int, default=0, help="FMA kernel partition size (0 auto)")
+    p.add_argument("--work-items", type=int, default=0, help="MFMA kernel waves per KV head (0 auto)")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate", action="store_true", help="also time the plain copy kernel (2 GiB)")
@@ -134,7 +135,8 @@ def main():
     torch.cuda.synchronize()
     out = torch.empty_like(q)
     ws = torch.empty(max(256, kvc.decode_workspace_bytes(wl.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
-                                                         wl.max_context_len, args.partition_tokens, args.kernel)),
+                                                         wl.max_context_len, args.partition_tokens, args.kernel,
+                                                         args.work_items)),
                      dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -145,7 +147,7 @@ def main():
     def step(events=None):
         cache.append(seqs, k_new, v_new)
         cache.decode(q, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws, kernel=args.kernel,
-                     partition_tokens=args.partition_tokens, split_events=events)
+                     partition_tokens=args.partition_tokens, work_items=args.work_items, split_events=events)
         for s, L in zip(seqs, hist_len):
             cache.truncate(s, L)
 
@@ -183,6 +185,7 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "attended_tokens": int(wl.attend_lens.sum()), "kv_bytes": ab["kv"],
                    "kernel": ["auto", "fma", "mfma"][args.kernel], "partition_tokens": args.partition_tokens or "auto",
+                   "work_items": args.work_items or "auto",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,

@@ -201,15 +201,24 @@ kvc_status kvc_export_tables(kvc_cache* cache, int32_t batch, const int64_t* seq
                              int32_t max_blocks, int32_t* context_lens, kvc_stream_t stream);
 
 /* Decode options; pass NULL for the defaults. */
+/* Work split of the decode.
+ *  MFMA kernel: per KV head, the blocks of all sequences (in batch order) form
+ *  one list that is cut into `work_items` equal runs, one wave each; a wave
+ *  writes one partial (max, sum, acc) per sequence it touches, or the final
+ *  output when it holds a whole sequence, and a merge kernel combines the
+ *  partials.  Results are bit-for-bit reproducible for a given work_items.
+ *  FMA kernel: every sequence is cut into partitions of partition_tokens. */
 typedef struct kvc_decode_opts {
-  int32_t partition_tokens; /* tokens per KV partition (multiple of block_size); 0 = chosen from the shape */
+  int32_t partition_tokens; /* FMA kernel: tokens per partition (multiple of 16, <= 1024); 0 = chosen from the shape */
   int32_t kernel;           /* 0 = auto, 1 = fp32 FMA (VALU) kernel, 2 = MFMA kernel (16-bit and fp8 KV) */
+  int32_t work_items;       /* MFMA kernel: waves per KV head; 0 = max(1, 2048 / num_kv_heads) */
   kvc_event_t split_start;  /* optional events recorded on `stream` around the split-K kernel */
   kvc_event_t split_end;
 } kvc_decode_opts;
 
-/* Workspace bytes kvc_decode_attention needs for this shape (partials of the
- * split-K kernel; 0 when every sequence fits one partition). */
+/* Workspace bytes kvc_decode_attention needs for this shape (the split
+ * kernel's partials).  With opts->kernel == 0 it is the larger of the two
+ * kernels' needs. */
 size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_context_len, const kvc_decode_opts* opts);
 
@@ -224,7 +233,8 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
  *  out:          device [batch][num_heads][head_dim], q_dtype (rounded to nearest even)
  *  workspace:    device, kvc_decode_workspace_bytes() bytes
  * Checks: num_heads % num_kv_heads == 0 and num_heads / num_kv_heads <= 16,
- * num_kv_heads / head_dim / block_size equal the cache's, block_size 16.
+ * num_kv_heads / head_dim / block_size equal the cache's, block_size 16,
+ * batch <= 8192.
  * Device-side values are clamped so every access stays inside the arrays the
  * arguments describe: a length above max_context_len or max_blocks_per_seq *
  * block_size is cut to it, a block id outside [0, num_blocks) reads block 0

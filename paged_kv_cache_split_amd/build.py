@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     # IEEE float32 division: the fp8 scale rule divides and must round exactly
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",
+    # matrix-core accumulators in ordinary VGPRs (no AGPR copies around the
+    # online-softmax rescale)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

@@ -268,20 +268,28 @@ int32_t auto_partition_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_c
   return (int32_t)pt;
 }
 
-bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, const kvc_decode_opts* opts,
-                 kvc::DecodePlan* plan) {
+bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int32_t kernel,
+                 const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
   int32_t pt = (opts && opts->partition_tokens > 0) ? opts->partition_tokens
                                                     : auto_partition_tokens(batch, num_kv_heads, max_context_len);
   if (pt % kDeviceBlockSize != 0 || pt > 1024) return false;
+  if (opts && opts->work_items < 0) return false;
+  plan->kernel = kernel;
   plan->partition_tokens = pt;
   plan->num_partitions = std::max(1, (max_context_len + pt - 1) / pt);
-  plan->kernel = opts ? opts->kernel : 0;
+  plan->work_items = (opts && opts->work_items > 0) ? opts->work_items
+                                                    : std::max(1, kvc::kDefaultWaves / std::max(1, num_kv_heads));
   return true;
 }
 
 size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t head_dim, const kvc::DecodePlan& p) {
-  if (p.num_partitions <= 1) return 0;
-  size_t rows = (size_t)batch * num_heads * p.num_partitions;
+  size_t rows;
+  if (p.kernel == 1) {
+    if (p.num_partitions <= 1) return 0;
+    rows = (size_t)batch * num_heads * p.num_partitions;
+  } else {
+    rows = (size_t)num_heads * ((size_t)batch + p.work_items);
+  }
   return align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
 }
 
@@ -567,9 +575,15 @@ kvc_status kvc_export_tables(kvc_cache* c, int32_t batch, const int64_t* seq_ids
 size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_context_len, const kvc_decode_opts* opts) {
   if (batch < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_context_len < 1) return 0;
-  kvc::DecodePlan p;
-  if (!plan_decode(batch, num_kv_heads, max_context_len, opts, &p)) return 0;
-  return workspace_bytes_for(batch, num_heads, head_dim, p);
+  const int32_t kernel = opts ? opts->kernel : 0;
+  size_t need = 0;
+  for (int32_t k = 1; k <= 2; ++k) {
+    if (kernel != 0 && kernel != k) continue;
+    kvc::DecodePlan p;
+    if (!plan_decode(batch, num_kv_heads, max_context_len, k, opts, &p)) return 0;
+    need = std::max(need, workspace_bytes_for(batch, num_heads, head_dim, p));
+  }
+  return need;
 }
 
 kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_dtype q_dtype,
@@ -597,13 +611,15 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   bool dt_ok = (kv == KVC_FP8_E4M3) ? (q_dtype == KVC_BF16) : (q_dtype == kv);
   if (!dt_ok) return fail(KVC_E_UNSUPPORTED, "q dtype %d with a cache of dtype %d", (int)q_dtype, (int)kv);
   if (!(scale == scale)) return fail(KVC_E_INVALID, "scale is NaN");
+  if (batch > kvc::kMaxBatch) return fail(KVC_E_UNSUPPORTED, "batch %d > %d", batch, kvc::kMaxBatch);
+  int32_t kernel = opts ? opts->kernel : 0;
+  if (kernel == 0) kernel = (kv == KVC_F32) ? 1 : 2;
+  if (kernel == 2 && kv == KVC_F32) return fail(KVC_E_UNSUPPORTED, "the MFMA kernel needs a 16-bit or fp8 cache");
+  if (kernel != 1 && kernel != 2) return fail(KVC_E_INVALID, "unknown kernel %d", kernel);
   kvc::DecodePlan plan;
   if (!plan_decode(batch, num_kv_heads, std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size),
-                   opts, &plan))
-    return fail(KVC_E_INVALID, "partition_tokens must be a multiple of 16 and at most 1024");
-  if (plan.kernel == 0) plan.kernel = (kv == KVC_F32) ? 1 : 2;
-  if (plan.kernel == 2 && kv == KVC_F32) return fail(KVC_E_UNSUPPORTED, "the MFMA kernel needs a 16-bit or fp8 cache");
-  if (plan.kernel != 1 && plan.kernel != 2) return fail(KVC_E_INVALID, "unknown kernel %d", plan.kernel);
+                   kernel, opts, &plan))
+    return fail(KVC_E_INVALID, "partition_tokens must be a multiple of 16 and at most 1024, work_items >= 0");
   size_t need = workspace_bytes_for(batch, num_heads, head_dim, plan);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);

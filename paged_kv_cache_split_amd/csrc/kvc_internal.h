@@ -54,10 +54,19 @@ __host__ __device__ inline int64_t tile_bytes(const PoolDesc& p) {
 }
 
 struct DecodePlan {
+  int32_t kernel;            // 1 = FMA, 2 = MFMA
+  // FMA kernel: fixed partitions
   int32_t partition_tokens;
-  int32_t num_partitions;  // max over the batch: ceil(max_context_len / partition_tokens)
-  int32_t kernel;          // 1 = FMA, 2 = MFMA
+  int32_t num_partitions;    // ceil(max_context_len / partition_tokens)
+  // MFMA kernel: even split of each KV head's blocks over work_items waves;
+  // partial slots per query head = batch + work_items
+  int32_t work_items;
 };
+
+// Default number of waves per decode launch of the MFMA kernel (8 per CU on
+// 256 CUs).  Fixed, so results do not depend on the device's CU count.
+constexpr int32_t kDefaultWaves = 2048;
+constexpr int32_t kMaxBatch = 8192;  // the per-sequence block scan lives in LDS
 
 // Launchers (kvc_kernels.hip).  They only launch; arguments are validated by
 // the caller.  Return hipSuccess or the launch error.

@@ -268,9 +268,10 @@ struct DecodeArgs {
   void* out;
   const int32_t* block_table;
   const int32_t* context_lens;
-  float* ws_acc;   // [B][Hq][NP][D]
-  float* ws_m;     // [B][Hq][NP]
-  float* ws_l;     // [B][Hq][NP]
+  // partials: FMA kernel [B][Hq][num_parts] rows, MFMA kernel [Hq][batch + work_items] rows
+  float* ws_acc;   // rows x D
+  float* ws_m;     // rows
+  float* ws_l;     // rows
   const char* k;   // layer base of the K pool
   const char* v;   // layer base of the V pool
   const float* k_scale;  // layer base (fp8)
@@ -284,6 +285,8 @@ struct DecodeArgs {
   int32_t group;
   int32_t part_tokens;
   int32_t num_parts;
+  int32_t batch;
+  int32_t work_items;
   float qk_scale;  // softmax scale * log2(e)
 };
 
@@ -490,12 +493,12 @@ __device__ __forceinline__ floatx4 mfma_pv(const u32x2& a, const u32x2& b, float
                                                      0);
 }
 
-// Two E4M3 codes (bytes 2*sel, 2*sel+1 of w) -> two bf16 packed in a dword.
-// E4M3 values are exact in bf16 (3-bit mantissa, exponents 2^-9 .. 2^8).
+// Two E4M3 codes (bytes 0,1 or 2,3 of w) -> two bf16 packed in a dword, with
+// unit scale.  E4M3 values are exact in bf16 (3-bit mantissa, exponents
+// 2^-9 .. 2^8).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  floatx2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 template <kvc_dtype KV, int D>
@@ -506,199 +509,362 @@ struct KvBlock {
   typename std::conditional<KV == KVC_FP8_E4M3, uint32_t, u32x2>::type v[NV];
 };
 
+// K/V tiles are read once per step: non-temporal loads (streaming cache
+// policy) sustain a markedly higher HBM read rate than ordinary loads.
+template <typename T>
+__device__ __forceinline__ T load_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
+
 template <kvc_dtype KV, int D>
 __device__ __forceinline__ void load_block(KvBlock<KV, D>& blk, const char* kt, const char* vt, int nn, int r) {
   if constexpr (KV == KVC_FP8_E4M3) {
     // K tile [D/16][16][16]: lane loads chunks r and r + 4 (16 dims each) of token nn.
 #pragma unroll
     for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2)
-      blk.k[c2] = *reinterpret_cast<const u32x4*>(kt + ((int64_t)(r + 4 * c2) * kBS + nn) * 16);
+      blk.k[c2] = load_stream<u32x4>(kt + ((int64_t)(r + 4 * c2) * kBS + nn) * 16);
     // V^T tile [D][16] bytes: tokens 4r..4r+3 of dim 16*dd + nn.
 #pragma unroll
     for (int dd = 0; dd < KvBlock<KV, D>::NV; ++dd)
-      blk.v[dd] = *reinterpret_cast<const uint32_t*>(vt + (int64_t)(16 * dd + nn) * kBS + 4 * r);
+      blk.v[dd] = load_stream<uint32_t>(vt + (int64_t)(16 * dd + nn) * kBS + 4 * r);
   } else {
     // K tile [D/8][16][8]: chunk 4*kk + r of token nn.
 #pragma unroll
     for (int kk = 0; kk < KvBlock<KV, D>::NK; ++kk)
-      blk.k[kk] = *reinterpret_cast<const u32x4*>(kt + ((int64_t)(4 * kk + r) * kBS + nn) * 16);
+      blk.k[kk] = load_stream<u32x4>(kt + ((int64_t)(4 * kk + r) * kBS + nn) * 16);
 #pragma unroll
     for (int dd = 0; dd < KvBlock<KV, D>::NV; ++dd)
-      blk.v[dd] = *reinterpret_cast<const u32x2*>(vt + ((int64_t)(16 * dd + nn) * kBS + 4 * r) * 2);
+      blk.v[dd] = load_stream<u32x2>(vt + ((int64_t)(16 * dd + nn) * kBS + 4 * r) * 2);
   }
 }
 
-template <kvc_dtype KV, int D>
+// The reference max only moves when a block's max exceeds it by more than
+// this many log2 units, so weights stay <= 2^8 and the accumulator rescale
+// (and the branch into it) is skipped for almost every block.  Any reference
+// gives the same softmax; the bound only guards the float range.
+constexpr float kRescaleThreshold = 8.0f;
+
+// Exclusive scan of the sequences' block counts into LDS: seq_start[b] is the
+// first block of sequence b in the batch's concatenated block list, and
+// seq_start[batch] the total.  Every wave of the decode and every merge
+// work-group computes the same values from context_lens.
+__device__ __forceinline__ int scan_block_counts(const DecodeArgs& a, int* seq_start, int lane) {
+  int carry = 0;
+  for (int base = 0; base < a.batch; base += 64) {
+    const int bb = base + lane;
+    int nb = 0;
+    if (bb < a.batch) {
+      const int n = attend_len(a.context_lens, bb, a.max_ctx, a.max_blocks);
+      nb = n > 0 ? (n + kBS - 1) / kBS : 0;
+    }
+    int incl = nb;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (bb < a.batch) seq_start[bb] = carry + incl - nb;
+    carry += __shfl(incl, 63);
+  }
+  if (lane == 0) seq_start[a.batch] = carry;
+  return carry;
+}
+
+// First block of wave w when `total` blocks are split evenly over W waves;
+// block x belongs to wave (x * W) / total.
+__device__ __forceinline__ int wave_first_block(int64_t w, int64_t total, int64_t W) {
+  return (int)((w * total + W - 1) / W);
+}
+
+template <kvc_dtype KV, int D, int PF>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  extern __shared__ int seq_start[];   // [batch + 1]
+  const int w = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x;
-  const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
-  const int t0 = part * a.part_tokens;
-  if (t0 >= n) return;
-  const int t1 = min(n, t0 + a.part_tokens);
+  const int total = scan_block_counts(a, seq_start, lane);
+  __syncthreads();
+  // never more waves than blocks, so every wave that runs owns >= 1 block
+  const int W = a.work_items < total ? a.work_items : total;
+  if (w >= W) return;
+  const int x0 = wave_first_block(w, total, W);
+  const int x1 = wave_first_block(w + 1, total, W);
   const int nn = lane & 15, r = lane >> 4;
   const int G = a.group;
   const bool head_ok = nn < G;
   const int h = g * G + nn;
   constexpr int NQK = D / 32;   // QK matrix-core steps (32 dims each)
   constexpr int NDD = D / 16;   // output dim tiles
-
-  // Query operand: for step kk the lane holds 8 dims of head nn, the same dims
-  // its K operand holds for token nn.
-  u32x4 qv[NQK];
-  {
-    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_heads + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < NQK; ++kk) {
-      int d0;
-      if constexpr (KV == KVC_FP8_E4M3) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
-      else d0 = (4 * kk + r) * 8;
-      qv[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
-    }
-  }
-  floatx4 acc[NDD];
-#pragma unroll
-  for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, l = 0.0f;
-
-  const int kb0 = t0 / kBS;
-  const int nblk = (t1 + kBS - 1) / kBS - kb0;   // <= 64 (partition <= 1024 tokens)
-  const int32_t* row = a.block_table + (int64_t)b * a.max_blocks + kb0;
-  const int my_id = lane < nblk ? clamp_block(row[lane], a.num_blocks) : 0;
   const int64_t head_off = (int64_t)g * a.tile_bytes;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
+  const int slots = a.batch + a.work_items;
 
-  KvBlock<KV, D> cur, nxt;
+  // sequence holding block x0: the last b with seq_start[b] <= x0
+  int b = 0;
   {
-    const int phys = __builtin_amdgcn_readfirstlane(my_id);
-    const int64_t toff = (int64_t)phys * a.num_kv_heads * a.tile_bytes + head_off;
-    load_block<KV, D>(cur, a.k + toff, a.v + toff, nn, r);
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seq_start[mid] <= x0) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
   }
-  for (int i = 0; i < nblk; ++i) {
-    const int phys = __builtin_amdgcn_readlane(my_id, i);
-    if (i + 1 < nblk) {
-      const int pn = __builtin_amdgcn_readlane(my_id, i + 1);
-      const int64_t toff = (int64_t)pn * a.num_kv_heads * a.tile_bytes + head_off;
-      load_block<KV, D>(nxt, a.k + toff, a.v + toff, nn, r);
-    }
-    // scores^T for the 16 tokens of this block
-    floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-    float qk = a.qk_scale;
-    float vsc = 1.0f;
-    if constexpr (KV == KVC_FP8_E4M3) {
-      qk *= a.k_scale[(int64_t)phys * a.num_kv_heads + g];
-      vsc = a.v_scale[(int64_t)phys * a.num_kv_heads + g];
+  for (int x = x0; x < x1; ++b) {
+    const int sb = seq_start[b], eb = seq_start[b + 1];
+    if (eb <= x) continue;                      // empty sequence
+    const int seg_end = eb < x1 ? eb : x1;
+    const int first = x - sb;                   // first local block of this segment
+    const int count = seg_end - x;              // blocks in this segment
+    const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
+
+    // Query operand: for step kk the lane holds 8 dims of head nn, the same
+    // dims its K operand holds for token nn.
+    u32x4 qv[NQK];
+    {
+      const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_heads + h) * D;
 #pragma unroll
-      for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
-        u32x4 lo, hi;
-        lo[0] = fp8x2_to_bf16x2<false>(cur.k[c2][0]);
-        lo[1] = fp8x2_to_bf16x2<true>(cur.k[c2][0]);
-        lo[2] = fp8x2_to_bf16x2<false>(cur.k[c2][1]);
-        lo[3] = fp8x2_to_bf16x2<true>(cur.k[c2][1]);
-        hi[0] = fp8x2_to_bf16x2<false>(cur.k[c2][2]);
-        hi[1] = fp8x2_to_bf16x2<true>(cur.k[c2][2]);
-        hi[2] = fp8x2_to_bf16x2<false>(cur.k[c2][3]);
-        hi[3] = fp8x2_to_bf16x2<true>(cur.k[c2][3]);
-        s = mfma_qk<KV>(lo, qv[2 * c2], s);
-        s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
+      for (int kk = 0; kk < NQK; ++kk) {
+        int d0;
+        if constexpr (KV == KVC_FP8_E4M3) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
+        else d0 = (4 * kk + r) * 8;
+        qv[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
       }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
     }
-    const int tbase = (kb0 + i) * kBS + 4 * r;
-    float sv[4];
-    float mx = kNegInf;
+    floatx4 acc[NDD];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = (tbase + e < t1) ? s[e] * qk : kNegInf;
-      mx = fmaxf(mx, sv[e]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    float pv[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
-      psum += pv[e];
-    }
-    l = l * alpha + psum;
-    m = mnew;
-    // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
-    // ~2^-17 relative), so rounding the weights to 16 bits costs no accuracy
-    // when the weighted values cancel.
-    u32x2 pb, pl;
-    if constexpr (KV == KVC_F16) {
-      pb[0] = pack_f16x2(pv[0], pv[1]);
-      pb[1] = pack_f16x2(pv[2], pv[3]);
-      pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
-      pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pv[e] *= vsc;
-      pb[0] = pack_bf16x2(pv[0], pv[1]);
-      pb[1] = pack_bf16x2(pv[2], pv[3]);
-      pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
-      pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
-    }
-#pragma unroll
-    for (int dd = 0; dd < NDD; ++dd) {
-      acc[dd] *= alpha;
-      u32x2 va;
+    for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, l = 0.0f;
+
+    // Block ids of the segment, 64 per register: ids0 holds local blocks
+    // [cbase, cbase + 64), ids1 the next 64.
+    const int32_t* row = a.block_table + (int64_t)b * a.max_blocks + first;
+    auto load_ids = [&](int from) -> int {
+      return lane + from < count ? clamp_block(row[lane + from], a.num_blocks) : 0;
+    };
+    int cbase = 0;
+    int ids0 = load_ids(0);
+    int ids1 = count > 64 ? load_ids(64) : 0;
+    // physical block of local block j (j past the end re-reads the last
+    // block, an L2 hit, so every prefetch is unconditional)
+    auto phys_of = [&](int j) -> int {
+      j = j < count ? j : count - 1;
+      const int k = j - cbase;
+      return k < 64 ? __builtin_amdgcn_readlane(ids0, k) : __builtin_amdgcn_readlane(ids1, k - 64);
+    };
+    auto tile_off = [&](int j) -> int64_t { return (int64_t)phys_of(j) * block_stride + head_off; };
+
+    auto process = [&](const KvBlock<KV, D>& cur, int i) {
+      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+      float qk = a.qk_scale;
+      float vsc = 1.0f;
       if constexpr (KV == KVC_FP8_E4M3) {
-        va[0] = fp8x2_to_bf16x2<false>(cur.v[dd]);
-        va[1] = fp8x2_to_bf16x2<true>(cur.v[dd]);
-      } else {
-        va = cur.v[dd];
-      }
-      acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
-      acc[dd] = mfma_pv<KV>(va, pl, acc[dd]);
-    }
-    if (i + 1 < nblk) cur = nxt;
-  }
-  // l over the head's 16 tokens-per-block lanes
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!head_ok) return;
-  const int parts_b = (n + a.part_tokens - 1) / a.part_tokens;
-  // lane holds out^T[d = 16*dd + 4r + e][head nn]
-  if (parts_b == 1) {
-    const float inv = 1.0f / l;
+        const int phys = phys_of(i);
+        qk *= a.k_scale[(int64_t)phys * a.num_kv_heads + g];
+        vsc = a.v_scale[(int64_t)phys * a.num_kv_heads + g];
 #pragma unroll
-    for (int dd = 0; dd < NDD; ++dd) {
-      const int64_t o = ((int64_t)b * a.num_heads + h) * D + 16 * dd + 4 * r;
-      u32x2 w;
+        for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
+          u32x4 lo, hi;
+          lo[0] = fp8x2_to_bf16x2<false>(cur.k[c2][0]);
+          lo[1] = fp8x2_to_bf16x2<true>(cur.k[c2][0]);
+          lo[2] = fp8x2_to_bf16x2<false>(cur.k[c2][1]);
+          lo[3] = fp8x2_to_bf16x2<true>(cur.k[c2][1]);
+          hi[0] = fp8x2_to_bf16x2<false>(cur.k[c2][2]);
+          hi[1] = fp8x2_to_bf16x2<true>(cur.k[c2][2]);
+          hi[2] = fp8x2_to_bf16x2<false>(cur.k[c2][3]);
+          hi[3] = fp8x2_to_bf16x2<true>(cur.k[c2][3]);
+          s = mfma_qk<KV>(lo, qv[2 * c2], s);
+          s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
+      }
+      const int tbase = (first + i) * kBS + 4 * r;   // token index of this lane's first row
+      float sv[4];
+      float mx = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = (tbase + e < n) ? s[e] * qk : kNegInf;
+        mx = fmaxf(mx, sv[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool grow = mx > m + kRescaleThreshold;
+      if (__any(grow)) {
+        const float mnew = grow ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        l *= alpha;
+#pragma unroll
+        for (int dd = 0; dd < NDD; ++dd) acc[dd] *= alpha;
+        m = mnew;
+      }
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(sv[e] - m);
+        l += pv[e];
+      }
+      // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
+      // ~2^-17 relative), so rounding the weights to 16 bits costs no
+      // accuracy when the weighted values cancel.
+      u32x2 pb, pl;
       if constexpr (KV == KVC_F16) {
-        w[0] = f32_to_f16_bits(acc[dd][0] * inv) | (f32_to_f16_bits(acc[dd][1] * inv) << 16);
-        w[1] = f32_to_f16_bits(acc[dd][2] * inv) | (f32_to_f16_bits(acc[dd][3] * inv) << 16);
+        pb[0] = pack_f16x2(pv[0], pv[1]);
+        pb[1] = pack_f16x2(pv[2], pv[3]);
+        pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
+        pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
       } else {
-        w[0] = f32_to_bf16_bits(acc[dd][0] * inv) | (f32_to_bf16_bits(acc[dd][1] * inv) << 16);
-        w[1] = f32_to_bf16_bits(acc[dd][2] * inv) | (f32_to_bf16_bits(acc[dd][3] * inv) << 16);
-      }
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = w;
-    }
-  } else {
-    const int64_t rr = ((int64_t)b * a.num_heads + h) * a.num_parts + part;
+        if constexpr (KV == KVC_FP8_E4M3) {
 #pragma unroll
-    for (int dd = 0; dd < NDD; ++dd)
-      *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[dd];
-    if (r == 0) {
-      a.ws_m[rr] = m;
-      a.ws_l[rr] = l;
+          for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+        }
+        pb[0] = pack_bf16x2(pv[0], pv[1]);
+        pb[1] = pack_bf16x2(pv[2], pv[3]);
+        pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
+        pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
+      }
+#pragma unroll
+      for (int dd = 0; dd < NDD; ++dd) {
+        u32x2 va;
+        if constexpr (KV == KVC_FP8_E4M3) {
+          va[0] = fp8x2_to_bf16x2<false>(cur.v[dd]);
+          va[1] = fp8x2_to_bf16x2<true>(cur.v[dd]);
+        } else {
+          va = cur.v[dd];
+        }
+        acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
+        acc[dd] = mfma_pv<KV>(va, pl, acc[dd]);
+      }
+    };
+
+    // Ring of PF + 1 register buffers: block i + PF is in flight while block
+    // i is consumed.  The ring index is a compile-time constant after
+    // unrolling.
+    KvBlock<KV, D> buf[PF + 1];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int64_t o = tile_off(j);
+      load_block<KV, D>(buf[j], a.k + o, a.v + o, nn, r);
     }
+    for (int i0 = 0; i0 < count; i0 += PF + 1) {
+#pragma unroll
+      for (int j = 0; j <= PF; ++j) {
+        const int i = i0 + j;
+        if (i >= count) break;
+        if (i + PF >= cbase + 128) {            // prefetch index leaves ids0/ids1: slide by 64
+          cbase += 64;
+          ids0 = ids1;
+          ids1 = load_ids(cbase + 64);
+        }
+        const int64_t o = tile_off(i + PF);
+        load_block<KV, D>(buf[(j + PF) % (PF + 1)], a.k + o, a.v + o, nn, r);
+        process(buf[j], i);
+      }
+    }
+    // l over the head's four lane groups
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (head_ok) {
+      if (x == sb && seg_end == eb) {
+        // the whole sequence is in this segment: write the output
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int dd = 0; dd < NDD; ++dd) {
+          const int64_t o = ((int64_t)b * a.num_heads + h) * D + 16 * dd + 4 * r;
+          u32x2 wv;
+          if constexpr (KV == KVC_F16) {
+            wv[0] = pack_f16x2(acc[dd][0] * inv, acc[dd][1] * inv);
+            wv[1] = pack_f16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+          } else {
+            wv[0] = pack_bf16x2(acc[dd][0] * inv, acc[dd][1] * inv);
+            wv[1] = pack_bf16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+          }
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
+        }
+      } else {
+        // partial of (sequence b, wave w): slot b + w is unique, since every
+        // segment boundary advances the sequence, the wave, or both
+        const int64_t rr = (int64_t)h * slots + b + w;
+#pragma unroll
+        for (int dd = 0; dd < NDD; ++dd)
+          *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[dd];
+        if (r == 0) {
+          a.ws_m[rr] = m;
+          a.ws_l[rr] = l;
+        }
+      }
+    }
+    x = seg_end;
+  }
+}
+
+// Merge of the MFMA kernel's partials for one (query head, sequence): the
+// waves (sb * W) / T .. ((eb - 1) * W) / T (W = min(work_items, T), so each
+// owns at least one block) each left a triple in slot b + w.
+template <kvc_dtype QT, int D>
+__global__ __launch_bounds__(256) void merge_segments_kernel(DecodeArgs a) {
+  extern __shared__ int seq_start[];   // [batch + 1]
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid < 64) scan_block_counts(a, seq_start, tid);
+  __syncthreads();
+  const int64_t T = seq_start[a.batch];
+  const int64_t W = a.work_items < T ? a.work_items : T;   // as in the decode kernel
+  const int sb = seq_start[b], eb = seq_start[b + 1];
+  if (eb <= sb) return;
+  const int w_first = (int)(((int64_t)sb * W) / T);
+  const int w_last = (int)(((int64_t)(eb - 1) * W) / T);
+  if (w_first == w_last) return;      // one wave held the whole sequence
+  const int np = w_last - w_first + 1;
+  const int64_t base = (int64_t)h * (a.batch + a.work_items) + b + w_first;
+  constexpr int TPR = D / 4;          // threads per partial row
+  constexpr int ROWS = 256 / TPR;     // rows in flight
+  __shared__ float red[256];
+  __shared__ floatx4 part_acc[ROWS][TPR];
+  __shared__ float part_l[ROWS];
+  float mx = kNegInf;
+  for (int p = tid; p < np; p += 256) mx = fmaxf(mx, a.ws_m[base + p]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  const int prow = tid / TPR, c = tid % TPR;
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.0f;
+  for (int p = prow; p < np; p += ROWS) {
+    const float wgt = __builtin_amdgcn_exp2f(a.ws_m[base + p] - M);
+    acc += *reinterpret_cast<const floatx4*>(a.ws_acc + (base + p) * D + 4 * c) * wgt;
+    L += wgt * a.ws_l[base + p];
+  }
+  part_acc[prow][c] = acc;
+  if (c == 0) part_l[prow] = L;
+  __syncthreads();
+  if (tid < TPR) {
+    floatx4 tot = part_acc[0][tid];
+    float lt = part_l[0];
+#pragma unroll
+    for (int rr = 1; rr < ROWS; ++rr) {
+      tot += part_acc[rr][tid];
+      lt += part_l[rr];
+    }
+    const float inv = 1.0f / lt;
+    const int64_t o = ((int64_t)b * a.num_heads + h) * D + 4 * tid;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, tot[e] * inv);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the per-partition triples: M = max_p m_p; out = sum_p acc_p 2^(m_p - M)
+// Merge of the FMA kernel's per-partition triples: M = max_p m_p; out = sum_p acc_p 2^(m_p - M)
 // / sum_p l_p 2^(m_p - M).  One work-group of 256 threads per (head, sequence);
 // D/4 threads cover one partition row with 16-byte loads, the rest stride over
 // partitions, and the rows are combined through LDS.
 // ---------------------------------------------------------------------------
 template <kvc_dtype QT, int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
@@ -767,29 +933,38 @@ hipError_t launch_fma(const DecodeArgs& a, int G, dim3 grid, hipStream_t s) {
 }
 
 template <kvc_dtype KV, kvc_dtype QT>
-hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, dim3 grid, dim3 mgrid, bool merge,
-                               hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
+hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merge, hipEvent_t ev0, hipEvent_t ev1,
+                               hipStream_t s) {
   hipError_t e = hipSuccess;
+  const size_t scan_lds = (size_t)(a.batch + 1) * sizeof(int);
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   if (kernel == 1) {
+    dim3 grid(a.num_parts, a.num_kv_heads, a.batch);
     e = (D == 64) ? launch_fma<KV, QT, 64>(a, a.group, grid, s) : launch_fma<KV, QT, 128>(a, a.group, grid, s);
-  } else {
-    if constexpr (KV != KVC_F32) {
-      if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64>), grid, dim3(64), 0, s, a);
-      else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128>), grid, dim3(64), 0, s, a);
+    if (e != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+    if (merge) {
+      dim3 mgrid(a.num_heads, a.batch);
+      if (D == 64) hipLaunchKernelGGL((merge_parts_kernel<QT, 64>), mgrid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((merge_parts_kernel<QT, 128>), mgrid, dim3(256), 0, s, a);
       e = hipGetLastError();
-    } else {
-      e = hipErrorInvalidValue;
     }
+    return e;
   }
-  if (e != hipSuccess) return e;
-  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
-  if (merge) {
-    if (D == 64) hipLaunchKernelGGL((merge_kernel<QT, 64>), mgrid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((merge_kernel<QT, 128>), mgrid, dim3(256), 0, s, a);
-    e = hipGetLastError();
+  if constexpr (KV != KVC_F32) {
+    constexpr int PF = (KV == KVC_FP8_E4M3) ? 5 : 3;  // blocks in flight per wave
+    dim3 grid(a.work_items, a.num_kv_heads);
+    if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64, PF>), grid, dim3(64), scan_lds, s, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128, PF>), grid, dim3(64), scan_lds, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+    dim3 mgrid(a.num_heads, a.batch);
+    if (D == 64) hipLaunchKernelGGL((merge_segments_kernel<QT, 64>), mgrid, dim3(256), scan_lds, s, a);
+    else hipLaunchKernelGGL((merge_segments_kernel<QT, 128>), mgrid, dim3(256), scan_lds, s, a);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
   }
-  return e;
 }
 
 }  // namespace
@@ -853,10 +1028,13 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   a.group = num_heads / pool.num_kv_heads;
   a.part_tokens = plan.partition_tokens;
   a.num_parts = plan.num_partitions;
+  a.batch = batch;
+  a.work_items = plan.work_items;
   a.qk_scale = scale * kLog2e;
-  const bool merge = plan.num_partitions > 1;
+  const bool merge = plan.kernel == 2 || plan.num_partitions > 1;
   if (merge) {
-    const size_t rows = (size_t)batch * num_heads * plan.num_partitions;
+    const size_t rows = plan.kernel == 1 ? (size_t)batch * num_heads * plan.num_partitions
+                                         : (size_t)num_heads * ((size_t)batch + plan.work_items);
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     char* w = static_cast<char*>(workspace);
     a.ws_acc = reinterpret_cast<float*>(w);
@@ -865,19 +1043,16 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   } else {
     a.ws_acc = a.ws_m = a.ws_l = nullptr;
   }
-  dim3 grid(plan.num_partitions, pool.num_kv_heads, batch);
-  dim3 mgrid(num_heads, batch);
   const int D = pool.head_dim;
   switch (pool.dtype) {
     case KVC_F32:
-      return launch_decode_typed<KVC_F32, KVC_F32>(a, D, plan.kernel, grid, mgrid, merge, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_F32, KVC_F32>(a, D, plan.kernel, merge, ev_start, ev_end, stream);
     case KVC_F16:
-      return launch_decode_typed<KVC_F16, KVC_F16>(a, D, plan.kernel, grid, mgrid, merge, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_F16, KVC_F16>(a, D, plan.kernel, merge, ev_start, ev_end, stream);
     case KVC_BF16:
-      return launch_decode_typed<KVC_BF16, KVC_BF16>(a, D, plan.kernel, grid, mgrid, merge, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_BF16, KVC_BF16>(a, D, plan.kernel, merge, ev_start, ev_end, stream);
     case KVC_FP8_E4M3:
-      return launch_decode_typed<KVC_FP8_E4M3, KVC_BF16>(a, D, plan.kernel, grid, mgrid, merge, ev_start, ev_end,
-                                                         stream);
+      return launch_decode_typed<KVC_FP8_E4M3, KVC_BF16>(a, D, plan.kernel, merge, ev_start, ev_end, stream);
   }
   (void)q_dtype;
   return hipErrorInvalidValue;

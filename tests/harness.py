@@ -76,20 +76,21 @@ def gpu_setup(wl, values, device="cuda"):
     return cache
 
 
-def gpu_step(cache, wl, values, kernel=0, partition_tokens=0, device="cuda", out=None):
+def gpu_step(cache, wl, values, kernel=0, partition_tokens=0, device="cuda", out=None, work_items=0):
     """The decode step: append each sequence's new token, export tables, decode."""
     seqs = list(range(wl.batch))
     cache.append(seqs, values["k_new"].to(device).contiguous(), values["v_new"].to(device).contiguous())
     bt, cl = cache.export_tables(seqs)
     q = values["q"].to(device).contiguous()
     o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
-                     out=out)
+                     out=out, work_items=work_items)
     return o, bt, cl
 
 
-def gpu_decode_again(cache, wl, values, bt, cl, kernel=0, partition_tokens=0, device="cuda"):
+def gpu_decode_again(cache, wl, values, bt, cl, kernel=0, partition_tokens=0, device="cuda", work_items=0):
     q = values["q"].to(device).contiguous()
-    return cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens)
+    return cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
+                        work_items=work_items)
 
 
 # -- oracle side ------------------------------------------------------------------

@@ -80,6 +80,10 @@ def test_small_configs_append_and_decode(cid):
 @pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "fp8"])
 @pytest.mark.parametrize("pt", [16, 64])
 def test_partition_boundaries(kv, pt):
+    # Lengths around block and partition edges.  The FMA kernel cuts each
+    # sequence into pt-token partitions; the MFMA kernel cuts the batch's
+    # concatenated blocks into work_items runs, swept from one wave holding
+    # everything to more waves than blocks.
     lens = [0, 14, 15, 16, pt - 2, pt - 1, pt, pt + 15, 2 * pt, 3 * pt + 5]
     wl = custom_workload(len(lens), 8, 2, 64 if kv == "f32" else 128, kv, lens, seed=11, name=f"boundary {kv} {pt}")
     _say(f"[parity] partition boundaries kv={kv} partition_tokens={pt}")
@@ -90,9 +94,30 @@ def test_partition_boundaries(kv, pt):
     torch.cuda.synchronize()
     _check_append(cache, st, wl, bt, cl)
     ref = oracle_decode(st, wl, values)
-    for kernel in _kernels_for(wl):
-        o = gpu_decode_again(cache, wl, values, bt, cl, kernel=kernel, partition_tokens=pt)
-        check_close(to_f64(o), ref, *TOL[kv], f"{kv} P={pt} kernel {kernel}")
+    o = gpu_decode_again(cache, wl, values, bt, cl, kernel=1, partition_tokens=pt)
+    check_close(to_f64(o), ref, *TOL[kv], f"{kv} P={pt} FMA kernel")
+    if kv != "f32":
+        for wi in (1, 2, 3, 7, 13, 64, 1000):
+            o = gpu_decode_again(cache, wl, values, bt, cl, kernel=2, work_items=wi)
+            check_close(to_f64(o), ref, *TOL[kv], f"{kv} MFMA kernel work_items={wi}")
+
+
+def test_long_segments_cross_the_block_id_window():
+    # one sequence of 300 blocks held by one wave: the wave walks its block ids
+    # 64 at a time while prefetching across the window edge
+    lens = [300 * 16 - 5, 7, 130 * 16]
+    for kv in ("bf16", "fp8"):
+        wl = custom_workload(len(lens), 8, 2, 128, kv, lens, seed=21, name="long segments")
+        values = make_values(wl, "cpu")
+        st = oracle_run(wl, values)
+        cache = gpu_setup(wl, values)
+        out, bt, cl = gpu_step(cache, wl, values, kernel=2, work_items=1)
+        torch.cuda.synchronize()
+        ref = oracle_decode(st, wl, values)
+        check_close(to_f64(out), ref, *TOL[kv], f"{kv} one wave")
+        for wi in (2, 5):
+            o = gpu_decode_again(cache, wl, values, bt, cl, kernel=2, work_items=wi)
+            check_close(to_f64(o), ref, *TOL[kv], f"{kv} work_items={wi}")
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (8, 4, 128), (16, 4, 64), (16, 1, 128), (32, 2, 128), (12, 3, 64)])
@@ -124,8 +149,8 @@ def test_placement_invariance_and_determinism(kv):
             wl.free_order = np.random.default_rng(seed_order).permutation(wl.num_blocks).astype(np.int32)
         values = make_values(wl, "cpu")
         cache = gpu_setup(wl, values)
-        out, bt, cl = gpu_step(cache, wl, values, partition_tokens=64)
-        again = gpu_decode_again(cache, wl, values, bt, cl, partition_tokens=64)
+        out, bt, cl = gpu_step(cache, wl, values, partition_tokens=64, work_items=5)
+        again = gpu_decode_again(cache, wl, values, bt, cl, partition_tokens=64, work_items=5)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "decode not deterministic"
         outs.append(out.cpu())
@@ -142,7 +167,7 @@ def test_fork_mid_block_copy_on_write(kv):
     values = make_values(wl, "cpu")
     st = oracle_run(wl, values)
     cache = gpu_setup(wl, values)
-    out, bt, cl = gpu_step(cache, wl, values, partition_tokens=32)
+    out, bt, cl = gpu_step(cache, wl, values, partition_tokens=32, work_items=3)
     torch.cuda.synchronize()
     assert cache.stats()["cow_copies"] == st.tables.cow_copies >= 2
     _check_append(cache, st, wl, bt, cl)

@@ -212,9 +212,13 @@ def test_device_calls_on_bookkeeping_only_cache_fail_cleanly():
 
 
 def test_workspace_sizes():
-    # one partition: no workspace; otherwise rows * (D + 2) floats, 256-byte aligned pieces
-    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, partition_tokens=256) == 0
-    ws = kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=256)
-    rows = 4 * 8 * 2
-    assert ws >= rows * (64 + 2) * 4
-    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=100) == 0   # invalid partition
+    # FMA kernel: nothing when one partition holds every sequence, else rows * (D + 2) floats
+    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, partition_tokens=256, kernel=1) == 0
+    ws = kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=256, kernel=1)
+    assert ws >= 4 * 8 * 2 * (64 + 2) * 4
+    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=100, kernel=1) == 0   # invalid partition
+    # MFMA kernel: Hq * (batch + work_items) partial rows
+    ws2 = kvc.decode_workspace_bytes(4, 8, 2, 64, 200, kernel=2, work_items=10)
+    assert ws2 >= 8 * (4 + 10) * (64 + 2) * 4
+    # auto covers both
+    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=256, work_items=10) == max(ws, ws2)
