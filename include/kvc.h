@@ -211,7 +211,8 @@ kvc_status kvc_export_tables(kvc_cache* cache, int32_t batch, const int64_t* seq
 typedef struct kvc_decode_opts {
   int32_t partition_tokens; /* FMA kernel: tokens per partition (multiple of 16, <= 1024); 0 = chosen from the shape */
   int32_t kernel;           /* 0 = auto, 1 = fp32 FMA (VALU) kernel, 2 = MFMA kernel (16-bit and fp8 KV) */
-  int32_t work_items;       /* MFMA kernel: waves per KV head; 0 = max(1, 2048 / num_kv_heads) */
+  int32_t work_items;       /* MFMA kernel: waves per KV head; 0 = max(1, W / num_kv_heads) with
+                               W = 1024 for 16-bit caches and 2048 for fp8 caches */
   kvc_event_t split_start;  /* optional events recorded on `stream` around the split-K kernel */
   kvc_event_t split_end;
 } kvc_decode_opts;

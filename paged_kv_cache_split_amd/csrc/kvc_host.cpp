@@ -51,7 +51,7 @@ bool valid_dtype(int t) { return t >= KVC_F32 && t <= KVC_FP8_E4M3; }
 
 constexpr int kDeviceBlockSize = 16;
 
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+using kvc::align256;
 
 // Upper bound on the segments (and copy pairs) an append of `tokens` rows over
 // `batch` sequences produces with 16-token blocks: each sequence's run of n
@@ -268,7 +268,9 @@ int32_t auto_partition_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_c
   return (int32_t)pt;
 }
 
-bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int32_t kernel,
+// kv: the cache dtype, or -1 when unknown (workspace sizing without a cache:
+// then the larger default wave count is assumed).
+bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int32_t kernel, int kv,
                  const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
   int32_t pt = (opts && opts->partition_tokens > 0) ? opts->partition_tokens
                                                     : auto_partition_tokens(batch, num_kv_heads, max_context_len);
@@ -277,20 +279,15 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
   plan->kernel = kernel;
   plan->partition_tokens = pt;
   plan->num_partitions = std::max(1, (max_context_len + pt - 1) / pt);
+  const int32_t waves = kv < 0 ? std::max(kvc::kDefaultWaves16, kvc::kDefaultWavesFp8)
+                               : kvc::default_waves(static_cast<kvc_dtype>(kv));
   plan->work_items = (opts && opts->work_items > 0) ? opts->work_items
-                                                    : std::max(1, kvc::kDefaultWaves / std::max(1, num_kv_heads));
+                                                    : std::max(1, waves / std::max(1, num_kv_heads));
   return true;
 }
 
 size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t head_dim, const kvc::DecodePlan& p) {
-  size_t rows;
-  if (p.kernel == 1) {
-    if (p.num_partitions <= 1) return 0;
-    rows = (size_t)batch * num_heads * p.num_partitions;
-  } else {
-    rows = (size_t)num_heads * ((size_t)batch + p.work_items);
-  }
-  return align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
+  return kvc::workspace_layout(p.kernel, p.num_partitions, p.work_items, batch, num_heads, head_dim).bytes;
 }
 
 }  // namespace
@@ -490,48 +487,69 @@ kvc_status kvc_append(kvc_cache* c, int32_t batch, const int64_t* seq_ids, const
   if (kv == KVC_FP8_E4M3 ? in_dtype == KVC_FP8_E4M3 : in_dtype != kv)
     return fail(KVC_E_UNSUPPORTED, "append rows of dtype %d into a cache of dtype %d", (int)in_dtype, (int)kv);
   if (batch < 0) return fail(KVC_E_INVALID, "batch must be >= 0");
-  int64_t total = 0;
+  int64_t total = 0, seg_bound = 0;
   int32_t active = 0;
   for (int32_t i = 0; i < batch; ++i) {
     int32_t n = n_new ? n_new[i] : 1;
     if (n < 0) return fail(KVC_E_INVALID, "n_new[%d] < 0", i);
     total += n;
     active += (n > 0);
+    // n rows starting anywhere inside a 16-token block span at most (n + 30) / 16 blocks
+    if (n > 0) seg_bound += ((int64_t)n + 2 * kDeviceBlockSize - 2) / kDeviceBlockSize;
   }
   if (total > 0 && (!k_new || !v_new)) return fail(KVC_E_INVALID, "k_new / v_new are NULL");
   if (total > INT32_MAX) return fail(KVC_E_INVALID, "too many rows in one append");
   size_t need = kvc_scratch_bytes(active, total);
   if (!c->cfg.dev_scratch || c->cfg.dev_scratch_bytes < need)
     return fail(KVC_E_WORKSPACE, "dev_scratch has %zu bytes, this append needs %zu", c->cfg.dev_scratch_bytes, need);
+  const kvc::PoolDesc pool = c->pool();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // A plan that fits the kernel arguments needs no upload (the usual decode
+  // step); larger ones, and any copy-on-write list, go through dev_scratch.
+  const int64_t smax = max_segments(active, total);
+  const bool may_inline = seg_bound <= kvc::kInlineSegments;
+  const size_t seg_bytes = align256((size_t)smax * sizeof(AppendSegment));
   // Get the staging buffer before touching the bookkeeping so that a HIP
   // failure here leaves the allocator unchanged.
-  const int64_t smax = max_segments(active, total);
-  const size_t seg_bytes = align256((size_t)smax * sizeof(AppendSegment));
-  st = staging_acquire(c, need);
-  if (st != KVC_OK) return st;
+  if (!may_inline) {
+    st = staging_acquire(c, need);
+    if (st != KVC_OK) return st;
+  }
   AppendPlan plan;
   st = plan_append(c, batch, seq_ids, n_new, false, INT64_MAX, &plan);
   if (st != KVC_OK) return st;
   if (plan.segs.empty()) return ok();
-  char* stg = static_cast<char*>(c->staging);
-  std::memcpy(stg, plan.segs.data(), plan.segs.size() * sizeof(AppendSegment));
-  if (!plan.cow.empty()) std::memcpy(stg + seg_bytes, plan.cow.data(), plan.cow.size() * sizeof(CowPair));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  size_t upload = plan.cow.empty() ? plan.segs.size() * sizeof(AppendSegment)
-                                   : seg_bytes + plan.cow.size() * sizeof(CowPair);
   // The bookkeeping is committed at this point; device failures below are
   // reported but the blocks stay reserved (the caller frees the sequences).
-  st = staging_upload(c, c->cfg.dev_scratch, upload, s);
-  if (st != KVC_OK) return st;
-  const kvc::PoolDesc pool = c->pool();
   char* scratch = static_cast<char*>(c->cfg.dev_scratch);
+  const bool inline_plan = may_inline && plan.cow.empty();
+  if (!inline_plan) {
+    if (may_inline) {
+      st = staging_acquire(c, need);
+      if (st != KVC_OK) return st;
+    }
+    char* stg = static_cast<char*>(c->staging);
+    std::memcpy(stg, plan.segs.data(), plan.segs.size() * sizeof(AppendSegment));
+    if (!plan.cow.empty()) std::memcpy(stg + seg_bytes, plan.cow.data(), plan.cow.size() * sizeof(CowPair));
+    size_t upload = plan.cow.empty() ? plan.segs.size() * sizeof(AppendSegment)
+                                     : seg_bytes + plan.cow.size() * sizeof(CowPair);
+    st = staging_upload(c, c->cfg.dev_scratch, upload, s);
+    if (st != KVC_OK) return st;
+  }
   if (!plan.cow.empty()) {
     hipError_t e = kvc::launch_copy_blocks(pool, reinterpret_cast<const CowPair*>(scratch + seg_bytes),
                                            (int32_t)plan.cow.size(), s);
     if (e != hipSuccess) return fail(KVC_E_HIP, "copy-on-write launch: %s", hipGetErrorString(e));
   }
-  hipError_t e = kvc::launch_append(pool, reinterpret_cast<const AppendSegment*>(scratch), (int32_t)plan.segs.size(),
-                                    k_new, v_new, in_dtype, total, s);
+  hipError_t e;
+  if (inline_plan) {
+    kvc::InlineSegments segs;
+    std::memcpy(segs.s, plan.segs.data(), plan.segs.size() * sizeof(AppendSegment));
+    e = kvc::launch_append(pool, nullptr, &segs, (int32_t)plan.segs.size(), k_new, v_new, in_dtype, total, s);
+  } else {
+    e = kvc::launch_append(pool, reinterpret_cast<const AppendSegment*>(scratch), nullptr, (int32_t)plan.segs.size(),
+                           k_new, v_new, in_dtype, total, s);
+  }
   if (e != hipSuccess) return fail(KVC_E_HIP, "append launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -580,7 +598,7 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
   for (int32_t k = 1; k <= 2; ++k) {
     if (kernel != 0 && kernel != k) continue;
     kvc::DecodePlan p;
-    if (!plan_decode(batch, num_kv_heads, max_context_len, k, opts, &p)) return 0;
+    if (!plan_decode(batch, num_kv_heads, max_context_len, k, -1, opts, &p)) return 0;
     need = std::max(need, workspace_bytes_for(batch, num_heads, head_dim, p));
   }
   return need;
@@ -618,7 +636,7 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   if (kernel != 1 && kernel != 2) return fail(KVC_E_INVALID, "unknown kernel %d", kernel);
   kvc::DecodePlan plan;
   if (!plan_decode(batch, num_kv_heads, std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size),
-                   kernel, opts, &plan))
+                   kernel, (int)kv, opts, &plan))
     return fail(KVC_E_INVALID, "partition_tokens must be a multiple of 16 and at most 1024, work_items >= 0");
   size_t need = workspace_bytes_for(batch, num_heads, head_dim, plan);
   if (need > 0 && (!workspace || workspace_bytes < need))

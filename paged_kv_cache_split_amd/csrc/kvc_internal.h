@@ -63,18 +63,57 @@ struct DecodePlan {
   int32_t work_items;
 };
 
-// Default number of waves per decode launch of the MFMA kernel (8 per CU on
-// 256 CUs).  Fixed, so results do not depend on the device's CU count.
-constexpr int32_t kDefaultWaves = 2048;
+// Default number of waves per launch of the MFMA kernel: one per SIMD of a
+// 256-CU part for 16-bit caches (HBM-bound, one wave streams best), two for
+// fp8 caches (more VALU work per byte, which a second wave hides).  Fixed, so
+// results do not depend on the device's CU count.
+constexpr int32_t kDefaultWaves16 = 1024;
+constexpr int32_t kDefaultWavesFp8 = 2048;
+inline int32_t default_waves(kvc_dtype kv) { return kv == KVC_FP8_E4M3 ? kDefaultWavesFp8 : kDefaultWaves16; }
+
+// Byte offsets inside the decode workspace.  FMA kernel: partial rows
+// [B][Hq][num_partitions] (acc, m, l).  MFMA kernel: partial rows
+// [Hq][B + work_items] (acc, m, l), then per sequence {first wave, waves}.
+struct WorkspaceLayout {
+  size_t acc, m, l, seginfo, bytes;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WorkspaceLayout workspace_layout(int32_t kernel, int32_t num_partitions, int32_t work_items, int32_t batch,
+                                        int32_t num_heads, int32_t head_dim) {
+  WorkspaceLayout w{0, 0, 0, 0, 0};
+  size_t rows;
+  if (kernel == 1) {
+    if (num_partitions <= 1) return w;
+    rows = (size_t)batch * num_heads * num_partitions;
+  } else {
+    rows = (size_t)num_heads * ((size_t)batch + work_items);
+  }
+  w.m = align256(rows * head_dim * sizeof(float));
+  w.l = w.m + align256(rows * sizeof(float));
+  w.seginfo = w.l + align256(rows * sizeof(float));
+  w.bytes = w.seginfo + (kernel == 2 ? align256((size_t)batch * 2 * sizeof(int32_t)) : 0);
+  return w;
+}
 constexpr int32_t kMaxBatch = 8192;  // the per-sequence block scan lives in LDS
 
 // Launchers (kvc_kernels.hip).  They only launch; arguments are validated by
 // the caller.  Return hipSuccess or the launch error.
 hipError_t launch_copy_blocks(const PoolDesc& pool, const CowPair* pairs_dev, int32_t num_pairs,
                               hipStream_t stream);
-hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, int32_t num_segments,
-                         const void* k_new, const void* v_new, kvc_dtype in_dtype, int64_t total_rows,
-                         hipStream_t stream);
+// Appends of at most kInlineSegments segments (a decode step over up to that
+// many sequences) pass their plan as a kernel argument: no upload.
+constexpr int32_t kInlineSegments = 192;
+struct InlineSegments {
+  AppendSegment s[kInlineSegments];
+};
+
+// segs_dev (device) or segs_inline (host, copied into the kernel arguments):
+// exactly one is non-NULL.
+hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, const InlineSegments* segs_inline,
+                         int32_t num_segments, const void* k_new, const void* v_new, kvc_dtype in_dtype,
+                         int64_t total_rows, hipStream_t stream);
 hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q,
                          kvc_dtype q_dtype, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* context_lens, int32_t max_context_len, int32_t batch, int32_t num_heads,

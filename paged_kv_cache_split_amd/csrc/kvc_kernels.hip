@@ -43,6 +43,14 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBS = 16;                       // tokens per block (device work)
+
+// Blocks each decode wave keeps in flight (16-bit and fp8 caches).
+#ifndef KVC_PREFETCH_16
+#define KVC_PREFETCH_16 3
+#endif
+#ifndef KVC_PREFETCH_FP8
+#define KVC_PREFETCH_FP8 3
+#endif
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -175,15 +183,26 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(PoolDesc p, const CowP
   }
 }
 
+// Where an append kernel finds its write plan: device memory, or its own
+// kernel arguments for small plans.
+struct SegFromDevice {
+  const AppendSegment* p;
+  __device__ __forceinline__ AppendSegment get(int i) const { return p[i]; }
+};
+struct SegFromArgs {
+  InlineSegments v;
+  __device__ __forceinline__ AppendSegment get(int i) const { return v.s[i]; }
+};
+
 // ---------------------------------------------------------------------------
 // Append (reshape-and-cache) for f32 / f16 / bf16 caches: a plain copy of
 // every new row into its slot.  grid (num_segments, num_kv_heads, num_layers),
 // 64 threads.
 // ---------------------------------------------------------------------------
-template <int EBYTES>
-__global__ __launch_bounds__(64) void append_copy_kernel(PoolDesc p, const AppendSegment* segs, const char* k_new,
+template <int EBYTES, typename SEGS>
+__global__ __launch_bounds__(64) void append_copy_kernel(PoolDesc p, SEGS segs, const char* k_new,
                                                          const char* v_new, int64_t total_rows) {
-  const AppendSegment sg = segs[blockIdx.x];
+  const AppendSegment sg = segs.get(blockIdx.x);
   const int h = blockIdx.y, layer = blockIdx.z;
   const int D = p.head_dim, H = p.num_kv_heads;
   constexpr int X = 16 / EBYTES;
@@ -217,10 +236,10 @@ __global__ __launch_bounds__(64) void append_copy_kernel(PoolDesc p, const Appen
 // scale grows; encode the new rows with s_new.  grid (num_segments,
 // num_kv_heads, 2 * num_layers), 64 threads (one wave).
 // ---------------------------------------------------------------------------
-template <kvc_dtype IN>
-__global__ __launch_bounds__(64) void append_fp8_kernel(PoolDesc p, const AppendSegment* segs, const void* k_new,
+template <kvc_dtype IN, typename SEGS>
+__global__ __launch_bounds__(64) void append_fp8_kernel(PoolDesc p, SEGS segs, const void* k_new,
                                                         const void* v_new, int64_t total_rows) {
-  const AppendSegment sg = segs[blockIdx.x];
+  const AppendSegment sg = segs.get(blockIdx.x);
   const int h = blockIdx.y;
   const int layer = blockIdx.z >> 1;
   const bool is_v = blockIdx.z & 1;
@@ -272,6 +291,7 @@ struct DecodeArgs {
   float* ws_acc;   // rows x D
   float* ws_m;     // rows
   float* ws_l;     // rows
+  int* ws_seginfo; // MFMA kernel: per sequence {first wave, number of waves}
   const char* k;   // layer base of the K pool
   const char* v;   // layer base of the V pool
   const float* k_scale;  // layer base (fp8)
@@ -616,6 +636,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const int first = x - sb;                   // first local block of this segment
     const int count = seg_end - x;              // blocks in this segment
     const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
+    if (first == 0 && g == 0 && lane == 0) {
+      // the wave holding a sequence's first block records which waves hold it
+      const int w_last = (int)(((int64_t)(eb - 1) * W) / total);
+      a.ws_seginfo[2 * b] = w;
+      a.ws_seginfo[2 * b + 1] = w_last - w + 1;
+    }
 
     // Query operand: for step kk the lane holds 8 dims of head nn, the same
     // dims its K operand holds for token nn.
@@ -798,62 +824,44 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the MFMA kernel's partials for one (query head, sequence): the
-// waves (sb * W) / T .. ((eb - 1) * W) / T (W = min(work_items, T), so each
-// owns at least one block) each left a triple in slot b + w.
+// Merge of the MFMA kernel's partials: one wave per (KV head, sequence)
+// combines, for each of the group's query heads, the triples the sequence's
+// waves w_first .. w_first + np - 1 left in slots b + w.  Lanes are laid out
+// as in the decode (head = lane % 16, dims 16*dd + 4*(lane / 16) + e).
 template <kvc_dtype QT, int D>
-__global__ __launch_bounds__(256) void merge_segments_kernel(DecodeArgs a) {
-  extern __shared__ int seq_start[];   // [batch + 1]
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  if (tid < 64) scan_block_counts(a, seq_start, tid);
-  __syncthreads();
-  const int64_t T = seq_start[a.batch];
-  const int64_t W = a.work_items < T ? a.work_items : T;   // as in the decode kernel
-  const int sb = seq_start[b], eb = seq_start[b + 1];
-  if (eb <= sb) return;
-  const int w_first = (int)(((int64_t)sb * W) / T);
-  const int w_last = (int)(((int64_t)(eb - 1) * W) / T);
-  if (w_first == w_last) return;      // one wave held the whole sequence
-  const int np = w_last - w_first + 1;
-  const int64_t base = (int64_t)h * (a.batch + a.work_items) + b + w_first;
-  constexpr int TPR = D / 4;          // threads per partial row
-  constexpr int ROWS = 256 / TPR;     // rows in flight
-  __shared__ float red[256];
-  __shared__ floatx4 part_acc[ROWS][TPR];
-  __shared__ float part_l[ROWS];
-  float mx = kNegInf;
-  for (int p = tid; p < np; p += 256) mx = fmaxf(mx, a.ws_m[base + p]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  const int prow = tid / TPR, c = tid % TPR;
-  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+__global__ __launch_bounds__(64) void merge_segments_kernel(DecodeArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int nn = lane & 15, r = lane >> 4;
+  constexpr int NDD = D / 16;
+  if (attend_len(a.context_lens, b, a.max_ctx, a.max_blocks) <= 0) return;
+  const int w_first = a.ws_seginfo[2 * b];
+  int np = a.ws_seginfo[2 * b + 1];
+  if (np <= 1 || nn >= a.group) return;        // one wave held the whole sequence
+  if (w_first < 0 || w_first >= a.work_items) return;
+  if (np > a.work_items - w_first) np = a.work_items - w_first;
+  const int h = g * a.group + nn;
+  const int64_t row0 = (int64_t)h * (a.batch + a.work_items) + b + w_first;
+  float M = kNegInf;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[row0 + p]);
+  floatx4 tot[NDD];
+#pragma unroll
+  for (int dd = 0; dd < NDD; ++dd) tot[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
   float L = 0.0f;
-  for (int p = prow; p < np; p += ROWS) {
-    const float wgt = __builtin_amdgcn_exp2f(a.ws_m[base + p] - M);
-    acc += *reinterpret_cast<const floatx4*>(a.ws_acc + (base + p) * D + 4 * c) * wgt;
-    L += wgt * a.ws_l[base + p];
+#pragma unroll 2
+  for (int p = 0; p < np; ++p) {
+    const float wgt = __builtin_amdgcn_exp2f(a.ws_m[row0 + p] - M);
+    L += wgt * a.ws_l[row0 + p];
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd)
+      tot[dd] += *reinterpret_cast<const floatx4*>(a.ws_acc + (row0 + p) * D + 16 * dd + 4 * r) * wgt;
   }
-  part_acc[prow][c] = acc;
-  if (c == 0) part_l[prow] = L;
-  __syncthreads();
-  if (tid < TPR) {
-    floatx4 tot = part_acc[0][tid];
-    float lt = part_l[0];
+  const float inv = 1.0f / L;
 #pragma unroll
-    for (int rr = 1; rr < ROWS; ++rr) {
-      tot += part_acc[rr][tid];
-      lt += part_l[rr];
-    }
-    const float inv = 1.0f / lt;
-    const int64_t o = ((int64_t)b * a.num_heads + h) * D + 4 * tid;
+  for (int dd = 0; dd < NDD; ++dd) {
+    const int64_t o = ((int64_t)b * a.num_heads + h) * D + 16 * dd + 4 * r;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, tot[e] * inv);
+    for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, tot[dd][e] * inv);
   }
 }
 
@@ -952,15 +960,15 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     return e;
   }
   if constexpr (KV != KVC_F32) {
-    constexpr int PF = (KV == KVC_FP8_E4M3) ? 5 : 3;  // blocks in flight per wave
+    constexpr int PF = (KV == KVC_FP8_E4M3) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_16;  // blocks in flight per wave
     dim3 grid(a.work_items, a.num_kv_heads);
     if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64, PF>), grid, dim3(64), scan_lds, s, a);
     else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128, PF>), grid, dim3(64), scan_lds, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
-    dim3 mgrid(a.num_heads, a.batch);
-    if (D == 64) hipLaunchKernelGGL((merge_segments_kernel<QT, 64>), mgrid, dim3(256), scan_lds, s, a);
-    else hipLaunchKernelGGL((merge_segments_kernel<QT, 128>), mgrid, dim3(256), scan_lds, s, a);
+    dim3 mgrid(a.num_kv_heads, a.batch);
+    if (D == 64) hipLaunchKernelGGL((merge_segments_kernel<QT, 64>), mgrid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((merge_segments_kernel<QT, 128>), mgrid, dim3(64), 0, s, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
@@ -975,33 +983,45 @@ hipError_t launch_copy_blocks(const PoolDesc& pool, const CowPair* pairs_dev, in
   return hipGetLastError();
 }
 
-hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, int32_t num_segments, const void* k_new,
-                         const void* v_new, kvc_dtype in_dtype, int64_t total_rows, hipStream_t stream) {
-  if (num_segments <= 0) return hipSuccess;
+template <typename SEGS>
+hipError_t launch_append_from(const PoolDesc& pool, const SEGS& segs, int32_t num_segments, const void* k_new,
+                              const void* v_new, kvc_dtype in_dtype, int64_t total_rows, hipStream_t stream) {
   const char* kn = static_cast<const char*>(k_new);
   const char* vn = static_cast<const char*>(v_new);
+  const dim3 grid(num_segments, pool.num_kv_heads, pool.num_layers);
   switch (pool.dtype) {
     case KVC_F32:
-      hipLaunchKernelGGL(append_copy_kernel<4>, dim3(num_segments, pool.num_kv_heads, pool.num_layers), dim3(64), 0,
-                         stream, pool, segs_dev, kn, vn, total_rows);
+      hipLaunchKernelGGL((append_copy_kernel<4, SEGS>), grid, dim3(64), 0, stream, pool, segs, kn, vn, total_rows);
       break;
     case KVC_F16:
     case KVC_BF16:
-      hipLaunchKernelGGL(append_copy_kernel<2>, dim3(num_segments, pool.num_kv_heads, pool.num_layers), dim3(64), 0,
-                         stream, pool, segs_dev, kn, vn, total_rows);
+      hipLaunchKernelGGL((append_copy_kernel<2, SEGS>), grid, dim3(64), 0, stream, pool, segs, kn, vn, total_rows);
       break;
     case KVC_FP8_E4M3: {
-      dim3 grid(num_segments, pool.num_kv_heads, 2 * pool.num_layers);
+      const dim3 g8(num_segments, pool.num_kv_heads, 2 * pool.num_layers);
       if (in_dtype == KVC_F32)
-        hipLaunchKernelGGL(append_fp8_kernel<KVC_F32>, grid, dim3(64), 0, stream, pool, segs_dev, k_new, v_new, total_rows);
+        hipLaunchKernelGGL((append_fp8_kernel<KVC_F32, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new, total_rows);
       else if (in_dtype == KVC_F16)
-        hipLaunchKernelGGL(append_fp8_kernel<KVC_F16>, grid, dim3(64), 0, stream, pool, segs_dev, k_new, v_new, total_rows);
+        hipLaunchKernelGGL((append_fp8_kernel<KVC_F16, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new, total_rows);
       else
-        hipLaunchKernelGGL(append_fp8_kernel<KVC_BF16>, grid, dim3(64), 0, stream, pool, segs_dev, k_new, v_new, total_rows);
+        hipLaunchKernelGGL((append_fp8_kernel<KVC_BF16, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new, total_rows);
       break;
     }
   }
   return hipGetLastError();
+}
+
+hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, const InlineSegments* segs_inline,
+                         int32_t num_segments, const void* k_new, const void* v_new, kvc_dtype in_dtype,
+                         int64_t total_rows, hipStream_t stream) {
+  if (num_segments <= 0) return hipSuccess;
+  if (segs_inline) {
+    if (num_segments > kInlineSegments) return hipErrorInvalidValue;
+    SegFromArgs segs;
+    segs.v = *segs_inline;
+    return launch_append_from(pool, segs, num_segments, k_new, v_new, in_dtype, total_rows, stream);
+  }
+  return launch_append_from(pool, SegFromDevice{segs_dev}, num_segments, k_new, v_new, in_dtype, total_rows, stream);
 }
 
 hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q, kvc_dtype q_dtype,
@@ -1032,17 +1052,13 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   a.work_items = plan.work_items;
   a.qk_scale = scale * kLog2e;
   const bool merge = plan.kernel == 2 || plan.num_partitions > 1;
-  if (merge) {
-    const size_t rows = plan.kernel == 1 ? (size_t)batch * num_heads * plan.num_partitions
-                                         : (size_t)num_heads * ((size_t)batch + plan.work_items);
-    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    char* w = static_cast<char*>(workspace);
-    a.ws_acc = reinterpret_cast<float*>(w);
-    a.ws_m = reinterpret_cast<float*>(w + al(rows * pool.head_dim * sizeof(float)));
-    a.ws_l = reinterpret_cast<float*>(w + al(rows * pool.head_dim * sizeof(float)) + al(rows * sizeof(float)));
-  } else {
-    a.ws_acc = a.ws_m = a.ws_l = nullptr;
-  }
+  const WorkspaceLayout wl = workspace_layout(plan.kernel, plan.num_partitions, plan.work_items, batch, num_heads,
+                                              pool.head_dim);
+  char* w = static_cast<char*>(workspace);
+  a.ws_acc = wl.bytes ? reinterpret_cast<float*>(w + wl.acc) : nullptr;
+  a.ws_m = wl.bytes ? reinterpret_cast<float*>(w + wl.m) : nullptr;
+  a.ws_l = wl.bytes ? reinterpret_cast<float*>(w + wl.l) : nullptr;
+  a.ws_seginfo = (wl.bytes && plan.kernel == 2) ? reinterpret_cast<int*>(w + wl.seginfo) : nullptr;
   const int D = pool.head_dim;
   switch (pool.dtype) {
     case KVC_F32:
