@@ -59,6 +59,30 @@ def algorithmic_bytes(wl):
                 split_kernel=kv + scales + q + tables)
 
 
+def profiled_traffic(config_id):
+    """HBM bytes per split-kernel launch from a committed rocprofv3 summary
+    (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy kernel's counts),
+    or None when no summary was taken on the current kernel source."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "paged_kv_cache_split_amd", "csrc", "kvc_kernels.hip")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    for fn in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        text = open(fn).read()
+        for line in text.splitlines():
+            if line.startswith("{") and "traffic_bytes_per_launch" in line:
+                try:
+                    rec = json.loads(line)
+                except ValueError:
+                    continue
+                if rec.get("config_id") == config_id and rec.get("kernel_source_sha256") == sha:
+                    return rec["traffic_bytes_per_launch"], os.path.relpath(fn, ROOT)
+    return None
+
+
 def cpu_baseline(wl, values, budget_s):
     """Time the fp64 oracle on a sample of the same workload (sequences in order
     until the budget is spent); report GB/s of KV it processed and the cores it
@@ -165,6 +189,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ab = algorithmic_bytes(wl)
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
+    prof = profiled_traffic(args.config) if args.kernel in (0, 2) and not args.work_items else None
+    traffic = prof[0] if prof else None
     achieved = ab["split_kernel"] / (split_avg_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -188,10 +214,11 @@ def main():
                    "work_items": args.work_items or "auto",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "decode split-K kernel", "avg_launch_us": round(split_avg_ms * 1e3, 2),
                      "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
-                     "algorithmic_bytes_per_launch": ab["split_kernel"]},
+                     "algorithmic_bytes_per_launch": ab["split_kernel"],
+                     "traffic_source": prof[1] if prof else None},
     }
     if args.calibrate:
         n = 1 << 31

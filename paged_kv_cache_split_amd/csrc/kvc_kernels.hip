@@ -824,45 +824,43 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the MFMA kernel's partials: one wave per (KV head, sequence)
-// combines, for each of the group's query heads, the triples the sequence's
-// waves w_first .. w_first + np - 1 left in slots b + w.  Lanes are laid out
-// as in the decode (head = lane % 16, dims 16*dd + 4*(lane / 16) + e).
+// Merge of the MFMA kernel's partials: one work-group per (KV head,
+// sequence), one thread per (query head of the group, 4 output dims).  The
+// triples of waves w_first .. w_first + np - 1 (slots b + w) are folded in a
+// single pass with the online-softmax recurrence, so every load can be
+// issued ahead of its use.
 template <kvc_dtype QT, int D>
-__global__ __launch_bounds__(64) void merge_segments_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int nn = lane & 15, r = lane >> 4;
-  constexpr int NDD = D / 16;
+  const int t = threadIdx.x;
+  constexpr int COLS = D / 4;
+  const int hh = t / COLS, c = t % COLS;
+  if (hh >= a.group) return;
   if (attend_len(a.context_lens, b, a.max_ctx, a.max_blocks) <= 0) return;
   const int w_first = a.ws_seginfo[2 * b];
   int np = a.ws_seginfo[2 * b + 1];
-  if (np <= 1 || nn >= a.group) return;        // one wave held the whole sequence
+  if (np <= 1) return;                         // one wave held the whole sequence
   if (w_first < 0 || w_first >= a.work_items) return;
   if (np > a.work_items - w_first) np = a.work_items - w_first;
-  const int h = g * a.group + nn;
+  const int h = g * a.group + hh;
   const int64_t row0 = (int64_t)h * (a.batch + a.work_items) + b + w_first;
-  float M = kNegInf;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[row0 + p]);
-  floatx4 tot[NDD];
-#pragma unroll
-  for (int dd = 0; dd < NDD; ++dd) tot[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.0f;
-#pragma unroll 2
+  float M = kNegInf, L = 0.0f;
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int p = 0; p < np; ++p) {
-    const float wgt = __builtin_amdgcn_exp2f(a.ws_m[row0 + p] - M);
-    L += wgt * a.ws_l[row0 + p];
-#pragma unroll
-    for (int dd = 0; dd < NDD; ++dd)
-      tot[dd] += *reinterpret_cast<const floatx4*>(a.ws_acc + (row0 + p) * D + 16 * dd + 4 * r) * wgt;
+    const float m = a.ws_m[row0 + p];
+    const float l = a.ws_l[row0 + p];
+    const floatx4 v = *reinterpret_cast<const floatx4*>(a.ws_acc + (row0 + p) * D + 4 * c);
+    const float Mn = fmaxf(M, m);
+    const float sa = __builtin_amdgcn_exp2f(M - Mn), sb = __builtin_amdgcn_exp2f(m - Mn);
+    acc = acc * sa + v * sb;
+    L = L * sa + l * sb;
+    M = Mn;
   }
   const float inv = 1.0f / L;
+  const int64_t o = ((int64_t)b * a.num_heads + h) * D + 4 * c;
 #pragma unroll
-  for (int dd = 0; dd < NDD; ++dd) {
-    const int64_t o = ((int64_t)b * a.num_heads + h) * D + 16 * dd + 4 * r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, tot[dd][e] * inv);
-  }
+  for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, acc[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -967,8 +965,9 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
     dim3 mgrid(a.num_kv_heads, a.batch);
-    if (D == 64) hipLaunchKernelGGL((merge_segments_kernel<QT, 64>), mgrid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((merge_segments_kernel<QT, 128>), mgrid, dim3(64), 0, s, a);
+    const int threads = ((a.group * (D / 4) + 63) / 64) * 64;   // <= 16 heads * 32 columns = 512
+    if (D == 64) hipLaunchKernelGGL((merge_segments_kernel<QT, 64>), mgrid, dim3(threads), 0, s, a);
+    else hipLaunchKernelGGL((merge_segments_kernel<QT, 128>), mgrid, dim3(threads), 0, s, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

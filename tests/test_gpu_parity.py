@@ -182,3 +182,27 @@ def test_stream_copy_calibration_kernel():
     stream_copy(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+def test_multi_layer_pool_and_cow(kv):
+    # three layers share one block id space: appends write every layer, a
+    # copy-on-write copies every layer (and fp8 scales), decode reads one layer
+    wl = custom_workload(3, 8, 2, 64, kv, [21 + 9, 21 + 2, 40], seed=6, shared_prefix=21, name="layers")
+    wl.num_layers = 3
+    wl.num_blocks += 4
+    wl.free_order = np.random.default_rng(2).permutation(wl.num_blocks).astype(np.int32)
+    values = make_values(wl, "cpu")
+    st = oracle_run(wl, values)
+    cache = gpu_setup(wl, values)
+    out0, bt, cl = gpu_step(cache, wl, values, partition_tokens=32, work_items=3)
+    torch.cuda.synchronize()
+    assert cache.stats()["cow_copies"] == st.tables.cow_copies >= 2
+    _check_append(cache, st, wl, bt, cl)
+    for layer in range(3):
+        ref = oracle_decode(st, wl, values, layer=layer)
+        for kernel in _kernels_for(wl):
+            q = values["q"].to("cuda").contiguous()
+            o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, layer=layer, kernel=kernel,
+                             partition_tokens=32, work_items=3)
+            check_close(to_f64(o), ref, *TOL[kv], f"{kv} layer {layer} kernel {kernel}")
