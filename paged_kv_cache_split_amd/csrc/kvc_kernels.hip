@@ -527,6 +527,7 @@ struct KvBlock {
   static constexpr int NV = D / 16;                                   // V^T loads per lane
   u32x4 k[NK];
   typename std::conditional<KV == KVC_FP8_E4M3, uint32_t, u32x2>::type v[NV];
+  float ks, vs;  // fp8: the (block, head) scales, fetched with the tile
 };
 
 // K/V tiles are read once per step: non-temporal loads (streaming cache
@@ -677,16 +678,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       const int k = j - cbase;
       return k < 64 ? __builtin_amdgcn_readlane(ids0, k) : __builtin_amdgcn_readlane(ids1, k - 64);
     };
-    auto tile_off = [&](int j) -> int64_t { return (int64_t)phys_of(j) * block_stride + head_off; };
 
     auto process = [&](const KvBlock<KV, D>& cur, int i) {
       floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
       float qk = a.qk_scale;
       float vsc = 1.0f;
       if constexpr (KV == KVC_FP8_E4M3) {
-        const int phys = phys_of(i);
-        qk *= a.k_scale[(int64_t)phys * a.num_kv_heads + g];
-        vsc = a.v_scale[(int64_t)phys * a.num_kv_heads + g];
+        qk *= cur.ks;
+        vsc = cur.vs;
 #pragma unroll
         for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
           u32x4 lo, hi;
@@ -767,11 +766,17 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     // i is consumed.  The ring index is a compile-time constant after
     // unrolling.
     KvBlock<KV, D> buf[PF + 1];
+    auto fetch = [&](KvBlock<KV, D>& dst, int j) {
+      const int ph = phys_of(j);
+      const int64_t o = (int64_t)ph * block_stride + head_off;
+      load_block<KV, D>(dst, a.k + o, a.v + o, nn, r);
+      if constexpr (KV == KVC_FP8_E4M3) {
+        dst.ks = a.k_scale[(int64_t)ph * a.num_kv_heads + g];
+        dst.vs = a.v_scale[(int64_t)ph * a.num_kv_heads + g];
+      }
+    };
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int64_t o = tile_off(j);
-      load_block<KV, D>(buf[j], a.k + o, a.v + o, nn, r);
-    }
+    for (int j = 0; j < PF; ++j) fetch(buf[j], j);
     for (int i0 = 0; i0 < count; i0 += PF + 1) {
 #pragma unroll
       for (int j = 0; j <= PF; ++j) {
@@ -782,8 +787,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
           ids0 = ids1;
           ids1 = load_ids(cbase + 64);
         }
-        const int64_t o = tile_off(i + PF);
-        load_block<KV, D>(buf[(j + PF) % (PF + 1)], a.k + o, a.v + o, nn, r);
+        fetch(buf[(j + PF) % (PF + 1)], i + PF);
         process(buf[j], i);
       }
     }
