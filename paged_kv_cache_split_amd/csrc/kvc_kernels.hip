@@ -41,6 +41,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+// Pointers into the constant address space: the compiler may treat memory read
+// through them as unchanging for the kernel's lifetime, so a load from a
+// wave-uniform address becomes a scalar load (counted on lgkmcnt, apart from
+// the vector loads).  Used only for block-table rows and fp8 scales, which no
+// decode kernel writes.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_kptr;
+typedef const float __attribute__((address_space(4)))* const_f32_kptr;
 
 constexpr int kBS = 16;                       // tokens per block (device work)
 
@@ -602,7 +609,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   extern __shared__ int seq_start[];   // [batch + 1]
   const int w = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x;
-  const int total = scan_block_counts(a, seq_start, lane);
+  const int total = __builtin_amdgcn_readfirstlane(scan_block_counts(a, seq_start, lane));
   __syncthreads();
   // never more waves than blocks, so every wave that runs owns >= 1 block
   const int W = a.work_items < total ? a.work_items : total;
@@ -628,15 +635,19 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       if (seq_start[mid] <= x0) lo = mid;
       else hi = mid - 1;
     }
-    b = lo;
+    b = __builtin_amdgcn_readfirstlane(lo);
   }
+  // Everything below that indexes memory is wave-uniform (scalar registers),
+  // so block ids and fp8 scales come through scalar loads, which are counted
+  // apart from the vector loads of the tiles and never drain the prefetch ring.
   for (int x = x0; x < x1; ++b) {
-    const int sb = seq_start[b], eb = seq_start[b + 1];
+    const int sb = __builtin_amdgcn_readfirstlane(seq_start[b]);
+    const int eb = __builtin_amdgcn_readfirstlane(seq_start[b + 1]);
     if (eb <= x) continue;                      // empty sequence
     const int seg_end = eb < x1 ? eb : x1;
     const int first = x - sb;                   // first local block of this segment
     const int count = seg_end - x;              // blocks in this segment
-    const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
+    const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
     if (first == 0 && g == 0 && lane == 0) {
       // the wave holding a sequence's first block records which waves hold it
       const int w_last = (int)(((int64_t)(eb - 1) * W) / total);
@@ -662,21 +673,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m = kNegInf, l = 0.0f;
 
-    // Block ids of the segment, 64 per register: ids0 holds local blocks
-    // [cbase, cbase + 64), ids1 the next 64.
-    const int32_t* row = a.block_table + (int64_t)b * a.max_blocks + first;
-    auto load_ids = [&](int from) -> int {
-      return lane + from < count ? clamp_block(row[lane + from], a.num_blocks) : 0;
-    };
-    int cbase = 0;
-    int ids0 = load_ids(0);
-    int ids1 = count > 64 ? load_ids(64) : 0;
-    // physical block of local block j (j past the end re-reads the last
-    // block, an L2 hit, so every prefetch is unconditional)
+    // Physical block of local block j of the segment (scalar load; indices
+    // past the end re-read the last block, an L2 hit, so every prefetch is
+    // unconditional).
+    const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + first);
     auto phys_of = [&](int j) -> int {
       j = j < count ? j : count - 1;
-      const int k = j - cbase;
-      return k < 64 ? __builtin_amdgcn_readlane(ids0, k) : __builtin_amdgcn_readlane(ids1, k - 64);
+      return clamp_block(row[j], a.num_blocks);
     };
 
     auto process = [&](const KvBlock<KV, D>& cur, int i) {
@@ -766,30 +769,40 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     // i is consumed.  The ring index is a compile-time constant after
     // unrolling.
     KvBlock<KV, D> buf[PF + 1];
-    auto fetch = [&](KvBlock<KV, D>& dst, int j) {
-      const int ph = phys_of(j);
+    auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
       const int64_t o = (int64_t)ph * block_stride + head_off;
       load_block<KV, D>(dst, a.k + o, a.v + o, nn, r);
       if constexpr (KV == KVC_FP8_E4M3) {
-        dst.ks = a.k_scale[(int64_t)ph * a.num_kv_heads + g];
-        dst.vs = a.v_scale[(int64_t)ph * a.num_kv_heads + g];
+        dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
+        dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
       }
     };
 #pragma unroll
-    for (int j = 0; j < PF; ++j) fetch(buf[j], j);
-    for (int i0 = 0; i0 < count; i0 += PF + 1) {
+    for (int j = 0; j < PF; ++j) fetch(buf[j], phys_of(j));
+    int ph_next = phys_of(PF);                  // id of the next block to prefetch, one step ahead
+    // Whole turns of the ring first, with no exit inside a turn: an exit that
+    // led back to the loop head would leave a load in flight there and force
+    // a full wait for it at the head of every turn.
+    int i0 = 0;
+    for (; i0 + PF + 1 <= count; i0 += PF + 1) {
 #pragma unroll
       for (int j = 0; j <= PF; ++j) {
         const int i = i0 + j;
-        if (i >= count) break;
-        if (i + PF >= cbase + 128) {            // prefetch index leaves ids0/ids1: slide by 64
-          cbase += 64;
-          ids0 = ids1;
-          ids1 = load_ids(cbase + 64);
-        }
-        fetch(buf[(j + PF) % (PF + 1)], i + PF);
+        const int ph = ph_next;
+        ph_next = phys_of(i + PF + 1);
+        fetch(buf[(j + PF) % (PF + 1)], ph);
         process(buf[j], i);
       }
+    }
+    // the last, partial turn
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int i = i0 + j;
+      if (i >= count) break;
+      const int ph = ph_next;
+      ph_next = phys_of(i + PF + 1);
+      fetch(buf[(j + PF) % (PF + 1)], ph);
+      process(buf[j], i);
     }
     // l over the head's four lane groups
     l += __shfl_xor(l, 16);
