@@ -203,16 +203,26 @@ kvc_status kvc_export_tables(kvc_cache* cache, int32_t batch, const int64_t* seq
 /* Decode options; pass NULL for the defaults. */
 /* Work split of the decode.
  *  MFMA kernel: per KV head, the blocks of all sequences (in batch order) form
- *  one list that is cut into `work_items` equal runs, one wave each; a wave
- *  writes one partial (max, sum, acc) per sequence it touches, or the final
- *  output when it holds a whole sequence, and a merge kernel combines the
- *  partials.  Results are bit-for-bit reproducible for a given work_items.
+ *  one list that is cut into `work_items` equal runs, one wave each.  With
+ *  pool_pieces > 0, the last 1/2^pool_shift of every run is further cut into
+ *  pool_pieces pieces that the waves of that head take at run time, first come
+ *  first served, so waves that progress faster take more of them (each piece
+ *  restarts the wave's prefetch, which costs about what the balance gains on
+ *  MI355X, hence off by default).  Each chunk (a run's main part or a
+ *  piece) yields one partial (max, sum, acc) per sequence it touches, or the
+ *  final output when it holds a whole sequence, and a merge kernel combines
+ *  the partials in list order.  Chunk bounds depend only on the lengths and
+ *  these options, not on which wave takes a piece, so results are bit-for-bit
+ *  reproducible for given options.
  *  FMA kernel: every sequence is cut into partitions of partition_tokens. */
 typedef struct kvc_decode_opts {
   int32_t partition_tokens; /* FMA kernel: tokens per partition (multiple of 16, <= 1024); 0 = chosen from the shape */
   int32_t kernel;           /* 0 = auto, 1 = fp32 FMA (VALU) kernel, 2 = MFMA kernel (16-bit and fp8 KV) */
-  int32_t work_items;       /* MFMA kernel: waves per KV head; 0 = max(1, W / num_kv_heads) with
-                               W = 1024 for 16-bit caches and 2048 for fp8 caches */
+  int32_t work_items;       /* MFMA kernel: waves per KV head; 0 = max(1, 1024 / num_kv_heads) */
+  int32_t pool_pieces;      /* MFMA kernel: pieces per run handed out at run time, <= 64; <= 0 = none
+                               (static split, the default); unused when a run's pool would hold fewer
+                               blocks than pieces */
+  int32_t pool_shift;       /* MFMA kernel: the pool is the last 1/2^pool_shift of each run, 1..6; 0 = 3 */
   kvc_event_t split_start;  /* optional events recorded on `stream` around the split-K kernel */
   kvc_event_t split_end;
 } kvc_decode_opts;

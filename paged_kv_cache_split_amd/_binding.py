@@ -54,6 +54,7 @@ class KvcStats(ctypes.Structure):
 
 class KvcDecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("work_items", ctypes.c_int32),
+                ("pool_pieces", ctypes.c_int32), ("pool_shift", ctypes.c_int32),
                 ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p)]
 
 
@@ -148,8 +149,8 @@ def scratch_bytes(max_batch, max_tokens) -> int:
 
 
 def decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len, partition_tokens=0,
-                           kernel=0, work_items=0) -> int:
-    opts = KvcDecodeOpts(partition_tokens, kernel, work_items, None, None)
+                           kernel=0, work_items=0, pool_pieces=0, pool_shift=0) -> int:
+    opts = KvcDecodeOpts(partition_tokens, kernel, work_items, pool_pieces, pool_shift, None, None)
     return _lib.kvc_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len,
                                            ctypes.byref(opts))
 
@@ -293,13 +294,15 @@ class KVCache:
         return block_table, context_lens
 
     def decode(self, q, block_table, context_lens, max_context_len, scale, layer=0, out=None, workspace=None,
-               partition_tokens=0, kernel=0, work_items=0, split_events=None, stream=None):
+               partition_tokens=0, kernel=0, work_items=0, pool_pieces=0, pool_shift=0, split_events=None,
+               stream=None):
         """Decode attention for one layer.  q: [B, Hq, D] device tensor."""
         import torch
         B, Hq, D = q.shape
         if not q.is_contiguous():
             raise ValueError("q must be contiguous")
-        opts = KvcDecodeOpts(int(partition_tokens), int(kernel), int(work_items), None, None)
+        opts = KvcDecodeOpts(int(partition_tokens), int(kernel), int(work_items), int(pool_pieces), int(pool_shift),
+                             None, None)
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event

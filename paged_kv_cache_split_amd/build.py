@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
     # matrix-core accumulators in ordinary VGPRs (no AGPR copies around the
     # online-softmax rescale)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # single-lane atomics stay single-lane: the wave-wide rewrite reads the
+    # result right after issuing it, which would stall the decode's ticket
+    # request that is meant to overlap the chunk's last blocks
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

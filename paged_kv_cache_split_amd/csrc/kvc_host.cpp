@@ -276,6 +276,7 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
                                                     : auto_partition_tokens(batch, num_kv_heads, max_context_len);
   if (pt % kDeviceBlockSize != 0 || pt > 1024) return false;
   if (opts && opts->work_items < 0) return false;
+  if (opts && (opts->pool_shift < 0 || opts->pool_shift > 6 || opts->pool_pieces > 64)) return false;
   plan->kernel = kernel;
   plan->partition_tokens = pt;
   plan->num_partitions = std::max(1, (max_context_len + pt - 1) / pt);
@@ -283,11 +284,14 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
                                : kvc::default_waves(static_cast<kvc_dtype>(kv));
   plan->work_items = (opts && opts->work_items > 0) ? opts->work_items
                                                     : std::max(1, waves / std::max(1, num_kv_heads));
-  return true;
+  plan->pool_pieces = (opts && opts->pool_pieces > 0) ? opts->pool_pieces : 0;
+  plan->pool_shift = (opts && opts->pool_shift > 0) ? opts->pool_shift : kvc::kDefaultPoolShift;
+  return plan->chunk_slots() <= (1 << 28);   // chunk ids stay far inside int32
 }
 
-size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t head_dim, const kvc::DecodePlan& p) {
-  return kvc::workspace_layout(p.kernel, p.num_partitions, p.work_items, batch, num_heads, head_dim).bytes;
+size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           const kvc::DecodePlan& p) {
+  return kvc::workspace_layout(p, batch, num_heads, num_kv_heads, head_dim).bytes;
 }
 
 }  // namespace
@@ -599,7 +603,7 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
     if (kernel != 0 && kernel != k) continue;
     kvc::DecodePlan p;
     if (!plan_decode(batch, num_kv_heads, max_context_len, k, -1, opts, &p)) return 0;
-    need = std::max(need, workspace_bytes_for(batch, num_heads, head_dim, p));
+    need = std::max(need, workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, p));
   }
   return need;
 }
@@ -637,8 +641,10 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   kvc::DecodePlan plan;
   if (!plan_decode(batch, num_kv_heads, std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size),
                    kernel, (int)kv, opts, &plan))
-    return fail(KVC_E_INVALID, "partition_tokens must be a multiple of 16 and at most 1024, work_items >= 0");
-  size_t need = workspace_bytes_for(batch, num_heads, head_dim, plan);
+    return fail(KVC_E_INVALID,
+                "partition_tokens must be a multiple of 16 and at most 1024, work_items >= 0, "
+                "pool_pieces <= 64, pool_shift in 0..6");
+  size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   hipError_t e = kvc::launch_decode(c->pool(), layer, plan, q, q_dtype, block_table, max_blocks_per_seq, context_lens,

@@ -58,42 +58,58 @@ struct DecodePlan {
   // FMA kernel: fixed partitions
   int32_t partition_tokens;
   int32_t num_partitions;    // ceil(max_context_len / partition_tokens)
-  // MFMA kernel: even split of each KV head's blocks over work_items waves;
-  // partial slots per query head = batch + work_items
+  // MFMA kernel: even split of each KV head's blocks over work_items waves,
+  // the last 1/2^pool_shift of each wave's run cut into pool_pieces pieces
+  // handed out at run time (0 = static split only); partial slots per query
+  // head = batch + chunk_slots()
   int32_t work_items;
+  int32_t pool_pieces;
+  int32_t pool_shift;
+  int64_t chunk_slots() const { return (int64_t)work_items * (pool_pieces + 1); }
 };
 
+// Dynamic pool: off unless asked for (each piece restarts the prefetch ring,
+// which costs about what the balance gains); the pool is the last eighth of
+// each wave's run unless pool_shift says otherwise.
+constexpr int32_t kDefaultPoolShift = 3;
+
 // Default number of waves per launch of the MFMA kernel: one per SIMD of a
-// 256-CU part for 16-bit caches (HBM-bound, one wave streams best), two for
-// fp8 caches (more VALU work per byte, which a second wave hides).  Fixed, so
+// 256-CU part (with the prefetch ring each wave keeps three blocks in flight,
+// which is enough to stream HBM for 16-bit and fp8 caches alike).  Fixed, so
 // results do not depend on the device's CU count.
 constexpr int32_t kDefaultWaves16 = 1024;
-constexpr int32_t kDefaultWavesFp8 = 2048;
+constexpr int32_t kDefaultWavesFp8 = 1024;
 inline int32_t default_waves(kvc_dtype kv) { return kv == KVC_FP8_E4M3 ? kDefaultWavesFp8 : kDefaultWaves16; }
 
 // Byte offsets inside the decode workspace.  FMA kernel: partial rows
 // [B][Hq][num_partitions] (acc, m, l).  MFMA kernel: partial rows
-// [Hq][B + work_items] (acc, m, l), then per sequence {first wave, waves}.
+// [Hq][B + chunk slots] (acc, m, l), then per sequence {first chunk, chunks},
+// then one ticket counter per KV head (zeroed by the launch sequence).
 struct WorkspaceLayout {
-  size_t acc, m, l, seginfo, bytes;
+  size_t acc, m, l, seginfo, tickets, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WorkspaceLayout workspace_layout(int32_t kernel, int32_t num_partitions, int32_t work_items, int32_t batch,
-                                        int32_t num_heads, int32_t head_dim) {
-  WorkspaceLayout w{0, 0, 0, 0, 0};
+inline WorkspaceLayout workspace_layout(const DecodePlan& p, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                        int32_t head_dim) {
+  WorkspaceLayout w{0, 0, 0, 0, 0, 0};
   size_t rows;
-  if (kernel == 1) {
-    if (num_partitions <= 1) return w;
-    rows = (size_t)batch * num_heads * num_partitions;
+  if (p.kernel == 1) {
+    if (p.num_partitions <= 1) return w;
+    rows = (size_t)batch * num_heads * p.num_partitions;
   } else {
-    rows = (size_t)num_heads * ((size_t)batch + work_items);
+    rows = (size_t)num_heads * ((size_t)batch + (size_t)p.chunk_slots());
   }
   w.m = align256(rows * head_dim * sizeof(float));
   w.l = w.m + align256(rows * sizeof(float));
   w.seginfo = w.l + align256(rows * sizeof(float));
-  w.bytes = w.seginfo + (kernel == 2 ? align256((size_t)batch * 2 * sizeof(int32_t)) : 0);
+  if (p.kernel == 2) {
+    w.tickets = w.seginfo + align256((size_t)batch * 2 * sizeof(int32_t));
+    w.bytes = w.tickets + align256((size_t)num_kv_heads * sizeof(int32_t));
+  } else {
+    w.tickets = w.bytes = w.seginfo;
+  }
   return w;
 }
 constexpr int32_t kMaxBatch = 8192;  // the per-sequence block scan lives in LDS

@@ -51,9 +51,12 @@ typedef const float __attribute__((address_space(4)))* const_f32_kptr;
 
 constexpr int kBS = 16;                       // tokens per block (device work)
 
-// Blocks each decode wave keeps in flight (16-bit and fp8 caches).
+// Blocks each decode wave keeps in flight (16-bit and fp8 caches).  With one
+// wave per SIMD the 16-bit kernel can spend all 256 VGPRs on a deeper ring
+// (measured: 4 blocks help long single-sequence runs, 5 gain nothing more);
+// the fp8 kernel's ring of 3 already streams at its best.
 #ifndef KVC_PREFETCH_16
-#define KVC_PREFETCH_16 3
+#define KVC_PREFETCH_16 4
 #endif
 #ifndef KVC_PREFETCH_FP8
 #define KVC_PREFETCH_FP8 3
@@ -294,11 +297,12 @@ struct DecodeArgs {
   void* out;
   const int32_t* block_table;
   const int32_t* context_lens;
-  // partials: FMA kernel [B][Hq][num_parts] rows, MFMA kernel [Hq][batch + work_items] rows
+  // partials: FMA kernel [B][Hq][num_parts] rows, MFMA kernel [Hq][batch + chunk_slots] rows
   float* ws_acc;   // rows x D
   float* ws_m;     // rows
   float* ws_l;     // rows
-  int* ws_seginfo; // MFMA kernel: per sequence {first wave, number of waves}
+  int* ws_seginfo; // MFMA kernel: per sequence {first chunk, number of chunks}
+  int* ws_ticket;  // MFMA kernel: per KV head, pool pieces handed out so far (zero at launch)
   const char* k;   // layer base of the K pool
   const char* v;   // layer base of the V pool
   const float* k_scale;  // layer base (fp8)
@@ -314,6 +318,9 @@ struct DecodeArgs {
   int32_t num_parts;
   int32_t batch;
   int32_t work_items;
+  int32_t pool_pieces;   // MFMA kernel: pool pieces per wave run (0 = static split)
+  int32_t pool_shift;    // MFMA kernel: pool = last 1/2^pool_shift of each run
+  int32_t chunk_slots;   // MFMA kernel: bound on chunk ids, work_items * (pool_pieces + 1)
   float qk_scale;  // softmax scale * log2(e)
 };
 
@@ -614,8 +621,29 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   // never more waves than blocks, so every wave that runs owns >= 1 block
   const int W = a.work_items < total ? a.work_items : total;
   if (w >= W) return;
-  const int x0 = wave_first_block(w, total, W);
-  const int x1 = wave_first_block(w + 1, total, W);
+  // Chunks.  Wave w owns blocks [x0, x1) of this head's list (an even split);
+  // with a dynamic pool, the last 1/2^pool_shift of that range is cut into
+  // KP pieces that go to whichever wave of this head asks first (a ticket
+  // counter), so waves that run fast (their XCD, their share of the memory
+  // system) take work from those that run slow.  Chunk ids follow the list
+  // order: wave w's main chunk is w * (KP + 1), its pieces follow it.  The
+  // pool is used only when every piece of every wave holds >= 1 block.
+  const int KP = (a.pool_pieces > 0 && ((total / W) >> a.pool_shift) >= a.pool_pieces) ? a.pool_pieces : 0;
+  const int CPW = KP + 1;
+  auto wave_range = [&](int ww, int& r0, int& r1, int& rm) {
+    r0 = wave_first_block(ww, total, W);
+    r1 = wave_first_block(ww + 1, total, W);
+    rm = KP ? r1 - ((r1 - r0) >> a.pool_shift) : r1;   // end of the main chunk
+  };
+  // chunk holding block y (piece j of a pool of len blocks starts at
+  // ceil(j * len / KP), so block o of the pool is in piece o * KP / len)
+  auto chunk_of_block = [&](int y) -> int {
+    const int ww = (int)(((int64_t)y * W) / total);
+    int r0, r1, rm;
+    wave_range(ww, r0, r1, rm);
+    if (y < rm) return ww * CPW;
+    return ww * CPW + 1 + (int)(((int64_t)(y - rm) * KP) / (r1 - rm));
+  };
   const int nn = lane & 15, r = lane >> 4;
   const int G = a.group;
   const bool head_ok = nn < G;
@@ -624,220 +652,245 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NDD = D / 16;   // output dim tiles
   const int64_t head_off = (int64_t)g * a.tile_bytes;
   const int64_t block_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
-  const int slots = a.batch + a.work_items;
+  const int slots = a.batch + a.chunk_slots;
 
-  // sequence holding block x0: the last b with seq_start[b] <= x0
-  int b = 0;
+  int xa, xb, c;   // the chunk being processed: blocks [xa, xb), id c
   {
-    int lo = 0, hi = a.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (seq_start[mid] <= x0) lo = mid;
-      else hi = mid - 1;
-    }
-    b = __builtin_amdgcn_readfirstlane(lo);
+    int r0, r1, rm;
+    wave_range(w, r0, r1, rm);
+    xa = r0;
+    xb = rm;
+    c = w * CPW;
   }
-  // Everything below that indexes memory is wave-uniform (scalar registers),
-  // so block ids and fp8 scales come through scalar loads, which are counted
-  // apart from the vector loads of the tiles and never drain the prefetch ring.
-  for (int x = x0; x < x1; ++b) {
-    const int sb = __builtin_amdgcn_readfirstlane(seq_start[b]);
-    const int eb = __builtin_amdgcn_readfirstlane(seq_start[b + 1]);
-    if (eb <= x) continue;                      // empty sequence
-    const int seg_end = eb < x1 ? eb : x1;
-    const int first = x - sb;                   // first local block of this segment
-    const int count = seg_end - x;              // blocks in this segment
-    const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
-    if (first == 0 && g == 0 && lane == 0) {
-      // the wave holding a sequence's first block records which waves hold it
-      const int w_last = (int)(((int64_t)(eb - 1) * W) / total);
-      a.ws_seginfo[2 * b] = w;
-      a.ws_seginfo[2 * b + 1] = w_last - w + 1;
-    }
-
-    // Query operand: for step kk the lane holds 8 dims of head nn, the same
-    // dims its K operand holds for token nn.
-    u32x4 qv[NQK];
+  for (;;) {
+    int t_next = 0;   // ticket of the next pool piece, asked for before the chunk's last blocks
+    // sequence holding block xa: the last b with seq_start[b] <= xa
+    int b = 0;
     {
-      const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_heads + h) * D;
-#pragma unroll
-      for (int kk = 0; kk < NQK; ++kk) {
-        int d0;
-        if constexpr (KV == KVC_FP8_E4M3) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
-        else d0 = (4 * kk + r) * 8;
-        qv[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
+      int lo = 0, hi = a.batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seq_start[mid] <= xa) lo = mid;
+        else hi = mid - 1;
       }
+      b = __builtin_amdgcn_readfirstlane(lo);
     }
-    floatx4 acc[NDD];
-#pragma unroll
-    for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInf, l = 0.0f;
+    // Everything below that indexes memory is wave-uniform (scalar registers),
+    // so block ids and fp8 scales come through scalar loads, which are counted
+    // apart from the vector loads of the tiles and never drain the prefetch ring.
+    for (int x = xa; x < xb; ++b) {
+      const int sb = __builtin_amdgcn_readfirstlane(seq_start[b]);
+      const int eb = __builtin_amdgcn_readfirstlane(seq_start[b + 1]);
+      if (eb <= x) continue;                      // empty sequence
+      const int seg_end = eb < xb ? eb : xb;
+      const int first = x - sb;                   // first local block of this segment
+      const int count = seg_end - x;              // blocks in this segment
+      const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
+      if (first == 0 && g == 0 && lane == 0) {
+        // the chunk holding a sequence's first block records which chunks hold it
+        a.ws_seginfo[2 * b] = c;
+        a.ws_seginfo[2 * b + 1] = chunk_of_block(eb - 1) - c + 1;
+      }
 
-    // Physical block of local block j of the segment (scalar load; indices
-    // past the end re-read the last block, an L2 hit, so every prefetch is
-    // unconditional).
-    const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + first);
-    auto phys_of = [&](int j) -> int {
-      j = j < count ? j : count - 1;
-      return clamp_block(row[j], a.num_blocks);
-    };
+      // Query operand: for step kk the lane holds 8 dims of head nn, the same
+      // dims its K operand holds for token nn.
+      u32x4 qv[NQK];
+      {
+        const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_heads + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < NQK; ++kk) {
+          int d0;
+          if constexpr (KV == KVC_FP8_E4M3) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
+          else d0 = (4 * kk + r) * 8;
+          qv[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
+        }
+      }
+      floatx4 acc[NDD];
+#pragma unroll
+      for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
+      float m = kNegInf, l = 0.0f;
 
-    auto process = [&](const KvBlock<KV, D>& cur, int i) {
-      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-      float qk = a.qk_scale;
-      float vsc = 1.0f;
-      if constexpr (KV == KVC_FP8_E4M3) {
-        qk *= cur.ks;
-        vsc = cur.vs;
-#pragma unroll
-        for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
-          u32x4 lo, hi;
-          lo[0] = fp8x2_to_bf16x2<false>(cur.k[c2][0]);
-          lo[1] = fp8x2_to_bf16x2<true>(cur.k[c2][0]);
-          lo[2] = fp8x2_to_bf16x2<false>(cur.k[c2][1]);
-          lo[3] = fp8x2_to_bf16x2<true>(cur.k[c2][1]);
-          hi[0] = fp8x2_to_bf16x2<false>(cur.k[c2][2]);
-          hi[1] = fp8x2_to_bf16x2<true>(cur.k[c2][2]);
-          hi[2] = fp8x2_to_bf16x2<false>(cur.k[c2][3]);
-          hi[3] = fp8x2_to_bf16x2<true>(cur.k[c2][3]);
-          s = mfma_qk<KV>(lo, qv[2 * c2], s);
-          s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
-      }
-      const int tbase = (first + i) * kBS + 4 * r;   // token index of this lane's first row
-      float sv[4];
-      float mx = kNegInf;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sv[e] = (tbase + e < n) ? s[e] * qk : kNegInf;
-        mx = fmaxf(mx, sv[e]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool grow = mx > m + kRescaleThreshold;
-      if (__any(grow)) {
-        const float mnew = grow ? mx : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        l *= alpha;
-#pragma unroll
-        for (int dd = 0; dd < NDD; ++dd) acc[dd] *= alpha;
-        m = mnew;
-      }
-      float pv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(sv[e] - m);
-        l += pv[e];
-      }
-      // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
-      // ~2^-17 relative), so rounding the weights to 16 bits costs no
-      // accuracy when the weighted values cancel.
-      u32x2 pb, pl;
-      if constexpr (KV == KVC_F16) {
-        pb[0] = pack_f16x2(pv[0], pv[1]);
-        pb[1] = pack_f16x2(pv[2], pv[3]);
-        pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
-        pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
-      } else {
+      // Physical block of local block j of the segment (scalar load).  Every
+      // prefetch is issued, so the count of loads in flight is the same on
+      // every path; one past the end reads the segment's last block with all
+      // lanes on one address: one cache line per load, no tile traffic.
+      const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + first);
+      auto phys_of = [&](int j) -> int {
+        j = j < count ? j : count - 1;
+        return clamp_block(row[j], a.num_blocks);
+      };
+
+      auto process = [&](const KvBlock<KV, D>& cur, int i) {
+        floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+        float qk = a.qk_scale;
+        float vsc = 1.0f;
         if constexpr (KV == KVC_FP8_E4M3) {
+          qk *= cur.ks;
+          vsc = cur.vs;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] *= vsc;
-        }
-        pb[0] = pack_bf16x2(pv[0], pv[1]);
-        pb[1] = pack_bf16x2(pv[2], pv[3]);
-        pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
-        pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
-      }
-#pragma unroll
-      for (int dd = 0; dd < NDD; ++dd) {
-        u32x2 va;
-        if constexpr (KV == KVC_FP8_E4M3) {
-          va[0] = fp8x2_to_bf16x2<false>(cur.v[dd]);
-          va[1] = fp8x2_to_bf16x2<true>(cur.v[dd]);
+          for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
+            u32x4 lo, hi;
+            lo[0] = fp8x2_to_bf16x2<false>(cur.k[c2][0]);
+            lo[1] = fp8x2_to_bf16x2<true>(cur.k[c2][0]);
+            lo[2] = fp8x2_to_bf16x2<false>(cur.k[c2][1]);
+            lo[3] = fp8x2_to_bf16x2<true>(cur.k[c2][1]);
+            hi[0] = fp8x2_to_bf16x2<false>(cur.k[c2][2]);
+            hi[1] = fp8x2_to_bf16x2<true>(cur.k[c2][2]);
+            hi[2] = fp8x2_to_bf16x2<false>(cur.k[c2][3]);
+            hi[3] = fp8x2_to_bf16x2<true>(cur.k[c2][3]);
+            s = mfma_qk<KV>(lo, qv[2 * c2], s);
+            s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
+          }
         } else {
-          va = cur.v[dd];
+#pragma unroll
+          for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
         }
-        acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
-        acc[dd] = mfma_pv<KV>(va, pl, acc[dd]);
-      }
-    };
-
-    // Ring of PF + 1 register buffers: block i + PF is in flight while block
-    // i is consumed.  The ring index is a compile-time constant after
-    // unrolling.
-    KvBlock<KV, D> buf[PF + 1];
-    auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
-      const int64_t o = (int64_t)ph * block_stride + head_off;
-      load_block<KV, D>(dst, a.k + o, a.v + o, nn, r);
-      if constexpr (KV == KVC_FP8_E4M3) {
-        dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
-        dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
-      }
-    };
+        const int tbase = (first + i) * kBS + 4 * r;   // token index of this lane's first row
+        float sv[4];
+        float mx = kNegInf;
 #pragma unroll
-    for (int j = 0; j < PF; ++j) fetch(buf[j], phys_of(j));
-    int ph_next = phys_of(PF);                  // id of the next block to prefetch, one step ahead
-    // Whole turns of the ring first, with no exit inside a turn: an exit that
-    // led back to the loop head would leave a load in flight there and force
-    // a full wait for it at the head of every turn.
-    int i0 = 0;
-    for (; i0 + PF + 1 <= count; i0 += PF + 1) {
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = (tbase + e < n) ? s[e] * qk : kNegInf;
+          mx = fmaxf(mx, sv[e]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool grow = mx > m + kRescaleThreshold;
+        if (__any(grow)) {
+          const float mnew = grow ? mx : m;
+          const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+          l *= alpha;
 #pragma unroll
-      for (int j = 0; j <= PF; ++j) {
-        const int i = i0 + j;
-        const int ph = ph_next;
-        ph_next = phys_of(i + PF + 1);
-        fetch(buf[(j + PF) % (PF + 1)], ph);
-        process(buf[j], i);
-      }
-    }
-    // the last, partial turn
+          for (int dd = 0; dd < NDD; ++dd) acc[dd] *= alpha;
+          m = mnew;
+        }
+        float pv[4];
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int i = i0 + j;
-      if (i >= count) break;
-      const int ph = ph_next;
-      ph_next = phys_of(i + PF + 1);
-      fetch(buf[(j + PF) % (PF + 1)], ph);
-      process(buf[j], i);
-    }
-    // l over the head's four lane groups
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (head_ok) {
-      if (x == sb && seg_end == eb) {
-        // the whole sequence is in this segment: write the output
-        const float inv = 1.0f / l;
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(sv[e] - m);
+          l += pv[e];
+        }
+        // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
+        // ~2^-17 relative), so rounding the weights to 16 bits costs no
+        // accuracy when the weighted values cancel.
+        u32x2 pb, pl;
+        if constexpr (KV == KVC_F16) {
+          pb[0] = pack_f16x2(pv[0], pv[1]);
+          pb[1] = pack_f16x2(pv[2], pv[3]);
+          pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
+          pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
+        } else {
+          if constexpr (KV == KVC_FP8_E4M3) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+          }
+          pb[0] = pack_bf16x2(pv[0], pv[1]);
+          pb[1] = pack_bf16x2(pv[2], pv[3]);
+          pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
+          pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
+        }
 #pragma unroll
         for (int dd = 0; dd < NDD; ++dd) {
-          const int64_t o = ((int64_t)b * a.num_heads + h) * D + 16 * dd + 4 * r;
-          u32x2 wv;
-          if constexpr (KV == KVC_F16) {
-            wv[0] = pack_f16x2(acc[dd][0] * inv, acc[dd][1] * inv);
-            wv[1] = pack_f16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+          u32x2 va;
+          if constexpr (KV == KVC_FP8_E4M3) {
+            va[0] = fp8x2_to_bf16x2<false>(cur.v[dd]);
+            va[1] = fp8x2_to_bf16x2<true>(cur.v[dd]);
           } else {
-            wv[0] = pack_bf16x2(acc[dd][0] * inv, acc[dd][1] * inv);
-            wv[1] = pack_bf16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+            va = cur.v[dd];
           }
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
+          acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
+          acc[dd] = mfma_pv<KV>(va, pl, acc[dd]);
         }
-      } else {
-        // partial of (sequence b, wave w): slot b + w is unique, since every
-        // segment boundary advances the sequence, the wave, or both
-        const int64_t rr = (int64_t)h * slots + b + w;
+      };
+
+      // Ring of PF + 1 register buffers: block i + PF is in flight while block
+      // i is consumed.  The ring index is a compile-time constant after
+      // unrolling.
+      KvBlock<KV, D> buf[PF + 1];
+      auto fetch = [&](KvBlock<KV, D>& dst, int ph, bool real) {
+        const int64_t o = (int64_t)ph * block_stride + head_off;
+        load_block<KV, D>(dst, a.k + o, a.v + o, real ? nn : 0, real ? r : 0);
+        if constexpr (KV == KVC_FP8_E4M3) {
+          dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
+          dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
+        }
+      };
 #pragma unroll
-        for (int dd = 0; dd < NDD; ++dd)
-          *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[dd];
-        if (r == 0) {
-          a.ws_m[rr] = m;
-          a.ws_l[rr] = l;
+      for (int j = 0; j < PF; ++j) fetch(buf[j], phys_of(j), j < count);
+      int ph_next = phys_of(PF);                  // id of the next block to prefetch, one step ahead
+      // Whole turns of the ring first, with no exit inside a turn: an exit that
+      // led back to the loop head would leave a load in flight there and force
+      // a full wait for it at the head of every turn.
+      int i0 = 0;
+      for (; i0 + PF + 1 <= count; i0 += PF + 1) {
+#pragma unroll
+        for (int j = 0; j <= PF; ++j) {
+          const int i = i0 + j;
+          const int ph = ph_next;
+          ph_next = phys_of(i + PF + 1);
+          fetch(buf[(j + PF) % (PF + 1)], ph, i + PF < count);
+          process(buf[j], i);
         }
       }
+      // The next piece is asked for now, so the ticket's round trip overlaps
+      // the last blocks of the chunk.
+      if (KP != 0 && seg_end == xb && lane == 0) t_next = atomicAdd(a.ws_ticket + g, 1);
+      // the last, partial turn
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int i = i0 + j;
+        if (i >= count) break;
+        const int ph = ph_next;
+        ph_next = phys_of(i + PF + 1);
+        fetch(buf[(j + PF) % (PF + 1)], ph, i + PF < count);
+        process(buf[j], i);
+      }
+      // l over the head's four lane groups
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      if (head_ok) {
+        if (x == sb && seg_end == eb) {
+          // the whole sequence is in this segment: write the output
+          const float inv = 1.0f / l;
+#pragma unroll
+          for (int dd = 0; dd < NDD; ++dd) {
+            const int64_t o = ((int64_t)b * a.num_heads + h) * D + 16 * dd + 4 * r;
+            u32x2 wv;
+            if constexpr (KV == KVC_F16) {
+              wv[0] = pack_f16x2(acc[dd][0] * inv, acc[dd][1] * inv);
+              wv[1] = pack_f16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+            } else {
+              wv[0] = pack_bf16x2(acc[dd][0] * inv, acc[dd][1] * inv);
+              wv[1] = pack_bf16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+            }
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
+          }
+        } else {
+          // partial of (sequence b, chunk c): slot b + c is unique, since every
+          // segment boundary advances the sequence, the chunk, or both
+          const int64_t rr = (int64_t)h * slots + b + c;
+#pragma unroll
+          for (int dd = 0; dd < NDD; ++dd)
+            *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[dd];
+          if (r == 0) {
+            a.ws_m[rr] = m;
+            a.ws_l[rr] = l;
+          }
+        }
+      }
+      x = seg_end;
     }
-    x = seg_end;
+    if (KP == 0) break;
+    // next pool piece of this head
+    const int t = __builtin_amdgcn_readfirstlane(t_next);
+    if (t >= W * KP) break;
+    const int ww = t / KP, j = t - ww * KP;
+    int r0, r1, rm;
+    wave_range(ww, r0, r1, rm);
+    const int len = r1 - rm;
+    xa = rm + (j * len + KP - 1) / KP;
+    xb = rm + ((j + 1) * len + KP - 1) / KP;
+    c = ww * CPW + 1 + j;
   }
 }
 
@@ -854,13 +907,13 @@ __global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
   const int hh = t / COLS, c = t % COLS;
   if (hh >= a.group) return;
   if (attend_len(a.context_lens, b, a.max_ctx, a.max_blocks) <= 0) return;
-  const int w_first = a.ws_seginfo[2 * b];
+  const int c_first = a.ws_seginfo[2 * b];
   int np = a.ws_seginfo[2 * b + 1];
-  if (np <= 1) return;                         // one wave held the whole sequence
-  if (w_first < 0 || w_first >= a.work_items) return;
-  if (np > a.work_items - w_first) np = a.work_items - w_first;
+  if (np <= 1) return;                         // one chunk held the whole sequence
+  if (c_first < 0 || c_first >= a.chunk_slots) return;
+  if (np > a.chunk_slots - c_first) np = a.chunk_slots - c_first;
   const int h = g * a.group + hh;
-  const int64_t row0 = (int64_t)h * (a.batch + a.work_items) + b + w_first;
+  const int64_t row0 = (int64_t)h * (a.batch + a.chunk_slots) + b + c_first;
   float M = kNegInf, L = 0.0f;
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
@@ -955,13 +1008,17 @@ hipError_t launch_fma(const DecodeArgs& a, int G, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(64) void zero_ints_kernel(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0;
+}
+
 template <kvc_dtype KV, kvc_dtype QT>
 hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merge, hipEvent_t ev0, hipEvent_t ev1,
                                hipStream_t s) {
   hipError_t e = hipSuccess;
   const size_t scan_lds = (size_t)(a.batch + 1) * sizeof(int);
-  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   if (kernel == 1) {
+    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
     dim3 grid(a.num_parts, a.num_kv_heads, a.batch);
     e = (D == 64) ? launch_fma<KV, QT, 64>(a, a.group, grid, s) : launch_fma<KV, QT, 128>(a, a.group, grid, s);
     if (e != hipSuccess) return e;
@@ -976,6 +1033,11 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
   }
   if constexpr (KV != KVC_F32) {
     constexpr int PF = (KV == KVC_FP8_E4M3) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_16;  // blocks in flight per wave
+    // ticket counters start at zero (a kernel, not a memset, so the sequence
+    // can be captured in a graph)
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, s, a.ws_ticket, a.num_kv_heads);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
     dim3 grid(a.work_items, a.num_kv_heads);
     if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64, PF>), grid, dim3(64), scan_lds, s, a);
     else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128, PF>), grid, dim3(64), scan_lds, s, a);
@@ -1066,15 +1128,18 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   a.num_parts = plan.num_partitions;
   a.batch = batch;
   a.work_items = plan.work_items;
+  a.pool_pieces = plan.pool_pieces;
+  a.pool_shift = plan.pool_shift;
+  a.chunk_slots = (int32_t)plan.chunk_slots();
   a.qk_scale = scale * kLog2e;
   const bool merge = plan.kernel == 2 || plan.num_partitions > 1;
-  const WorkspaceLayout wl = workspace_layout(plan.kernel, plan.num_partitions, plan.work_items, batch, num_heads,
-                                              pool.head_dim);
+  const WorkspaceLayout wl = workspace_layout(plan, batch, num_heads, pool.num_kv_heads, pool.head_dim);
   char* w = static_cast<char*>(workspace);
   a.ws_acc = wl.bytes ? reinterpret_cast<float*>(w + wl.acc) : nullptr;
   a.ws_m = wl.bytes ? reinterpret_cast<float*>(w + wl.m) : nullptr;
   a.ws_l = wl.bytes ? reinterpret_cast<float*>(w + wl.l) : nullptr;
   a.ws_seginfo = (wl.bytes && plan.kernel == 2) ? reinterpret_cast<int*>(w + wl.seginfo) : nullptr;
+  a.ws_ticket = (wl.bytes && plan.kernel == 2) ? reinterpret_cast<int*>(w + wl.tickets) : nullptr;
   const int D = pool.head_dim;
   switch (pool.dtype) {
     case KVC_F32:

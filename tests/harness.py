@@ -76,21 +76,22 @@ def gpu_setup(wl, values, device="cuda"):
     return cache
 
 
-def gpu_step(cache, wl, values, kernel=0, partition_tokens=0, device="cuda", out=None, work_items=0):
-    """The decode step: append each sequence's new token, export tables, decode."""
+def gpu_step(cache, wl, values, kernel=0, partition_tokens=0, device="cuda", out=None, work_items=0, **split):
+    """The decode step: append each sequence's new token, export tables, decode.
+    ``split``: pool_pieces / pool_shift of the MFMA kernel."""
     seqs = list(range(wl.batch))
     cache.append(seqs, values["k_new"].to(device).contiguous(), values["v_new"].to(device).contiguous())
     bt, cl = cache.export_tables(seqs)
     q = values["q"].to(device).contiguous()
     o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
-                     out=out, work_items=work_items)
+                     out=out, work_items=work_items, **split)
     return o, bt, cl
 
 
-def gpu_decode_again(cache, wl, values, bt, cl, kernel=0, partition_tokens=0, device="cuda", work_items=0):
+def gpu_decode_again(cache, wl, values, bt, cl, kernel=0, partition_tokens=0, device="cuda", work_items=0, **split):
     q = values["q"].to(device).contiguous()
     return cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
-                        work_items=work_items)
+                        work_items=work_items, **split)
 
 
 # -- oracle side ------------------------------------------------------------------

@@ -120,6 +120,33 @@ def test_long_segments_cross_the_block_id_window():
             check_close(to_f64(o), ref, *TOL[kv], f"{kv} work_items={wi}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8"])
+def test_dynamic_pool_pieces(kv):
+    # The MFMA kernel hands the last 1/2^shift of every wave's run out at run
+    # time in `pieces` pieces.  Cases: pieces cut across sequence boundaries,
+    # one wave taking its own pool, many waves competing for pieces, pools too
+    # small for their piece count (pool unused).  Every result matches the
+    # oracle and repeats bit for bit, whichever wave took which piece.
+    lens = [16 * 90 + 3, 1, 17, 16 * 41, 5, 16 * 200 - 1, 33, 16 * 7]
+    wl = custom_workload(len(lens), 16, 4, 128, kv, lens, seed=41, name="dynamic pool")
+    _say(f"[parity] dynamic pool kv={kv}")
+    values = make_values(wl, "cpu")
+    st = oracle_run(wl, values)
+    cache = gpu_setup(wl, values)
+    out, bt, cl = gpu_step(cache, wl, values, kernel=2, work_items=3, pool_pieces=-1)
+    torch.cuda.synchronize()
+    ref = oracle_decode(st, wl, values)
+    check_close(to_f64(out), ref, *TOL[kv], f"{kv} static split")
+    for wi, pieces, shift in [(1, 1, 1), (3, 2, 3), (3, 8, 1), (5, 3, 2), (7, 64, 6), (16, 4, 2), (40, 2, 3),
+                              (2, 5, 4), (64, 1, 1)]:
+        split = dict(kernel=2, work_items=wi, pool_pieces=pieces, pool_shift=shift)
+        o = gpu_decode_again(cache, wl, values, bt, cl, **split)
+        check_close(to_f64(o), ref, *TOL[kv], f"{kv} work_items={wi} pieces={pieces} shift={shift}")
+        again = gpu_decode_again(cache, wl, values, bt, cl, **split)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), again.view(torch.int16)), f"not deterministic: {split}"
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (8, 4, 128), (16, 4, 64), (16, 1, 128), (32, 2, 128), (12, 3, 64)])
 @pytest.mark.parametrize("kv", ["bf16", "f16", "fp8"])
 def test_head_groupings(hq, hkv, d, kv):

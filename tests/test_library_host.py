@@ -217,8 +217,15 @@ def test_workspace_sizes():
     ws = kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=256, kernel=1)
     assert ws >= 4 * 8 * 2 * (64 + 2) * 4
     assert kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=100, kernel=1) == 0   # invalid partition
-    # MFMA kernel: Hq * (batch + work_items) partial rows
+    # MFMA kernel: Hq * (batch + chunk slots) partial rows, chunk slots =
+    # work_items * (pool pieces + 1); no pool by default
     ws2 = kvc.decode_workspace_bytes(4, 8, 2, 64, 200, kernel=2, work_items=10)
     assert ws2 >= 8 * (4 + 10) * (64 + 2) * 4
+    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, kernel=2, work_items=10, pool_pieces=-1) == ws2
+    pooled = kvc.decode_workspace_bytes(4, 8, 2, 64, 200, kernel=2, work_items=10, pool_pieces=2)
+    assert pooled >= 8 * (4 + 30) * (64 + 2) * 4 and pooled > ws2
     # auto covers both
     assert kvc.decode_workspace_bytes(4, 8, 2, 64, 257, partition_tokens=256, work_items=10) == max(ws, ws2)
+    # out-of-range pool options are rejected (size 0)
+    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, kernel=2, pool_shift=7) == 0
+    assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, kernel=2, pool_pieces=65) == 0
