@@ -240,7 +240,8 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
  *  context_lens: device int32 [batch], tokens to attend per sequence, >= 1,
  *                including the appended token (what kvc_export_tables writes)
  *  max_context_len: host upper bound of context_lens (sizes the grid)
- *  scale:        softmax scale (normally 1/sqrt(head_dim))
+ *  scale:        softmax scale (normally 1/sqrt(head_dim)); finite and >= 0,
+ *                else KVC_E_INVALID
  *  out:          device [batch][num_heads][head_dim], q_dtype (rounded to nearest even)
  *  workspace:    device, kvc_decode_workspace_bytes() bytes
  * Checks: num_heads % num_kv_heads == 0 and num_heads / num_kv_heads <= 16,

@@ -632,7 +632,9 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   const kvc_dtype kv = f.kv_dtype;
   bool dt_ok = (kv == KVC_FP8_E4M3) ? (q_dtype == KVC_BF16) : (q_dtype == kv);
   if (!dt_ok) return fail(KVC_E_UNSUPPORTED, "q dtype %d with a cache of dtype %d", (int)q_dtype, (int)kv);
-  if (!(scale == scale)) return fail(KVC_E_INVALID, "scale is NaN");
+  // the split kernel takes the block max of the raw scores and scales it, so
+  // the scale must not flip the order of the scores
+  if (!(scale >= 0.0f) || scale > 3.0e38f) return fail(KVC_E_INVALID, "scale must be finite and >= 0");
   if (batch > kvc::kMaxBatch) return fail(KVC_E_UNSUPPORTED, "batch %d > %d", batch, kvc::kMaxBatch);
   int32_t kernel = opts ? opts->kernel : 0;
   if (kernel == 0) kernel = (kv == KVC_F32) ? 1 : 2;

@@ -551,26 +551,51 @@ __device__ __forceinline__ T load_stream(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
+// Lane offsets inside a (block, head) tile, fixed for the kernel: with a
+// wave-uniform tile base they make every tile load a scalar-base +
+// 32-bit-offset load with the step folded into the immediate.
+//  K tile [D/(16/E)][16][16/E]: lane (nn, r) reads 16-byte chunk r + 4*kk of
+//  token nn, so its offset is lane * 16 plus kk * 1 KiB.
+//  V^T tile [D][16]: lane reads tokens 4r..4r+3 of dim 16*dd + nn.
+template <kvc_dtype KV>
+__device__ __forceinline__ uint32_t k_lane_offset(int lane) { return (uint32_t)lane * 16u; }
+template <kvc_dtype KV>
+__device__ __forceinline__ uint32_t v_lane_offset(int nn, int r) {
+  constexpr uint32_t E = (KV == KVC_FP8_E4M3) ? 1u : 2u;
+  return ((uint32_t)nn * kBS + 4u * (uint32_t)r) * E;
+}
+
 template <kvc_dtype KV, int D>
-__device__ __forceinline__ void load_block(KvBlock<KV, D>& blk, const char* kt, const char* vt, int nn, int r) {
-  if constexpr (KV == KVC_FP8_E4M3) {
-    // K tile [D/16][16][16]: lane loads chunks r and r + 4 (16 dims each) of token nn.
+__device__ __forceinline__ void load_block(KvBlock<KV, D>& blk, const char* kt, const char* vt, uint32_t koff,
+                                           uint32_t voff) {
+  constexpr int E = (KV == KVC_FP8_E4M3) ? 1 : 2;
 #pragma unroll
-    for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2)
-      blk.k[c2] = load_stream<u32x4>(kt + ((int64_t)(r + 4 * c2) * kBS + nn) * 16);
-    // V^T tile [D][16] bytes: tokens 4r..4r+3 of dim 16*dd + nn.
+  for (int kk = 0; kk < KvBlock<KV, D>::NK; ++kk) blk.k[kk] = load_stream<u32x4>(kt + koff + kk * 1024);
 #pragma unroll
-    for (int dd = 0; dd < KvBlock<KV, D>::NV; ++dd)
-      blk.v[dd] = load_stream<uint32_t>(vt + (int64_t)(16 * dd + nn) * kBS + 4 * r);
-  } else {
-    // K tile [D/8][16][8]: chunk 4*kk + r of token nn.
-#pragma unroll
-    for (int kk = 0; kk < KvBlock<KV, D>::NK; ++kk)
-      blk.k[kk] = load_stream<u32x4>(kt + ((int64_t)(4 * kk + r) * kBS + nn) * 16);
-#pragma unroll
-    for (int dd = 0; dd < KvBlock<KV, D>::NV; ++dd)
-      blk.v[dd] = load_stream<u32x2>(vt + ((int64_t)(16 * dd + nn) * kBS + 4 * r) * 2);
+  for (int dd = 0; dd < KvBlock<KV, D>::NV; ++dd) {
+    if constexpr (KV == KVC_FP8_E4M3) blk.v[dd] = load_stream<uint32_t>(vt + voff + dd * 16 * kBS * E);
+    else blk.v[dd] = load_stream<u32x2>(vt + voff + dd * 16 * kBS * E);
   }
+}
+
+// Max over the lanes l, l^16, l^32, l^48 (the four row groups of a wave)
+// with the gfx950 row-swap permutes: no LDS round trip.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+  const uint32_t xb = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  const float y = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const uint32_t yb = __float_as_uint(y);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+__device__ __forceinline__ float sum_over_row_groups(float x) {
+  const uint32_t xb = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  const float y = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const uint32_t yb = __float_as_uint(y);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
 // The reference max only moves when a block's max exceeds it by more than
@@ -645,6 +670,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     return ww * CPW + 1 + (int)(((int64_t)(y - rm) * KP) / (r1 - rm));
   };
   const int nn = lane & 15, r = lane >> 4;
+  const uint32_t koff = k_lane_offset<KV>(lane), voff = v_lane_offset<KV>(nn, r);
   const int G = a.group;
   const bool head_ok = nn < G;
   const int h = g * G + nn;
@@ -712,8 +738,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 
       // Physical block of local block j of the segment (scalar load).  Every
       // prefetch is issued, so the count of loads in flight is the same on
-      // every path; one past the end reads the segment's last block with all
-      // lanes on one address: one cache line per load, no tile traffic.
+      // every path; past the end it re-reads the segment's last block, which
+      // the L2 still holds.
       const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + first);
       auto phys_of = [&](int j) -> int {
         j = j < count ? j : count - 1;
@@ -745,16 +771,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
           for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
         }
-        const int tbase = (first + i) * kBS + 4 * r;   // token index of this lane's first row
-        float sv[4];
-        float mx = kNegInf;
+        // Rows past the sequence's end exist only in its last block (a
+        // wave-uniform test): mask them there, before the max and after exp.
+        const int rem = n - (first + i) * kBS;        // rows of this block inside the sequence
+        float sv[4] = {s[0], s[1], s[2], s[3]};
+        if (rem < kBS) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sv[e] = (tbase + e < n) ? s[e] * qk : kNegInf;
-          mx = fmaxf(mx, sv[e]);
+          for (int e = 0; e < 4; ++e)
+            if (4 * r + e >= rem) sv[e] = kNegInf;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // the scale is positive, so the max of the raw scores, scaled, is the
+        // max of the scaled scores; exp2(s * qk - m) is one fma
+        float mx = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * qk;
         const bool grow = mx > m + kRescaleThreshold;
         if (__any(grow)) {
           const float mnew = grow ? mx : m;
@@ -766,10 +794,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         }
         float pv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(sv[e] - m);
-          l += pv[e];
+        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m));
+        if (rem < kBS) {
+          // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * r + e >= rem) pv[e] = 0.0f;
         }
+        l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
         // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
         // ~2^-17 relative), so rounding the weights to 16 bits costs no
         // accuracy when the weighted values cancel.
@@ -807,16 +839,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       // i is consumed.  The ring index is a compile-time constant after
       // unrolling.
       KvBlock<KV, D> buf[PF + 1];
-      auto fetch = [&](KvBlock<KV, D>& dst, int ph, bool real) {
+      auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
         const int64_t o = (int64_t)ph * block_stride + head_off;
-        load_block<KV, D>(dst, a.k + o, a.v + o, real ? nn : 0, real ? r : 0);
+        load_block<KV, D>(dst, a.k + o, a.v + o, koff, voff);
         if constexpr (KV == KVC_FP8_E4M3) {
           dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
           dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
         }
       };
 #pragma unroll
-      for (int j = 0; j < PF; ++j) fetch(buf[j], phys_of(j), j < count);
+      for (int j = 0; j < PF; ++j) fetch(buf[j], phys_of(j));
       int ph_next = phys_of(PF);                  // id of the next block to prefetch, one step ahead
       // Whole turns of the ring first, with no exit inside a turn: an exit that
       // led back to the loop head would leave a load in flight there and force
@@ -828,7 +860,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
           const int i = i0 + j;
           const int ph = ph_next;
           ph_next = phys_of(i + PF + 1);
-          fetch(buf[(j + PF) % (PF + 1)], ph, i + PF < count);
+          fetch(buf[(j + PF) % (PF + 1)], ph);
           process(buf[j], i);
         }
       }
@@ -842,12 +874,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         if (i >= count) break;
         const int ph = ph_next;
         ph_next = phys_of(i + PF + 1);
-        fetch(buf[(j + PF) % (PF + 1)], ph, i + PF < count);
+        fetch(buf[(j + PF) % (PF + 1)], ph);
         process(buf[j], i);
       }
       // l over the head's four lane groups
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
+      l = sum_over_row_groups(l);
       if (head_ok) {
         if (x == sb && seg_end == eb) {
           // the whole sequence is in this segment: write the output

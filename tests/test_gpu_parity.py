@@ -233,3 +233,27 @@ def test_multi_layer_pool_and_cow(kv):
             o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, layer=layer, kernel=kernel,
                              partition_tokens=32, work_items=3)
             check_close(to_f64(o), ref, *TOL[kv], f"{kv} layer {layer} kernel {kernel}")
+
+
+def test_decode_rejects_negative_or_infinite_scale():
+    from paged_kv_cache_split_amd import KvcError
+    lens = [20, 3]
+    wl = custom_workload(len(lens), 8, 2, 128, "bf16", lens, seed=11, name="scale checks")
+    values = make_values(wl, "cpu")
+    cache = gpu_setup(wl, values)
+    out, bt, cl = gpu_step(cache, wl, values)
+    torch.cuda.synchronize()
+    q = values["q"].to("cuda").contiguous()
+    for bad in (-0.125, float("inf"), float("nan")):
+        with pytest.raises(KvcError):
+            cache.decode(q, bt, cl, wl.max_context_len, bad)
+    # scale 0 is allowed: every weight is equal, the output is the mean of V
+    z = cache.decode(q, bt, cl, wl.max_context_len, 0.0)
+    torch.cuda.synchronize()
+    start = 0
+    for b, n in enumerate(lens):
+        v = torch.cat([values["v_hist"][0, start:start + n], values["v_new"][0, b:b + 1]]).to(torch.float64)
+        start += n
+        mean = v.mean(0)                                   # [Hkv, D]
+        ref = mean.repeat_interleave(wl.num_heads // wl.num_kv_heads, 0).numpy()
+        check_close(to_f64(z[b]), ref, *TOL["bf16"], f"scale 0 seq {b}")
