@@ -12,8 +12,9 @@ method's fp8 storage step is itself defined in float32 (see ``fp8_policy``).
 Modules and the passages each follows (pages are cited by title and section):
 
 * ``attention`` -- decode attention softmax(q K^T * scale) V per query head over
-  a contiguously gathered history, GQA head grouping, and a brute-force full
-  causal attention used to pin it.
+  a contiguously gathered history, GQA head grouping, the multi-token causal
+  form (several new tokens per sequence), and a brute-force full causal
+  attention used to pin them.
 * ``blocktable`` -- the block allocator: free list, per-sequence tables,
   refcounts, copy-on-write fork, slot mapping for appends.
 * ``e4m3`` -- the OCP 8-bit float E4M3 ("FN") format, decode and round-to-

@@ -24,6 +24,15 @@ What is computed (the pages' statement of the decode step):
   ``naive_attention`` keeps all kv_len columns for q_len = 1; the LLaMA code in
   "大模型推理加速——KV Cache篇" §3 builds a mask only when seqlen > 1).
 
+``extend_attention`` is the same step for several new query tokens per
+sequence -- the target model's parallel pass over the draft tokens of
+speculative decoding ("LLM推理优化实战…" §4.2, all gamma candidates verified in
+one forward pass) or one chunk of a chunked prefill ("苦猿的大模型日记" PART 03,
+long-prompt prefill where q_len > 1).  The new tokens are appended first, then
+each one attends causally: the token at position p sees positions 0..p, which
+is the mask of "苦猿的大模型日记" PART 04's ``naive_attention`` (lower triangle
+shifted by kv_len - q_len).
+
 ``causal_attention`` is the full-recompute definition (page 5's
 ``naive_attention`` with ``tril(diagonal = kv_len - q_len)``), written here
 without torch, used to pin ``decode_attention`` by brute force.
@@ -73,6 +82,38 @@ def decode_attention_batch(q, k_list, v_list, scale):
     out = np.empty(q.shape, dtype=np.float64)
     for b in range(q.shape[0]):
         out[b] = decode_attention(q[b], k_list[b], v_list[b], scale)
+    return out
+
+
+def extend_attention(q, k, v, scale):
+    """Attention of the last nq tokens of a sequence over its whole history.
+
+    q: [nq, Hq, D]   queries of the nq newest tokens, oldest first
+    k, v: [n, Hkv, D]  the sequence's K/V rows in position order, the nq new
+        tokens' rows last (n >= nq >= 1)
+    scale: float, the softmax scale
+    returns: [nq, Hq, D] fp64; row i is the token at position n - nq + i,
+        which attends over rows 0 .. n - nq + i.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nq, hq, d = q.shape
+    n, hkv, dk = k.shape
+    if not 1 <= nq <= n:
+        raise ValueError("need 1 <= nq <= n")
+    if dk != d or v.shape != k.shape or hq % hkv != 0:
+        raise ValueError("shape mismatch")
+    group = hq // hkv
+    scale = float(scale)
+    out = np.empty((nq, hq, d), dtype=np.float64)
+    for i in range(nq):
+        visible = n - nq + i + 1                      # rows 0 .. visible - 1
+        for h in range(hq):
+            g = h // group
+            scores = scale * (k[:visible, g, :] @ q[i, h])
+            w = np.exp(scores - scores.max())
+            out[i, h] = (w @ v[:visible, g, :]) / w.sum()
     return out
 
 

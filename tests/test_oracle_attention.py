@@ -179,3 +179,106 @@ def test_batch_wrapper_is_per_sequence():
     out = attention.decode_attention_batch(q, ks, vs, 0.3)
     for b in range(3):
         np.testing.assert_array_equal(out[b], attention.decode_attention(q[b], ks[b], vs[b], 0.3))
+
+
+# -- several new tokens per sequence (verify pass / prefill chunk) ----------------
+
+def test_extend_worked_example_against_page_procedure(worked):
+    # The page's step-2 prompt of three tokens, with its printed causal mask, run
+    # by torch in fp64 (the page's procedure), against the oracle's multi-token
+    # form: all three tokens at once (an uncached prefill), and the last two
+    # tokens as a chunk over the first one cached (a chunked prefill / verify).
+    g = worked["g"]
+    Xt = torch.tensor(worked["X2"], dtype=torch.float64)
+    Q = Xt @ torch.tensor(g["W_Q"], dtype=torch.float64)
+    K = Xt @ torch.tensor(g["W_K"], dtype=torch.float64)
+    V = Xt @ torch.tensor(g["W_V"], dtype=torch.float64)
+    m = torch.tensor([[float(x) for x in row] for row in g["mask_step2"]], dtype=torch.float64)
+    ref = (F.softmax(Q @ K.T / g["score_divisor"] + m, dim=-1) @ V).numpy()
+    Qn, Kn, Vn = Q.numpy()[:, None, :], K.numpy()[:, None, :], V.numpy()[:, None, :]
+    whole = attention.extend_attention(Qn, Kn, Vn, worked["scale"])
+    np.testing.assert_allclose(whole[:, 0], ref, rtol=0, atol=1e-15)
+    chunk = attention.extend_attention(Qn[1:], Kn, Vn, worked["scale"])
+    np.testing.assert_allclose(chunk[:, 0], ref[1:], rtol=0, atol=1e-15)
+    # first row is the first value row exactly (it sees one key)
+    assert np.array_equal(whole[0, 0], Vn[0, 0])
+
+
+def test_extend_of_one_token_is_decode():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((1, 8, 32))
+    K, V = rng.standard_normal((19, 2, 32)), rng.standard_normal((19, 2, 32))
+    np.testing.assert_array_equal(attention.extend_attention(q, K, V, 0.2)[0],
+                                  attention.decode_attention(q[0], K, V, 0.2))
+
+
+def _sdpa_causal(q, K, V, scale):
+    # torch SDPA in fp64 with an explicit boolean mask: query i (of nq) sees key
+    # j iff j <= i + n - nq; enable_gqa groups query heads contiguously.
+    nq, n = q.shape[0], K.shape[0]
+    mask = torch.ones(nq, n, dtype=torch.bool).tril(diagonal=n - nq)
+    qt = torch.tensor(q, dtype=torch.float64).permute(1, 0, 2)[None]      # [1, Hq, nq, D]
+    kt = torch.tensor(K, dtype=torch.float64).permute(1, 0, 2)[None]      # [1, Hkv, n, D]
+    vt = torch.tensor(V, dtype=torch.float64).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(), attn_mask=mask, scale=scale,
+                                       enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("hq,hkv,nq,n", [(8, 2, 5, 40), (4, 4, 16, 16), (16, 1, 3, 70), (6, 3, 9, 9),
+                                         (64, 8, 2, 33)])
+def test_extend_matches_torch_sdpa_with_causal_mask(hq, hkv, nq, n):
+    rng = np.random.default_rng(hq * 31 + nq)
+    d = 64
+    q = rng.standard_normal((nq, hq, d))
+    K, V = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    s = float(np.float32(1 / math.sqrt(d)))
+    np.testing.assert_allclose(attention.extend_attention(q, K, V, s), _sdpa_causal(q, K, V, s),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_extend_equals_last_rows_of_full_recompute():
+    rng = np.random.default_rng(8)
+    hq, hkv, d, n, nq = 6, 2, 16, 23, 7
+    Q = rng.standard_normal((n, hq, d))
+    K, V = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    ext = attention.extend_attention(Q[n - nq:], K, V, 0.25)
+    for h in range(hq):
+        full = attention.causal_attention(Q[:, h], K[:, h // 3], V[:, h // 3], 0.25)
+        np.testing.assert_allclose(ext[:, h], full[n - nq:], rtol=1e-12, atol=1e-14)
+
+
+def test_chunked_prefill_equals_one_pass():
+    # A prompt processed in chunks (each chunk attending to everything before
+    # it) gives the same rows as processing it whole.
+    rng = np.random.default_rng(12)
+    n, hq, hkv, d = 30, 4, 2, 8
+    Q = rng.standard_normal((n, hq, d))
+    K, V = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    whole = attention.extend_attention(Q, K, V, 0.3)
+    start = 0
+    for c in (7, 1, 16, 6):
+        part = attention.extend_attention(Q[start:start + c], K[:start + c], V[:start + c], 0.3)
+        np.testing.assert_allclose(part, whole[start:start + c], rtol=1e-13, atol=1e-15)
+        start += c
+
+
+def test_planted_causal_offset_mistake_is_caught():
+    # Off by one in the visible range (the token not seeing itself) must fail
+    # the SDPA pin.
+    def wrong(q, K, V, scale):
+        nq, hq, d = q.shape
+        n, hkv, _ = K.shape
+        out = np.empty_like(q)
+        for i in range(nq):
+            vis = max(1, n - nq + i)
+            for h in range(hq):
+                sc = scale * (K[:vis, h // (hq // hkv)] @ q[i, h])
+                w = np.exp(sc - sc.max())
+                out[i, h] = w @ V[:vis, h // (hq // hkv)] / w.sum()
+        return out
+    rng = np.random.default_rng(2)
+    q, K, V = rng.standard_normal((4, 4, 8)), rng.standard_normal((10, 2, 8)), rng.standard_normal((10, 2, 8))
+    ref = _sdpa_causal(q, K, V, 0.4)
+    assert not np.allclose(wrong(q, K, V, 0.4), ref, atol=1e-6)
+    assert np.allclose(attention.extend_attention(q, K, V, 0.4), ref, atol=1e-12)
