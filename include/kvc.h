@@ -41,7 +41,9 @@
  *    fp8 only: k_scale, v_scale float32 [num_layers][num_blocks][num_kv_heads];
  *            the value of a stored code c is e4m3(c) * scale.
  *  Token position p of a sequence lives in block table[p / block_size] at
- *  slot p % block_size.
+ *  slot p % block_size.  The slots past a sequence's length in its last block
+ *  may hold anything, never-written memory included (the pools need no
+ *  clearing): the kernels read them but mask them out before they are used.
  *
  * fp8 (E4M3) storage: OCP E4M3 "FN" (bias 7, max 448, S.1111.111 = NaN).
  *  For each write of c new rows into one (layer, block, KV head) that already
@@ -252,6 +254,48 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
  * block_size is cut to it, a block id outside [0, num_blocks) reads block 0
  * (the result for that sequence is then meaningless, but nothing faults). */
 kvc_status kvc_decode_attention(kvc_cache* cache, int32_t layer, const void* q, kvc_dtype q_dtype,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                float scale, void* out, void* workspace, size_t workspace_bytes,
+                                const kvc_decode_opts* opts, kvc_stream_t stream);
+
+/* ---- several new query tokens per sequence --------------------------------- */
+
+/* Attention of several new tokens per sequence over the paged cache: the
+ * target model's pass over the draft tokens of speculative decoding (all
+ * candidates verified in one forward pass, "LLM推理优化实战：从KV-Cache到Continuous
+ * Batching…" §4.2) or one chunk of a chunked prefill (q_len > 1,
+ * "苦猿的大模型日记 · Day45" PART 03).  The new tokens' K/V rows are appended first
+ * (kvc_append with n_new = the tokens of each sequence); then query token i of
+ * sequence b, which sits at position context_lens[b] - ql_b + i, attends
+ * causally over rows 0 .. context_lens[b] - ql_b + i of that sequence (the
+ * mask of "苦猿的大模型日记" PART 04's naive_attention, the lower triangle shifted
+ * by kv_len - q_len).  With one token per sequence this is
+ * kvc_decode_attention.
+ *  q:            device [total_query][num_heads][head_dim], q_dtype (as for decode)
+ *  query_start:  device int32 [batch + 1], non-decreasing, query_start[0] = 0,
+ *                query_start[batch] = total_query: the query rows of sequence b
+ *                are query_start[b] .. query_start[b + 1] - 1, oldest token first;
+ *                ql_b = query_start[b + 1] - query_start[b] may be 0
+ *  total_query:  rows of q and out (host)
+ *  max_query_len: host upper bound of ql_b, 1..4096 (sizes the grid and the workspace)
+ *  context_lens: device int32 [batch], rows cached per sequence including the
+ *                ql_b new ones (what kvc_export_tables writes after the append);
+ *                ql_b <= context_lens[b]
+ *  out:          device [total_query][num_heads][head_dim], q_dtype
+ *  workspace:    device, kvc_extend_workspace_bytes() bytes
+ *  opts:         NULL, or kernel 0 / 2 and work_items (waves per KV head and
+ *                column-tile group); the other fields are ignored
+ * Other arguments and checks as for kvc_decode_attention; an f32 cache gives
+ * KVC_E_UNSUPPORTED (the kernel runs on matrix cores).  Device-side values are
+ * clamped as for decode; ql_b is cut to min(max_query_len, context_lens[b]) and
+ * rows outside [0, total_query) are neither read nor written, so a malformed
+ * query_start gives meaningless rows but nothing faults. */
+size_t kvc_extend_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_query_len, const kvc_decode_opts* opts);
+kvc_status kvc_extend_attention(kvc_cache* cache, int32_t layer, const void* q, kvc_dtype q_dtype,
+                                const int32_t* query_start, int32_t total_query, int32_t max_query_len,
                                 const int32_t* block_table, int32_t max_blocks_per_seq,
                                 const int32_t* context_lens, int32_t max_context_len, int32_t batch,
                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -32,7 +32,8 @@ SYMBOLS = [
     "kvc_bytes_per_token", "kvc_pool_bytes", "kvc_scale_bytes", "kvc_scratch_bytes", "kvc_create", "kvc_destroy",
     "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_reserve_host",
     "kvc_get_table", "kvc_stats", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
-    "kvc_decode_attention", "kvc_stream_copy", "kvc_last_error",
+    "kvc_decode_attention", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_stream_copy",
+    "kvc_last_error",
 ]
 
 
@@ -81,6 +82,10 @@ _sig = {
     "kvc_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
     "kvc_decode_attention": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f, _vp, _vp, _sz, ctypes.POINTER(KvcDecodeOpts), _vp]),
+    "kvc_extend_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
+    "kvc_extend_attention": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
+                                            _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp, _sz,
+                                            ctypes.POINTER(KvcDecodeOpts), _vp]),
     "kvc_stream_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
     "kvc_last_error": (ctypes.c_char_p, []),
 }
@@ -152,6 +157,12 @@ def decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context
                            kernel=0, work_items=0, pool_pieces=0, pool_shift=0) -> int:
     opts = KvcDecodeOpts(partition_tokens, kernel, work_items, pool_pieces, pool_shift, None, None)
     return _lib.kvc_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len,
+                                           ctypes.byref(opts))
+
+
+def extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len, work_items=0) -> int:
+    opts = KvcDecodeOpts(0, 0, work_items, 0, 0, None, None)
+    return _lib.kvc_extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len,
                                            ctypes.byref(opts))
 
 
@@ -318,4 +329,34 @@ class KVCache:
             ctypes.c_void_p(context_lens.data_ptr()), int(max_context_len), B, Hq, self.num_kv_heads, D,
             self.block_size, float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
             workspace.numel(), ctypes.byref(opts), _stream_ptr(stream)), "kvc_decode_attention")
+        return out
+
+    def extend(self, q, query_start, max_query_len, block_table, context_lens, max_context_len, scale, layer=0,
+               out=None, workspace=None, work_items=0, split_events=None, stream=None):
+        """Attention of several new tokens per sequence (causal among them) for
+        one layer.  q: [total_query, Hq, D] device tensor; query_start: device
+        int32 [B + 1] (rows of sequence b are query_start[b] .. query_start[b+1]-1)."""
+        import torch
+        T, Hq, D = q.shape
+        B = int(context_lens.shape[0])
+        if not q.is_contiguous():
+            raise ValueError("q must be contiguous")
+        if query_start.dtype != torch.int32 or query_start.numel() != B + 1:
+            raise ValueError("query_start must be int32 with batch + 1 entries")
+        opts = KvcDecodeOpts(0, 0, int(work_items), 0, 0, None, None)
+        if split_events is not None:
+            opts.split_start = split_events[0].cuda_event
+            opts.split_end = split_events[1].cuda_event
+        ws_need = _lib.kvc_extend_workspace_bytes(B, Hq, self.num_kv_heads, D, int(max_query_len), ctypes.byref(opts))
+        if workspace is None or workspace.numel() < ws_need:
+            workspace = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty_like(q)
+        _check(_lib.kvc_extend_attention(
+            self._h, int(layer), ctypes.c_void_p(q.data_ptr()), _dtype_code(q.dtype),
+            ctypes.c_void_p(query_start.data_ptr()), T, int(max_query_len),
+            ctypes.c_void_p(block_table.data_ptr()), int(block_table.shape[1]),
+            ctypes.c_void_p(context_lens.data_ptr()), int(max_context_len), B, Hq, self.num_kv_heads, D,
+            self.block_size, float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+            workspace.numel(), ctypes.byref(opts), _stream_ptr(stream)), "kvc_extend_attention")
         return out

@@ -286,7 +286,43 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
                                                     : std::max(1, waves / std::max(1, num_kv_heads));
   plan->pool_pieces = (opts && opts->pool_pieces > 0) ? opts->pool_pieces : 0;
   plan->pool_shift = (opts && opts->pool_shift > 0) ? opts->pool_shift : kvc::kDefaultPoolShift;
+  plan->tile_groups = 0;
+  plan->waves_per_group = 1;
+  plan->max_q = 1;
   return plan->chunk_slots() <= (1 << 28);   // chunk ids stay far inside int32
+}
+
+// Several query tokens per sequence (MFMA kernel).  A sequence's columns are
+// ceil(max_q * G / 16) tiles of 16 (query token, head) pairs; up to 4 tiles
+// share a work-group (one wave each, side by side on one chunk of blocks, so
+// the chunk's tiles are read from HBM once and served to the others from
+// cache), the rest go to grid.z.  The waves per KV head are divided among the
+// tile groups so a launch keeps about one wave per SIMD, and capped so the
+// partials stay within kExtendRowBudget rows per query head.
+constexpr int64_t kExtendRowBudget = 1 << 16;
+constexpr int32_t kMaxQueryTokens = 4096;
+
+bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t max_q, int kv,
+                 const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
+  if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2))) return false;
+  if (max_q < 1 || max_q > kMaxQueryTokens) return false;
+  const int32_t G = num_heads / num_kv_heads;
+  const int32_t tiles = (max_q * G + 15) / 16;
+  plan->kernel = 2;
+  plan->partition_tokens = 0;
+  plan->num_partitions = 1;
+  plan->pool_pieces = 0;
+  plan->pool_shift = kvc::kDefaultPoolShift;
+  plan->waves_per_group = std::min(4, tiles);
+  plan->tile_groups = (tiles + plan->waves_per_group - 1) / plan->waves_per_group;
+  plan->max_q = max_q;
+  const int32_t waves = kv < 0 ? std::max(kvc::kDefaultWaves16, kvc::kDefaultWavesFp8)
+                               : kvc::default_waves(static_cast<kvc_dtype>(kv));
+  int64_t w = waves / ((int64_t)num_kv_heads * plan->waves_per_group * plan->tile_groups);
+  w = std::min<int64_t>(w, kExtendRowBudget / max_q - batch);
+  if (opts && opts->work_items > 0) w = opts->work_items;
+  plan->work_items = (int32_t)std::max<int64_t>(1, w);
+  return plan->chunk_slots() <= (1 << 28);
 }
 
 size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -608,24 +644,30 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
   return need;
 }
 
-kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_dtype q_dtype,
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the decode and the multi-token call, in order: cache,
+// layer, shape against the cache, head grouping, pointers, dtypes, scale,
+// batch.  Returns KVC_OK or the failure (already recorded).
+kvc_status check_attention_args(const kvc_cache* c, int32_t layer, const void* q, kvc_dtype q_dtype,
                                 const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
                                 int32_t max_context_len, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t block_size, float scale, void* out, void* workspace,
-                                size_t workspace_bytes, const kvc_decode_opts* opts, kvc_stream_t stream) {
+                                int32_t head_dim, int32_t block_size, float scale, const void* out) {
   if (!c) return fail(KVC_E_INVALID, "cache is NULL");
   kvc_status st = check_device_ready(c);
   if (st != KVC_OK) return st;
   const kvc_config& f = c->cfg;
   if (layer < 0 || layer >= f.num_layers) return fail(KVC_E_INVALID, "layer %d outside 0..%d", layer, f.num_layers - 1);
   if (batch < 0) return fail(KVC_E_INVALID, "batch must be >= 0");
-  if (batch == 0) return ok();
   if (num_kv_heads != f.num_kv_heads) return fail(KVC_E_INVALID, "num_kv_heads %d != cache's %d", num_kv_heads, f.num_kv_heads);
   if (head_dim != f.head_dim) return fail(KVC_E_INVALID, "head_dim %d != cache's %d", head_dim, f.head_dim);
   if (block_size != f.block_size) return fail(KVC_E_INVALID, "block_size %d != cache's %d", block_size, f.block_size);
   if (num_heads < 1 || num_heads % num_kv_heads != 0)
     return fail(KVC_E_INVALID, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
   if (num_heads / num_kv_heads > 16) return fail(KVC_E_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (batch == 0) return KVC_OK;
   if (!q || !block_table || !context_lens || !out) return fail(KVC_E_INVALID, "NULL device argument");
   if (max_blocks_per_seq < 1) return fail(KVC_E_INVALID, "max_blocks_per_seq must be >= 1");
   if (max_context_len < 1) return fail(KVC_E_INVALID, "max_context_len must be >= 1");
@@ -636,6 +678,24 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   // the scale must not flip the order of the scores
   if (!(scale >= 0.0f) || scale > 3.0e38f) return fail(KVC_E_INVALID, "scale must be finite and >= 0");
   if (batch > kvc::kMaxBatch) return fail(KVC_E_UNSUPPORTED, "batch %d > %d", batch, kvc::kMaxBatch);
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_dtype q_dtype,
+                                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, float scale, void* out, void* workspace,
+                                size_t workspace_bytes, const kvc_decode_opts* opts, kvc_stream_t stream) {
+  kvc_status st = check_attention_args(c, layer, q, q_dtype, block_table, max_blocks_per_seq, context_lens,
+                                       max_context_len, batch, num_heads, num_kv_heads, head_dim, block_size, scale,
+                                       out);
+  if (st != KVC_OK) return st;
+  if (batch == 0) return ok();
+  const kvc_dtype kv = c->cfg.kv_dtype;
   int32_t kernel = opts ? opts->kernel : 0;
   if (kernel == 0) kernel = (kv == KVC_F32) ? 1 : 2;
   if (kernel == 2 && kv == KVC_F32) return fail(KVC_E_UNSUPPORTED, "the MFMA kernel needs a 16-bit or fp8 cache");
@@ -649,12 +709,55 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  hipError_t e = kvc::launch_decode(c->pool(), layer, plan, q, q_dtype, block_table, max_blocks_per_seq, context_lens,
-                                    max_context_len, batch, num_heads, scale, out, workspace,
+  hipError_t e = kvc::launch_decode(c->pool(), layer, plan, q, q_dtype, nullptr, batch, block_table,
+                                    max_blocks_per_seq, context_lens, max_context_len, batch, num_heads, scale, out,
+                                    workspace,
                                     opts ? static_cast<hipEvent_t>(opts->split_start) : nullptr,
                                     opts ? static_cast<hipEvent_t>(opts->split_end) : nullptr,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVC_E_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t kvc_extend_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_query_len, const kvc_decode_opts* opts) {
+  if (batch < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || num_heads % num_kv_heads != 0) return 0;
+  kvc::DecodePlan p;
+  if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len, -1, opts, &p)) return 0;
+  return workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, p);
+}
+
+kvc_status kvc_extend_attention(kvc_cache* c, int32_t layer, const void* q, kvc_dtype q_dtype,
+                                const int32_t* query_start, int32_t total_query, int32_t max_query_len,
+                                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, float scale, void* out, void* workspace,
+                                size_t workspace_bytes, const kvc_decode_opts* opts, kvc_stream_t stream) {
+  kvc_status st = check_attention_args(c, layer, q, q_dtype, block_table, max_blocks_per_seq, context_lens,
+                                       max_context_len, batch, num_heads, num_kv_heads, head_dim, block_size, scale,
+                                       out);
+  if (st != KVC_OK) return st;
+  if (batch == 0) return ok();
+  if (!query_start) return fail(KVC_E_INVALID, "NULL device argument");
+  if (total_query < 0) return fail(KVC_E_INVALID, "total_query must be >= 0");
+  if (total_query == 0) return ok();
+  if (max_query_len < 1 || max_query_len > kMaxQueryTokens)
+    return fail(KVC_E_INVALID, "max_query_len must be in 1..%d", kMaxQueryTokens);
+  const kvc_dtype kv = c->cfg.kv_dtype;
+  if (kv == KVC_F32) return fail(KVC_E_UNSUPPORTED, "several query tokens need a 16-bit or fp8 cache");
+  kvc::DecodePlan plan;
+  if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len, (int)kv, opts, &plan))
+    return fail(KVC_E_INVALID, "opts: kernel must be 0 or 2, work_items >= 0");
+  size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  hipError_t e = kvc::launch_decode(c->pool(), layer, plan, q, q_dtype, query_start, total_query, block_table,
+                                    max_blocks_per_seq, context_lens, max_context_len, batch, num_heads, scale, out,
+                                    workspace,
+                                    opts ? static_cast<hipEvent_t>(opts->split_start) : nullptr,
+                                    opts ? static_cast<hipEvent_t>(opts->split_end) : nullptr,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVC_E_HIP, "extend launch: %s", hipGetErrorString(e));
   return ok();
 }
 

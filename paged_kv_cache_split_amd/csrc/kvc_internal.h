@@ -65,7 +65,15 @@ struct DecodePlan {
   int32_t work_items;
   int32_t pool_pieces;
   int32_t pool_shift;
+  // several query tokens per sequence (MFMA kernel only): tile_groups = 0 for
+  // decode; else the 16-column tiles of (query token, head) pairs are spread
+  // over waves_per_group waves of a work-group and tile_groups groups (grid.z),
+  // and the partial rows hold one set of slots per query token index
+  int32_t tile_groups;
+  int32_t waves_per_group;
+  int32_t max_q;
   int64_t chunk_slots() const { return (int64_t)work_items * (pool_pieces + 1); }
+  int64_t query_slots() const { return tile_groups ? max_q : 1; }
 };
 
 // Dynamic pool: off unless asked for (each piece restarts the prefetch ring,
@@ -83,7 +91,9 @@ inline int32_t default_waves(kvc_dtype kv) { return kv == KVC_FP8_E4M3 ? kDefaul
 
 // Byte offsets inside the decode workspace.  FMA kernel: partial rows
 // [B][Hq][num_partitions] (acc, m, l).  MFMA kernel: partial rows
-// [Hq][B + chunk slots] (acc, m, l), then per sequence {first chunk, chunks},
+// [query slots][Hq][B + chunk slots] (acc, m, l) -- one query slot for decode,
+// max_q with several query tokens per sequence -- then per sequence
+// {first chunk, chunks},
 // then one ticket counter per KV head (zeroed by the launch sequence).
 struct WorkspaceLayout {
   size_t acc, m, l, seginfo, tickets, bytes;
@@ -99,7 +109,7 @@ inline WorkspaceLayout workspace_layout(const DecodePlan& p, int32_t batch, int3
     if (p.num_partitions <= 1) return w;
     rows = (size_t)batch * num_heads * p.num_partitions;
   } else {
-    rows = (size_t)num_heads * ((size_t)batch + (size_t)p.chunk_slots());
+    rows = (size_t)p.query_slots() * num_heads * ((size_t)batch + (size_t)p.chunk_slots());
   }
   w.m = align256(rows * head_dim * sizeof(float));
   w.l = w.m + align256(rows * sizeof(float));
@@ -130,11 +140,13 @@ struct InlineSegments {
 hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, const InlineSegments* segs_inline,
                          int32_t num_segments, const void* k_new, const void* v_new, kvc_dtype in_dtype,
                          int64_t total_rows, hipStream_t stream);
+// q_start / total_q: several query tokens per sequence (plan.tile_groups > 0);
+// NULL / ignored for decode.
 hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q,
-                         kvc_dtype q_dtype, const int32_t* block_table, int32_t max_blocks,
-                         const int32_t* context_lens, int32_t max_context_len, int32_t batch, int32_t num_heads,
-                         float scale, void* out, void* workspace, hipEvent_t ev_start, hipEvent_t ev_end,
-                         hipStream_t stream);
+                         kvc_dtype q_dtype, const int32_t* q_start, int32_t total_q, const int32_t* block_table,
+                         int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+                         int32_t num_heads, float scale, void* out, void* workspace, hipEvent_t ev_start,
+                         hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 }  // namespace kvc

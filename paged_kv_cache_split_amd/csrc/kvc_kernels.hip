@@ -322,6 +322,11 @@ struct DecodeArgs {
   int32_t pool_shift;    // MFMA kernel: pool = last 1/2^pool_shift of each run
   int32_t chunk_slots;   // MFMA kernel: bound on chunk ids, work_items * (pool_pieces + 1)
   float qk_scale;  // softmax scale * log2(e)
+  // several query tokens per sequence (extend kernel; decode: NULL, 1, batch, 1)
+  const int32_t* q_start;   // [batch + 1]: query rows of sequence b are q_start[b] .. q_start[b + 1] - 1
+  int32_t max_q;            // bound on query tokens per sequence
+  int32_t total_q;          // rows of q and out
+  int32_t waves_per_group;  // waves per work-group, one column tile each
 };
 
 template <kvc_dtype QT>
@@ -459,6 +464,15 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
             vx[h2 * 8 + e] = (KV == KVC_F16) ? f16_bits_to_f32(bits) : bf16_bits_to_f32(bits);
           }
         }
+      }
+      // rows past the end (only in the sequence's last block) hold whatever the
+      // slot held before: their weight is zero, and zeroing the values keeps a
+      // NaN pattern there out of the sum
+      const int vrows = t1 - kb * kBS;
+      if (vrows < kBS) {
+#pragma unroll
+        for (int tt = 0; tt < kBS; ++tt)
+          if (tt >= vrows) vx[tt] = 0.0f;
       }
 #pragma unroll
       for (int hh = 0; hh < GMAX; ++hh) {
@@ -604,10 +618,23 @@ __device__ __forceinline__ float sum_over_row_groups(float x) {
 // gives the same softmax; the bound only guards the float range.
 constexpr float kRescaleThreshold = 8.0f;
 
+// Query tokens of sequence b in a multi-token call: q_start[b + 1] - q_start[b],
+// clamped to 0 .. min(max_q, n) so every row index stays inside the arrays.
+// The loads go through the constant address space: scalar when b is uniform.
+__device__ __forceinline__ int query_len(const DecodeArgs& a, int b, int n) {
+  const const_i32_kptr qs = (const_i32_kptr)a.q_start;
+  int ql = qs[b + 1] - qs[b];
+  ql = ql < a.max_q ? ql : a.max_q;
+  ql = ql < n ? ql : n;
+  return ql > 0 ? ql : 0;
+}
+
 // Exclusive scan of the sequences' block counts into LDS: seq_start[b] is the
 // first block of sequence b in the batch's concatenated block list, and
 // seq_start[batch] the total.  Every wave of the decode and every merge
-// work-group computes the same values from context_lens.
+// work-group computes the same values from context_lens.  With several query
+// tokens per sequence (EXT), a sequence with no query token owns no blocks.
+template <bool EXT>
 __device__ __forceinline__ int scan_block_counts(const DecodeArgs& a, int* seq_start, int lane) {
   int carry = 0;
   for (int base = 0; base < a.batch; base += 64) {
@@ -616,6 +643,9 @@ __device__ __forceinline__ int scan_block_counts(const DecodeArgs& a, int* seq_s
     if (bb < a.batch) {
       const int n = attend_len(a.context_lens, bb, a.max_ctx, a.max_blocks);
       nb = n > 0 ? (n + kBS - 1) / kBS : 0;
+      if constexpr (EXT) {
+        if (query_len(a, bb, n) == 0) nb = 0;
+      }
     }
     int incl = nb;
 #pragma unroll
@@ -636,24 +666,43 @@ __device__ __forceinline__ int wave_first_block(int64_t w, int64_t total, int64_
   return (int)((w * total + W - 1) / W);
 }
 
-template <kvc_dtype KV, int D, int PF>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
-  extern __shared__ int seq_start[];   // [batch + 1]
+// The split-K kernel body.  EXT = false: decode, one new query token per
+// sequence, one wave per work item, the G query heads of a KV head are the 16
+// columns of the matrix-core tiles.  EXT = true: several new query tokens per
+// sequence (q_start), each attending causally -- the token at position p sees
+// rows 0..p -- so a column is a (query token, head) pair with its own count of
+// visible rows; the ceil(ql * G / 16) column tiles of a sequence are spread
+// over the waves of a work-group (side by side on one chunk of blocks) and
+// over grid.z.  Decode is the EXT case with one token, compiled apart so its
+// loop carries none of the per-column bookkeeping.
+template <kvc_dtype KV, int D, int PF, bool EXT>
+__device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start) {
   const int w = blockIdx.x, g = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int total = __builtin_amdgcn_readfirstlane(scan_block_counts(a, seq_start, lane));
-  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  // column tile of this wave (EXT)
+  const int ct = EXT ? __builtin_amdgcn_readfirstlane((int)blockIdx.z * a.waves_per_group + (int)(threadIdx.x >> 6))
+                     : 0;
+  int total;
+  if constexpr (EXT) {
+    if (threadIdx.x < 64) scan_block_counts<true>(a, seq_start, lane);
+    __syncthreads();
+    total = __builtin_amdgcn_readfirstlane(seq_start[a.batch]);
+  } else {
+    total = __builtin_amdgcn_readfirstlane(scan_block_counts<false>(a, seq_start, lane));
+    __syncthreads();
+  }
   // never more waves than blocks, so every wave that runs owns >= 1 block
   const int W = a.work_items < total ? a.work_items : total;
   if (w >= W) return;
   // Chunks.  Wave w owns blocks [x0, x1) of this head's list (an even split);
-  // with a dynamic pool, the last 1/2^pool_shift of that range is cut into
-  // KP pieces that go to whichever wave of this head asks first (a ticket
-  // counter), so waves that run fast (their XCD, their share of the memory
-  // system) take work from those that run slow.  Chunk ids follow the list
-  // order: wave w's main chunk is w * (KP + 1), its pieces follow it.  The
-  // pool is used only when every piece of every wave holds >= 1 block.
-  const int KP = (a.pool_pieces > 0 && ((total / W) >> a.pool_shift) >= a.pool_pieces) ? a.pool_pieces : 0;
+  // with a dynamic pool (decode only), the last 1/2^pool_shift of that range
+  // is cut into KP pieces that go to whichever wave of this head asks first (a
+  // ticket counter), so waves that run fast (their XCD, their share of the
+  // memory system) take work from those that run slow.  Chunk ids follow the
+  // list order: wave w's main chunk is w * (KP + 1), its pieces follow it.
+  // The pool is used only when every piece of every wave holds >= 1 block.
+  const int KP =
+      (!EXT && a.pool_pieces > 0 && ((total / W) >> a.pool_shift) >= a.pool_pieces) ? a.pool_pieces : 0;
   const int CPW = KP + 1;
   auto wave_range = [&](int ww, int& r0, int& r1, int& rm) {
     r0 = wave_first_block(ww, total, W);
@@ -672,8 +721,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const int nn = lane & 15, r = lane >> 4;
   const uint32_t koff = k_lane_offset<KV>(lane), voff = v_lane_offset<KV>(nn, r);
   const int G = a.group;
-  const bool head_ok = nn < G;
-  const int h = g * G + nn;
   constexpr int NQK = D / 32;   // QK matrix-core steps (32 dims each)
   constexpr int NDD = D / 16;   // output dim tiles
   const int64_t head_off = (int64_t)g * a.tile_bytes;
@@ -712,17 +759,42 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       const int first = x - sb;                   // first local block of this segment
       const int count = seg_end - x;              // blocks in this segment
       const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
-      if (first == 0 && g == 0 && lane == 0) {
+      if (first == 0 && g == 0 && threadIdx.x == 0 && (!EXT || blockIdx.z == 0)) {
         // the chunk holding a sequence's first block records which chunks hold it
         a.ws_seginfo[2 * b] = c;
         a.ws_seginfo[2 * b + 1] = chunk_of_block(eb - 1) - c + 1;
       }
+      // Columns of this lane.  Decode: head nn of the group, every column sees
+      // the n rows.  EXT: column 16 ct + nn is (query token tok, head hh); the
+      // token sits at position n - ql + tok and sees n - ql + 1 + tok rows.
+      int ql = 1, tok = 0, hh = nn, cnt = count, n_lo = n, q_row = b;
+      bool head_ok = nn < G;
+      if constexpr (EXT) {
+        ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
+        if (ct * 16 >= ql * G) {                  // no column of this sequence in the tile
+          x = seg_end;
+          continue;
+        }
+        const int col = ct * 16 + nn;
+        tok = col / G;
+        hh = col - tok * G;
+        const int q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
+        q_row = q0 + tok;
+        head_ok = tok < ql && q_row >= 0 && q_row < a.total_q;
+        n_lo = n - ql + 1 + (ct * 16) / G;        // fewest rows a column of the tile sees
+        const int tok_hi = min(ql - 1, (ct * 16 + 15) / G);
+        const int nb_hi = (n - ql + 1 + tok_hi + kBS - 1) / kBS - first;   // blocks the tile needs
+        cnt = count < nb_hi ? count : nb_hi;      // <= 0: no row of this segment is visible to the tile
+      }
+      // rows this lane's column sees (padding columns: all n, so they stay finite)
+      const int ncol = head_ok ? n - ql + 1 + tok : n;
+      const int h = g * G + hh;
 
-      // Query operand: for step kk the lane holds 8 dims of head nn, the same
-      // dims its K operand holds for token nn.
+      // Query operand: for step kk the lane holds 8 dims of its column's head,
+      // the same dims its K operand holds for token nn.
       u32x4 qv[NQK];
       {
-        const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_heads + h) * D;
+        const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)q_row * a.num_heads + h) * D;
 #pragma unroll
         for (int kk = 0; kk < NQK; ++kk) {
           int d0;
@@ -736,146 +808,168 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
       float m = kNegInf, l = 0.0f;
 
-      // Physical block of local block j of the segment (scalar load).  Every
-      // prefetch is issued, so the count of loads in flight is the same on
-      // every path; past the end it re-reads the segment's last block, which
-      // the L2 still holds.
-      const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + first);
-      auto phys_of = [&](int j) -> int {
-        j = j < count ? j : count - 1;
-        return clamp_block(row[j], a.num_blocks);
-      };
+      if (cnt > 0) {
+        // Physical block of local block j of the segment (scalar load).  Every
+        // prefetch is issued, so the count of loads in flight is the same on
+        // every path; past the end it re-reads the segment's last block, which
+        // the L2 still holds.
+        const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + first);
+        auto phys_of = [&](int j) -> int {
+          j = j < cnt ? j : cnt - 1;
+          return clamp_block(row[j], a.num_blocks);
+        };
 
-      auto process = [&](const KvBlock<KV, D>& cur, int i) {
-        floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-        float qk = a.qk_scale;
-        float vsc = 1.0f;
-        if constexpr (KV == KVC_FP8_E4M3) {
-          qk *= cur.ks;
-          vsc = cur.vs;
-#pragma unroll
-          for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
-            u32x4 lo, hi;
-            lo[0] = fp8x2_to_bf16x2<false>(cur.k[c2][0]);
-            lo[1] = fp8x2_to_bf16x2<true>(cur.k[c2][0]);
-            lo[2] = fp8x2_to_bf16x2<false>(cur.k[c2][1]);
-            lo[3] = fp8x2_to_bf16x2<true>(cur.k[c2][1]);
-            hi[0] = fp8x2_to_bf16x2<false>(cur.k[c2][2]);
-            hi[1] = fp8x2_to_bf16x2<true>(cur.k[c2][2]);
-            hi[2] = fp8x2_to_bf16x2<false>(cur.k[c2][3]);
-            hi[3] = fp8x2_to_bf16x2<true>(cur.k[c2][3]);
-            s = mfma_qk<KV>(lo, qv[2 * c2], s);
-            s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
-        }
-        // Rows past the sequence's end exist only in its last block (a
-        // wave-uniform test): mask them there, before the max and after exp.
-        const int rem = n - (first + i) * kBS;        // rows of this block inside the sequence
-        float sv[4] = {s[0], s[1], s[2], s[3]};
-        if (rem < kBS) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * r + e >= rem) sv[e] = kNegInf;
-        }
-        // the scale is positive, so the max of the raw scores, scaled, is the
-        // max of the scaled scores; exp2(s * qk - m) is one fma
-        float mx = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * qk;
-        const bool grow = mx > m + kRescaleThreshold;
-        if (__any(grow)) {
-          const float mnew = grow ? mx : m;
-          const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-          l *= alpha;
-#pragma unroll
-          for (int dd = 0; dd < NDD; ++dd) acc[dd] *= alpha;
-          m = mnew;
-        }
-        float pv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m));
-        if (rem < kBS) {
-          // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * r + e >= rem) pv[e] = 0.0f;
-        }
-        l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
-        // ~2^-17 relative), so rounding the weights to 16 bits costs no
-        // accuracy when the weighted values cancel.
-        u32x2 pb, pl;
-        if constexpr (KV == KVC_F16) {
-          pb[0] = pack_f16x2(pv[0], pv[1]);
-          pb[1] = pack_f16x2(pv[2], pv[3]);
-          pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
-          pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
-        } else {
+        auto process = [&](KvBlock<KV, D>& cur, int i) {
+          floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+          float qk = a.qk_scale;
+          float vsc = 1.0f;
           if constexpr (KV == KVC_FP8_E4M3) {
+            qk *= cur.ks;
+            vsc = cur.vs;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] *= vsc;
-          }
-          pb[0] = pack_bf16x2(pv[0], pv[1]);
-          pb[1] = pack_bf16x2(pv[2], pv[3]);
-          pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
-          pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
-        }
-#pragma unroll
-        for (int dd = 0; dd < NDD; ++dd) {
-          u32x2 va;
-          if constexpr (KV == KVC_FP8_E4M3) {
-            va[0] = fp8x2_to_bf16x2<false>(cur.v[dd]);
-            va[1] = fp8x2_to_bf16x2<true>(cur.v[dd]);
+            for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
+              u32x4 lo, hi;
+              lo[0] = fp8x2_to_bf16x2<false>(cur.k[c2][0]);
+              lo[1] = fp8x2_to_bf16x2<true>(cur.k[c2][0]);
+              lo[2] = fp8x2_to_bf16x2<false>(cur.k[c2][1]);
+              lo[3] = fp8x2_to_bf16x2<true>(cur.k[c2][1]);
+              hi[0] = fp8x2_to_bf16x2<false>(cur.k[c2][2]);
+              hi[1] = fp8x2_to_bf16x2<true>(cur.k[c2][2]);
+              hi[2] = fp8x2_to_bf16x2<false>(cur.k[c2][3]);
+              hi[3] = fp8x2_to_bf16x2<true>(cur.k[c2][3]);
+              s = mfma_qk<KV>(lo, qv[2 * c2], s);
+              s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
+            }
           } else {
-            va = cur.v[dd];
+#pragma unroll
+            for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
           }
-          acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
-          acc[dd] = mfma_pv<KV>(va, pl, acc[dd]);
-        }
-      };
+          // Rows some column of the tile may not see exist only near the end of
+          // the sequence (a wave-uniform test): mask them there, before the max
+          // and after exp.  Rows past the sequence's end hold whatever the slot
+          // held before (never written, or a previous owner's rows); zeroing
+          // their values as well keeps a NaN pattern there out of the
+          // accumulator (its weight is zero, but 0 * NaN is NaN).
+          const int t0 = (first + i) * kBS + 4 * r;   // this lane's first row
+          const bool edge = (first + i) * kBS + kBS > n_lo;
+          float sv[4] = {s[0], s[1], s[2], s[3]};
+          if (edge) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (t0 + e >= ncol) sv[e] = kNegInf;
+            const int vr = n - t0;                     // rows of this lane's four inside the sequence
+            if constexpr (KV == KVC_FP8_E4M3) {
+              const uint32_t keep = vr >= 4 ? 0xFFFFFFFFu : (vr <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * vr)));
+#pragma unroll
+              for (int dd = 0; dd < NDD; ++dd) cur.v[dd] &= keep;
+            } else {
+              const uint32_t keep0 = vr >= 2 ? 0xFFFFFFFFu : (vr == 1 ? 0xFFFFu : 0u);
+              const uint32_t keep1 = vr >= 4 ? 0xFFFFFFFFu : (vr == 3 ? 0xFFFFu : 0u);
+#pragma unroll
+              for (int dd = 0; dd < NDD; ++dd) {
+                cur.v[dd][0] &= keep0;
+                cur.v[dd][1] &= keep1;
+              }
+            }
+          }
+          // the scale is positive, so the max of the raw scores, scaled, is the
+          // max of the scaled scores; exp2(s * qk - m) is one fma
+          float mx = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * qk;
+          const bool grow = mx > m + kRescaleThreshold;
+          if (__any(grow)) {
+            const float mnew = grow ? mx : m;
+            // (a column that has seen no row yet keeps m = -inf: alpha 1, not NaN)
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
+            l *= alpha;
+#pragma unroll
+            for (int dd = 0; dd < NDD; ++dd) acc[dd] *= alpha;
+            m = mnew;
+          }
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m));
+          if (edge) {
+            // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (t0 + e >= ncol) pv[e] = 0.0f;
+          }
+          l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+          // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
+          // ~2^-17 relative), so rounding the weights to 16 bits costs no
+          // accuracy when the weighted values cancel.
+          u32x2 pb, pl;
+          if constexpr (KV == KVC_F16) {
+            pb[0] = pack_f16x2(pv[0], pv[1]);
+            pb[1] = pack_f16x2(pv[2], pv[3]);
+            pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
+            pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
+          } else {
+            if constexpr (KV == KVC_FP8_E4M3) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+            }
+            pb[0] = pack_bf16x2(pv[0], pv[1]);
+            pb[1] = pack_bf16x2(pv[2], pv[3]);
+            pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
+            pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
+          }
+#pragma unroll
+          for (int dd = 0; dd < NDD; ++dd) {
+            u32x2 va;
+            if constexpr (KV == KVC_FP8_E4M3) {
+              va[0] = fp8x2_to_bf16x2<false>(cur.v[dd]);
+              va[1] = fp8x2_to_bf16x2<true>(cur.v[dd]);
+            } else {
+              va = cur.v[dd];
+            }
+            acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
+            acc[dd] = mfma_pv<KV>(va, pl, acc[dd]);
+          }
+        };
 
-      // Ring of PF + 1 register buffers: block i + PF is in flight while block
-      // i is consumed.  The ring index is a compile-time constant after
-      // unrolling.
-      KvBlock<KV, D> buf[PF + 1];
-      auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
-        const int64_t o = (int64_t)ph * block_stride + head_off;
-        load_block<KV, D>(dst, a.k + o, a.v + o, koff, voff);
-        if constexpr (KV == KVC_FP8_E4M3) {
-          dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
-          dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
+        // Ring of PF + 1 register buffers: block i + PF is in flight while block
+        // i is consumed.  The ring index is a compile-time constant after
+        // unrolling.
+        KvBlock<KV, D> buf[PF + 1];
+        auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
+          const int64_t o = (int64_t)ph * block_stride + head_off;
+          load_block<KV, D>(dst, a.k + o, a.v + o, koff, voff);
+          if constexpr (KV == KVC_FP8_E4M3) {
+            dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
+            dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
+          }
+        };
+#pragma unroll
+        for (int j = 0; j < PF; ++j) fetch(buf[j], phys_of(j));
+        int ph_next = phys_of(PF);                  // id of the next block to prefetch, one step ahead
+        // Whole turns of the ring first, with no exit inside a turn: an exit that
+        // led back to the loop head would leave a load in flight there and force
+        // a full wait for it at the head of every turn.
+        int i0 = 0;
+        for (; i0 + PF + 1 <= cnt; i0 += PF + 1) {
+#pragma unroll
+          for (int j = 0; j <= PF; ++j) {
+            const int i = i0 + j;
+            const int ph = ph_next;
+            ph_next = phys_of(i + PF + 1);
+            fetch(buf[(j + PF) % (PF + 1)], ph);
+            process(buf[j], i);
+          }
         }
-      };
+        // The next piece is asked for now, so the ticket's round trip overlaps
+        // the last blocks of the chunk.
+        if (KP != 0 && seg_end == xb && lane == 0) t_next = atomicAdd(a.ws_ticket + g, 1);
+        // the last, partial turn
 #pragma unroll
-      for (int j = 0; j < PF; ++j) fetch(buf[j], phys_of(j));
-      int ph_next = phys_of(PF);                  // id of the next block to prefetch, one step ahead
-      // Whole turns of the ring first, with no exit inside a turn: an exit that
-      // led back to the loop head would leave a load in flight there and force
-      // a full wait for it at the head of every turn.
-      int i0 = 0;
-      for (; i0 + PF + 1 <= count; i0 += PF + 1) {
-#pragma unroll
-        for (int j = 0; j <= PF; ++j) {
+        for (int j = 0; j < PF; ++j) {
           const int i = i0 + j;
+          if (i >= cnt) break;
           const int ph = ph_next;
           ph_next = phys_of(i + PF + 1);
           fetch(buf[(j + PF) % (PF + 1)], ph);
           process(buf[j], i);
         }
-      }
-      // The next piece is asked for now, so the ticket's round trip overlaps
-      // the last blocks of the chunk.
-      if (KP != 0 && seg_end == xb && lane == 0) t_next = atomicAdd(a.ws_ticket + g, 1);
-      // the last, partial turn
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int i = i0 + j;
-        if (i >= count) break;
-        const int ph = ph_next;
-        ph_next = phys_of(i + PF + 1);
-        fetch(buf[(j + PF) % (PF + 1)], ph);
-        process(buf[j], i);
       }
       // l over the head's four lane groups
       l = sum_over_row_groups(l);
@@ -885,7 +979,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
           const float inv = 1.0f / l;
 #pragma unroll
           for (int dd = 0; dd < NDD; ++dd) {
-            const int64_t o = ((int64_t)b * a.num_heads + h) * D + 16 * dd + 4 * r;
+            const int64_t o = ((int64_t)q_row * a.num_heads + h) * D + 16 * dd + 4 * r;
             u32x2 wv;
             if constexpr (KV == KVC_F16) {
               wv[0] = pack_f16x2(acc[dd][0] * inv, acc[dd][1] * inv);
@@ -897,9 +991,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
             *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
           }
         } else {
-          // partial of (sequence b, chunk c): slot b + c is unique, since every
-          // segment boundary advances the sequence, the chunk, or both
-          const int64_t rr = (int64_t)h * slots + b + c;
+          // partial of (sequence b, chunk c) for this column: slot b + c is
+          // unique, since every segment boundary advances the sequence, the
+          // chunk, or both (EXT: one set of slots per query token index)
+          const int64_t rr = ((EXT ? (int64_t)tok * a.num_heads : 0) + h) * slots + b + c;
 #pragma unroll
           for (int dd = 0; dd < NDD; ++dd)
             *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[dd];
@@ -925,26 +1020,48 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
+template <kvc_dtype KV, int D, int PF>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+  extern __shared__ int seq_start[];   // [batch + 1]
+  attend_mfma<KV, D, PF, false>(a, seq_start);
+}
+
+// grid (work items, KV heads, column-tile groups), waves_per_group waves each
+template <kvc_dtype KV, int D, int PF>
+__global__ __launch_bounds__(256) void extend_mfma_kernel(DecodeArgs a) {
+  extern __shared__ int seq_start[];   // [batch + 1]
+  attend_mfma<KV, D, PF, true>(a, seq_start);
+}
+
 // Merge of the MFMA kernel's partials: one work-group per (KV head,
-// sequence), one thread per (query head of the group, 4 output dims).  The
-// triples of waves w_first .. w_first + np - 1 (slots b + w) are folded in a
-// single pass with the online-softmax recurrence, so every load can be
-// issued ahead of its use.
-template <kvc_dtype QT, int D>
+// sequence[, query token]), one thread per (query head of the group, 4 output
+// dims).  The triples of chunks c_first .. c_first + np - 1 (slots b + c) are
+// folded in a single pass with the online-softmax recurrence, so every load
+// can be issued ahead of its use.  EXT: a chunk whose rows a query token does
+// not see left an empty triple (m = -inf, l = 0), skipped.
+template <kvc_dtype QT, int D, bool EXT>
 __global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
+  const int tok = EXT ? (int)blockIdx.z : 0;
   const int t = threadIdx.x;
   constexpr int COLS = D / 4;
   const int hh = t / COLS, c = t % COLS;
   if (hh >= a.group) return;
-  if (attend_len(a.context_lens, b, a.max_ctx, a.max_blocks) <= 0) return;
+  const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
+  if (n <= 0) return;
+  int q_row = b;
+  if constexpr (EXT) {
+    if (tok >= query_len(a, b, n)) return;
+    q_row = a.q_start[b] + tok;
+    if (q_row < 0 || q_row >= a.total_q) return;
+  }
   const int c_first = a.ws_seginfo[2 * b];
   int np = a.ws_seginfo[2 * b + 1];
   if (np <= 1) return;                         // one chunk held the whole sequence
   if (c_first < 0 || c_first >= a.chunk_slots) return;
   if (np > a.chunk_slots - c_first) np = a.chunk_slots - c_first;
   const int h = g * a.group + hh;
-  const int64_t row0 = (int64_t)h * (a.batch + a.chunk_slots) + b + c_first;
+  const int64_t row0 = ((EXT ? (int64_t)tok * a.num_heads : 0) + h) * (a.batch + a.chunk_slots) + b + c_first;
   float M = kNegInf, L = 0.0f;
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
@@ -952,6 +1069,9 @@ __global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
     const float m = a.ws_m[row0 + p];
     const float l = a.ws_l[row0 + p];
     const floatx4 v = *reinterpret_cast<const floatx4*>(a.ws_acc + (row0 + p) * D + 4 * c);
+    if constexpr (EXT) {
+      if (m == kNegInf) continue;
+    }
     const float Mn = fmaxf(M, m);
     const float sa = __builtin_amdgcn_exp2f(M - Mn), sb = __builtin_amdgcn_exp2f(m - Mn);
     acc = acc * sa + v * sb;
@@ -959,7 +1079,7 @@ __global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
     M = Mn;
   }
   const float inv = 1.0f / L;
-  const int64_t o = ((int64_t)b * a.num_heads + h) * D + 4 * c;
+  const int64_t o = ((int64_t)q_row * a.num_heads + h) * D + 4 * c;
 #pragma unroll
   for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, acc[e] * inv);
 }
@@ -1043,9 +1163,10 @@ __global__ __launch_bounds__(64) void zero_ints_kernel(int* p, int n) {
   for (int i = threadIdx.x; i < n; i += 64) p[i] = 0;
 }
 
+// tile_groups: 0 for decode; else the extend kernel's grid.z
 template <kvc_dtype KV, kvc_dtype QT>
-hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merge, hipEvent_t ev0, hipEvent_t ev1,
-                               hipStream_t s) {
+hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merge, int tile_groups, hipEvent_t ev0,
+                               hipEvent_t ev1, hipStream_t s) {
   hipError_t e = hipSuccess;
   const size_t scan_lds = (size_t)(a.batch + 1) * sizeof(int);
   if (kernel == 1) {
@@ -1069,15 +1190,27 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, s, a.ws_ticket, a.num_kv_heads);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
-    dim3 grid(a.work_items, a.num_kv_heads);
-    if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64, PF>), grid, dim3(64), scan_lds, s, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128, PF>), grid, dim3(64), scan_lds, s, a);
+    const int threads = ((a.group * (D / 4) + 63) / 64) * 64;   // <= 16 heads * 32 columns = 512
+    if (tile_groups == 0) {
+      dim3 grid(a.work_items, a.num_kv_heads);
+      if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64, PF>), grid, dim3(64), scan_lds, s, a);
+      else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128, PF>), grid, dim3(64), scan_lds, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+      dim3 mgrid(a.num_kv_heads, a.batch);
+      if (D == 64) hipLaunchKernelGGL((merge_segments_kernel<QT, 64, false>), mgrid, dim3(threads), 0, s, a);
+      else hipLaunchKernelGGL((merge_segments_kernel<QT, 128, false>), mgrid, dim3(threads), 0, s, a);
+      return hipGetLastError();
+    }
+    dim3 grid(a.work_items, a.num_kv_heads, tile_groups);
+    dim3 block(64 * a.waves_per_group);
+    if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, PF>), grid, block, scan_lds, s, a);
+    else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, PF>), grid, block, scan_lds, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
-    dim3 mgrid(a.num_kv_heads, a.batch);
-    const int threads = ((a.group * (D / 4) + 63) / 64) * 64;   // <= 16 heads * 32 columns = 512
-    if (D == 64) hipLaunchKernelGGL((merge_segments_kernel<QT, 64>), mgrid, dim3(threads), 0, s, a);
-    else hipLaunchKernelGGL((merge_segments_kernel<QT, 128>), mgrid, dim3(threads), 0, s, a);
+    dim3 mgrid(a.num_kv_heads, a.batch, a.max_q);
+    if (D == 64) hipLaunchKernelGGL((merge_segments_kernel<QT, 64, true>), mgrid, dim3(threads), 0, s, a);
+    else hipLaunchKernelGGL((merge_segments_kernel<QT, 128, true>), mgrid, dim3(threads), 0, s, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
@@ -1134,9 +1267,10 @@ hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, co
 }
 
 hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q, kvc_dtype q_dtype,
-                         const int32_t* block_table, int32_t max_blocks, const int32_t* context_lens,
-                         int32_t max_context_len, int32_t batch, int32_t num_heads, float scale, void* out,
-                         void* workspace, hipEvent_t ev_start, hipEvent_t ev_end, hipStream_t stream) {
+                         const int32_t* q_start, int32_t total_q, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* context_lens, int32_t max_context_len, int32_t batch, int32_t num_heads,
+                         float scale, void* out, void* workspace, hipEvent_t ev_start, hipEvent_t ev_end,
+                         hipStream_t stream) {
   DecodeArgs a;
   const int64_t tb = tile_bytes(pool);
   const int64_t layer_bytes = (int64_t)pool.num_blocks * pool.num_kv_heads * tb;
@@ -1163,6 +1297,10 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   a.pool_shift = plan.pool_shift;
   a.chunk_slots = (int32_t)plan.chunk_slots();
   a.qk_scale = scale * kLog2e;
+  a.q_start = q_start;
+  a.max_q = plan.tile_groups ? plan.max_q : 1;
+  a.total_q = plan.tile_groups ? total_q : batch;
+  a.waves_per_group = plan.tile_groups ? plan.waves_per_group : 1;
   const bool merge = plan.kernel == 2 || plan.num_partitions > 1;
   const WorkspaceLayout wl = workspace_layout(plan, batch, num_heads, pool.num_kv_heads, pool.head_dim);
   char* w = static_cast<char*>(workspace);
@@ -1174,13 +1312,13 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   const int D = pool.head_dim;
   switch (pool.dtype) {
     case KVC_F32:
-      return launch_decode_typed<KVC_F32, KVC_F32>(a, D, plan.kernel, merge, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_F32, KVC_F32>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
     case KVC_F16:
-      return launch_decode_typed<KVC_F16, KVC_F16>(a, D, plan.kernel, merge, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_F16, KVC_F16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
     case KVC_BF16:
-      return launch_decode_typed<KVC_BF16, KVC_BF16>(a, D, plan.kernel, merge, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_BF16, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
     case KVC_FP8_E4M3:
-      return launch_decode_typed<KVC_FP8_E4M3, KVC_BF16>(a, D, plan.kernel, merge, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_FP8_E4M3, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
   }
   (void)q_dtype;
   return hipErrorInvalidValue;

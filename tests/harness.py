@@ -53,11 +53,15 @@ def read_pools(cache):
 
 # -- GPU side -------------------------------------------------------------------
 
-def gpu_setup(wl, values, device="cuda"):
-    """Build the cache and the history through libkvc; returns the KVCache."""
+def gpu_setup(wl, values, device="cuda", pool_fill=None):
+    """Build the cache and the history through libkvc; returns the KVCache.
+    ``pool_fill``: a byte value written over both pools before anything else."""
     from paged_kv_cache_split_amd import KVCache
     cache = KVCache(wl.num_layers, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.kv_dtype,
                     block_size=wl.block_size, device=device, free_order=wl.free_order)
+    if pool_fill is not None:
+        cache.k_pool.fill_(pool_fill)
+        cache.v_pool.fill_(pool_fill)
     k_hist = values["k_hist"].to(device)
     v_hist = values["v_hist"].to(device)
     row = 0
@@ -115,7 +119,7 @@ def oracle_run(wl, values):
             assert status == 0
             row += t
     seqs = list(range(wl.batch))
-    status, slots, cow = st.append(seqs, [1] * wl.batch, to_bits(values["k_new"], wl.new_dtype),
+    status, slots, cow = st.append(seqs, [int(x) for x in wl.q_lens], to_bits(values["k_new"], wl.new_dtype),
                                    to_bits(values["v_new"], wl.new_dtype))
     assert status == 0
     return st
@@ -130,6 +134,39 @@ def oracle_decode(st, wl, values, seqs=None, layer=0):
     for i, b in enumerate(seqs):
         k, v = st.gather(b, layer)
         out[i] = decode_attention(q[b], k, v, wl.scale)
+    return out
+
+
+def query_start(wl):
+    """Exclusive prefix sum of the step's new tokens per sequence: [B + 1]."""
+    return np.concatenate([[0], np.cumsum(wl.q_lens)]).astype(np.int32)
+
+
+def gpu_extend_step(cache, wl, values, device="cuda", work_items=0):
+    """A step with several new tokens per sequence: append them all, export the
+    tables, then attention of every new token (causal among them)."""
+    seqs = list(range(wl.batch))
+    cache.append(seqs, values["k_new"].to(device).contiguous(), values["v_new"].to(device).contiguous(),
+                 n_new=[int(x) for x in wl.q_lens])
+    bt, cl = cache.export_tables(seqs)
+    qs = torch.from_numpy(query_start(wl)).to(device)
+    q = values["q"].to(device).contiguous()
+    o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=work_items)
+    return o, bt, cl, qs
+
+
+def oracle_extend(st, wl, values, seqs=None, layer=0):
+    """fp64 outputs [Q, Hq, D] of every new token from the oracle store's stored
+    values (rows of sequence b at query_start[b] ..)."""
+    from oracle.attention import extend_attention
+    q = to_f64(values["q"])
+    qs = query_start(wl)
+    out = np.full((wl.total_queries, wl.num_heads, wl.head_dim), np.nan)
+    for b in (range(wl.batch) if seqs is None else seqs):
+        if qs[b + 1] == qs[b]:
+            continue
+        k, v = st.gather(b, layer)
+        out[qs[b]:qs[b + 1]] = extend_attention(q[qs[b]:qs[b + 1]], k, v, wl.scale)
     return out
 
 

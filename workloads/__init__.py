@@ -6,5 +6,5 @@ values rounded to the storage dtype.  It holds none of the method's
 arithmetic, and both the HIP path's callers and the oracle's callers take
 their inputs from it.
 """
-from .configs import (CONFIGS, SMALL, Workload, custom_workload, make_values,  # noqa: F401
-                      make_workload, setup_ops)
+from .configs import (CONFIGS, EXTEND_CONFIGS, EXTEND_SMALL, SMALL, Workload, custom_workload,  # noqa: F401
+                      make_extend_workload, make_values, make_workload, setup_ops)

@@ -43,6 +43,22 @@ class Workload:
     num_layers: int = 1
     block_size: int = BLOCK_SIZE
     extra: dict = field(default_factory=dict)
+    query_lens: np.ndarray | None = None   # [B] new tokens per sequence in the step (None: 1 each, decode)
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        """New tokens each sequence appends and queries in the step."""
+        if self.query_lens is None:
+            return np.ones(self.batch, dtype=np.int64)
+        return np.asarray(self.query_lens, dtype=np.int64)
+
+    @property
+    def total_queries(self) -> int:
+        return int(self.q_lens.sum())
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.q_lens.max()) if self.batch else 0
 
     @property
     def scale(self) -> float:
@@ -51,8 +67,8 @@ class Workload:
 
     @property
     def attend_lens(self) -> np.ndarray:
-        """Tokens each sequence attends in the step: L_b + 1 (the appended one)."""
-        return self.context_lens + 1
+        """Rows each sequence holds in the step: L_b plus its appended token(s)."""
+        return self.context_lens + self.q_lens
 
     @property
     def history_rows(self) -> int:
@@ -70,11 +86,13 @@ def _blocks(n: int) -> int:
     return (n + BLOCK_SIZE - 1) // BLOCK_SIZE
 
 
-def _exact_pool(lens, shared_prefix: int) -> int:
+def _exact_pool(lens, shared_prefix: int, q_lens=None) -> int:
     lens = np.asarray(lens)
+    q_lens = np.ones(len(lens), dtype=np.int64) if q_lens is None else np.asarray(q_lens)
     if shared_prefix:
-        return _blocks(shared_prefix) + int(np.sum([_blocks(l + 1) - _blocks(shared_prefix) for l in lens]))
-    return int(np.sum([_blocks(l + 1) for l in lens]))
+        return _blocks(shared_prefix) + int(np.sum([_blocks(l + q) - _blocks(shared_prefix)
+                                                    for l, q in zip(lens, q_lens)]))
+    return int(np.sum([_blocks(l + q) for l, q in zip(lens, q_lens)]))
 
 
 def _lengths(cid: int, rng, p) -> np.ndarray:
@@ -145,18 +163,69 @@ def make_workload(cid: int, seed: int | None = None, small: bool = False, **over
 
 
 def custom_workload(batch, num_heads, num_kv_heads, head_dim, kv_dtype, context_lens,
-                    q_dtype=None, num_blocks=None, seed=0, shared_prefix=0, name="custom") -> Workload:
-    """A workload of any shape (used by edge-case and sweep tests)."""
+                    q_dtype=None, num_blocks=None, seed=0, shared_prefix=0, name="custom",
+                    query_lens=None) -> Workload:
+    """A workload of any shape (used by edge-case and sweep tests).
+    ``query_lens``: new tokens per sequence in the step (default 1 each)."""
     lens = np.asarray(context_lens, dtype=np.int64)
     rng = np.random.default_rng(seed)
-    pool = num_blocks or _exact_pool(lens, shared_prefix)
+    qls = None if query_lens is None else np.asarray(query_lens, dtype=np.int64)
+    pool = num_blocks or _exact_pool(lens, shared_prefix, qls)
     free_order = rng.permutation(pool).astype(np.int32)
     q_dtype = q_dtype or ("bf16" if kv_dtype == "fp8" else kv_dtype)
     return Workload(name=name, batch=batch, num_heads=num_heads, num_kv_heads=num_kv_heads,
                     head_dim=head_dim, q_dtype=q_dtype, kv_dtype=kv_dtype,
                     new_dtype=("bf16" if kv_dtype == "fp8" else kv_dtype),
                     context_lens=lens, shared_prefix=int(shared_prefix), num_blocks=int(pool),
-                    free_order=free_order, seed=seed)
+                    free_order=free_order, seed=seed, query_lens=qls)
+
+
+# Steps with several new tokens per sequence.  "verify": the target model's
+# pass over gamma = 5 draft tokens of speculative decoding ("LLM推理优化实战…"
+# §4.2 uses gamma = 5) on the 70B-shaped GQA layer's batch; "prefill": page 5
+# PART 04's attention benchmark shape (batch 1, 16 heads, head_dim 64, fp16,
+# causal, 2048 tokens) as one uncached prompt written into the paged cache;
+# "chunk": the last 512-token chunk of a 4096-token prompt (PART 04's long-
+# input group) over its first 3584 tokens cached, on the 70B-shaped layer.
+EXTEND_CONFIGS = {
+    "verify": dict(name="speculative verify, 5 draft tokens, 70B-shaped GQA bf16, B64, 64/8 heads, D128, "
+                        "L lognormal(median 4096) in [128, 8192]",
+                   batch=64, num_heads=64, num_kv_heads=8, head_dim=128, kv_dtype="bf16",
+                   lens=("lognormal", 4096, 1.0, 128, 8192), q=("const", 5)),
+    "prefill": dict(name="causal prefill of a 2048-token prompt into the paged cache, fp16, B1, 16/16 heads, D64",
+                    batch=1, num_heads=16, num_kv_heads=16, head_dim=64, kv_dtype="f16",
+                    lens=("const", 0), q=("const", 2048)),
+    "chunk": dict(name="chunked prefill, 512-token chunk over 3584 cached, 70B-shaped GQA bf16, B4, 64/8 heads, D128",
+                  batch=4, num_heads=64, num_kv_heads=8, head_dim=128, kv_dtype="bf16",
+                  lens=("const", 3584), q=("const", 512)),
+}
+
+EXTEND_SMALL = {
+    "verify": dict(EXTEND_CONFIGS["verify"], name="speculative verify (scaled down), B8, 64/8 heads, D128",
+                   batch=8, lens=("lognormal", 300, 1.0, 1, 1200)),
+    "prefill": dict(EXTEND_CONFIGS["prefill"], name="causal prefill (scaled down), fp16, B1, 16/16 heads, D64, 160 tokens",
+                    q=("const", 160)),
+    "chunk": dict(EXTEND_CONFIGS["chunk"], name="chunked prefill (scaled down), B2, 64/8 heads, D128, 64 over 200",
+                  batch=2, lens=("const", 200), q=("const", 64)),
+}
+
+EXTEND_SEEDS = {"verify": 3, "prefill": 6, "chunk": 7}
+
+
+def make_extend_workload(kind: str, seed: int | None = None, small: bool = False) -> Workload:
+    """Build a multi-token step workload ("verify", "prefill" or "chunk")."""
+    p = dict((EXTEND_SMALL if small else EXTEND_CONFIGS)[kind])
+    seed = EXTEND_SEEDS[kind] if seed is None else seed
+    rng = np.random.default_rng(seed)
+    lens = _lengths(0, rng, p)
+    qls = _lengths(0, rng, dict(p, lens=p["q"]))
+    pool = _exact_pool(lens, 0, qls)
+    free_order = rng.permutation(pool).astype(np.int32)
+    kv = p["kv_dtype"]
+    return Workload(name=p["name"], batch=p["batch"], num_heads=p["num_heads"], num_kv_heads=p["num_kv_heads"],
+                    head_dim=p["head_dim"], q_dtype=("bf16" if kv == "fp8" else kv), kv_dtype=kv,
+                    new_dtype=("bf16" if kv == "fp8" else kv), context_lens=lens, shared_prefix=0,
+                    num_blocks=int(pool), free_order=free_order, seed=seed, query_lens=qls)
 
 
 def setup_ops(wl: Workload):
@@ -198,7 +267,8 @@ def make_values(wl: Workload, device="cpu"):
     """Tensors of the workload, drawn on ``device`` (torch generator seeded with wl.seed).
 
     k_hist, v_hist: [layers, history_rows, Hkv, D] (new_dtype), rows in setup-op order
-    q: [B, Hq, D] (q_dtype); k_new, v_new: [layers, B, Hkv, D] (new_dtype)
+    q: [Q, Hq, D] (q_dtype); k_new, v_new: [layers, Q, Hkv, D] (new_dtype), where Q
+    is the step's new tokens (B for decode; rows of sequence b follow those of b - 1)
     """
     import torch
     gen = torch.Generator(device=device)
@@ -206,7 +276,8 @@ def make_values(wl: Workload, device="cpu"):
     L, T, H, D = wl.num_layers, wl.history_rows, wl.num_kv_heads, wl.head_dim
     k_hist = _randn((L, T, H, D), wl.new_dtype, gen, device)
     v_hist = _randn((L, T, H, D), wl.new_dtype, gen, device)
-    q = _randn((wl.batch, wl.num_heads, D), wl.q_dtype, gen, device)
-    k_new = _randn((L, wl.batch, H, D), wl.new_dtype, gen, device)
-    v_new = _randn((L, wl.batch, H, D), wl.new_dtype, gen, device)
+    Q = wl.total_queries
+    q = _randn((Q, wl.num_heads, D), wl.q_dtype, gen, device)
+    k_new = _randn((L, Q, H, D), wl.new_dtype, gen, device)
+    v_new = _randn((L, Q, H, D), wl.new_dtype, gen, device)
     return dict(k_hist=k_hist, v_hist=v_hist, q=q, k_new=k_new, v_new=v_new)
