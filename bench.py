@@ -10,6 +10,11 @@ same slots.
 Prints ONE JSON line: value = KV-read GB/s (distinct K/V bytes the step
 attends / step time), plus us_per_step, the split kernel's roofline (HIP
 events on the launch stream) and the fp64 CPU oracle timed on a sample.
+
+``--extend verify|prefill|chunk`` times a step with several new tokens per
+sequence instead (kvc_append of all of them, then kvc_extend_attention), with
+its own metric line; the roofline is HBM or the matrix cores, whichever the
+workload's flops per algorithmic byte puts it under.
 """
 from __future__ import annotations
 
@@ -40,6 +45,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate", action="store_true", help="also time the plain copy kernel (2 GiB)")
+    p.add_argument("--extend", choices=["verify", "prefill", "chunk"], default=None,
+                   help="time a step with several new tokens per sequence instead of decode: the verify pass "
+                        "of speculative decoding (5 draft tokens, 70B-shaped batch), a 2048-token causal "
+                        "prefill, or a 512-token prefill chunk over 3584 cached tokens")
     return p.parse_args()
 
 
@@ -119,12 +128,172 @@ def cpu_baseline(wl, values, budget_s):
                       f"os.cpu_count()={os.cpu_count()}"}
 
 
+EXTEND_METRIC = "paged multi-token attention (causal among the new tokens): µs/step, KV-read GB/s, TFLOP/s"
+PEAK_MFMA_TFLOPS = 2500.0   # dense bf16 / fp16 matrix-core peak
+
+
+def extend_work(wl):
+    """Algorithmic bytes and flops of one multi-token attention call: distinct
+    K/V rows once, q, out, tables; 4 * D flops per (query token, head, visible
+    row) -- QK^T and PV, counted on the definition (no causal padding)."""
+    eb = ELEM_BYTES[wl.kv_dtype]
+    rows = int(wl.attend_lens.sum())
+    kv = 2 * rows * wl.num_kv_heads * wl.head_dim * eb
+    scales = 2 * 4 * wl.num_blocks * wl.num_kv_heads if wl.kv_dtype == "fp8" else 0
+    q = wl.total_queries * wl.num_heads * wl.head_dim * ELEM_BYTES[wl.q_dtype]
+    tables = 4 * sum((int(n) + 15) // 16 for n in wl.attend_lens) + 8 * wl.batch + 4
+    visible = sum(int(ql) * (int(n) - int(ql)) + int(ql) * (int(ql) + 1) // 2
+                  for n, ql in zip(wl.attend_lens, wl.q_lens))
+    flops = 4 * wl.head_dim * wl.num_heads * visible
+    return dict(kv=kv, bytes=kv + scales + 2 * q + tables, flops=flops)
+
+
+def cpu_baseline_extend(wl, values, budget_s):
+    """The fp64 oracle's multi-token attention on sequences of the same
+    workload, in order, until the budget is spent; reported in TFLOP/s of the
+    definition's work."""
+    import numpy as np
+    import torch
+    from oracle.attention import extend_attention
+    qs = np.concatenate([[0], np.cumsum(wl.q_lens)])
+    lens = [int(x) for x in wl.context_lens]
+    q = values["q"].to(torch.float64).cpu().numpy()
+    done_flops, n_seq, wall, cpu, row = 0, 0, 0.0, 0.0, 0
+    for b in range(wl.batch):
+        hist = slice(row, row + lens[b])
+        row += lens[b]
+        k = torch.cat([values["k_hist"][0, hist], values["k_new"][0, qs[b]:qs[b + 1]]]).to(torch.float64).cpu()
+        v = torch.cat([values["v_hist"][0, hist], values["v_new"][0, qs[b]:qs[b + 1]]]).to(torch.float64).cpu()
+        t0, c0 = time.perf_counter(), time.process_time()
+        extend_attention(q[qs[b]:qs[b + 1]], k.numpy(), v.numpy(), wl.scale)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        n_seq += 1
+        ql, n = int(wl.q_lens[b]), lens[b] + int(wl.q_lens[b])
+        done_flops += 4 * wl.head_dim * wl.num_heads * (ql * (n - ql) + ql * (ql + 1) // 2)
+        if wall > budget_s:
+            break
+    return {"value": round(done_flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {wl.batch} sequences of the same workload, fp64 NumPy, {wall:.1f} s wall; "
+                      f"os.cpu_count()={os.cpu_count()}"}
+
+
+def run_extend(args):
+    import numpy as np
+    import torch
+    import paged_kv_cache_split_amd as kvc
+    from workloads import make_extend_workload, make_values, setup_ops
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    wl = make_extend_workload(args.extend, seed=args.seed)
+    print(f"[bench] extend {args.extend}: {wl.name}; blocks {wl.num_blocks}, {wl.total_queries} queries",
+          file=sys.stderr, flush=True)
+    values = make_values(wl, dev)
+    cache = kvc.KVCache(wl.num_layers, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.kv_dtype, device=dev,
+                        free_order=wl.free_order)
+    row = 0
+    for op in setup_ops(wl):
+        if op[0] == "add":
+            cache.add_seq(op[1], op[2])
+        elif op[0] == "append":
+            t = int(sum(op[2]))
+            if t:
+                cache.append(op[1], values["k_hist"][:, row:row + t].contiguous(),
+                             values["v_hist"][:, row:row + t].contiguous(), n_new=op[2])
+            row += t
+    seqs = list(range(wl.batch))
+    hist_len = [int(x) for x in wl.context_lens]
+    n_new = [int(x) for x in wl.q_lens]
+    k_new, v_new, q = values["k_new"].contiguous(), values["v_new"].contiguous(), values["q"].contiguous()
+    cache.append(seqs, k_new, v_new, n_new=n_new)
+    bt, cl = cache.export_tables(seqs)
+    for s_, L in zip(seqs, hist_len):
+        cache.truncate(s_, L)
+    qs = torch.from_numpy(np.concatenate([[0], np.cumsum(wl.q_lens)]).astype(np.int32)).to(dev)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, kvc.extend_workspace_bytes(wl.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
+                                                         wl.max_query_len, args.work_items)),
+                     dtype=torch.uint8, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+
+    def step(events=None):
+        cache.append(seqs, k_new, v_new, n_new=n_new)
+        cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws,
+                     work_items=args.work_items, split_events=events)
+        for s_, L in zip(seqs, hist_len):
+            cache.truncate(s_, L)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    split_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    split_avg_ms = sum(split_ms) / len(split_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    w = extend_work(wl)
+    intensity = w["flops"] / w["bytes"]
+    mfma_bound = intensity > PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved = w["flops"] / (split_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_MFMA_TFLOPS, 4)}
+    else:
+        achieved = w["bytes"] / (split_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": None, "kernel": "multi-token split-K kernel", "avg_launch_us": round(split_avg_ms * 1e3, 2),
+                 "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
+                 "algorithmic_bytes_per_launch": w["bytes"], "algorithmic_flops_per_launch": w["flops"],
+                 "intensity_flop_per_byte": round(intensity, 1)})
+    kv_gbs = w["kv"] / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": EXTEND_METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "tflops_step": round(w["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+        "pct_of_peak_hbm": round(100.0 * kv_gbs / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block placement)",
+        "config": {"workload": wl.name, "extend": args.extend, "batch": wl.batch, "num_heads": wl.num_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "new_tokens": wl.total_queries, "rows_attended": int(wl.attend_lens.sum()), "kv_bytes": w["kv"],
+                   "work_items": args.work_items or "auto", "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_extend(wl, values, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path here is single-GPU by design "
               f"(--gpus {args.gpus} requested); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.extend:
+        run_extend(args)
+        return
     import torch
     import paged_kv_cache_split_amd as kvc
     from workloads import make_values, make_workload, setup_ops

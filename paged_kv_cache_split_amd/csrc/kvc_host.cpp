@@ -296,10 +296,14 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
 // ceil(max_q * G / 16) tiles of 16 (query token, head) pairs; up to 4 tiles
 // share a work-group (one wave each, side by side on one chunk of blocks, so
 // the chunk's tiles are read from HBM once and served to the others from
-// cache), the rest go to grid.z.  The waves per KV head are divided among the
-// tile groups so a launch keeps about one wave per SIMD, and capped so the
-// partials stay within kExtendRowBudget rows per query head.
+// cache), the rest go to grid.z.  A wave uses the whole register file of its
+// SIMD, so a CU holds 4 / waves_per_group work-groups; the default launches
+// two such rounds over the chip, divided among the KV heads and tile groups
+// (measured on the verify and prefill workloads: one round leaves too few
+// blocks in flight, more rounds gain nothing), capped so the partials stay
+// within kExtendRowBudget rows per query head.
 constexpr int64_t kExtendRowBudget = 1 << 16;
+constexpr int64_t kExtendCUs = 256;   // fixed (not queried), so results do not depend on the device
 constexpr int32_t kMaxQueryTokens = 4096;
 
 bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t max_q, int kv,
@@ -316,9 +320,9 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   plan->waves_per_group = std::min(4, tiles);
   plan->tile_groups = (tiles + plan->waves_per_group - 1) / plan->waves_per_group;
   plan->max_q = max_q;
-  const int32_t waves = kv < 0 ? std::max(kvc::kDefaultWaves16, kvc::kDefaultWavesFp8)
-                               : kvc::default_waves(static_cast<kvc_dtype>(kv));
-  int64_t w = waves / ((int64_t)num_kv_heads * plan->waves_per_group * plan->tile_groups);
+  (void)kv;
+  const int64_t groups_per_round = (int64_t)kExtendCUs * std::max(1, 4 / plan->waves_per_group);
+  int64_t w = 2 * groups_per_round / ((int64_t)num_kv_heads * plan->tile_groups);
   w = std::min<int64_t>(w, kExtendRowBudget / max_q - batch);
   if (opts && opts->work_items > 0) w = opts->work_items;
   plan->work_items = (int32_t)std::max<int64_t>(1, w);
