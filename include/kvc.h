@@ -155,8 +155,19 @@ kvc_status kvc_fork(kvc_cache* cache, int64_t parent_id, int64_t child_id);
 /* Page 2 free: every block loses one reference; at 0 it returns to the free list. */
 kvc_status kvc_free_seq(kvc_cache* cache, int64_t seq_id);
 /* Drop tokens past num_tokens (<= length); blocks past ceil(num_tokens/bs) are
- * released last-first, so re-appending takes the same blocks back. */
+ * released last-first, so re-appending takes the same blocks back.
+ * KVC_E_INVALID if the new end would fall inside a block kvc_evict released. */
 kvc_status kvc_truncate(kvc_cache* cache, int64_t seq_id, int32_t num_tokens);
+/* Sliding-window eviction ("苦猿的大模型日记 · Day45" PART 05: a fixed cache bound
+ * paid for with the history that leaves the window).  Every block of the
+ * sequence that holds only positions < keep_from (0 <= keep_from <= length)
+ * loses this sequence's reference (freed at 0, in table order); its table
+ * entry becomes -1, so logical indexing is unchanged and length stays.  With
+ * a window w, keep_from = (position of the next query token) - w + 1 keeps
+ * every row that token will see; attention calls must then pass that window
+ * (a released block is never read inside it).  Forks share only the live
+ * blocks; an append never lands in a released block. */
+kvc_status kvc_evict(kvc_cache* cache, int64_t seq_id, int32_t keep_from);
 
 /* Reserve slots for n_new[i] new tokens of seq_ids[i] (n_new NULL = 1 each)
  * without moving data: the bookkeeping half of kvc_append.  Sequences are
@@ -175,8 +186,9 @@ kvc_status kvc_reserve_host(kvc_cache* cache, int32_t batch, const int64_t* seq_
                             int32_t* slots_out, int32_t* cow_src, int32_t* cow_dst, int32_t cow_capacity,
                             int32_t* num_cow);
 
-/* Host copy of one sequence's table: up to max_blocks ids into blocks_out,
- * *num_blocks = table length, *length = tokens written. */
+/* Host copy of one sequence's table: up to max_blocks ids into blocks_out
+ * (-1 for a block kvc_evict released), *num_blocks = table length,
+ * *length = tokens written. */
 kvc_status kvc_get_table(const kvc_cache* cache, int64_t seq_id, int32_t* blocks_out, int32_t max_blocks,
                          int32_t* num_blocks, int32_t* length);
 kvc_status kvc_stats(const kvc_cache* cache, kvc_stats_t* out);
@@ -227,6 +239,8 @@ typedef struct kvc_decode_opts {
   int32_t pool_shift;       /* MFMA kernel: the pool is the last 1/2^pool_shift of each run, 1..6; 0 = 3 */
   kvc_event_t split_start;  /* optional events recorded on `stream` around the split-K kernel */
   kvc_event_t split_end;
+  int32_t window;           /* sliding window (both kernels, decode and several tokens): the token at
+                               position p sees positions max(0, p - window + 1) .. p; 0 = all of them */
 } kvc_decode_opts;
 
 /* Workspace bytes kvc_decode_attention needs for this shape (the split

@@ -33,6 +33,14 @@ each one attends causally: the token at position p sees positions 0..p, which
 is the mask of "苦猿的大模型日记" PART 04's ``naive_attention`` (lower triangle
 shifted by kv_len - q_len).
 
+A sliding window (``window`` > 0) limits what each token sees to its own
+row and the window - 1 rows before it ("苦猿的大模型日记" PART 05: the sliding
+window or KV eviction trades visible history for a fixed cache bound;
+"LLM推理优化实战…" §7.2 names sliding-window attention among the forms that
+restrict the attention range).  The pages give no formula; the plainest
+reading, taken here, is that the token at position p sees positions
+max(0, p - window + 1) .. p.
+
 ``causal_attention`` is the full-recompute definition (page 5's
 ``naive_attention`` with ``tril(diagonal = kv_len - q_len)``), written here
 without torch, used to pin ``decode_attention`` by brute force.
@@ -85,15 +93,18 @@ def decode_attention_batch(q, k_list, v_list, scale):
     return out
 
 
-def extend_attention(q, k, v, scale):
+def extend_attention(q, k, v, scale, window=0):
     """Attention of the last nq tokens of a sequence over its whole history.
 
     q: [nq, Hq, D]   queries of the nq newest tokens, oldest first
     k, v: [n, Hkv, D]  the sequence's K/V rows in position order, the nq new
         tokens' rows last (n >= nq >= 1)
     scale: float, the softmax scale
-    returns: [nq, Hq, D] fp64; row i is the token at position n - nq + i,
-        which attends over rows 0 .. n - nq + i.
+    window: 0 for none, else each token sees at most this many rows ending at
+        its own
+    returns: [nq, Hq, D] fp64; row i is the token at position p = n - nq + i,
+        which attends over rows max(0, p - window + 1) .. p (0 .. p without a
+        window).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -104,16 +115,19 @@ def extend_attention(q, k, v, scale):
         raise ValueError("need 1 <= nq <= n")
     if dk != d or v.shape != k.shape or hq % hkv != 0:
         raise ValueError("shape mismatch")
+    if window < 0:
+        raise ValueError("window must be >= 0")
     group = hq // hkv
     scale = float(scale)
     out = np.empty((nq, hq, d), dtype=np.float64)
     for i in range(nq):
-        visible = n - nq + i + 1                      # rows 0 .. visible - 1
+        p = n - nq + i                                # this token's position
+        first = max(0, p - window + 1) if window else 0
         for h in range(hq):
             g = h // group
-            scores = scale * (k[:visible, g, :] @ q[i, h])
+            scores = scale * (k[first:p + 1, g, :] @ q[i, h])
             w = np.exp(scores - scores.max())
-            out[i, h] = (w @ v[:visible, g, :]) / w.sum()
+            out[i, h] = (w @ v[first:p + 1, g, :]) / w.sum()
     return out
 
 

@@ -26,6 +26,13 @@ reading restored here (plainest one the rest of the code supports):
   old block's valid rows are copied only if this sequence has rows in it
   (p % bs > 0).  A position past the last block takes a fresh block.
 
+* ``evict(seq, keep_from)``: the sliding-window / KV-eviction item of
+  "苦猿的大模型日记 · Day45" PART 05 (a fixed cache bound bought with the history
+  that leaves the window).  Every block of the sequence whose positions all
+  lie before ``keep_from`` loses this sequence's reference (freed at 0); its
+  table entry becomes -1 so logical indexing is unchanged.  Not on the pages
+  as code; released in table order.
+
 Ordering rules (so that physical ids are reproducible bit for bit): sequences
 are processed in call order, positions ascending; every new block comes from
 ``free.pop()`` at the moment it is needed.  ``truncate`` (not on the pages; the
@@ -86,13 +93,16 @@ class BlockTableModel:
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
         for b in self.tables[child]:
-            self.ref[b] += 1
+            if b >= 0:
+                self.ref[b] += 1
         return OK
 
     def free_seq(self, seq: int) -> int:
         if seq not in self.tables:
             return E_NO_SEQ
         for b in self.tables[seq]:
+            if b < 0:
+                continue
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
@@ -135,6 +145,9 @@ class BlockTableModel:
                     b = self.free.pop()
                     self.ref[b] = 1
                     table.append(b)
+                elif table[idx] < 0:
+                    self._restore(saved)
+                    return E_INVALID, [], []
                 elif self.ref[table[idx]] > 1:
                     if not self.free:
                         self._restore(saved)
@@ -156,14 +169,35 @@ class BlockTableModel:
             return E_NO_SEQ
         if num_tokens < 0 or num_tokens > self.lens[seq]:
             return E_INVALID
-        keep = (num_tokens + self.block_size - 1) // self.block_size
         table = self.tables[seq]
+        if num_tokens % self.block_size and table[num_tokens // self.block_size] < 0:
+            return E_INVALID                            # the next write would land in a released block
+        keep = (num_tokens + self.block_size - 1) // self.block_size
         for b in reversed(table[keep:]):
+            if b < 0:
+                continue
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
         del table[keep:]
         self.lens[seq] = num_tokens
+        return OK
+
+    def evict(self, seq: int, keep_from: int) -> int:
+        """Release the blocks of ``seq`` that hold only positions < keep_from."""
+        if seq not in self.tables:
+            return E_NO_SEQ
+        if keep_from < 0 or keep_from > self.lens[seq]:
+            return E_INVALID
+        table = self.tables[seq]
+        for j in range(keep_from // self.block_size):
+            b = table[j]
+            if b < 0:
+                continue
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+            table[j] = -1
         return OK
 
     def _restore(self, saved):
@@ -185,9 +219,12 @@ class BlockTableModel:
         """Raise AssertionError if the bookkeeping is inconsistent."""
         count = [0] * self.num_blocks
         for s, t in self.tables.items():
-            assert len(set(t)) == len(t), "block repeated inside one table"
+            live = [b for b in t if b >= 0]
+            assert len(set(live)) == len(live), "block repeated inside one table"
             assert self.lens[s] <= len(t) * self.block_size, "length beyond capacity"
-            for b in t:
+            first_live = next((j for j, b in enumerate(t) if b >= 0), len(t))
+            assert all(b >= 0 for b in t[first_live:]), "released entry after a live one"
+            for b in live:
                 count[b] += 1
         assert count == self.ref, "refcount != number of tables holding the block"
         assert len(set(self.free)) == len(self.free), "block twice in the free list"

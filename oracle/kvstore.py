@@ -63,6 +63,9 @@ class KVStoreModel:
     def free_seq(self, seq):
         return self.tables.free_seq(seq)
 
+    def evict(self, seq, keep_from):
+        return self.tables.evict(seq, keep_from)
+
     def truncate(self, seq, n):
         return self.tables.truncate(seq, n)
 
@@ -116,15 +119,17 @@ class KVStoreModel:
         return status, slots, cow
 
     # logical views
-    def gather(self, seq, layer=0):
+    def gather(self, seq, layer=0, start=0):
         """Stored K/V of one sequence in position order, as fp64 values
-        (dequantised for fp8): ([n, Hkv, D], [n, Hkv, D])."""
+        (dequantised for fp8): ([n, Hkv, D], [n, Hkv, D]).  Positions before
+        ``start`` (released by eviction, say) are returned as zeros."""
         n = self.tables.lens[seq]
         table = self.tables.tables[seq]
-        ks = np.empty((n, self.H, self.D))
-        vs = np.empty((n, self.H, self.D))
-        for p in range(n):
+        ks = np.zeros((n, self.H, self.D))
+        vs = np.zeros((n, self.H, self.D))
+        for p in range(start, n):
             blk, off = table[p // self.bs], p % self.bs
+            assert blk >= 0, "position inside a released block"
             if self.kv_dtype == "fp8":
                 ks[p] = e4m3.decode_array(self.k[blk, layer, :, off, :]) * \
                     self.k_scale[blk, layer, :, None].astype(np.float64)

@@ -30,7 +30,7 @@ DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8}
 
 SYMBOLS = [
     "kvc_bytes_per_token", "kvc_pool_bytes", "kvc_scale_bytes", "kvc_scratch_bytes", "kvc_create", "kvc_destroy",
-    "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_reserve_host",
+    "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_evict", "kvc_reserve_host",
     "kvc_get_table", "kvc_stats", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
     "kvc_decode_attention", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_stream_copy",
     "kvc_last_error",
@@ -56,7 +56,7 @@ class KvcStats(ctypes.Structure):
 class KvcDecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("work_items", ctypes.c_int32),
                 ("pool_pieces", ctypes.c_int32), ("pool_shift", ctypes.c_int32),
-                ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p)]
+                ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p), ("window", ctypes.c_int32)]
 
 
 _i32, _i64, _sz, _vp, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -74,6 +74,7 @@ _sig = {
     "kvc_fork": (ctypes.c_int, [_vp, _i64, _i64]),
     "kvc_free_seq": (ctypes.c_int, [_vp, _i64]),
     "kvc_truncate": (ctypes.c_int, [_vp, _i64, _i32]),
+    "kvc_evict": (ctypes.c_int, [_vp, _i64, _i32]),
     "kvc_reserve_host": (ctypes.c_int, [_vp, _i32, _P64, _P32, _P32, _P32, _P32, _i32, _P32]),
     "kvc_get_table": (ctypes.c_int, [_vp, _i64, _P32, _i32, _P32, _P32]),
     "kvc_stats": (ctypes.c_int, [_vp, ctypes.POINTER(KvcStats)]),
@@ -155,13 +156,13 @@ def scratch_bytes(max_batch, max_tokens) -> int:
 
 def decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len, partition_tokens=0,
                            kernel=0, work_items=0, pool_pieces=0, pool_shift=0) -> int:
-    opts = KvcDecodeOpts(partition_tokens, kernel, work_items, pool_pieces, pool_shift, None, None)
+    opts = KvcDecodeOpts(partition_tokens, kernel, work_items, pool_pieces, pool_shift, None, None, 0)
     return _lib.kvc_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len,
                                            ctypes.byref(opts))
 
 
 def extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len, work_items=0) -> int:
-    opts = KvcDecodeOpts(0, 0, work_items, 0, 0, None, None)
+    opts = KvcDecodeOpts(0, 0, work_items, 0, 0, None, None, 0)
     return _lib.kvc_extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len,
                                            ctypes.byref(opts))
 
@@ -233,6 +234,10 @@ class KVCache:
 
     def free_seq(self, seq_id):
         _check(_lib.kvc_free_seq(self._h, int(seq_id)), "kvc_free_seq")
+
+    def evict(self, seq_id, keep_from):
+        """Release the blocks of seq_id holding only positions < keep_from."""
+        _check(_lib.kvc_evict(self._h, int(seq_id), int(keep_from)), "kvc_evict")
 
     def truncate(self, seq_id, num_tokens):
         _check(_lib.kvc_truncate(self._h, int(seq_id), int(num_tokens)), "kvc_truncate")
@@ -306,14 +311,15 @@ class KVCache:
 
     def decode(self, q, block_table, context_lens, max_context_len, scale, layer=0, out=None, workspace=None,
                partition_tokens=0, kernel=0, work_items=0, pool_pieces=0, pool_shift=0, split_events=None,
-               stream=None):
-        """Decode attention for one layer.  q: [B, Hq, D] device tensor."""
+               stream=None, window=0):
+        """Decode attention for one layer.  q: [B, Hq, D] device tensor.
+        ``window`` > 0: each token sees at most that many rows ending at its own."""
         import torch
         B, Hq, D = q.shape
         if not q.is_contiguous():
             raise ValueError("q must be contiguous")
         opts = KvcDecodeOpts(int(partition_tokens), int(kernel), int(work_items), int(pool_pieces), int(pool_shift),
-                             None, None)
+                             None, None, int(window))
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event
@@ -332,7 +338,7 @@ class KVCache:
         return out
 
     def extend(self, q, query_start, max_query_len, block_table, context_lens, max_context_len, scale, layer=0,
-               out=None, workspace=None, work_items=0, split_events=None, stream=None):
+               out=None, workspace=None, work_items=0, split_events=None, stream=None, window=0):
         """Attention of several new tokens per sequence (causal among them) for
         one layer.  q: [total_query, Hq, D] device tensor; query_start: device
         int32 [B + 1] (rows of sequence b are query_start[b] .. query_start[b+1]-1)."""
@@ -343,7 +349,7 @@ class KVCache:
             raise ValueError("q must be contiguous")
         if query_start.dtype != torch.int32 or query_start.numel() != B + 1:
             raise ValueError("query_start must be int32 with batch + 1 entries")
-        opts = KvcDecodeOpts(0, 0, int(work_items), 0, 0, None, None)
+        opts = KvcDecodeOpts(0, 0, int(work_items), 0, 0, None, None, int(window))
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event

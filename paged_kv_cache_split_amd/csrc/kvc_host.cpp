@@ -193,6 +193,8 @@ kvc_status plan_append(kvc_cache* c, int32_t batch, const int64_t* ids, const in
         ++need;
       } else {
         int32_t b = s.blocks[idx];
+        if (b < 0)
+          return fail(KVC_E_INVALID, "sequence %lld would write into a released block", (long long)ids[i]);
         int32_t r = c->ref[b] - drop[b];
         if (r > 1) {
           ++need;
@@ -289,6 +291,8 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
   plan->tile_groups = 0;
   plan->waves_per_group = 1;
   plan->max_q = 1;
+  if (opts && opts->window < 0) return false;
+  plan->window = opts ? opts->window : 0;
   return plan->chunk_slots() <= (1 << 28);   // chunk ids stay far inside int32
 }
 
@@ -297,19 +301,21 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
 // share a work-group (one wave each, side by side on one chunk of blocks, so
 // the chunk's tiles are read from HBM once and served to the others from
 // cache), the rest go to grid.z.  A wave uses the whole register file of its
-// SIMD, so a CU holds 4 / waves_per_group work-groups; the default launches
-// two such rounds over the chip, divided among the KV heads and tile groups
-// (measured on the verify and prefill workloads: one round leaves too few
-// blocks in flight, more rounds gain nothing), capped so the partials stay
-// within kExtendRowBudget rows per query head.
+// SIMD, so a CU holds 4 / waves_per_group work-groups; with several waves per
+// group the default launches two such rounds over the chip, divided among the
+// KV heads and tile groups (measured on the verify and prefill workloads: one
+// round leaves too few blocks in flight, more rounds gain nothing), with one
+// wave per group one round, as decode; capped so the partials stay within
+// kExtendRowBudget rows per query head.
 constexpr int64_t kExtendRowBudget = 1 << 16;
 constexpr int64_t kExtendCUs = 256;   // fixed (not queried), so results do not depend on the device
 constexpr int32_t kMaxQueryTokens = 4096;
 
 bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t max_q, int kv,
                  const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
-  if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2))) return false;
+  if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2) || opts->window < 0)) return false;
   if (max_q < 1 || max_q > kMaxQueryTokens) return false;
+  plan->window = opts ? opts->window : 0;
   const int32_t G = num_heads / num_kv_heads;
   const int32_t tiles = (max_q * G + 15) / 16;
   plan->kernel = 2;
@@ -322,7 +328,8 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   plan->max_q = max_q;
   (void)kv;
   const int64_t groups_per_round = (int64_t)kExtendCUs * std::max(1, 4 / plan->waves_per_group);
-  int64_t w = 2 * groups_per_round / ((int64_t)num_kv_heads * plan->tile_groups);
+  const int64_t rounds = plan->waves_per_group == 1 ? 1 : 2;   // one tile: shaped like decode, one round
+  int64_t w = rounds * groups_per_round / ((int64_t)num_kv_heads * plan->tile_groups);
   w = std::min<int64_t>(w, kExtendRowBudget / max_q - batch);
   if (opts && opts->work_items > 0) w = opts->work_items;
   plan->work_items = (int32_t)std::max<int64_t>(1, w);
@@ -436,7 +443,8 @@ kvc_status kvc_fork(kvc_cache* c, int64_t parent_id, int64_t child_id) {
   if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown parent %lld", (long long)parent_id);
   if (c->seqs.count(child_id)) return fail(KVC_E_SEQ_EXISTS, "sequence %lld exists", (long long)child_id);
   kvc_cache::Seq child = it->second;
-  for (int32_t b : child.blocks) ++c->ref[b];
+  for (int32_t b : child.blocks)
+    if (b >= 0) ++c->ref[b];
   c->seqs.emplace(child_id, std::move(child));
   return ok();
 }
@@ -446,7 +454,8 @@ kvc_status kvc_free_seq(kvc_cache* c, int64_t seq_id) {
   std::lock_guard<std::mutex> lock(c->mu);
   auto it = c->seqs.find(seq_id);
   if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)seq_id);
-  for (int32_t b : it->second.blocks) c->release(b);
+  for (int32_t b : it->second.blocks)
+    if (b >= 0) c->release(b);
   c->seqs.erase(it);
   return ok();
 }
@@ -459,12 +468,32 @@ kvc_status kvc_truncate(kvc_cache* c, int64_t seq_id, int32_t num_tokens) {
   kvc_cache::Seq& s = it->second;
   if (num_tokens < 0 || num_tokens > s.len)
     return fail(KVC_E_INVALID, "truncate to %d outside 0..%d", num_tokens, s.len);
-  size_t keep = ((int64_t)num_tokens + c->cfg.block_size - 1) / c->cfg.block_size;
+  const int32_t bs = c->cfg.block_size;
+  if (num_tokens % bs != 0 && s.blocks[num_tokens / bs] < 0)
+    return fail(KVC_E_INVALID, "truncate to %d would end inside a released block", num_tokens);
+  size_t keep = ((int64_t)num_tokens + bs - 1) / bs;
   while (s.blocks.size() > keep) {
-    c->release(s.blocks.back());
+    if (s.blocks.back() >= 0) c->release(s.blocks.back());
     s.blocks.pop_back();
   }
   s.len = num_tokens;
+  return ok();
+}
+
+kvc_status kvc_evict(kvc_cache* c, int64_t seq_id, int32_t keep_from) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  auto it = c->seqs.find(seq_id);
+  if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)seq_id);
+  kvc_cache::Seq& s = it->second;
+  if (keep_from < 0 || keep_from > s.len)
+    return fail(KVC_E_INVALID, "keep_from %d outside 0..%d", keep_from, s.len);
+  const int32_t whole = keep_from / c->cfg.block_size;   // blocks holding only positions < keep_from
+  for (int32_t j = 0; j < whole; ++j) {
+    if (s.blocks[j] < 0) continue;
+    c->release(s.blocks[j]);
+    s.blocks[j] = -1;
+  }
   return ok();
 }
 
@@ -709,7 +738,7 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
                    kernel, (int)kv, opts, &plan))
     return fail(KVC_E_INVALID,
                 "partition_tokens must be a multiple of 16 and at most 1024, work_items >= 0, "
-                "pool_pieces <= 64, pool_shift in 0..6");
+                "pool_pieces <= 64, pool_shift in 0..6, window >= 0");
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
@@ -751,7 +780,7 @@ kvc_status kvc_extend_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   if (kv == KVC_F32) return fail(KVC_E_UNSUPPORTED, "several query tokens need a 16-bit or fp8 cache");
   kvc::DecodePlan plan;
   if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len, (int)kv, opts, &plan))
-    return fail(KVC_E_INVALID, "opts: kernel must be 0 or 2, work_items >= 0");
+    return fail(KVC_E_INVALID, "opts: kernel must be 0 or 2, work_items >= 0, window >= 0");
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
   if (!workspace || workspace_bytes < need)
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);

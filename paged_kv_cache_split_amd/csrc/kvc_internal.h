@@ -72,6 +72,9 @@ struct DecodePlan {
   int32_t tile_groups;
   int32_t waves_per_group;
   int32_t max_q;
+  // sliding window (both kernels): a token sees at most `window` rows ending
+  // at its own; 0 = the whole history
+  int32_t window;
   int64_t chunk_slots() const { return (int64_t)work_items * (pool_pieces + 1); }
   int64_t query_slots() const { return tile_groups ? max_q : 1; }
 };

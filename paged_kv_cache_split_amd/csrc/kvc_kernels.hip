@@ -327,6 +327,7 @@ struct DecodeArgs {
   int32_t max_q;            // bound on query tokens per sequence
   int32_t total_q;          // rows of q and out
   int32_t waves_per_group;  // waves per work-group, one column tile each
+  int32_t window;           // sliding window: a token sees at most this many rows ending at its own (0 = all)
 };
 
 template <kvc_dtype QT>
@@ -352,6 +353,20 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
   if (t0 >= n) return;
   const int t1 = min(n, t0 + a.part_tokens);
   const int G = a.group;
+  // window: rows before lo are not seen; a partition wholly before it leaves
+  // an empty partial (m = -inf, l = 0, acc = 0: weight zero in the merge)
+  const int lo = a.window > 0 ? max(0, n - a.window) : 0;
+  if (t1 <= lo) {
+    for (int hh = 0; hh < G; ++hh) {
+      const int64_t rr = ((int64_t)b * a.num_heads + g * G + hh) * a.num_parts + part;
+      for (int d = lane; d < D; d += 64) a.ws_acc[rr * D + d] = 0.0f;
+      if (lane == 0) {
+        a.ws_m[rr] = kNegInf;
+        a.ws_l[rr] = 0.0f;
+      }
+    }
+    return;
+  }
   constexpr int EB = (KV == KVC_F32) ? 4 : (KV == KVC_FP8_E4M3 ? 1 : 2);
   constexpr int X = 16 / EB;
   constexpr int NCH = D / X;        // 16-byte chunks per token row
@@ -378,7 +393,7 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
     for (int i = 0; i < DPL; ++i) acc[hh][i] = 0.0f;
   }
   const int32_t* row = a.block_table + (int64_t)b * a.max_blocks;
-  for (int kb = t0 / kBS; kb * kBS < t1; ++kb) {
+  for (int kb = max(t0, lo) / kBS; kb * kBS < t1; ++kb) {
     const int phys = clamp_block(row[kb], a.num_blocks);
     const int64_t toff = ((int64_t)phys * a.num_kv_heads + g) * a.tile_bytes;
     const char* kt = a.k + toff;
@@ -417,7 +432,7 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
         }
       }
     }
-    const bool valid = kb * kBS + t < t1;
+    const bool valid = kb * kBS + t < t1 && kb * kBS + t >= lo;
     float alpha[GMAX];
 #pragma unroll
     for (int hh = 0; hh < GMAX; ++hh) {
@@ -629,11 +644,21 @@ __device__ __forceinline__ int query_len(const DecodeArgs& a, int b, int n) {
   return ql > 0 ? ql : 0;
 }
 
+// First table block of a sequence holding a row some query token sees: with a
+// window, the oldest new token (position n - ql) sees rows from
+// n - ql + 1 - window on; blocks before that are never read (and may have
+// been released by eviction).
+__device__ __forceinline__ int first_visible_block(int n, int ql, int window) {
+  const int lo = n - ql + 1 - window;
+  return (window > 0 && lo > 0) ? lo / kBS : 0;
+}
+
 // Exclusive scan of the sequences' block counts into LDS: seq_start[b] is the
 // first block of sequence b in the batch's concatenated block list, and
 // seq_start[batch] the total.  Every wave of the decode and every merge
 // work-group computes the same values from context_lens.  With several query
-// tokens per sequence (EXT), a sequence with no query token owns no blocks.
+// tokens per sequence (EXT), a sequence with no query token owns no blocks;
+// with a window, a sequence's list starts at its first visible block.
 template <bool EXT>
 __device__ __forceinline__ int scan_block_counts(const DecodeArgs& a, int* seq_start, int lane) {
   int carry = 0;
@@ -643,9 +668,12 @@ __device__ __forceinline__ int scan_block_counts(const DecodeArgs& a, int* seq_s
     if (bb < a.batch) {
       const int n = attend_len(a.context_lens, bb, a.max_ctx, a.max_blocks);
       nb = n > 0 ? (n + kBS - 1) / kBS : 0;
+      int ql = 1;
       if constexpr (EXT) {
-        if (query_len(a, bb, n) == 0) nb = 0;
+        ql = query_len(a, bb, n);
+        if (ql == 0) nb = 0;
       }
+      if (nb > 0) nb -= first_visible_block(n, ql, a.window);
     }
     int incl = nb;
 #pragma unroll
@@ -756,7 +784,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
       const int eb = __builtin_amdgcn_readfirstlane(seq_start[b + 1]);
       if (eb <= x) continue;                      // empty sequence
       const int seg_end = eb < xb ? eb : xb;
-      const int first = x - sb;                   // first local block of this segment
+      const int first = x - sb;                   // first block of this segment in the sequence's list
       const int count = seg_end - x;              // blocks in this segment
       const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
       if (first == 0 && g == 0 && threadIdx.x == 0 && (!EXT || blockIdx.z == 0)) {
@@ -766,8 +794,10 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
       }
       // Columns of this lane.  Decode: head nn of the group, every column sees
       // the n rows.  EXT: column 16 ct + nn is (query token tok, head hh); the
-      // token sits at position n - ql + tok and sees n - ql + 1 + tok rows.
-      int ql = 1, tok = 0, hh = nn, cnt = count, n_lo = n, q_row = b;
+      // token sits at position n - ql + tok and sees rows up to n - ql + tok.
+      // With a window a column sees rows [col_lo, ncol), col_lo = ncol - window.
+      int ql = 1, tok = 0, hh = nn, q_row = b;
+      int n_lo = n, n_hi = n;                     // fewest / most rows a column of the tile sees
       bool head_ok = nn < G;
       if constexpr (EXT) {
         ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
@@ -781,13 +811,22 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
         const int q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
         q_row = q0 + tok;
         head_ok = tok < ql && q_row >= 0 && q_row < a.total_q;
-        n_lo = n - ql + 1 + (ct * 16) / G;        // fewest rows a column of the tile sees
-        const int tok_hi = min(ql - 1, (ct * 16 + 15) / G);
-        const int nb_hi = (n - ql + 1 + tok_hi + kBS - 1) / kBS - first;   // blocks the tile needs
-        cnt = count < nb_hi ? count : nb_hi;      // <= 0: no row of this segment is visible to the tile
+        n_lo = n - ql + 1 + (ct * 16) / G;
+        n_hi = n - ql + 1 + min(ql - 1, (ct * 16 + 15) / G);
       }
       // rows this lane's column sees (padding columns: all n, so they stay finite)
       const int ncol = head_ok ? n - ql + 1 + tok : n;
+      const int win = a.window;
+      const int col_lo = win > 0 ? max(0, ncol - win) : 0;
+      const int lo_lo = win > 0 ? max(0, n_lo - win) : 0;   // lowest first row over the tile's columns
+      const int lo_hi = win > 0 ? max(0, n_hi - win) : 0;   // highest
+      // table index of the segment's first block, and the blocks [j0, j1) of
+      // the segment that some column of the tile sees (cnt <= 0: none)
+      const int tb0 = __builtin_amdgcn_readfirstlane(first_visible_block(n, ql, win)) + first;
+      const int j0 = max(0, lo_lo / kBS - tb0);
+      const int j1 = min(count, (n_hi + kBS - 1) / kBS - tb0);
+      const int cnt = j1 - j0;
+      const int tb = tb0 + j0;                    // table index of the tile's first block here
       const int h = g * G + hh;
 
       // Query operand: for step kk the lane holds 8 dims of its column's head,
@@ -813,7 +852,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
         // prefetch is issued, so the count of loads in flight is the same on
         // every path; past the end it re-reads the segment's last block, which
         // the L2 still holds.
-        const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + first);
+        const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + tb);
         auto phys_of = [&](int j) -> int {
           j = j < cnt ? j : cnt - 1;
           return clamp_block(row[j], a.num_blocks);
@@ -845,18 +884,20 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
             for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
           }
           // Rows some column of the tile may not see exist only near the end of
-          // the sequence (a wave-uniform test): mask them there, before the max
-          // and after exp.  Rows past the sequence's end hold whatever the slot
+          // the sequence, or before the window's start (a wave-uniform test):
+          // mask them there, before the max and after exp.  Rows past the
+          // sequence's end hold whatever the slot
           // held before (never written, or a previous owner's rows); zeroing
           // their values as well keeps a NaN pattern there out of the
           // accumulator (its weight is zero, but 0 * NaN is NaN).
-          const int t0 = (first + i) * kBS + 4 * r;   // this lane's first row
-          const bool edge = (first + i) * kBS + kBS > n_lo;
+          const int blk_row = (tb + i) * kBS;          // the block's first row
+          const int t0 = blk_row + 4 * r;                // this lane's first row
+          const bool edge = blk_row + kBS > n_lo || blk_row < lo_hi;
           float sv[4] = {s[0], s[1], s[2], s[3]};
           if (edge) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (t0 + e >= ncol) sv[e] = kNegInf;
+              if (t0 + e >= ncol || t0 + e < col_lo) sv[e] = kNegInf;
             const int vr = n - t0;                     // rows of this lane's four inside the sequence
             if constexpr (KV == KVC_FP8_E4M3) {
               const uint32_t keep = vr >= 4 ? 0xFFFFFFFFu : (vr <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * vr)));
@@ -892,7 +933,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
             // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (t0 + e >= ncol) pv[e] = 0.0f;
+              if (t0 + e >= ncol || t0 + e < col_lo) pv[e] = 0.0f;
           }
           l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
           // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
@@ -1301,6 +1342,7 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   a.max_q = plan.tile_groups ? plan.max_q : 1;
   a.total_q = plan.tile_groups ? total_q : batch;
   a.waves_per_group = plan.tile_groups ? plan.waves_per_group : 1;
+  a.window = plan.window;
   const bool merge = plan.kernel == 2 || plan.num_partitions > 1;
   const WorkspaceLayout wl = workspace_layout(plan, batch, num_heads, pool.num_kv_heads, pool.head_dim);
   char* w = static_cast<char*>(workspace);

@@ -77,6 +77,8 @@ def gpu_setup(wl, values, device="cuda", pool_fill=None):
                 cache.append(seqs, k_hist[:, row:row + t].contiguous(), v_hist[:, row:row + t].contiguous(),
                              n_new=n_new)
             row += t
+        elif op[0] == "evict":
+            cache.evict(op[1], op[2])
     return cache
 
 
@@ -88,14 +90,14 @@ def gpu_step(cache, wl, values, kernel=0, partition_tokens=0, device="cuda", out
     bt, cl = cache.export_tables(seqs)
     q = values["q"].to(device).contiguous()
     o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
-                     out=out, work_items=work_items, **split)
+                     out=out, work_items=work_items, window=wl.window, **split)
     return o, bt, cl
 
 
 def gpu_decode_again(cache, wl, values, bt, cl, kernel=0, partition_tokens=0, device="cuda", work_items=0, **split):
     q = values["q"].to(device).contiguous()
     return cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
-                        work_items=work_items, **split)
+                        work_items=work_items, window=wl.window, **split)
 
 
 # -- oracle side ------------------------------------------------------------------
@@ -118,6 +120,8 @@ def oracle_run(wl, values):
             status, _, _ = st.append(op[1], op[2], kb[:, row:row + t], vb[:, row:row + t])
             assert status == 0
             row += t
+        elif op[0] == "evict":
+            assert st.evict(op[1], op[2]) == 0
     seqs = list(range(wl.batch))
     status, slots, cow = st.append(seqs, [int(x) for x in wl.q_lens], to_bits(values["k_new"], wl.new_dtype),
                                    to_bits(values["v_new"], wl.new_dtype))
@@ -127,13 +131,18 @@ def oracle_run(wl, values):
 
 def oracle_decode(st, wl, values, seqs=None, layer=0):
     """fp64 decode outputs [len(seqs), Hq, D] from the oracle store's stored values."""
-    from oracle.attention import decode_attention
+    from oracle.attention import decode_attention, extend_attention
     q = to_f64(values["q"])
     seqs = list(range(wl.batch)) if seqs is None else list(seqs)
     out = np.empty((len(seqs), wl.num_heads, wl.head_dim))
     for i, b in enumerate(seqs):
-        k, v = st.gather(b, layer)
-        out[i] = decode_attention(q[b], k, v, wl.scale)
+        if wl.window:
+            n = st.tables.lens[b]
+            k, v = st.gather(b, layer, start=max(0, n - wl.window))
+            out[i] = extend_attention(q[b:b + 1], k, v, wl.scale, window=wl.window)[0]
+        else:
+            k, v = st.gather(b, layer)
+            out[i] = decode_attention(q[b], k, v, wl.scale)
     return out
 
 
@@ -151,7 +160,8 @@ def gpu_extend_step(cache, wl, values, device="cuda", work_items=0):
     bt, cl = cache.export_tables(seqs)
     qs = torch.from_numpy(query_start(wl)).to(device)
     q = values["q"].to(device).contiguous()
-    o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=work_items)
+    o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=work_items,
+                     window=wl.window)
     return o, bt, cl, qs
 
 
@@ -165,8 +175,10 @@ def oracle_extend(st, wl, values, seqs=None, layer=0):
     for b in (range(wl.batch) if seqs is None else seqs):
         if qs[b + 1] == qs[b]:
             continue
-        k, v = st.gather(b, layer)
-        out[qs[b]:qs[b + 1]] = extend_attention(q[qs[b]:qs[b + 1]], k, v, wl.scale)
+        n = st.tables.lens[b]
+        first = max(0, n - int(qs[b + 1] - qs[b]) + 1 - wl.window) if wl.window else 0
+        k, v = st.gather(b, layer, start=first)
+        out[qs[b]:qs[b + 1]] = extend_attention(q[qs[b]:qs[b + 1]], k, v, wl.scale, window=wl.window)
     return out
 
 
@@ -181,13 +193,8 @@ def logical_history(wl, values, b, layer=0):
 
 
 def _history_rows(wl, b):
-    lens = [int(x) for x in wl.context_lens]
-    if wl.shared_prefix:
-        p = wl.shared_prefix
-        start = p + sum(l - p for l in lens[:b])
-        return torch.cat([torch.arange(0, p), torch.arange(start, start + lens[b] - p)])
-    start = sum(lens[:b])
-    return torch.arange(start, start + lens[b])
+    from workloads import history_rows_of
+    return torch.from_numpy(history_rows_of(wl, b))
 
 
 def check_close(gpu: np.ndarray, ref: np.ndarray, atol: float, rtol: float, what: str):

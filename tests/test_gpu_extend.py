@@ -87,9 +87,9 @@ def test_one_token_per_sequence_matches_decode_bitwise(kv):
     wl = custom_workload(len(lens), 32, 8, 128, kv, lens, seed=17, name="extend = decode")
     values = make_values(wl, "cpu")
     cache = gpu_setup(wl, values)
-    dec, bt, cl = gpu_step(cache, wl, values)
+    dec, bt, cl = gpu_step(cache, wl, values, work_items=100)
     qs = torch.arange(wl.batch + 1, dtype=torch.int32, device="cuda")
-    ext = cache.extend(values["q"].cuda().contiguous(), qs, 1, bt, cl, wl.max_context_len, wl.scale)
+    ext = cache.extend(values["q"].cuda().contiguous(), qs, 1, bt, cl, wl.max_context_len, wl.scale, work_items=100)
     torch.cuda.synchronize()
     assert torch.equal(dec.view(torch.int16), ext.view(torch.int16))
 

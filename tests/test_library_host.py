@@ -113,8 +113,18 @@ def test_randomised_against_oracle_model():
             elif op < 0.55:
                 s = rng.choice(live)
                 n = rng.randint(0, m.lens[s])
-                c.truncate(s, n)
-                m.truncate(s, n)
+                expect = m.truncate(s, n)
+                try:
+                    c.truncate(s, n)
+                    got = 0
+                except kvc.KvcError as e:
+                    got = e.status
+                assert got == expect
+            elif op < 0.62:
+                s = rng.choice(live)
+                k = rng.randint(0, m.lens[s])
+                assert m.evict(s, k) == 0
+                c.evict(s, k)
             else:
                 seqs = rng.sample(live, rng.randint(1, len(live)))
                 n_new = [rng.randint(0, 3 * bs) for _ in seqs]

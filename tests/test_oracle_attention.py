@@ -282,3 +282,73 @@ def test_planted_causal_offset_mistake_is_caught():
     ref = _sdpa_causal(q, K, V, 0.4)
     assert not np.allclose(wrong(q, K, V, 0.4), ref, atol=1e-6)
     assert np.allclose(attention.extend_attention(q, K, V, 0.4), ref, atol=1e-12)
+
+
+# -- sliding window ---------------------------------------------------------------
+
+def _sdpa_window(q, K, V, scale, window):
+    # torch SDPA in fp64 with a banded boolean mask: query i (position
+    # p = n - nq + i) sees key j iff p - window < j <= p.
+    nq, n = q.shape[0], K.shape[0]
+    causal = torch.ones(nq, n, dtype=torch.bool).tril(diagonal=n - nq)
+    band = torch.ones(nq, n, dtype=torch.bool).triu(diagonal=n - nq - window + 1)
+    qt = torch.tensor(q, dtype=torch.float64).permute(1, 0, 2)[None]
+    kt = torch.tensor(K, dtype=torch.float64).permute(1, 0, 2)[None]
+    vt = torch.tensor(V, dtype=torch.float64).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(), attn_mask=causal & band, scale=scale,
+                                       enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("hq,hkv,nq,n,window", [(8, 2, 1, 40, 7), (8, 2, 5, 40, 16), (4, 4, 16, 16, 3),
+                                                (16, 1, 3, 70, 64), (6, 3, 9, 30, 1)])
+def test_window_matches_torch_sdpa_with_banded_mask(hq, hkv, nq, n, window):
+    rng = np.random.default_rng(hq * 13 + window)
+    d = 32
+    q = rng.standard_normal((nq, hq, d))
+    K, V = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    np.testing.assert_allclose(attention.extend_attention(q, K, V, 0.2, window=window),
+                               _sdpa_window(q, K, V, 0.2, window), rtol=1e-12, atol=1e-13)
+
+
+def test_window_special_cases():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((3, 4, 16))
+    K, V = rng.standard_normal((25, 2, 16)), rng.standard_normal((25, 2, 16))
+    full = attention.extend_attention(q, K, V, 0.3)
+    # a window at least as long as the history changes nothing
+    for w in (25, 26, 1000):
+        np.testing.assert_array_equal(attention.extend_attention(q, K, V, 0.3, window=w), full)
+    # a window of one row: each token returns its own value row
+    one = attention.extend_attention(q, K, V, 0.3, window=1)
+    for i in range(3):
+        for h in range(4):
+            assert np.array_equal(one[i, h], V[22 + i, h // 2])
+    # brute force: the window equals plain attention over the sliced history
+    w = 9
+    win = attention.extend_attention(q, K, V, 0.3, window=w)
+    for i in range(3):
+        p = 22 + i
+        dec = attention.decode_attention(q[i], K[p - w + 1:p + 1], V[p - w + 1:p + 1], 0.3)
+        np.testing.assert_allclose(win[i], dec, rtol=1e-13, atol=1e-15)
+
+
+def test_planted_window_off_by_one_is_caught():
+    def wrong(q, K, V, scale, window):
+        # sees window + 1 rows
+        nq, hq, d = q.shape
+        n, hkv, _ = K.shape
+        out = np.empty_like(q)
+        for i in range(nq):
+            p = n - nq + i
+            lo = max(0, p - window)
+            for h in range(hq):
+                sc = scale * (K[lo:p + 1, h // (hq // hkv)] @ q[i, h])
+                wt = np.exp(sc - sc.max())
+                out[i, h] = wt @ V[lo:p + 1, h // (hq // hkv)] / wt.sum()
+        return out
+    rng = np.random.default_rng(6)
+    q, K, V = rng.standard_normal((2, 4, 8)), rng.standard_normal((20, 2, 8)), rng.standard_normal((20, 2, 8))
+    ref = _sdpa_window(q, K, V, 0.5, 5)
+    assert not np.allclose(wrong(q, K, V, 0.5, 5), ref, atol=1e-6)
+    assert np.allclose(attention.extend_attention(q, K, V, 0.5, window=5), ref, atol=1e-12)

@@ -169,9 +169,17 @@ def test_randomised_operation_sequences_keep_invariants():
                 s = rng.choice(live)
                 assert bt.free_seq(s) == blocktable.OK
                 live.remove(s)
-            elif op < 0.6:
+            elif op < 0.55:
                 s = rng.choice(live)
                 bt.truncate(s, rng.randint(0, bt.lens[s]))
+            elif op < 0.6:
+                s = rng.choice(live)
+                before = list(bt.tables[s])
+                k = rng.randint(0, bt.lens[s])
+                assert bt.evict(s, k) == blocktable.OK
+                # exactly the blocks wholly before k are gone; the rest are untouched
+                for j, b in enumerate(bt.tables[s]):
+                    assert b == (-1 if (j + 1) * bs <= k else before[j])
             else:
                 k = rng.randint(1, len(live))
                 seqs = rng.sample(live, k)
@@ -244,3 +252,47 @@ def test_paged_history_is_placement_invariant():
         outs.append(st.gather(0)[0])
     np.testing.assert_array_equal(outs[0], outs[1])
     np.testing.assert_array_equal(outs[0], kvstore.bits_to_f64(k[0], "f16"))
+
+
+# -- sliding-window eviction ----------------------------------------------------
+
+def test_eviction_keeps_the_cache_bounded():
+    # A sequence that keeps generating under a window of w tokens, releasing
+    # what leaves the window after every step, never holds more than
+    # ceil(w / bs) + 1 blocks, and the blocks it releases serve other sequences.
+    bs, w = 4, 10
+    bt = BlockTableModel(8, bs)
+    assert bt.allocate(0, 0) == blocktable.OK
+    for step in range(200):
+        assert bt.append([0], [1])[0] == blocktable.OK
+        n = bt.lens[0]                                   # the next token sits at position n
+        assert bt.evict(0, max(0, n - w + 1)) == blocktable.OK   # it sees positions n - w + 1 .. n
+        live = [b for b in bt.tables[0] if b >= 0]
+        assert len(live) <= -(-w // bs) + 1
+        bt.check_invariants()
+    assert len(bt.tables[0]) == -(-200 // bs)             # logical indexing unchanged
+    # the released blocks are back on the free list
+    assert len(bt.free) == 8 - len([b for b in bt.tables[0] if b >= 0])
+
+
+def test_evict_fork_and_free_respect_released_entries():
+    bs = 4
+    bt = BlockTableModel(10, bs)
+    bt.allocate(0, 0)
+    bt.append([0], [14])                                  # blocks 0..3, last one half full
+    assert bt.evict(0, 9) == blocktable.OK                # positions 0..7 gone: blocks 0, 1
+    assert bt.tables[0][:2] == [-1, -1]
+    assert bt.fork(0, 1) == blocktable.OK                 # shares the two live blocks only
+    for b in bt.tables[0][2:]:
+        assert bt.ref[b] == 2
+    bt.check_invariants()
+    assert bt.truncate(1, 6) == blocktable.E_INVALID      # would end inside a released block
+    assert bt.truncate(1, 8) == blocktable.OK             # a block boundary is fine
+    assert bt.append([1], [1])[0] == blocktable.OK        # position 8: a fresh block after two released
+    bt.check_invariants()
+    assert bt.free_seq(0) == blocktable.OK and bt.free_seq(1) == blocktable.OK
+    assert sorted(bt.free) == list(range(10))
+    assert bt.evict(5, 0) == blocktable.E_NO_SEQ
+    bt.allocate(2, 0)
+    bt.append([2], [3])
+    assert bt.evict(2, 4) == blocktable.E_INVALID          # beyond the length

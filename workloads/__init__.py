@@ -6,5 +6,6 @@ values rounded to the storage dtype.  It holds none of the method's
 arithmetic, and both the HIP path's callers and the oracle's callers take
 their inputs from it.
 """
-from .configs import (CONFIGS, EXTEND_CONFIGS, EXTEND_SMALL, SMALL, Workload, custom_workload,  # noqa: F401
-                      make_extend_workload, make_values, make_workload, setup_ops)
+from .configs import (CONFIGS, EXTEND_CONFIGS, EXTEND_SMALL, SMALL, WINDOW_CONFIGS, Workload,  # noqa: F401
+                      custom_workload, history_rows_of, make_extend_workload, make_values, make_window_workload,
+                      make_workload, setup_ops)

@@ -44,6 +44,8 @@ class Workload:
     block_size: int = BLOCK_SIZE
     extra: dict = field(default_factory=dict)
     query_lens: np.ndarray | None = None   # [B] new tokens per sequence in the step (None: 1 each, decode)
+    window: int = 0         # sliding window (0 = none): the history is written in chunks of
+    evict_chunk: int = 0    # evict_chunk rows and what leaves the window is evicted after each
 
     @property
     def q_lens(self) -> np.ndarray:
@@ -235,9 +237,27 @@ def setup_ops(wl: Workload):
     ("append", seqs, n_new)    append n_new[i] history rows to seqs[i]; rows are
                                taken in order from the K/V history tensors
     ("fork", parent, child)    share the parent's blocks copy-on-write
+    ("evict", seq, keep_from)  release the blocks of seq holding only positions
+                               before keep_from (sliding window)
     """
     ops = []
     B = wl.batch
+    if wl.window:
+        # chunks of evict_chunk rows for every sequence, then eviction of what
+        # the step's oldest new token (at position L_b) will not see
+        for b in range(B):
+            ops.append(("add", b, 0))
+        lens = [int(l) for l in wl.context_lens]
+        done = [0] * B
+        while any(d < l for d, l in zip(done, lens)):
+            n_new = [min(wl.evict_chunk, l - d) for d, l in zip(done, lens)]
+            ops.append(("append", list(range(B)), n_new))
+            done = [d + n for d, n in zip(done, n_new)]
+            for b in range(B):
+                keep = max(0, min(done[b], lens[b] - wl.window + 1))
+                if n_new[b] and keep > 0:
+                    ops.append(("evict", b, keep))
+        return ops
     if wl.shared_prefix:
         ops.append(("add", 0, 0))
         ops.append(("append", [0], [wl.shared_prefix]))
@@ -249,6 +269,62 @@ def setup_ops(wl: Workload):
             ops.append(("add", b, 0))
         ops.append(("append", list(range(B)), [int(l) for l in wl.context_lens]))
     return ops
+
+
+def history_rows_of(wl: Workload, b: int):
+    """Indices, in the K/V history tensors, of sequence b's history rows in
+    position order (the order setup_ops consumes rows in)."""
+    lens = [int(x) for x in wl.context_lens]
+    if wl.window:
+        rows, base, done = [], 0, [0] * wl.batch
+        while any(d < l for d, l in zip(done, lens)):
+            n_new = [min(wl.evict_chunk, l - d) for d, l in zip(done, lens)]
+            rows.extend(range(base + sum(n_new[:b]), base + sum(n_new[:b]) + n_new[b]))
+            base += sum(n_new)
+            done = [d + n for d, n in zip(done, n_new)]
+        return np.asarray(rows, dtype=np.int64)
+    if wl.shared_prefix:
+        p = wl.shared_prefix
+        start = p + sum(l - p for l in lens[:b])
+        return np.concatenate([np.arange(0, p), np.arange(start, start + lens[b] - p)]).astype(np.int64)
+    start = sum(lens[:b])
+    return np.arange(start, start + lens[b], dtype=np.int64)
+
+
+# Decode (or several new tokens) under a sliding window with eviction: the
+# 70B-shaped GQA layer over 16K-token contexts, each token seeing the last
+# 4096 positions ("苦猿的大模型日记" PART 05's sliding window / KV eviction; the
+# window length is a builder's choice, the pages give none), the history
+# written 1024 rows at a time with what leaves the window evicted after each.
+WINDOW_CONFIGS = {
+    "decode": dict(name="sliding-window decode, window 4096 over 16K contexts, evicted, 70B-shaped GQA bf16, "
+                        "B64, 64/8 heads, D128",
+                   batch=64, num_heads=64, num_kv_heads=8, head_dim=128, kv_dtype="bf16", lens=16384, q=1,
+                   window=4096, chunk=1024),
+}
+WINDOW_SMALL = {
+    "decode": dict(WINDOW_CONFIGS["decode"], name="sliding-window decode (scaled down), window 200, B4, 32/8, D128",
+                   batch=4, num_heads=32, lens=700, window=200, chunk=64),
+}
+
+
+def make_window_workload(kind: str = "decode", seed: int = 8, small: bool = False, kv_dtype=None,
+                         query_lens=None) -> Workload:
+    p = dict((WINDOW_SMALL if small else WINDOW_CONFIGS)[kind])
+    rng = np.random.default_rng(seed)
+    B, W, C = p["batch"], p["window"], p["chunk"]
+    lens = np.full(B, p["lens"], dtype=np.int64)
+    qls = None if query_lens is None else np.asarray(query_lens, dtype=np.int64)
+    q_max = 1 if qls is None else int(qls.max())
+    # live blocks per sequence never exceed those of window + chunk + new rows
+    pool = B * ((W + C + q_max + BLOCK_SIZE - 1) // BLOCK_SIZE + 2)
+    free_order = rng.permutation(pool).astype(np.int32)
+    kv = kv_dtype or p["kv_dtype"]
+    return Workload(name=p["name"], batch=B, num_heads=p["num_heads"], num_kv_heads=p["num_kv_heads"],
+                    head_dim=p["head_dim"], q_dtype=("bf16" if kv == "fp8" else kv), kv_dtype=kv,
+                    new_dtype=("bf16" if kv == "fp8" else kv), context_lens=lens, shared_prefix=0,
+                    num_blocks=int(pool), free_order=free_order, seed=seed, query_lens=qls, window=W,
+                    evict_chunk=C)
 
 
 def _randn(shape, dtype_name, gen, device):
