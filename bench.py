@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged GQA decode attn: µs/step, KV-read HBM GB/s and % of MI355X peak"
 PEAK_HBM_GBS = 8000.0
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}
 
 
 def parse():
@@ -49,6 +49,12 @@ def parse():
                    help="time a step with several new tokens per sequence instead of decode: the verify pass "
                         "of speculative decoding (5 draft tokens, 70B-shaped batch), a 2048-token causal "
                         "prefill, or a 512-token prefill chunk over 3584 cached tokens")
+    p.add_argument("--kv", choices=["f32", "f16", "bf16", "fp8", "int8"], default=None,
+                   help="cache dtype override for --config (e.g. --config 5 --kv int8: the mixed batch with an "
+                        "int8 cache)")
+    p.add_argument("--window", action="store_true",
+                   help="time decode under a sliding window of 4096 over 16K-token contexts whose older blocks "
+                        "were evicted (70B-shaped batch) instead of --config")
     return p.parse_args()
 
 
@@ -56,13 +62,17 @@ def algorithmic_bytes(wl):
     """Bytes the decode must move, per step (what the method reads and writes)."""
     eb = ELEM_BYTES[wl.kv_dtype]
     tokens = wl.history_rows + wl.batch            # distinct rows attended (shared prefix once)
+    if wl.window:                                  # only the rows inside each window
+        tokens = int(sum(min(int(n), wl.window) for n in wl.attend_lens))
     kv = 2 * tokens * wl.num_kv_heads * wl.head_dim * eb
     blocks_distinct = wl.num_blocks
-    scales = 2 * 4 * blocks_distinct * wl.num_kv_heads if wl.kv_dtype == "fp8" else 0
+    scales = 2 * 4 * blocks_distinct * wl.num_kv_heads if wl.kv_dtype in ("fp8", "int8") else 0
     qb = ELEM_BYTES[wl.q_dtype]
     q = wl.batch * wl.num_heads * wl.head_dim * qb
     out = q
     tables = 4 * sum((int(n) + 15) // 16 for n in wl.attend_lens) + 4 * wl.batch
+    if wl.window:
+        tables = 4 * sum((int(n) + 15) // 16 - max(0, int(n) - wl.window) // 16 for n in wl.attend_lens) + 4 * wl.batch
     append = 2 * wl.batch * wl.num_kv_heads * wl.head_dim * eb
     return dict(kv=kv, scales=scales, q=q, out=out, tables=tables, append=append,
                 split_kernel=kv + scales + q + tables)
@@ -128,6 +138,36 @@ def cpu_baseline(wl, values, budget_s):
                       f"os.cpu_count()={os.cpu_count()}"}
 
 
+def cpu_baseline_window(wl, values, budget_s):
+    """The fp64 oracle's windowed attention (one new token per sequence, over
+    the rows of its window) on sequences of the same workload until the budget
+    is spent; GB/s of KV in the windows it processed."""
+    import numpy as np
+    import torch
+    from oracle.attention import extend_attention
+    from workloads import history_rows_of
+    q = values["q"].to(torch.float64).cpu().numpy()
+    done_bytes, n_seq, wall, cpu = 0, 0, 0.0, 0.0
+    for b in range(wl.batch):
+        L = int(wl.context_lens[b])
+        keep = min(L + 1, wl.window) - 1                  # history rows inside the window
+        rows = torch.from_numpy(history_rows_of(wl, b)[L - keep:]).to(values["k_hist"].device)
+        k = torch.cat([values["k_hist"][0, rows], values["k_new"][0, b:b + 1]]).to(torch.float64).cpu().numpy()
+        v = torch.cat([values["v_hist"][0, rows], values["v_new"][0, b:b + 1]]).to(torch.float64).cpu().numpy()
+        t0, c0 = time.perf_counter(), time.process_time()
+        extend_attention(q[b:b + 1], k, v, wl.scale, window=wl.window)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        n_seq += 1
+        done_bytes += 2 * (keep + 1) * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
+        if wall > budget_s:
+            break
+    return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {wl.batch} sequences of the same workload ({done_bytes / 1e9:.3f} GB of KV in "
+                      f"their windows, fp64 NumPy, {wall:.1f} s wall); os.cpu_count()={os.cpu_count()}"}
+
+
 EXTEND_METRIC = "paged multi-token attention (causal among the new tokens): µs/step, KV-read GB/s, TFLOP/s"
 PEAK_MFMA_TFLOPS = 2500.0   # dense bf16 / fp16 matrix-core peak
 
@@ -139,7 +179,7 @@ def extend_work(wl):
     eb = ELEM_BYTES[wl.kv_dtype]
     rows = int(wl.attend_lens.sum())
     kv = 2 * rows * wl.num_kv_heads * wl.head_dim * eb
-    scales = 2 * 4 * wl.num_blocks * wl.num_kv_heads if wl.kv_dtype == "fp8" else 0
+    scales = 2 * 4 * wl.num_blocks * wl.num_kv_heads if wl.kv_dtype in ("fp8", "int8") else 0
     q = wl.total_queries * wl.num_heads * wl.head_dim * ELEM_BYTES[wl.q_dtype]
     tables = 4 * sum((int(n) + 15) // 16 for n in wl.attend_lens) + 8 * wl.batch + 4
     visible = sum(int(ql) * (int(n) - int(ql)) + int(ql) * (int(ql) + 1) // 2
@@ -296,13 +336,14 @@ def main():
         return
     import torch
     import paged_kv_cache_split_amd as kvc
-    from workloads import make_values, make_workload, setup_ops
+    from workloads import make_values, make_window_workload, make_workload, setup_ops
 
     dev = "cuda"
     torch.cuda.set_device(0)
-    wl = make_workload(args.config, seed=args.seed)
-    print(f"[bench] config {args.config}: {wl.name}; blocks {wl.num_blocks}, attended tokens "
-          f"{int(wl.attend_lens.sum())}", file=sys.stderr, flush=True)
+    over = {"kv_dtype": args.kv} if args.kv else {}
+    wl = make_window_workload() if args.window else make_workload(args.config, seed=args.seed, **over)
+    print(f"[bench] {'window' if args.window else 'config %d' % args.config}: {wl.name}; blocks {wl.num_blocks}, "
+          f"attended tokens {int(wl.attend_lens.sum())}", file=sys.stderr, flush=True)
     values = make_values(wl, dev)
     cache = kvc.KVCache(wl.num_layers, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.kv_dtype, device=dev,
                         free_order=wl.free_order)
@@ -312,6 +353,8 @@ def main():
             cache.add_seq(op[1], op[2])
         elif op[0] == "fork":
             cache.fork(op[1], op[2])
+        elif op[0] == "evict":
+            cache.evict(op[1], op[2])
         else:
             t = int(sum(op[2]))
             cache.append(op[1], values["k_hist"][:, row:row + t].contiguous(),
@@ -340,7 +383,8 @@ def main():
     def step(events=None):
         cache.append(seqs, k_new, v_new)
         cache.decode(q, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws, kernel=args.kernel,
-                     partition_tokens=args.partition_tokens, work_items=args.work_items, split_events=events)
+                     partition_tokens=args.partition_tokens, work_items=args.work_items, split_events=events,
+                     window=wl.window)
         for s, L in zip(seqs, hist_len):
             cache.truncate(s, L)
 
@@ -358,7 +402,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ab = algorithmic_bytes(wl)
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
-    prof = profiled_traffic(args.config) if args.kernel in (0, 2) and not args.work_items else None
+    prof = (profiled_traffic(args.config) if args.kernel in (0, 2) and not args.work_items and not args.window
+            and not args.kv else None)
     traffic = prof[0] if prof else None
     achieved = ab["split_kernel"] / (split_avg_ms * 1e-3) / 1e9
     result = {
@@ -374,9 +419,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.kv_dtype if wl.kv_dtype != "fp8" else "fp8-e4m3 kv / bf16 q",
+        "dtype": {"fp8": "fp8-e4m3 kv / bf16 q", "int8": "int8 kv / bf16 q"}.get(wl.kv_dtype, wl.kv_dtype),
         "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block placement)",
-        "config": {"workload": wl.name, "config_id": args.config, "batch": wl.batch, "num_heads": wl.num_heads,
+        "config": {"workload": wl.name, "config_id": None if args.window else args.config, "window": wl.window,
+                   "batch": wl.batch, "num_heads": wl.num_heads,
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "attended_tokens": int(wl.attend_lens.sum()), "kv_bytes": ab["kv"],
                    "kernel": ["auto", "fma", "mfma"][args.kernel], "partition_tokens": args.partition_tokens or "auto",
@@ -406,7 +452,8 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, values, args.cpu_seconds)
+        result["cpu_baseline"] = (cpu_baseline_window(wl, values, args.cpu_seconds) if wl.window
+                                  else cpu_baseline(wl, values, args.cpu_seconds))
     print(json.dumps(result), flush=True)
 
 

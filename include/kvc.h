@@ -38,7 +38,7 @@
  *            (a (block, head) tile is head_dim/x rows of block_size 16-byte chunks)
  *    V pool: [num_layers][num_blocks][num_kv_heads][head_dim][block_size]
  *            (a (block, head) tile is V transposed: token index fastest)
- *    fp8 only: k_scale, v_scale float32 [num_layers][num_blocks][num_kv_heads];
+ *    fp8 and int8 only: k_scale, v_scale float32 [num_layers][num_blocks][num_kv_heads];
  *            the value of a stored code c is e4m3(c) * scale.
  *  Token position p of a sequence lives in block table[p / block_size] at
  *  slot p % block_size.  The slots past a sequence's length in its last block
@@ -54,6 +54,12 @@
  *  round-to-nearest-even with saturation at +-448.  The pages name E4M3 KV but
  *  give no scale rule; this is the plainest rule that never saturates a
  *  block's largest element.
+ *
+ * int8 storage: the same rule with 127 in place of 448 and enc(x) = x rounded
+ *  to the nearest integer (ties to even), clamped to +-127, stored as a
+ *  two's-complement byte; the value of code c is c * scale.  The pages list
+ *  INT8 KV quantisation ("LLM推理优化实战…" §3.4, "LLM推理优化核心技术…" §1.2) but
+ *  fix no scheme.
  */
 #ifndef KVC_H_
 #define KVC_H_
@@ -85,7 +91,8 @@ typedef enum kvc_dtype {
   KVC_F32 = 0,
   KVC_F16 = 1,
   KVC_BF16 = 2,
-  KVC_FP8_E4M3 = 3
+  KVC_FP8_E4M3 = 3,
+  KVC_INT8 = 4      /* symmetric int8 codes with per-(block, KV head) scales (rule below) */
 } kvc_dtype;
 
 typedef struct kvc_config {
@@ -97,8 +104,8 @@ typedef struct kvc_config {
   kvc_dtype kv_dtype;     /* storage dtype of the pools */
   void* k_pool;           /* device, kvc_pool_bytes() bytes; may be NULL for bookkeeping-only use */
   void* v_pool;           /* device, same size as k_pool */
-  float* k_scale;         /* device, fp8 only: kvc_scale_bytes() bytes */
-  float* v_scale;         /* device, fp8 only */
+  float* k_scale;         /* device, fp8 and int8 only: kvc_scale_bytes() bytes */
+  float* v_scale;         /* device, fp8 and int8 only */
   void* dev_scratch;      /* device, >= kvc_scratch_bytes(max batch, max tokens per append) bytes */
   size_t dev_scratch_bytes;
   const int32_t* free_order; /* host, optional: initial free list (a permutation of
@@ -196,12 +203,12 @@ kvc_status kvc_stats(const kvc_cache* cache, kvc_stats_t* out);
 /* ---- device work (asynchronous on `stream`) ------------------------------ */
 
 /* Reserve (as kvc_reserve_host) and write: copies every copy-on-write block
- * (all layers, K and V, fp8 scales) then stores the new rows of every layer in
+ * (all layers, K and V, fp8 / int8 scales) then stores the new rows of every layer in
  * their slots.  k_new / v_new: device [num_layers][T][num_kv_heads][head_dim]
  * in in_dtype, T = sum(n_new), rows sequence by sequence in call order,
- * positions ascending.  in_dtype must equal kv_dtype, except that an fp8 cache
+ * positions ascending.  in_dtype must equal kv_dtype, except that an fp8 or int8 cache
  * takes f32, f16 or bf16 rows and quantises them (rule above).  Requires
- * block_size 16, non-NULL pools (and scales for fp8) and dev_scratch of at
+ * block_size 16, non-NULL pools (and scales for fp8 / int8) and dev_scratch of at
  * least kvc_scratch_bytes(batch, T).  Calls on one handle must use one stream
  * (or the caller orders them): the device scratch is reused call to call. */
 kvc_status kvc_append(kvc_cache* cache, int32_t batch, const int64_t* seq_ids, const int32_t* n_new,
@@ -251,7 +258,7 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
 
 /* Decode attention for one layer.
  *  q:            device [batch][num_heads][head_dim], q_dtype (f32 for an f32 cache,
- *                f16 / bf16 for 16-bit caches of the same dtype, bf16 for fp8)
+ *                f16 / bf16 for 16-bit caches of the same dtype, bf16 for fp8 and int8)
  *  block_table:  device int32 [batch][max_blocks_per_seq], physical block ids
  *  context_lens: device int32 [batch], tokens to attend per sequence, >= 1,
  *                including the appended token (what kvc_export_tables writes)

@@ -22,5 +22,8 @@ Modules and the passages each follows (pages are cited by title and section):
 * ``fp8_policy`` -- the per-(block, KV head) scale rule used when fp8 KV is
   written.  Parity unpinned by the pages (they name FP8/E4M3 KV but give no
   scale rule); pinned only by self-consistency invariants.
+* ``int8_policy`` -- the same kind of scale rule for a symmetric int8 code
+  (round half to even, clamp to +-127).  Parity unpinned by the pages (they
+  list INT8 KV quantisation but give no scheme); pinned only by invariants.
 * ``sizing`` -- the KV bytes-per-token formula and pool sizes.
 """

@@ -6,7 +6,7 @@ A ``KVStoreModel`` owns a ``BlockTableModel`` and, per physical block, the
 stored rows of every (layer, KV head, slot) -- raw bit patterns for the 16/32-
 bit dtypes (writes are plain copies, so the expected contents are the input
 bits), E4M3 codes plus one fp32 scale per (layer, KV head) for fp8 (written
-with ``fp8_policy``).  It knows nothing about how the device lays blocks out in
+with ``fp8_policy``), int8 codes plus the same scales for int8 (``int8_policy``).  It knows nothing about how the device lays blocks out in
 memory; tests map device memory onto (block, layer, head, slot, dim) through
 the pool layout the library's header documents.
 
@@ -21,9 +21,11 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import blocktable, fp8_policy, e4m3
+from . import blocktable, e4m3, fp8_policy, int8_policy
 
-BITS_DTYPE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
+QUANTISED = {"fp8": fp8_policy, "int8": int8_policy}
+
+BITS_DTYPE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8, "int8": np.uint8}
 
 
 def bits_to_f64(bits, dtype: str) -> np.ndarray:
@@ -43,13 +45,13 @@ class KVStoreModel:
                  kv_dtype, free_order=None, in_dtype=None):
         self.L, self.N, self.H, self.D, self.bs = num_layers, num_blocks, num_kv_heads, head_dim, block_size
         self.kv_dtype = kv_dtype
-        self.in_dtype = in_dtype or (kv_dtype if kv_dtype != "fp8" else "bf16")
+        self.in_dtype = in_dtype or (kv_dtype if kv_dtype not in QUANTISED else "bf16")
         self.tables = blocktable.BlockTableModel(num_blocks, block_size, free_order)
         shape = (num_blocks, num_layers, num_kv_heads, block_size, head_dim)
         self.k = np.zeros(shape, dtype=BITS_DTYPE[kv_dtype])
         self.v = np.zeros(shape, dtype=BITS_DTYPE[kv_dtype])
         self.written = np.zeros((num_blocks, block_size), dtype=bool)
-        if kv_dtype == "fp8":
+        if kv_dtype in QUANTISED:
             self.k_scale = np.zeros((num_blocks, num_layers, num_kv_heads), dtype=np.float32)
             self.v_scale = np.zeros((num_blocks, num_layers, num_kv_heads), dtype=np.float32)
 
@@ -80,19 +82,20 @@ class KVStoreModel:
             self.k[dst] = self.k[src]
             self.v[dst] = self.v[src]
             self.written[dst] = self.written[src]
-            if self.kv_dtype == "fp8":
+            if self.kv_dtype in QUANTISED:
                 self.k_scale[dst] = self.k_scale[src]
                 self.v_scale[dst] = self.v_scale[src]
         k_new_bits = np.asarray(k_new_bits)
         v_new_bits = np.asarray(v_new_bits)
-        if self.kv_dtype != "fp8":
+        if self.kv_dtype not in QUANTISED:
             for t, slot in enumerate(slots):
                 blk, off = divmod(slot, self.bs)
                 self.k[blk, :, :, off, :] = k_new_bits[:, t]
                 self.v[blk, :, :, off, :] = v_new_bits[:, t]
                 self.written[blk, off] = True
             return status, slots, cow
-        # fp8: one scale update per (block, layer, head) per run of rows in a block
+        # fp8 / int8: one scale update per (block, layer, head) per run of rows in a block
+        policy = QUANTISED[self.kv_dtype]
         kx = bits_to_f64(k_new_bits, self.in_dtype).astype(np.float32)
         vx = bits_to_f64(v_new_bits, self.in_dtype).astype(np.float32)
         t = 0
@@ -107,7 +110,7 @@ class KVStoreModel:
                     for h in range(self.H):
                         for pool, scales, x in ((self.k, self.k_scale, kx), (self.v, self.v_scale, vx)):
                             held = pool[blk, layer, h, :off, :]
-                            held2, new_codes, s_new = fp8_policy.write_rows(
+                            held2, new_codes, s_new = policy.write_rows(
                                 held, scales[blk, layer, h], x[layer, t + i:t + i + run, h, :])
                             pool[blk, layer, h, :off, :] = held2
                             pool[blk, layer, h, off:off + run, :] = new_codes
@@ -121,7 +124,7 @@ class KVStoreModel:
     # logical views
     def gather(self, seq, layer=0, start=0):
         """Stored K/V of one sequence in position order, as fp64 values
-        (dequantised for fp8): ([n, Hkv, D], [n, Hkv, D]).  Positions before
+        (dequantised for fp8 and int8): ([n, Hkv, D], [n, Hkv, D]).  Positions before
         ``start`` (released by eviction, say) are returned as zeros."""
         n = self.tables.lens[seq]
         table = self.tables.tables[seq]
@@ -130,11 +133,10 @@ class KVStoreModel:
         for p in range(start, n):
             blk, off = table[p // self.bs], p % self.bs
             assert blk >= 0, "position inside a released block"
-            if self.kv_dtype == "fp8":
-                ks[p] = e4m3.decode_array(self.k[blk, layer, :, off, :]) * \
-                    self.k_scale[blk, layer, :, None].astype(np.float64)
-                vs[p] = e4m3.decode_array(self.v[blk, layer, :, off, :]) * \
-                    self.v_scale[blk, layer, :, None].astype(np.float64)
+            if self.kv_dtype in QUANTISED:
+                dec = e4m3.decode_array if self.kv_dtype == "fp8" else int8_policy.decode_array
+                ks[p] = dec(self.k[blk, layer, :, off, :]) * self.k_scale[blk, layer, :, None].astype(np.float64)
+                vs[p] = dec(self.v[blk, layer, :, off, :]) * self.v_scale[blk, layer, :, None].astype(np.float64)
             else:
                 ks[p] = bits_to_f64(self.k[blk, layer, :, off, :], self.kv_dtype)
                 vs[p] = bits_to_f64(self.v[blk, layer, :, off, :], self.kv_dtype)

@@ -4,12 +4,13 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Formula from "苦猿的大模型日记 · Day45 · 大模型推理加速", PART 02 (the one-line
 per-token formula): KV bytes per token = 2 (K and V) x num_layers x
-num_kv_heads x head_dim x dtype_bytes.  fp8 stores one byte per element; its
-per-(block, KV head) fp32 scales are extra and counted separately.
+num_kv_heads x head_dim x dtype_bytes.  fp8 and int8 store one byte per
+element; their per-(block, KV head) fp32 scales are extra and counted
+separately.
 """
 from __future__ import annotations
 
-DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}
 
 
 def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype: str) -> int:
@@ -30,5 +31,5 @@ def pool_bytes(num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: in
 
 
 def scale_bytes(num_layers: int, num_blocks: int, num_kv_heads: int) -> int:
-    """Bytes of ONE fp8 scale array (K or V): one fp32 per (layer, block, KV head)."""
+    """Bytes of ONE fp8 / int8 scale array (K or V): one fp32 per (layer, block, KV head)."""
     return num_layers * num_blocks * num_kv_heads * 4

@@ -25,8 +25,8 @@ OK, E_INVALID, E_UNSUPPORTED, E_NO_BLOCKS, E_NO_SEQ, E_SEQ_EXISTS, E_HIP, E_WORK
 STATUS_NAMES = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_NO_BLOCKS", 4: "E_NO_SEQ",
                 5: "E_SEQ_EXISTS", 6: "E_HIP", 7: "E_WORKSPACE"}
 # dtypes (kvc_dtype)
-F32, F16, BF16, FP8 = 0, 1, 2, 3
-DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8}
+F32, F16, BF16, FP8, INT8 = 0, 1, 2, 3, 4
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8, "int8": INT8}
 
 SYMBOLS = [
     "kvc_bytes_per_token", "kvc_pool_bytes", "kvc_scale_bytes", "kvc_scratch_bytes", "kvc_create", "kvc_destroy",
@@ -197,7 +197,7 @@ class KVCache:
             self.k_pool = torch.zeros(nbytes, dtype=torch.uint8, device=device)
             self.v_pool = torch.zeros(nbytes, dtype=torch.uint8, device=device)
             cfg.k_pool, cfg.v_pool = self.k_pool.data_ptr(), self.v_pool.data_ptr()
-            if kv_dtype == "fp8":
+            if kv_dtype in ("fp8", "int8"):
                 n = scale_bytes(num_layers, num_blocks, num_kv_heads) // 4
                 self.k_scale = torch.zeros(n, dtype=torch.float32, device=device)
                 self.v_scale = torch.zeros(n, dtype=torch.float32, device=device)

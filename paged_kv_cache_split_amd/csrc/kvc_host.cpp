@@ -47,7 +47,10 @@ kvc_status ok() {
   return KVC_OK;
 }
 
-bool valid_dtype(int t) { return t >= KVC_F32 && t <= KVC_FP8_E4M3; }
+bool valid_dtype(int t) { return t >= KVC_F32 && t <= KVC_INT8; }
+
+// Caches of one-byte codes with per-(block, KV head) scales.
+bool is_quantised(kvc_dtype t) { return t == KVC_FP8_E4M3 || t == KVC_INT8; }
 
 constexpr int kDeviceBlockSize = 16;
 
@@ -252,8 +255,8 @@ kvc_status check_device_ready(const kvc_cache* c) {
   if (f.block_size != kDeviceBlockSize)
     return fail(KVC_E_UNSUPPORTED, "device work needs block_size 16 (cache has %d)", f.block_size);
   if (!f.k_pool || !f.v_pool) return fail(KVC_E_INVALID, "pools are NULL (bookkeeping-only cache)");
-  if (f.kv_dtype == KVC_FP8_E4M3 && (!f.k_scale || !f.v_scale))
-    return fail(KVC_E_INVALID, "fp8 cache needs k_scale and v_scale");
+  if (is_quantised(f.kv_dtype) && (!f.k_scale || !f.v_scale))
+    return fail(KVC_E_INVALID, "an fp8 or int8 cache needs k_scale and v_scale");
   return KVC_OK;
 }
 
@@ -557,7 +560,7 @@ kvc_status kvc_append(kvc_cache* c, int32_t batch, const int64_t* seq_ids, const
   if (st != KVC_OK) return st;
   const kvc_dtype kv = c->cfg.kv_dtype;
   if (!valid_dtype(in_dtype)) return fail(KVC_E_INVALID, "unknown in_dtype");
-  if (kv == KVC_FP8_E4M3 ? in_dtype == KVC_FP8_E4M3 : in_dtype != kv)
+  if (is_quantised(kv) ? is_quantised(in_dtype) : in_dtype != kv)
     return fail(KVC_E_UNSUPPORTED, "append rows of dtype %d into a cache of dtype %d", (int)in_dtype, (int)kv);
   if (batch < 0) return fail(KVC_E_INVALID, "batch must be >= 0");
   int64_t total = 0, seg_bound = 0;
@@ -705,7 +708,7 @@ kvc_status check_attention_args(const kvc_cache* c, int32_t layer, const void* q
   if (max_blocks_per_seq < 1) return fail(KVC_E_INVALID, "max_blocks_per_seq must be >= 1");
   if (max_context_len < 1) return fail(KVC_E_INVALID, "max_context_len must be >= 1");
   const kvc_dtype kv = f.kv_dtype;
-  bool dt_ok = (kv == KVC_FP8_E4M3) ? (q_dtype == KVC_BF16) : (q_dtype == kv);
+  bool dt_ok = is_quantised(kv) ? (q_dtype == KVC_BF16) : (q_dtype == kv);
   if (!dt_ok) return fail(KVC_E_UNSUPPORTED, "q dtype %d with a cache of dtype %d", (int)q_dtype, (int)kv);
   // the split kernel takes the block max of the raw scores and scales it, so
   // the scale must not flip the order of the scores

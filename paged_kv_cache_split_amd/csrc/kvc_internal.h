@@ -44,6 +44,7 @@ __host__ __device__ inline int dtype_bytes(kvc_dtype t) {
     case KVC_F16: return 2;
     case KVC_BF16: return 2;
     case KVC_FP8_E4M3: return 1;
+    case KVC_INT8: return 1;
   }
   return 0;
 }
@@ -90,7 +91,9 @@ constexpr int32_t kDefaultPoolShift = 3;
 // results do not depend on the device's CU count.
 constexpr int32_t kDefaultWaves16 = 1024;
 constexpr int32_t kDefaultWavesFp8 = 1024;
-inline int32_t default_waves(kvc_dtype kv) { return kv == KVC_FP8_E4M3 ? kDefaultWavesFp8 : kDefaultWaves16; }
+inline int32_t default_waves(kvc_dtype kv) {
+  return (kv == KVC_FP8_E4M3 || kv == KVC_INT8) ? kDefaultWavesFp8 : kDefaultWaves16;
+}
 
 // Byte offsets inside the decode workspace.  FMA kernel: partial rows
 // [B][Hq][num_partitions] (acc, m, l).  MFMA kernel: partial rows

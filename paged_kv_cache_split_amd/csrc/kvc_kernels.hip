@@ -137,6 +137,24 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | (code > 0x7Eu ? 0x7Eu : code);
 }
 
+// int8 code (a two's-complement byte) -> its integer value.
+__device__ __forceinline__ float int8_decode(uint32_t c) { return (float)(int8_t)(uint8_t)c; }
+
+// float -> int8 code: nearest integer, ties to even, clamped to +-127.
+__device__ __forceinline__ uint32_t int8_encode(float x) {
+  const float q = fminf(fmaxf(__builtin_rintf(x), -127.0f), 127.0f);
+  return (uint32_t)(uint8_t)(int8_t)(int)q;
+}
+
+// One-byte caches (fp8 E4M3 and int8): codes times a per-(block, KV head) scale.
+constexpr bool is_byte_code(kvc_dtype t) { return t == KVC_FP8_E4M3 || t == KVC_INT8; }
+
+template <kvc_dtype KV>
+__device__ __forceinline__ float code_decode(uint32_t c) {
+  if constexpr (KV == KVC_FP8_E4M3) return e4m3_decode(c);
+  else return int8_decode(c);
+}
+
 template <kvc_dtype T>
 __device__ __forceinline__ float load_elem(const void* base, int64_t i) {
   if constexpr (T == KVC_F32) return static_cast<const float*>(base)[i];
@@ -183,7 +201,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(PoolDesc p, const CowP
     *reinterpret_cast<u32x4*>(p.k + dst + i) = *reinterpret_cast<const u32x4*>(p.k + src + i);
     *reinterpret_cast<u32x4*>(p.v + dst + i) = *reinterpret_cast<const u32x4*>(p.v + src + i);
   }
-  if (p.dtype == KVC_FP8_E4M3) {
+  if (is_byte_code(p.dtype)) {
     const int64_t so = ((int64_t)layer * p.num_blocks + pr.src) * p.num_kv_heads;
     const int64_t dof = ((int64_t)layer * p.num_blocks + pr.dst) * p.num_kv_heads;
     for (int h = threadIdx.x; h < p.num_kv_heads; h += 256) {
@@ -241,14 +259,20 @@ __global__ __launch_bounds__(64) void append_copy_kernel(PoolDesc p, SEGS segs, 
 }
 
 // ---------------------------------------------------------------------------
-// Append into an fp8 (E4M3) cache: per (segment, KV head, K or V) apply the
-// scale rule -- s_new = max(s_old, amax/448); re-encode held codes when the
-// scale grows; encode the new rows with s_new.  grid (num_segments,
-// num_kv_heads, 2 * num_layers), 64 threads (one wave).
+// Append into a one-byte cache (fp8 E4M3, or int8): per (segment, KV head, K
+// or V) apply the scale rule -- s_new = max(s_old, amax / MAXC) with MAXC =
+// 448 (E4M3) or 127 (int8); re-encode held codes when the scale grows; encode
+// the new rows with s_new.  grid (num_segments, num_kv_heads, 2 *
+// num_layers), 64 threads (one wave).
 // ---------------------------------------------------------------------------
-template <kvc_dtype IN, typename SEGS>
-__global__ __launch_bounds__(64) void append_fp8_kernel(PoolDesc p, SEGS segs, const void* k_new,
-                                                        const void* v_new, int64_t total_rows) {
+template <kvc_dtype KV, kvc_dtype IN, typename SEGS>
+__global__ __launch_bounds__(64) void append_quant_kernel(PoolDesc p, SEGS segs, const void* k_new,
+                                                          const void* v_new, int64_t total_rows) {
+  constexpr float kMaxCode = (KV == KVC_FP8_E4M3) ? 448.0f : 127.0f;
+  auto enc = [](float x) -> uint32_t {
+    if constexpr (KV == KVC_FP8_E4M3) return e4m3_encode(x);
+    else return int8_encode(x);
+  };
   const AppendSegment sg = segs.get(blockIdx.x);
   const int h = blockIdx.y;
   const int layer = blockIdx.z >> 1;
@@ -272,19 +296,19 @@ __global__ __launch_bounds__(64) void append_fp8_kernel(PoolDesc p, SEGS segs, c
   }
   amax = wave_max(amax);
   const float s_old = sg.offset > 0 ? *scale_ptr : 0.0f;
-  const float s_new = fmaxf(s_old, amax / 448.0f);
+  const float s_new = fmaxf(s_old, amax / kMaxCode);
   if (s_new > s_old && sg.offset > 0) {
     for (int i = lane; i < sg.offset * D; i += 64) {
       int r = i / D, d = i % D;
       int64_t o = at(r, d);
-      float x = e4m3_decode(tile[o]) * s_old;
-      tile[o] = (uint8_t)e4m3_encode(x / s_new);
+      float x = code_decode<KV>(tile[o]) * s_old;
+      tile[o] = (uint8_t)enc(x / s_new);
     }
   }
   for (int i = lane; i < sg.count * D; i += 64) {
     int r = i / D, d = i % D;
     float x = load_elem<IN>(src, src_row0 + (int64_t)r * H * D + d);
-    tile[at(sg.offset + r, d)] = (uint8_t)e4m3_encode(s_new > 0.0f ? x / s_new : x);
+    tile[at(sg.offset + r, d)] = (uint8_t)enc(s_new > 0.0f ? x / s_new : x);
   }
   if (lane == 0) *scale_ptr = s_new;
 }
@@ -367,7 +391,7 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
     }
     return;
   }
-  constexpr int EB = (KV == KVC_F32) ? 4 : (KV == KVC_FP8_E4M3 ? 1 : 2);
+  constexpr int EB = (KV == KVC_F32) ? 4 : (is_byte_code(KV) ? 1 : 2);
   constexpr int X = 16 / EB;
   constexpr int NCH = D / X;        // 16-byte chunks per token row
   constexpr int CPL = NCH / 4;      // chunks per lane
@@ -399,7 +423,7 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
     const char* kt = a.k + toff;
     const char* vt = a.v + toff;
     float ksc = 1.0f, vsc = 1.0f;
-    if constexpr (KV == KVC_FP8_E4M3) {
+    if constexpr (is_byte_code(KV)) {
       ksc = a.k_scale[(int64_t)phys * a.num_kv_heads + g];
       vsc = a.v_scale[(int64_t)phys * a.num_kv_heads + g];
     }
@@ -414,9 +438,9 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
       if constexpr (KV == KVC_F32) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) kx[e] = __uint_as_float(raw[e]);
-      } else if constexpr (KV == KVC_FP8_E4M3) {
+      } else if constexpr (is_byte_code(KV)) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) kx[e] = e4m3_decode((raw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        for (int e = 0; e < 16; ++e) kx[e] = code_decode<KV>((raw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -465,10 +489,10 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) vx[q4 * 4 + e] = __uint_as_float(r[e]);
         }
-      } else if constexpr (KV == KVC_FP8_E4M3) {
+      } else if constexpr (is_byte_code(KV)) {
         u32x4 r = *reinterpret_cast<const u32x4*>(vrow);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) vx[e] = e4m3_decode((r[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        for (int e = 0; e < 16; ++e) vx[e] = code_decode<KV>((r[e >> 2] >> (8 * (e & 3))) & 0xFFu);
       } else {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -564,13 +588,27 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// Two int8 codes (bytes 0,1 or 2,3 of w) -> two bf16 packed in a dword.
+// Integers up to 127 in magnitude are exact in bf16.
+template <bool HI>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
+  constexpr int sh = HI ? 16 : 0;
+  return pack_bf16x2((float)(int8_t)(w >> sh), (float)(int8_t)(w >> (sh + 8)));
+}
+
+template <kvc_dtype KV, bool HI>
+__device__ __forceinline__ uint32_t code2_to_bf16x2(uint32_t w) {
+  if constexpr (KV == KVC_FP8_E4M3) return fp8x2_to_bf16x2<HI>(w);
+  else return i8x2_to_bf16x2<HI>(w);
+}
+
 template <kvc_dtype KV, int D>
 struct KvBlock {
-  static constexpr int NK = (KV == KVC_FP8_E4M3) ? D / 64 : D / 32;  // 16-byte K loads per lane
+  static constexpr int NK = is_byte_code(KV) ? D / 64 : D / 32;  // 16-byte K loads per lane
   static constexpr int NV = D / 16;                                   // V^T loads per lane
   u32x4 k[NK];
-  typename std::conditional<KV == KVC_FP8_E4M3, uint32_t, u32x2>::type v[NV];
-  float ks, vs;  // fp8: the (block, head) scales, fetched with the tile
+  typename std::conditional<is_byte_code(KV), uint32_t, u32x2>::type v[NV];
+  float ks, vs;  // one-byte codes: the (block, head) scales, fetched with the tile
 };
 
 // K/V tiles are read once per step: non-temporal loads (streaming cache
@@ -590,19 +628,19 @@ template <kvc_dtype KV>
 __device__ __forceinline__ uint32_t k_lane_offset(int lane) { return (uint32_t)lane * 16u; }
 template <kvc_dtype KV>
 __device__ __forceinline__ uint32_t v_lane_offset(int nn, int r) {
-  constexpr uint32_t E = (KV == KVC_FP8_E4M3) ? 1u : 2u;
+  constexpr uint32_t E = is_byte_code(KV) ? 1u : 2u;
   return ((uint32_t)nn * kBS + 4u * (uint32_t)r) * E;
 }
 
 template <kvc_dtype KV, int D>
 __device__ __forceinline__ void load_block(KvBlock<KV, D>& blk, const char* kt, const char* vt, uint32_t koff,
                                            uint32_t voff) {
-  constexpr int E = (KV == KVC_FP8_E4M3) ? 1 : 2;
+  constexpr int E = is_byte_code(KV) ? 1 : 2;
 #pragma unroll
   for (int kk = 0; kk < KvBlock<KV, D>::NK; ++kk) blk.k[kk] = load_stream<u32x4>(kt + koff + kk * 1024);
 #pragma unroll
   for (int dd = 0; dd < KvBlock<KV, D>::NV; ++dd) {
-    if constexpr (KV == KVC_FP8_E4M3) blk.v[dd] = load_stream<uint32_t>(vt + voff + dd * 16 * kBS * E);
+    if constexpr (is_byte_code(KV)) blk.v[dd] = load_stream<uint32_t>(vt + voff + dd * 16 * kBS * E);
     else blk.v[dd] = load_stream<u32x2>(vt + voff + dd * 16 * kBS * E);
   }
 }
@@ -837,7 +875,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
 #pragma unroll
         for (int kk = 0; kk < NQK; ++kk) {
           int d0;
-          if constexpr (KV == KVC_FP8_E4M3) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
+          if constexpr (is_byte_code(KV)) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
           else d0 = (4 * kk + r) * 8;
           qv[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
         }
@@ -862,20 +900,20 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
           floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
           float qk = a.qk_scale;
           float vsc = 1.0f;
-          if constexpr (KV == KVC_FP8_E4M3) {
+          if constexpr (is_byte_code(KV)) {
             qk *= cur.ks;
             vsc = cur.vs;
 #pragma unroll
             for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
               u32x4 lo, hi;
-              lo[0] = fp8x2_to_bf16x2<false>(cur.k[c2][0]);
-              lo[1] = fp8x2_to_bf16x2<true>(cur.k[c2][0]);
-              lo[2] = fp8x2_to_bf16x2<false>(cur.k[c2][1]);
-              lo[3] = fp8x2_to_bf16x2<true>(cur.k[c2][1]);
-              hi[0] = fp8x2_to_bf16x2<false>(cur.k[c2][2]);
-              hi[1] = fp8x2_to_bf16x2<true>(cur.k[c2][2]);
-              hi[2] = fp8x2_to_bf16x2<false>(cur.k[c2][3]);
-              hi[3] = fp8x2_to_bf16x2<true>(cur.k[c2][3]);
+              lo[0] = code2_to_bf16x2<KV, false>(cur.k[c2][0]);
+              lo[1] = code2_to_bf16x2<KV, true>(cur.k[c2][0]);
+              lo[2] = code2_to_bf16x2<KV, false>(cur.k[c2][1]);
+              lo[3] = code2_to_bf16x2<KV, true>(cur.k[c2][1]);
+              hi[0] = code2_to_bf16x2<KV, false>(cur.k[c2][2]);
+              hi[1] = code2_to_bf16x2<KV, true>(cur.k[c2][2]);
+              hi[2] = code2_to_bf16x2<KV, false>(cur.k[c2][3]);
+              hi[3] = code2_to_bf16x2<KV, true>(cur.k[c2][3]);
               s = mfma_qk<KV>(lo, qv[2 * c2], s);
               s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
             }
@@ -899,7 +937,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
             for (int e = 0; e < 4; ++e)
               if (t0 + e >= ncol || t0 + e < col_lo) sv[e] = kNegInf;
             const int vr = n - t0;                     // rows of this lane's four inside the sequence
-            if constexpr (KV == KVC_FP8_E4M3) {
+            if constexpr (is_byte_code(KV)) {
               const uint32_t keep = vr >= 4 ? 0xFFFFFFFFu : (vr <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * vr)));
 #pragma unroll
               for (int dd = 0; dd < NDD; ++dd) cur.v[dd] &= keep;
@@ -946,7 +984,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
             pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
             pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
           } else {
-            if constexpr (KV == KVC_FP8_E4M3) {
+            if constexpr (is_byte_code(KV)) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) pv[e] *= vsc;
             }
@@ -958,9 +996,9 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
 #pragma unroll
           for (int dd = 0; dd < NDD; ++dd) {
             u32x2 va;
-            if constexpr (KV == KVC_FP8_E4M3) {
-              va[0] = fp8x2_to_bf16x2<false>(cur.v[dd]);
-              va[1] = fp8x2_to_bf16x2<true>(cur.v[dd]);
+            if constexpr (is_byte_code(KV)) {
+              va[0] = code2_to_bf16x2<KV, false>(cur.v[dd]);
+              va[1] = code2_to_bf16x2<KV, true>(cur.v[dd]);
             } else {
               va = cur.v[dd];
             }
@@ -976,7 +1014,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
         auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
           const int64_t o = (int64_t)ph * block_stride + head_off;
           load_block<KV, D>(dst, a.k + o, a.v + o, koff, voff);
-          if constexpr (KV == KVC_FP8_E4M3) {
+          if constexpr (is_byte_code(KV)) {
             dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
             dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
           }
@@ -1225,11 +1263,13 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     return e;
   }
   if constexpr (KV != KVC_F32) {
-    constexpr int PF = (KV == KVC_FP8_E4M3) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_16;  // blocks in flight per wave
+    constexpr int PF = is_byte_code(KV) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_16;  // blocks in flight per wave
     // ticket counters start at zero (a kernel, not a memset, so the sequence
-    // can be captured in a graph)
-    hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, s, a.ws_ticket, a.num_kv_heads);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // can be captured in a graph); without a pool no wave touches them
+    if (a.pool_pieces > 0 && tile_groups == 0) {
+      hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, s, a.ws_ticket, a.num_kv_heads);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
     const int threads = ((a.group * (D / 4) + 63) / 64) * 64;   // <= 16 heads * 32 columns = 512
     if (tile_groups == 0) {
@@ -1266,6 +1306,22 @@ hipError_t launch_copy_blocks(const PoolDesc& pool, const CowPair* pairs_dev, in
   return hipGetLastError();
 }
 
+template <kvc_dtype KV, typename SEGS>
+hipError_t launch_append_quant(const PoolDesc& pool, const SEGS& segs, int32_t num_segments, const void* k_new,
+                               const void* v_new, kvc_dtype in_dtype, int64_t total_rows, hipStream_t stream) {
+  const dim3 g8(num_segments, pool.num_kv_heads, 2 * pool.num_layers);
+  if (in_dtype == KVC_F32)
+    hipLaunchKernelGGL((append_quant_kernel<KV, KVC_F32, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new,
+                       total_rows);
+  else if (in_dtype == KVC_F16)
+    hipLaunchKernelGGL((append_quant_kernel<KV, KVC_F16, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new,
+                       total_rows);
+  else
+    hipLaunchKernelGGL((append_quant_kernel<KV, KVC_BF16, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new,
+                       total_rows);
+  return hipGetLastError();
+}
+
 template <typename SEGS>
 hipError_t launch_append_from(const PoolDesc& pool, const SEGS& segs, int32_t num_segments, const void* k_new,
                               const void* v_new, kvc_dtype in_dtype, int64_t total_rows, hipStream_t stream) {
@@ -1280,16 +1336,10 @@ hipError_t launch_append_from(const PoolDesc& pool, const SEGS& segs, int32_t nu
     case KVC_BF16:
       hipLaunchKernelGGL((append_copy_kernel<2, SEGS>), grid, dim3(64), 0, stream, pool, segs, kn, vn, total_rows);
       break;
-    case KVC_FP8_E4M3: {
-      const dim3 g8(num_segments, pool.num_kv_heads, 2 * pool.num_layers);
-      if (in_dtype == KVC_F32)
-        hipLaunchKernelGGL((append_fp8_kernel<KVC_F32, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new, total_rows);
-      else if (in_dtype == KVC_F16)
-        hipLaunchKernelGGL((append_fp8_kernel<KVC_F16, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new, total_rows);
-      else
-        hipLaunchKernelGGL((append_fp8_kernel<KVC_BF16, SEGS>), g8, dim3(64), 0, stream, pool, segs, k_new, v_new, total_rows);
-      break;
-    }
+    case KVC_FP8_E4M3:
+      return launch_append_quant<KVC_FP8_E4M3>(pool, segs, num_segments, k_new, v_new, in_dtype, total_rows, stream);
+    case KVC_INT8:
+      return launch_append_quant<KVC_INT8>(pool, segs, num_segments, k_new, v_new, in_dtype, total_rows, stream);
   }
   return hipGetLastError();
 }
@@ -1361,6 +1411,8 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
       return launch_decode_typed<KVC_BF16, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
     case KVC_FP8_E4M3:
       return launch_decode_typed<KVC_FP8_E4M3, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
+    case KVC_INT8:
+      return launch_decode_typed<KVC_INT8, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
   }
   (void)q_dtype;
   return hipErrorInvalidValue;

@@ -14,14 +14,15 @@ from workloads import make_values, setup_ops
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 BITS_TORCH = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
-BITS_NP = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+BITS_NP = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8, "int8": np.uint8}
+QUANTISED = ("fp8", "int8")
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}
 
 
 def to_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
     """Raw storage bits of a tensor of the given dtype, as an unsigned numpy array."""
     t = t.detach().cpu().contiguous()
-    if dtype == "fp8":
+    if dtype in QUANTISED:
         return t.view(torch.uint8).numpy()
     return t.view(BITS_TORCH[dtype]).numpy().view(BITS_NP[dtype])
 
@@ -45,7 +46,7 @@ def read_pools(cache):
     v = cache.v_pool.detach().cpu().numpy().view(BITS_NP[dt]).reshape(L, N, H, D, bs)
     v = v.transpose(1, 0, 2, 4, 3)
     out = dict(k=np.ascontiguousarray(k), v=np.ascontiguousarray(v))
-    if dt == "fp8":
+    if dt in QUANTISED:
         out["k_scale"] = cache.k_scale.cpu().numpy().reshape(L, N, H).transpose(1, 0, 2).copy()
         out["v_scale"] = cache.v_scale.cpu().numpy().reshape(L, N, H).transpose(1, 0, 2).copy()
     return out

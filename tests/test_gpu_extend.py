@@ -35,7 +35,7 @@ def _check_pools(cache, st, wl):
     pools = read_pools(cache)
     assert np.array_equal(pools["k"], st.k), "K pool differs from the oracle's store"
     assert np.array_equal(pools["v"], st.v), "V pool differs from the oracle's store"
-    if wl.kv_dtype == "fp8":
+    if wl.kv_dtype in ("fp8", "int8"):
         assert np.array_equal(pools["k_scale"].view(np.uint32), st.k_scale.view(np.uint32))
         assert np.array_equal(pools["v_scale"].view(np.uint32), st.v_scale.view(np.uint32))
 
@@ -54,7 +54,7 @@ def test_small_extend_workloads(kind):
     check_close(to_f64(out), oracle_extend(st, wl, values), *TOL, f"extend {kind}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "int8"])
 @pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (16, 16, 64), (16, 1, 128), (12, 3, 64), (64, 8, 128)])
 def test_ragged_query_counts(kv, hq, hkv, d):
     # history lengths and new tokens per sequence: none, one, within a tile,
@@ -94,7 +94,7 @@ def test_one_token_per_sequence_matches_decode_bitwise(kv):
     assert torch.equal(dec.view(torch.int16), ext.view(torch.int16))
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "f32"])
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "int8", "f32"])
 def test_unwritten_slots_holding_nan(kv):
     # Pools whose every byte is 0xFF (a NaN in each dtype) before anything is
     # written: the slots past each sequence's end in its last block are read

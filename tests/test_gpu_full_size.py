@@ -81,14 +81,14 @@ def test_full_size_sampled(cid):
         for i, blk in enumerate(st.tables.tables[0]):
             assert np.array_equal(pools["k"][tab[i]], st.k[blk]), f"seq {b} block {i} K"
             assert np.array_equal(pools["v"][tab[i]], st.v[blk]), f"seq {b} block {i} V"
-            if wl.kv_dtype == "fp8":
+            if wl.kv_dtype in ("fp8", "int8"):
                 assert np.array_equal(pools["k_scale"][tab[i]].view(np.uint32), st.k_scale[blk].view(np.uint32))
                 assert np.array_equal(pools["v_scale"][tab[i]].view(np.uint32), st.v_scale[blk].view(np.uint32))
         k, v = st.gather(0)
         ref = decode_attention(q[b], k, v, wl.scale)
         ma, mr = check_close(got_all[b], ref, 2e-3, 1e-2, f"config {cid} seq {b}")
         msg = f"  seq {b} (L={int(L[b])}): max_abs {ma:.2e} max_rel {mr:.2e}"
-        if wl.kv_dtype == "fp8":
+        if wl.kv_dtype in ("fp8", "int8"):
             ku, vu = logical_history(wl, values, b)
             ma2, _ = check_close(got_all[b], decode_attention(q[b], ku, vu, wl.scale), 5e-2, 1e-2,
                                  f"config {cid} seq {b} vs unquantised rows")

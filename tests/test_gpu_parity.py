@@ -21,7 +21,7 @@ from workloads import custom_workload, make_values, make_workload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-TOL = {"f32": (2e-3, 1e-2), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2), "fp8": (2e-3, 1e-2)}
+TOL = {"f32": (2e-3, 1e-2), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2), "fp8": (2e-3, 1e-2), "int8": (2e-3, 1e-2)}
 FP8_UNQUANT_TOL = (5e-2, 1e-2)
 
 
@@ -37,7 +37,7 @@ def _check_append(cache, st, wl, bt, cl):
     pools = read_pools(cache)
     assert np.array_equal(pools["k"], st.k), "K pool differs from the oracle's store"
     assert np.array_equal(pools["v"], st.v), "V pool differs from the oracle's store"
-    if wl.kv_dtype == "fp8":
+    if wl.kv_dtype in ("fp8", "int8"):
         assert np.array_equal(pools["k_scale"].view(np.uint32), st.k_scale.view(np.uint32))
         assert np.array_equal(pools["v_scale"].view(np.uint32), st.v_scale.view(np.uint32))
     rows, lens = st.tables.export(list(range(wl.batch)), bt.shape[1])
@@ -46,9 +46,10 @@ def _check_append(cache, st, wl, bt, cl):
     assert np.array_equal(cl.cpu().numpy(), wl.attend_lens)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, "5-int8"])
 def test_small_configs_append_and_decode(cid):
-    wl = make_workload(cid, small=True)
+    # "5-int8": the fp8 mixed batch with an int8 cache instead
+    wl = make_workload(5, small=True, kv_dtype="int8") if cid == "5-int8" else make_workload(cid, small=True)
     _say(f"[parity] config {cid} (small): {wl.name}")
     values = make_values(wl, "cpu")
     st = oracle_run(wl, values)
@@ -63,7 +64,7 @@ def test_small_configs_append_and_decode(cid):
         got = to_f64(o)
         ma, mr = check_close(got, ref, atol, rtol, f"config {cid} kernel {kernel}")
         _say(f"  kernel {kernel}: max_abs {ma:.2e} max_rel {mr:.2e}")
-    if wl.kv_dtype == "fp8":
+    if wl.kv_dtype in ("fp8", "int8"):
         # end to end, quantisation error included: against the unquantised rows
         # (the lengths here start at 256, as in the full fp8 workload)
         from oracle.attention import decode_attention
@@ -72,12 +73,12 @@ def test_small_configs_append_and_decode(cid):
         for b in range(wl.batch):
             k, v = logical_history(wl, values, b)
             r = decode_attention(q[b], k, v, wl.scale)
-            ma, _ = check_close(to_f64(out[b]), r, *FP8_UNQUANT_TOL, f"config 5 seq {b} vs unquantised rows")
+            ma, _ = check_close(to_f64(out[b]), r, *FP8_UNQUANT_TOL, f"config {cid} seq {b} vs unquantised rows")
             worst = max(worst, ma)
-        _say(f"  fp8 vs unquantised rows: max_abs {worst:.2e}")
+        _say(f"  {wl.kv_dtype} vs unquantised rows: max_abs {worst:.2e}")
 
 
-@pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "fp8", "int8"])
 @pytest.mark.parametrize("pt", [16, 64])
 def test_partition_boundaries(kv, pt):
     # Lengths around block and partition edges.  The FMA kernel cuts each
@@ -120,7 +121,7 @@ def test_long_segments_cross_the_block_id_window():
             check_close(to_f64(o), ref, *TOL[kv], f"{kv} work_items={wi}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "int8"])
 def test_dynamic_pool_pieces(kv):
     # The MFMA kernel hands the last 1/2^shift of every wave's run out at run
     # time in `pieces` pieces.  Cases: pieces cut across sequence boundaries,
@@ -148,7 +149,7 @@ def test_dynamic_pool_pieces(kv):
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (8, 4, 128), (16, 4, 64), (16, 1, 128), (32, 2, 128), (12, 3, 64)])
-@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "int8"])
 def test_head_groupings(hq, hkv, d, kv):
     lens = [5, 40, 300, 129]
     wl = custom_workload(len(lens), hq, hkv, d, kv, lens, seed=hq * 7 + hkv, name="groupings")
@@ -164,7 +165,7 @@ def test_head_groupings(hq, hkv, d, kv):
         check_close(to_f64(o), ref, *TOL[kv], f"{hq}/{hkv} D{d} {kv} kernel {kernel}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 def test_placement_invariance_and_determinism(kv):
     lens = [100, 33, 257, 1]
     outs = []
@@ -184,7 +185,7 @@ def test_placement_invariance_and_determinism(kv):
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "result depends on placement"
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 def test_fork_mid_block_copy_on_write(kv):
     # prefix of 21 tokens (block 1 half full) shared by 3 sequences; each then
     # appends its own rows: the first write into the shared half block copies it.
@@ -211,7 +212,7 @@ def test_stream_copy_calibration_kernel():
     assert torch.equal(src, dst)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8", "f32"])
 def test_multi_layer_pool_and_cow(kv):
     # three layers share one block id space: appends write every layer, a
     # copy-on-write copies every layer (and fp8 scales), decode reads one layer

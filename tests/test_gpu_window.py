@@ -36,7 +36,7 @@ def _check_state(cache, st, wl, bt, cl):
     pools = read_pools(cache)
     assert np.array_equal(pools["k"], st.k), "K pool differs from the oracle's store"
     assert np.array_equal(pools["v"], st.v), "V pool differs from the oracle's store"
-    if wl.kv_dtype == "fp8":
+    if wl.kv_dtype in ("fp8", "int8"):
         assert np.array_equal(pools["k_scale"].view(np.uint32), st.k_scale.view(np.uint32))
         assert np.array_equal(pools["v_scale"].view(np.uint32), st.v_scale.view(np.uint32))
     rows, lens = st.tables.export(list(range(wl.batch)), bt.shape[1])
@@ -45,7 +45,7 @@ def _check_state(cache, st, wl, bt, cl):
     assert (bt.cpu().numpy() == -1).any(), "no block was released"
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "f32"])
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "int8", "f32"])
 def test_window_decode_after_eviction(kv):
     wl = make_window_workload(small=True, kv_dtype=kv)
     _say(f"[window] decode {kv}: {wl.name}")

@@ -121,3 +121,50 @@ def test_all_zero_rows_store_zero_codes():
     neg = -np.zeros((1, 8), np.float32)
     _, codes, _ = fp8_policy.write_rows(np.zeros((0, 8), np.uint8), 0.0, neg)
     assert np.all(codes == 0x80)
+
+
+# -- int8 scale rule (parity unpinned by the pages: invariants only) -------------
+
+from oracle import int8_policy  # noqa: E402
+
+
+def test_int8_codec_is_twos_complement_rounding_half_even():
+    x = np.array([0.0, 0.5, 1.5, 2.5, -0.5, -1.5, 126.5, 127.4, 200.0, -127.6, -300.0], dtype=np.float32)
+    codes = int8_policy.encode_array(x)
+    assert codes.dtype == np.uint8
+    assert list(int8_policy.decode_array(codes)) == [0, 0, 2, 2, -0.0, -2, 126, 127, 127, -127, -127]
+    # every code decodes to its own integer
+    allc = np.arange(256, dtype=np.int32).astype(np.uint8)
+    assert np.array_equal(int8_policy.decode_array(allc), allc.view(np.int8).astype(np.float64))
+
+
+def test_int8_rule_invariants():
+    rng = np.random.default_rng(17)
+    for trial in range(200):
+        d = 16
+        held_vals = rng.standard_normal((rng.integers(0, 6), d)).astype(np.float32) * rng.choice([0.01, 1, 50])
+        held, _, s0 = int8_policy.write_rows(np.zeros((0, d), np.uint8), 0, held_vals)
+        new_vals = rng.standard_normal((rng.integers(1, 5), d)).astype(np.float32) * rng.choice([0.01, 1, 300])
+        held2, new_codes, s1 = int8_policy.write_rows(held, s0, new_vals)
+        assert s1.dtype == np.float32
+        if held.shape[0]:
+            assert s1 >= s0                                            # a filled block's scale never shrinks
+        amax = float(np.max(np.abs(new_vals)))
+        assert s1 >= np.float32(amax / np.float32(127))
+        # the largest new element is not clipped, and every new value is
+        # within half a step of its code
+        deq = int8_policy.dequantize(new_codes, s1)
+        assert np.all(np.abs(deq - new_vals.astype(np.float64)) <= 0.5 * float(s1) * (1 + 1e-6) + 1e-30)
+        # held rows: unchanged when the scale did not move, else within one step
+        if held.shape[0]:
+            if s1 == s0:
+                assert np.array_equal(held2, held)
+            else:
+                before = int8_policy.dequantize(held, s0)
+                after = int8_policy.dequantize(held2, s1)
+                assert np.all(np.abs(after - before) <= 0.5 * float(s1) * (1 + 1e-6) + 1e-30)
+
+
+def test_int8_zero_rows_keep_scale_zero():
+    held, new, s = int8_policy.write_rows(np.zeros((0, 8), np.uint8), 0, np.zeros((3, 8), np.float32))
+    assert s == 0 and not new.any()

@@ -23,6 +23,7 @@ import numpy as np
 BLOCK_SIZE = 16
 
 TORCH_DTYPE_NAMES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+QUANTISED = ("fp8", "int8")   # caches of one-byte codes; q and the appended rows are bf16
 
 
 @dataclass
@@ -150,6 +151,8 @@ def make_workload(cid: int, seed: int | None = None, small: bool = False, **over
     """Build config ``cid`` (1..5).  ``seed`` defaults to the config number."""
     p = dict((SMALL if small else CONFIGS)[cid])
     p.update(override)
+    if "kv_dtype" in override and override["kv_dtype"] != CONFIGS[cid]["kv_dtype"]:
+        p["name"] = f"{p['name']} -- with a {override['kv_dtype']} cache"
     seed = cid if seed is None else seed
     rng = np.random.default_rng(seed)
     lens = _lengths(cid, rng, p)
@@ -159,7 +162,7 @@ def make_workload(cid: int, seed: int | None = None, small: bool = False, **over
     return Workload(name=p["name"], batch=p["batch"], num_heads=p["num_heads"],
                     num_kv_heads=p["num_kv_heads"], head_dim=p["head_dim"],
                     q_dtype=p["q_dtype"], kv_dtype=kv,
-                    new_dtype=("bf16" if kv == "fp8" else kv),
+                    new_dtype=("bf16" if kv in QUANTISED else kv),
                     context_lens=lens, shared_prefix=int(p["shared_prefix"]),
                     num_blocks=int(pool), free_order=free_order, seed=seed)
 
@@ -174,10 +177,10 @@ def custom_workload(batch, num_heads, num_kv_heads, head_dim, kv_dtype, context_
     qls = None if query_lens is None else np.asarray(query_lens, dtype=np.int64)
     pool = num_blocks or _exact_pool(lens, shared_prefix, qls)
     free_order = rng.permutation(pool).astype(np.int32)
-    q_dtype = q_dtype or ("bf16" if kv_dtype == "fp8" else kv_dtype)
+    q_dtype = q_dtype or ("bf16" if kv_dtype in QUANTISED else kv_dtype)
     return Workload(name=name, batch=batch, num_heads=num_heads, num_kv_heads=num_kv_heads,
                     head_dim=head_dim, q_dtype=q_dtype, kv_dtype=kv_dtype,
-                    new_dtype=("bf16" if kv_dtype == "fp8" else kv_dtype),
+                    new_dtype=("bf16" if kv_dtype in QUANTISED else kv_dtype),
                     context_lens=lens, shared_prefix=int(shared_prefix), num_blocks=int(pool),
                     free_order=free_order, seed=seed, query_lens=qls)
 
@@ -225,8 +228,8 @@ def make_extend_workload(kind: str, seed: int | None = None, small: bool = False
     free_order = rng.permutation(pool).astype(np.int32)
     kv = p["kv_dtype"]
     return Workload(name=p["name"], batch=p["batch"], num_heads=p["num_heads"], num_kv_heads=p["num_kv_heads"],
-                    head_dim=p["head_dim"], q_dtype=("bf16" if kv == "fp8" else kv), kv_dtype=kv,
-                    new_dtype=("bf16" if kv == "fp8" else kv), context_lens=lens, shared_prefix=0,
+                    head_dim=p["head_dim"], q_dtype=("bf16" if kv in QUANTISED else kv), kv_dtype=kv,
+                    new_dtype=("bf16" if kv in QUANTISED else kv), context_lens=lens, shared_prefix=0,
                     num_blocks=int(pool), free_order=free_order, seed=seed, query_lens=qls)
 
 
@@ -321,8 +324,8 @@ def make_window_workload(kind: str = "decode", seed: int = 8, small: bool = Fals
     free_order = rng.permutation(pool).astype(np.int32)
     kv = kv_dtype or p["kv_dtype"]
     return Workload(name=p["name"], batch=B, num_heads=p["num_heads"], num_kv_heads=p["num_kv_heads"],
-                    head_dim=p["head_dim"], q_dtype=("bf16" if kv == "fp8" else kv), kv_dtype=kv,
-                    new_dtype=("bf16" if kv == "fp8" else kv), context_lens=lens, shared_prefix=0,
+                    head_dim=p["head_dim"], q_dtype=("bf16" if kv in QUANTISED else kv), kv_dtype=kv,
+                    new_dtype=("bf16" if kv in QUANTISED else kv), context_lens=lens, shared_prefix=0,
                     num_blocks=int(pool), free_order=free_order, seed=seed, query_lens=qls, window=W,
                     evict_chunk=C)
 
