@@ -323,6 +323,62 @@ kvc_status kvc_extend_attention(kvc_cache* cache, int32_t layer, const void* q, 
                                 float scale, void* out, void* workspace, size_t workspace_bytes,
                                 const kvc_decode_opts* opts, kvc_stream_t stream);
 
+/* ---- continuous-batching scheduler (host only) ------------------------------ */
+
+/* Iteration-level scheduling of requests over one cache ("LLM推理优化实战…" §5.2:
+ * every iteration keeps the unfinished running requests, tops the batch up
+ * from the waiting queue, and frees a finished request's KV cache), with
+ * recompute preemption when the pool cannot hold an iteration ("苦猿的大模型日记"
+ * PART 05: wait, preempt, drop the cache and recompute rather than fail).
+ * A request of P prompt tokens producing M tokens writes its K/V rows in
+ * position order: the prompt in chunks of at most chunk_tokens, then the row
+ * of each token it emitted.  An iteration that brings a request's cache up
+ * to every known token (prompt + emitted) emits its next token; it finishes
+ * after M (the last token's row is never written) and its blocks are freed.
+ * Per iteration: every decoding request gets one row; prefill chunks follow
+ * in admission order within max_tokens rows; if the running requests' new
+ * blocks do not fit the free list, the most recently admitted one is
+ * preempted (its blocks freed, its progress reset, requeued first: on
+ * readmission it re-prefills prompt + emitted tokens); then waiting requests
+ * are admitted in order while the batch (max_batch), the budget and the pool
+ * allow -- the first that does not fit stops admission.  Request ids are the
+ * cache's sequence ids.  The caller owns the cache and must not touch the
+ * scheduler's sequences except through the plan. */
+typedef struct kvc_sched kvc_sched;
+
+typedef struct kvc_sched_config {
+  int32_t max_batch;     /* sequences per iteration, >= 1 */
+  int32_t chunk_tokens;  /* prefill rows per request per iteration, >= 1 */
+  int32_t max_tokens;    /* rows per iteration (prefill chunks are cut to fit), >= 1 */
+} kvc_sched_config;
+
+typedef struct kvc_sched_stats {
+  int64_t submitted, running, waiting, finished, preemptions, iterations, tokens_scheduled;
+} kvc_sched_stats;
+
+kvc_status kvc_sched_create(kvc_cache* cache, const kvc_sched_config* cfg, kvc_sched** out);
+void kvc_sched_destroy(kvc_sched* sched);
+/* Queue a request (prompt_len >= 1, max_new_tokens >= 1). */
+kvc_status kvc_sched_submit(kvc_sched* sched, int64_t req_id, int32_t prompt_len, int32_t max_new_tokens);
+/* Plan the next iteration (host arrays of at least max_batch entries):
+ * seq_ids[i], n_new[i] rows to append, start[i] = position of the first
+ * (optional), emits[i] = 1 if the iteration emits that request's next token
+ * (optional); *batch = entries.  Preempted requests' ids go to preempted
+ * (optional, up to preempt_capacity; *num_preempted counts all).  The caller
+ * then appends the rows (kvc_append with these ids and n_new), runs the
+ * attention and calls kvc_sched_commit.  KVC_E_NO_BLOCKS if the pool cannot
+ * hold the next rows of even one request (the oldest running one is never
+ * preempted to make room for itself; requests preempted on the way stay
+ * preempted); KVC_E_INVALID if the previous plan was not committed. */
+kvc_status kvc_sched_plan(kvc_sched* sched, int32_t capacity, int64_t* seq_ids, int32_t* n_new, int32_t* start,
+                          int32_t* emits, int32_t* batch, int64_t* preempted, int32_t preempt_capacity,
+                          int32_t* num_preempted);
+/* Record the planned iteration as done (KVC_E_INVALID if the planned rows were
+ * not appended); requests that emitted their last token are finished, their
+ * blocks freed, their ids written to finished (optional, up to capacity). */
+kvc_status kvc_sched_commit(kvc_sched* sched, int64_t* finished, int32_t capacity, int32_t* num_finished);
+kvc_status kvc_sched_get_stats(const kvc_sched* sched, kvc_sched_stats* out);
+
 /* ---- measurement helper ---------------------------------------------------- */
 
 /* Streaming copy of `bytes` (multiple of 16) from src to dst on `stream`: a

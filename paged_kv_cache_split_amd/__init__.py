@@ -7,7 +7,7 @@ mask among them) and the merge.  This package is its ctypes binding; torch
 provides device memory and streams.  Importing it fails if libkvc.so has not
 been built (``python paged_kv_cache_split_amd/build.py``).
 """
-from ._binding import (BF16, F16, F32, FP8, INT8, KVCache, KvcError, bytes_per_token,  # noqa: F401
+from ._binding import (BF16, F16, F32, FP8, INT8, KVCache, KvcError, Scheduler, bytes_per_token,  # noqa: F401
                        decode_workspace_bytes, extend_workspace_bytes, lib, pool_bytes, scale_bytes,
                        scratch_bytes, stream_copy)
 from ._binding import LIB_PATH, SYMBOLS  # noqa: F401

@@ -32,8 +32,9 @@ SYMBOLS = [
     "kvc_bytes_per_token", "kvc_pool_bytes", "kvc_scale_bytes", "kvc_scratch_bytes", "kvc_create", "kvc_destroy",
     "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_evict", "kvc_reserve_host",
     "kvc_get_table", "kvc_stats", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
-    "kvc_decode_attention", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_stream_copy",
-    "kvc_last_error",
+    "kvc_decode_attention", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_sched_create",
+    "kvc_sched_destroy", "kvc_sched_submit", "kvc_sched_plan", "kvc_sched_commit", "kvc_sched_get_stats",
+    "kvc_stream_copy", "kvc_last_error",
 ]
 
 
@@ -51,6 +52,15 @@ class KvcConfig(ctypes.Structure):
 class KvcStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("total_blocks", "free_blocks", "used_blocks", "shared_blocks",
                                                "peak_used_blocks", "cow_copies", "num_seqs")]
+
+
+class KvcSchedConfig(ctypes.Structure):
+    _fields_ = [("max_batch", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32), ("max_tokens", ctypes.c_int32)]
+
+
+class KvcSchedStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("submitted", "running", "waiting", "finished", "preemptions",
+                                              "iterations", "tokens_scheduled")]
 
 
 class KvcDecodeOpts(ctypes.Structure):
@@ -87,6 +97,12 @@ _sig = {
     "kvc_extend_attention": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp, _sz,
                                             ctypes.POINTER(KvcDecodeOpts), _vp]),
+    "kvc_sched_create": (ctypes.c_int, [_vp, ctypes.POINTER(KvcSchedConfig), ctypes.POINTER(_vp)]),
+    "kvc_sched_destroy": (None, [_vp]),
+    "kvc_sched_submit": (ctypes.c_int, [_vp, _i64, _i32, _i32]),
+    "kvc_sched_plan": (ctypes.c_int, [_vp, _i32, _P64, _P32, _P32, _P32, _P32, _P64, _i32, _P32]),
+    "kvc_sched_commit": (ctypes.c_int, [_vp, _P64, _i32, _P32]),
+    "kvc_sched_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(KvcSchedStats)]),
     "kvc_stream_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
     "kvc_last_error": (ctypes.c_char_p, []),
 }
@@ -366,3 +382,61 @@ class KVCache:
             self.block_size, float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
             workspace.numel(), ctypes.byref(opts), _stream_ptr(stream)), "kvc_extend_attention")
         return out
+
+
+class Scheduler:
+    """Continuous-batching scheduler (libkvc's kvc_sched_*) over a KVCache.
+
+    Each iteration: ``plan()`` -> the rows to append per request, then the
+    caller appends them (``cache.append(ids, k, v, n_new)``) and runs the
+    attention, then ``commit()`` -> the requests that finished."""
+
+    def __init__(self, cache: "KVCache", max_batch: int, chunk_tokens: int, max_tokens: int):
+        self.cache = cache
+        self.max_batch = int(max_batch)
+        cfg = KvcSchedConfig(int(max_batch), int(chunk_tokens), int(max_tokens))
+        h = ctypes.c_void_p()
+        _check(_lib.kvc_sched_create(cache.handle, ctypes.byref(cfg), ctypes.byref(h)), "kvc_sched_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.kvc_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, req_id, prompt_len, max_new_tokens):
+        _check(_lib.kvc_sched_submit(self._h, int(req_id), int(prompt_len), int(max_new_tokens)), "kvc_sched_submit")
+
+    def plan(self):
+        """-> dict(ids, n_new, start, emits, preempted) for the next iteration."""
+        cap = self.max_batch
+        ids, pids = _i64_array(np.zeros(cap))
+        n, pn = _i32_array(np.zeros(cap))
+        st, pst = _i32_array(np.zeros(cap))
+        em, pem = _i32_array(np.zeros(cap))
+        pre, ppre = _i64_array(np.zeros(max(cap, 64)))
+        batch, npre = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(_lib.kvc_sched_plan(self._h, cap, pids, pn, pst, pem, ctypes.byref(batch), ppre, len(pre),
+                                   ctypes.byref(npre)), "kvc_sched_plan")
+        b, k = batch.value, min(npre.value, len(pre))
+        return dict(ids=[int(x) for x in ids[:b]], n_new=[int(x) for x in n[:b]], start=[int(x) for x in st[:b]],
+                    emits=[int(x) for x in em[:b]], preempted=[int(x) for x in pre[:k]])
+
+    def commit(self):
+        """-> ids of the requests that finished in this iteration."""
+        cap = max(self.max_batch, 1)
+        fin, pfin = _i64_array(np.zeros(cap))
+        nf = ctypes.c_int32(0)
+        _check(_lib.kvc_sched_commit(self._h, pfin, cap, ctypes.byref(nf)), "kvc_sched_commit")
+        return [int(x) for x in fin[:min(nf.value, cap)]]
+
+    def stats(self) -> dict:
+        st = KvcSchedStats()
+        _check(_lib.kvc_sched_get_stats(self._h, ctypes.byref(st)), "kvc_sched_get_stats")
+        return {n: int(getattr(st, n)) for n, _ in KvcSchedStats._fields_}

@@ -13,7 +13,8 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libkvc.so")
-SOURCES = [os.path.join(CSRC, "kvc_host.cpp"), os.path.join(CSRC, "kvc_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "kvc_host.cpp"), os.path.join(CSRC, "kvc_sched.cpp"),
+           os.path.join(CSRC, "kvc_kernels.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

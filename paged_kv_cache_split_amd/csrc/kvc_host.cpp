@@ -346,6 +346,11 @@ size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t num_kv_head
 
 }  // namespace
 
+namespace kvc {
+kvc_status host_fail(kvc_status st, const char* msg) { return fail(st, "%s", msg); }
+int32_t cache_block_size(const kvc_cache* c) { return c->cfg.block_size; }
+}  // namespace kvc
+
 extern "C" {
 
 size_t kvc_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim, kvc_dtype dtype) {

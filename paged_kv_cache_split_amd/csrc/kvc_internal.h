@@ -155,4 +155,8 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
                          hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
+// Shared by the host sources (defined in kvc_host.cpp).
+kvc_status host_fail(kvc_status st, const char* msg);   // records msg as the thread's last error
+int32_t cache_block_size(const kvc_cache* c);
+
 }  // namespace kvc

@@ -152,7 +152,7 @@ def make_workload(cid: int, seed: int | None = None, small: bool = False, **over
     p = dict((SMALL if small else CONFIGS)[cid])
     p.update(override)
     if "kv_dtype" in override and override["kv_dtype"] != CONFIGS[cid]["kv_dtype"]:
-        p["name"] = f"{p['name']} -- with a {override['kv_dtype']} cache"
+        p["name"] = f"{p['name']} -- {override['kv_dtype']} cache instead"
     seed = cid if seed is None else seed
     rng = np.random.default_rng(seed)
     lens = _lengths(cid, rng, p)
@@ -340,6 +340,23 @@ def _randn(shape, dtype_name, gen, device):
         n = min(chunk, flat.numel() - i)
         flat[i:i + n] = torch.randn(n, generator=gen, dtype=torch.float32, device=device).to(tdt)
     return out
+
+
+def make_request_values(seed: int, req_id: int, num_layers: int, length: int, num_heads: int, num_kv_heads: int,
+                        head_dim: int, q_dtype: str, kv_in_dtype: str, device="cpu"):
+    """K/V rows and queries of one request's tokens 0..length-1, drawn from a
+    torch generator seeded by (seed, req_id) in the order k, v, q, each as
+    float32 N(0, 1) rounded to its dtype.  A request recomputed after
+    preemption draws the same values.
+
+    returns dict(k=[layers, length, Hkv, D], v=..., q=[length, Hq, D])"""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1_000_003 + int(req_id))
+    k = _randn((num_layers, length, num_kv_heads, head_dim), kv_in_dtype, gen, device)
+    v = _randn((num_layers, length, num_kv_heads, head_dim), kv_in_dtype, gen, device)
+    q = _randn((length, num_heads, head_dim), q_dtype, gen, device)
+    return dict(k=k, v=v, q=q)
 
 
 def make_values(wl: Workload, device="cpu"):
