@@ -58,7 +58,7 @@
  * int8 storage: the same rule with 127 in place of 448 and enc(x) = x rounded
  *  to the nearest integer (ties to even), clamped to +-127, stored as a
  *  two's-complement byte; the value of code c is c * scale.  The pages list
- *  INT8 KV quantisation ("LLM推理优化实战…" §3.4, "LLM推理优化核心技术…" §1.2) but
+ *  INT8 KV quantisation ("LLM推理优化实战…" §6.1, "LLM推理优化核心技术…" §1.2) but
  *  fix no scheme.
  */
 #ifndef KVC_H_
@@ -165,7 +165,7 @@ kvc_status kvc_free_seq(kvc_cache* cache, int64_t seq_id);
  * released last-first, so re-appending takes the same blocks back.
  * KVC_E_INVALID if the new end would fall inside a block kvc_evict released. */
 kvc_status kvc_truncate(kvc_cache* cache, int64_t seq_id, int32_t num_tokens);
-/* Sliding-window eviction ("苦猿的大模型日记 · Day45" PART 05: a fixed cache bound
+/* Sliding-window eviction ("苦猿的大模型日记 · Day45" PART 02: a fixed cache bound
  * paid for with the history that leaves the window).  Every block of the
  * sequence that holds only positions < keep_from (0 <= keep_from <= length)
  * loses this sequence's reference (freed at 0, in table order); its table

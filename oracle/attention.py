@@ -34,7 +34,7 @@ is the mask of "苦猿的大模型日记" PART 04's ``naive_attention`` (lower t
 shifted by kv_len - q_len).
 
 A sliding window (``window`` > 0) limits what each token sees to its own
-row and the window - 1 rows before it ("苦猿的大模型日记" PART 05: the sliding
+row and the window - 1 rows before it ("苦猿的大模型日记" PART 02: the sliding
 window or KV eviction trades visible history for a fixed cache bound;
 "LLM推理优化实战…" §7.2 names sliding-window attention among the forms that
 restrict the attention range).  The pages give no formula; the plainest

@@ -27,7 +27,7 @@ reading restored here (plainest one the rest of the code supports):
   (p % bs > 0).  A position past the last block takes a fresh block.
 
 * ``evict(seq, keep_from)``: the sliding-window / KV-eviction item of
-  "苦猿的大模型日记 · Day45" PART 05 (a fixed cache bound bought with the history
+  "苦猿的大模型日记 · Day45" PART 02 (a fixed cache bound bought with the history
   that leaves the window).  Every block of the sequence whose positions all
   lie before ``keep_from`` loses this sequence's reference (freed at 0); its
   table entry becomes -1 so logical indexing is unchanged.  Not on the pages

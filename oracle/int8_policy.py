@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 PARITY UNPINNED BY THE PAGES.  They list INT8 beside FP8 and INT4 as KV
-quantisation options ("LLM推理优化实战…" §3.4 serving options, "FP8/INT4/INT8";
+quantisation options ("LLM推理优化实战…" §6.1, the deployed engine supports FP8/INT4/INT8;
 "LLM推理优化核心技术…" §1.2, one byte per element in the cache-size formula and
 an INT8 column in its table) but fix no scheme.  The reading adopted mirrors
 the fp8 rule (``fp8_policy``) with a symmetric integer code:

@@ -296,7 +296,7 @@ def history_rows_of(wl: Workload, b: int):
 
 # Decode (or several new tokens) under a sliding window with eviction: the
 # 70B-shaped GQA layer over 16K-token contexts, each token seeing the last
-# 4096 positions ("苦猿的大模型日记" PART 05's sliding window / KV eviction; the
+# 4096 positions ("苦猿的大模型日记" PART 02's sliding window / KV eviction; the
 # window length is a builder's choice, the pages give none), the history
 # written 1024 rows at a time with what leaves the window evicted after each.
 WINDOW_CONFIGS = {
