@@ -49,6 +49,8 @@ def parse():
                    help="time a step with several new tokens per sequence instead of decode: the verify pass "
                         "of speculative decoding (5 draft tokens, 70B-shaped batch), a 2048-token causal "
                         "prefill, or a 512-token prefill chunk over 3584 cached tokens")
+    p.add_argument("--tiles-per-wave", type=int, default=0,
+                   help="--extend: 16-column tiles each wave holds (1..4, 0 auto)")
     p.add_argument("--kv", choices=["f32", "f16", "bf16", "fp8", "int8"], default=None,
                    help="cache dtype override for --config (e.g. --config 5 --kv int8: the mixed batch with an "
                         "int8 cache)")
@@ -255,7 +257,8 @@ def run_extend(args):
     torch.cuda.synchronize()
     out = torch.empty_like(q)
     ws = torch.empty(max(256, kvc.extend_workspace_bytes(wl.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
-                                                         wl.max_query_len, args.work_items)),
+                                                         wl.max_query_len, wl.max_context_len, args.work_items,
+                                                         args.tiles_per_wave)),
                      dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in ev:
@@ -265,7 +268,7 @@ def run_extend(args):
     def step(events=None):
         cache.append(seqs, k_new, v_new, n_new=n_new)
         cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws,
-                     work_items=args.work_items, split_events=events)
+                     work_items=args.work_items, split_events=events, tiles_per_wave=args.tiles_per_wave)
         for s_, L in zip(seqs, hist_len):
             cache.truncate(s_, L)
 
@@ -316,7 +319,8 @@ def run_extend(args):
         "config": {"workload": wl.name, "extend": args.extend, "batch": wl.batch, "num_heads": wl.num_heads,
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "new_tokens": wl.total_queries, "rows_attended": int(wl.attend_lens.sum()), "kv_bytes": w["kv"],
-                   "work_items": args.work_items or "auto", "parallelism": "single GPU"},
+                   "work_items": args.work_items or "auto", "tiles_per_wave": args.tiles_per_wave or "auto",
+                   "parallelism": "single GPU"},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -248,6 +248,7 @@ typedef struct kvc_decode_opts {
   kvc_event_t split_end;
   int32_t window;           /* sliding window (both kernels, decode and several tokens): the token at
                                position p sees positions max(0, p - window + 1) .. p; 0 = all of them */
+  int32_t tiles_per_wave;   /* several tokens: 16-column (token, head) tiles each wave holds, 1..4; 0 = auto */
 } kvc_decode_opts;
 
 /* Workspace bytes kvc_decode_attention needs for this shape (the split
@@ -306,15 +307,16 @@ kvc_status kvc_decode_attention(kvc_cache* cache, int32_t layer, const void* q, 
  *                ql_b <= context_lens[b]
  *  out:          device [total_query][num_heads][head_dim], q_dtype
  *  workspace:    device, kvc_extend_workspace_bytes() bytes
- *  opts:         NULL, or kernel 0 / 2 and work_items (waves per KV head and
- *                column-tile group); the other fields are ignored
+ *  opts:         NULL, or kernel 0 / 2, work_items (waves per KV head and
+ *                column-tile group), window and tiles_per_wave; the other
+ *                fields are ignored
  * Other arguments and checks as for kvc_decode_attention; an f32 cache gives
  * KVC_E_UNSUPPORTED (the kernel runs on matrix cores).  Device-side values are
  * clamped as for decode; ql_b is cut to min(max_query_len, context_lens[b]) and
  * rows outside [0, total_query) are neither read nor written, so a malformed
  * query_start gives meaningless rows but nothing faults. */
 size_t kvc_extend_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t max_query_len, const kvc_decode_opts* opts);
+                                  int32_t max_query_len, int32_t max_context_len, const kvc_decode_opts* opts);
 kvc_status kvc_extend_attention(kvc_cache* cache, int32_t layer, const void* q, kvc_dtype q_dtype,
                                 const int32_t* query_start, int32_t total_query, int32_t max_query_len,
                                 const int32_t* block_table, int32_t max_blocks_per_seq,

@@ -66,7 +66,8 @@ class KvcSchedStats(ctypes.Structure):
 class KvcDecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("work_items", ctypes.c_int32),
                 ("pool_pieces", ctypes.c_int32), ("pool_shift", ctypes.c_int32),
-                ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p), ("window", ctypes.c_int32)]
+                ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p), ("window", ctypes.c_int32),
+                ("tiles_per_wave", ctypes.c_int32)]
 
 
 _i32, _i64, _sz, _vp, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -93,7 +94,7 @@ _sig = {
     "kvc_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
     "kvc_decode_attention": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f, _vp, _vp, _sz, ctypes.POINTER(KvcDecodeOpts), _vp]),
-    "kvc_extend_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
+    "kvc_extend_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
     "kvc_extend_attention": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp, _sz,
                                             ctypes.POINTER(KvcDecodeOpts), _vp]),
@@ -172,14 +173,15 @@ def scratch_bytes(max_batch, max_tokens) -> int:
 
 def decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len, partition_tokens=0,
                            kernel=0, work_items=0, pool_pieces=0, pool_shift=0) -> int:
-    opts = KvcDecodeOpts(partition_tokens, kernel, work_items, pool_pieces, pool_shift, None, None, 0)
+    opts = KvcDecodeOpts(partition_tokens, kernel, work_items, pool_pieces, pool_shift, None, None, 0, 0)
     return _lib.kvc_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len,
                                            ctypes.byref(opts))
 
 
-def extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len, work_items=0) -> int:
-    opts = KvcDecodeOpts(0, 0, work_items, 0, 0, None, None, 0)
-    return _lib.kvc_extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len,
+def extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len, max_context_len, work_items=0,
+                           tiles_per_wave=0) -> int:
+    opts = KvcDecodeOpts(0, 0, work_items, 0, 0, None, None, 0, tiles_per_wave)
+    return _lib.kvc_extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len, max_context_len,
                                            ctypes.byref(opts))
 
 
@@ -335,7 +337,7 @@ class KVCache:
         if not q.is_contiguous():
             raise ValueError("q must be contiguous")
         opts = KvcDecodeOpts(int(partition_tokens), int(kernel), int(work_items), int(pool_pieces), int(pool_shift),
-                             None, None, int(window))
+                             None, None, int(window), 0)
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event
@@ -354,7 +356,7 @@ class KVCache:
         return out
 
     def extend(self, q, query_start, max_query_len, block_table, context_lens, max_context_len, scale, layer=0,
-               out=None, workspace=None, work_items=0, split_events=None, stream=None, window=0):
+               out=None, workspace=None, work_items=0, split_events=None, stream=None, window=0, tiles_per_wave=0):
         """Attention of several new tokens per sequence (causal among them) for
         one layer.  q: [total_query, Hq, D] device tensor; query_start: device
         int32 [B + 1] (rows of sequence b are query_start[b] .. query_start[b+1]-1)."""
@@ -365,11 +367,12 @@ class KVCache:
             raise ValueError("q must be contiguous")
         if query_start.dtype != torch.int32 or query_start.numel() != B + 1:
             raise ValueError("query_start must be int32 with batch + 1 entries")
-        opts = KvcDecodeOpts(0, 0, int(work_items), 0, 0, None, None, int(window))
+        opts = KvcDecodeOpts(0, 0, int(work_items), 0, 0, None, None, int(window), int(tiles_per_wave))
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event
-        ws_need = _lib.kvc_extend_workspace_bytes(B, Hq, self.num_kv_heads, D, int(max_query_len), ctypes.byref(opts))
+        ws_need = _lib.kvc_extend_workspace_bytes(B, Hq, self.num_kv_heads, D, int(max_query_len), int(max_context_len),
+                                                  ctypes.byref(opts))
         if workspace is None or workspace.numel() < ws_need:
             workspace = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=q.device)
         if out is None:

@@ -293,6 +293,7 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
   plan->pool_shift = (opts && opts->pool_shift > 0) ? opts->pool_shift : kvc::kDefaultPoolShift;
   plan->tile_groups = 0;
   plan->waves_per_group = 1;
+  plan->tiles_per_wave = 1;
   plan->max_q = 1;
   if (opts && opts->window < 0) return false;
   plan->window = opts ? opts->window : 0;
@@ -300,10 +301,11 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
 }
 
 // Several query tokens per sequence (MFMA kernel).  A sequence's columns are
-// ceil(max_q * G / 16) tiles of 16 (query token, head) pairs; up to 4 tiles
-// share a work-group (one wave each, side by side on one chunk of blocks, so
-// the chunk's tiles are read from HBM once and served to the others from
-// cache), the rest go to grid.z.  A wave uses the whole register file of its
+// ceil(max_q * G / 16) tiles of 16 (query token, head) pairs.  A wave holds up
+// to 4 of them (tiles_per_wave) and reuses every K/V block it loads for all of
+// them; up to 4 waves share a work-group (side by side on one chunk of blocks,
+// so the chunk is read from HBM once and served to the others from cache),
+// the rest go to grid.z.  A wave uses the whole register file of its
 // SIMD, so a CU holds 4 / waves_per_group work-groups; with several waves per
 // group the default launches two such rounds over the chip, divided among the
 // KV heads and tile groups (measured on the verify and prefill workloads: one
@@ -314,9 +316,11 @@ constexpr int64_t kExtendRowBudget = 1 << 16;
 constexpr int64_t kExtendCUs = 256;   // fixed (not queried), so results do not depend on the device
 constexpr int32_t kMaxQueryTokens = 4096;
 
-bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t max_q, int kv,
-                 const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
-  if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2) || opts->window < 0)) return false;
+bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t max_q, int32_t max_context_len,
+                 int kv, const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
+  if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2) || opts->window < 0 ||
+               opts->tiles_per_wave < 0 || opts->tiles_per_wave > 4))
+    return false;
   if (max_q < 1 || max_q > kMaxQueryTokens) return false;
   plan->window = opts ? opts->window : 0;
   const int32_t G = num_heads / num_kv_heads;
@@ -326,8 +330,19 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   plan->num_partitions = 1;
   plan->pool_pieces = 0;
   plan->pool_shift = kvc::kDefaultPoolShift;
-  plan->waves_per_group = std::min(4, tiles);
-  plan->tile_groups = (tiles + plan->waves_per_group - 1) / plan->waves_per_group;
+  // A wave walks the union of its tiles' block ranges.  When the new tokens
+  // are most of what is attended (a prompt with little or no cached history),
+  // those ranges differ tile to tile along the causal diagonal, so one tile
+  // per wave is cheaper (measured on a 2048-token prompt: 56 us against 66 us
+  // for four); with a long history they nearly coincide and four tiles share
+  // every block load.
+  const bool mostly_new = max_context_len > 0 && (int64_t)max_context_len <= 2 * (int64_t)max_q;
+  plan->tiles_per_wave = (opts && opts->tiles_per_wave > 0) ? opts->tiles_per_wave
+                                                            : (mostly_new && tiles > 4 ? 1 : std::min(4, tiles));
+  plan->tiles_per_wave = std::min(plan->tiles_per_wave, tiles);
+  const int32_t wave_slots = (tiles + plan->tiles_per_wave - 1) / plan->tiles_per_wave;
+  plan->waves_per_group = std::min(4, wave_slots);
+  plan->tile_groups = (wave_slots + plan->waves_per_group - 1) / plan->waves_per_group;
   plan->max_q = max_q;
   (void)kv;
   const int64_t groups_per_round = (int64_t)kExtendCUs * std::max(1, 4 / plan->waves_per_group);
@@ -761,10 +776,10 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
 }
 
 size_t kvc_extend_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t max_query_len, const kvc_decode_opts* opts) {
+                                  int32_t max_query_len, int32_t max_context_len, const kvc_decode_opts* opts) {
   if (batch < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || num_heads % num_kv_heads != 0) return 0;
   kvc::DecodePlan p;
-  if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len, -1, opts, &p)) return 0;
+  if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len, max_context_len, -1, opts, &p)) return 0;
   return workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, p);
 }
 
@@ -787,7 +802,8 @@ kvc_status kvc_extend_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   const kvc_dtype kv = c->cfg.kv_dtype;
   if (kv == KVC_F32) return fail(KVC_E_UNSUPPORTED, "several query tokens need a 16-bit or fp8 cache");
   kvc::DecodePlan plan;
-  if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len, (int)kv, opts, &plan))
+  if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len,
+                   std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size), (int)kv, opts, &plan))
     return fail(KVC_E_INVALID, "opts: kernel must be 0 or 2, work_items >= 0, window >= 0");
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
   if (!workspace || workspace_bytes < need)

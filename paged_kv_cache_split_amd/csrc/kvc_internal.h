@@ -72,6 +72,7 @@ struct DecodePlan {
   // and the partial rows hold one set of slots per query token index
   int32_t tile_groups;
   int32_t waves_per_group;
+  int32_t tiles_per_wave;    // column tiles each wave holds (1..4), reusing every K/V block it loads
   int32_t max_q;
   // sliding window (both kernels): a token sees at most `window` rows ending
   // at its own; 0 = the whole history

@@ -61,6 +61,17 @@ constexpr int kBS = 16;                       // tokens per block (device work)
 #ifndef KVC_PREFETCH_FP8
 #define KVC_PREFETCH_FP8 3
 #endif
+// Blocks in flight for the several-token kernel with 2, 3 or 4 column tiles
+// per wave (their queries and accumulators take the registers).
+#ifndef KVC_PREFETCH_T2
+#define KVC_PREFETCH_T2 2
+#endif
+#ifndef KVC_PREFETCH_T3
+#define KVC_PREFETCH_T3 1
+#endif
+#ifndef KVC_PREFETCH_T4
+#define KVC_PREFETCH_T4 1
+#endif
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -737,17 +748,20 @@ __device__ __forceinline__ int wave_first_block(int64_t w, int64_t total, int64_
 // columns of the matrix-core tiles.  EXT = true: several new query tokens per
 // sequence (q_start), each attending causally -- the token at position p sees
 // rows 0..p -- so a column is a (query token, head) pair with its own count of
-// visible rows; the ceil(ql * G / 16) column tiles of a sequence are spread
+// visible rows.  A sequence's ceil(ql * G / 16) column tiles are spread TPW
+// to a wave (the wave reuses each K/V block it loads for all of its tiles),
 // over the waves of a work-group (side by side on one chunk of blocks) and
-// over grid.z.  Decode is the EXT case with one token, compiled apart so its
-// loop carries none of the per-column bookkeeping.
-template <kvc_dtype KV, int D, int PF, bool EXT>
+// over grid.z.  Decode is the EXT case with one token and one tile, compiled
+// apart so its loop carries none of the per-column bookkeeping.
+template <kvc_dtype KV, int D, int PF, bool EXT, int TPW>
 __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start) {
+  static_assert(EXT || TPW == 1, "decode has one column tile per wave");
   const int w = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  // column tile of this wave (EXT)
-  const int ct = EXT ? __builtin_amdgcn_readfirstlane((int)blockIdx.z * a.waves_per_group + (int)(threadIdx.x >> 6))
-                     : 0;
+  // first column tile of this wave (EXT)
+  const int ct0 =
+      EXT ? __builtin_amdgcn_readfirstlane(((int)blockIdx.z * a.waves_per_group + (int)(threadIdx.x >> 6)) * TPW)
+          : 0;
   int total;
   if constexpr (EXT) {
     if (threadIdx.x < 64) scan_block_counts<true>(a, seq_start, lane);
@@ -830,66 +844,88 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
         a.ws_seginfo[2 * b] = c;
         a.ws_seginfo[2 * b + 1] = chunk_of_block(eb - 1) - c + 1;
       }
-      // Columns of this lane.  Decode: head nn of the group, every column sees
-      // the n rows.  EXT: column 16 ct + nn is (query token tok, head hh); the
-      // token sits at position n - ql + tok and sees rows up to n - ql + tok.
-      // With a window a column sees rows [col_lo, ncol), col_lo = ncol - window.
-      int ql = 1, tok = 0, hh = nn, q_row = b;
-      int n_lo = n, n_hi = n;                     // fewest / most rows a column of the tile sees
-      bool head_ok = nn < G;
+      int ql = 1, q0 = b;
       if constexpr (EXT) {
         ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
-        if (ct * 16 >= ql * G) {                  // no column of this sequence in the tile
+        if (ct0 * 16 >= ql * G) {                 // no column of this sequence in the wave's tiles
           x = seg_end;
           continue;
         }
-        const int col = ct * 16 + nn;
-        tok = col / G;
-        hh = col - tok * G;
-        const int q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
-        q_row = q0 + tok;
-        head_ok = tok < ql && q_row >= 0 && q_row < a.total_q;
-        n_lo = n - ql + 1 + (ct * 16) / G;
-        n_hi = n - ql + 1 + min(ql - 1, (ct * 16 + 15) / G);
+        q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
       }
-      // rows this lane's column sees (padding columns: all n, so they stay finite)
-      const int ncol = head_ok ? n - ql + 1 + tok : n;
       const int win = a.window;
-      const int col_lo = win > 0 ? max(0, ncol - win) : 0;
-      const int lo_lo = win > 0 ? max(0, n_lo - win) : 0;   // lowest first row over the tile's columns
-      const int lo_hi = win > 0 ? max(0, n_hi - win) : 0;   // highest
-      // table index of the segment's first block, and the blocks [j0, j1) of
-      // the segment that some column of the tile sees (cnt <= 0: none)
+      // table index of the segment's first block
       const int tb0 = __builtin_amdgcn_readfirstlane(first_visible_block(n, ql, win)) + first;
-      const int j0 = max(0, lo_lo / kBS - tb0);
-      const int j1 = min(count, (n_hi + kBS - 1) / kBS - tb0);
-      const int cnt = j1 - j0;
-      const int tb = tb0 + j0;                    // table index of the tile's first block here
-      const int h = g * G + hh;
+      // Columns of this lane, one per tile.  Decode: head nn of the group, every
+      // column sees the n rows.  EXT: column 16 ct + nn is (query token tok,
+      // head hh); the token sits at position n - ql + tok and sees rows up to
+      // n - ql + tok.  With a window a column sees rows [col_lo, ncol),
+      // col_lo = ncol - window.  Per tile, n_lo is the fewest rows a column
+      // sees, lo_hi the highest window start, and [j0, j1) the blocks of the
+      // segment some column of the tile sees; the wave walks their union.
+      int hh[TPW], q_row[TPW], ncol[TPW], col_lo[TPW], n_lo[TPW], lo_hi[TPW], j0[TPW], j1[TPW];
+      bool head_ok[TPW], active[TPW];
+      int J0 = count, J1 = 0;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        int tok = 0, n_hi = n;
+        hh[t] = nn;
+        q_row[t] = b;
+        head_ok[t] = nn < G;
+        active[t] = true;
+        n_lo[t] = n;
+        if constexpr (EXT) {
+          const int ct = ct0 + t;
+          active[t] = ct * 16 < ql * G;
+          const int col = ct * 16 + nn;
+          tok = col / G;
+          hh[t] = col - tok * G;
+          q_row[t] = q0 + tok;
+          head_ok[t] = active[t] && tok < ql && q_row[t] >= 0 && q_row[t] < a.total_q;
+          n_lo[t] = n - ql + 1 + (ct * 16) / G;
+          n_hi = n - ql + 1 + min(ql - 1, (ct * 16 + 15) / G);
+        }
+        // padding columns see all n rows, so they stay finite
+        ncol[t] = head_ok[t] ? n - ql + 1 + tok : n;
+        col_lo[t] = win > 0 ? max(0, ncol[t] - win) : 0;
+        const int lo_lo = win > 0 ? max(0, n_lo[t] - win) : 0;
+        lo_hi[t] = win > 0 ? max(0, n_hi - win) : 0;
+        j0[t] = max(0, lo_lo / kBS - tb0);
+        j1[t] = min(count, (n_hi + kBS - 1) / kBS - tb0);
+        if (active[t] && j1[t] > j0[t]) {
+          J0 = min(J0, j0[t]);
+          J1 = max(J1, j1[t]);
+        }
+      }
+      const int cnt = J1 - J0;                    // blocks the wave walks here (<= 0: none)
+      const int tb = tb0 + J0;                    // table index of the first of them
 
-      // Query operand: for step kk the lane holds 8 dims of its column's head,
+      // Query operands: for step kk the lane holds 8 dims of its column's head,
       // the same dims its K operand holds for token nn.
-      u32x4 qv[NQK];
-      {
-        const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)q_row * a.num_heads + h) * D;
+      u32x4 qv[TPW][NQK];
+      floatx4 acc[TPW][NDD];
+      float m[TPW], l[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const uint16_t* qh =
+            static_cast<const uint16_t*>(a.q) + ((int64_t)q_row[t] * a.num_heads + g * G + hh[t]) * D;
 #pragma unroll
         for (int kk = 0; kk < NQK; ++kk) {
           int d0;
           if constexpr (is_byte_code(KV)) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
           else d0 = (4 * kk + r) * 8;
-          qv[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
+          qv[t][kk] = head_ok[t] ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
         }
-      }
-      floatx4 acc[NDD];
 #pragma unroll
-      for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
-      float m = kNegInf, l = 0.0f;
+        for (int dd = 0; dd < NDD; ++dd) acc[t][dd] = floatx4{0.f, 0.f, 0.f, 0.f};
+        m[t] = kNegInf;
+        l[t] = 0.0f;
+      }
 
       if (cnt > 0) {
-        // Physical block of local block j of the segment (scalar load).  Every
-        // prefetch is issued, so the count of loads in flight is the same on
-        // every path; past the end it re-reads the segment's last block, which
-        // the L2 still holds.
+        // Physical block of local block j (scalar load).  Every prefetch is
+        // issued, so the count of loads in flight is the same on every path;
+        // past the end it re-reads the last block, which the L2 still holds.
         const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + tb);
         auto phys_of = [&](int j) -> int {
           j = j < cnt ? j : cnt - 1;
@@ -897,45 +933,14 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
         };
 
         auto process = [&](KvBlock<KV, D>& cur, int i) {
-          floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-          float qk = a.qk_scale;
-          float vsc = 1.0f;
-          if constexpr (is_byte_code(KV)) {
-            qk *= cur.ks;
-            vsc = cur.vs;
-#pragma unroll
-            for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
-              u32x4 lo, hi;
-              lo[0] = code2_to_bf16x2<KV, false>(cur.k[c2][0]);
-              lo[1] = code2_to_bf16x2<KV, true>(cur.k[c2][0]);
-              lo[2] = code2_to_bf16x2<KV, false>(cur.k[c2][1]);
-              lo[3] = code2_to_bf16x2<KV, true>(cur.k[c2][1]);
-              hi[0] = code2_to_bf16x2<KV, false>(cur.k[c2][2]);
-              hi[1] = code2_to_bf16x2<KV, true>(cur.k[c2][2]);
-              hi[2] = code2_to_bf16x2<KV, false>(cur.k[c2][3]);
-              hi[3] = code2_to_bf16x2<KV, true>(cur.k[c2][3]);
-              s = mfma_qk<KV>(lo, qv[2 * c2], s);
-              s = mfma_qk<KV>(hi, qv[2 * c2 + 1], s);
-            }
-          } else {
-#pragma unroll
-            for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[kk], s);
-          }
-          // Rows some column of the tile may not see exist only near the end of
-          // the sequence, or before the window's start (a wave-uniform test):
-          // mask them there, before the max and after exp.  Rows past the
-          // sequence's end hold whatever the slot
-          // held before (never written, or a previous owner's rows); zeroing
-          // their values as well keeps a NaN pattern there out of the
-          // accumulator (its weight is zero, but 0 * NaN is NaN).
+          const int jj = J0 + i;                       // index of this block in the segment
           const int blk_row = (tb + i) * kBS;          // the block's first row
-          const int t0 = blk_row + 4 * r;                // this lane's first row
-          const bool edge = blk_row + kBS > n_lo || blk_row < lo_hi;
-          float sv[4] = {s[0], s[1], s[2], s[3]};
-          if (edge) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (t0 + e >= ncol || t0 + e < col_lo) sv[e] = kNegInf;
+          const int t0 = blk_row + 4 * r;              // this lane's first row
+          // Rows past the sequence's end (only in its last block) hold whatever
+          // the slot held before (never written, or a previous owner's rows):
+          // their weight is zero, and zeroing their values keeps a NaN pattern
+          // there out of the accumulator (0 * NaN is NaN).
+          if (blk_row + kBS > n) {
             const int vr = n - t0;                     // rows of this lane's four inside the sequence
             if constexpr (is_byte_code(KV)) {
               const uint32_t keep = vr >= 4 ? 0xFFFFFFFFu : (vr <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * vr)));
@@ -951,59 +956,113 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
               }
             }
           }
-          // the scale is positive, so the max of the raw scores, scaled, is the
-          // max of the scaled scores; exp2(s * qk - m) is one fma
-          float mx = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * qk;
-          const bool grow = mx > m + kRescaleThreshold;
-          if (__any(grow)) {
-            const float mnew = grow ? mx : m;
-            // (a column that has seen no row yet keeps m = -inf: alpha 1, not NaN)
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
-            l *= alpha;
+          float qk = a.qk_scale;
+          float vsc = 1.0f;
+          // one-byte codes become bf16 once per block, for every tile
+          u32x4 kconv[is_byte_code(KV) ? 2 * KvBlock<KV, D>::NK : 1];
+          u32x2 vconv[is_byte_code(KV) ? NDD : 1];
+          if constexpr (is_byte_code(KV)) {
+            qk *= cur.ks;
+            vsc = cur.vs;
 #pragma unroll
-            for (int dd = 0; dd < NDD; ++dd) acc[dd] *= alpha;
-            m = mnew;
-          }
-          float pv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m));
-          if (edge) {
-            // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (t0 + e >= ncol || t0 + e < col_lo) pv[e] = 0.0f;
-          }
-          l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-          // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
-          // ~2^-17 relative), so rounding the weights to 16 bits costs no
-          // accuracy when the weighted values cancel.
-          u32x2 pb, pl;
-          if constexpr (KV == KVC_F16) {
-            pb[0] = pack_f16x2(pv[0], pv[1]);
-            pb[1] = pack_f16x2(pv[2], pv[3]);
-            pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
-            pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
-          } else {
-            if constexpr (is_byte_code(KV)) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+            for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
+              kconv[2 * c2][0] = code2_to_bf16x2<KV, false>(cur.k[c2][0]);
+              kconv[2 * c2][1] = code2_to_bf16x2<KV, true>(cur.k[c2][0]);
+              kconv[2 * c2][2] = code2_to_bf16x2<KV, false>(cur.k[c2][1]);
+              kconv[2 * c2][3] = code2_to_bf16x2<KV, true>(cur.k[c2][1]);
+              kconv[2 * c2 + 1][0] = code2_to_bf16x2<KV, false>(cur.k[c2][2]);
+              kconv[2 * c2 + 1][1] = code2_to_bf16x2<KV, true>(cur.k[c2][2]);
+              kconv[2 * c2 + 1][2] = code2_to_bf16x2<KV, false>(cur.k[c2][3]);
+              kconv[2 * c2 + 1][3] = code2_to_bf16x2<KV, true>(cur.k[c2][3]);
             }
-            pb[0] = pack_bf16x2(pv[0], pv[1]);
-            pb[1] = pack_bf16x2(pv[2], pv[3]);
-            pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
-            pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
+            if constexpr (TPW > 1) {
+#pragma unroll
+              for (int dd = 0; dd < NDD; ++dd) {
+                vconv[dd][0] = code2_to_bf16x2<KV, false>(cur.v[dd]);
+                vconv[dd][1] = code2_to_bf16x2<KV, true>(cur.v[dd]);
+              }
+            }
           }
 #pragma unroll
-          for (int dd = 0; dd < NDD; ++dd) {
-            u32x2 va;
+          for (int t = 0; t < TPW; ++t) {
+            // (wave-uniform) this tile sees no row of this block
+            if (!active[t] || jj < j0[t] || jj >= j1[t]) continue;
+            floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
             if constexpr (is_byte_code(KV)) {
-              va[0] = code2_to_bf16x2<KV, false>(cur.v[dd]);
-              va[1] = code2_to_bf16x2<KV, true>(cur.v[dd]);
+#pragma unroll
+              for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(kconv[kk], qv[t][kk], s);
             } else {
-              va = cur.v[dd];
+#pragma unroll
+              for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[t][kk], s);
             }
-            acc[dd] = mfma_pv<KV>(va, pb, acc[dd]);
-            acc[dd] = mfma_pv<KV>(va, pl, acc[dd]);
+            // Rows some column of the tile may not see exist only near the end
+            // of the sequence, or before the window's start (a wave-uniform
+            // test): mask them there, before the max and after exp.
+            const bool edge = blk_row + kBS > n_lo[t] || blk_row < lo_hi[t];
+            float sv[4] = {s[0], s[1], s[2], s[3]};
+            if (edge) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (t0 + e >= ncol[t] || t0 + e < col_lo[t]) sv[e] = kNegInf;
+            }
+            // the scale is positive, so the max of the raw scores, scaled, is the
+            // max of the scaled scores; exp2(s * qk - m) is one fma
+            const float mx = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * qk;
+            const bool grow = mx > m[t] + kRescaleThreshold;
+            if (__any(grow)) {
+              const float mnew = grow ? mx : m[t];
+              // (a column that has seen no row yet keeps m = -inf: alpha 1, not NaN)
+              const float alpha = grow ? __builtin_amdgcn_exp2f(m[t] - mnew) : 1.0f;
+              l[t] *= alpha;
+#pragma unroll
+              for (int dd = 0; dd < NDD; ++dd) acc[t][dd] *= alpha;
+              m[t] = mnew;
+            }
+            float pv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m[t]));
+            if (edge) {
+              // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (t0 + e >= ncol[t] || t0 + e < col_lo[t]) pv[e] = 0.0f;
+            }
+            l[t] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+            // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo
+            // to ~2^-17 relative), so rounding the weights to 16 bits costs no
+            // accuracy when the weighted values cancel.
+            u32x2 pb, pl;
+            if constexpr (KV == KVC_F16) {
+              pb[0] = pack_f16x2(pv[0], pv[1]);
+              pb[1] = pack_f16x2(pv[2], pv[3]);
+              pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
+              pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
+            } else {
+              if constexpr (is_byte_code(KV)) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+              }
+              pb[0] = pack_bf16x2(pv[0], pv[1]);
+              pb[1] = pack_bf16x2(pv[2], pv[3]);
+              pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
+              pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
+            }
+#pragma unroll
+            for (int dd = 0; dd < NDD; ++dd) {
+              u32x2 va;
+              if constexpr (is_byte_code(KV)) {
+                if constexpr (TPW > 1) {
+                  va = vconv[dd];
+                } else {
+                  va[0] = code2_to_bf16x2<KV, false>(cur.v[dd]);
+                  va[1] = code2_to_bf16x2<KV, true>(cur.v[dd]);
+                }
+              } else {
+                va = cur.v[dd];
+              }
+              acc[t][dd] = mfma_pv<KV>(va, pb, acc[t][dd]);
+              acc[t][dd] = mfma_pv<KV>(va, pl, acc[t][dd]);
+            }
           }
         };
 
@@ -1050,22 +1109,26 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
           process(buf[j], i);
         }
       }
-      // l over the head's four lane groups
-      l = sum_over_row_groups(l);
-      if (head_ok) {
-        if (x == sb && seg_end == eb) {
-          // the whole sequence is in this segment: write the output
-          const float inv = 1.0f / l;
+      const bool whole = x == sb && seg_end == eb;   // the whole sequence is in this segment
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        if (!active[t]) continue;
+        // l over the head's four lane groups
+        const float lt = sum_over_row_groups(l[t]);
+        if (!head_ok[t]) continue;
+        const int h = g * G + hh[t];
+        if (whole) {
+          const float inv = 1.0f / lt;
 #pragma unroll
           for (int dd = 0; dd < NDD; ++dd) {
-            const int64_t o = ((int64_t)q_row * a.num_heads + h) * D + 16 * dd + 4 * r;
+            const int64_t o = ((int64_t)q_row[t] * a.num_heads + h) * D + 16 * dd + 4 * r;
             u32x2 wv;
             if constexpr (KV == KVC_F16) {
-              wv[0] = pack_f16x2(acc[dd][0] * inv, acc[dd][1] * inv);
-              wv[1] = pack_f16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+              wv[0] = pack_f16x2(acc[t][dd][0] * inv, acc[t][dd][1] * inv);
+              wv[1] = pack_f16x2(acc[t][dd][2] * inv, acc[t][dd][3] * inv);
             } else {
-              wv[0] = pack_bf16x2(acc[dd][0] * inv, acc[dd][1] * inv);
-              wv[1] = pack_bf16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+              wv[0] = pack_bf16x2(acc[t][dd][0] * inv, acc[t][dd][1] * inv);
+              wv[1] = pack_bf16x2(acc[t][dd][2] * inv, acc[t][dd][3] * inv);
             }
             *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
           }
@@ -1073,13 +1136,14 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
           // partial of (sequence b, chunk c) for this column: slot b + c is
           // unique, since every segment boundary advances the sequence, the
           // chunk, or both (EXT: one set of slots per query token index)
+          const int tok = q_row[t] - q0;
           const int64_t rr = ((EXT ? (int64_t)tok * a.num_heads : 0) + h) * slots + b + c;
 #pragma unroll
           for (int dd = 0; dd < NDD; ++dd)
-            *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[dd];
+            *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[t][dd];
           if (r == 0) {
-            a.ws_m[rr] = m;
-            a.ws_l[rr] = l;
+            a.ws_m[rr] = m[t];
+            a.ws_l[rr] = lt;
           }
         }
       }
@@ -1102,14 +1166,15 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
 template <kvc_dtype KV, int D, int PF>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   extern __shared__ int seq_start[];   // [batch + 1]
-  attend_mfma<KV, D, PF, false>(a, seq_start);
+  attend_mfma<KV, D, PF, false, 1>(a, seq_start);
 }
 
-// grid (work items, KV heads, column-tile groups), waves_per_group waves each
-template <kvc_dtype KV, int D, int PF>
+// grid (work items, KV heads, tile groups), waves_per_group waves each, TPW
+// column tiles per wave
+template <kvc_dtype KV, int D, int PF, int TPW>
 __global__ __launch_bounds__(256) void extend_mfma_kernel(DecodeArgs a) {
   extern __shared__ int seq_start[];   // [batch + 1]
-  attend_mfma<KV, D, PF, true>(a, seq_start);
+  attend_mfma<KV, D, PF, true, TPW>(a, seq_start);
 }
 
 // Merge of the MFMA kernel's partials: one work-group per (KV head,
@@ -1242,10 +1307,11 @@ __global__ __launch_bounds__(64) void zero_ints_kernel(int* p, int n) {
   for (int i = threadIdx.x; i < n; i += 64) p[i] = 0;
 }
 
-// tile_groups: 0 for decode; else the extend kernel's grid.z
+// tile_groups: 0 for decode; else the extend kernel's grid.z, with
+// tiles_per_wave column tiles per wave
 template <kvc_dtype KV, kvc_dtype QT>
-hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merge, int tile_groups, hipEvent_t ev0,
-                               hipEvent_t ev1, hipStream_t s) {
+hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merge, int tile_groups,
+                               int tiles_per_wave, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
   hipError_t e = hipSuccess;
   const size_t scan_lds = (size_t)(a.batch + 1) * sizeof(int);
   if (kernel == 1) {
@@ -1285,8 +1351,25 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     }
     dim3 grid(a.work_items, a.num_kv_heads, tile_groups);
     dim3 block(64 * a.waves_per_group);
-    if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, PF>), grid, block, scan_lds, s, a);
-    else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, PF>), grid, block, scan_lds, s, a);
+    // several tiles per wave leave fewer registers for the prefetch ring
+    switch (tiles_per_wave) {
+      case 1:
+        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, PF, 1>), grid, block, scan_lds, s, a);
+        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, PF, 1>), grid, block, scan_lds, s, a);
+        break;
+      case 2:
+        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T2, 2>), grid, block, scan_lds, s, a);
+        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T2, 2>), grid, block, scan_lds, s, a);
+        break;
+      case 3:
+        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T3, 3>), grid, block, scan_lds, s, a);
+        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T3, 3>), grid, block, scan_lds, s, a);
+        break;
+      default:
+        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T4, 4>), grid, block, scan_lds, s, a);
+        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T4, 4>), grid, block, scan_lds, s, a);
+        break;
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
     dim3 mgrid(a.num_kv_heads, a.batch, a.max_q);
@@ -1404,15 +1487,20 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   const int D = pool.head_dim;
   switch (pool.dtype) {
     case KVC_F32:
-      return launch_decode_typed<KVC_F32, KVC_F32>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_F32, KVC_F32>(a, D, plan.kernel, merge, plan.tile_groups, plan.tiles_per_wave,
+                                                   ev_start, ev_end, stream);
     case KVC_F16:
-      return launch_decode_typed<KVC_F16, KVC_F16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_F16, KVC_F16>(a, D, plan.kernel, merge, plan.tile_groups, plan.tiles_per_wave,
+                                                   ev_start, ev_end, stream);
     case KVC_BF16:
-      return launch_decode_typed<KVC_BF16, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_BF16, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, plan.tiles_per_wave,
+                                                     ev_start, ev_end, stream);
     case KVC_FP8_E4M3:
-      return launch_decode_typed<KVC_FP8_E4M3, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_FP8_E4M3, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, plan.tiles_per_wave,
+                                                         ev_start, ev_end, stream);
     case KVC_INT8:
-      return launch_decode_typed<KVC_INT8, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, ev_start, ev_end, stream);
+      return launch_decode_typed<KVC_INT8, KVC_BF16>(a, D, plan.kernel, merge, plan.tile_groups, plan.tiles_per_wave,
+                                                     ev_start, ev_end, stream);
   }
   (void)q_dtype;
   return hipErrorInvalidValue;

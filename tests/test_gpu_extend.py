@@ -75,10 +75,11 @@ def test_ragged_query_counts(kv, hq, hkv, d):
     # many chunks per sequence: tiles whose tokens see none of a chunk's rows
     # leave empty partials that the merge must skip
     q = values["q"].cuda().contiguous()
-    for wi in (2, 7, 64):
-        o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi)
+    for wi, tpw in ((2, 0), (7, 0), (64, 0), (0, 1), (5, 2), (3, 3), (9, 4)):
+        o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi,
+                         tiles_per_wave=tpw)
         torch.cuda.synchronize()
-        check_close(to_f64(o), ref, *TOL, f"ragged {hq}/{hkv} D{d} {kv} work_items {wi}")
+        check_close(to_f64(o), ref, *TOL, f"ragged {hq}/{hkv} D{d} {kv} work_items {wi} tiles/wave {tpw}")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])

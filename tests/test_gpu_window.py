@@ -76,9 +76,9 @@ def test_window_several_new_tokens(kv):
     ref = oracle_extend(st, wl, values)
     check_close(to_f64(out), ref, *TOL, f"window extend {kv}")
     q = values["q"].cuda().contiguous()
-    for wi in (2, 9):
+    for wi, tpw in ((2, 0), (9, 0), (4, 1), (3, 2), (6, 3)):
         o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi,
-                         window=wl.window)
+                         window=wl.window, tiles_per_wave=tpw)
         torch.cuda.synchronize()
         check_close(to_f64(o), ref, *TOL, f"window extend {kv} work_items {wi}")
 
