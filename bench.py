@@ -49,6 +49,9 @@ def parse():
                    help="time a step with several new tokens per sequence instead of decode: the verify pass "
                         "of speculative decoding (5 draft tokens, 70B-shaped batch), a 2048-token causal "
                         "prefill, or a 512-token prefill chunk over 3584 cached tokens")
+    p.add_argument("--pool-pieces", type=int, default=0,
+                   help="MFMA decode: pieces of each run handed out at run time (0 = static split, the default)")
+    p.add_argument("--pool-shift", type=int, default=0, help="MFMA decode: the pool is the last 1/2^shift of a run")
     p.add_argument("--tiles-per-wave", type=int, default=0,
                    help="--extend: 16-column tiles each wave holds (1..4, 0 auto)")
     p.add_argument("--kv", choices=["f32", "f16", "bf16", "fp8", "int8"], default=None,
@@ -376,7 +379,7 @@ def main():
     out = torch.empty_like(q)
     ws = torch.empty(max(256, kvc.decode_workspace_bytes(wl.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
                                                          wl.max_context_len, args.partition_tokens, args.kernel,
-                                                         args.work_items)),
+                                                         args.work_items, args.pool_pieces, args.pool_shift)),
                      dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -388,7 +391,7 @@ def main():
         cache.append(seqs, k_new, v_new)
         cache.decode(q, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws, kernel=args.kernel,
                      partition_tokens=args.partition_tokens, work_items=args.work_items, split_events=events,
-                     window=wl.window)
+                     window=wl.window, pool_pieces=args.pool_pieces, pool_shift=args.pool_shift)
         for s, L in zip(seqs, hist_len):
             cache.truncate(s, L)
 
@@ -407,7 +410,7 @@ def main():
     ab = algorithmic_bytes(wl)
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
     prof = (profiled_traffic(args.config) if args.kernel in (0, 2) and not args.work_items and not args.window
-            and not args.kv else None)
+            and not args.kv and not args.pool_pieces else None)
     traffic = prof[0] if prof else None
     achieved = ab["split_kernel"] / (split_avg_ms * 1e-3) / 1e9
     result = {
@@ -430,7 +433,7 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "attended_tokens": int(wl.attend_lens.sum()), "kv_bytes": ab["kv"],
                    "kernel": ["auto", "fma", "mfma"][args.kernel], "partition_tokens": args.partition_tokens or "auto",
-                   "work_items": args.work_items or "auto",
+                   "work_items": args.work_items or "auto", "pool_pieces": args.pool_pieces,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,

@@ -758,9 +758,12 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
   static_assert(EXT || TPW == 1, "decode has one column tile per wave");
   const int w = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  // first column tile of this wave (EXT)
+  // first column tile of this wave (EXT).  Tile groups run last group first:
+  // under the causal mask the last tokens' tiles see the most blocks, so the
+  // longest work-groups start first and the short ones fill in behind them.
   const int ct0 =
-      EXT ? __builtin_amdgcn_readfirstlane(((int)blockIdx.z * a.waves_per_group + (int)(threadIdx.x >> 6)) * TPW)
+      EXT ? __builtin_amdgcn_readfirstlane(((int)(gridDim.z - 1 - blockIdx.z) * a.waves_per_group +
+                                            (int)(threadIdx.x >> 6)) * TPW)
           : 0;
   int total;
   if constexpr (EXT) {
@@ -839,7 +842,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
       const int first = x - sb;                   // first block of this segment in the sequence's list
       const int count = seg_end - x;              // blocks in this segment
       const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
-      if (first == 0 && g == 0 && threadIdx.x == 0 && (!EXT || blockIdx.z == 0)) {
+      if (first == 0 && g == 0 && threadIdx.x == 0 && (!EXT || blockIdx.z == gridDim.z - 1)) {
         // the chunk holding a sequence's first block records which chunks hold it
         a.ws_seginfo[2 * b] = c;
         a.ws_seginfo[2 * b + 1] = chunk_of_block(eb - 1) - c + 1;
