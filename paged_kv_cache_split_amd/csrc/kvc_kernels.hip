@@ -61,6 +61,11 @@ constexpr int kBS = 16;                       // tokens per block (device work)
 #ifndef KVC_PREFETCH_FP8
 #define KVC_PREFETCH_FP8 3
 #endif
+// 16-bit decode with the continuous ring (its next-query registers come out
+// of the ring's).
+#ifndef KVC_PREFETCH_STREAM16
+#define KVC_PREFETCH_STREAM16 4
+#endif
 // Blocks in flight for the several-token kernel with 2, 3 or 4 column tiles
 // per wave (their queries and accumulators take the registers).
 #ifndef KVC_PREFETCH_T2
@@ -743,6 +748,160 @@ __device__ __forceinline__ int wave_first_block(int64_t w, int64_t total, int64_
   return (int)((w * total + W - 1) / W);
 }
 
+// Rows past a sequence's end (only in its last block) hold whatever the slot
+// held before (never written, or a previous owner's rows): their weight is
+// zero, and zeroing their values keeps a NaN pattern there out of the
+// accumulator (0 * NaN is NaN).  t0 = this lane's first row of the block.
+template <kvc_dtype KV, int D>
+__device__ __forceinline__ void zero_rows_past_end(KvBlock<KV, D>& cur, int n, int t0) {
+  constexpr int NDD = D / 16;
+  const int vr = n - t0;                     // rows of this lane's four inside the sequence
+  if constexpr (is_byte_code(KV)) {
+    const uint32_t keep = vr >= 4 ? 0xFFFFFFFFu : (vr <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * vr)));
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) cur.v[dd] &= keep;
+  } else {
+    const uint32_t keep0 = vr >= 2 ? 0xFFFFFFFFu : (vr == 1 ? 0xFFFFu : 0u);
+    const uint32_t keep1 = vr >= 4 ? 0xFFFFFFFFu : (vr == 3 ? 0xFFFFu : 0u);
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) {
+      cur.v[dd][0] &= keep0;
+      cur.v[dd][1] &= keep1;
+    }
+  }
+}
+
+// Matrix-core operands of one block: the K tile (D/32 steps of 16 bytes per
+// lane) and the V^T tile (D/16 dim tiles of 8 bytes per lane) as bf16 / f16.
+// One-byte codes are converted here once per block; 16-bit tiles are used as
+// loaded.
+template <kvc_dtype KV, int D>
+struct BlockOps {
+  u32x4 k[D / 32];
+  u32x2 v[D / 16];
+};
+
+template <kvc_dtype KV, int D>
+__device__ __forceinline__ void convert_codes(const KvBlock<KV, D>& cur, BlockOps<KV, D>& ops) {
+#pragma unroll
+  for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
+    ops.k[2 * c2][0] = code2_to_bf16x2<KV, false>(cur.k[c2][0]);
+    ops.k[2 * c2][1] = code2_to_bf16x2<KV, true>(cur.k[c2][0]);
+    ops.k[2 * c2][2] = code2_to_bf16x2<KV, false>(cur.k[c2][1]);
+    ops.k[2 * c2][3] = code2_to_bf16x2<KV, true>(cur.k[c2][1]);
+    ops.k[2 * c2 + 1][0] = code2_to_bf16x2<KV, false>(cur.k[c2][2]);
+    ops.k[2 * c2 + 1][1] = code2_to_bf16x2<KV, true>(cur.k[c2][2]);
+    ops.k[2 * c2 + 1][2] = code2_to_bf16x2<KV, false>(cur.k[c2][3]);
+    ops.k[2 * c2 + 1][3] = code2_to_bf16x2<KV, true>(cur.k[c2][3]);
+  }
+#pragma unroll
+  for (int dd = 0; dd < D / 16; ++dd) {
+    ops.v[dd][0] = code2_to_bf16x2<KV, false>(cur.v[dd]);
+    ops.v[dd][1] = code2_to_bf16x2<KV, true>(cur.v[dd]);
+  }
+}
+
+// One block's update of one tile of 16 columns: the 16 rows' scores on the
+// matrix cores, the mask (only where `edge`: rows at or past the column's
+// ncol, or before its col_lo), the online-softmax step with the lazily moved
+// reference max, and the PV accumulation.  kop / vop: the block's operands;
+// qk: softmax scale * log2(e) (times the K scale for one-byte codes); vsc: the
+// V scale (1 for 16-bit tiles).
+template <kvc_dtype KV, int D>
+__device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, const u32x4* q, floatx4* acc,
+                                          float& m, float& l, float qk, float vsc, bool edge, int t0, int ncol,
+                                          int col_lo) {
+  constexpr int NQK = D / 32, NDD = D / 16;
+  floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(kop[kk], q[kk], s);
+  float sv[4] = {s[0], s[1], s[2], s[3]};
+  if (edge) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (t0 + e >= ncol || t0 + e < col_lo) sv[e] = kNegInf;
+  }
+  // the scale is positive, so the max of the raw scores, scaled, is the max
+  // of the scaled scores; exp2(s * qk - m) is one fma
+  const float mx = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * qk;
+  const bool grow = mx > m + kRescaleThreshold;
+  if (__any(grow)) {
+    const float mnew = grow ? mx : m;
+    // (a column that has seen no row yet keeps m = -inf: alpha 1, not NaN)
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
+    l *= alpha;
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) acc[dd] *= alpha;
+    m = mnew;
+  }
+  float pv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m));
+  if (edge) {
+    // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (t0 + e >= ncol || t0 + e < col_lo) pv[e] = 0.0f;
+  }
+  l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+  // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
+  // ~2^-17 relative), so rounding the weights to 16 bits costs no accuracy
+  // when the weighted values cancel.
+  u32x2 pb, pl;
+  if constexpr (KV == KVC_F16) {
+    pb[0] = pack_f16x2(pv[0], pv[1]);
+    pb[1] = pack_f16x2(pv[2], pv[3]);
+    pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
+    pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
+  } else {
+    if constexpr (is_byte_code(KV)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+    }
+    pb[0] = pack_bf16x2(pv[0], pv[1]);
+    pb[1] = pack_bf16x2(pv[2], pv[3]);
+    pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
+    pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
+  }
+#pragma unroll
+  for (int dd = 0; dd < NDD; ++dd) {
+    acc[dd] = mfma_pv<KV>(vop[dd], pb, acc[dd]);
+    acc[dd] = mfma_pv<KV>(vop[dd], pl, acc[dd]);
+  }
+}
+
+// Output of one column tile: the normalised rows (out, in the 16-bit dtype of
+// q) or the partial (m, l, acc) at partial row rr.
+template <kvc_dtype KV, int D>
+__device__ __forceinline__ void write_out(const DecodeArgs& a, int64_t out_row, int h, int r, const floatx4* acc,
+                                          float lt) {
+  const float inv = 1.0f / lt;
+#pragma unroll
+  for (int dd = 0; dd < D / 16; ++dd) {
+    const int64_t o = (out_row * a.num_heads + h) * D + 16 * dd + 4 * r;
+    u32x2 wv;
+    if constexpr (KV == KVC_F16) {
+      wv[0] = pack_f16x2(acc[dd][0] * inv, acc[dd][1] * inv);
+      wv[1] = pack_f16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+    } else {
+      wv[0] = pack_bf16x2(acc[dd][0] * inv, acc[dd][1] * inv);
+      wv[1] = pack_bf16x2(acc[dd][2] * inv, acc[dd][3] * inv);
+    }
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t rr, int r, const floatx4* acc, float m,
+                                              float lt) {
+#pragma unroll
+  for (int dd = 0; dd < D / 16; ++dd) *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[dd];
+  if (r == 0) {
+    a.ws_m[rr] = m;
+    a.ws_l[rr] = lt;
+  }
+}
+
 // The split-K kernel body.  EXT = false: decode, one new query token per
 // sequence, one wave per work item, the G query heads of a KV head are the 16
 // columns of the matrix-core tiles.  EXT = true: several new query tokens per
@@ -939,133 +1098,26 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
           const int jj = J0 + i;                       // index of this block in the segment
           const int blk_row = (tb + i) * kBS;          // the block's first row
           const int t0 = blk_row + 4 * r;              // this lane's first row
-          // Rows past the sequence's end (only in its last block) hold whatever
-          // the slot held before (never written, or a previous owner's rows):
-          // their weight is zero, and zeroing their values keeps a NaN pattern
-          // there out of the accumulator (0 * NaN is NaN).
-          if (blk_row + kBS > n) {
-            const int vr = n - t0;                     // rows of this lane's four inside the sequence
-            if constexpr (is_byte_code(KV)) {
-              const uint32_t keep = vr >= 4 ? 0xFFFFFFFFu : (vr <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * vr)));
-#pragma unroll
-              for (int dd = 0; dd < NDD; ++dd) cur.v[dd] &= keep;
-            } else {
-              const uint32_t keep0 = vr >= 2 ? 0xFFFFFFFFu : (vr == 1 ? 0xFFFFu : 0u);
-              const uint32_t keep1 = vr >= 4 ? 0xFFFFFFFFu : (vr == 3 ? 0xFFFFu : 0u);
-#pragma unroll
-              for (int dd = 0; dd < NDD; ++dd) {
-                cur.v[dd][0] &= keep0;
-                cur.v[dd][1] &= keep1;
-              }
-            }
-          }
+          if (blk_row + kBS > n) zero_rows_past_end<KV, D>(cur, n, t0);
           float qk = a.qk_scale;
           float vsc = 1.0f;
-          // one-byte codes become bf16 once per block, for every tile
-          u32x4 kconv[is_byte_code(KV) ? 2 * KvBlock<KV, D>::NK : 1];
-          u32x2 vconv[is_byte_code(KV) ? NDD : 1];
+          BlockOps<KV, D> conv;                        // one-byte codes: converted once, for every tile
           if constexpr (is_byte_code(KV)) {
             qk *= cur.ks;
             vsc = cur.vs;
-#pragma unroll
-            for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
-              kconv[2 * c2][0] = code2_to_bf16x2<KV, false>(cur.k[c2][0]);
-              kconv[2 * c2][1] = code2_to_bf16x2<KV, true>(cur.k[c2][0]);
-              kconv[2 * c2][2] = code2_to_bf16x2<KV, false>(cur.k[c2][1]);
-              kconv[2 * c2][3] = code2_to_bf16x2<KV, true>(cur.k[c2][1]);
-              kconv[2 * c2 + 1][0] = code2_to_bf16x2<KV, false>(cur.k[c2][2]);
-              kconv[2 * c2 + 1][1] = code2_to_bf16x2<KV, true>(cur.k[c2][2]);
-              kconv[2 * c2 + 1][2] = code2_to_bf16x2<KV, false>(cur.k[c2][3]);
-              kconv[2 * c2 + 1][3] = code2_to_bf16x2<KV, true>(cur.k[c2][3]);
-            }
-            if constexpr (TPW > 1) {
-#pragma unroll
-              for (int dd = 0; dd < NDD; ++dd) {
-                vconv[dd][0] = code2_to_bf16x2<KV, false>(cur.v[dd]);
-                vconv[dd][1] = code2_to_bf16x2<KV, true>(cur.v[dd]);
-              }
-            }
+            convert_codes<KV, D>(cur, conv);
           }
+          const u32x4* kop = is_byte_code(KV) ? conv.k : cur.k;
+          const u32x2* vop = is_byte_code(KV) ? conv.v : reinterpret_cast<const u32x2*>(cur.v);
 #pragma unroll
           for (int t = 0; t < TPW; ++t) {
             // (wave-uniform) this tile sees no row of this block
             if (!active[t] || jj < j0[t] || jj >= j1[t]) continue;
-            floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (is_byte_code(KV)) {
-#pragma unroll
-              for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(kconv[kk], qv[t][kk], s);
-            } else {
-#pragma unroll
-              for (int kk = 0; kk < NQK; ++kk) s = mfma_qk<KV>(cur.k[kk], qv[t][kk], s);
-            }
             // Rows some column of the tile may not see exist only near the end
             // of the sequence, or before the window's start (a wave-uniform
-            // test): mask them there, before the max and after exp.
+            // test): they are masked there.
             const bool edge = blk_row + kBS > n_lo[t] || blk_row < lo_hi[t];
-            float sv[4] = {s[0], s[1], s[2], s[3]};
-            if (edge) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (t0 + e >= ncol[t] || t0 + e < col_lo[t]) sv[e] = kNegInf;
-            }
-            // the scale is positive, so the max of the raw scores, scaled, is the
-            // max of the scaled scores; exp2(s * qk - m) is one fma
-            const float mx = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * qk;
-            const bool grow = mx > m[t] + kRescaleThreshold;
-            if (__any(grow)) {
-              const float mnew = grow ? mx : m[t];
-              // (a column that has seen no row yet keeps m = -inf: alpha 1, not NaN)
-              const float alpha = grow ? __builtin_amdgcn_exp2f(m[t] - mnew) : 1.0f;
-              l[t] *= alpha;
-#pragma unroll
-              for (int dd = 0; dd < NDD; ++dd) acc[t][dd] *= alpha;
-              m[t] = mnew;
-            }
-            float pv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m[t]));
-            if (edge) {
-              // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (t0 + e >= ncol[t] || t0 + e < col_lo[t]) pv[e] = 0.0f;
-            }
-            l[t] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-            // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo
-            // to ~2^-17 relative), so rounding the weights to 16 bits costs no
-            // accuracy when the weighted values cancel.
-            u32x2 pb, pl;
-            if constexpr (KV == KVC_F16) {
-              pb[0] = pack_f16x2(pv[0], pv[1]);
-              pb[1] = pack_f16x2(pv[2], pv[3]);
-              pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
-              pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
-            } else {
-              if constexpr (is_byte_code(KV)) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pv[e] *= vsc;
-              }
-              pb[0] = pack_bf16x2(pv[0], pv[1]);
-              pb[1] = pack_bf16x2(pv[2], pv[3]);
-              pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
-              pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
-            }
-#pragma unroll
-            for (int dd = 0; dd < NDD; ++dd) {
-              u32x2 va;
-              if constexpr (is_byte_code(KV)) {
-                if constexpr (TPW > 1) {
-                  va = vconv[dd];
-                } else {
-                  va[0] = code2_to_bf16x2<KV, false>(cur.v[dd]);
-                  va[1] = code2_to_bf16x2<KV, true>(cur.v[dd]);
-                }
-              } else {
-                va = cur.v[dd];
-              }
-              acc[t][dd] = mfma_pv<KV>(va, pb, acc[t][dd]);
-              acc[t][dd] = mfma_pv<KV>(va, pl, acc[t][dd]);
-            }
+            tile_step<KV, D>(kop, vop, qv[t], acc[t], m[t], l[t], qk, vsc, edge, t0, ncol[t], col_lo[t]);
           }
         };
 
@@ -1121,33 +1173,13 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
         if (!head_ok[t]) continue;
         const int h = g * G + hh[t];
         if (whole) {
-          const float inv = 1.0f / lt;
-#pragma unroll
-          for (int dd = 0; dd < NDD; ++dd) {
-            const int64_t o = ((int64_t)q_row[t] * a.num_heads + h) * D + 16 * dd + 4 * r;
-            u32x2 wv;
-            if constexpr (KV == KVC_F16) {
-              wv[0] = pack_f16x2(acc[t][dd][0] * inv, acc[t][dd][1] * inv);
-              wv[1] = pack_f16x2(acc[t][dd][2] * inv, acc[t][dd][3] * inv);
-            } else {
-              wv[0] = pack_bf16x2(acc[t][dd][0] * inv, acc[t][dd][1] * inv);
-              wv[1] = pack_bf16x2(acc[t][dd][2] * inv, acc[t][dd][3] * inv);
-            }
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
-          }
+          write_out<KV, D>(a, q_row[t], h, r, acc[t], lt);
         } else {
           // partial of (sequence b, chunk c) for this column: slot b + c is
           // unique, since every segment boundary advances the sequence, the
           // chunk, or both (EXT: one set of slots per query token index)
           const int tok = q_row[t] - q0;
-          const int64_t rr = ((EXT ? (int64_t)tok * a.num_heads : 0) + h) * slots + b + c;
-#pragma unroll
-          for (int dd = 0; dd < NDD; ++dd)
-            *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 16 * dd + 4 * r) = acc[t][dd];
-          if (r == 0) {
-            a.ws_m[rr] = m[t];
-            a.ws_l[rr] = lt;
-          }
+          write_partial<D>(a, ((EXT ? (int64_t)tok * a.num_heads : 0) + h) * slots + b + c, r, acc[t], m[t], lt);
         }
       }
       x = seg_end;
@@ -1170,6 +1202,198 @@ template <kvc_dtype KV, int D, int PF>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   extern __shared__ int seq_start[];   // [batch + 1]
   attend_mfma<KV, D, PF, false, 1>(a, seq_start);
+}
+
+// Decode with one continuous prefetch ring over the wave's whole chunk.  The
+// chunk is cut into segments (its runs of one sequence's blocks); instead of
+// draining the ring and refilling it at every segment, the prefetch cursor
+// runs PF blocks ahead straight across segment boundaries, and the next
+// segment's query is loaded when the current one begins, so a segment change
+// costs its output write and nothing in flight is lost.  Same arithmetic,
+// block for block, as attend_mfma<.., false, 1>.
+template <kvc_dtype KV, int D, int PF>
+__device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_start) {
+  const int w = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int total = __builtin_amdgcn_readfirstlane(scan_block_counts<false>(a, seq_start, lane));
+  __syncthreads();
+  // never more waves than blocks, so every wave that runs owns >= 1 block
+  const int W = a.work_items < total ? a.work_items : total;
+  if (w >= W) return;
+  const int xa = wave_first_block(w, total, W), xb = wave_first_block(w + 1, total, W);
+  const int c = w;                             // chunk id (no pool on this path)
+  const int nn = lane & 15, r = lane >> 4;
+  const uint32_t koff = k_lane_offset<KV>(lane), voff = v_lane_offset<KV>(nn, r);
+  const int G = a.group;
+  constexpr int NQK = D / 32;
+  constexpr int NDD = D / 16;
+  const int64_t head_off = (int64_t)g * a.tile_bytes;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
+  const int slots = a.batch + a.chunk_slots;
+  const bool head_ok = nn < G;
+  const int h = g * G + nn;
+  const int win = a.window;
+
+  auto seq_len = [&](int bb) -> int {
+    return __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, bb, a.max_ctx, a.max_blocks));
+  };
+  auto start_of = [&](int bb) -> int { return __builtin_amdgcn_readfirstlane(seq_start[bb]); };
+  // Block-table row of sequence bb indexed by list position: entry x is the
+  // physical block of list block x (the list starts at the first visible block).
+  auto row_of = [&](int bb, int n_bb) -> const_i32_kptr {
+    return (const_i32_kptr)(a.block_table + (int64_t)bb * a.max_blocks + first_visible_block(n_bb, 1, win)) -
+           start_of(bb);
+  };
+  // the first sequence after bb holding a block at or after list position x
+  auto next_seq = [&](int bb, int x) -> int {
+    do {
+      ++bb;
+    } while (start_of(bb + 1) <= x);
+    return bb;
+  };
+  int b = 0;                                   // sequence holding block xa
+  {
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seq_start[mid] <= xa) lo = mid;
+      else hi = mid - 1;
+    }
+    b = __builtin_amdgcn_readfirstlane(lo);
+  }
+
+  // ---- prefetch cursor: list block xf of sequence bf ----
+  int xf = xa, bf = b, ebf = start_of(b + 1);
+  const_i32_kptr rowf = row_of(b, seq_len(b));
+  int ph_last = 0;
+  // physical id of the next block to fetch; past the chunk's end the last one
+  // again (the L2 still holds it), so every step issues the same loads
+  auto next_phys = [&]() -> int {
+    if (xf < xb) {
+      if (xf == ebf) {
+        bf = next_seq(bf, xf);
+        ebf = start_of(bf + 1);
+        rowf = row_of(bf, seq_len(bf));
+      }
+      ph_last = clamp_block(rowf[xf], a.num_blocks);
+      ++xf;
+    }
+    return ph_last;
+  };
+
+  // ---- process cursor: the segment of sequence b from list block x0 to seg_end ----
+  int sb = 0, eb = 0, x0 = 0, seg_end = 0, n = 0, fbp = 0, lo_hi = 0, nb_q = -1;
+  u32x4 q[NQK], q_next[NQK];
+  floatx4 acc[NDD];
+  float m = kNegInf, l = 0.0f;
+  auto load_q = [&](u32x4* dst, int bq) {
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)bq * a.num_heads + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < NQK; ++kk) {
+      int d0;
+      if constexpr (is_byte_code(KV)) d0 = (r + 4 * (kk >> 1)) * 16 + (kk & 1) * 8;
+      else d0 = (4 * kk + r) * 8;
+      dst[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
+    }
+  };
+  // set up the segment of sequence b starting at list block x; its query is
+  // already in q.  The next segment's query is requested now.
+  auto begin = [&](int x) {
+    sb = start_of(b);
+    eb = start_of(b + 1);
+    x0 = x;
+    seg_end = eb < xb ? eb : xb;
+    n = seq_len(b);
+    fbp = first_visible_block(n, 1, win);
+    lo_hi = win > 0 ? max(0, n - win) : 0;
+    if (x == sb && g == 0 && lane == 0) {
+      // the chunk holding a sequence's first block records which chunks hold it
+      a.ws_seginfo[2 * b] = c;
+      a.ws_seginfo[2 * b + 1] = (int)(((int64_t)(eb - 1) * W) / total) - c + 1;
+    }
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
+    m = kNegInf;
+    l = 0.0f;
+    nb_q = -1;
+    if (seg_end < xb) {
+      nb_q = next_seq(b, seg_end);
+      load_q(q_next, nb_q);
+    }
+  };
+  // after the segment's last block: write it out, move to the next segment
+  auto finish = [&]() {
+    const float lt = sum_over_row_groups(l);
+    if (head_ok) {
+      if (x0 == sb && seg_end == eb) write_out<KV, D>(a, b, h, r, acc, lt);
+      else write_partial<D>(a, (int64_t)h * slots + b + c, r, acc, m, lt);
+    }
+    if (seg_end < xb) {
+      b = nb_q;
+#pragma unroll
+      for (int kk = 0; kk < NQK; ++kk) q[kk] = q_next[kk];
+      begin(seg_end);
+    }
+  };
+  auto process = [&](KvBlock<KV, D>& cur, int x) {
+    const int blk_row = (fbp + (x - sb)) * kBS;   // the block's first row
+    const int t0 = blk_row + 4 * r;               // this lane's first row
+    if (blk_row + kBS > n) zero_rows_past_end<KV, D>(cur, n, t0);
+    float qk = a.qk_scale;
+    float vsc = 1.0f;
+    BlockOps<KV, D> conv;
+    if constexpr (is_byte_code(KV)) {
+      qk *= cur.ks;
+      vsc = cur.vs;
+      convert_codes<KV, D>(cur, conv);
+    }
+    const u32x4* kop = is_byte_code(KV) ? conv.k : cur.k;
+    const u32x2* vop = is_byte_code(KV) ? conv.v : reinterpret_cast<const u32x2*>(cur.v);
+    const bool edge = blk_row + kBS > n || blk_row < lo_hi;
+    tile_step<KV, D>(kop, vop, q, acc, m, l, qk, vsc, edge, t0, n, lo_hi);
+    if (x + 1 == seg_end) finish();
+  };
+
+  load_q(q, b);
+  begin(xa);
+  KvBlock<KV, D> buf[PF + 1];
+  auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
+    const int64_t o = (int64_t)ph * block_stride + head_off;
+    load_block<KV, D>(dst, a.k + o, a.v + o, koff, voff);
+    if constexpr (is_byte_code(KV)) {
+      dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
+      dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < PF; ++j) fetch(buf[j], next_phys());
+  int ph_next = next_phys();                  // one step ahead
+  const int cnt = xb - xa;
+  int i0 = 0;
+  for (; i0 + PF + 1 <= cnt; i0 += PF + 1) {
+#pragma unroll
+    for (int j = 0; j <= PF; ++j) {
+      const int ph = ph_next;
+      ph_next = next_phys();
+      fetch(buf[(j + PF) % (PF + 1)], ph);
+      process(buf[j], xa + i0 + j);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int i = i0 + j;
+    if (i >= cnt) break;
+    const int ph = ph_next;
+    ph_next = next_phys();
+    fetch(buf[(j + PF) % (PF + 1)], ph);
+    process(buf[j], xa + i);
+  }
+}
+
+template <kvc_dtype KV, int D, int PF>
+__global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
+  extern __shared__ int seq_start[];   // [batch + 1]
+  decode_stream<KV, D, PF>(a, seq_start);
 }
 
 // grid (work items, KV heads, tile groups), waves_per_group waves each, TPW
@@ -1333,6 +1557,8 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
   }
   if constexpr (KV != KVC_F32) {
     constexpr int PF = is_byte_code(KV) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_16;  // blocks in flight per wave
+    // the continuous ring holds the next segment's query too
+    constexpr int KVC_STREAM_PF = is_byte_code(KV) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_STREAM16;
     // ticket counters start at zero (a kernel, not a memset, so the sequence
     // can be captured in a graph); without a pool no wave touches them
     if (a.pool_pieces > 0 && tile_groups == 0) {
@@ -1343,8 +1569,15 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     const int threads = ((a.group * (D / 4) + 63) / 64) * 64;   // <= 16 heads * 32 columns = 512
     if (tile_groups == 0) {
       dim3 grid(a.work_items, a.num_kv_heads);
-      if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64, PF>), grid, dim3(64), scan_lds, s, a);
-      else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128, PF>), grid, dim3(64), scan_lds, s, a);
+      // static split: one continuous ring per chunk; with the dynamic pool the
+      // segment-by-segment body, whose chunks come and go at run time
+      if (a.pool_pieces > 0) {
+        if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64, PF>), grid, dim3(64), scan_lds, s, a);
+        else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128, PF>), grid, dim3(64), scan_lds, s, a);
+      } else {
+        if (D == 64) hipLaunchKernelGGL((decode_stream_kernel<KV, 64, KVC_STREAM_PF>), grid, dim3(64), scan_lds, s, a);
+        else hipLaunchKernelGGL((decode_stream_kernel<KV, 128, KVC_STREAM_PF>), grid, dim3(64), scan_lds, s, a);
+      }
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
       dim3 mgrid(a.num_kv_heads, a.batch);
