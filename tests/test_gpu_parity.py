@@ -145,7 +145,20 @@ def test_dynamic_pool_pieces(kv):
         check_close(to_f64(o), ref, *TOL[kv], f"{kv} work_items={wi} pieces={pieces} shift={shift}")
         again = gpu_decode_again(cache, wl, values, bt, cl, **split)
         torch.cuda.synchronize()
-        assert torch.equal(o.view(torch.int16), again.view(torch.int16)), f"not deterministic: {split}"
+        check_close(to_f64(again), ref, *TOL[kv], f"{kv} repeat of work_items={wi} pieces={pieces} shift={shift}")
+        assert_same_bits(o, again, f"not deterministic: {split}")
+
+
+def assert_same_bits(a, b, what):
+    """a and b bit for bit; else name the (sequence, head) pairs that differ."""
+    same = a.view(torch.int16) == b.view(torch.int16)
+    if bool(same.all()):
+        return
+    bad = (~same).nonzero().cpu().tolist()
+    pairs = sorted({(s, h) for s, h, _ in bad})
+    diff = (a.float() - b.float()).abs().max().item()
+    raise AssertionError(f"{what}: {len(bad)} elements differ, max |diff| {diff:.3g}, "
+                         f"(sequence, head) pairs {pairs[:24]}")
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (8, 4, 128), (16, 4, 64), (16, 1, 128), (32, 2, 128), (12, 3, 64)])
