@@ -83,10 +83,20 @@ def algorithmic_bytes(wl):
                 split_kernel=kv + scales + q + tables)
 
 
-def profiled_traffic(config_id):
+def workload_key(args):
+    """The workload a run measures, as the profile summaries name it."""
+    if args.extend:
+        return f"extend {args.extend}"
+    if args.window:
+        return "window"
+    return f"config {args.config}" + (f" kv {args.kv}" if args.kv else "")
+
+
+def profiled_traffic(key):
     """HBM bytes per split-kernel launch from a committed rocprofv3 summary
-    (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy kernel's counts),
-    or None when no summary was taken on the current kernel source."""
+    (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy kernel's counts)
+    of the workload `key`, or None when no summary was taken on the current
+    kernel source."""
     import glob
     import hashlib
     src = os.path.join(ROOT, "paged_kv_cache_split_amd", "csrc", "kvc_kernels.hip")
@@ -102,7 +112,7 @@ def profiled_traffic(config_id):
                     rec = json.loads(line)
                 except ValueError:
                     continue
-                if rec.get("config_id") == config_id and rec.get("kernel_source_sha256") == sha:
+                if rec.get("workload_key") == key and rec.get("kernel_source_sha256") == sha:
                     return rec["traffic_bytes_per_launch"], os.path.relpath(fn, ROOT)
     return None
 
@@ -224,6 +234,27 @@ def cpu_baseline_extend(wl, values, budget_s):
                       f"os.cpu_count()={os.cpu_count()}"}
 
 
+def calibrate_copy(dev):
+    """Time the plain 2 GiB copy kernel (its known bytes scale the profiler's
+    HBM byte counters)."""
+    import torch
+    import paged_kv_cache_split_amd as kvc
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    kvc.stream_copy(dst, src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        kvc.stream_copy(dst, src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del src, dst
+    return {"copy_bytes": n, "copy_read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
 def run_extend(args):
     import numpy as np
     import torch
@@ -298,7 +329,9 @@ def run_extend(args):
         achieved = w["bytes"] / (split_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof.update({"traffic": None, "kernel": "multi-token split-K kernel", "avg_launch_us": round(split_avg_ms * 1e3, 2),
+    prof = profiled_traffic(workload_key(args)) if not args.work_items and not args.tiles_per_wave else None
+    roof.update({"traffic": prof[0] if prof else None, "traffic_source": prof[1] if prof else None,
+                 "kernel": "multi-token split-K kernel", "avg_launch_us": round(split_avg_ms * 1e3, 2),
                  "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
                  "algorithmic_bytes_per_launch": w["bytes"], "algorithmic_flops_per_launch": w["flops"],
                  "intensity_flop_per_byte": round(intensity, 1)})
@@ -326,6 +359,8 @@ def run_extend(args):
                    "parallelism": "single GPU"},
         "roofline": roof,
     }
+    if args.calibrate:
+        result["calibration"] = calibrate_copy(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_extend(wl, values, args.cpu_seconds)
@@ -409,8 +444,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ab = algorithmic_bytes(wl)
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
-    prof = (profiled_traffic(args.config) if args.kernel in (0, 2) and not args.work_items and not args.window
-            and not args.kv and not args.pool_pieces else None)
+    prof = (profiled_traffic(workload_key(args)) if args.kernel in (0, 2) and not args.work_items
+            and not args.pool_pieces else None)
     traffic = prof[0] if prof else None
     achieved = ab["split_kernel"] / (split_avg_ms * 1e-3) / 1e9
     result = {
@@ -443,20 +478,7 @@ def main():
                      "traffic_source": prof[1] if prof else None},
     }
     if args.calibrate:
-        n = 1 << 31
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty(n, dtype=torch.uint8, device=dev)
-        kvc.stream_copy(dst, src)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            kvc.stream_copy(dst, src)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 5
-        result["calibration"] = {"copy_bytes": n, "copy_read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
-        del src, dst
+        result["calibration"] = calibrate_copy(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = (cpu_baseline_window(wl, values, args.cpu_seconds) if wl.window
