@@ -227,9 +227,9 @@ kvc_status kvc_export_tables(kvc_cache* cache, int32_t batch, const int64_t* seq
  *  one list that is cut into `work_items` equal runs, one wave each.  With
  *  pool_pieces > 0, the last 1/2^pool_shift of every run is further cut into
  *  pool_pieces pieces that the waves of that head take at run time, first come
- *  first served, so waves that progress faster take more of them (each piece
- *  restarts the wave's prefetch, which costs about what the balance gains on
- *  MI355X, hence off by default).  Each chunk (a run's main part or a
+ *  first served, so waves that progress faster take more of them (a wave's
+ *  prefetch runs on into the pieces it takes; on MI355X the balance gains at
+ *  most ~1% and costs fp8 caches ~5%, hence off by default).  Each chunk (a run's main part or a
  *  piece) yields one partial (max, sum, acc) per sequence it touches, or the
  *  final output when it holds a whole sequence, and a merge kernel combines
  *  the partials in list order.  Chunk bounds depend only on the lengths and
@@ -241,8 +241,9 @@ typedef struct kvc_decode_opts {
   int32_t kernel;           /* 0 = auto, 1 = fp32 FMA (VALU) kernel, 2 = MFMA kernel (16-bit and fp8 KV) */
   int32_t work_items;       /* MFMA kernel: waves per KV head; 0 = max(1, 1024 / num_kv_heads) */
   int32_t pool_pieces;      /* MFMA kernel: pieces per run handed out at run time, <= 64; <= 0 = none
-                               (static split, the default); unused when a run's pool would hold fewer
-                               blocks than pieces */
+                               (static split, the default); unused when a piece would hold fewer than
+                               two turns of the wave's prefetch ring (8 blocks for one-byte codes, 10
+                               for 16-bit caches) */
   int32_t pool_shift;       /* MFMA kernel: the pool is the last 1/2^pool_shift of each run, 1..6; 0 = 3 */
   kvc_event_t split_start;  /* optional events recorded on `stream` around the split-K kernel */
   kvc_event_t split_end;

@@ -748,6 +748,54 @@ __device__ __forceinline__ int wave_first_block(int64_t w, int64_t total, int64_
   return (int)((w * total + W - 1) / W);
 }
 
+// Chunks of one KV head's block list: `total` blocks split evenly over W
+// waves.  With a pool (KP > 0) the last 1/2^shift of every wave's run is cut
+// into KP pieces that go, at run time, to whichever wave of the head asks
+// first.  Chunk ids follow the list order -- wave w's main chunk is
+// w * (KP + 1), its pieces follow it -- so the chunks holding one sequence
+// have consecutive ids whichever waves processed them, and the chunk bounds
+// (hence the result) do not depend on who took which piece.
+struct ChunkGeometry {
+  int total, W, KP, shift;
+  // wave ww's run is [r0, r1); its main chunk ends at rm
+  __device__ void wave_range(int ww, int& r0, int& r1, int& rm) const {
+    r0 = wave_first_block(ww, total, W);
+    r1 = wave_first_block(ww + 1, total, W);
+    rm = KP ? r1 - ((r1 - r0) >> shift) : r1;
+  }
+  // chunk holding list block y (piece j of a pool of len blocks starts at
+  // ceil(j * len / KP), so block o of the pool is in piece o * KP / len)
+  __device__ int chunk_of_block(int y) const {
+    const int ww = (int)(((int64_t)y * W) / total);
+    int r0, r1, rm;
+    wave_range(ww, r0, r1, rm);
+    if (y < rm) return ww * (KP + 1);
+    return ww * (KP + 1) + 1 + (int)(((int64_t)(y - rm) * KP) / (r1 - rm));
+  }
+  // ticket t < W * KP: piece t % KP of wave t / KP's pool, blocks [xa, xb), id c
+  __device__ void piece(int t, int& xa, int& xb, int& c) const {
+    const int ww = t / KP, j = t - ww * KP;
+    int r0, r1, rm;
+    wave_range(ww, r0, r1, rm);
+    const int64_t len = r1 - rm;
+    xa = rm + (int)((j * len + KP - 1) / KP);
+    xb = rm + (int)(((j + 1) * len + KP - 1) / KP);
+    c = ww * (KP + 1) + 1 + j;
+  }
+};
+
+// The sequence holding list block x: the last b with seq_start[b] <= x
+// (an empty sequence shares its start with the next one).
+__device__ __forceinline__ int seq_holding(const int* seq_start, int batch, int x) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(seq_start[mid]) <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return __builtin_amdgcn_readfirstlane(lo);
+}
+
 // Rows past a sequence's end (only in its last block) hold whatever the slot
 // held before (never written, or a previous owner's rows): their weight is
 // zero, and zeroing their values keeps a NaN pattern there out of the
@@ -902,64 +950,31 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t rr, i
   }
 }
 
-// The split-K kernel body.  EXT = false: decode, one new query token per
-// sequence, one wave per work item, the G query heads of a KV head are the 16
-// columns of the matrix-core tiles.  EXT = true: several new query tokens per
-// sequence (q_start), each attending causally -- the token at position p sees
-// rows 0..p -- so a column is a (query token, head) pair with its own count of
-// visible rows.  A sequence's ceil(ql * G / 16) column tiles are spread TPW
-// to a wave (the wave reuses each K/V block it loads for all of its tiles),
-// over the waves of a work-group (side by side on one chunk of blocks) and
-// over grid.z.  Decode is the EXT case with one token and one tile, compiled
-// apart so its loop carries none of the per-column bookkeeping.
-template <kvc_dtype KV, int D, int PF, bool EXT, int TPW>
-__device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start) {
-  static_assert(EXT || TPW == 1, "decode has one column tile per wave");
+// The split-K body for several new query tokens per sequence (q_start), each
+// attending causally -- the token at position p sees rows 0..p -- so a column
+// of the matrix-core tiles is a (query token, head) pair with its own count of
+// visible rows.  A sequence's ceil(ql * G / 16) column tiles are spread TPW to
+// a wave (the wave reuses each K/V block it loads for all of its tiles), over
+// the waves of a work-group (side by side on one chunk of blocks) and over
+// grid.z.  One token per sequence is decode (decode_stream, the same per-block
+// arithmetic without the per-column bookkeeping).
+template <kvc_dtype KV, int D, int PF, int TPW>
+__device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_start) {
   const int w = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  // first column tile of this wave (EXT).  Tile groups run last group first:
-  // under the causal mask the last tokens' tiles see the most blocks, so the
-  // longest work-groups start first and the short ones fill in behind them.
-  const int ct0 =
-      EXT ? __builtin_amdgcn_readfirstlane(((int)(gridDim.z - 1 - blockIdx.z) * a.waves_per_group +
-                                            (int)(threadIdx.x >> 6)) * TPW)
-          : 0;
-  int total;
-  if constexpr (EXT) {
-    if (threadIdx.x < 64) scan_block_counts<true>(a, seq_start, lane);
-    __syncthreads();
-    total = __builtin_amdgcn_readfirstlane(seq_start[a.batch]);
-  } else {
-    total = __builtin_amdgcn_readfirstlane(scan_block_counts<false>(a, seq_start, lane));
-    __syncthreads();
-  }
+  // first column tile of this wave.  Tile groups run last group first: under
+  // the causal mask the last tokens' tiles see the most blocks, so the longest
+  // work-groups start first and the short ones fill in behind them.
+  const int ct0 = __builtin_amdgcn_readfirstlane(
+      ((int)(gridDim.z - 1 - blockIdx.z) * a.waves_per_group + (int)(threadIdx.x >> 6)) * TPW);
+  if (threadIdx.x < 64) scan_block_counts<true>(a, seq_start, lane);
+  __syncthreads();
+  const int total = __builtin_amdgcn_readfirstlane(seq_start[a.batch]);
   // never more waves than blocks, so every wave that runs owns >= 1 block
   const int W = a.work_items < total ? a.work_items : total;
   if (w >= W) return;
-  // Chunks.  Wave w owns blocks [x0, x1) of this head's list (an even split);
-  // with a dynamic pool (decode only), the last 1/2^pool_shift of that range
-  // is cut into KP pieces that go to whichever wave of this head asks first (a
-  // ticket counter), so waves that run fast (their XCD, their share of the
-  // memory system) take work from those that run slow.  Chunk ids follow the
-  // list order: wave w's main chunk is w * (KP + 1), its pieces follow it.
-  // The pool is used only when every piece of every wave holds >= 1 block.
-  const int KP =
-      (!EXT && a.pool_pieces > 0 && ((total / W) >> a.pool_shift) >= a.pool_pieces) ? a.pool_pieces : 0;
-  const int CPW = KP + 1;
-  auto wave_range = [&](int ww, int& r0, int& r1, int& rm) {
-    r0 = wave_first_block(ww, total, W);
-    r1 = wave_first_block(ww + 1, total, W);
-    rm = KP ? r1 - ((r1 - r0) >> a.pool_shift) : r1;   // end of the main chunk
-  };
-  // chunk holding block y (piece j of a pool of len blocks starts at
-  // ceil(j * len / KP), so block o of the pool is in piece o * KP / len)
-  auto chunk_of_block = [&](int y) -> int {
-    const int ww = (int)(((int64_t)y * W) / total);
-    int r0, r1, rm;
-    wave_range(ww, r0, r1, rm);
-    if (y < rm) return ww * CPW;
-    return ww * CPW + 1 + (int)(((int64_t)(y - rm) * KP) / (r1 - rm));
-  };
+  // chunk w: blocks [xa, xb) of this head's list (an even split)
+  const ChunkGeometry geo{total, W, 0, 0};
   const int nn = lane & 15, r = lane >> 4;
   const uint32_t koff = k_lane_offset<KV>(lane), voff = v_lane_offset<KV>(nn, r);
   const int G = a.group;
@@ -969,27 +984,11 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
   const int64_t block_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
   const int slots = a.batch + a.chunk_slots;
 
-  int xa, xb, c;   // the chunk being processed: blocks [xa, xb), id c
+  int xa, xb, rm_unused;
+  geo.wave_range(w, xa, xb, rm_unused);
+  const int c = w;
   {
-    int r0, r1, rm;
-    wave_range(w, r0, r1, rm);
-    xa = r0;
-    xb = rm;
-    c = w * CPW;
-  }
-  for (;;) {
-    int t_next = 0;   // ticket of the next pool piece, asked for before the chunk's last blocks
-    // sequence holding block xa: the last b with seq_start[b] <= xa
-    int b = 0;
-    {
-      int lo = 0, hi = a.batch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seq_start[mid] <= xa) lo = mid;
-        else hi = mid - 1;
-      }
-      b = __builtin_amdgcn_readfirstlane(lo);
-    }
+    int b = seq_holding(seq_start, a.batch, xa);
     // Everything below that indexes memory is wave-uniform (scalar registers),
     // so block ids and fp8 scales come through scalar loads, which are counted
     // apart from the vector loads of the tiles and never drain the prefetch ring.
@@ -1001,27 +1000,23 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
       const int first = x - sb;                   // first block of this segment in the sequence's list
       const int count = seg_end - x;              // blocks in this segment
       const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
-      if (first == 0 && g == 0 && threadIdx.x == 0 && (!EXT || blockIdx.z == gridDim.z - 1)) {
+      if (first == 0 && g == 0 && threadIdx.x == 0 && blockIdx.z == gridDim.z - 1) {
         // the chunk holding a sequence's first block records which chunks hold it
         a.ws_seginfo[2 * b] = c;
-        a.ws_seginfo[2 * b + 1] = chunk_of_block(eb - 1) - c + 1;
+        a.ws_seginfo[2 * b + 1] = geo.chunk_of_block(eb - 1) - c + 1;
       }
-      int ql = 1, q0 = b;
-      if constexpr (EXT) {
-        ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
-        if (ct0 * 16 >= ql * G) {                 // no column of this sequence in the wave's tiles
-          x = seg_end;
-          continue;
-        }
-        q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
+      const int ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
+      if (ct0 * 16 >= ql * G) {                   // no column of this sequence in the wave's tiles
+        x = seg_end;
+        continue;
       }
+      const int q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
       const int win = a.window;
       // table index of the segment's first block
       const int tb0 = __builtin_amdgcn_readfirstlane(first_visible_block(n, ql, win)) + first;
-      // Columns of this lane, one per tile.  Decode: head nn of the group, every
-      // column sees the n rows.  EXT: column 16 ct + nn is (query token tok,
-      // head hh); the token sits at position n - ql + tok and sees rows up to
-      // n - ql + tok.  With a window a column sees rows [col_lo, ncol),
+      // Columns of this lane, one per tile: column 16 ct + nn is (query token
+      // tok, head hh); the token sits at position n - ql + tok and sees rows up
+      // to n - ql + tok.  With a window a column sees rows [col_lo, ncol),
       // col_lo = ncol - window.  Per tile, n_lo is the fewest rows a column
       // sees, lo_hi the highest window start, and [j0, j1) the blocks of the
       // segment some column of the tile sees; the wave walks their union.
@@ -1030,23 +1025,15 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
       int J0 = count, J1 = 0;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        int tok = 0, n_hi = n;
-        hh[t] = nn;
-        q_row[t] = b;
-        head_ok[t] = nn < G;
-        active[t] = true;
-        n_lo[t] = n;
-        if constexpr (EXT) {
-          const int ct = ct0 + t;
-          active[t] = ct * 16 < ql * G;
-          const int col = ct * 16 + nn;
-          tok = col / G;
-          hh[t] = col - tok * G;
-          q_row[t] = q0 + tok;
-          head_ok[t] = active[t] && tok < ql && q_row[t] >= 0 && q_row[t] < a.total_q;
-          n_lo[t] = n - ql + 1 + (ct * 16) / G;
-          n_hi = n - ql + 1 + min(ql - 1, (ct * 16 + 15) / G);
-        }
+        const int ct = ct0 + t;
+        active[t] = ct * 16 < ql * G;
+        const int col = ct * 16 + nn;
+        const int tok = col / G;
+        hh[t] = col - tok * G;
+        q_row[t] = q0 + tok;
+        head_ok[t] = active[t] && tok < ql && q_row[t] >= 0 && q_row[t] < a.total_q;
+        n_lo[t] = n - ql + 1 + (ct * 16) / G;
+        const int n_hi = n - ql + 1 + min(ql - 1, (ct * 16 + 15) / G);
         // padding columns see all n rows, so they stay finite
         ncol[t] = head_ok[t] ? n - ql + 1 + tok : n;
         col_lo[t] = win > 0 ? max(0, ncol[t] - win) : 0;
@@ -1150,9 +1137,6 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
             process(buf[j], i);
           }
         }
-        // The next piece is asked for now, so the ticket's round trip overlaps
-        // the last blocks of the chunk.
-        if (KP != 0 && seg_end == xb && lane == 0) t_next = atomicAdd(a.ws_ticket + g, 1);
         // the last, partial turn
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
@@ -1177,42 +1161,38 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int* seq_start)
         } else {
           // partial of (sequence b, chunk c) for this column: slot b + c is
           // unique, since every segment boundary advances the sequence, the
-          // chunk, or both (EXT: one set of slots per query token index)
+          // chunk, or both; one set of slots per query token index
           const int tok = q_row[t] - q0;
-          write_partial<D>(a, ((EXT ? (int64_t)tok * a.num_heads : 0) + h) * slots + b + c, r, acc[t], m[t], lt);
+          write_partial<D>(a, ((int64_t)tok * a.num_heads + h) * slots + b + c, r, acc[t], m[t], lt);
         }
       }
       x = seg_end;
     }
-    if (KP == 0) break;
-    // next pool piece of this head
-    const int t = __builtin_amdgcn_readfirstlane(t_next);
-    if (t >= W * KP) break;
-    const int ww = t / KP, j = t - ww * KP;
-    int r0, r1, rm;
-    wave_range(ww, r0, r1, rm);
-    const int len = r1 - rm;
-    xa = rm + (j * len + KP - 1) / KP;
-    xb = rm + ((j + 1) * len + KP - 1) / KP;
-    c = ww * CPW + 1 + j;
   }
 }
 
-template <kvc_dtype KV, int D, int PF>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
-  extern __shared__ int seq_start[];   // [batch + 1]
-  attend_mfma<KV, D, PF, false, 1>(a, seq_start);
-}
-
-// Decode with one continuous prefetch ring over the wave's whole chunk.  The
-// chunk is cut into segments (its runs of one sequence's blocks); instead of
-// draining the ring and refilling it at every segment, the prefetch cursor
-// runs PF blocks ahead straight across segment boundaries, and the next
-// segment's query is loaded when the current one begins, so a segment change
-// costs its output write and nothing in flight is lost.  Same arithmetic,
-// block for block, as attend_mfma<.., false, 1>.
-template <kvc_dtype KV, int D, int PF>
+// Decode with one continuous prefetch ring per wave.  A wave walks a sequence
+// of ranges of its KV head's block list: its main chunk, then (with a pool)
+// the pieces it wins.  A range is cut into segments (its runs of one
+// sequence's blocks).  Two cursors walk the ranges: the prefetch cursor runs
+// PF + 1 blocks ahead of the process cursor, straight across segment and
+// range boundaries, so nothing in flight is drained when a segment or range
+// ends; the next segment's query is loaded while the current one runs, and a
+// segment change costs its output write.
+//
+// Pieces are claimed with a per-head ticket counter.  The ring runs in whole
+// turns of PF + 1 blocks; the ticket for the range after the prefetch
+// cursor's current one is requested at the head of the turn before the one in
+// which that cursor reaches the range's end, and read at the next turn's head.
+// A turn's worth of tile loads is issued after the request, so the wait for
+// its result is a wait for the ticket alone (vector memory results return in
+// issue order), not for the tiles in flight.  This needs every range to
+// outlast two turns, which the pool's size test below guarantees; then the
+// prefetch cursor is also never more than one range ahead of the process
+// cursor, so one pending range is handed between them.
+template <kvc_dtype KV, int D, int PF, bool POOL>
 __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_start) {
+  constexpr int TURN = PF + 1;
   const int w = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x;
   const int total = __builtin_amdgcn_readfirstlane(scan_block_counts<false>(a, seq_start, lane));
@@ -1220,8 +1200,16 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
   // never more waves than blocks, so every wave that runs owns >= 1 block
   const int W = a.work_items < total ? a.work_items : total;
   if (w >= W) return;
-  const int xa = wave_first_block(w, total, W), xb = wave_first_block(w + 1, total, W);
-  const int c = w;                             // chunk id (no pool on this path)
+  // The pool is used when every piece holds >= 2 turns of blocks (a wave's
+  // pool is >= floor(total / W) >> shift blocks; the main chunk is at least
+  // as long as the pool since shift >= 1).
+  const int KP = (POOL && a.pool_pieces > 0 && a.pool_shift >= 1 &&
+                  ((total / W) >> a.pool_shift) >= a.pool_pieces * 2 * TURN)
+                     ? a.pool_pieces
+                     : 0;
+  const ChunkGeometry geo{total, W, KP, a.pool_shift};
+  int xa, xb_main, r1_unused;
+  geo.wave_range(w, xa, r1_unused, xb_main);
   const int nn = lane & 15, r = lane >> 4;
   const uint32_t koff = k_lane_offset<KV>(lane), voff = v_lane_offset<KV>(nn, r);
   const int G = a.group;
@@ -1251,41 +1239,6 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
     } while (start_of(bb + 1) <= x);
     return bb;
   };
-  int b = 0;                                   // sequence holding block xa
-  {
-    int lo = 0, hi = a.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (seq_start[mid] <= xa) lo = mid;
-      else hi = mid - 1;
-    }
-    b = __builtin_amdgcn_readfirstlane(lo);
-  }
-
-  // ---- prefetch cursor: list block xf of sequence bf ----
-  int xf = xa, bf = b, ebf = start_of(b + 1);
-  const_i32_kptr rowf = row_of(b, seq_len(b));
-  int ph_last = 0;
-  // physical id of the next block to fetch; past the chunk's end the last one
-  // again (the L2 still holds it), so every step issues the same loads
-  auto next_phys = [&]() -> int {
-    if (xf < xb) {
-      if (xf == ebf) {
-        bf = next_seq(bf, xf);
-        ebf = start_of(bf + 1);
-        rowf = row_of(bf, seq_len(bf));
-      }
-      ph_last = clamp_block(rowf[xf], a.num_blocks);
-      ++xf;
-    }
-    return ph_last;
-  };
-
-  // ---- process cursor: the segment of sequence b from list block x0 to seg_end ----
-  int sb = 0, eb = 0, x0 = 0, seg_end = 0, n = 0, fbp = 0, lo_hi = 0, nb_q = -1;
-  u32x4 q[NQK], q_next[NQK];
-  floatx4 acc[NDD];
-  float m = kNegInf, l = 0.0f;
   auto load_q = [&](u32x4* dst, int bq) {
     const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)bq * a.num_heads + h) * D;
 #pragma unroll
@@ -1296,47 +1249,129 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
       dst[kk] = head_ok ? *reinterpret_cast<const u32x4*>(qh + d0) : u32x4{0, 0, 0, 0};
     }
   };
-  // set up the segment of sequence b starting at list block x; its query is
-  // already in q.  The next segment's query is requested now.
-  auto begin = [&](int x) {
-    sb = start_of(b);
-    eb = start_of(b + 1);
-    x0 = x;
-    seg_end = eb < xb ? eb : xb;
-    n = seq_len(b);
-    fbp = first_visible_block(n, 1, win);
-    lo_hi = win > 0 ? max(0, n - win) : 0;
-    if (x == sb && g == 0 && lane == 0) {
-      // the chunk holding a sequence's first block records which chunks hold it
-      a.ws_seginfo[2 * b] = c;
-      a.ws_seginfo[2 * b + 1] = (int)(((int64_t)(eb - 1) * W) / total) - c + 1;
+
+  // ---- process cursor: block xp of the segment of sequence b, [x0, seg_end),
+  // in the range ending at xbp with chunk id c ----
+  int b = seq_holding(seq_start, a.batch, xa);
+  int xp = xa, xbp = xb_main, c = w * (KP + 1);
+  // (row0: the table index of list block 0 in sequence b, so list block x
+  // holds rows (row0 + x) * 16 ..)
+  int seg_end = 0, n = 0, row0 = 0, lo_hi = 0, nb_q = -1;
+  u32x4 q[NQK], q_next[NQK];
+  floatx4 acc[NDD];
+  float m = kNegInf, l = 0.0f;
+  // Wave-uniform flags, one word (scalar registers are the scarce resource here).
+  // The next range [na, nb) with id nc (its first block in sequence nbf) is
+  // named by the prefetch cursor's ticket, entered by that cursor (F_NEXT
+  // cleared, F_PEND set), then by the process cursor (F_PEND cleared); a new
+  // ticket is read only after both, so the two cursors share these registers.
+  constexpr int F_MORE = 1;   // a pool piece may still come
+  constexpr int F_REQ = 2;    // a ticket request is in flight
+  constexpr int F_NEXT = 4;   // the range after the prefetch cursor's is known
+  constexpr int F_PEND = 8;   // the prefetch cursor has entered a range the process cursor has not
+  constexpr int F_LAST = 16;  // the process cursor's segment is its range's last
+  constexpr int F_WHOLE = 32; // the segment is its sequence's whole list
+  int flags = KP != 0 ? F_MORE : 0;
+  int na = 0, nb = 0, nc = 0, nbf = 0;
+
+  // The chunk holding a sequence's first block records which chunks hold the
+  // sequence (for the merge): done for a whole range when it is taken, one
+  // sequence per lane.
+  auto record_range = [&](int ra, int rb, int cc) {
+    if (g != 0) return;
+    int b0 = seq_holding(seq_start, a.batch, ra);
+    if (start_of(b0) < ra) ++b0;               // it began in an earlier chunk
+    for (int bb = b0 + lane; bb < a.batch; bb += 64) {
+      const int s0 = seq_start[bb], s1 = seq_start[bb + 1];
+      if (s0 >= rb) break;
+      if (s1 > s0) {
+        a.ws_seginfo[2 * bb] = cc;
+        a.ws_seginfo[2 * bb + 1] = geo.chunk_of_block(s1 - 1) - cc + 1;
+      }
     }
+  };
+
+  // ---- prefetch cursor: list block xf of sequence bf, in a range ending at xbf ----
+  int xf = xa, xbf = xb_main, bf = b, ebf = start_of(b + 1);
+  const_i32_kptr rowf = row_of(b, seq_len(b));
+  int ph_last = 0;
+  int left = 0;                                // blocks named by the prefetch cursor, not yet processed
+  int ticket = 0;                              // lane 0: the requested ticket
+
+  // set up the segment of sequence b starting at list block x; its query is
+  // already in q.  The next segment's query (or the next range's first) is
+  // requested now when known.
+  auto begin = [&](int x) {
+    const int sb = start_of(b), eb = start_of(b + 1);
+    seg_end = eb < xbp ? eb : xbp;
+    flags = (x == sb && seg_end == eb) ? (flags | F_WHOLE) : (flags & ~F_WHOLE);
+    n = seq_len(b);
+    row0 = first_visible_block(n, 1, win) - sb;
+    lo_hi = win > 0 ? max(0, n - win) : 0;
 #pragma unroll
     for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
     m = kNegInf;
     l = 0.0f;
-    nb_q = -1;
-    if (seg_end < xb) {
+    // the query needed after this segment: the next segment's, or the next
+    // range's first when that range is known
+    bool want;
+    if (seg_end < xbp) {
+      flags &= ~F_LAST;
       nb_q = next_seq(b, seg_end);
-      load_q(q_next, nb_q);
+      want = true;
+    } else {
+      flags |= F_LAST;
+      nb_q = nbf;
+      want = POOL && (flags & F_PEND);
     }
+    if (want) load_q(q_next, nb_q);
   };
   // after the segment's last block: write it out, move to the next segment
   auto finish = [&]() {
     const float lt = sum_over_row_groups(l);
     if (head_ok) {
-      if (x0 == sb && seg_end == eb) write_out<KV, D>(a, b, h, r, acc, lt);
+      if (flags & F_WHOLE) write_out<KV, D>(a, b, h, r, acc, lt);
       else write_partial<D>(a, (int64_t)h * slots + b + c, r, acc, m, lt);
     }
-    if (seg_end < xb) {
-      b = nb_q;
-#pragma unroll
-      for (int kk = 0; kk < NQK; ++kk) q[kk] = q_next[kk];
-      begin(seg_end);
+    if (flags & F_LAST) {
+      if (!POOL || !(flags & F_PEND)) return;  // the wave's last range is done
+      flags &= ~F_PEND;                        // on to the next range
+      nb_q = nbf;
+      xp = na;
+      xbp = nb;
+      c = nc;
     }
+    b = nb_q;
+#pragma unroll
+    for (int kk = 0; kk < NQK; ++kk) q[kk] = q_next[kk];
+    begin(xp);
   };
-  auto process = [&](KvBlock<KV, D>& cur, int x) {
-    const int blk_row = (fbp + (x - sb)) * kBS;   // the block's first row
+  // physical id of the next block to fetch; past the last range's end the
+  // last one again (the L2 still holds it), so every step issues the same loads
+  auto next_phys = [&]() -> int {
+    if (POOL && xf == xbf && (flags & F_NEXT)) {  // enter the next range
+      flags = (flags & ~F_NEXT) | F_PEND;
+      xf = na;
+      xbf = nb;
+      bf = nbf;
+      ebf = start_of(bf + 1);
+      rowf = row_of(bf, seq_len(bf));
+      if (flags & F_LAST) load_q(q_next, nbf);  // the process cursor is in its range's last segment
+    }
+    if (xf < xbf) {
+      if (xf == ebf) {
+        bf = next_seq(bf, xf);
+        ebf = start_of(bf + 1);
+        rowf = row_of(bf, seq_len(bf));
+      }
+      ph_last = clamp_block(rowf[xf], a.num_blocks);
+      ++xf;
+      ++left;
+    }
+    return ph_last;
+  };
+  auto process = [&](KvBlock<KV, D>& cur) {
+    const int blk_row = (row0 + xp) * kBS;         // the block's first row
     const int t0 = blk_row + 4 * r;               // this lane's first row
     if (blk_row + kBS > n) zero_rows_past_end<KV, D>(cur, n, t0);
     float qk = a.qk_scale;
@@ -1351,12 +1386,15 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
     const u32x2* vop = is_byte_code(KV) ? conv.v : reinterpret_cast<const u32x2*>(cur.v);
     const bool edge = blk_row + kBS > n || blk_row < lo_hi;
     tile_step<KV, D>(kop, vop, q, acc, m, l, qk, vsc, edge, t0, n, lo_hi);
-    if (x + 1 == seg_end) finish();
+    ++xp;
+    --left;
+    if (xp == seg_end) finish();
   };
 
+  record_range(xa, xb_main, c);
   load_q(q, b);
   begin(xa);
-  KvBlock<KV, D> buf[PF + 1];
+  KvBlock<KV, D> buf[TURN];
   auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
     const int64_t o = (int64_t)ph * block_stride + head_off;
     load_block<KV, D>(dst, a.k + o, a.v + o, koff, voff);
@@ -1368,32 +1406,51 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
 #pragma unroll
   for (int j = 0; j < PF; ++j) fetch(buf[j], next_phys());
   int ph_next = next_phys();                  // one step ahead
-  const int cnt = xb - xa;
-  int i0 = 0;
-  for (; i0 + PF + 1 <= cnt; i0 += PF + 1) {
+  // Whole turns while TURN named blocks wait (every block a turn processes is
+  // real); fewer means the last range has been named to its end.
+  while (left >= TURN) {
+    // The prefetch cursor names blocks xf .. xf + PF in this turn.
+    if (POOL && (flags & F_REQ) && xbf - xf <= PF) {  // it reaches its range's end: the next range is needed
+      const int t = __builtin_amdgcn_readfirstlane(ticket);
+      flags &= ~F_REQ;
+      if (t < W * KP) {
+        geo.piece(t, na, nb, nc);
+        nbf = seq_holding(seq_start, a.batch, na);
+        record_range(na, nb, nc);
+        flags |= F_NEXT;
+      } else {
+        flags &= ~F_MORE;
+      }
+    }
+    // it does so in the next turn (a request is made only then, so its answer
+    // always comes in time to be used)
+    if (POOL && (flags & (F_MORE | F_REQ | F_NEXT)) == F_MORE && xbf - xf > PF && xbf - xf <= PF + TURN) {
+      if (lane == 0) ticket = atomicAdd(a.ws_ticket + g, 1);
+      flags |= F_REQ;
+    }
 #pragma unroll
-    for (int j = 0; j <= PF; ++j) {
+    for (int j = 0; j < TURN; ++j) {
       const int ph = ph_next;
       ph_next = next_phys();
-      fetch(buf[(j + PF) % (PF + 1)], ph);
-      process(buf[j], xa + i0 + j);
+      fetch(buf[(j + PF) % TURN], ph);
+      process(buf[j]);
     }
   }
+  const int rest = left;
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
-    const int i = i0 + j;
-    if (i >= cnt) break;
+    if (j >= rest) break;
     const int ph = ph_next;
     ph_next = next_phys();
-    fetch(buf[(j + PF) % (PF + 1)], ph);
-    process(buf[j], xa + i);
+    fetch(buf[(j + PF) % TURN], ph);
+    process(buf[j]);
   }
 }
 
-template <kvc_dtype KV, int D, int PF>
+template <kvc_dtype KV, int D, int PF, bool POOL>
 __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
   extern __shared__ int seq_start[];   // [batch + 1]
-  decode_stream<KV, D, PF>(a, seq_start);
+  decode_stream<KV, D, PF, POOL>(a, seq_start);
 }
 
 // grid (work items, KV heads, tile groups), waves_per_group waves each, TPW
@@ -1401,7 +1458,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
 template <kvc_dtype KV, int D, int PF, int TPW>
 __global__ __launch_bounds__(256) void extend_mfma_kernel(DecodeArgs a) {
   extern __shared__ int seq_start[];   // [batch + 1]
-  attend_mfma<KV, D, PF, true, TPW>(a, seq_start);
+  attend_extend<KV, D, PF, TPW>(a, seq_start);
 }
 
 // Merge of the MFMA kernel's partials: one work-group per (KV head,
@@ -1569,14 +1626,14 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     const int threads = ((a.group * (D / 4) + 63) / 64) * 64;   // <= 16 heads * 32 columns = 512
     if (tile_groups == 0) {
       dim3 grid(a.work_items, a.num_kv_heads);
-      // static split: one continuous ring per chunk; with the dynamic pool the
-      // segment-by-segment body, whose chunks come and go at run time
+      // the pooled walk is a variant of its own: its bookkeeping costs scalar
+      // registers the static walk needs for its loads
       if (a.pool_pieces > 0) {
-        if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<KV, 64, PF>), grid, dim3(64), scan_lds, s, a);
-        else hipLaunchKernelGGL((decode_mfma_kernel<KV, 128, PF>), grid, dim3(64), scan_lds, s, a);
+        if (D == 64) hipLaunchKernelGGL((decode_stream_kernel<KV, 64, KVC_STREAM_PF, true>), grid, dim3(64), scan_lds, s, a);
+        else hipLaunchKernelGGL((decode_stream_kernel<KV, 128, KVC_STREAM_PF, true>), grid, dim3(64), scan_lds, s, a);
       } else {
-        if (D == 64) hipLaunchKernelGGL((decode_stream_kernel<KV, 64, KVC_STREAM_PF>), grid, dim3(64), scan_lds, s, a);
-        else hipLaunchKernelGGL((decode_stream_kernel<KV, 128, KVC_STREAM_PF>), grid, dim3(64), scan_lds, s, a);
+        if (D == 64) hipLaunchKernelGGL((decode_stream_kernel<KV, 64, KVC_STREAM_PF, false>), grid, dim3(64), scan_lds, s, a);
+        else hipLaunchKernelGGL((decode_stream_kernel<KV, 128, KVC_STREAM_PF, false>), grid, dim3(64), scan_lds, s, a);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;

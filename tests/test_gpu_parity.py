@@ -123,9 +123,11 @@ def test_long_segments_cross_the_block_id_window():
 
 @pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "int8"])
 def test_dynamic_pool_pieces(kv):
-    # The MFMA kernel hands the last 1/2^shift of every wave's run out at run
-    # time in `pieces` pieces.  Cases: pieces cut across sequence boundaries,
-    # one wave taking its own pool, many waves competing for pieces, pools too
+    # The MFMA decode hands the last 1/2^shift of every wave's run out at run
+    # time in `pieces` pieces, each at least two turns of the prefetch ring
+    # long (10 blocks for 16-bit caches, 8 for one-byte codes; 346 blocks per
+    # head here).  Cases: one wave taking its own pool, several waves
+    # competing for pieces that cut across sequence boundaries, and pools too
     # small for their piece count (pool unused).  Every result matches the
     # oracle and repeats bit for bit, whichever wave took which piece.
     lens = [16 * 90 + 3, 1, 17, 16 * 41, 5, 16 * 200 - 1, 33, 16 * 7]
@@ -138,8 +140,8 @@ def test_dynamic_pool_pieces(kv):
     torch.cuda.synchronize()
     ref = oracle_decode(st, wl, values)
     check_close(to_f64(out), ref, *TOL[kv], f"{kv} static split")
-    for wi, pieces, shift in [(1, 1, 1), (3, 2, 3), (3, 8, 1), (5, 3, 2), (7, 64, 6), (16, 4, 2), (40, 2, 3),
-                              (2, 5, 4), (64, 1, 1)]:
+    for wi, pieces, shift in [(1, 1, 1), (2, 1, 1), (3, 2, 1), (3, 4, 1), (4, 2, 2), (5, 3, 1), (8, 1, 2),
+                              (16, 1, 1), (3, 2, 3), (3, 8, 1), (7, 64, 6), (40, 2, 3), (2, 5, 4), (64, 1, 1)]:
         split = dict(kernel=2, work_items=wi, pool_pieces=pieces, pool_shift=shift)
         o = gpu_decode_again(cache, wl, values, bt, cl, **split)
         check_close(to_f64(o), ref, *TOL[kv], f"{kv} work_items={wi} pieces={pieces} shift={shift}")
