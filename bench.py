@@ -234,6 +234,23 @@ def cpu_baseline_extend(wl, values, budget_s):
                       f"os.cpu_count()={os.cpu_count()}"}
 
 
+def step_percentiles(step_ev):
+    """Median and 95th percentile of single steps (events on the current
+    stream around each step of a pass after the timed one), in microseconds."""
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in step_ev)
+    p95 = us[min(len(us) - 1, int(round(0.95 * (len(us) - 1))))]
+    return {"step_us_median": round(us[len(us) // 2], 2), "step_us_p95": round(p95, 2)}
+
+
+def environment():
+    """Software and device the numbers were taken on."""
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    return {"torch": torch.__version__, "hip": torch.version.hip, "device": prop.name,
+            "arch": getattr(prop, "gcnArchName", None), "compute_units": prop.multi_processor_count,
+            "memory_gib": round(prop.total_memory / 2 ** 30, 1)}
+
+
 def calibrate_copy(dev):
     """Time the plain 2 GiB copy kernel (its known bytes scale the profiler's
     HBM byte counters)."""
@@ -295,6 +312,7 @@ def run_extend(args):
                                                          args.tiles_per_wave)),
                      dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in ev:
         a.record()
         b.record()
@@ -315,7 +333,14 @@ def run_extend(args):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # per-step percentiles from a second pass, so the markers do not touch the timed region
+    for i in range(args.steps):
+        step_ev[i][0].record()
+        step()
+        step_ev[i][1].record()
+    torch.cuda.synchronize()
     split_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    step_stats = step_percentiles(step_ev)
     split_avg_ms = sum(split_ms) / len(split_ms)
     ms_per_step = wall * 1e3 / args.steps
     w = extend_work(wl)
@@ -358,6 +383,8 @@ def run_extend(args):
                    "work_items": args.work_items or "auto", "tiles_per_wave": args.tiles_per_wave or "auto",
                    "parallelism": "single GPU"},
         "roofline": roof,
+        **step_stats,
+        "env": environment(),
     }
     if args.calibrate:
         result["calibration"] = calibrate_copy(dev)
@@ -418,6 +445,8 @@ def main():
                      dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     for a, b in ev:          # materialise the events before handing them to the library
         a.record()
         b.record()
@@ -439,7 +468,14 @@ def main():
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # per-step percentiles from a second pass, so the markers do not touch the timed region
+    for i in range(args.steps):
+        step_ev[i][0].record()
+        step()
+        step_ev[i][1].record()
+    torch.cuda.synchronize()
     split_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    step_stats = step_percentiles(step_ev)
     split_avg_ms = sum(split_ms) / len(split_ms)
     ms_per_step = wall * 1e3 / args.steps
     ab = algorithmic_bytes(wl)
@@ -476,6 +512,8 @@ def main():
                      "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
                      "algorithmic_bytes_per_launch": ab["split_kernel"],
                      "traffic_source": prof[1] if prof else None},
+        **step_stats,
+        "env": environment(),
     }
     if args.calibrate:
         result["calibration"] = calibrate_copy(dev)
