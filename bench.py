@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--pool-pieces", type=int, default=0,
                    help="MFMA decode: pieces of each run handed out at run time (0 = static split, the default)")
     p.add_argument("--pool-shift", type=int, default=0, help="MFMA decode: the pool is the last 1/2^shift of a run")
+    p.add_argument("--extend-kernel", type=int, choices=[0, 2, 3], default=0,
+                   help="several-token kernel: 0 auto, 2 rows split over waves, 3 one wave per 32 columns")
     p.add_argument("--tiles-per-wave", type=int, default=0,
                    help="--extend: 16-column tiles each wave holds (1..4, 0 auto)")
     p.add_argument("--kv", choices=["f32", "f16", "bf16", "fp8", "int8"], default=None,
@@ -309,7 +311,7 @@ def run_extend(args):
     out = torch.empty_like(q)
     ws = torch.empty(max(256, kvc.extend_workspace_bytes(wl.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
                                                          wl.max_query_len, wl.max_context_len, args.work_items,
-                                                         args.tiles_per_wave)),
+                                                         args.tiles_per_wave, args.extend_kernel)),
                      dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -320,7 +322,8 @@ def run_extend(args):
     def step(events=None):
         cache.append(seqs, k_new, v_new, n_new=n_new)
         cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws,
-                     work_items=args.work_items, split_events=events, tiles_per_wave=args.tiles_per_wave)
+                     work_items=args.work_items, split_events=events, tiles_per_wave=args.tiles_per_wave,
+                     kernel=args.extend_kernel)
         for s_, L in zip(seqs, hist_len):
             cache.truncate(s_, L)
 
@@ -354,7 +357,8 @@ def run_extend(args):
         achieved = w["bytes"] / (split_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    prof = profiled_traffic(workload_key(args)) if not args.work_items and not args.tiles_per_wave else None
+    prof = (profiled_traffic(workload_key(args))
+            if not args.work_items and not args.tiles_per_wave and not args.extend_kernel else None)
     roof.update({"traffic": prof[0] if prof else None, "traffic_source": prof[1] if prof else None,
                  "kernel": "multi-token split-K kernel", "avg_launch_us": round(split_avg_ms * 1e3, 2),
                  "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
@@ -380,6 +384,7 @@ def run_extend(args):
         "config": {"workload": wl.name, "extend": args.extend, "batch": wl.batch, "num_heads": wl.num_heads,
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "new_tokens": wl.total_queries, "rows_attended": int(wl.attend_lens.sum()), "kv_bytes": w["kv"],
+                   "kernel": {0: "auto", 2: "rows split over waves", 3: "one wave per 32 columns"}[args.extend_kernel],
                    "work_items": args.work_items or "auto", "tiles_per_wave": args.tiles_per_wave or "auto",
                    "parallelism": "single GPU"},
         "roofline": roof,

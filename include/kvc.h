@@ -307,10 +307,15 @@ kvc_status kvc_decode_attention(kvc_cache* cache, int32_t layer, const void* q, 
  *                ql_b new ones (what kvc_export_tables writes after the append);
  *                ql_b <= context_lens[b]
  *  out:          device [total_query][num_heads][head_dim], q_dtype
- *  workspace:    device, kvc_extend_workspace_bytes() bytes
- *  opts:         NULL, or kernel 0 / 2, work_items (waves per KV head and
- *                column-tile group), window and tiles_per_wave; the other
- *                fields are ignored
+ *  workspace:    device, kvc_extend_workspace_bytes() bytes (may be NULL when
+ *                that is 0)
+ *  opts:         NULL, or kernel: 0 = auto (3 when max_query_len >= 64, else
+ *                2); 2 = each KV head's rows split over waves, partials merged
+ *                (needs the workspace; work_items = waves per KV head and
+ *                column-tile group, tiles_per_wave = 16-column tiles per wave);
+ *                3 = one wave per 32 (token, head) columns over every row they
+ *                see, outputs written directly (no workspace: 0 bytes).  window
+ *                applies to both; the other fields are ignored
  * Other arguments and checks as for kvc_decode_attention; an f32 cache gives
  * KVC_E_UNSUPPORTED (the kernel runs on matrix cores).  Device-side values are
  * clamped as for decode; ql_b is cut to min(max_query_len, context_lens[b]) and

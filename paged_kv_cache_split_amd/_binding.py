@@ -179,8 +179,8 @@ def decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context
 
 
 def extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len, max_context_len, work_items=0,
-                           tiles_per_wave=0) -> int:
-    opts = KvcDecodeOpts(0, 0, work_items, 0, 0, None, None, 0, tiles_per_wave)
+                           tiles_per_wave=0, kernel=0) -> int:
+    opts = KvcDecodeOpts(0, kernel, work_items, 0, 0, None, None, 0, tiles_per_wave)
     return _lib.kvc_extend_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_query_len, max_context_len,
                                            ctypes.byref(opts))
 
@@ -356,10 +356,13 @@ class KVCache:
         return out
 
     def extend(self, q, query_start, max_query_len, block_table, context_lens, max_context_len, scale, layer=0,
-               out=None, workspace=None, work_items=0, split_events=None, stream=None, window=0, tiles_per_wave=0):
+               out=None, workspace=None, work_items=0, split_events=None, stream=None, window=0, tiles_per_wave=0,
+               kernel=0):
         """Attention of several new tokens per sequence (causal among them) for
         one layer.  q: [total_query, Hq, D] device tensor; query_start: device
-        int32 [B + 1] (rows of sequence b are query_start[b] .. query_start[b+1]-1)."""
+        int32 [B + 1] (rows of sequence b are query_start[b] .. query_start[b+1]-1).
+        ``kernel``: 0 auto, 2 rows split over waves and merged, 3 one wave per
+        32 (token, head) columns over all their rows."""
         import torch
         T, Hq, D = q.shape
         B = int(context_lens.shape[0])
@@ -367,7 +370,7 @@ class KVCache:
             raise ValueError("q must be contiguous")
         if query_start.dtype != torch.int32 or query_start.numel() != B + 1:
             raise ValueError("query_start must be int32 with batch + 1 entries")
-        opts = KvcDecodeOpts(0, 0, int(work_items), 0, 0, None, None, int(window), int(tiles_per_wave))
+        opts = KvcDecodeOpts(0, int(kernel), int(work_items), 0, 0, None, None, int(window), int(tiles_per_wave))
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event

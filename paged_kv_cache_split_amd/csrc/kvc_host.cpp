@@ -283,6 +283,8 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
   if (opts && opts->work_items < 0) return false;
   if (opts && (opts->pool_shift < 0 || opts->pool_shift > 6 || opts->pool_pieces > 64)) return false;
   plan->kernel = kernel;
+  plan->split_steps = 0;
+  plan->max_pieces = 1;
   plan->partition_tokens = pt;
   plan->num_partitions = std::max(1, (max_context_len + pt - 1) / pt);
   const int32_t waves = kv < 0 ? std::max(kvc::kDefaultWaves16, kvc::kDefaultWavesFp8)
@@ -315,21 +317,59 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
 constexpr int64_t kExtendRowBudget = 1 << 16;
 constexpr int64_t kExtendCUs = 256;   // fixed (not queried), so results do not depend on the device
 constexpr int32_t kMaxQueryTokens = 4096;
+// From this many new tokens in a sequence on, several-token calls take the
+// kernel without a row split by default (enough column tiles to fill the chip).
+constexpr int32_t kFlashMinQueryTokens = 64;
+// Cutting its rows: about this many waves in all, pieces of at least this many
+// steps (two blocks each), at most this many pieces per column tile.
+constexpr int64_t kFlashWaves = 8192;
+constexpr int64_t kFlashMinSteps = 4;
+constexpr int64_t kFlashMaxPieces = 64;
 
 bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t max_q, int32_t max_context_len,
                  int kv, const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
-  if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2) || opts->window < 0 ||
-               opts->tiles_per_wave < 0 || opts->tiles_per_wave > 4))
+  if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2 && opts->kernel != 3) ||
+               opts->window < 0 || opts->tiles_per_wave < 0 || opts->tiles_per_wave > 4))
     return false;
   if (max_q < 1 || max_q > kMaxQueryTokens) return false;
   plan->window = opts ? opts->window : 0;
   const int32_t G = num_heads / num_kv_heads;
   const int32_t tiles = (max_q * G + 15) / 16;
-  plan->kernel = 2;
   plan->partition_tokens = 0;
   plan->num_partitions = 1;
   plan->pool_pieces = 0;
   plan->pool_shift = kvc::kDefaultPoolShift;
+  plan->max_q = max_q;
+  plan->kernel = (opts && opts->kernel != 0) ? opts->kernel : (max_q >= kFlashMinQueryTokens ? 3 : 2);
+  plan->split_steps = 0;
+  plan->max_pieces = 1;
+  if (plan->kernel == 3) {
+    // one wave per 32 (token, head) columns, every row its columns see; tile
+    // groups on grid.z (work_items and tiles_per_wave do not apply)
+    plan->tiles_per_wave = 1;
+    plan->waves_per_group = 1;
+    plan->tile_groups = (max_q * G + 31) / 32;
+    plan->work_items = 1;
+    // Too few tiles to fill the chip (a single prompt): each tile's steps of
+    // two blocks are cut into pieces, so the waves holding the causal
+    // diagonal's far end do not run alone; about kFlashWaves waves in all.
+    const int64_t tiles = (int64_t)batch * num_kv_heads * plan->tile_groups;
+    const int64_t max_steps = ((int64_t)(max_context_len + 15) / 16 + 1) / 2 + 1;
+    if (tiles < kFlashWaves / 2 && max_steps > kFlashMinSteps) {
+      int64_t S = std::max<int64_t>(kFlashMinSteps, (max_steps * tiles + kFlashWaves - 1) / kFlashWaves);
+      int64_t pieces = (max_steps + S - 1) / S;
+      const int64_t cap = std::min<int64_t>(kFlashMaxPieces, 65535 / plan->tile_groups);
+      if (pieces > cap) {
+        S = (max_steps + cap - 1) / cap;
+        pieces = (max_steps + S - 1) / S;
+      }
+      if (pieces > 1) {
+        plan->split_steps = (int32_t)S;
+        plan->max_pieces = (int32_t)pieces;
+      }
+    }
+    return true;
+  }
   // A wave walks the union of its tiles' block ranges.  When the new tokens
   // are most of what is attended (a prompt with little or no cached history),
   // those ranges differ tile to tile along the causal diagonal, so one tile
@@ -343,7 +383,6 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   const int32_t wave_slots = (tiles + plan->tiles_per_wave - 1) / plan->tiles_per_wave;
   plan->waves_per_group = std::min(4, wave_slots);
   plan->tile_groups = (wave_slots + plan->waves_per_group - 1) / plan->waves_per_group;
-  plan->max_q = max_q;
   (void)kv;
   const int64_t groups_per_round = (int64_t)kExtendCUs * std::max(1, 4 / plan->waves_per_group);
   const int64_t rounds = plan->waves_per_group == 1 ? 1 : 2;   // one tile: shaped like decode, one round
@@ -804,9 +843,9 @@ kvc_status kvc_extend_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   kvc::DecodePlan plan;
   if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len,
                    std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size), (int)kv, opts, &plan))
-    return fail(KVC_E_INVALID, "opts: kernel must be 0 or 2, work_items >= 0, window >= 0");
+    return fail(KVC_E_INVALID, "opts: kernel must be 0, 2 or 3, work_items >= 0, window >= 0");
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
-  if (!workspace || workspace_bytes < need)
+  if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   hipError_t e = kvc::launch_decode(c->pool(), layer, plan, q, q_dtype, query_start, total_query, block_table,
                                     max_blocks_per_seq, context_lens, max_context_len, batch, num_heads, scale, out,

@@ -55,7 +55,7 @@ __host__ __device__ inline int64_t tile_bytes(const PoolDesc& p) {
 }
 
 struct DecodePlan {
-  int32_t kernel;            // 1 = FMA, 2 = MFMA
+  int32_t kernel;            // 1 = FMA, 2 = MFMA split-K, 3 = several tokens without a row split
   // FMA kernel: fixed partitions
   int32_t partition_tokens;
   int32_t num_partitions;    // ceil(max_context_len / partition_tokens)
@@ -77,13 +77,19 @@ struct DecodePlan {
   // sliding window (both kernels): a token sees at most `window` rows ending
   // at its own; 0 = the whole history
   int32_t window;
+  // several tokens without a row split over waves (kernel 3): each 32-column
+  // tile's steps (two blocks each) are cut into pieces of split_steps steps
+  // when there are too few tiles to fill the chip (0 = no cut), at most
+  // max_pieces per tile; partial rows [batch * max_q][Hq][max_pieces]
+  int32_t split_steps;
+  int32_t max_pieces;
   int64_t chunk_slots() const { return (int64_t)work_items * (pool_pieces + 1); }
   int64_t query_slots() const { return tile_groups ? max_q : 1; }
 };
 
-// Dynamic pool: off unless asked for (each piece restarts the prefetch ring,
-// which costs about what the balance gains); the pool is the last eighth of
-// each wave's run unless pool_shift says otherwise.
+// Dynamic pool: off unless asked for (on MI355X the balance it brings gains
+// next to nothing); the pool is the last eighth of each wave's run unless
+// pool_shift says otherwise.
 constexpr int32_t kDefaultPoolShift = 3;
 
 // Default number of waves per launch of the MFMA kernel: one per SIMD of a
@@ -112,7 +118,10 @@ inline WorkspaceLayout workspace_layout(const DecodePlan& p, int32_t batch, int3
                                         int32_t head_dim) {
   WorkspaceLayout w{0, 0, 0, 0, 0, 0};
   size_t rows;
-  if (p.kernel == 1) {
+  if (p.kernel == 3) {
+    if (p.max_pieces <= 1) return w;   // every tile in one piece: outputs only
+    rows = (size_t)batch * p.max_q * num_heads * p.max_pieces;
+  } else if (p.kernel == 1) {
     if (p.num_partitions <= 1) return w;
     rows = (size_t)batch * num_heads * p.num_partitions;
   } else {

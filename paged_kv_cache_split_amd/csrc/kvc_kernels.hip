@@ -368,6 +368,10 @@ struct DecodeArgs {
   int32_t total_q;          // rows of q and out
   int32_t waves_per_group;  // waves per work-group, one column tile each
   int32_t window;           // sliding window: a token sees at most this many rows ending at its own (0 = all)
+  // several tokens, one wave per 32 columns: steps per piece of a tile's rows
+  // (0 = the whole range in one piece) and pieces per tile bound
+  int32_t split_steps;
+  int32_t max_pieces;
 };
 
 template <kvc_dtype QT>
@@ -1461,6 +1465,423 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(DecodeArgs a) {
   attend_extend<KV, D, PF, TPW>(a, seq_start);
 }
 
+// ---------------------------------------------------------------------------
+// Several query tokens per sequence, many of them (a prompt, a long chunk):
+// one wave per 32 (token, head) columns of one sequence and KV head.  The wave
+// walks every row its columns see, 32 rows (two blocks) per step, on 32x32x16
+// matrix-core tiles, and writes its columns' outputs itself: a long run of new
+// tokens has enough column tiles to fill the chip without splitting the rows.
+//
+// Scores: S^T[32 rows x 32 columns] = K[32 rows x D] . Q^T[D x 32 columns].
+// Operand and result layouts of the 32x32x16 step: lane l holds A[l % 32][8
+// (l / 32) + i] and B[8 (l / 32) + i][l % 32] (i = 0..7), and result element
+// 4 g + j of lane l is C[8 g + 4 (l / 32) + j][l % 32].  The rows of a block
+// enter S^T in the order rho(r) = r with bits 2 and 3 swapped, so lane l's
+// results for block s (g = 2 s, 2 s + 1) are its column's weights for tokens
+// 8 (l / 32) .. 8 (l / 32) + 7 of block s in order: exactly the P^T operand of
+// O^T[D x 32] += V^T[D x 16] . P^T[16 x 32] for that block, whose V^T operand
+// is then those 8 tokens of one dim of the transposed V tile, one load.
+// ---------------------------------------------------------------------------
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+template <kvc_dtype KV>
+__device__ __forceinline__ floatx16 mfma32(const u32x4& a, const u32x4& b, floatx16 c) {
+  if constexpr (KV == KVC_F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                   0);
+}
+
+// eight one-byte codes -> eight bf16 (unit scale)
+template <kvc_dtype KV>
+__device__ __forceinline__ u32x4 codes8_to_bf16(const u32x2& w) {
+  return u32x4{code2_to_bf16x2<KV, false>(w[0]), code2_to_bf16x2<KV, true>(w[0]), code2_to_bf16x2<KV, false>(w[1]),
+               code2_to_bf16x2<KV, true>(w[1])};
+}
+
+// Raw tiles of one step, as loaded: K (D/16 k-steps) and V^T (D/32 dim tiles x
+// 2 blocks); 16 bytes per piece for 16-bit caches, 8 for one-byte codes.
+template <kvc_dtype KV, int D>
+struct FlashK {
+  typename std::conditional<is_byte_code(KV), u32x2, u32x4>::type k[D / 16];
+  float ks0, ks1;   // one-byte codes: the two blocks' K scales
+};
+template <kvc_dtype KV, int D>
+struct FlashV {
+  typename std::conditional<is_byte_code(KV), u32x2, u32x4>::type v[D / 32][2];
+  float vs0, vs1;   // one-byte codes: the two blocks' V scales
+};
+
+// The rows column tile ct (32 columns) of a sequence walks: table blocks
+// [jb0, jb1), two per step; n_lo / n_hi the fewest / most rows one of its
+// columns sees, lo_lo / lo_hi the lowest / highest window start.
+struct FlashTile {
+  int n_lo, n_hi, lo_lo, lo_hi, jb0, jb1, nsteps;
+};
+__device__ __forceinline__ FlashTile flash_tile(int n, int ql, int G, int win, int ct) {
+  FlashTile t;
+  const int tok_first = (ct * 32) / G;
+  const int tok_last = min(ql - 1, (ct * 32 + 31) / G);
+  t.n_lo = n - ql + 1 + tok_first;
+  t.n_hi = n - ql + 1 + tok_last;
+  t.lo_lo = win > 0 ? max(0, t.n_lo - win) : 0;
+  t.lo_hi = win > 0 ? max(0, t.n_hi - win) : 0;
+  t.jb0 = t.lo_lo / kBS;
+  t.jb1 = (t.n_hi + kBS - 1) / kBS;
+  t.nsteps = (t.jb1 - t.jb0 + 1) >> 1;
+  return t;
+}
+
+// pieces of a tile of nsteps steps (one when its rows are not cut)
+__device__ __forceinline__ int flash_pieces(int nsteps, int split_steps) {
+  return split_steps > 0 ? (nsteps + split_steps - 1) / split_steps : 1;
+}
+
+template <kvc_dtype KV, int D>
+__global__ __launch_bounds__(64) void extend_flash_kernel(DecodeArgs a) {
+  constexpr int NK = D / 16;   // k-steps of the score product
+  constexpr int NO = D / 32;   // 32-dim tiles of the output
+  constexpr int EB = is_byte_code(KV) ? 1 : 2;   // bytes per stored element
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int half = lane >> 5, c32 = lane & 31;
+  const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
+  if (n <= 0) return;
+  const int ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
+  const int G = a.group;
+  const int ntiles = (ql * G + 31) / 32;
+  // grid.z = (tile rank, piece); rank 0 is every sequence's last tile: under
+  // the causal mask the last tokens see the most rows, so the longest waves
+  // start first
+  const int rank = (int)blockIdx.z / a.max_pieces, piece = (int)blockIdx.z - rank * a.max_pieces;
+  const int ct = ntiles - 1 - rank;
+  if (ct < 0) return;
+  const int q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
+  // this lane's column: token tok, head hh of the group
+  const int col = ct * 32 + c32;
+  const int tok = col / G, hh = col - tok * G;
+  const int q_row = q0 + tok;
+  const bool col_ok = tok < ql && q_row >= 0 && q_row < a.total_q;
+  const int h = g * G + hh;
+  const int win = a.window;
+  // rows the column sees: [col_lo, ncol) (a padding column sees all n rows)
+  const int ncol = col_ok ? n - ql + 1 + tok : n;
+  const int col_lo = win > 0 ? max(0, ncol - win) : 0;
+  // the wave's rows: the first column sees the fewest, the last the most
+  const FlashTile tile = flash_tile(n, ql, G, win, ct);
+  const int n_lo = tile.n_lo, lo_hi = tile.lo_hi, jb0 = tile.jb0, jb1 = tile.jb1, nsteps = tile.nsteps;
+  // this piece's steps [s_begin, s_end)
+  const int npieces = flash_pieces(nsteps, a.split_steps);
+  if (piece >= npieces) return;
+  const int s_begin = npieces > 1 ? piece * a.split_steps : 0;
+  const int s_end = npieces > 1 ? min(nsteps, s_begin + a.split_steps) : nsteps;
+
+  const int64_t head_off = (int64_t)g * a.tile_bytes;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
+  const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks);
+  // the K row this lane loads: block c32 / 16 of the step, token rho(c32 % 16)
+  const int kr = c32 & 15;
+  const int ktok = (kr & 3) | ((kr & 4) << 1) | ((kr & 8) >> 1);
+  const int kblk = c32 >> 4;
+
+  // Q^T operand: dims 16 kk + 8 half .. + 7 of the lane's column
+  u32x4 qv[NK];
+  {
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((int64_t)q_row * a.num_heads + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      qv[kk] = col_ok ? *reinterpret_cast<const u32x4*>(qh + 16 * kk + 8 * half) : u32x4{0, 0, 0, 0};
+  }
+
+  auto phys = [&](int j) -> int {   // table block j, or block jb0 past the end (its rows are all masked)
+    return clamp_block(row[j < jb1 ? j : jb0], a.num_blocks);
+  };
+  // Block ids of a step, read one step before its tiles are requested: scalar
+  // loads complete out of order, so their first use waits for every scalar
+  // load in flight, and a use right after the read would stall the wave.
+  struct Ids {
+    int p0, p1;
+  };
+  auto ids_of = [&](int st) -> Ids {
+    st = st < s_end ? st : s_end - 1;
+    return Ids{phys(jb0 + 2 * st), phys(jb0 + 2 * st + 1)};
+  };
+  auto load_k = [&](FlashK<KV, D>& dst, const Ids& id) {
+    const int p0 = id.p0, p1 = id.p1;
+    const char* base = a.k + (int64_t)(kblk ? p1 : p0) * block_stride + head_off;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      if constexpr (is_byte_code(KV)) {
+        // [D/16][16 tokens][16 codes]: codes 8 half .. of dims 16 kk ..
+        dst.k[kk] = *reinterpret_cast<const u32x2*>(base + ((kk * kBS + ktok) * 16 + 8 * half));
+      } else {
+        // [D/8][16 tokens][8 elements]: dim group 2 kk + half
+        dst.k[kk] = *reinterpret_cast<const u32x4*>(base + (((2 * kk + half) * kBS + ktok) * 8) * EB);
+      }
+    }
+    if constexpr (is_byte_code(KV)) {
+      dst.ks0 = ((const_f32_kptr)a.k_scale)[(int64_t)p0 * a.num_kv_heads + g];
+      dst.ks1 = ((const_f32_kptr)a.k_scale)[(int64_t)p1 * a.num_kv_heads + g];
+    }
+  };
+  auto load_v = [&](FlashV<KV, D>& dst, const Ids& id) {
+    const int p[2] = {id.p0, id.p1};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const char* base = a.v + (int64_t)p[s2] * block_stride + head_off;
+#pragma unroll
+      for (int od = 0; od < NO; ++od) {
+        // [D][16 tokens]: tokens 8 half .. 8 half + 7 of dim 32 od + c32
+        const int64_t off = ((int64_t)(32 * od + c32) * kBS + 8 * half) * EB;
+        if constexpr (is_byte_code(KV)) dst.v[od][s2] = *reinterpret_cast<const u32x2*>(base + off);
+        else dst.v[od][s2] = *reinterpret_cast<const u32x4*>(base + off);
+      }
+    }
+    if constexpr (is_byte_code(KV)) {
+      dst.vs0 = ((const_f32_kptr)a.v_scale)[(int64_t)p[0] * a.num_kv_heads + g];
+      dst.vs1 = ((const_f32_kptr)a.v_scale)[(int64_t)p[1] * a.num_kv_heads + g];
+    }
+  };
+
+  floatx16 acc[NO];
+#pragma unroll
+  for (int od = 0; od < NO; ++od)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[od][e] = 0.0f;
+  float m = kNegInf, l = 0.0f;
+
+  // one step: scores from kb, softmax, PV with vb.  K of step st + 1 is
+  // already in flight; V of step st + 1 is requested once the scores are done.
+  // EDGE (compile time): the step holds rows some column must not see (near
+  // the causal edge, the window's start or the sequence's end); every other
+  // step is a plain one with no per-element tests.
+  auto step = [&](auto edge_c, const FlashK<KV, D>& kb, FlashV<KV, D>& vb, FlashV<KV, D>& vnext, int st,
+                  const Ids& idn) {
+    constexpr bool EDGE = decltype(edge_c)::value;
+    floatx16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      u32x4 kop;
+      if constexpr (is_byte_code(KV)) kop = codes8_to_bf16<KV>(kb.k[kk]);
+      else kop = kb.k[kk];
+      s = mfma32<KV>(kop, qv[kk], s);
+    }
+    load_v(vnext, idn);
+    const int k0 = (jb0 + 2 * st) * kBS;             // the step's first row
+    // rows the column sees (EDGE only); raw scores of the others are -inf
+    bool vis[16];
+    if constexpr (EDGE) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int gi = e >> 2;
+        const int key = k0 + 16 * (gi >> 1) + 8 * half + 4 * (gi & 1) + (e & 3);
+        vis[e] = key < ncol && key >= col_lo;
+        if (!vis[e]) s[e] = kNegInf;
+      }
+    }
+    // Scale per block (softmax scale * log2 e, times the K scale for one-byte
+    // codes): both are >= 0, so a block's max of the raw scores, scaled, is its
+    // max of the scaled scores, and exp2(s * qk - m) is one fma.
+    float qk0 = a.qk_scale, qk1 = a.qk_scale;
+    if constexpr (is_byte_code(KV)) {
+      qk0 *= kb.ks0;
+      qk1 *= kb.ks1;
+    }
+    float m0 = s[0], m1 = s[8];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      m0 = fmaxf(m0, s[e]);
+      m1 = fmaxf(m1, s[8 + e]);
+    }
+    // (-inf * 0 is NaN: fmaxf keeps the other operand, and a column with no
+    // visible row in the step keeps its reference)
+    float mx = fmaxf(m0 * qk0, m1 * qk1);
+    {
+      const uint32_t xb = __float_as_uint(mx);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+      mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+    }
+    const bool grow = mx > m + kRescaleThreshold;
+    if (__any(grow)) {
+      const float mnew = grow ? mx : m;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
+      l *= alpha;
+#pragma unroll
+      for (int od = 0; od < NO; ++od) acc[od] *= alpha;
+      m = mnew;
+    }
+    float pv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], e < 8 ? qk0 : qk1, -m));
+      if constexpr (EDGE) {
+        if (!vis[e]) pv[e] = 0.0f;
+      }
+    }
+    l += (((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]))) +
+         (((pv[8] + pv[9]) + (pv[10] + pv[11])) + ((pv[12] + pv[13]) + (pv[14] + pv[15])));
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w[i] = pv[8 * s2 + i];
+        if constexpr (is_byte_code(KV)) w[i] *= (s2 == 0 ? vb.vs0 : vb.vs1);
+      }
+      // P^T operand as a 16-bit hi part plus a 16-bit lo part
+      u32x4 pb, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (KV == KVC_F16) {
+          pb[i] = pack_f16x2(w[2 * i], w[2 * i + 1]);
+          pl[i] = pack_f16x2(w[2 * i] - f16_lo(pb[i]), w[2 * i + 1] - f16_hi(pb[i]));
+        } else {
+          pb[i] = pack_bf16x2(w[2 * i], w[2 * i + 1]);
+          pl[i] = pack_bf16x2(w[2 * i] - bf16_lo(pb[i]), w[2 * i + 1] - bf16_hi(pb[i]));
+        }
+      }
+      const int t0 = k0 + kBS * s2 + 8 * half;   // this lane's first row of the block
+#pragma unroll
+      for (int od = 0; od < NO; ++od) {
+        u32x4 vop;
+        if constexpr (is_byte_code(KV)) vop = codes8_to_bf16<KV>(vb.v[od][s2]);
+        else vop = vb.v[od][s2];
+        if constexpr (EDGE) {
+          // rows past the sequence's end may hold anything (NaN included):
+          // zero their values, since weight 0 times NaN would still be NaN
+          if (t0 + 8 > n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t keep_lo = (t0 + 2 * i < n) ? 0xFFFFu : 0u;
+              const uint32_t keep_hi = (t0 + 2 * i + 1 < n) ? 0xFFFF0000u : 0u;
+              vop[i] &= keep_lo | keep_hi;
+            }
+          }
+        }
+        acc[od] = mfma32<KV>(vop, pb, acc[od]);
+        acc[od] = mfma32<KV>(vop, pl, acc[od]);
+      }
+    }
+  };
+  // a step is plain when every column sees every row of it
+  auto run_step = [&](const FlashK<KV, D>& kb, FlashV<KV, D>& vb, FlashV<KV, D>& vnext, int st, const Ids& idn) {
+    const int k0 = (jb0 + 2 * st) * kBS;
+    if (k0 + 2 * kBS > n_lo || k0 < lo_hi) step(std::true_type{}, kb, vb, vnext, st, idn);
+    else step(std::false_type{}, kb, vb, vnext, st, idn);
+  };
+
+  if (s_end > s_begin) {
+    FlashK<KV, D> kbuf[2];
+    FlashV<KV, D> vbuf[2];
+    {
+      const Ids id0 = ids_of(s_begin);
+      load_k(kbuf[0], id0);
+      load_v(vbuf[0], id0);
+    }
+    Ids idn = ids_of(s_begin + 1);   // step st + 1 (past the end: the last step again)
+    int st = s_begin;
+    for (; st + 2 <= s_end; st += 2) {
+      load_k(kbuf[1], idn);
+      const Ids id2 = ids_of(st + 2);
+      run_step(kbuf[0], vbuf[0], vbuf[1], st, idn);
+      idn = id2;
+      load_k(kbuf[0], idn);
+      const Ids id3 = ids_of(st + 3);
+      run_step(kbuf[1], vbuf[1], vbuf[0], st + 1, idn);
+      idn = id3;
+    }
+    if (st < s_end) run_step(kbuf[0], vbuf[0], vbuf[1], st, idn);
+  }
+
+  // the column's sum over both halves of the wave, then its outputs
+  float lt;
+  {
+    const uint32_t xb = __float_as_uint(l);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+    lt = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+  }
+  if (!col_ok) return;
+  if (npieces > 1) {
+    // this piece's partial (m, l, acc) of the column, merged by
+    // merge_flash_kernel (the partial rows cover batch * max_q query rows; a
+    // malformed query_start may name more, which are left unwritten)
+    if ((int64_t)q_row >= (int64_t)a.batch * a.max_q) return;
+    const int64_t rr = ((int64_t)q_row * a.num_heads + h) * a.max_pieces + piece;
+#pragma unroll
+    for (int od = 0; od < NO; ++od)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+        *reinterpret_cast<floatx4*>(a.ws_acc + rr * D + 32 * od + 8 * gi + 4 * half) =
+            floatx4{acc[od][4 * gi], acc[od][4 * gi + 1], acc[od][4 * gi + 2], acc[od][4 * gi + 3]};
+    if (half == 0) {
+      a.ws_m[rr] = m;
+      a.ws_l[rr] = lt;
+    }
+    return;
+  }
+  const float inv = 1.0f / lt;
+#pragma unroll
+  for (int od = 0; od < NO; ++od)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int64_t o = ((int64_t)q_row * a.num_heads + h) * D + 32 * od + 8 * gi + 4 * half;
+      u32x2 wv;
+      if constexpr (KV == KVC_F16) {
+        wv[0] = pack_f16x2(acc[od][4 * gi] * inv, acc[od][4 * gi + 1] * inv);
+        wv[1] = pack_f16x2(acc[od][4 * gi + 2] * inv, acc[od][4 * gi + 3] * inv);
+      } else {
+        wv[0] = pack_bf16x2(acc[od][4 * gi] * inv, acc[od][4 * gi + 1] * inv);
+        wv[1] = pack_bf16x2(acc[od][4 * gi + 2] * inv, acc[od][4 * gi + 3] * inv);
+      }
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
+    }
+}
+
+// Merge of the pieces of the several-token kernel's cut tiles: one
+// work-group per (KV head, sequence, query token), one thread per (query head
+// of the group, 4 output dims); columns whose tile was not cut were written
+// by the kernel itself.  A piece whose rows the column does not see left an
+// empty partial (m = -inf, l = 0), skipped.
+template <kvc_dtype QT, int D>
+__global__ __launch_bounds__(512) void merge_flash_kernel(DecodeArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y, tok = blockIdx.z;
+  constexpr int COLS = D / 4;
+  const int hh = threadIdx.x / COLS, c = threadIdx.x % COLS;
+  const int G = a.group;
+  if (hh >= G) return;
+  const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
+  if (n <= 0) return;
+  const int ql = query_len(a, b, n);
+  if (tok >= ql) return;
+  const int q_row = a.q_start[b] + tok;
+  if (q_row < 0 || q_row >= a.total_q || (int64_t)q_row >= (int64_t)a.batch * a.max_q) return;
+  const FlashTile tile = flash_tile(n, ql, G, a.window, (tok * G + hh) / 32);
+  const int np = flash_pieces(tile.nsteps, a.split_steps);
+  if (np <= 1) return;
+  const int h = g * G + hh;
+  const int64_t row0 = ((int64_t)q_row * a.num_heads + h) * a.max_pieces;
+  float M = kNegInf, L = 0.0f;
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < np; ++p) {
+    const float m = a.ws_m[row0 + p];
+    if (m == kNegInf) continue;
+    const float l = a.ws_l[row0 + p];
+    const floatx4 v = *reinterpret_cast<const floatx4*>(a.ws_acc + (row0 + p) * D + 4 * c);
+    const float Mn = fmaxf(M, m);
+    const float sa = __builtin_amdgcn_exp2f(M - Mn), sb = __builtin_amdgcn_exp2f(m - Mn);
+    acc = acc * sa + v * sb;
+    L = L * sa + l * sb;
+    M = Mn;
+  }
+  const float inv = 1.0f / L;
+  const int64_t o = ((int64_t)q_row * a.num_heads + h) * D + 4 * c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, acc[e] * inv);
+}
+
 // Merge of the MFMA kernel's partials: one work-group per (KV head,
 // sequence[, query token]), one thread per (query head of the group, 4 output
 // dims).  The triples of chunks c_first .. c_first + np - 1 (slots b + c) are
@@ -1613,6 +2034,22 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     return e;
   }
   if constexpr (KV != KVC_F32) {
+    if (kernel == 3) {   // several tokens, one wave per 32 columns (and piece of their rows)
+      if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+      dim3 grid(a.num_kv_heads, a.batch, tile_groups * a.max_pieces);
+      if (D == 64) hipLaunchKernelGGL((extend_flash_kernel<KV, 64>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((extend_flash_kernel<KV, 128>), grid, dim3(64), 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+      if (a.max_pieces > 1) {
+        const int threads = ((a.group * (D / 4) + 63) / 64) * 64;
+        dim3 mgrid(a.num_kv_heads, a.batch, a.max_q);
+        if (D == 64) hipLaunchKernelGGL((merge_flash_kernel<QT, 64>), mgrid, dim3(threads), 0, s, a);
+        else hipLaunchKernelGGL((merge_flash_kernel<QT, 128>), mgrid, dim3(threads), 0, s, a);
+        e = hipGetLastError();
+      }
+      return e;
+    }
     constexpr int PF = is_byte_code(KV) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_16;  // blocks in flight per wave
     // the continuous ring holds the next segment's query too
     constexpr int KVC_STREAM_PF = is_byte_code(KV) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_STREAM16;
@@ -1769,6 +2206,8 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   a.total_q = plan.tile_groups ? total_q : batch;
   a.waves_per_group = plan.tile_groups ? plan.waves_per_group : 1;
   a.window = plan.window;
+  a.split_steps = plan.split_steps;
+  a.max_pieces = plan.max_pieces;
   const bool merge = plan.kernel == 2 || plan.num_partitions > 1;
   const WorkspaceLayout wl = workspace_layout(plan, batch, num_heads, pool.num_kv_heads, pool.head_dim);
   char* w = static_cast<char*>(workspace);

@@ -8,7 +8,9 @@ the oracle's ``extend_attention`` on the stored values.
 * ragged query counts (0, 1, one tile, many tiles per sequence), head
   groupings, forced splits of every sequence over many chunks (partials that
   see none of a chunk's rows), one token per sequence bitwise equal to the
-  decode kernel, and pools whose unused slots hold NaN bit patterns;
+  decode kernel, and pools whose unused slots hold NaN bit patterns; both
+  several-token kernels (rows split over waves and merged, and one wave per
+  32 columns over all their rows);
 * the three multi-token workloads at full size on sampled sequences.
 """
 import sys
@@ -51,7 +53,13 @@ def test_small_extend_workloads(kind):
     torch.cuda.synchronize()
     _check_pools(cache, st, wl)
     assert np.array_equal(cl.cpu().numpy(), wl.attend_lens)
-    check_close(to_f64(out), oracle_extend(st, wl, values), *TOL, f"extend {kind}")
+    ref = oracle_extend(st, wl, values)
+    check_close(to_f64(out), ref, *TOL, f"extend {kind}")
+    q = values["q"].cuda().contiguous()
+    for kernel in (2, 3):
+        o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, kernel=kernel)
+        torch.cuda.synchronize()
+        check_close(to_f64(o), ref, *TOL, f"extend {kind} kernel {kernel}")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "int8"])
@@ -77,9 +85,15 @@ def test_ragged_query_counts(kv, hq, hkv, d):
     q = values["q"].cuda().contiguous()
     for wi, tpw in ((2, 0), (7, 0), (64, 0), (0, 1), (5, 2), (3, 3), (9, 4)):
         o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi,
-                         tiles_per_wave=tpw)
+                         tiles_per_wave=tpw, kernel=2)
         torch.cuda.synchronize()
         check_close(to_f64(o), ref, *TOL, f"ragged {hq}/{hkv} D{d} {kv} work_items {wi} tiles/wave {tpw}")
+    # one wave per 32 (token, head) columns over all their rows: tiles with
+    # padding columns, tokens of one column tile in several sequences' worth of
+    # heads, an odd number of blocks
+    o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, kernel=3)
+    torch.cuda.synchronize()
+    check_close(to_f64(o), ref, *TOL, f"ragged {hq}/{hkv} D{d} {kv} kernel 3")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
@@ -122,10 +136,16 @@ def test_unwritten_slots_holding_nan(kv):
     values2 = make_values(wl2, "cpu")
     st2 = oracle_run(wl2, values2)
     cache2 = gpu_setup(wl2, values2, pool_fill=255)
-    out2, _, _, _ = gpu_extend_step(cache2, wl2, values2)
+    out2, bt2, cl2, qs2 = gpu_extend_step(cache2, wl2, values2)
     torch.cuda.synchronize()
     assert torch.isfinite(out2.float()).all()
-    check_close(to_f64(out2), oracle_extend(st2, wl2, values2), *TOL, f"nan slots extend {kv}")
+    ref2 = oracle_extend(st2, wl2, values2)
+    check_close(to_f64(out2), ref2, *TOL, f"nan slots extend {kv}")
+    o3 = cache2.extend(values2["q"].cuda().contiguous(), qs2, wl2.max_query_len, bt2, cl2, wl2.max_context_len,
+                       wl2.scale, kernel=3)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o3.float()).all(), "kernel 3: NaN from unused slots"
+    check_close(to_f64(o3), ref2, *TOL, f"nan slots extend {kv} kernel 3")
 
 
 def _oracle_single(wl, values, b):

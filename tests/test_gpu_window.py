@@ -78,9 +78,12 @@ def test_window_several_new_tokens(kv):
     q = values["q"].cuda().contiguous()
     for wi, tpw in ((2, 0), (9, 0), (4, 1), (3, 2), (6, 3)):
         o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi,
-                         window=wl.window, tiles_per_wave=tpw)
+                         window=wl.window, tiles_per_wave=tpw, kernel=2)
         torch.cuda.synchronize()
         check_close(to_f64(o), ref, *TOL, f"window extend {kv} work_items {wi}")
+    o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, window=wl.window, kernel=3)
+    torch.cuda.synchronize()
+    check_close(to_f64(o), ref, *TOL, f"window extend {kv} kernel 3")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])

@@ -239,3 +239,23 @@ def test_workspace_sizes():
     # out-of-range pool options are rejected (size 0)
     assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, kernel=2, pool_shift=7) == 0
     assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, kernel=2, pool_pieces=65) == 0
+
+
+def test_extend_workspace_sizes():
+    # rows split over waves: one set of partial rows per query-token index
+    split = kvc.extend_workspace_bytes(4, 8, 2, 64, 40, 300, work_items=10, kernel=2)
+    assert split >= 40 * 8 * (4 + 10) * (64 + 2) * 4
+    # one wave per 32 columns over all their rows: with enough column tiles to
+    # fill the chip (64 x 8 x 128 here), outputs only, no workspace
+    assert kvc.extend_workspace_bytes(64, 64, 8, 128, 512, 4096, kernel=3) == 0
+    # few tiles (4 x 2 x 5): each tile's steps of two blocks (at most 11 for
+    # 300 rows) are cut into pieces of 4 steps, 3 partial rows per (token, head)
+    cut = kvc.extend_workspace_bytes(4, 8, 2, 64, 40, 300, kernel=3)
+    assert cut >= 4 * 40 * 8 * 3 * (64 + 2) * 4
+    # auto: the row split below 64 new tokens per sequence, the column kernel from 64 on
+    assert kvc.extend_workspace_bytes(4, 8, 2, 64, 40, 300) == kvc.extend_workspace_bytes(4, 8, 2, 64, 40, 300, kernel=2)
+    assert kvc.extend_workspace_bytes(64, 64, 8, 128, 512, 4096) == 0
+    # unknown kernels and out-of-range query counts are rejected (size 0)
+    assert kvc.extend_workspace_bytes(4, 8, 2, 64, 40, 300, kernel=1) == 0
+    assert kvc.extend_workspace_bytes(4, 8, 2, 64, 40, 300, kernel=4) == 0
+    assert kvc.extend_workspace_bytes(4, 8, 2, 64, 4097, 5000, kernel=2) == 0
