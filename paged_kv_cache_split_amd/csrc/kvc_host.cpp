@@ -325,6 +325,7 @@ constexpr int32_t kFlashMinQueryTokens = 64;
 constexpr int64_t kFlashWaves = 8192;
 constexpr int64_t kFlashMinSteps = 4;
 constexpr int64_t kFlashMaxPieces = 64;
+constexpr int32_t kFlashWavesPerGroup = 4;   // column tiles (waves) per work-group
 
 bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t max_q, int32_t max_context_len,
                  int kv, const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
@@ -344,19 +345,20 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   plan->split_steps = 0;
   plan->max_pieces = 1;
   if (plan->kernel == 3) {
-    // one wave per 32 (token, head) columns, every row its columns see; tile
-    // groups on grid.z (work_items and tiles_per_wave do not apply)
+    // one wave per 32 (token, head) columns, every row its columns see, four
+    // column tiles per work-group sharing the K/V steps; groups of tiles on
+    // grid.z (work_items and tiles_per_wave do not apply)
     plan->tiles_per_wave = 1;
-    plan->waves_per_group = 1;
-    plan->tile_groups = (max_q * G + 31) / 32;
+    plan->waves_per_group = kFlashWavesPerGroup;
+    plan->tile_groups = ((max_q * G + 31) / 32 + kFlashWavesPerGroup - 1) / kFlashWavesPerGroup;
     plan->work_items = 1;
-    // Too few tiles to fill the chip (a single prompt): each tile's steps of
-    // two blocks are cut into pieces, so the waves holding the causal
+    // Too few tiles to fill the chip (a single prompt): each group's steps of
+    // two blocks are cut into pieces, so the groups holding the causal
     // diagonal's far end do not run alone; about kFlashWaves waves in all.
-    const int64_t tiles = (int64_t)batch * num_kv_heads * plan->tile_groups;
+    const int64_t waves = (int64_t)batch * num_kv_heads * plan->tile_groups * kFlashWavesPerGroup;
     const int64_t max_steps = ((int64_t)(max_context_len + 15) / 16 + 1) / 2 + 1;
-    if (tiles < kFlashWaves / 2 && max_steps > kFlashMinSteps) {
-      int64_t S = std::max<int64_t>(kFlashMinSteps, (max_steps * tiles + kFlashWaves - 1) / kFlashWaves);
+    if (waves < kFlashWaves / 2 && max_steps > kFlashMinSteps) {
+      int64_t S = std::max<int64_t>(kFlashMinSteps, (max_steps * waves + kFlashWaves - 1) / kFlashWaves);
       int64_t pieces = (max_steps + S - 1) / S;
       const int64_t cap = std::min<int64_t>(kFlashMaxPieces, 65535 / plan->tile_groups);
       if (pieces > cap) {

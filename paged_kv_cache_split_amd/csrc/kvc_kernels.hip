@@ -1467,10 +1467,12 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Several query tokens per sequence, many of them (a prompt, a long chunk):
-// one wave per 32 (token, head) columns of one sequence and KV head.  The wave
-// walks every row its columns see, 32 rows (two blocks) per step, on 32x32x16
-// matrix-core tiles, and writes its columns' outputs itself: a long run of new
-// tokens has enough column tiles to fill the chip without splitting the rows.
+// one wave per 32 (token, head) columns of one sequence and KV head, WT waves
+// (consecutive column tiles) per work-group sharing every K/V step through
+// LDS.  The work-group walks every row its columns see, 32 rows (two blocks)
+// per step, on 32x32x16 matrix-core tiles, and writes the outputs itself: a
+// long run of new tokens has enough column tiles to fill the chip without
+// splitting the rows (with too few, each group's steps are cut into pieces).
 //
 // Scores: S^T[32 rows x 32 columns] = K[32 rows x D] . Q^T[D x 32 columns].
 // Operand and result layouts of the 32x32x16 step: lane l holds A[l % 32][8
@@ -1513,16 +1515,17 @@ struct FlashV {
   float vs0, vs1;   // one-byte codes: the two blocks' V scales
 };
 
-// The rows column tile ct (32 columns) of a sequence walks: table blocks
-// [jb0, jb1), two per step; n_lo / n_hi the fewest / most rows one of its
-// columns sees, lo_lo / lo_hi the lowest / highest window start.
+// The rows that columns ct * cols .. ct * cols + cols - 1 of a sequence see
+// (a 32-column tile, or a work-group's tiles): table blocks [jb0, jb1), two
+// per step; n_lo / n_hi the fewest / most rows one of the columns sees, lo_lo /
+// lo_hi the lowest / highest window start.
 struct FlashTile {
   int n_lo, n_hi, lo_lo, lo_hi, jb0, jb1, nsteps;
 };
-__device__ __forceinline__ FlashTile flash_tile(int n, int ql, int G, int win, int ct) {
+__device__ __forceinline__ FlashTile flash_tile(int n, int ql, int G, int win, int ct, int cols) {
   FlashTile t;
-  const int tok_first = (ct * 32) / G;
-  const int tok_last = min(ql - 1, (ct * 32 + 31) / G);
+  const int tok_first = (ct * cols) / G;
+  const int tok_last = min(ql - 1, (ct * cols + cols - 1) / G);
   t.n_lo = n - ql + 1 + tok_first;
   t.n_hi = n - ql + 1 + tok_last;
   t.lo_lo = win > 0 ? max(0, t.n_lo - win) : 0;
@@ -1538,52 +1541,67 @@ __device__ __forceinline__ int flash_pieces(int nsteps, int split_steps) {
   return split_steps > 0 ? (nsteps + split_steps - 1) / split_steps : 1;
 }
 
-template <kvc_dtype KV, int D>
-__global__ __launch_bounds__(64) void extend_flash_kernel(DecodeArgs a) {
-  constexpr int NK = D / 16;   // k-steps of the score product
-  constexpr int NO = D / 32;   // 32-dim tiles of the output
-  constexpr int EB = is_byte_code(KV) ? 1 : 2;   // bytes per stored element
+template <kvc_dtype KV, int D, int WT>
+__global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
+  constexpr int NK = D / 16;                  // k-steps of the score product
+  constexpr int NO = D / 32;                  // 32-dim tiles of the output
+  constexpr int NT = 64 * WT;                 // threads of the work-group
+  // One step's tiles in LDS, as 16-bit values (one-byte codes converted on the
+  // way in).  K: 32 rows (in score-tile order) x D, V^T: D rows x 32 tokens.
+  // Rows are padded by 16 bytes so the 16-byte operand reads of 8 consecutive
+  // lanes (8 consecutive rows) fall in 8 distinct groups of 4 banks.
+  constexpr int KROW = 2 * D + 16, VROW = 2 * 32 + 16;
+  constexpr int KBYTES = 32 * KROW, STAGE = KBYTES + D * VROW;
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+  // global pieces of one step: 16 bytes each, both blocks, K then V
+  constexpr int CHB = is_byte_code(KV) ? D : 2 * D;   // 16-byte pieces per (block, head) tile
+  constexpr int PER = 2 * 2 * CHB / NT;               // per thread (K and V, two blocks)
+  static_assert(2 * 2 * CHB % NT == 0, "pieces per thread");
+
   const int g = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, c32 = lane & 31;
   const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
   if (n <= 0) return;
   const int ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
   const int G = a.group;
+  const int win = a.window;
   const int ntiles = (ql * G + 31) / 32;
-  // grid.z = (tile rank, piece); rank 0 is every sequence's last tile: under
-  // the causal mask the last tokens see the most rows, so the longest waves
-  // start first
+  const int ngroups = (ntiles + WT - 1) / WT;
+  // grid.z = (group rank, piece); rank 0 is every sequence's last group of
+  // tiles: under the causal mask the last tokens see the most rows, so the
+  // longest work-groups start first
   const int rank = (int)blockIdx.z / a.max_pieces, piece = (int)blockIdx.z - rank * a.max_pieces;
-  const int ct = ntiles - 1 - rank;
-  if (ct < 0) return;
+  const int cg = ngroups - 1 - rank;
+  if (cg < 0) return;
+  // the rows the group walks: the union of its tiles' rows
+  const FlashTile grp = flash_tile(n, ql, G, win, cg, 32 * WT);
+  const int npieces = flash_pieces(grp.nsteps, a.split_steps);
+  if (piece >= npieces) return;
+  const int jb0 = grp.jb0, jb1 = grp.jb1;
+  const int s_begin = npieces > 1 ? piece * a.split_steps : 0;
+  const int s_end = npieces > 1 ? min(grp.nsteps, s_begin + a.split_steps) : grp.nsteps;
   const int q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
-  // this lane's column: token tok, head hh of the group
+
+  // this wave's tile and this lane's column: token tok, head hh of the group
+  const int ct = cg * WT + wave;
+  const bool tile_ok = ct < ntiles;
   const int col = ct * 32 + c32;
   const int tok = col / G, hh = col - tok * G;
   const int q_row = q0 + tok;
-  const bool col_ok = tok < ql && q_row >= 0 && q_row < a.total_q;
+  const bool col_ok = tile_ok && tok < ql && q_row >= 0 && q_row < a.total_q;
   const int h = g * G + hh;
-  const int win = a.window;
   // rows the column sees: [col_lo, ncol) (a padding column sees all n rows)
   const int ncol = col_ok ? n - ql + 1 + tok : n;
   const int col_lo = win > 0 ? max(0, ncol - win) : 0;
-  // the wave's rows: the first column sees the fewest, the last the most
-  const FlashTile tile = flash_tile(n, ql, G, win, ct);
-  const int n_lo = tile.n_lo, lo_hi = tile.lo_hi, jb0 = tile.jb0, jb1 = tile.jb1, nsteps = tile.nsteps;
-  // this piece's steps [s_begin, s_end)
-  const int npieces = flash_pieces(nsteps, a.split_steps);
-  if (piece >= npieces) return;
-  const int s_begin = npieces > 1 ? piece * a.split_steps : 0;
-  const int s_end = npieces > 1 ? min(nsteps, s_begin + a.split_steps) : nsteps;
+  // the wave's own rows: steps outside them are skipped, steps inside them
+  // with no masked row run the plain body
+  const FlashTile own = flash_tile(n, ql, G, win, tile_ok ? ct : cg * WT, 32);
+  const int w_lo = own.lo_lo, w_hi = own.n_hi, n_lo = own.n_lo, lo_hi = own.lo_hi;
 
   const int64_t head_off = (int64_t)g * a.tile_bytes;
   const int64_t block_stride = (int64_t)a.num_kv_heads * a.tile_bytes;
   const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks);
-  // the K row this lane loads: block c32 / 16 of the step, token rho(c32 % 16)
-  const int kr = c32 & 15;
-  const int ktok = (kr & 3) | ((kr & 4) << 1) | ((kr & 8) >> 1);
-  const int kblk = c32 >> 4;
 
   // Q^T operand: dims 16 kk + 8 half .. + 7 of the lane's column
   u32x4 qv[NK];
@@ -1594,53 +1612,97 @@ __global__ __launch_bounds__(64) void extend_flash_kernel(DecodeArgs a) {
       qv[kk] = col_ok ? *reinterpret_cast<const u32x4*>(qh + 16 * kk + 8 * half) : u32x4{0, 0, 0, 0};
   }
 
-  auto phys = [&](int j) -> int {   // table block j, or block jb0 past the end (its rows are all masked)
-    return clamp_block(row[j < jb1 ? j : jb0], a.num_blocks);
-  };
-  // Block ids of a step, read one step before its tiles are requested: scalar
-  // loads complete out of order, so their first use waits for every scalar
-  // load in flight, and a use right after the read would stall the wave.
+  // Block ids of a step, read a step before its tiles are requested (scalar
+  // loads complete out of order: their first use waits for all in flight).
   struct Ids {
     int p0, p1;
+  };
+  auto phys = [&](int j) -> int {   // table block j, or block jb0 past the end (its rows are all masked)
+    return clamp_block(row[j < jb1 ? j : jb0], a.num_blocks);
   };
   auto ids_of = [&](int st) -> Ids {
     st = st < s_end ? st : s_end - 1;
     return Ids{phys(jb0 + 2 * st), phys(jb0 + 2 * st + 1)};
   };
-  auto load_k = [&](FlashK<KV, D>& dst, const Ids& id) {
-    const int p0 = id.p0, p1 = id.p1;
-    const char* base = a.k + (int64_t)(kblk ? p1 : p0) * block_stride + head_off;
+  // one step's global pieces held between their load and their LDS store,
+  // with the blocks' scales for one-byte codes
+  struct Staged {
+    u32x4 w[PER];
+    float ks0, ks1, vs0, vs1;
+  };
+  auto load_stage = [&](Staged& r, const Ids& id) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      if constexpr (is_byte_code(KV)) {
-        // [D/16][16 tokens][16 codes]: codes 8 half .. of dims 16 kk ..
-        dst.k[kk] = *reinterpret_cast<const u32x2*>(base + ((kk * kBS + ktok) * 16 + 8 * half));
-      } else {
-        // [D/8][16 tokens][8 elements]: dim group 2 kk + half
-        dst.k[kk] = *reinterpret_cast<const u32x4*>(base + (((2 * kk + half) * kBS + ktok) * 8) * EB);
-      }
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * NT;                 // piece: K pieces first, then V
+      const bool is_v = c >= 2 * CHB;
+      const int cc = is_v ? c - 2 * CHB : c;
+      const int blk = cc / CHB, r16 = cc - blk * CHB;
+      const char* base = (is_v ? a.v : a.k) + (int64_t)(blk ? id.p1 : id.p0) * block_stride + head_off;
+      r.w[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)r16 * 16);
     }
     if constexpr (is_byte_code(KV)) {
-      dst.ks0 = ((const_f32_kptr)a.k_scale)[(int64_t)p0 * a.num_kv_heads + g];
-      dst.ks1 = ((const_f32_kptr)a.k_scale)[(int64_t)p1 * a.num_kv_heads + g];
+      r.ks0 = ((const_f32_kptr)a.k_scale)[(int64_t)id.p0 * a.num_kv_heads + g];
+      r.ks1 = ((const_f32_kptr)a.k_scale)[(int64_t)id.p1 * a.num_kv_heads + g];
+      r.vs0 = ((const_f32_kptr)a.v_scale)[(int64_t)id.p0 * a.num_kv_heads + g];
+      r.vs1 = ((const_f32_kptr)a.v_scale)[(int64_t)id.p1 * a.num_kv_heads + g];
     }
   };
-  auto load_v = [&](FlashV<KV, D>& dst, const Ids& id) {
-    const int p[2] = {id.p0, id.p1};
+  // Store one step's pieces into LDS buffer buf.  K row of block blk, token t
+  // goes to score row 16 blk + rho(t) (rho swaps bits 2 and 3 of t, its own
+  // inverse); V^T keeps its dims as rows.  V values of rows past the
+  // sequence's end (which may hold anything, NaN included) are zeroed: their
+  // weight is 0, and 0 times NaN would still be NaN.
+  auto store_stage = [&](const Staged& r, int buf, int k0) {
+    char* kl = lds + buf * STAGE;
+    char* vl = kl + KBYTES;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const char* base = a.v + (int64_t)p[s2] * block_stride + head_off;
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * NT;
+      const bool is_v = c >= 2 * CHB;
+      const int cc = is_v ? c - 2 * CHB : c;
+      const int blk = cc / CHB, r16 = cc - blk * CHB;
+      if constexpr (is_byte_code(KV)) {
+        // 16 codes: K [D/16][16 tokens][16 dims], V [D][16 tokens]
+        const u32x4 w = r.w[i];
+        u32x4 lo = u32x4{code2_to_bf16x2<KV, false>(w[0]), code2_to_bf16x2<KV, true>(w[0]),
+                         code2_to_bf16x2<KV, false>(w[1]), code2_to_bf16x2<KV, true>(w[1])};
+        u32x4 hi = u32x4{code2_to_bf16x2<KV, false>(w[2]), code2_to_bf16x2<KV, true>(w[2]),
+                         code2_to_bf16x2<KV, false>(w[3]), code2_to_bf16x2<KV, true>(w[3])};
+        if (!is_v) {
+          const int dg = r16 >> 4, t = r16 & 15;
+          const int rr = 16 * blk + ((t & 3) | ((t & 4) << 1) | ((t & 8) >> 1));
+          *reinterpret_cast<u32x4*>(kl + rr * KROW + dg * 32) = lo;
+          *reinterpret_cast<u32x4*>(kl + rr * KROW + dg * 32 + 16) = hi;
+        } else {
+          const int d = r16, t0 = k0 + 16 * blk;
+          if (t0 + 16 > n) {
 #pragma unroll
-      for (int od = 0; od < NO; ++od) {
-        // [D][16 tokens]: tokens 8 half .. 8 half + 7 of dim 32 od + c32
-        const int64_t off = ((int64_t)(32 * od + c32) * kBS + 8 * half) * EB;
-        if constexpr (is_byte_code(KV)) dst.v[od][s2] = *reinterpret_cast<const u32x2*>(base + off);
-        else dst.v[od][s2] = *reinterpret_cast<const u32x4*>(base + off);
+            for (int e = 0; e < 4; ++e) {
+              lo[e] &= ((t0 + 2 * e < n) ? 0xFFFFu : 0u) | ((t0 + 2 * e + 1 < n) ? 0xFFFF0000u : 0u);
+              hi[e] &= ((t0 + 8 + 2 * e < n) ? 0xFFFFu : 0u) | ((t0 + 8 + 2 * e + 1 < n) ? 0xFFFF0000u : 0u);
+            }
+          }
+          *reinterpret_cast<u32x4*>(vl + d * VROW + 32 * blk) = lo;
+          *reinterpret_cast<u32x4*>(vl + d * VROW + 32 * blk + 16) = hi;
+        }
+      } else {
+        // 8 values: K [D/8][16 tokens][8 dims], V [D][16 tokens] (two pieces per dim)
+        u32x4 w = r.w[i];
+        if (!is_v) {
+          const int dg = r16 >> 4, t = r16 & 15;
+          const int rr = 16 * blk + ((t & 3) | ((t & 4) << 1) | ((t & 8) >> 1));
+          *reinterpret_cast<u32x4*>(kl + rr * KROW + dg * 16) = w;
+        } else {
+          const int d = r16 >> 1, hv = r16 & 1;
+          const int t0 = k0 + 16 * blk + 8 * hv;
+          if (t0 + 8 > n) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              w[e] &= ((t0 + 2 * e < n) ? 0xFFFFu : 0u) | ((t0 + 2 * e + 1 < n) ? 0xFFFF0000u : 0u);
+          }
+          *reinterpret_cast<u32x4*>(vl + d * VROW + 32 * blk + 16 * hv) = w;
+        }
       }
-    }
-    if constexpr (is_byte_code(KV)) {
-      dst.vs0 = ((const_f32_kptr)a.v_scale)[(int64_t)p[0] * a.num_kv_heads + g];
-      dst.vs1 = ((const_f32_kptr)a.v_scale)[(int64_t)p[1] * a.num_kv_heads + g];
     }
   };
 
@@ -1651,27 +1713,22 @@ __global__ __launch_bounds__(64) void extend_flash_kernel(DecodeArgs a) {
     for (int e = 0; e < 16; ++e) acc[od][e] = 0.0f;
   float m = kNegInf, l = 0.0f;
 
-  // one step: scores from kb, softmax, PV with vb.  K of step st + 1 is
-  // already in flight; V of step st + 1 is requested once the scores are done.
-  // EDGE (compile time): the step holds rows some column must not see (near
-  // the causal edge, the window's start or the sequence's end); every other
-  // step is a plain one with no per-element tests.
-  auto step = [&](auto edge_c, const FlashK<KV, D>& kb, FlashV<KV, D>& vb, FlashV<KV, D>& vnext, int st,
-                  const Ids& idn) {
+  // One step of this wave: scores from the K rows in LDS, softmax, PV with the
+  // V^T rows.  EDGE (compile time): the step holds rows some column must not
+  // see (the causal edge, the window's start, the sequence's end); every
+  // other step is a plain one with no per-element tests.
+  auto step = [&](auto edge_c, int buf, int k0, const Staged& sc) {
     constexpr bool EDGE = decltype(edge_c)::value;
+    const char* kl = lds + buf * STAGE;
+    const char* vl = kl + KBYTES;
     floatx16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      u32x4 kop;
-      if constexpr (is_byte_code(KV)) kop = codes8_to_bf16<KV>(kb.k[kk]);
-      else kop = kb.k[kk];
+      const u32x4 kop = *reinterpret_cast<const u32x4*>(kl + c32 * KROW + 32 * kk + 16 * half);
       s = mfma32<KV>(kop, qv[kk], s);
     }
-    load_v(vnext, idn);
-    const int k0 = (jb0 + 2 * st) * kBS;             // the step's first row
-    // rows the column sees (EDGE only); raw scores of the others are -inf
     bool vis[16];
     if constexpr (EDGE) {
 #pragma unroll
@@ -1683,12 +1740,12 @@ __global__ __launch_bounds__(64) void extend_flash_kernel(DecodeArgs a) {
       }
     }
     // Scale per block (softmax scale * log2 e, times the K scale for one-byte
-    // codes): both are >= 0, so a block's max of the raw scores, scaled, is its
-    // max of the scaled scores, and exp2(s * qk - m) is one fma.
+    // codes): both are >= 0, so a block's max of the raw scores, scaled, is
+    // its max of the scaled scores, and exp2(s * qk - m) is one fma.
     float qk0 = a.qk_scale, qk1 = a.qk_scale;
     if constexpr (is_byte_code(KV)) {
-      qk0 *= kb.ks0;
-      qk1 *= kb.ks1;
+      qk0 *= sc.ks0;
+      qk1 *= sc.ks1;
     }
     float m0 = s[0], m1 = s[8];
 #pragma unroll
@@ -1729,7 +1786,7 @@ __global__ __launch_bounds__(64) void extend_flash_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         w[i] = pv[8 * s2 + i];
-        if constexpr (is_byte_code(KV)) w[i] *= (s2 == 0 ? vb.vs0 : vb.vs1);
+        if constexpr (is_byte_code(KV)) w[i] *= (s2 == 0 ? sc.vs0 : sc.vs1);
       }
       // P^T operand as a 16-bit hi part plus a 16-bit lo part
       u32x4 pb, pl;
@@ -1743,57 +1800,40 @@ __global__ __launch_bounds__(64) void extend_flash_kernel(DecodeArgs a) {
           pl[i] = pack_bf16x2(w[2 * i] - bf16_lo(pb[i]), w[2 * i + 1] - bf16_hi(pb[i]));
         }
       }
-      const int t0 = k0 + kBS * s2 + 8 * half;   // this lane's first row of the block
 #pragma unroll
       for (int od = 0; od < NO; ++od) {
-        u32x4 vop;
-        if constexpr (is_byte_code(KV)) vop = codes8_to_bf16<KV>(vb.v[od][s2]);
-        else vop = vb.v[od][s2];
-        if constexpr (EDGE) {
-          // rows past the sequence's end may hold anything (NaN included):
-          // zero their values, since weight 0 times NaN would still be NaN
-          if (t0 + 8 > n) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t keep_lo = (t0 + 2 * i < n) ? 0xFFFFu : 0u;
-              const uint32_t keep_hi = (t0 + 2 * i + 1 < n) ? 0xFFFF0000u : 0u;
-              vop[i] &= keep_lo | keep_hi;
-            }
-          }
-        }
+        const u32x4 vop = *reinterpret_cast<const u32x4*>(vl + (32 * od + c32) * VROW + 32 * s2 + 16 * half);
         acc[od] = mfma32<KV>(vop, pb, acc[od]);
         acc[od] = mfma32<KV>(vop, pl, acc[od]);
       }
     }
   };
-  // a step is plain when every column sees every row of it
-  auto run_step = [&](const FlashK<KV, D>& kb, FlashV<KV, D>& vb, FlashV<KV, D>& vnext, int st, const Ids& idn) {
-    const int k0 = (jb0 + 2 * st) * kBS;
-    if (k0 + 2 * kBS > n_lo || k0 < lo_hi) step(std::true_type{}, kb, vb, vnext, st, idn);
-    else step(std::false_type{}, kb, vb, vnext, st, idn);
-  };
 
   if (s_end > s_begin) {
-    FlashK<KV, D> kbuf[2];
-    FlashV<KV, D> vbuf[2];
-    {
-      const Ids id0 = ids_of(s_begin);
-      load_k(kbuf[0], id0);
-      load_v(vbuf[0], id0);
+    Staged r;
+    Ids id = ids_of(s_begin);
+    load_stage(r, id);
+    Ids idn = ids_of(s_begin + 1);
+    store_stage(r, 0, (jb0 + 2 * s_begin) * kBS);
+    Staged cur = r;   // (scales of the step being computed)
+    __syncthreads();
+    for (int st = s_begin; st < s_end; ++st) {
+      const int buf = (st - s_begin) & 1;
+      const bool more = st + 1 < s_end;
+      if (more) load_stage(r, idn);              // the next step's tiles, in flight meanwhile
+      idn = ids_of(st + 2);
+      const int k0 = (jb0 + 2 * st) * kBS;
+      // this wave's columns see some row of the step
+      if (tile_ok && k0 < w_hi && k0 + 2 * kBS > w_lo) {
+        if (k0 + 2 * kBS > n_lo || k0 < lo_hi) step(std::true_type{}, buf, k0, cur);
+        else step(std::false_type{}, buf, k0, cur);
+      }
+      if (more) {
+        store_stage(r, buf ^ 1, k0 + 2 * kBS);
+        cur = r;
+      }
+      __syncthreads();
     }
-    Ids idn = ids_of(s_begin + 1);   // step st + 1 (past the end: the last step again)
-    int st = s_begin;
-    for (; st + 2 <= s_end; st += 2) {
-      load_k(kbuf[1], idn);
-      const Ids id2 = ids_of(st + 2);
-      run_step(kbuf[0], vbuf[0], vbuf[1], st, idn);
-      idn = id2;
-      load_k(kbuf[0], idn);
-      const Ids id3 = ids_of(st + 3);
-      run_step(kbuf[1], vbuf[1], vbuf[0], st + 1, idn);
-      idn = id3;
-    }
-    if (st < s_end) run_step(kbuf[0], vbuf[0], vbuf[1], st, idn);
   }
 
   // the column's sum over both halves of the wave, then its outputs
@@ -1858,7 +1898,8 @@ __global__ __launch_bounds__(512) void merge_flash_kernel(DecodeArgs a) {
   if (tok >= ql) return;
   const int q_row = a.q_start[b] + tok;
   if (q_row < 0 || q_row >= a.total_q || (int64_t)q_row >= (int64_t)a.batch * a.max_q) return;
-  const FlashTile tile = flash_tile(n, ql, G, a.window, (tok * G + hh) / 32);
+  const int cols = 32 * a.waves_per_group;   // columns of a work-group
+  const FlashTile tile = flash_tile(n, ql, G, a.window, (tok * G + hh) / cols, cols);
   const int np = flash_pieces(tile.nsteps, a.split_steps);
   if (np <= 1) return;
   const int h = g * G + hh;
@@ -2036,9 +2077,10 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
   if constexpr (KV != KVC_F32) {
     if (kernel == 3) {   // several tokens, one wave per 32 columns (and piece of their rows)
       if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+      // tile_groups: work-groups of waves_per_group (4) column tiles per sequence and head
       dim3 grid(a.num_kv_heads, a.batch, tile_groups * a.max_pieces);
-      if (D == 64) hipLaunchKernelGGL((extend_flash_kernel<KV, 64>), grid, dim3(64), 0, s, a);
-      else hipLaunchKernelGGL((extend_flash_kernel<KV, 128>), grid, dim3(64), 0, s, a);
+      if (D == 64) hipLaunchKernelGGL((extend_flash_kernel<KV, 64, 4>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((extend_flash_kernel<KV, 128, 4>), grid, dim3(256), 0, s, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
       if (a.max_pieces > 1) {
