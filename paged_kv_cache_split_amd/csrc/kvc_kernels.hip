@@ -1541,6 +1541,19 @@ __device__ __forceinline__ int flash_pieces(int nsteps, int split_steps) {
   return split_steps > 0 ? (nsteps + split_steps - 1) / split_steps : 1;
 }
 
+// The several-token kernel's P operand: a 16-bit hi part plus a 16-bit lo
+// part (1), as in decode, or the hi part alone (0).
+#ifndef KVC_FLASH_P_LO
+#define KVC_FLASH_P_LO 1
+#endif
+
+// K piece r16 = 16 * dim group + score row of a block -> its piece in the
+// stored tile, 16 * dim group + token (the token of score row r is rho(r))
+__device__ __forceinline__ int k_piece(int r16) {
+  const int r = r16 & 15;
+  return (r16 & ~15) | (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
 template <kvc_dtype KV, int D, int WT>
 __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   constexpr int NK = D / 16;                  // k-steps of the score product
@@ -1638,7 +1651,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
       const int cc = is_v ? c - 2 * CHB : c;
       const int blk = cc / CHB, r16 = cc - blk * CHB;
       const char* base = (is_v ? a.v : a.k) + (int64_t)(blk ? id.p1 : id.p0) * block_stride + head_off;
-      r.w[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)r16 * 16);
+      r.w[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)(is_v ? r16 : k_piece(r16)) * 16);
     }
     if constexpr (is_byte_code(KV)) {
       r.ks0 = ((const_f32_kptr)a.k_scale)[(int64_t)id.p0 * a.num_kv_heads + g];
@@ -1649,7 +1662,9 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   };
   // Store one step's pieces into LDS buffer buf.  K row of block blk, token t
   // goes to score row 16 blk + rho(t) (rho swaps bits 2 and 3 of t, its own
-  // inverse); V^T keeps its dims as rows.  V values of rows past the
+  // inverse); consecutive threads take consecutive score rows (k_piece), so
+  // eight lanes' 16-byte stores land in eight distinct groups of banks.  V^T
+  // keeps its dims as rows.  V values of rows past the
   // sequence's end (which may hold anything, NaN included) are zeroed: their
   // weight is 0, and 0 times NaN would still be NaN.
   auto store_stage = [&](const Staged& r, int buf, int k0) {
@@ -1669,8 +1684,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
         u32x4 hi = u32x4{code2_to_bf16x2<KV, false>(w[2]), code2_to_bf16x2<KV, true>(w[2]),
                          code2_to_bf16x2<KV, false>(w[3]), code2_to_bf16x2<KV, true>(w[3])};
         if (!is_v) {
-          const int dg = r16 >> 4, t = r16 & 15;
-          const int rr = 16 * blk + ((t & 3) | ((t & 4) << 1) | ((t & 8) >> 1));
+          const int dg = r16 >> 4, rr = 16 * blk + (r16 & 15);
           *reinterpret_cast<u32x4*>(kl + rr * KROW + dg * 32) = lo;
           *reinterpret_cast<u32x4*>(kl + rr * KROW + dg * 32 + 16) = hi;
         } else {
@@ -1689,8 +1703,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
         // 8 values: K [D/8][16 tokens][8 dims], V [D][16 tokens] (two pieces per dim)
         u32x4 w = r.w[i];
         if (!is_v) {
-          const int dg = r16 >> 4, t = r16 & 15;
-          const int rr = 16 * blk + ((t & 3) | ((t & 4) << 1) | ((t & 8) >> 1));
+          const int dg = r16 >> 4, rr = 16 * blk + (r16 & 15);
           *reinterpret_cast<u32x4*>(kl + rr * KROW + dg * 16) = w;
         } else {
           const int d = r16 >> 1, hv = r16 & 1;
@@ -1788,23 +1801,23 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
         w[i] = pv[8 * s2 + i];
         if constexpr (is_byte_code(KV)) w[i] *= (s2 == 0 ? sc.vs0 : sc.vs1);
       }
-      // P^T operand as a 16-bit hi part plus a 16-bit lo part
+      // P^T operand as a 16-bit hi part plus (KVC_FLASH_P_LO) a 16-bit lo part
       u32x4 pb, pl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (KV == KVC_F16) {
           pb[i] = pack_f16x2(w[2 * i], w[2 * i + 1]);
-          pl[i] = pack_f16x2(w[2 * i] - f16_lo(pb[i]), w[2 * i + 1] - f16_hi(pb[i]));
+          if constexpr (KVC_FLASH_P_LO) pl[i] = pack_f16x2(w[2 * i] - f16_lo(pb[i]), w[2 * i + 1] - f16_hi(pb[i]));
         } else {
           pb[i] = pack_bf16x2(w[2 * i], w[2 * i + 1]);
-          pl[i] = pack_bf16x2(w[2 * i] - bf16_lo(pb[i]), w[2 * i + 1] - bf16_hi(pb[i]));
+          if constexpr (KVC_FLASH_P_LO) pl[i] = pack_bf16x2(w[2 * i] - bf16_lo(pb[i]), w[2 * i + 1] - bf16_hi(pb[i]));
         }
       }
 #pragma unroll
       for (int od = 0; od < NO; ++od) {
         const u32x4 vop = *reinterpret_cast<const u32x4*>(vl + (32 * od + c32) * VROW + 32 * s2 + 16 * half);
         acc[od] = mfma32<KV>(vop, pb, acc[od]);
-        acc[od] = mfma32<KV>(vop, pl, acc[od]);
+        if constexpr (KVC_FLASH_P_LO) acc[od] = mfma32<KV>(vop, pl, acc[od]);
       }
     }
   };
