@@ -1893,18 +1893,28 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
     }
 }
 
-// Merge of the pieces of the several-token kernel's cut tiles: one
-// work-group per (KV head, sequence, query token), one thread per (query head
-// of the group, 4 output dims); columns whose tile was not cut were written
-// by the kernel itself.  A piece whose rows the column does not see left an
-// empty partial (m = -inf, l = 0), skipped.
+// Merge of the pieces of the several-token kernel's cut tiles: one thread per
+// (query token, query head of the group, 4 output dims), merge_tokens(G, D)
+// tokens of one sequence and KV head per work-group; columns whose tile was
+// not cut were written by the kernel itself.  A piece whose rows the column
+// does not see left an empty partial (m = -inf, l = 0), skipped.
+__host__ __device__ __forceinline__ int merge_tokens(int G, int D) {
+  const int per = G * (D / 4);   // threads per query token (<= 512)
+  return 512 / per;
+}
+
 template <kvc_dtype QT, int D>
 __global__ __launch_bounds__(512) void merge_flash_kernel(DecodeArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y, tok = blockIdx.z;
+  const int g = blockIdx.x, b = blockIdx.y;
   constexpr int COLS = D / 4;
-  const int hh = threadIdx.x / COLS, c = threadIdx.x % COLS;
   const int G = a.group;
-  if (hh >= G) return;
+  const int per = G * COLS;
+  const int mt = merge_tokens(G, D);
+  if ((int)threadIdx.x >= mt * per) return;   // (threads rounded up to whole waves)
+  const int tok = (int)blockIdx.z * mt + (int)threadIdx.x / per;
+  const int rem = (int)threadIdx.x % per;
+  const int hh = rem / COLS, c = rem % COLS;
+  if (tok >= a.max_q) return;
   const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
   if (n <= 0) return;
   const int ql = query_len(a, b, n);
@@ -2097,8 +2107,9 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
       if (a.max_pieces > 1) {
-        const int threads = ((a.group * (D / 4) + 63) / 64) * 64;
-        dim3 mgrid(a.num_kv_heads, a.batch, a.max_q);
+        const int mt = merge_tokens(a.group, D);
+        const int threads = ((mt * a.group * (D / 4) + 63) / 64) * 64;
+        dim3 mgrid(a.num_kv_heads, a.batch, (a.max_q + mt - 1) / mt);
         if (D == 64) hipLaunchKernelGGL((merge_flash_kernel<QT, 64>), mgrid, dim3(threads), 0, s, a);
         else hipLaunchKernelGGL((merge_flash_kernel<QT, 128>), mgrid, dim3(threads), 0, s, a);
         e = hipGetLastError();
