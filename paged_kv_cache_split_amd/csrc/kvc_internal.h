@@ -66,21 +66,23 @@ struct DecodePlan {
   int32_t work_items;
   int32_t pool_pieces;
   int32_t pool_shift;
-  // several query tokens per sequence (MFMA kernel only): tile_groups = 0 for
-  // decode; else the 16-column tiles of (query token, head) pairs are spread
-  // over waves_per_group waves of a work-group and tile_groups groups (grid.z),
-  // and the partial rows hold one set of slots per query token index
+  // several query tokens per sequence: tile_groups = 0 for decode.  Kernel 2:
+  // the 16-column tiles of (query token, head) pairs are spread over
+  // waves_per_group waves of a work-group and tile_groups groups (grid.z),
+  // and the partial rows hold one set of slots per query token index.  Kernel
+  // 3: waves_per_group 32-column tiles per work-group, tile_groups groups of
+  // them per sequence (grid.z, times max_pieces).
   int32_t tile_groups;
   int32_t waves_per_group;
-  int32_t tiles_per_wave;    // column tiles each wave holds (1..4), reusing every K/V block it loads
+  int32_t tiles_per_wave;    // kernel 2: column tiles each wave holds (1..4), reusing every K/V block it loads
   int32_t max_q;
-  // sliding window (both kernels): a token sees at most `window` rows ending
+  // sliding window (every kernel): a token sees at most `window` rows ending
   // at its own; 0 = the whole history
   int32_t window;
-  // several tokens without a row split over waves (kernel 3): each 32-column
-  // tile's steps (two blocks each) are cut into pieces of split_steps steps
-  // when there are too few tiles to fill the chip (0 = no cut), at most
-  // max_pieces per tile; partial rows [batch * max_q][Hq][max_pieces]
+  // kernel 3: each group's steps (two blocks each) are cut into pieces of
+  // split_steps steps when there are too few groups to fill the chip (0 = no
+  // cut), at most max_pieces per group; partial rows
+  // [batch * max_q][Hq][max_pieces]
   int32_t split_steps;
   int32_t max_pieces;
   int64_t chunk_slots() const { return (int64_t)work_items * (pool_pieces + 1); }
