@@ -239,7 +239,8 @@ kvc_status kvc_export_tables(kvc_cache* cache, int32_t batch, const int64_t* seq
 typedef struct kvc_decode_opts {
   int32_t partition_tokens; /* FMA kernel: tokens per partition (multiple of 16, <= 1024); 0 = chosen from the shape */
   int32_t kernel;           /* 0 = auto, 1 = fp32 FMA (VALU) kernel, 2 = MFMA kernel (16-bit and fp8 KV) */
-  int32_t work_items;       /* MFMA kernel: waves per KV head; 0 = max(1, 1024 / num_kv_heads) */
+  int32_t work_items;       /* MFMA kernel: waves per KV head; 0 = max(1, W / num_kv_heads) with W = 1024
+                               (16-bit and fp8 caches) or 2048 (int8) */
   int32_t pool_pieces;      /* MFMA kernel: pieces per run handed out at run time, <= 64; <= 0 = none
                                (static split, the default); unused when a piece would hold fewer than
                                two turns of the wave's prefetch ring (8 blocks for one-byte codes, 10

@@ -287,8 +287,7 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
   plan->max_pieces = 1;
   plan->partition_tokens = pt;
   plan->num_partitions = std::max(1, (max_context_len + pt - 1) / pt);
-  const int32_t waves = kv < 0 ? std::max(kvc::kDefaultWaves16, kvc::kDefaultWavesFp8)
-                               : kvc::default_waves(static_cast<kvc_dtype>(kv));
+  const int32_t waves = kv < 0 ? kvc::kMaxDefaultWaves : kvc::default_waves(static_cast<kvc_dtype>(kv));
   plan->work_items = (opts && opts->work_items > 0) ? opts->work_items
                                                     : std::max(1, waves / std::max(1, num_kv_heads));
   plan->pool_pieces = (opts && opts->pool_pieces > 0) ? opts->pool_pieces : 0;

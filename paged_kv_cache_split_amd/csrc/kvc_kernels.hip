@@ -66,6 +66,12 @@ constexpr int kBS = 16;                       // tokens per block (device work)
 #ifndef KVC_PREFETCH_STREAM16
 #define KVC_PREFETCH_STREAM16 4
 #endif
+// One-byte decode with the continuous ring: a block is half a 16-bit one, so
+// the ring holds more of them (measured on the mixed batch, 3 / 4 / 5 / 6
+// blocks: fp8 367 / 364 / 364 / 364 us, int8 412 / 406 / 405 / 396 us).
+#ifndef KVC_PREFETCH_STREAM8
+#define KVC_PREFETCH_STREAM8 6
+#endif
 // Blocks in flight for the several-token kernel with 2, 3 or 4 column tiles
 // per wave (their queries and accumulators take the registers).
 #ifndef KVC_PREFETCH_T2
@@ -2118,7 +2124,7 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     }
     constexpr int PF = is_byte_code(KV) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_16;  // blocks in flight per wave
     // the continuous ring holds the next segment's query too
-    constexpr int KVC_STREAM_PF = is_byte_code(KV) ? KVC_PREFETCH_FP8 : KVC_PREFETCH_STREAM16;
+    constexpr int KVC_STREAM_PF = is_byte_code(KV) ? KVC_PREFETCH_STREAM8 : KVC_PREFETCH_STREAM16;
     // ticket counters start at zero (a kernel, not a memset, so the sequence
     // can be captured in a graph); without a pool no wave touches them
     if (a.pool_pieces > 0 && tile_groups == 0) {
