@@ -41,6 +41,16 @@ restrict the attention range).  The pages give no formula; the plainest
 reading, taken here, is that the token at position p sees positions
 max(0, p - window + 1) .. p.
 
+``cascade_decode_attention`` is decode attention taken apart at a fork point:
+when many sequences share one prefix (requests under one system prompt share
+its physical blocks, "大模型推理加速核心KV Cache 复用机制与内存布局优化" §三;
+"苦猿的大模型日记" PART 02 reuses identical prefixes across requests), the
+prefix rows and each sequence's own rows are attended apart, each giving a
+running max, sum and weighted value sum, and the two are combined with the
+merge of partial softmax results ("大模型推理加速核心KV Cache 复用机制与内存布局
+优化" §四, merging between blocks; the recurrence of "LLM推理优化实战…" §3.2).
+Exactly (up to rounding) the same as ``decode_attention`` over all rows.
+
 ``causal_attention`` is the full-recompute definition (page 5's
 ``naive_attention`` with ``tril(diagonal = kv_len - q_len)``), written here
 without torch, used to pin ``decode_attention`` by brute force.
@@ -90,6 +100,44 @@ def decode_attention_batch(q, k_list, v_list, scale):
     out = np.empty(q.shape, dtype=np.float64)
     for b in range(q.shape[0]):
         out[b] = decode_attention(q[b], k_list[b], v_list[b], scale)
+    return out
+
+
+def _partial(scores, v):
+    """(max, sum of exp(s - max), sum of exp(s - max) * v) of one row range."""
+    m = scores.max()
+    w = np.exp(scores - m)
+    return m, w.sum(), w @ v
+
+
+def cascade_decode_attention(q, k, v, scale, prefix):
+    """Decode attention of one query token, the rows split at ``prefix``.
+
+    q: [Hq, D]; k, v: [n, Hkv, D] as for ``decode_attention``; 0 < prefix < n.
+    Rows [0, prefix) (the shared prefix) and [prefix, n) (the sequence's own
+    rows) each give a partial (m, l, acc); the output is
+    (acc_1 e^(m_1 - M) + acc_2 e^(m_2 - M)) / (l_1 e^(m_1 - M) + l_2 e^(m_2 - M)),
+    M = max(m_1, m_2).  returns: [Hq, D] fp64
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    hq, d = q.shape
+    n, hkv, _ = k.shape
+    if not 0 < prefix < n:
+        raise ValueError("need 0 < prefix < n")
+    if hq % hkv != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    group = hq // hkv
+    out = np.empty((hq, d), dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        scores = float(scale) * (k[:, g, :] @ q[h])
+        m1, l1, a1 = _partial(scores[:prefix], v[:prefix, g, :])
+        m2, l2, a2 = _partial(scores[prefix:], v[prefix:, g, :])
+        big = max(m1, m2)
+        c1, c2 = np.exp(m1 - big), np.exp(m2 - big)
+        out[h] = (a1 * c1 + a2 * c2) / (l1 * c1 + l2 * c2)
     return out
 
 

@@ -352,3 +352,58 @@ def test_planted_window_off_by_one_is_caught():
     ref = _sdpa_window(q, K, V, 0.5, 5)
     assert not np.allclose(wrong(q, K, V, 0.5, 5), ref, atol=1e-6)
     assert np.allclose(attention.extend_attention(q, K, V, 0.5, window=5), ref, atol=1e-12)
+
+
+# -- cascade (shared-prefix) decode -------------------------------------------
+
+@pytest.mark.parametrize("hq,hkv,n", [(4, 1, 40), (8, 2, 300), (32, 8, 129)])
+def test_cascade_decode_equals_decode(hq, hkv, n):
+    # the merge of the prefix's and the own rows' partials is decode attention
+    # over all rows, at every split point
+    rng = np.random.default_rng(n + hq)
+    q = rng.standard_normal((hq, 64))
+    k = rng.standard_normal((n, hkv, 64)) * 2.0
+    v = rng.standard_normal((n, hkv, 64))
+    ref = attention.decode_attention(q, k, v, 0.125)
+    for prefix in (1, 16, n // 2, n - 1):
+        got = attention.cascade_decode_attention(q, k, v, 0.125, prefix)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), prefix
+
+
+def test_cascade_split_point_matters_only_through_rows():
+    # two sequences forked from one prefix: their outputs agree with a decode
+    # over (shared prefix + own rows), and the prefix's rows enter both
+    rng = np.random.default_rng(5)
+    P, hq, hkv, d = 48, 8, 2, 32
+    kp, vp = rng.standard_normal((P, hkv, d)), rng.standard_normal((P, hkv, d))
+    for own in (1, 17, 100):
+        ko, vo = rng.standard_normal((own, hkv, d)), rng.standard_normal((own, hkv, d))
+        q = rng.standard_normal((hq, d))
+        k, v = np.concatenate([kp, ko]), np.concatenate([vp, vo])
+        got = attention.cascade_decode_attention(q, k, v, 0.2, P)
+        assert np.allclose(got, attention.decode_attention(q, k, v, 0.2), rtol=1e-12, atol=1e-12)
+        # dropping the prefix changes the answer (the prefix is really attended)
+        assert not np.allclose(got, attention.decode_attention(q, ko, vo, 0.2), atol=1e-3)
+
+
+def test_planted_unscaled_merge_is_caught():
+    # merging the two partials without rescaling to the common max is a
+    # plausible mistake; the pin against decode_attention must reject it
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((4, 16))
+    k = rng.standard_normal((60, 1, 16)) * 3.0
+    v = rng.standard_normal((60, 1, 16))
+    ref = attention.decode_attention(q, k, v, 0.5)
+    scores = 0.5 * (k[:, 0, :] @ q[0])
+    m1, l1, a1 = attention._partial(scores[:20], v[:20, 0, :])
+    m2, l2, a2 = attention._partial(scores[20:], v[20:, 0, :])
+    wrong = (a1 + a2) / (l1 + l2)
+    assert not np.allclose(wrong, ref[0], atol=1e-3)
+    assert np.allclose(attention.cascade_decode_attention(q, k, v, 0.5, 20)[0], ref[0], rtol=1e-12, atol=1e-12)
+
+
+def test_cascade_rejects_a_split_outside_the_rows():
+    q, k = np.zeros((2, 8)), np.zeros((5, 1, 8))
+    for prefix in (0, 5, 7):
+        with pytest.raises(ValueError):
+            attention.cascade_decode_attention(q, k, k, 1.0, prefix)
