@@ -251,6 +251,17 @@ typedef struct kvc_decode_opts {
   int32_t window;           /* sliding window (both kernels, decode and several tokens): the token at
                                position p sees positions max(0, p - window + 1) .. p; 0 = all of them */
   int32_t tiles_per_wave;   /* several tokens: 16-column (token, head) tiles each wave holds, 1..4; 0 = auto */
+  int32_t shared_prefix;    /* decode, MFMA kernel: 0, or P > 0, a multiple of block_size, when the first P
+                               tokens of every sequence are one shared prefix (the same block ids in every
+                               block table, as after kvc_fork of a P-token sequence) and every sequence
+                               holds more than P tokens.  The prefix is then attended once for the whole
+                               batch (its rows read by one pass, the batch's queries its columns, rows of
+                               sequence 0's table) and each sequence's own rows apart, and the partials
+                               are merged: a cascade split at the fork point, for requests that share one
+                               system prompt's physical blocks ("大模型推理加速核心KV Cache 复用机制与内存
+                               布局优化" §三; "苦猿的大模型日记 · Day45 · 大模型推理加速" PART 02).  Needs
+                               window 0 and no pool; other fields as for decode.  A batch that breaks
+                               these conditions gets meaningless outputs (nothing faults). */
 } kvc_decode_opts;
 
 /* Workspace bytes kvc_decode_attention needs for this shape (the split

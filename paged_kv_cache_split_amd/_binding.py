@@ -67,7 +67,7 @@ class KvcDecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("work_items", ctypes.c_int32),
                 ("pool_pieces", ctypes.c_int32), ("pool_shift", ctypes.c_int32),
                 ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p), ("window", ctypes.c_int32),
-                ("tiles_per_wave", ctypes.c_int32)]
+                ("tiles_per_wave", ctypes.c_int32), ("shared_prefix", ctypes.c_int32)]
 
 
 _i32, _i64, _sz, _vp, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -172,8 +172,9 @@ def scratch_bytes(max_batch, max_tokens) -> int:
 
 
 def decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len, partition_tokens=0,
-                           kernel=0, work_items=0, pool_pieces=0, pool_shift=0) -> int:
-    opts = KvcDecodeOpts(partition_tokens, kernel, work_items, pool_pieces, pool_shift, None, None, 0, 0)
+                           kernel=0, work_items=0, pool_pieces=0, pool_shift=0, shared_prefix=0) -> int:
+    opts = KvcDecodeOpts(partition_tokens, kernel, work_items, pool_pieces, pool_shift, None, None, 0, 0,
+                         shared_prefix)
     return _lib.kvc_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_context_len,
                                            ctypes.byref(opts))
 
@@ -329,15 +330,17 @@ class KVCache:
 
     def decode(self, q, block_table, context_lens, max_context_len, scale, layer=0, out=None, workspace=None,
                partition_tokens=0, kernel=0, work_items=0, pool_pieces=0, pool_shift=0, split_events=None,
-               stream=None, window=0):
+               stream=None, window=0, shared_prefix=0):
         """Decode attention for one layer.  q: [B, Hq, D] device tensor.
-        ``window`` > 0: each token sees at most that many rows ending at its own."""
+        ``window`` > 0: each token sees at most that many rows ending at its own.
+        ``shared_prefix`` > 0: the first that many tokens of every sequence are one
+        shared prefix, attended once for the batch (the cascade split)."""
         import torch
         B, Hq, D = q.shape
         if not q.is_contiguous():
             raise ValueError("q must be contiguous")
         opts = KvcDecodeOpts(int(partition_tokens), int(kernel), int(work_items), int(pool_pieces), int(pool_shift),
-                             None, None, int(window), 0)
+                             None, None, int(window), 0, int(shared_prefix))
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event

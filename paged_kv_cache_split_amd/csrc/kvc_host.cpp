@@ -285,6 +285,10 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, i
   plan->kernel = kernel;
   plan->split_steps = 0;
   plan->max_pieces = 1;
+  plan->skip_blocks = 0;
+  plan->pre_groups = 0;
+  plan->pre_split_steps = 0;
+  plan->pre_pieces = 0;
   plan->partition_tokens = pt;
   plan->num_partitions = std::max(1, (max_context_len + pt - 1) / pt);
   const int32_t waves = kv < 0 ? kvc::kMaxDefaultWaves : kvc::default_waves(static_cast<kvc_dtype>(kv));
@@ -392,6 +396,40 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   if (opts && opts->work_items > 0) w = opts->work_items;
   plan->work_items = (int32_t)std::max<int64_t>(1, w);
   return plan->chunk_slots() <= (1 << 28);
+}
+
+// Shared-prefix (cascade) decode on top of a kernel-2 decode plan: the
+// prefix's blocks are skipped by every sequence's decode list and attended
+// once by a prefix pass, the several-token kernel without the causal mask
+// over one virtual sequence (sequence 0's first prefix_tokens rows, the
+// batch's queries as its columns, four 32-column tiles per work-group), cut
+// into pieces like a prompt when its groups are too few to fill the chip.
+bool plan_shared_prefix(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t prefix_tokens,
+                        const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
+  if (plan->kernel != 2 || prefix_tokens <= 0 || prefix_tokens % kDeviceBlockSize != 0) return false;
+  if (opts && (opts->window != 0 || opts->pool_pieces > 0)) return false;
+  const int32_t G = num_heads / num_kv_heads;
+  const int64_t tiles = ((int64_t)batch * G + 31) / 32;
+  const int64_t groups = (tiles + kFlashWavesPerGroup - 1) / kFlashWavesPerGroup;
+  if (groups > 65535) return false;
+  const int64_t steps = ((int64_t)prefix_tokens / kDeviceBlockSize + 1) / 2;   // as the kernel counts them
+  const int64_t waves = (int64_t)num_kv_heads * groups * kFlashWavesPerGroup;
+  int64_t S = 0, pieces = 1;
+  if (waves < kFlashWaves / 2 && steps > kFlashMinSteps) {
+    S = std::max<int64_t>(kFlashMinSteps, (steps * waves + kFlashWaves - 1) / kFlashWaves);
+    pieces = (steps + S - 1) / S;
+    const int64_t cap = std::min<int64_t>(kFlashMaxPieces, 65535 / groups);
+    if (pieces > cap) {
+      S = (steps + cap - 1) / cap;
+      pieces = (steps + S - 1) / S;
+    }
+    if (pieces <= 1) S = 0, pieces = 1;
+  }
+  plan->skip_blocks = prefix_tokens / kDeviceBlockSize;
+  plan->pre_groups = (int32_t)groups;
+  plan->pre_split_steps = (int32_t)S;
+  plan->pre_pieces = (int32_t)pieces;
+  return true;
 }
 
 size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -730,11 +768,15 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
                                   int32_t max_context_len, const kvc_decode_opts* opts) {
   if (batch < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_context_len < 1) return 0;
   const int32_t kernel = opts ? opts->kernel : 0;
+  const int32_t prefix = opts ? opts->shared_prefix : 0;
+  if (prefix < 0 || num_heads % num_kv_heads != 0) return 0;
   size_t need = 0;
   for (int32_t k = 1; k <= 2; ++k) {
     if (kernel != 0 && kernel != k) continue;
+    if (prefix > 0 && k != 2) continue;   // the shared-prefix decode runs the MFMA kernel
     kvc::DecodePlan p;
     if (!plan_decode(batch, num_kv_heads, max_context_len, k, -1, opts, &p)) return 0;
+    if (prefix > 0 && !plan_shared_prefix(batch, num_heads, num_kv_heads, prefix, opts, &p)) return 0;
     need = std::max(need, workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, p));
   }
   return need;
@@ -802,6 +844,14 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
     return fail(KVC_E_INVALID,
                 "partition_tokens must be a multiple of 16 and at most 1024, work_items >= 0, "
                 "pool_pieces <= 64, pool_shift in 0..6, window >= 0");
+  if (opts && opts->shared_prefix != 0) {
+    const int32_t P = opts->shared_prefix;
+    if (P < 0 || !plan_shared_prefix(batch, num_heads, num_kv_heads, P, opts, &plan) ||
+        P / block_size >= max_blocks_per_seq)
+      return fail(KVC_E_INVALID,
+                  "shared_prefix must be a positive multiple of the block size below the table length, with "
+                  "the MFMA kernel, window 0 and no pool");
+  }
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);

@@ -55,36 +55,45 @@ __host__ __device__ inline int64_t tile_bytes(const PoolDesc& p) {
 }
 
 struct DecodePlan {
-  int32_t kernel;            // 1 = FMA, 2 = MFMA split-K, 3 = several tokens without a row split
+  int32_t kernel = 0;            // 1 = FMA, 2 = MFMA split-K, 3 = several tokens without a row split
   // FMA kernel: fixed partitions
-  int32_t partition_tokens;
-  int32_t num_partitions;    // ceil(max_context_len / partition_tokens)
+  int32_t partition_tokens = 0;
+  int32_t num_partitions = 0;    // ceil(max_context_len / partition_tokens)
   // MFMA kernel: even split of each KV head's blocks over work_items waves,
   // the last 1/2^pool_shift of each wave's run cut into pool_pieces pieces
   // handed out at run time (0 = static split only); partial slots per query
   // head = batch + chunk_slots()
-  int32_t work_items;
-  int32_t pool_pieces;
-  int32_t pool_shift;
+  int32_t work_items = 0;
+  int32_t pool_pieces = 0;
+  int32_t pool_shift = 0;
   // several query tokens per sequence: tile_groups = 0 for decode.  Kernel 2:
   // the 16-column tiles of (query token, head) pairs are spread over
   // waves_per_group waves of a work-group and tile_groups groups (grid.z),
   // and the partial rows hold one set of slots per query token index.  Kernel
   // 3: waves_per_group 32-column tiles per work-group, tile_groups groups of
   // them per sequence (grid.z, times max_pieces).
-  int32_t tile_groups;
-  int32_t waves_per_group;
-  int32_t tiles_per_wave;    // kernel 2: column tiles each wave holds (1..4), reusing every K/V block it loads
-  int32_t max_q;
+  int32_t tile_groups = 0;
+  int32_t waves_per_group = 0;
+  int32_t tiles_per_wave = 0;    // kernel 2: column tiles each wave holds (1..4), reusing every K/V block it loads
+  int32_t max_q = 0;
   // sliding window (every kernel): a token sees at most `window` rows ending
   // at its own; 0 = the whole history
-  int32_t window;
+  int32_t window = 0;
   // kernel 3: each group's steps (two blocks each) are cut into pieces of
   // split_steps steps when there are too few groups to fill the chip (0 = no
   // cut), at most max_pieces per group; partial rows
   // [batch * max_q][Hq][max_pieces]
-  int32_t split_steps;
-  int32_t max_pieces;
+  int32_t split_steps = 0;
+  int32_t max_pieces = 0;
+  // shared-prefix (cascade) decode, kernel 2: 0, or the prefix's blocks,
+  // which every sequence's decode list skips; the prefix pass (kernel 3
+  // without the causal mask over sequence 0's first skip_blocks blocks, the
+  // batch's queries as its columns) runs pre_groups work-groups per KV head,
+  // its steps cut into pre_pieces pieces of pre_split_steps (0: one piece)
+  int32_t skip_blocks = 0;
+  int32_t pre_groups = 0;
+  int32_t pre_split_steps = 0;
+  int32_t pre_pieces = 0;
   int64_t chunk_slots() const { return (int64_t)work_items * (pool_pieces + 1); }
   int64_t query_slots() const { return tile_groups ? max_q : 1; }
 };
@@ -117,13 +126,16 @@ inline int32_t default_waves(kvc_dtype kv) {
 // then one ticket counter per KV head (zeroed by the launch sequence).
 struct WorkspaceLayout {
   size_t acc, m, l, seginfo, tickets, bytes;
+  // shared-prefix decode: the prefix pass's partial rows [batch][Hq][pieces]
+  // and the arguments of its one virtual sequence (query_start[2], length)
+  size_t pre_acc, pre_m, pre_l, pre_args;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline WorkspaceLayout workspace_layout(const DecodePlan& p, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                         int32_t head_dim) {
-  WorkspaceLayout w{0, 0, 0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   size_t rows;
   if (p.kernel == 3) {
     if (p.max_pieces <= 1) return w;   // every tile in one piece: outputs only
@@ -142,6 +154,14 @@ inline WorkspaceLayout workspace_layout(const DecodePlan& p, int32_t batch, int3
     w.bytes = w.tickets + align256((size_t)num_kv_heads * sizeof(int32_t));
   } else {
     w.tickets = w.bytes = w.seginfo;
+  }
+  if (p.kernel == 2 && p.skip_blocks > 0) {
+    const size_t pre_rows = (size_t)batch * num_heads * p.pre_pieces;
+    w.pre_acc = w.bytes;
+    w.pre_m = w.pre_acc + align256(pre_rows * head_dim * sizeof(float));
+    w.pre_l = w.pre_m + align256(pre_rows * sizeof(float));
+    w.pre_args = w.pre_l + align256(pre_rows * sizeof(float));
+    w.bytes = w.pre_args + align256(4 * sizeof(int32_t));
   }
   return w;
 }

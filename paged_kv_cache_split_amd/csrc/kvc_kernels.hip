@@ -378,6 +378,21 @@ struct DecodeArgs {
   // (0 = the whole range in one piece) and pieces per tile bound
   int32_t split_steps;
   int32_t max_pieces;
+  // shared-prefix (cascade) decode: the decode list of every sequence starts
+  // at table block skip_blocks (the prefix is attended separately); outputs
+  // are then never written by the row pass itself (partials_only), and the
+  // merge also folds pre_pieces partial rows per (sequence, head) from
+  // pre_acc / pre_m / pre_l ([batch][Hq][pre_max_pieces]).  The prefix pass
+  // runs the several-token kernel with every column seeing all rows
+  // (noncausal).
+  int32_t skip_blocks;
+  int32_t partials_only;
+  int32_t noncausal;
+  int32_t pre_pieces;
+  int32_t pre_max_pieces;
+  const float* pre_acc;
+  const float* pre_m;
+  const float* pre_l;
 };
 
 template <kvc_dtype QT>
@@ -717,6 +732,13 @@ __device__ __forceinline__ int first_visible_block(int n, int ql, int window) {
   return (window > 0 && lo > 0) ? lo / kBS : 0;
 }
 
+// First table block of a sequence's decode list: the first the window lets
+// the new token see, and none of a shared prefix attended apart.
+__device__ __forceinline__ int decode_first_block(const DecodeArgs& a, int n) {
+  const int f = first_visible_block(n, 1, a.window);
+  return f > a.skip_blocks ? f : a.skip_blocks;
+}
+
 // Exclusive scan of the sequences' block counts into LDS: seq_start[b] is the
 // first block of sequence b in the batch's concatenated block list, and
 // seq_start[batch] the total.  Every wave of the decode and every merge
@@ -737,7 +759,8 @@ __device__ __forceinline__ int scan_block_counts(const DecodeArgs& a, int* seq_s
         ql = query_len(a, bb, n);
         if (ql == 0) nb = 0;
       }
-      if (nb > 0) nb -= first_visible_block(n, ql, a.window);
+      if (nb > 0) nb -= EXT ? first_visible_block(n, ql, a.window) : decode_first_block(a, n);
+      if (nb < 0) nb = 0;
     }
     int incl = nb;
 #pragma unroll
@@ -1239,7 +1262,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
   // Block-table row of sequence bb indexed by list position: entry x is the
   // physical block of list block x (the list starts at the first visible block).
   auto row_of = [&](int bb, int n_bb) -> const_i32_kptr {
-    return (const_i32_kptr)(a.block_table + (int64_t)bb * a.max_blocks + first_visible_block(n_bb, 1, win)) -
+    return (const_i32_kptr)(a.block_table + (int64_t)bb * a.max_blocks + decode_first_block(a, n_bb)) -
            start_of(bb);
   };
   // the first sequence after bb holding a block at or after list position x
@@ -1314,9 +1337,9 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
   auto begin = [&](int x) {
     const int sb = start_of(b), eb = start_of(b + 1);
     seg_end = eb < xbp ? eb : xbp;
-    flags = (x == sb && seg_end == eb) ? (flags | F_WHOLE) : (flags & ~F_WHOLE);
+    flags = (x == sb && seg_end == eb && !a.partials_only) ? (flags | F_WHOLE) : (flags & ~F_WHOLE);
     n = seq_len(b);
-    row0 = first_visible_block(n, 1, win) - sb;
+    row0 = decode_first_block(a, n) - sb;
     lo_hi = win > 0 ? max(0, n - win) : 0;
 #pragma unroll
     for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1528,12 +1551,12 @@ struct FlashV {
 struct FlashTile {
   int n_lo, n_hi, lo_lo, lo_hi, jb0, jb1, nsteps;
 };
-__device__ __forceinline__ FlashTile flash_tile(int n, int ql, int G, int win, int ct, int cols) {
+__device__ __forceinline__ FlashTile flash_tile(int n, int ql, int G, int win, int ct, int cols, bool noncausal) {
   FlashTile t;
   const int tok_first = (ct * cols) / G;
   const int tok_last = min(ql - 1, (ct * cols + cols - 1) / G);
-  t.n_lo = n - ql + 1 + tok_first;
-  t.n_hi = n - ql + 1 + tok_last;
+  t.n_lo = noncausal ? n : n - ql + 1 + tok_first;
+  t.n_hi = noncausal ? n : n - ql + 1 + tok_last;
   t.lo_lo = win > 0 ? max(0, t.n_lo - win) : 0;
   t.lo_hi = win > 0 ? max(0, t.n_hi - win) : 0;
   t.jb0 = t.lo_lo / kBS;
@@ -1582,7 +1605,11 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   const int half = lane >> 5, c32 = lane & 31;
   const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
   if (n <= 0) return;
-  const int ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
+  const bool noncausal = a.noncausal != 0;
+  // (with every column seeing all n rows, the query count is not bounded by n)
+  const int ql = __builtin_amdgcn_readfirstlane(
+      noncausal ? max(0, min(((const_i32_kptr)a.q_start)[b + 1] - ((const_i32_kptr)a.q_start)[b], a.max_q))
+                : query_len(a, b, n));
   const int G = a.group;
   const int win = a.window;
   const int ntiles = (ql * G + 31) / 32;
@@ -1594,7 +1621,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   const int cg = ngroups - 1 - rank;
   if (cg < 0) return;
   // the rows the group walks: the union of its tiles' rows
-  const FlashTile grp = flash_tile(n, ql, G, win, cg, 32 * WT);
+  const FlashTile grp = flash_tile(n, ql, G, win, cg, 32 * WT, noncausal);
   const int npieces = flash_pieces(grp.nsteps, a.split_steps);
   if (piece >= npieces) return;
   const int jb0 = grp.jb0, jb1 = grp.jb1;
@@ -1611,11 +1638,11 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   const bool col_ok = tile_ok && tok < ql && q_row >= 0 && q_row < a.total_q;
   const int h = g * G + hh;
   // rows the column sees: [col_lo, ncol) (a padding column sees all n rows)
-  const int ncol = col_ok ? n - ql + 1 + tok : n;
+  const int ncol = (col_ok && !noncausal) ? n - ql + 1 + tok : n;
   const int col_lo = win > 0 ? max(0, ncol - win) : 0;
   // the wave's own rows: steps outside them are skipped, steps inside them
   // with no masked row run the plain body
-  const FlashTile own = flash_tile(n, ql, G, win, tile_ok ? ct : cg * WT, 32);
+  const FlashTile own = flash_tile(n, ql, G, win, tile_ok ? ct : cg * WT, 32, noncausal);
   const int w_lo = own.lo_lo, w_hi = own.n_hi, n_lo = own.n_lo, lo_hi = own.lo_hi;
 
   const int64_t head_off = (int64_t)g * a.tile_bytes;
@@ -1863,10 +1890,11 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
     lt = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
   }
   if (!col_ok) return;
-  if (npieces > 1) {
+  if (npieces > 1 || a.partials_only) {
     // this piece's partial (m, l, acc) of the column, merged by
-    // merge_flash_kernel (the partial rows cover batch * max_q query rows; a
-    // malformed query_start may name more, which are left unwritten)
+    // merge_flash_kernel or, for a shared prefix, by the decode's merge (the
+    // partial rows cover batch * max_q query rows; a malformed query_start
+    // may name more, which are left unwritten)
     if ((int64_t)q_row >= (int64_t)a.batch * a.max_q) return;
     const int64_t rr = ((int64_t)q_row * a.num_heads + h) * a.max_pieces + piece;
 #pragma unroll
@@ -1928,7 +1956,7 @@ __global__ __launch_bounds__(512) void merge_flash_kernel(DecodeArgs a) {
   const int q_row = a.q_start[b] + tok;
   if (q_row < 0 || q_row >= a.total_q || (int64_t)q_row >= (int64_t)a.batch * a.max_q) return;
   const int cols = 32 * a.waves_per_group;   // columns of a work-group
-  const FlashTile tile = flash_tile(n, ql, G, a.window, (tok * G + hh) / cols, cols);
+  const FlashTile tile = flash_tile(n, ql, G, a.window, (tok * G + hh) / cols, cols, false);
   const int np = flash_pieces(tile.nsteps, a.split_steps);
   if (np <= 1) return;
   const int h = g * G + hh;
@@ -1974,15 +2002,36 @@ __global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
     q_row = a.q_start[b] + tok;
     if (q_row < 0 || q_row >= a.total_q) return;
   }
-  const int c_first = a.ws_seginfo[2 * b];
-  int np = a.ws_seginfo[2 * b + 1];
-  if (np <= 1) return;                         // one chunk held the whole sequence
-  if (c_first < 0 || c_first >= a.chunk_slots) return;
+  // Shared-prefix decode: every sequence goes through here, with the prefix
+  // pass's partials and those of its own rows past the prefix (none when the
+  // prefix holds them all).
+  const bool cascade = !EXT && a.pre_pieces > 0;
+  int c_first = 0, np = 0;
+  if (!cascade || (n + kBS - 1) / kBS > decode_first_block(a, n)) {
+    c_first = a.ws_seginfo[2 * b];
+    np = a.ws_seginfo[2 * b + 1];
+  }
+  if (!cascade && np <= 1) return;             // one chunk held the whole sequence
+  if (c_first < 0 || c_first >= a.chunk_slots) np = 0;
   if (np > a.chunk_slots - c_first) np = a.chunk_slots - c_first;
   const int h = g * a.group + hh;
   const int64_t row0 = ((EXT ? (int64_t)tok * a.num_heads : 0) + h) * (a.batch + a.chunk_slots) + b + c_first;
   float M = kNegInf, L = 0.0f;
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (cascade) {
+    const int64_t pr = ((int64_t)b * a.num_heads + h) * a.pre_max_pieces;
+    for (int p = 0; p < a.pre_pieces; ++p) {
+      const float m = a.pre_m[pr + p];
+      if (m == kNegInf) continue;
+      const float l = a.pre_l[pr + p];
+      const floatx4 v = *reinterpret_cast<const floatx4*>(a.pre_acc + (pr + p) * D + 4 * c);
+      const float Mn = fmaxf(M, m);
+      const float sa = __builtin_amdgcn_exp2f(M - Mn), sb = __builtin_amdgcn_exp2f(m - Mn);
+      acc = acc * sa + v * sb;
+      L = L * sa + l * sb;
+      M = Mn;
+    }
+  }
 #pragma unroll 4
   for (int p = 0; p < np; ++p) {
     const float m = a.ws_m[row0 + p];
@@ -2112,7 +2161,7 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
       else hipLaunchKernelGGL((extend_flash_kernel<KV, 128, 4>), grid, dim3(256), 0, s, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
-      if (a.max_pieces > 1) {
+      if (a.max_pieces > 1 && !a.partials_only) {
         const int mt = merge_tokens(a.group, D);
         const int threads = ((mt * a.group * (D / 4) + 63) / 64) * 64;
         dim3 mgrid(a.num_kv_heads, a.batch, (a.max_q + mt - 1) / mt);
@@ -2242,6 +2291,51 @@ hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, co
   return launch_append_from(pool, SegFromDevice{segs_dev}, num_segments, k_new, v_new, in_dtype, total_rows, stream);
 }
 
+// The one virtual sequence of a shared-prefix decode's prefix pass: its
+// query_start {0, batch} and its length, the prefix.
+__global__ __launch_bounds__(64) void cascade_args_kernel(int* args, int batch, int prefix) {
+  if (threadIdx.x == 0) {
+    args[0] = 0;
+    args[1] = batch;
+    args[2] = prefix;
+    args[3] = 0;
+  }
+}
+
+// Shared-prefix decode: the prefix pass (the several-token kernel without
+// the causal mask, partials only), then the decode over every sequence's
+// rows past the prefix, whose merge folds in the prefix's partials.
+template <kvc_dtype KV, kvc_dtype QT>
+hipError_t launch_cascade_typed(const DecodeArgs& a, const DecodePlan& plan, int* pre_args, int D, hipEvent_t ev0,
+                                hipEvent_t ev1, hipStream_t s) {
+  hipError_t e;
+  const int prefix = plan.skip_blocks * kBS;
+  hipLaunchKernelGGL(cascade_args_kernel, dim3(1), dim3(64), 0, s, pre_args, a.batch, prefix);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  DecodeArgs ap = a;
+  ap.batch = 1;
+  ap.q_start = pre_args;
+  ap.total_q = a.batch;
+  ap.max_q = a.batch;
+  ap.context_lens = pre_args + 2;
+  ap.max_ctx = prefix;
+  ap.noncausal = 1;
+  ap.partials_only = 1;
+  ap.ws_acc = const_cast<float*>(a.pre_acc);
+  ap.ws_m = const_cast<float*>(a.pre_m);
+  ap.ws_l = const_cast<float*>(a.pre_l);
+  ap.max_pieces = plan.pre_pieces;
+  ap.split_steps = plan.pre_split_steps;
+  ap.waves_per_group = 4;
+  ap.window = 0;
+  ap.skip_blocks = 0;
+  ap.pre_pieces = 0;
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+  if ((e = launch_decode_typed<KV, QT>(ap, D, 3, false, plan.pre_groups, 1, nullptr, nullptr, s)) != hipSuccess)
+    return e;
+  return launch_decode_typed<KV, QT>(a, D, 2, true, 0, 1, nullptr, ev1, s);
+}
+
 hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q, kvc_dtype q_dtype,
                          const int32_t* q_start, int32_t total_q, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* context_lens, int32_t max_context_len, int32_t batch, int32_t num_heads,
@@ -2280,6 +2374,12 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   a.window = plan.window;
   a.split_steps = plan.split_steps;
   a.max_pieces = plan.max_pieces;
+  a.skip_blocks = plan.skip_blocks;
+  a.partials_only = plan.skip_blocks > 0;
+  a.noncausal = 0;
+  a.pre_pieces = plan.skip_blocks > 0 ? plan.pre_pieces : 0;
+  a.pre_max_pieces = plan.pre_pieces;
+  a.pre_acc = a.pre_m = a.pre_l = nullptr;
   const bool merge = plan.kernel == 2 || plan.num_partitions > 1;
   const WorkspaceLayout wl = workspace_layout(plan, batch, num_heads, pool.num_kv_heads, pool.head_dim);
   char* w = static_cast<char*>(workspace);
@@ -2289,6 +2389,24 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   a.ws_seginfo = (wl.bytes && plan.kernel == 2) ? reinterpret_cast<int*>(w + wl.seginfo) : nullptr;
   a.ws_ticket = (wl.bytes && plan.kernel == 2) ? reinterpret_cast<int*>(w + wl.tickets) : nullptr;
   const int D = pool.head_dim;
+  if (plan.kernel == 2 && plan.skip_blocks > 0) {
+    a.pre_acc = reinterpret_cast<const float*>(w + wl.pre_acc);
+    a.pre_m = reinterpret_cast<const float*>(w + wl.pre_m);
+    a.pre_l = reinterpret_cast<const float*>(w + wl.pre_l);
+    int* pre_args = reinterpret_cast<int*>(w + wl.pre_args);
+    switch (pool.dtype) {
+      case KVC_F16:
+        return launch_cascade_typed<KVC_F16, KVC_F16>(a, plan, pre_args, D, ev_start, ev_end, stream);
+      case KVC_BF16:
+        return launch_cascade_typed<KVC_BF16, KVC_BF16>(a, plan, pre_args, D, ev_start, ev_end, stream);
+      case KVC_FP8_E4M3:
+        return launch_cascade_typed<KVC_FP8_E4M3, KVC_BF16>(a, plan, pre_args, D, ev_start, ev_end, stream);
+      case KVC_INT8:
+        return launch_cascade_typed<KVC_INT8, KVC_BF16>(a, plan, pre_args, D, ev_start, ev_end, stream);
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   switch (pool.dtype) {
     case KVC_F32:
       return launch_decode_typed<KVC_F32, KVC_F32>(a, D, plan.kernel, merge, plan.tile_groups, plan.tiles_per_wave,

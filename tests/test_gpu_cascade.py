@@ -1,0 +1,90 @@
+"""GPU parity of the shared-prefix (cascade) decode: kvc_decode_attention with
+opts.shared_prefix = P (every sequence forked from one P-token prefix) against
+the oracle's decode attention over all rows, per element within
+|gpu - ref| <= 2e-3 + 1e-2 |ref| (fp8 / int8 against the stored values), and
+close to the plain decode of the same step.
+
+Cases: the scaled-down shared-prefix workload in every cache dtype; head
+groupings from MHA to 16 query heads per KV head; batches whose queries fill
+one, several and a partial prefix work-group (32-column tiles of (sequence,
+head) pairs, four per group); prefixes of one block and of many (the prefix
+pass cut into pieces); own rows of one token, within a block, across blocks;
+forced splits of the own rows over many waves; and the options the mode
+rejects.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_split_amd as kvc
+from conftest import gpu_available
+from harness import check_close, gpu_decode_again, gpu_setup, gpu_step, oracle_decode, oracle_run, to_f64
+from workloads import custom_workload, make_values, make_workload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+TOL = (2e-3, 1e-2)
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _run(wl, **split):
+    values = make_values(wl, "cpu")
+    st = oracle_run(wl, values)
+    cache = gpu_setup(wl, values)
+    plain, bt, cl = gpu_step(cache, wl, values)
+    torch.cuda.synchronize()
+    ref = oracle_decode(st, wl, values)
+    o = gpu_decode_again(cache, wl, values, bt, cl, kernel=2, shared_prefix=wl.shared_prefix, **split)
+    torch.cuda.synchronize()
+    return o, plain, ref
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8", "int8"])
+def test_shared_prefix_workload(kv):
+    wl = make_workload(4, small=True, kv_dtype=kv)
+    _say(f"[cascade] {wl.name}")
+    o, plain, ref = _run(wl)
+    check_close(to_f64(o), ref, *TOL, f"cascade {kv}")
+    check_close(to_f64(o), to_f64(plain), 4e-3, 2e-2, f"cascade vs plain decode {kv}")
+
+
+@pytest.mark.parametrize("hq,hkv,d,B,P", [(8, 2, 128, 40, 16), (16, 1, 64, 3, 512), (32, 8, 128, 9, 64),
+                                          (12, 3, 64, 70, 256), (4, 4, 128, 5, 1024), (16, 16, 64, 33, 48)])
+def test_shapes(hq, hkv, d, B, P):
+    rng = np.random.default_rng(hq * 31 + B)
+    own = rng.choice([0, 1, 5, 15, 16, 17, 40, 200], size=B)   # rows past the prefix before the step
+    lens = P + own
+    wl = custom_workload(B, hq, hkv, d, "bf16", lens, seed=B + P, shared_prefix=P, name="cascade shapes")
+    _say(f"[cascade] heads {hq}/{hkv} D{d} B{B} prefix {P}")
+    o, plain, ref = _run(wl)
+    check_close(to_f64(o), ref, *TOL, f"cascade {hq}/{hkv} D{d} B{B} P{P}")
+
+
+@pytest.mark.parametrize("wi", [1, 3, 100])
+def test_own_rows_split_over_waves(wi):
+    lens = [128 + x for x in (0, 3, 300, 16, 33, 1)]
+    wl = custom_workload(len(lens), 16, 4, 128, "fp8", lens, seed=7, shared_prefix=128, name="cascade splits")
+    o, plain, ref = _run(wl, work_items=wi)
+    check_close(to_f64(o), ref, *TOL, f"cascade work_items {wi}")
+
+
+def test_options_the_mode_rejects():
+    lens = [64 + 5, 64 + 20]
+    wl = custom_workload(len(lens), 8, 2, 128, "bf16", lens, seed=3, shared_prefix=64, name="cascade options")
+    values = make_values(wl, "cpu")
+    cache = gpu_setup(wl, values)
+    _, bt, cl = gpu_step(cache, wl, values)
+    q = values["q"].cuda().contiguous()
+    for bad in (dict(shared_prefix=40), dict(shared_prefix=-16), dict(shared_prefix=64, window=32),
+                dict(shared_prefix=64, kernel=1), dict(shared_prefix=64, pool_pieces=2),
+                dict(shared_prefix=16 * bt.shape[1])):
+        with pytest.raises(kvc.KvcError):
+            cache.decode(q, bt, cl, wl.max_context_len, wl.scale, **bad)
+    assert kvc.decode_workspace_bytes(2, 8, 2, 128, 100, shared_prefix=40) == 0
+    assert kvc.decode_workspace_bytes(2, 8, 2, 128, 100, shared_prefix=64) > \
+        kvc.decode_workspace_bytes(2, 8, 2, 128, 100)

@@ -153,6 +153,9 @@ def make_workload(cid: int, seed: int | None = None, small: bool = False, **over
     p.update(override)
     if "kv_dtype" in override and override["kv_dtype"] != CONFIGS[cid]["kv_dtype"]:
         p["name"] = f"{p['name']} -- {override['kv_dtype']} cache instead"
+        # q in the cache's own dtype for 16-bit caches, bf16 with one-byte codes
+        if "q_dtype" not in override:
+            p["q_dtype"] = "bf16" if override["kv_dtype"] in QUANTISED else override["kv_dtype"]
     seed = cid if seed is None else seed
     rng = np.random.default_rng(seed)
     lens = _lengths(cid, rng, p)
