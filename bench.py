@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--pool-pieces", type=int, default=0,
                    help="MFMA decode: pieces of each run handed out at run time (0 = static split, the default)")
     p.add_argument("--pool-shift", type=int, default=0, help="MFMA decode: the pool is the last 1/2^shift of a run")
+    p.add_argument("--shared-prefix", action="store_true",
+                   help="decode: attend the workload's shared prefix once for the batch (cascade split)")
     p.add_argument("--extend-kernel", type=int, choices=[0, 2, 3], default=0,
                    help="several-token kernel: 0 auto, 2 rows split over waves, 3 one wave per 32 columns")
     p.add_argument("--tiles-per-wave", type=int, default=0,
@@ -444,9 +446,13 @@ def main():
         cache.truncate(s, L)
     torch.cuda.synchronize()
     out = torch.empty_like(q)
+    prefix = wl.shared_prefix if args.shared_prefix else 0
+    if args.shared_prefix and not prefix:
+        raise SystemExit("--shared-prefix needs a workload with a shared prefix (config 4)")
     ws = torch.empty(max(256, kvc.decode_workspace_bytes(wl.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
                                                          wl.max_context_len, args.partition_tokens, args.kernel,
-                                                         args.work_items, args.pool_pieces, args.pool_shift)),
+                                                         args.work_items, args.pool_pieces, args.pool_shift,
+                                                         prefix)),
                      dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -460,7 +466,8 @@ def main():
         cache.append(seqs, k_new, v_new)
         cache.decode(q, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws, kernel=args.kernel,
                      partition_tokens=args.partition_tokens, work_items=args.work_items, split_events=events,
-                     window=wl.window, pool_pieces=args.pool_pieces, pool_shift=args.pool_shift)
+                     window=wl.window, pool_pieces=args.pool_pieces, pool_shift=args.pool_shift,
+                     shared_prefix=prefix)
         for s, L in zip(seqs, hist_len):
             cache.truncate(s, L)
 
@@ -486,7 +493,7 @@ def main():
     ab = algorithmic_bytes(wl)
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
     prof = (profiled_traffic(workload_key(args)) if args.kernel in (0, 2) and not args.work_items
-            and not args.pool_pieces else None)
+            and not args.pool_pieces and not args.shared_prefix else None)
     traffic = prof[0] if prof else None
     achieved = ab["split_kernel"] / (split_avg_ms * 1e-3) / 1e9
     result = {
@@ -510,10 +517,13 @@ def main():
                    "attended_tokens": int(wl.attend_lens.sum()), "kv_bytes": ab["kv"],
                    "kernel": ["auto", "fma", "mfma"][args.kernel], "partition_tokens": args.partition_tokens or "auto",
                    "work_items": args.work_items or "auto", "pool_pieces": args.pool_pieces,
-                   "parallelism": "single GPU"},
+                   "shared_prefix": prefix, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "decode split-K kernel", "avg_launch_us": round(split_avg_ms * 1e3, 2),
+                     # with a shared prefix: the prefix pass and the own-rows decode, priced at the
+                     # plain decode's bytes (an effective rate: the prefix is read once, not B times)
+                     "kernel": "decode split-K kernel" + (" (prefix pass + own rows)" if prefix else ""),
+                     "avg_launch_us": round(split_avg_ms * 1e3, 2),
                      "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
                      "algorithmic_bytes_per_launch": ab["split_kernel"],
                      "traffic_source": prof[1] if prof else None},

@@ -127,15 +127,14 @@ inline int32_t default_waves(kvc_dtype kv) {
 struct WorkspaceLayout {
   size_t acc, m, l, seginfo, tickets, bytes;
   // shared-prefix decode: the prefix pass's partial rows [batch][Hq][pieces]
-  // and the arguments of its one virtual sequence (query_start[2], length)
-  size_t pre_acc, pre_m, pre_l, pre_args;
+  size_t pre_acc, pre_m, pre_l;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline WorkspaceLayout workspace_layout(const DecodePlan& p, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                         int32_t head_dim) {
-  WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0};
   size_t rows;
   if (p.kernel == 3) {
     if (p.max_pieces <= 1) return w;   // every tile in one piece: outputs only
@@ -160,8 +159,7 @@ inline WorkspaceLayout workspace_layout(const DecodePlan& p, int32_t batch, int3
     w.pre_acc = w.bytes;
     w.pre_m = w.pre_acc + align256(pre_rows * head_dim * sizeof(float));
     w.pre_l = w.pre_m + align256(pre_rows * sizeof(float));
-    w.pre_args = w.pre_l + align256(pre_rows * sizeof(float));
-    w.bytes = w.pre_args + align256(4 * sizeof(int32_t));
+    w.bytes = w.pre_l + align256(pre_rows * sizeof(float));
   }
   return w;
 }

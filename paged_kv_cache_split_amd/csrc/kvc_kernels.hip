@@ -384,7 +384,9 @@ struct DecodeArgs {
   // merge also folds pre_pieces partial rows per (sequence, head) from
   // pre_acc / pre_m / pre_l ([batch][Hq][pre_max_pieces]).  The prefix pass
   // runs the several-token kernel with every column seeing all rows
-  // (noncausal).
+  // (noncausal): one sequence (batch 1) of max_ctx rows read through the
+  // block table's first row, with total_q query rows; q_start and
+  // context_lens are not read then.
   int32_t skip_blocks;
   int32_t partials_only;
   int32_t noncausal;
@@ -1603,13 +1605,13 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, c32 = lane & 31;
-  const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
-  if (n <= 0) return;
+  // Without the causal mask (a shared prefix's pass) there is one sequence of
+  // max_ctx rows whose query rows are the total_q (<= max_q) rows of q.
   const bool noncausal = a.noncausal != 0;
-  // (with every column seeing all n rows, the query count is not bounded by n)
-  const int ql = __builtin_amdgcn_readfirstlane(
-      noncausal ? max(0, min(((const_i32_kptr)a.q_start)[b + 1] - ((const_i32_kptr)a.q_start)[b], a.max_q))
-                : query_len(a, b, n));
+  const int n = __builtin_amdgcn_readfirstlane(noncausal ? min(a.max_ctx, a.max_blocks * kBS)
+                                                         : attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
+  if (n <= 0) return;
+  const int ql = __builtin_amdgcn_readfirstlane(noncausal ? min(a.max_q, a.total_q) : query_len(a, b, n));
   const int G = a.group;
   const int win = a.window;
   const int ntiles = (ql * G + 31) / 32;
@@ -1627,7 +1629,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   const int jb0 = grp.jb0, jb1 = grp.jb1;
   const int s_begin = npieces > 1 ? piece * a.split_steps : 0;
   const int s_end = npieces > 1 ? min(grp.nsteps, s_begin + a.split_steps) : grp.nsteps;
-  const int q0 = __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
+  const int q0 = noncausal ? 0 : __builtin_amdgcn_readfirstlane(((const_i32_kptr)a.q_start)[b]);
 
   // this wave's tile and this lane's column: token tok, head hh of the group
   const int ct = cg * WT + wave;
@@ -2019,14 +2021,18 @@ __global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
   float M = kNegInf, L = 0.0f;
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
   if (cascade) {
+    // Every prefix piece holds rows, so its max is finite; the first step's
+    // weight of the empty start (M = -inf) is a select, not a branch, so the
+    // unrolled loads all issue ahead of their use.
     const int64_t pr = ((int64_t)b * a.num_heads + h) * a.pre_max_pieces;
+#pragma unroll 8
     for (int p = 0; p < a.pre_pieces; ++p) {
       const float m = a.pre_m[pr + p];
-      if (m == kNegInf) continue;
       const float l = a.pre_l[pr + p];
       const floatx4 v = *reinterpret_cast<const floatx4*>(a.pre_acc + (pr + p) * D + 4 * c);
       const float Mn = fmaxf(M, m);
-      const float sa = __builtin_amdgcn_exp2f(M - Mn), sb = __builtin_amdgcn_exp2f(m - Mn);
+      const float sa = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+      const float sb = __builtin_amdgcn_exp2f(m - Mn);
       acc = acc * sa + v * sb;
       L = L * sa + l * sb;
       M = Mn;
@@ -2291,33 +2297,24 @@ hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, co
   return launch_append_from(pool, SegFromDevice{segs_dev}, num_segments, k_new, v_new, in_dtype, total_rows, stream);
 }
 
-// The one virtual sequence of a shared-prefix decode's prefix pass: its
-// query_start {0, batch} and its length, the prefix.
-__global__ __launch_bounds__(64) void cascade_args_kernel(int* args, int batch, int prefix) {
-  if (threadIdx.x == 0) {
-    args[0] = 0;
-    args[1] = batch;
-    args[2] = prefix;
-    args[3] = 0;
-  }
-}
-
 // Shared-prefix decode: the prefix pass (the several-token kernel without
-// the causal mask, partials only), then the decode over every sequence's
-// rows past the prefix, whose merge folds in the prefix's partials.
+// the causal mask over sequence 0's first rows, partials only), then the
+// decode over every sequence's rows past the prefix, whose merge folds in the
+// prefix's partials.  Timing events (ev0, ev1) span both passes.  (Run on a
+// second stream beside the decode, the prefix pass costs more than it hides:
+// the decode's waves slow down where it lands, and the fork and join add
+// their own gaps.)
 template <kvc_dtype KV, kvc_dtype QT>
-hipError_t launch_cascade_typed(const DecodeArgs& a, const DecodePlan& plan, int* pre_args, int D, hipEvent_t ev0,
-                                hipEvent_t ev1, hipStream_t s) {
+hipError_t launch_cascade_typed(const DecodeArgs& a, const DecodePlan& plan, int D, hipEvent_t ev0, hipEvent_t ev1,
+                                hipStream_t s) {
   hipError_t e;
   const int prefix = plan.skip_blocks * kBS;
-  hipLaunchKernelGGL(cascade_args_kernel, dim3(1), dim3(64), 0, s, pre_args, a.batch, prefix);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   DecodeArgs ap = a;
   ap.batch = 1;
-  ap.q_start = pre_args;
+  ap.q_start = nullptr;        // (not read without the causal mask)
   ap.total_q = a.batch;
   ap.max_q = a.batch;
-  ap.context_lens = pre_args + 2;
+  ap.context_lens = nullptr;
   ap.max_ctx = prefix;
   ap.noncausal = 1;
   ap.partials_only = 1;
@@ -2393,16 +2390,15 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
     a.pre_acc = reinterpret_cast<const float*>(w + wl.pre_acc);
     a.pre_m = reinterpret_cast<const float*>(w + wl.pre_m);
     a.pre_l = reinterpret_cast<const float*>(w + wl.pre_l);
-    int* pre_args = reinterpret_cast<int*>(w + wl.pre_args);
     switch (pool.dtype) {
       case KVC_F16:
-        return launch_cascade_typed<KVC_F16, KVC_F16>(a, plan, pre_args, D, ev_start, ev_end, stream);
+        return launch_cascade_typed<KVC_F16, KVC_F16>(a, plan, D, ev_start, ev_end, stream);
       case KVC_BF16:
-        return launch_cascade_typed<KVC_BF16, KVC_BF16>(a, plan, pre_args, D, ev_start, ev_end, stream);
+        return launch_cascade_typed<KVC_BF16, KVC_BF16>(a, plan, D, ev_start, ev_end, stream);
       case KVC_FP8_E4M3:
-        return launch_cascade_typed<KVC_FP8_E4M3, KVC_BF16>(a, plan, pre_args, D, ev_start, ev_end, stream);
+        return launch_cascade_typed<KVC_FP8_E4M3, KVC_BF16>(a, plan, D, ev_start, ev_end, stream);
       case KVC_INT8:
-        return launch_cascade_typed<KVC_INT8, KVC_BF16>(a, plan, pre_args, D, ev_start, ev_end, stream);
+        return launch_cascade_typed<KVC_INT8, KVC_BF16>(a, plan, D, ev_start, ev_end, stream);
       default:
         return hipErrorInvalidValue;
     }
