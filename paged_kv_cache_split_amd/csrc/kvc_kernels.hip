@@ -921,10 +921,13 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
 #pragma unroll
   for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m));
   if (edge) {
-    // (a zero fp8 scale makes a masked -inf * 0 a NaN: force the zeros)
+    // Masked rows weigh 0 (forced: with m still -inf, or a zero one-byte
+    // scale, the exponent above is NaN).  Scores of finite values are finite,
+    // so -inf marks exactly the masked rows, and the index tests stay in the
+    // edge path.
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (t0 + e >= ncol || t0 + e < col_lo) pv[e] = 0.0f;
+      if (sv[e] == kNegInf) pv[e] = 0.0f;
   }
   l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
   // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
