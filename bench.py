@@ -520,8 +520,8 @@ def main():
                    "shared_prefix": prefix, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     # with a shared prefix: the prefix pass and the own-rows decode, priced at the
-                     # plain decode's bytes (an effective rate: the prefix is read once, not B times)
+                     # with a shared prefix: the prefix pass and the own-rows decode together, over the
+                     # same unique bytes as the plain decode (the prefix counted once in both)
                      "kernel": "decode split-K kernel" + (" (prefix pass + own rows)" if prefix else ""),
                      "avg_launch_us": round(split_avg_ms * 1e3, 2),
                      "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
