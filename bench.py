@@ -3,9 +3,9 @@
 A step is the whole hot path over one batch: kvc_append of every sequence's
 new K/V row (slot reservation on the host, upload of the write plan, the
 append kernel), then kvc_decode_attention (split-K kernel + merge kernel).
-The step is made repeatable by truncating each sequence back to its history
-length afterwards (host bookkeeping only), so every step appends into the
-same slots.
+The step is made repeatable by truncating every sequence back to its history
+length afterwards (host bookkeeping only, one kvc_truncate_many call), so
+every step appends into the same slots.
 
 Prints ONE JSON line: value = KV-read GB/s (distinct K/V bytes the step
 attends / step time), plus us_per_step, the split kernel's roofline (HIP
@@ -19,6 +19,8 @@ workload's flops per algorithmic byte puts it under.
 from __future__ import annotations
 
 import argparse
+import ctypes
+import gc
 import json
 import os
 import sys
@@ -65,6 +67,58 @@ def parse():
                    help="time decode under a sliding window of 4096 over 16K-token contexts whose older blocks "
                         "were evicted (70B-shaped batch) instead of --config")
     return p.parse_args()
+
+
+class TimingEvent:
+    """A HIP event used only to time the kernels between two records on one
+    stream.  Made with hipEventDisableSystemFence: its record takes no
+    system-scope fence, so it does not write back and invalidate the caches
+    between the kernels it brackets (default events do, and that cost ~6 us of
+    every timed decode step).  Elapsed times are read after a device
+    synchronize; the library records it through `cuda_event`, as it would a
+    torch event's handle."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        if TimingEvent._hip is None:
+            TimingEvent._hip = ctypes.CDLL("libamdhip64.so.7")   # the HIP runtime torch has loaded
+        h = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def record(self, stream_handle: int):
+        rc = self._hip.hipEventRecord(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(stream_handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    @staticmethod
+    def pairs(n: int):
+        """n (start, end) pairs, each recorded once on the current stream so
+        that no first-use cost lands in a timed step."""
+        import torch
+        out = [(TimingEvent(), TimingEvent()) for _ in range(n)]
+        h = torch.cuda.current_stream().cuda_stream
+        for a, b in out:
+            a.record(h)
+            b.record(h)
+        torch.cuda.synchronize()
+        return out
+
+    def elapsed_time(self, end) -> float:
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                           ctypes.c_void_p(end.cuda_event))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.cuda_event:
+            self._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
 
 
 def algorithmic_bytes(wl):
@@ -306,8 +360,7 @@ def run_extend(args):
     k_new, v_new, q = values["k_new"].contiguous(), values["v_new"].contiguous(), values["q"].contiguous()
     cache.append(seqs, k_new, v_new, n_new=n_new)
     bt, cl = cache.export_tables(seqs)
-    for s_, L in zip(seqs, hist_len):
-        cache.truncate(s_, L)
+    cache.truncate_many(seqs, hist_len)
     qs = torch.from_numpy(np.concatenate([[0], np.cumsum(wl.q_lens)]).astype(np.int32)).to(dev)
     torch.cuda.synchronize()
     out = torch.empty_like(q)
@@ -315,20 +368,20 @@ def run_extend(args):
                                                          wl.max_query_len, wl.max_context_len, args.work_items,
                                                          args.tiles_per_wave, args.extend_kernel)),
                      dtype=torch.uint8, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = TimingEvent.pairs(args.steps)
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in ev:
-        a.record()
-        b.record()
 
     def step(events=None):
         cache.append(seqs, k_new, v_new, n_new=n_new)
         cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws,
                      work_items=args.work_items, split_events=events, tiles_per_wave=args.tiles_per_wave,
                      kernel=args.extend_kernel)
-        for s_, L in zip(seqs, hist_len):
-            cache.truncate(s_, L)
+        cache.truncate_many(seqs, hist_len)
 
+    # a full garbage-collector pass over the setup's objects inside the timed
+    # loop costs tens of milliseconds: collect now and exempt what exists
+    gc.collect()
+    gc.freeze()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -442,8 +495,7 @@ def main():
     # tables as they are after the step's append (the decode reads L+1 tokens)
     cache.append(seqs, k_new, v_new)
     bt, cl = cache.export_tables(seqs)
-    for s, L in zip(seqs, hist_len):
-        cache.truncate(s, L)
+    cache.truncate_many(seqs, hist_len)
     torch.cuda.synchronize()
     out = torch.empty_like(q)
     prefix = wl.shared_prefix if args.shared_prefix else 0
@@ -454,13 +506,9 @@ def main():
                                                          args.work_items, args.pool_pieces, args.pool_shift,
                                                          prefix)),
                      dtype=torch.uint8, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = TimingEvent.pairs(args.steps)
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
-    for a, b in ev:          # materialise the events before handing them to the library
-        a.record()
-        b.record()
 
     def step(events=None):
         cache.append(seqs, k_new, v_new)
@@ -468,9 +516,12 @@ def main():
                      partition_tokens=args.partition_tokens, work_items=args.work_items, split_events=events,
                      window=wl.window, pool_pieces=args.pool_pieces, pool_shift=args.pool_shift,
                      shared_prefix=prefix)
-        for s, L in zip(seqs, hist_len):
-            cache.truncate(s, L)
+        cache.truncate_many(seqs, hist_len)
 
+    # a full garbage-collector pass over the setup's objects inside the timed
+    # loop costs tens of milliseconds: collect now and exempt what exists
+    gc.collect()
+    gc.freeze()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

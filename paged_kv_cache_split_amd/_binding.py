@@ -30,7 +30,8 @@ DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8, "int8": INT8}
 
 SYMBOLS = [
     "kvc_bytes_per_token", "kvc_pool_bytes", "kvc_scale_bytes", "kvc_scratch_bytes", "kvc_create", "kvc_destroy",
-    "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_evict", "kvc_reserve_host",
+    "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_truncate_many", "kvc_evict",
+    "kvc_reserve_host",
     "kvc_get_table", "kvc_stats", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
     "kvc_decode_attention", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_sched_create",
     "kvc_sched_destroy", "kvc_sched_submit", "kvc_sched_plan", "kvc_sched_commit", "kvc_sched_get_stats",
@@ -85,6 +86,7 @@ _sig = {
     "kvc_fork": (ctypes.c_int, [_vp, _i64, _i64]),
     "kvc_free_seq": (ctypes.c_int, [_vp, _i64]),
     "kvc_truncate": (ctypes.c_int, [_vp, _i64, _i32]),
+    "kvc_truncate_many": (ctypes.c_int, [_vp, _i32, _P64, _P32]),
     "kvc_evict": (ctypes.c_int, [_vp, _i64, _i32]),
     "kvc_reserve_host": (ctypes.c_int, [_vp, _i32, _P64, _P32, _P32, _P32, _P32, _i32, _P32]),
     "kvc_get_table": (ctypes.c_int, [_vp, _i64, _P32, _i32, _P32, _P32]),
@@ -260,6 +262,14 @@ class KVCache:
 
     def truncate(self, seq_id, num_tokens):
         _check(_lib.kvc_truncate(self._h, int(seq_id), int(num_tokens)), "kvc_truncate")
+
+    def truncate_many(self, seq_ids, num_tokens):
+        """truncate of every (seq_ids[i], num_tokens[i]) in one call, all or nothing."""
+        ids, pids = _i64_array(seq_ids)
+        nt, pnt = _i32_array(num_tokens)
+        if len(ids) != len(nt):
+            raise ValueError("seq_ids and num_tokens differ in length")
+        _check(_lib.kvc_truncate_many(self._h, len(ids), pids, pnt), "kvc_truncate_many")
 
     def reserve_host(self, seq_ids, n_new=None):
         ids, pids = _i64_array(seq_ids)

@@ -581,6 +581,42 @@ kvc_status kvc_truncate(kvc_cache* c, int64_t seq_id, int32_t num_tokens) {
   return ok();
 }
 
+kvc_status kvc_truncate_many(kvc_cache* c, int32_t n, const int64_t* seq_ids, const int32_t* num_tokens) {
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  if (n < 0) return fail(KVC_E_INVALID, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!seq_ids || !num_tokens) return fail(KVC_E_INVALID, "NULL host array");
+  std::lock_guard<std::mutex> lock(c->mu);
+  const int32_t bs = c->cfg.block_size;
+  std::vector<kvc_cache::Seq*> seqs((size_t)n);
+  std::unordered_set<int64_t> seen;
+  seen.reserve((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (!seen.insert(seq_ids[i]).second)
+      return fail(KVC_E_INVALID, "sequence %lld appears twice", (long long)seq_ids[i]);
+    auto it = c->seqs.find(seq_ids[i]);
+    if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    kvc_cache::Seq& s = it->second;
+    const int32_t t = num_tokens[i];
+    if (t < 0 || t > s.len)
+      return fail(KVC_E_INVALID, "sequence %lld: truncate to %d outside 0..%d", (long long)seq_ids[i], t, s.len);
+    if (t % bs != 0 && s.blocks[t / bs] < 0)
+      return fail(KVC_E_INVALID, "sequence %lld: truncate to %d would end inside a released block",
+                  (long long)seq_ids[i], t);
+    seqs[(size_t)i] = &s;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    kvc_cache::Seq& s = *seqs[(size_t)i];
+    const size_t keep = ((int64_t)num_tokens[i] + bs - 1) / bs;
+    while (s.blocks.size() > keep) {
+      if (s.blocks.back() >= 0) c->release(s.blocks.back());
+      s.blocks.pop_back();
+    }
+    s.len = num_tokens[i];
+  }
+  return ok();
+}
+
 kvc_status kvc_evict(kvc_cache* c, int64_t seq_id, int32_t keep_from) {
   if (!c) return fail(KVC_E_INVALID, "cache is NULL");
   std::lock_guard<std::mutex> lock(c->mu);

@@ -259,3 +259,38 @@ def test_extend_workspace_sizes():
     assert kvc.extend_workspace_bytes(4, 8, 2, 64, 40, 300, kernel=1) == 0
     assert kvc.extend_workspace_bytes(4, 8, 2, 64, 40, 300, kernel=4) == 0
     assert kvc.extend_workspace_bytes(4, 8, 2, 64, 4097, 5000, kernel=2) == 0
+
+
+def test_truncate_many_is_truncate_in_order_all_or_nothing():
+    # the batched rollback leaves the same tables and free list as one call per
+    # sequence, and a bad entry anywhere changes nothing
+    order = list(np.random.default_rng(3).permutation(40))
+    a, b, m = _host_cache(40, 4, order), _host_cache(40, 4, order), BlockTableModel(40, 4, order)
+    for c in (a, b):
+        for s, n in enumerate([9, 16, 3]):
+            c.add_seq(s, 0)
+            c.reserve_host([s], [n])
+    for s, n in enumerate([9, 16, 3]):
+        m.allocate(s, 0)
+        m.append([s], [n])
+    a.fork(1, 7)
+    b.fork(1, 7)
+    m.fork(1, 7)
+    plan = [(1, 5), (0, 8), (7, 16), (2, 0)]
+    for s, n in plan:
+        a.truncate(s, n)
+        assert m.truncate(s, n) == 0
+    b.truncate_many([s for s, _ in plan], [n for _, n in plan])
+    _same_state(a, m, [0, 1, 2, 7])
+    _same_state(b, m, [0, 1, 2, 7])
+    before = {s: b.get_table(s) for s in (0, 1, 2, 7)}
+    stats = b.stats()
+    # the first entry of each is valid and would release a block: it must not happen
+    for ids, lens, status in (([0, 1], [4, 6], B.E_INVALID),     # past the length
+                              ([0, 99], [4, 0], B.E_NO_SEQ),     # unknown sequence
+                              ([0, 0], [4, 4], B.E_INVALID)):    # repeated id
+        with pytest.raises(kvc.KvcError) as e:
+            b.truncate_many(ids, lens)
+        assert e.value.status == status
+        assert {s: b.get_table(s) for s in (0, 1, 2, 7)} == before and b.stats() == stats
+    b.truncate_many([], [])
