@@ -166,9 +166,12 @@ kvc_status kvc_free_seq(kvc_cache* cache, int64_t seq_id);
  * KVC_E_INVALID if the new end would fall inside a block kvc_evict released. */
 kvc_status kvc_truncate(kvc_cache* cache, int64_t seq_id, int32_t num_tokens);
 /* kvc_truncate of n sequences in one call: seq_ids[i] (host, n distinct ids)
- * to num_tokens[i] (host), in array order.  Every entry is checked first (as
- * kvc_truncate checks it; a repeated id is KVC_E_INVALID); on any failure
- * nothing changes.  For rolling back a batch at once, as a verifier of draft
+ * to num_tokens[i] (host), applied from the last entry to the first, so that
+ * rolling back an append of the same sequences in the same order returns the
+ * blocks it took to the free list in the reverse of the order it took them,
+ * and a repeat of that append takes the same blocks again.  Every entry is
+ * checked first (as kvc_truncate checks it; a repeated id is KVC_E_INVALID);
+ * on any failure nothing changes.  For rolling back a batch at once, as a verifier of draft
  * tokens does with the ones it rejects ("LLM推理优化实战…" §4.2: the target
  * model checks every draft token in one pass and keeps the accepted prefix). */
 kvc_status kvc_truncate_many(kvc_cache* cache, int32_t n, const int64_t* seq_ids, const int32_t* num_tokens);

@@ -264,7 +264,8 @@ class KVCache:
         _check(_lib.kvc_truncate(self._h, int(seq_id), int(num_tokens)), "kvc_truncate")
 
     def truncate_many(self, seq_ids, num_tokens):
-        """truncate of every (seq_ids[i], num_tokens[i]) in one call, all or nothing."""
+        """truncate of every (seq_ids[i], num_tokens[i]) in one call, last entry
+        first, all or nothing."""
         ids, pids = _i64_array(seq_ids)
         nt, pnt = _i32_array(num_tokens)
         if len(ids) != len(nt):

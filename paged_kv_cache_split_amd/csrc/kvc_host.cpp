@@ -605,7 +605,7 @@ kvc_status kvc_truncate_many(kvc_cache* c, int32_t n, const int64_t* seq_ids, co
                   (long long)seq_ids[i], t);
     seqs[(size_t)i] = &s;
   }
-  for (int32_t i = 0; i < n; ++i) {
+  for (int32_t i = n - 1; i >= 0; --i) {   // last entry first: blocks return in reverse order of taking
     kvc_cache::Seq& s = *seqs[(size_t)i];
     const size_t keep = ((int64_t)num_tokens[i] + bs - 1) / bs;
     while (s.blocks.size() > keep) {

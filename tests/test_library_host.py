@@ -261,9 +261,10 @@ def test_extend_workspace_sizes():
     assert kvc.extend_workspace_bytes(4, 8, 2, 64, 4097, 5000, kernel=2) == 0
 
 
-def test_truncate_many_is_truncate_in_order_all_or_nothing():
+def test_truncate_many_is_truncate_last_first_all_or_nothing():
     # the batched rollback leaves the same tables and free list as one call per
-    # sequence, and a bad entry anywhere changes nothing
+    # sequence from the last entry to the first, and a bad entry anywhere
+    # changes nothing
     order = list(np.random.default_rng(3).permutation(40))
     a, b, m = _host_cache(40, 4, order), _host_cache(40, 4, order), BlockTableModel(40, 4, order)
     for c in (a, b):
@@ -277,7 +278,7 @@ def test_truncate_many_is_truncate_in_order_all_or_nothing():
     b.fork(1, 7)
     m.fork(1, 7)
     plan = [(1, 5), (0, 8), (7, 16), (2, 0)]
-    for s, n in plan:
+    for s, n in reversed(plan):
         a.truncate(s, n)
         assert m.truncate(s, n) == 0
     b.truncate_many([s for s, _ in plan], [n for _, n in plan])
@@ -294,3 +295,23 @@ def test_truncate_many_is_truncate_in_order_all_or_nothing():
         assert e.value.status == status
         assert {s: b.get_table(s) for s in (0, 1, 2, 7)} == before and b.stats() == stats
     b.truncate_many([], [])
+
+
+def test_truncate_many_rolls_an_append_back_exactly():
+    # append one row to every sequence (some of them start a block), roll back,
+    # append again: the same slots, so tables exported after the first append
+    # stay valid for every repeat
+    order = list(np.random.default_rng(5).permutation(64))
+    c = _host_cache(64, 16, order)
+    lens = [16, 31, 32, 7, 48, 0]
+    for s, n in enumerate(lens):
+        c.add_seq(s, 0)
+        if n:
+            c.reserve_host([s], [n])
+    seqs = list(range(len(lens)))
+    first, _ = c.reserve_host(seqs)
+    tables = [c.get_table(s) for s in seqs]
+    for _ in range(3):
+        c.truncate_many(seqs, lens)
+        again, _ = c.reserve_host(seqs)
+        assert again == first and [c.get_table(s) for s in seqs] == tables
