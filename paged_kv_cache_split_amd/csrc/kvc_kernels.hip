@@ -1581,11 +1581,41 @@ __device__ __forceinline__ int flash_pieces(int nsteps, int split_steps) {
 #define KVC_FLASH_P_LO 1
 #endif
 
+// 16-bit caches: each step's tiles go from HBM straight into LDS
+// (global_load_lds, no registers in between), three steps deep (1), or
+// through registers, two deep (0).
+#ifndef KVC_FLASH_DMA
+#define KVC_FLASH_DMA 1
+#endif
+
+// One 16-byte load of every lane of the wave straight into LDS: lane i's 16
+// bytes from src go to LDS byte lds_wave_base + 16 i (lds_wave_base
+// wave-uniform).  The caller waits for it with vm_wait (it counts on the
+// vector-memory counter like any load) and makes it visible to the other
+// waves with a barrier.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(uintptr_t)lds_wave_base, 16, 0, 0);
+}
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maximum)
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_barrier with no fence: the callers order their own LDS and memory traffic
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // K piece r16 = 16 * dim group + score row of a block -> its piece in the
 // stored tile, 16 * dim group + token (the token of score row r is rho(r))
 __device__ __forceinline__ int k_piece(int r16) {
   const int r = r16 & 15;
   return (r16 & ~15) | (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// position of K chunk j of score row r: j ^ ksw<CR>(r), CR chunks per row
+template <int CR>
+__device__ __forceinline__ int ksw(int r) {
+  return (r / (16 / CR)) & (CR - 1);
 }
 
 template <kvc_dtype KV, int D, int WT>
@@ -1599,7 +1629,20 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   // lanes (8 consecutive rows) fall in 8 distinct groups of 4 banks.
   constexpr int KROW = 2 * D + 16, VROW = 2 * 32 + 16;
   constexpr int KBYTES = 32 * KROW, STAGE = KBYTES + D * VROW;
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+  // Loaded straight into LDS (16-bit caches) the rows cannot be padded (one
+  // load instruction fills 1 KB contiguously), so the 16-byte chunks of a row
+  // are permuted instead: K chunk j (dims 8j .. 8j + 7) of score row r sits at
+  // position j ^ ksw(r) of its 2D-byte row, V^T chunk q (tokens 8q .. 8q + 7
+  // of the step) of dim d at position q ^ ((d >> 2) & 3) of its 64-byte row;
+  // either way the operand reads of 16 consecutive lanes hit 16 distinct
+  // groups of banks.
+  constexpr bool DMA = KVC_FLASH_DMA && !is_byte_code(KV);
+  constexpr int RK = 2 * D, CR = RK / 16;             // K row bytes, 16-byte chunks per row
+  constexpr int KBYTES_D = 32 * RK, STAGE_D = KBYTES_D + D * 64;
+  constexpr int NSTAGE = DMA ? 3 : 2, SBYTES = DMA ? STAGE_D : STAGE, KOFF = DMA ? KBYTES_D : KBYTES;
+  constexpr int PERD = STAGE_D / (16 * NT);           // loads per thread and step, straight to LDS
+  static_assert(STAGE_D % (16 * NT) == 0 && (32 * CR) % NT == 0, "whole loads per stage, K and V apart");
+  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * SBYTES];
   // global pieces of one step: 16 bytes each, both blocks, K then V
   constexpr int CHB = is_byte_code(KV) ? D : 2 * D;   // 16-byte pieces per (block, head) tile
   constexpr int PER = 2 * 2 * CHB / NT;               // per thread (K and V, two blocks)
@@ -1662,6 +1705,9 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
     for (int kk = 0; kk < NK; ++kk)
       qv[kk] = col_ok ? *reinterpret_cast<const u32x4*>(qh + 16 * kk + 8 * half) : u32x4{0, 0, 0, 0};
   }
+  // With loads straight into LDS in flight the vector-memory counter counts
+  // them too: take the queries in now, so no wait for them lands in the loop.
+  if constexpr (DMA) vm_wait<0>();
 
   // Block ids of a step, read a step before its tiles are requested (scalar
   // loads complete out of order: their first use waits for all in flight).
@@ -1706,7 +1752,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   // sequence's end (which may hold anything, NaN included) are zeroed: their
   // weight is 0, and 0 times NaN would still be NaN.
   auto store_stage = [&](const Staged& r, int buf, int k0) {
-    char* kl = lds + buf * STAGE;
+    char* kl = lds + buf * SBYTES;
     char* vl = kl + KBYTES;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -1770,14 +1816,15 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   // other step is a plain one with no per-element tests.
   auto step = [&](auto edge_c, int buf, int k0, const Staged& sc) {
     constexpr bool EDGE = decltype(edge_c)::value;
-    const char* kl = lds + buf * STAGE;
-    const char* vl = kl + KBYTES;
+    const char* kl = lds + buf * SBYTES;
+    const char* vl = kl + KOFF;
     floatx16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const u32x4 kop = *reinterpret_cast<const u32x4*>(kl + c32 * KROW + 32 * kk + 16 * half);
+      const u32x4 kop = DMA ? *reinterpret_cast<const u32x4*>(kl + c32 * RK + 16 * ((2 * kk + half) ^ ksw<CR>(c32)))
+                            : *reinterpret_cast<const u32x4*>(kl + c32 * KROW + 32 * kk + 16 * half);
       s = mfma32<KV>(kop, qv[kk], s);
     }
     bool vis[16];
@@ -1853,14 +1900,82 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int od = 0; od < NO; ++od) {
-        const u32x4 vop = *reinterpret_cast<const u32x4*>(vl + (32 * od + c32) * VROW + 32 * s2 + 16 * half);
+        u32x4 vop;
+        if constexpr (DMA) {
+          vop = *reinterpret_cast<const u32x4*>(vl + (32 * od + c32) * 64 + 16 * ((2 * s2 + half) ^ ((c32 >> 2) & 3)));
+          if constexpr (EDGE) {
+            // rows past the sequence's end came in as they lie in the block
+            // (anything, NaN included): their weight is 0, and 0 times NaN
+            // would still be NaN
+            const int t0 = k0 + 16 * s2 + 8 * half;
+            if (t0 + 8 > n) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                vop[e] &= ((t0 + 2 * e < n) ? 0xFFFFu : 0u) | ((t0 + 2 * e + 1 < n) ? 0xFFFF0000u : 0u);
+            }
+          }
+        } else {
+          vop = *reinterpret_cast<const u32x4*>(vl + (32 * od + c32) * VROW + 32 * s2 + 16 * half);
+        }
         acc[od] = mfma32<KV>(vop, pb, acc[od]);
         if constexpr (KVC_FLASH_P_LO) acc[od] = mfma32<KV>(vop, pl, acc[od]);
       }
     }
   };
 
-  if (s_end > s_begin) {
+  // One step's tiles straight into LDS stage stg: load i of thread tid
+  // fills stage chunk i * NT + tid (K chunks first, then V^T), so each load
+  // instruction of a wave fills 64 consecutive chunks.
+  auto dma_stage = [&](int stg, Ids id) {
+    char* base = lds + stg * SBYTES;
+    // the two blocks' tiles of this head (wave-uniform offsets)
+    const int64_t o0 = (int64_t)id.p0 * block_stride + head_off, o1 = (int64_t)id.p1 * block_stride + head_off;
+#pragma unroll
+    for (int i = 0; i < PERD; ++i) {
+      const int L = i * NT + tid;
+      const char* src;
+      if (i * NT < 32 * CR) {                     // K: score row r, position pos
+        const int r = L / CR, pos = L % CR;
+        const int dg = pos ^ ksw<CR>(r), rr = r & 15;
+        const int tkn = (rr & 3) | ((rr & 4) << 1) | ((rr & 8) >> 1);   // rho(rr)
+        src = a.k + ((r >> 4) ? o1 : o0) + (int64_t)(dg * 16 + tkn) * 16;
+      } else {                                    // V^T: dim d, position pos
+        const int L2 = L - 32 * CR, d = L2 >> 2, pos = L2 & 3;
+        const int q = pos ^ ((d >> 2) & 3);
+        src = a.v + ((q >> 1) ? o1 : o0) + (int64_t)(2 * d + (q & 1)) * 16;
+      }
+      const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(base) +
+                           (uint32_t)__builtin_amdgcn_readfirstlane((i * NT + 64 * wave) * 16);
+      lds_dma16(src, dst);
+    }
+  };
+
+  if constexpr (DMA) {
+    // Three stages: step st's tiles were requested two steps earlier.  At
+    // the head of step st every wave waits for its own loads of st (those of
+    // st + 1 may stay in flight), then the barrier makes all of them visible
+    // and tells that every wave is done with step st - 1, whose stage then
+    // takes the loads of st + 2.
+    if (s_end > s_begin) {
+      const Staged none{};
+      dma_stage(0, ids_of(s_begin));
+      if (s_begin + 1 < s_end) dma_stage(1, ids_of(s_begin + 1));
+      Ids idn = ids_of(s_begin + 2);
+      for (int st = s_begin; st < s_end; ++st) {
+        const int i = st - s_begin, buf = i % 3;
+        if (st + 1 < s_end) vm_wait<PERD>();
+        else vm_wait<0>();
+        wg_barrier();
+        if (st + 2 < s_end) dma_stage((i + 2) % 3, idn);
+        idn = ids_of(st + 3);
+        const int k0 = (jb0 + 2 * st) * kBS;
+        if (tile_ok && k0 < w_hi && k0 + 2 * kBS > w_lo) {
+          if (k0 + 2 * kBS > n_lo || k0 < lo_hi) step(std::true_type{}, buf, k0, none);
+          else step(std::false_type{}, buf, k0, none);
+        }
+      }
+    }
+  } else if (s_end > s_begin) {
     Staged r;
     Ids id = ids_of(s_begin);
     load_stage(r, id);
