@@ -1587,6 +1587,9 @@ __device__ __forceinline__ int flash_pieces(int nsteps, int split_steps) {
 #ifndef KVC_FLASH_DMA
 #define KVC_FLASH_DMA 1
 #endif
+#ifndef KVC_FLASH_STAGES
+#define KVC_FLASH_STAGES 3
+#endif
 
 // One 16-byte load of every lane of the wave straight into LDS: lane i's 16
 // bytes from src go to LDS byte lds_wave_base + 16 i (lds_wave_base
@@ -1639,7 +1642,8 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   constexpr bool DMA = KVC_FLASH_DMA && !is_byte_code(KV);
   constexpr int RK = 2 * D, CR = RK / 16;             // K row bytes, 16-byte chunks per row
   constexpr int KBYTES_D = 32 * RK, STAGE_D = KBYTES_D + D * 64;
-  constexpr int NSTAGE = DMA ? 3 : 2, SBYTES = DMA ? STAGE_D : STAGE, KOFF = DMA ? KBYTES_D : KBYTES;
+  constexpr int NSTAGE = DMA ? KVC_FLASH_STAGES : 2, SBYTES = DMA ? STAGE_D : STAGE, KOFF = DMA ? KBYTES_D : KBYTES;
+  static_assert(NSTAGE == 2 || NSTAGE == 3 || NSTAGE == 4, "2 to 4 stages");
   constexpr int PERD = STAGE_D / (16 * NT);           // loads per thread and step, straight to LDS
   static_assert(STAGE_D % (16 * NT) == 0 && (32 * CR) % NT == 0, "whole loads per stage, K and V apart");
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * SBYTES];
@@ -1951,23 +1955,26 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   };
 
   if constexpr (DMA) {
-    // Three stages: step st's tiles were requested two steps earlier.  At
-    // the head of step st every wave waits for its own loads of st (those of
-    // st + 1 may stay in flight), then the barrier makes all of them visible
-    // and tells that every wave is done with step st - 1, whose stage then
-    // takes the loads of st + 2.
+    // NSTAGE stages: step st's tiles were requested NSTAGE - 1 steps earlier.
+    // At the head of step st every wave waits for its own loads of st (those
+    // of the steps after it may stay in flight), then the barrier makes all
+    // of them visible and tells that every wave is done with step st - 1,
+    // whose stage then takes the loads of st + NSTAGE - 1.
     if (s_end > s_begin) {
       const Staged none{};
-      dma_stage(0, ids_of(s_begin));
-      if (s_begin + 1 < s_end) dma_stage(1, ids_of(s_begin + 1));
-      Ids idn = ids_of(s_begin + 2);
+#pragma unroll
+      for (int j = 0; j < NSTAGE - 1; ++j)
+        if (s_begin + j < s_end) dma_stage(j, ids_of(s_begin + j));
+      Ids idn = ids_of(s_begin + NSTAGE - 1);
       for (int st = s_begin; st < s_end; ++st) {
-        const int i = st - s_begin, buf = i % 3;
-        if (st + 1 < s_end) vm_wait<PERD>();
+        const int i = st - s_begin, buf = i % NSTAGE;
+        const int ahead = min(s_end - 1 - st, NSTAGE - 2);   // later steps whose loads are in flight
+        if (NSTAGE > 3 && ahead >= 2) vm_wait<(NSTAGE > 3 ? 2 : 1) * PERD>();
+        else if (ahead >= 1) vm_wait<PERD>();
         else vm_wait<0>();
         wg_barrier();
-        if (st + 2 < s_end) dma_stage((i + 2) % 3, idn);
-        idn = ids_of(st + 3);
+        if (st + NSTAGE - 1 < s_end) dma_stage((i + NSTAGE - 1) % NSTAGE, idn);
+        idn = ids_of(st + NSTAGE);
         const int k0 = (jb0 + 2 * st) * kBS;
         if (tile_ok && k0 < w_hi && k0 + 2 * kBS > w_lo) {
           if (k0 + 2 * kBS > n_lo || k0 < lo_hi) step(std::true_type{}, buf, k0, none);
