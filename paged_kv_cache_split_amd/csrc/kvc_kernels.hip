@@ -1882,6 +1882,9 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
     }
     l += (((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]))) +
          (((pv[8] + pv[9]) + (pv[10] + pv[11])) + ((pv[12] + pv[13]) + (pv[14] + pv[15])));
+    // the PV products at raised wave priority: the SIMD's other wave (another
+    // work-group) does its softmax meanwhile (measured ~2% faster)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       float w[8];
@@ -1925,6 +1928,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
         if constexpr (KVC_FLASH_P_LO) acc[od] = mfma32<KV>(vop, pl, acc[od]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // One step's tiles straight into LDS stage stg: load i of thread tid
