@@ -88,3 +88,20 @@ def test_options_the_mode_rejects():
     assert kvc.decode_workspace_bytes(2, 8, 2, 128, 100, shared_prefix=40) == 0
     assert kvc.decode_workspace_bytes(2, 8, 2, 128, 100, shared_prefix=64) > \
         kvc.decode_workspace_bytes(2, 8, 2, 128, 100)
+
+
+def test_layers_of_a_multi_layer_pool():
+    # the prefix pass and the own-rows decode read the requested layer's tiles
+    import dataclasses
+    lens = [96 + x for x in (1, 17, 40, 0, 65)]
+    wl = dataclasses.replace(custom_workload(len(lens), 16, 4, 128, "bf16", lens, seed=41, shared_prefix=96,
+                                             name="cascade layers"), num_layers=3)
+    _say(f"[cascade] {wl.num_layers} layers")
+    values = make_values(wl, "cpu")
+    st = oracle_run(wl, values)
+    cache = gpu_setup(wl, values)
+    _, bt, cl = gpu_step(cache, wl, values)
+    for layer in (0, 2):
+        o = gpu_decode_again(cache, wl, values, bt, cl, kernel=2, shared_prefix=96, layer=layer)
+        torch.cuda.synchronize()
+        check_close(to_f64(o), oracle_decode(st, wl, values, layer=layer), *TOL, f"cascade layer {layer}")
