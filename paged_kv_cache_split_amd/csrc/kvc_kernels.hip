@@ -1,6 +1,9 @@
 // HIP kernels of libkvc for CDNA4 (gfx950): append into the paged pool
-// (with fp8 quantisation), copy-on-write block copies, the split-K paged
-// decode kernels (fp32 FMA and MFMA variants), the partial merge, and a plain
+// (with fp8 E4M3 or int8 quantisation), copy-on-write block copies, the
+// split-K paged decode (fp32 FMA kernel; matrix-core kernel walking an even
+// split of each KV head's blocks), the several-token kernels (a row split
+// like decode for few new tokens per sequence; 32x32 matrix-core tiles with
+// their K/V steps staged in LDS for many), their merges, and a plain
 // streaming copy used for bandwidth calibration.
 //
 // Pool layout (one (block, KV head) tile of block_size = 16 tokens):
@@ -15,14 +18,15 @@
 // the one just appended ("LLM推理优化实战：从KV-Cache到Continuous Batching…" §1.1;
 // "苦猿的大模型日记 · Day45 · 大模型推理加速" PART 02); query head h reads KV head
 // h / G ("大模型推理加速核心KV Cache 复用机制与内存布局优化" §二); rows are reached
-// through a per-sequence block table (same page §三).  Each work-group covers
-// one (KV partition, KV head, sequence); inside it the rows are consumed 16
-// at a time with the online-softmax recurrence (running max m, sum l and
-// accumulator rescaled by exp(m_old - m_new), "LLM推理优化实战…" §3.2), and the
-// per-partition (m, l, acc) triples are merged exactly by a second kernel
-// (the "merge between blocks" of "大模型推理加速核心KV Cache…" §四).  Scores are
-// kept in the base-2 domain (scale * log2(e) folded in), which leaves the
-// softmax unchanged.
+// through a per-sequence block table (same page §三).  The rows are consumed
+// 16 (or 32) at a time with the online-softmax recurrence (running max m, sum
+// l and accumulator rescaled by exp(m_old - m_new), "LLM推理优化实战…" §3.2),
+// each piece of a sequence's rows leaving a (m, l, acc) triple that a second
+// kernel merges exactly (the "merge between blocks" of "大模型推理加速核心KV
+// Cache…" §四).  Scores are kept in the base-2 domain (scale * log2(e) folded
+// in), which leaves the softmax unchanged.  Options: a sliding window (each
+// token sees the window's rows ending at its own), and a shared prefix
+// attended once for the whole batch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
