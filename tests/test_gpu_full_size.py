@@ -5,7 +5,9 @@ The whole batch runs on the GPU; the oracle checks sampled sequences one by
 one (first, last, shortest, longest): its own single-sequence store replays
 that sequence's writes (history in one append, then the new token) and the
 fp64 decode runs on the stored values.  Block tables of every sequence are
-checked bit-exactly against the oracle's allocator model.
+checked bit-exactly against the oracle's allocator model.  The workload with a
+shared prefix is also decoded with the prefix attended once for the batch and
+checked on the same samples.
 """
 import sys
 
@@ -74,6 +76,12 @@ def test_full_size_sampled(cid):
     pools = read_pools(cache)
     q = to_f64(values["q"])
     got_all = to_f64(out)
+    got_sp = None
+    if wl.shared_prefix:   # the same step with the shared prefix attended once for the batch
+        o_sp = cache.decode(values["q"].contiguous(), bt, cl, wl.max_context_len, wl.scale, kernel=2,
+                            shared_prefix=wl.shared_prefix)
+        torch.cuda.synchronize()
+        got_sp = to_f64(o_sp)
     for b in sample:
         st = _oracle_single(wl, values, b)
         # stored rows of b, bit-exact, through its exported table
@@ -88,6 +96,9 @@ def test_full_size_sampled(cid):
         ref = decode_attention(q[b], k, v, wl.scale)
         ma, mr = check_close(got_all[b], ref, 2e-3, 1e-2, f"config {cid} seq {b}")
         msg = f"  seq {b} (L={int(L[b])}): max_abs {ma:.2e} max_rel {mr:.2e}"
+        if got_sp is not None:
+            ma3, _ = check_close(got_sp[b], ref, 2e-3, 1e-2, f"config {cid} seq {b} shared prefix")
+            msg += f"; shared prefix max_abs {ma3:.2e}"
         if wl.kv_dtype in ("fp8", "int8"):
             ku, vu = logical_history(wl, values, b)
             ma2, _ = check_close(got_all[b], decode_attention(q[b], ku, vu, wl.scale), 5e-2, 1e-2,
