@@ -209,6 +209,18 @@ kvc_status kvc_reserve_host(kvc_cache* cache, int32_t batch, const int64_t* seq_
 kvc_status kvc_get_table(const kvc_cache* cache, int64_t seq_id, int32_t* blocks_out, int32_t max_blocks,
                          int32_t* num_blocks, int32_t* length);
 kvc_status kvc_stats(const kvc_cache* cache, kvc_stats_t* out);
+/* The shared-prefix decode's preconditions (kvc_decode_opts.shared_prefix),
+ * checked on the tables the handle owns: every one of the batch sequences
+ * seq_ids (host, [batch]) exists, holds more than prefix_tokens tokens, and
+ * starts with the same prefix_tokens / block_size physical blocks as
+ * seq_ids[0] (as after kvc_fork of a prefix_tokens-token sequence, before any
+ * write into those blocks), none of them released.  prefix_tokens must be a
+ * positive multiple of block_size.  KVC_OK, KVC_E_NO_SEQ, or KVC_E_INVALID
+ * naming the first sequence that breaks a condition.  Requests under one
+ * system prompt share its physical blocks ("大模型推理加速核心KV Cache 复用机制与
+ * 内存布局优化" §三). */
+kvc_status kvc_check_shared_prefix(const kvc_cache* cache, int32_t batch, const int64_t* seq_ids,
+                                   int32_t prefix_tokens);
 
 /* ---- device work (asynchronous on `stream`) ------------------------------ */
 
@@ -270,8 +282,13 @@ typedef struct kvc_decode_opts {
                                are merged: a cascade split at the fork point, for requests that share one
                                system prompt's physical blocks ("大模型推理加速核心KV Cache 复用机制与内存
                                布局优化" §三; "苦猿的大模型日记 · Day45 · 大模型推理加速" PART 02).  Needs
-                               window 0 and no pool; other fields as for decode.  A batch that breaks
-                               these conditions gets meaningless outputs (nothing faults). */
+                               window 0 and no pool; other fields as for decode.  A sequence whose table
+                               does not start with sequence 0's P / block_size block ids, or that holds
+                               no row past the prefix, gets NaN outputs (nothing faults); seq_ids below
+                               turns such a batch into KVC_E_INVALID before any launch. */
+  const int64_t* seq_ids;   /* host, optional, [batch]: the cache's ids of the batch's rows (the order of
+                               kvc_export_tables).  With shared_prefix > 0 the decode first runs
+                               kvc_check_shared_prefix on them and fails as it does; ignored otherwise. */
 } kvc_decode_opts;
 
 /* Workspace bytes kvc_decode_attention needs for this shape (the split

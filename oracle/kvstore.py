@@ -127,17 +127,17 @@ class KVStoreModel:
         (dequantised for fp8 and int8): ([n, Hkv, D], [n, Hkv, D]).  Positions before
         ``start`` (released by eviction, say) are returned as zeros."""
         n = self.tables.lens[seq]
-        table = self.tables.tables[seq]
+        table = np.asarray(self.tables.tables[seq], dtype=np.int64)
         ks = np.zeros((n, self.H, self.D))
         vs = np.zeros((n, self.H, self.D))
-        for p in range(start, n):
-            blk, off = table[p // self.bs], p % self.bs
-            assert blk >= 0, "position inside a released block"
-            if self.kv_dtype in QUANTISED:
-                dec = e4m3.decode_array if self.kv_dtype == "fp8" else int8_policy.decode_array
-                ks[p] = dec(self.k[blk, layer, :, off, :]) * self.k_scale[blk, layer, :, None].astype(np.float64)
-                vs[p] = dec(self.v[blk, layer, :, off, :]) * self.v_scale[blk, layer, :, None].astype(np.float64)
-            else:
-                ks[p] = bits_to_f64(self.k[blk, layer, :, off, :], self.kv_dtype)
-                vs[p] = bits_to_f64(self.v[blk, layer, :, off, :], self.kv_dtype)
+        pos = np.arange(start, n)
+        blk, off = table[pos // self.bs], pos % self.bs      # the slot of every position
+        assert np.all(blk >= 0), "position inside a released block"
+        if self.kv_dtype in QUANTISED:
+            dec = e4m3.decode_array if self.kv_dtype == "fp8" else int8_policy.decode_array
+            ks[start:] = dec(self.k[blk, layer, :, off, :]) * self.k_scale[blk, layer, :, None].astype(np.float64)
+            vs[start:] = dec(self.v[blk, layer, :, off, :]) * self.v_scale[blk, layer, :, None].astype(np.float64)
+        else:
+            ks[start:] = bits_to_f64(self.k[blk, layer, :, off, :], self.kv_dtype)
+            vs[start:] = bits_to_f64(self.v[blk, layer, :, off, :], self.kv_dtype)
         return ks, vs

@@ -32,7 +32,7 @@ SYMBOLS = [
     "kvc_bytes_per_token", "kvc_pool_bytes", "kvc_scale_bytes", "kvc_scratch_bytes", "kvc_create", "kvc_destroy",
     "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_truncate_many", "kvc_evict",
     "kvc_reserve_host",
-    "kvc_get_table", "kvc_stats", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
+    "kvc_get_table", "kvc_stats", "kvc_check_shared_prefix", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
     "kvc_decode_attention", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_sched_create",
     "kvc_sched_destroy", "kvc_sched_submit", "kvc_sched_plan", "kvc_sched_commit", "kvc_sched_get_stats",
     "kvc_stream_copy", "kvc_last_error",
@@ -68,7 +68,8 @@ class KvcDecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("work_items", ctypes.c_int32),
                 ("pool_pieces", ctypes.c_int32), ("pool_shift", ctypes.c_int32),
                 ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p), ("window", ctypes.c_int32),
-                ("tiles_per_wave", ctypes.c_int32), ("shared_prefix", ctypes.c_int32)]
+                ("tiles_per_wave", ctypes.c_int32), ("shared_prefix", ctypes.c_int32),
+                ("seq_ids", ctypes.POINTER(ctypes.c_int64))]
 
 
 _i32, _i64, _sz, _vp, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -91,6 +92,7 @@ _sig = {
     "kvc_reserve_host": (ctypes.c_int, [_vp, _i32, _P64, _P32, _P32, _P32, _P32, _i32, _P32]),
     "kvc_get_table": (ctypes.c_int, [_vp, _i64, _P32, _i32, _P32, _P32]),
     "kvc_stats": (ctypes.c_int, [_vp, ctypes.POINTER(KvcStats)]),
+    "kvc_check_shared_prefix": (ctypes.c_int, [_vp, _i32, _P64, _i32]),
     "kvc_append": (ctypes.c_int, [_vp, _i32, _P64, _P32, _vp, _vp, ctypes.c_int, _vp]),
     "kvc_export_tables": (ctypes.c_int, [_vp, _i32, _P64, _vp, _i32, _vp, _vp]),
     "kvc_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
@@ -296,6 +298,12 @@ class KVCache:
                                   ctypes.byref(ln)), "kvc_get_table")
         return out[:nb.value].tolist(), ln.value
 
+    def check_shared_prefix(self, seq_ids, prefix_tokens):
+        """Raise KvcError unless every sequence holds more than prefix_tokens
+        tokens and starts with seq_ids[0]'s first prefix_tokens / block_size blocks."""
+        ids, pids = _i64_array(seq_ids)
+        _check(_lib.kvc_check_shared_prefix(self._h, len(ids), pids, int(prefix_tokens)), "kvc_check_shared_prefix")
+
     def stats(self) -> dict:
         st = KvcStats()
         _check(_lib.kvc_stats(self._h, ctypes.byref(st)), "kvc_stats")
@@ -341,17 +349,22 @@ class KVCache:
 
     def decode(self, q, block_table, context_lens, max_context_len, scale, layer=0, out=None, workspace=None,
                partition_tokens=0, kernel=0, work_items=0, pool_pieces=0, pool_shift=0, split_events=None,
-               stream=None, window=0, shared_prefix=0):
+               stream=None, window=0, shared_prefix=0, seq_ids=None):
         """Decode attention for one layer.  q: [B, Hq, D] device tensor.
         ``window`` > 0: each token sees at most that many rows ending at its own.
         ``shared_prefix`` > 0: the first that many tokens of every sequence are one
-        shared prefix, attended once for the batch (the cascade split)."""
+        shared prefix, attended once for the batch (the cascade split);
+        ``seq_ids`` (the batch's sequence ids) has the library check that first."""
         import torch
         B, Hq, D = q.shape
         if not q.is_contiguous():
             raise ValueError("q must be contiguous")
         opts = KvcDecodeOpts(int(partition_tokens), int(kernel), int(work_items), int(pool_pieces), int(pool_shift),
                              None, None, int(window), 0, int(shared_prefix))
+        if seq_ids is not None:
+            ids_arr, opts.seq_ids = _i64_array(seq_ids)
+            if len(ids_arr) != B:
+                raise ValueError("seq_ids must name one sequence per row of q")
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event

@@ -437,6 +437,38 @@ size_t workspace_bytes_for(int32_t batch, int32_t num_heads, int32_t num_kv_head
   return kvc::workspace_layout(p, batch, num_heads, num_kv_heads, head_dim).bytes;
 }
 
+// The shared-prefix decode's preconditions, from the tables the handle owns:
+// every listed sequence exists, holds more than prefix_tokens tokens, and its
+// first prefix_tokens / block_size table entries are the first sequence's.
+// The caller holds the handle's lock.
+kvc_status check_prefix_tables(kvc_cache* c, int32_t batch, const int64_t* seq_ids, int32_t prefix_tokens) {
+  const int32_t bs = c->cfg.block_size;
+  if (batch < 1 || !seq_ids) return fail(KVC_E_INVALID, "shared prefix check: batch >= 1 and seq_ids needed");
+  if (prefix_tokens <= 0 || prefix_tokens % bs != 0)
+    return fail(KVC_E_INVALID, "shared prefix %d is not a positive multiple of the block size", prefix_tokens);
+  const int32_t nb = prefix_tokens / bs;
+  const kvc_cache::Seq* first = nullptr;
+  for (int32_t i = 0; i < batch; ++i) {
+    auto it = c->seqs.find(seq_ids[i]);
+    if (it == c->seqs.end()) return fail(KVC_E_NO_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    const kvc_cache::Seq& s = it->second;
+    if (s.len <= prefix_tokens)
+      return fail(KVC_E_INVALID, "sequence %lld holds %d tokens, not more than the shared prefix %d",
+                  (long long)seq_ids[i], s.len, prefix_tokens);
+    if (!first) {
+      first = &s;
+      for (int32_t j = 0; j < nb; ++j)
+        if (s.blocks[j] < 0)
+          return fail(KVC_E_INVALID, "sequence %lld released block %d of the prefix", (long long)seq_ids[i], j);
+      continue;
+    }
+    if (!std::equal(s.blocks.begin(), s.blocks.begin() + nb, first->blocks.begin()))
+      return fail(KVC_E_INVALID, "sequence %lld does not share the first %d blocks of sequence %lld",
+                  (long long)seq_ids[i], nb, (long long)seq_ids[0]);
+  }
+  return KVC_OK;
+}
+
 }  // namespace
 
 namespace kvc {
@@ -670,6 +702,14 @@ kvc_status kvc_get_table(const kvc_cache* cc, int64_t seq_id, int32_t* blocks_ou
   return ok();
 }
 
+kvc_status kvc_check_shared_prefix(const kvc_cache* cc, int32_t batch, const int64_t* seq_ids,
+                                   int32_t prefix_tokens) {
+  kvc_cache* c = const_cast<kvc_cache*>(cc);
+  if (!c) return fail(KVC_E_INVALID, "cache is NULL");
+  std::lock_guard<std::mutex> lock(c->mu);
+  return check_prefix_tables(c, batch, seq_ids, prefix_tokens);
+}
+
 kvc_status kvc_stats(const kvc_cache* cc, kvc_stats_t* out) {
   kvc_cache* c = const_cast<kvc_cache*>(cc);
   if (!c || !out) return fail(KVC_E_INVALID, "cache and out must be non-NULL");
@@ -887,6 +927,11 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
       return fail(KVC_E_INVALID,
                   "shared_prefix must be a positive multiple of the block size below the table length, with "
                   "the MFMA kernel, window 0 and no pool");
+    if (opts->seq_ids) {
+      std::lock_guard<std::mutex> lock(c->mu);
+      kvc_status pst = check_prefix_tables(c, batch, opts->seq_ids, P);
+      if (pst != KVC_OK) return pst;
+    }
   }
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
   if (need > 0 && (!workspace || workspace_bytes < need))

@@ -2128,6 +2128,17 @@ __global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
   const int t = threadIdx.x;
   constexpr int COLS = D / 4;
   const int hh = t / COLS, c = t % COLS;
+  // Shared-prefix decode: the prefix pass read sequence 0's first skip_blocks
+  // blocks for every sequence, which is its answer only if this sequence's
+  // table starts with the same blocks and it holds rows past them; otherwise
+  // its outputs are NaN.  (Every thread takes part: before any return.)
+  bool bad_prefix = false;
+  if (!EXT && a.pre_pieces > 0) {
+    bool bad = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks) <= a.skip_blocks * kBS;
+    const int32_t* row_b = a.block_table + (int64_t)b * a.max_blocks;
+    for (int i = t; i < a.skip_blocks; i += (int)blockDim.x) bad |= row_b[i] != a.block_table[i];
+    bad_prefix = __syncthreads_or(bad);
+  }
   if (hh >= a.group) return;
   const int n = attend_len(a.context_lens, b, a.max_ctx, a.max_blocks);
   if (n <= 0) return;
@@ -2185,7 +2196,7 @@ __global__ __launch_bounds__(512) void merge_segments_kernel(DecodeArgs a) {
     L = L * sa + l * sb;
     M = Mn;
   }
-  const float inv = 1.0f / L;
+  const float inv = bad_prefix ? __builtin_nanf("") : 1.0f / L;
   const int64_t o = ((int64_t)q_row * a.num_heads + h) * D + 4 * c;
 #pragma unroll
   for (int e = 0; e < 4; ++e) store_out<QT>(a.out, o + e, acc[e] * inv);

@@ -83,22 +83,72 @@ def gpu_setup(wl, values, device="cuda", pool_fill=None):
     return cache
 
 
+POISON_BYTE = 0xFF   # as float32 a NaN, as int32 -1
+
+
+def poisoned_buffers(cache, q, max_context_len, **opts):
+    """A decode workspace and an output filled with 0xFF bytes: a partial,
+    chunk record or output the kernels read or leave without having written
+    it turns into NaN (or an out-of-range chunk index) in one run."""
+    from paged_kv_cache_split_amd import decode_workspace_bytes
+    B, Hq, D = q.shape
+    keys = ("partition_tokens", "kernel", "work_items", "pool_pieces", "pool_shift", "shared_prefix")
+    need = decode_workspace_bytes(B, Hq, cache.num_kv_heads, D, int(max_context_len),
+                                  **{k: int(v) for k, v in opts.items() if k in keys})
+    ws = torch.full((max(need, 256),), POISON_BYTE, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    out.view(torch.uint8).fill_(POISON_BYTE)
+    return ws, out
+
+
+def decode_poisoned(cache, q, block_table, context_lens, max_context_len, scale, **kw):
+    """cache.decode into a poisoned workspace and output (unless given)."""
+    ws, out = poisoned_buffers(cache, q, max_context_len, **kw)
+    kw.setdefault("workspace", ws)
+    kw.setdefault("out", out)
+    return cache.decode(q, block_table, context_lens, max_context_len, scale, **kw)
+
+
+def extend_poisoned(cache, q, query_start, max_query_len, block_table, context_lens, max_context_len, scale, **kw):
+    """cache.extend into a workspace and an output filled with 0xFF bytes."""
+    from paged_kv_cache_split_amd import extend_workspace_bytes
+    T, Hq, D = q.shape
+    B = int(context_lens.shape[0])
+    need = extend_workspace_bytes(B, Hq, cache.num_kv_heads, D, int(max_query_len), int(max_context_len),
+                                  work_items=int(kw.get("work_items", 0)),
+                                  tiles_per_wave=int(kw.get("tiles_per_wave", 0)), kernel=int(kw.get("kernel", 0)))
+    if "workspace" not in kw:
+        kw["workspace"] = torch.full((max(need, 256),), POISON_BYTE, dtype=torch.uint8, device=q.device)
+    if "out" not in kw:
+        out = torch.empty_like(q)
+        out.view(torch.uint8).fill_(POISON_BYTE)
+        kw["out"] = out
+    return cache.extend(q, query_start, max_query_len, block_table, context_lens, max_context_len, scale, **kw)
+
+
 def gpu_step(cache, wl, values, kernel=0, partition_tokens=0, device="cuda", out=None, work_items=0, **split):
-    """The decode step: append each sequence's new token, export tables, decode.
-    ``split``: pool_pieces / pool_shift of the MFMA kernel."""
+    """The decode step: append each sequence's new token, export tables, decode
+    (into a poisoned workspace and output).  ``split``: pool_pieces /
+    pool_shift of the MFMA kernel."""
     seqs = list(range(wl.batch))
     cache.append(seqs, values["k_new"].to(device).contiguous(), values["v_new"].to(device).contiguous())
     bt, cl = cache.export_tables(seqs)
     q = values["q"].to(device).contiguous()
+    ws, out_p = poisoned_buffers(cache, q, wl.max_context_len, kernel=kernel, partition_tokens=partition_tokens,
+                                 work_items=work_items, **split)
     o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
-                     out=out, work_items=work_items, window=wl.window, **split)
+                     out=out_p if out is None else out, workspace=ws, work_items=work_items, window=wl.window,
+                     **split)
     return o, bt, cl
 
 
 def gpu_decode_again(cache, wl, values, bt, cl, kernel=0, partition_tokens=0, device="cuda", work_items=0, **split):
+    """Decode again on the same tables, into a poisoned workspace and output."""
     q = values["q"].to(device).contiguous()
+    ws, out = poisoned_buffers(cache, q, wl.max_context_len, kernel=kernel, partition_tokens=partition_tokens,
+                               work_items=work_items, **split)
     return cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=partition_tokens,
-                        work_items=work_items, window=wl.window, **split)
+                        work_items=work_items, window=wl.window, out=out, workspace=ws, **split)
 
 
 # -- oracle side ------------------------------------------------------------------
@@ -161,7 +211,7 @@ def gpu_extend_step(cache, wl, values, device="cuda", work_items=0):
     bt, cl = cache.export_tables(seqs)
     qs = torch.from_numpy(query_start(wl)).to(device)
     q = values["q"].to(device).contiguous()
-    o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=work_items,
+    o = extend_poisoned(cache, q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=work_items,
                      window=wl.window)
     return o, bt, cl, qs
 

@@ -20,7 +20,8 @@ import torch
 
 import paged_kv_cache_split_amd as kvc
 from conftest import gpu_available
-from harness import check_close, gpu_decode_again, gpu_setup, gpu_step, oracle_decode, oracle_run, to_f64
+from harness import (check_close, decode_poisoned, gpu_decode_again, gpu_setup, gpu_step, oracle_decode, oracle_run,
+                     to_f64)
 from workloads import custom_workload, make_values, make_workload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -84,7 +85,7 @@ def test_options_the_mode_rejects():
                 dict(shared_prefix=64, kernel=1), dict(shared_prefix=64, pool_pieces=2),
                 dict(shared_prefix=16 * bt.shape[1])):
         with pytest.raises(kvc.KvcError):
-            cache.decode(q, bt, cl, wl.max_context_len, wl.scale, **bad)
+            decode_poisoned(cache, q, bt, cl, wl.max_context_len, wl.scale, **bad)
     assert kvc.decode_workspace_bytes(2, 8, 2, 128, 100, shared_prefix=40) == 0
     assert kvc.decode_workspace_bytes(2, 8, 2, 128, 100, shared_prefix=64) > \
         kvc.decode_workspace_bytes(2, 8, 2, 128, 100)
@@ -105,3 +106,37 @@ def test_layers_of_a_multi_layer_pool():
         o = gpu_decode_again(cache, wl, values, bt, cl, kernel=2, shared_prefix=96, layer=layer)
         torch.cuda.synchronize()
         check_close(to_f64(o), oracle_decode(st, wl, values, layer=layer), *TOL, f"cascade layer {layer}")
+
+
+def test_batch_breaking_the_prefix_conditions():
+    # sequences 0-2 share a 64-token prefix; sequence 10 has its own blocks.
+    # Decoding [0, 1, 10] with shared_prefix = 64 gives sequence 10 NaN rows
+    # (its table does not start with the prefix blocks) and the others their
+    # plain decode; with seq_ids the library refuses the batch before launch.
+    lens = [64 + 5, 64 + 20, 64 + 30]
+    wl = custom_workload(len(lens), 8, 2, 128, "bf16", lens, seed=12, shared_prefix=64, name="cascade misuse")
+    wl.num_blocks += 8
+    wl.free_order = np.random.default_rng(3).permutation(wl.num_blocks).astype(np.int32)
+    values = make_values(wl, "cpu")
+    cache = gpu_setup(wl, values)
+    gen = torch.Generator().manual_seed(5)
+    rows = torch.randn((1, 100, 2, 128), generator=gen).to(torch.bfloat16).cuda()
+    cache.add_seq(10, 0)
+    cache.append([10], rows, rows.flip(1).contiguous(), n_new=[100])
+    seqs = [0, 1, 10]
+    new = torch.randn((1, 3, 2, 128), generator=gen).to(torch.bfloat16).cuda()
+    cache.append(seqs, new, new.neg().contiguous())
+    bt, cl = cache.export_tables(seqs)
+    q = torch.randn((3, 8, 128), generator=gen).to(torch.bfloat16).cuda()
+    plain = decode_poisoned(cache, q, bt, cl, int(cl.max()), wl.scale, kernel=2)
+    casc = decode_poisoned(cache, q, bt, cl, int(cl.max()), wl.scale, kernel=2, shared_prefix=64)
+    torch.cuda.synchronize()
+    check_close(to_f64(casc[:2]), to_f64(plain[:2]), 4e-3, 2e-2, "sequences that share the prefix")
+    assert torch.isnan(casc[2].float()).all(), "a sequence outside the prefix must get NaN rows"
+    with pytest.raises(kvc.KvcError) as e:
+        decode_poisoned(cache, q, bt, cl, int(cl.max()), wl.scale, kernel=2, shared_prefix=64, seq_ids=seqs)
+    assert "does not share" in str(e.value)
+    ok = decode_poisoned(cache, q[:2].contiguous(), bt[:2].contiguous(), cl[:2].contiguous(), int(cl.max()),
+                         wl.scale, kernel=2, shared_prefix=64, seq_ids=[0, 1])
+    torch.cuda.synchronize()
+    check_close(to_f64(ok), to_f64(plain[:2]), 4e-3, 2e-2, "checked batch")

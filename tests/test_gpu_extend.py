@@ -20,8 +20,8 @@ import pytest
 import torch
 
 from conftest import gpu_available
-from harness import (check_close, gpu_extend_step, gpu_setup, gpu_step, oracle_decode, oracle_extend, oracle_run,
-                     query_start, read_pools, to_bits, to_f64, _history_rows)
+from harness import (check_close, decode_poisoned, extend_poisoned, gpu_extend_step, gpu_setup, gpu_step, oracle_decode,
+                     oracle_extend, oracle_run, query_start, read_pools, to_bits, to_f64, _history_rows)
 from workloads import custom_workload, make_extend_workload, make_values
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -57,7 +57,7 @@ def test_small_extend_workloads(kind):
     check_close(to_f64(out), ref, *TOL, f"extend {kind}")
     q = values["q"].cuda().contiguous()
     for kernel in (2, 3):
-        o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, kernel=kernel)
+        o = extend_poisoned(cache, q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, kernel=kernel)
         torch.cuda.synchronize()
         check_close(to_f64(o), ref, *TOL, f"extend {kind} kernel {kernel}")
 
@@ -84,14 +84,14 @@ def test_ragged_query_counts(kv, hq, hkv, d):
     # leave empty partials that the merge must skip
     q = values["q"].cuda().contiguous()
     for wi, tpw in ((2, 0), (7, 0), (64, 0), (0, 1), (5, 2), (3, 3), (9, 4)):
-        o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi,
+        o = extend_poisoned(cache, q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi,
                          tiles_per_wave=tpw, kernel=2)
         torch.cuda.synchronize()
         check_close(to_f64(o), ref, *TOL, f"ragged {hq}/{hkv} D{d} {kv} work_items {wi} tiles/wave {tpw}")
     # one wave per 32 (token, head) columns over all their rows: tiles with
     # padding columns, tokens of one column tile in several sequences' worth of
     # heads, an odd number of blocks
-    o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, kernel=3)
+    o = extend_poisoned(cache, q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, kernel=3)
     torch.cuda.synchronize()
     check_close(to_f64(o), ref, *TOL, f"ragged {hq}/{hkv} D{d} {kv} kernel 3")
 
@@ -104,7 +104,7 @@ def test_one_token_per_sequence_matches_decode_bitwise(kv):
     cache = gpu_setup(wl, values)
     dec, bt, cl = gpu_step(cache, wl, values, work_items=100)
     qs = torch.arange(wl.batch + 1, dtype=torch.int32, device="cuda")
-    ext = cache.extend(values["q"].cuda().contiguous(), qs, 1, bt, cl, wl.max_context_len, wl.scale, work_items=100)
+    ext = extend_poisoned(cache, values["q"].cuda().contiguous(), qs, 1, bt, cl, wl.max_context_len, wl.scale, work_items=100)
     torch.cuda.synchronize()
     assert torch.equal(dec.view(torch.int16), ext.view(torch.int16))
 
@@ -124,7 +124,7 @@ def test_unwritten_slots_holding_nan(kv):
     torch.cuda.synchronize()
     ref = oracle_decode(st, wl, values)
     for kernel in ([1] if kv == "f32" else [1, 2]):
-        o = cache.decode(values["q"].cuda().contiguous(), bt, cl, wl.max_context_len, wl.scale, kernel=kernel,
+        o = decode_poisoned(cache, values["q"].cuda().contiguous(), bt, cl, wl.max_context_len, wl.scale, kernel=kernel,
                          partition_tokens=32)
         torch.cuda.synchronize()
         assert torch.isfinite(o.float()).all(), f"kernel {kernel}: NaN from unused slots"

@@ -1,13 +1,15 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (automatic partition size and kernel choice).
 
-The whole batch runs on the GPU; the oracle checks sampled sequences one by
-one (first, last, shortest, longest): its own single-sequence store replays
-that sequence's writes (history in one append, then the new token) and the
-fp64 decode runs on the stored values.  Block tables of every sequence are
-checked bit-exactly against the oracle's allocator model.  The workload with a
-shared prefix is also decoded with the prefix attended once for the batch and
-checked on the same samples.
+The whole batch runs on the GPU; the oracle checks every sequence of
+configs 2-4 and 16 sequences of config 5 (first, last, shortest, longest and
+twelve spread over the batch; most of them straddle a boundary between two
+waves' chunks in the launch the benchmark times) one by one: its own
+single-sequence store replays that sequence's writes (history in one append,
+then the new token) and the fp64 decode runs on the stored values.  Block
+tables of every sequence are checked bit-exactly against the oracle's
+allocator model.  The workload with a shared prefix is also decoded with the
+prefix attended once for the batch and checked on the same sequences.
 """
 import sys
 
@@ -16,7 +18,8 @@ import pytest
 import torch
 
 from conftest import gpu_available
-from harness import (check_close, gpu_setup, gpu_step, logical_history, read_pools, to_bits, to_f64, _history_rows)
+from harness import (check_close, decode_poisoned, gpu_setup, gpu_step, logical_history, read_pools, to_bits, to_f64,
+                     _history_rows)
 from workloads import make_values, make_workload, setup_ops
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -46,8 +49,18 @@ def _oracle_single(wl, values, b):
     return st
 
 
+def _straddlers(wl, W):
+    """Sequences whose blocks fall in more than one chunk of the even split of
+    the batch's blocks over W waves per KV head."""
+    from score_walk import decode_chunks
+    seen = {}
+    for b, _, _ in decode_chunks(wl.attend_lens, W):
+        seen[b] = seen.get(b, 0) + 1
+    return {b for b, c in seen.items() if c > 1}
+
+
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
-def test_full_size_sampled(cid):
+def test_full_size_every_sequence(cid):
     from oracle.attention import decode_attention
     from oracle.blocktable import BlockTableModel
     wl = make_workload(cid)
@@ -70,15 +83,23 @@ def test_full_size_sampled(cid):
     rows, lens = model.export(list(range(wl.batch)), bt.shape[1])
     assert np.array_equal(bt.cpu().numpy(), np.array(rows, dtype=np.int32))
     assert np.array_equal(cl.cpu().numpy(), np.array(lens, dtype=np.int32))
-    # sampled sequences
+    # every sequence (config 5: 16 of them)
     L = wl.context_lens
-    sample = sorted({0, wl.batch - 1, int(np.argmin(L)), int(np.argmax(L))})
+    if cid == 5:
+        spread = np.linspace(1, wl.batch - 2, 12).astype(int).tolist()
+        sample = sorted({0, wl.batch - 1, int(np.argmin(L)), int(np.argmax(L))} | set(spread))
+    else:
+        sample = list(range(wl.batch))
+    straddle = _straddlers(wl, 1024 // wl.num_kv_heads) & set(sample)
+    _say(f"  checking {len(sample)} sequences, {len(straddle)} of them across a chunk boundary")
+    if cid in (3, 5):
+        assert len(straddle) >= 8
     pools = read_pools(cache)
     q = to_f64(values["q"])
     got_all = to_f64(out)
     got_sp = None
     if wl.shared_prefix:   # the same step with the shared prefix attended once for the batch
-        o_sp = cache.decode(values["q"].contiguous(), bt, cl, wl.max_context_len, wl.scale, kernel=2,
+        o_sp = decode_poisoned(cache, values["q"].contiguous(), bt, cl, wl.max_context_len, wl.scale, kernel=2,
                             shared_prefix=wl.shared_prefix)
         torch.cuda.synchronize()
         got_sp = to_f64(o_sp)

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from conftest import gpu_available
-from harness import check_close, read_pools, to_bits, to_f64
+from harness import check_close, extend_poisoned, read_pools, to_bits, to_f64
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -72,7 +72,7 @@ def test_scheduled_lifecycle_multi_layer(kv):
         bt, cl = cache.export_tables(ids)
         qs = torch.tensor(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32), device="cuda")
         qd = q_rows.cuda()
-        outs = [cache.extend(qd, qs, max(n_new), bt, cl, int(cl.max().item()), scale, layer=layer)
+        outs = [extend_poisoned(cache, qd, qs, max(n_new), bt, cl, int(cl.max().item()), scale, layer=layer)
                 for layer in range(L)]
         torch.cuda.synchronize()
         for layer in range(L):

@@ -15,8 +15,8 @@ import pytest
 import torch
 
 from conftest import gpu_available
-from harness import (check_close, gpu_decode_again, gpu_setup, gpu_step, logical_history, oracle_decode, oracle_run,
-                     read_pools, to_f64)
+from harness import (check_close, decode_poisoned, gpu_decode_again, gpu_setup, gpu_step, logical_history,
+                     oracle_decode, oracle_run, read_pools, to_f64)
 from workloads import custom_workload, make_values, make_workload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -246,7 +246,7 @@ def test_multi_layer_pool_and_cow(kv):
         ref = oracle_decode(st, wl, values, layer=layer)
         for kernel in _kernels_for(wl):
             q = values["q"].to("cuda").contiguous()
-            o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, layer=layer, kernel=kernel,
+            o = decode_poisoned(cache, q, bt, cl, wl.max_context_len, wl.scale, layer=layer, kernel=kernel,
                              partition_tokens=32, work_items=3)
             check_close(to_f64(o), ref, *TOL[kv], f"{kv} layer {layer} kernel {kernel}")
 
@@ -262,9 +262,9 @@ def test_decode_rejects_negative_or_infinite_scale():
     q = values["q"].to("cuda").contiguous()
     for bad in (-0.125, float("inf"), float("nan")):
         with pytest.raises(KvcError):
-            cache.decode(q, bt, cl, wl.max_context_len, bad)
+            decode_poisoned(cache, q, bt, cl, wl.max_context_len, bad)
     # scale 0 is allowed: every weight is equal, the output is the mean of V
-    z = cache.decode(q, bt, cl, wl.max_context_len, 0.0)
+    z = decode_poisoned(cache, q, bt, cl, wl.max_context_len, 0.0)
     torch.cuda.synchronize()
     start = 0
     for b, n in enumerate(lens):

@@ -19,8 +19,8 @@ import pytest
 import torch
 
 from conftest import gpu_available
-from harness import (check_close, gpu_decode_again, gpu_extend_step, gpu_setup, gpu_step, oracle_decode,
-                     oracle_extend, oracle_run, read_pools, to_f64)
+from harness import (check_close, decode_poisoned, extend_poisoned, gpu_decode_again, gpu_extend_step, gpu_setup,
+                     gpu_step, oracle_decode, oracle_extend, oracle_run, read_pools, to_f64)
 from workloads import custom_workload, make_values, make_window_workload, setup_ops
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -77,11 +77,11 @@ def test_window_several_new_tokens(kv):
     check_close(to_f64(out), ref, *TOL, f"window extend {kv}")
     q = values["q"].cuda().contiguous()
     for wi, tpw in ((2, 0), (9, 0), (4, 1), (3, 2), (6, 3)):
-        o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi,
+        o = extend_poisoned(cache, q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, work_items=wi,
                          window=wl.window, tiles_per_wave=tpw, kernel=2)
         torch.cuda.synchronize()
         check_close(to_f64(o), ref, *TOL, f"window extend {kv} work_items {wi}")
-    o = cache.extend(q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, window=wl.window, kernel=3)
+    o = extend_poisoned(cache, q, qs, wl.max_query_len, bt, cl, wl.max_context_len, wl.scale, window=wl.window, kernel=3)
     torch.cuda.synchronize()
     check_close(to_f64(o), ref, *TOL, f"window extend {kv} kernel 3")
 
@@ -97,15 +97,15 @@ def test_window_limits(kv):
     q = values["q"].cuda().contiguous()
     # a window longer than every history changes nothing, bit for bit
     for kernel in (1, 2):
-        ref_k = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=32)
-        o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=32, window=258)
+        ref_k = decode_poisoned(cache, q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=32)
+        o = decode_poisoned(cache, q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=32, window=258)
         torch.cuda.synchronize()
         assert torch.equal(ref_k.view(torch.int16), o.view(torch.int16)), f"kernel {kernel}"
     # a window of one row: each token returns its own value row (dequantised)
     wl.window = 1
     ref = oracle_decode(st, wl, values)
     for kernel in (1, 2):
-        o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=32, window=1)
+        o = decode_poisoned(cache, q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=32, window=1)
         torch.cuda.synchronize()
         check_close(to_f64(o), ref, *TOL, f"window 1 kernel {kernel}")
     # assorted windows, including one ending inside a block
@@ -113,7 +113,7 @@ def test_window_limits(kv):
         wl.window = w
         ref = oracle_decode(st, wl, values)
         for kernel in (1, 2):
-            o = cache.decode(q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=32, window=w,
+            o = decode_poisoned(cache, q, bt, cl, wl.max_context_len, wl.scale, kernel=kernel, partition_tokens=32, window=w,
                              work_items=4)
             torch.cuda.synchronize()
             check_close(to_f64(o), ref, *TOL, f"window {w} kernel {kernel}")

@@ -315,3 +315,36 @@ def test_truncate_many_rolls_an_append_back_exactly():
         c.truncate_many(seqs, lens)
         again, _ = c.reserve_host(seqs)
         assert again == first and [c.get_table(s) for s in seqs] == tables
+
+
+def test_shared_prefix_check_on_the_tables():
+    # three sequences forked from one 64-token prefix (4 blocks), each then
+    # writing past it; the check passes for the prefix and any block-aligned
+    # part of it, and names what breaks it otherwise
+    c = _host_cache(64)
+    c.add_seq(0, 0)
+    c.reserve_host([0], [64])
+    c.fork(0, 1)
+    c.fork(0, 2)
+    c.reserve_host([0, 1, 2], [3, 5, 20])
+    c.add_seq(3, 0)
+    c.reserve_host([3], [100])          # its own blocks
+    c.fork(0, 4)                         # holds exactly the prefix + 3 rows, shares block 4 too
+    c.add_seq(5, 0)
+    c.fork(0, 6)
+    c.truncate(6, 64)                    # exactly the prefix: no row past it
+    c.check_shared_prefix([0, 1, 2], 64)
+    c.check_shared_prefix([2, 0, 1], 48)
+    c.check_shared_prefix([0, 4], 64)
+    for ids, p in (([0, 1, 3], 64), ([0, 1, 2], 80), ([0, 6], 64), ([0, 1], 40), ([0, 1], 0), ([5, 0], 16)):
+        with pytest.raises(kvc.KvcError) as e:
+            c.check_shared_prefix(ids, p)
+        assert e.value.status == B.E_INVALID, (ids, p)
+    with pytest.raises(kvc.KvcError) as e:
+        c.check_shared_prefix([0, 99], 64)
+    assert e.value.status == B.E_NO_SEQ
+    c.evict(1, 32)                       # releases this sequence's hold on prefix blocks 0 and 1
+    with pytest.raises(kvc.KvcError):
+        c.check_shared_prefix([1, 0], 64)
+    with pytest.raises(kvc.KvcError):
+        c.check_shared_prefix([0, 1], 64)

@@ -8,4 +8,4 @@ their inputs from it.
 """
 from .configs import (CONFIGS, EXTEND_CONFIGS, EXTEND_SMALL, SMALL, WINDOW_CONFIGS, Workload,  # noqa: F401
                       custom_workload, history_rows_of, make_extend_workload, make_request_values, make_values,
-                      make_window_workload, make_workload, setup_ops)
+                      make_window_workload, make_workload, setup_ops, shape_scores)

@@ -362,6 +362,54 @@ def make_request_values(seed: int, req_id: int, num_layers: int, length: int, nu
     return dict(k=k, v=v, q=q)
 
 
+LOG2E = 1.4426950408889634
+
+
+def shape_scores(wl: Workload, values: dict, pattern: str, strength: float = 10.0, q_dim0: float = 16.0):
+    """Reshape drawn inputs (in place) so that the scores of a decode or
+    several-token step follow a planted profile over the positions, in units
+    of log2 of a softmax weight (score * scale * log2 e):
+
+    * "ramp": every query row gets q[..., 0] = q_dim0 and key row p gets
+      k[0] = offset(p) / (scale * log2 e * q_dim0) with offset(p) = strength *
+      ((p // 16) % 24): the block maxima climb by `strength` per block for 24
+      blocks, then fall back and climb again;
+    * "sink": as "ramp" but offset(p) = strength for one key row per sequence
+      at position ~0.7 n placed mid-block (slot 7), 0 elsewhere;
+    * "qscale": every query value multiplied by `strength` (no key change).
+
+    Other values keep their N(0, 1) draws.  The step's new key rows sit at the
+    positions after the history.  Returns values (modified)."""
+    import torch
+    unit = 1.0 / (wl.scale * LOG2E * q_dim0)
+    if pattern == "qscale":
+        values["q"] = (values["q"].float() * strength).to(values["q"].dtype)
+        return values
+    if pattern not in ("ramp", "sink"):
+        raise ValueError(pattern)
+    values["q"][..., 0] = q_dim0
+    qls = wl.q_lens
+    q0 = np.concatenate([[0], np.cumsum(qls)])
+    for b in range(wl.batch):
+        L = int(wl.context_lens[b])
+        n = L + int(qls[b])
+        pos = np.arange(n)
+        if pattern == "ramp":
+            off = strength * ((pos // 16) % 24)
+        else:
+            off = np.zeros(n)
+            p_s = (int(0.7 * n) // 16) * 16 + 7
+            if p_s >= n:
+                p_s = n - 1
+            off[p_s] = strength
+        col = torch.from_numpy(off * unit).to(torch.float32)
+        rows = torch.from_numpy(history_rows_of(wl, b))
+        kh, kn = values["k_hist"], values["k_new"]
+        kh[:, rows.to(kh.device), :, 0] = col[:L, None].to(kh.dtype).to(kh.device)
+        kn[:, int(q0[b]):int(q0[b + 1]), :, 0] = col[L:, None].to(kn.dtype).to(kn.device)
+    return values
+
+
 def make_values(wl: Workload, device="cpu"):
     """Tensors of the workload, drawn on ``device`` (torch generator seeded with wl.seed).
 
