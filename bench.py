@@ -1,15 +1,23 @@
 """Benchmark one paged GQA decode step on one MI355X.
 
-A step is the whole hot path over one batch: kvc_append of every sequence's
-new K/V row (slot reservation on the host, upload of the write plan, the
-append kernel), then kvc_decode_attention (split-K kernel + merge kernel).
-The step is made repeatable by truncating every sequence back to its history
-length afterwards (host bookkeeping only, one kvc_truncate_many call), so
-every step appends into the same slots.
+A step is the whole hot path over one batch: the slot reservation of every
+sequence's new token (host bookkeeping, kvc_append without rows), then
+kvc_decode_attention with the new K/V rows, which writes them into their
+slots and attends (for 16-bit caches the split-K kernel's walk writes them
+itself; one-byte caches run the quantising append kernel first), then the
+merge kernel.  ``--append kernel`` times the two-call form instead (kvc_append
+with rows, its own kernel, then the decode).  The step is made repeatable by
+truncating every sequence back to its history length afterwards (host
+bookkeeping only, one kvc_truncate_many call), so every step appends into the
+same slots.
 
 Prints ONE JSON line: value = KV-read GB/s (distinct K/V bytes the step
 attends / step time), plus us_per_step, the split kernel's roofline (HIP
-events on the launch stream) and the fp64 CPU oracle timed on a sample.
+events on the launch stream), the fp64 CPU oracle timed on a sample, the
+plain copy kernel's bandwidth on the same box, the shader and memory clocks
+seen while the steps ran, and -- on the default run -- the same measurements
+for the other decode workloads (configs 2, 4, 4 with its shared prefix
+attended once, and 5) under "also".
 
 ``--extend verify|prefill|chunk`` times a step with several new tokens per
 sequence instead (kvc_append of all of them, then kvc_extend_attention), with
@@ -30,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged GQA decode attn: µs/step, KV-read HBM GB/s and % of MI355X peak"
+EVENT_EVERY = 4   # timed steps per HIP-event-bracketed split-kernel launch
 PEAK_HBM_GBS = 8000.0
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}
 
@@ -46,7 +55,15 @@ def parse():
     p.add_argument("--work-items", type=int, default=0, help="MFMA kernel waves per KV head (0 auto)")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--calibrate", action="store_true", help="also time the plain copy kernel (2 GiB)")
+    p.add_argument("--no-calibrate", action="store_true", help="skip timing the plain copy kernel (2 GiB)")
+    p.add_argument("--no-clocks", action="store_true", help="skip sampling the shader clock under load")
+    p.add_argument("--no-also", action="store_true",
+                   help="default run only: skip the extra workloads (configs 2, 4, 4 with the shared prefix "
+                        "attended once, 5) measured after the headline one")
+    p.add_argument("--append", choices=["fold", "kernel"], default="fold",
+                   help="decode step's append: 'fold' = slots reserved without rows, the rows handed to the "
+                        "decode (written by the decode walk itself for 16-bit caches); 'kernel' = kvc_append "
+                        "with rows (its own kernel) before the decode")
     p.add_argument("--extend", choices=["verify", "prefill", "chunk"], default=None,
                    help="time a step with several new tokens per sequence instead of decode: the verify pass "
                         "of speculative decoding (5 draft tokens, 70B-shaped batch), a 2048-token causal "
@@ -300,18 +317,102 @@ def step_percentiles(step_ev):
     return {"step_us_median": round(us[len(us) // 2], 2), "step_us_p95": round(p95, 2)}
 
 
-def environment():
-    """Software and device the numbers were taken on."""
+def _dpm_files():
+    """The power-management clock tables (sysfs) of the device torch uses:
+    (shader clock file, memory clock file) or None."""
+    import glob
     import torch
     prop = torch.cuda.get_device_properties(0)
-    return {"torch": torch.__version__, "hip": torch.version.hip, "device": prop.name,
-            "arch": getattr(prop, "gcnArchName", None), "compute_units": prop.multi_processor_count,
-            "memory_gib": round(prop.total_memory / 2 ** 30, 1)}
+    bus = getattr(prop, "pci_bus_id", None)
+    cands = []
+    if bus is not None:
+        dom = getattr(prop, "pci_domain_id", 0) or 0
+        dv = getattr(prop, "pci_device_id", 0) or 0
+        cands.append(f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{dv:02x}.0")
+    cands += sorted(os.path.dirname(p) for p in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    for d in cands:
+        s, m = os.path.join(d, "pp_dpm_sclk"), os.path.join(d, "pp_dpm_mclk")
+        if os.path.exists(s):
+            return s, (m if os.path.exists(m) else None), d
+    return None
+
+
+def _read_dpm(path):
+    """(levels in MHz, current level's MHz or None) of one pp_dpm_* table."""
+    import re
+    levels, cur = [], None
+    try:
+        for line in open(path).read().splitlines():
+            m = re.search(r"(\d+)\s*Mhz(\s*\*)?", line, re.I)
+            if m:
+                levels.append(int(m.group(1)))
+                if m.group(2):
+                    cur = int(m.group(1))
+    except OSError:
+        return None, None
+    return levels, cur
+
+
+def sample_clocks_under_load(step, seconds=0.3):
+    """Shader and memory clocks read from the power-management tables every
+    ~2 ms while decode steps run back to back for `seconds`."""
+    import threading
+    import torch
+    files = _dpm_files()
+    if not files:
+        return {"source": "no pp_dpm_sclk table readable"}
+    sfile, mfile, dev_dir = files
+    samples_s, samples_m, stop = [], [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            _, c = _read_dpm(sfile)
+            if c is not None:
+                samples_s.append(c)
+            if mfile:
+                _, cm = _read_dpm(mfile)
+                if cm is not None:
+                    samples_m.append(cm)
+            time.sleep(0.002)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    sl, _ = _read_dpm(sfile)
+    ml, _ = _read_dpm(mfile) if mfile else (None, None)
+
+    def summary(xs):
+        xs = sorted(xs)
+        return {"samples": len(xs), "min": xs[0], "median": xs[len(xs) // 2], "max": xs[-1]} if xs else None
+    return {"source": dev_dir, "sclk_levels_mhz": sl, "mclk_levels_mhz": ml, "steps_run": n,
+            "sclk_mhz_under_load": summary(samples_s), "mclk_mhz_under_load": summary(samples_m)}
+
+
+def environment(clocks=None):
+    """Software and device the numbers were taken on (and the clocks seen
+    while the steps ran, when sampled)."""
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    env = {"torch": torch.__version__, "hip": torch.version.hip, "device": prop.name,
+           "arch": getattr(prop, "gcnArchName", None), "compute_units": prop.multi_processor_count,
+           "memory_gib": round(prop.total_memory / 2 ** 30, 1)}
+    if clocks is not None:
+        env["clocks"] = clocks
+    return env
 
 
 def calibrate_copy(dev):
     """Time the plain 2 GiB copy kernel (its known bytes scale the profiler's
-    HBM byte counters)."""
+    HBM byte counters) and a plain streaming read of the same 2 GiB (the
+    achievable read rate, the decode's own ceiling on this machine)."""
     import torch
     import paged_kv_cache_split_amd as kvc
     n = 1 << 31
@@ -326,8 +427,20 @@ def calibrate_copy(dev):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 5
-    del src, dst
-    return {"copy_bytes": n, "copy_read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+    del dst
+    # the achievable streaming read rate: every byte of 2 GiB read once
+    sink = torch.empty(1 << 16, dtype=torch.uint32, device=dev)
+    kvc.stream_read(src, sink)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        kvc.stream_read(src, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_r = e0.elapsed_time(e1) / 5
+    del src, sink
+    return {"copy_bytes": n, "copy_read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "read_GBs": round(n / (ms_r * 1e-3) / 1e9, 1)}
 
 
 def run_extend(args):
@@ -368,7 +481,7 @@ def run_extend(args):
                                                          wl.max_query_len, wl.max_context_len, args.work_items,
                                                          args.tiles_per_wave, args.extend_kernel)),
                      dtype=torch.uint8, device=dev)
-    ev = TimingEvent.pairs(args.steps)
+    ev = TimingEvent.pairs((args.steps + EVENT_EVERY - 1) // EVENT_EVERY)
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
 
     def step(events=None):
@@ -388,7 +501,7 @@ def run_extend(args):
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev[i])
+        step(ev[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # per-step percentiles from a second pass, so the markers do not touch the timed region
@@ -446,33 +559,18 @@ def run_extend(args):
         **step_stats,
         "env": environment(),
     }
-    if args.calibrate:
-        result["calibration"] = calibrate_copy(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_extend(wl, values, args.cpu_seconds)
+    if not args.no_calibrate:
+        result["calibration"] = calibrate_copy(dev)
     print(json.dumps(result), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the decode path here is single-GPU by design "
-              f"(--gpus {args.gpus} requested); run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-    if args.extend:
-        run_extend(args)
-        return
-    import torch
+def build_decode_cache(wl, dev):
+    """The workload's cache with its history written through the library."""
     import paged_kv_cache_split_amd as kvc
-    from workloads import make_values, make_window_workload, make_workload, setup_ops
-
-    dev = "cuda"
-    torch.cuda.set_device(0)
-    over = {"kv_dtype": args.kv} if args.kv else {}
-    wl = make_window_workload() if args.window else make_workload(args.config, seed=args.seed, **over)
-    print(f"[bench] {'window' if args.window else 'config %d' % args.config}: {wl.name}; blocks {wl.num_blocks}, "
-          f"attended tokens {int(wl.attend_lens.sum())}", file=sys.stderr, flush=True)
+    from workloads import make_values, setup_ops
     values = make_values(wl, dev)
     cache = kvc.KVCache(wl.num_layers, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.kv_dtype, device=dev,
                         free_order=wl.free_order)
@@ -489,64 +587,152 @@ def main():
             cache.append(op[1], values["k_hist"][:, row:row + t].contiguous(),
                          values["v_hist"][:, row:row + t].contiguous(), n_new=op[2])
             row += t
+    return cache, values
+
+
+def time_decode(wl, values, cache, o, steps, warmup, dev, load_clock=False):
+    """Time `steps` decode steps of one workload (after `warmup` untimed ones).
+
+    A step: the slot reservation and append of every sequence's new token,
+    the decode (split-K kernel and merge), and the host rollback that makes the
+    next step append into the same slots.  With o.append == "fold" the append
+    is kvc_append without rows plus the rows handed to the decode, which
+    writes them itself (16-bit caches) or runs the append kernel first;
+    with "kernel" it is kvc_append with rows (its own kernel), then the
+    decode."""
+    import torch
+    import paged_kv_cache_split_amd as kvc
     seqs = list(range(wl.batch))
     hist_len = [int(x) for x in wl.context_lens]
     k_new, v_new, q = values["k_new"].contiguous(), values["v_new"].contiguous(), values["q"].contiguous()
+    k_row, v_row = k_new[0].contiguous(), v_new[0].contiguous()
     # tables as they are after the step's append (the decode reads L+1 tokens)
     cache.append(seqs, k_new, v_new)
     bt, cl = cache.export_tables(seqs)
     cache.truncate_many(seqs, hist_len)
     torch.cuda.synchronize()
     out = torch.empty_like(q)
-    prefix = wl.shared_prefix if args.shared_prefix else 0
-    if args.shared_prefix and not prefix:
-        raise SystemExit("--shared-prefix needs a workload with a shared prefix (config 4)")
+    prefix = wl.shared_prefix if o.shared_prefix else 0
     ws = torch.empty(max(256, kvc.decode_workspace_bytes(wl.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
-                                                         wl.max_context_len, args.partition_tokens, args.kernel,
-                                                         args.work_items, args.pool_pieces, args.pool_shift,
-                                                         prefix)),
+                                                         wl.max_context_len, o.partition_tokens, o.kernel,
+                                                         o.work_items, o.pool_pieces, o.pool_shift, prefix)),
                      dtype=torch.uint8, device=dev)
-    ev = TimingEvent.pairs(args.steps)
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+    # HIP events bracket the split kernel of every EVENT_EVERY-th timed step:
+    # each record is a packet the GPU processes between kernels (~2 us), so
+    # bracketing every launch would add ~4 us to every timed step
+    ev = TimingEvent.pairs((steps + EVENT_EVERY - 1) // EVENT_EVERY)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    fold = o.append == "fold"
 
     def step(events=None):
-        cache.append(seqs, k_new, v_new)
-        cache.decode(q, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws, kernel=args.kernel,
-                     partition_tokens=args.partition_tokens, work_items=args.work_items, split_events=events,
-                     window=wl.window, pool_pieces=args.pool_pieces, pool_shift=args.pool_shift,
-                     shared_prefix=prefix)
+        if fold:
+            cache.append(seqs, None, None)
+        else:
+            cache.append(seqs, k_new, v_new)
+        cache.decode(q, bt, cl, wl.max_context_len, wl.scale, out=out, workspace=ws, kernel=o.kernel,
+                     partition_tokens=o.partition_tokens, work_items=o.work_items, split_events=events,
+                     window=wl.window, pool_pieces=o.pool_pieces, pool_shift=o.pool_shift, shared_prefix=prefix,
+                     k_new=k_row if fold else None, v_new=v_row if fold else None)
         cache.truncate_many(seqs, hist_len)
 
     # a full garbage-collector pass over the setup's objects inside the timed
     # loop costs tens of milliseconds: collect now and exempt what exists
     gc.collect()
     gc.freeze()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
+    for i in range(steps):
+        step(ev[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # per-step percentiles from a second pass, so the markers do not touch the timed region
-    for i in range(args.steps):
+    for i in range(steps):
         step_ev[i][0].record()
         step()
         step_ev[i][1].record()
     torch.cuda.synchronize()
+    clocks = sample_clocks_under_load(step) if load_clock else None
+    gc.unfreeze()
     split_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    step_stats = step_percentiles(step_ev)
     split_avg_ms = sum(split_ms) / len(split_ms)
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     ab = algorithmic_bytes(wl)
+    if fold and wl.kv_dtype in ("f16", "bf16") and o.kernel in (0, 2) and not o.pool_pieces:
+        # the walk also reads the new rows and writes them into their slots
+        ab["split_kernel"] += 2 * ab["append"]
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
+    achieved = ab["split_kernel"] / (split_avg_ms * 1e-3) / 1e9
+    return dict(ms_per_step=ms_per_step, kv_gbs=kv_gbs, ab=ab, achieved=achieved, split_avg_ms=split_avg_ms,
+                split_median_ms=split_ms[len(split_ms) // 2], step_stats=step_percentiles(step_ev), clocks=clocks)
+
+
+class DecodeOpts:
+    def __init__(self, args, shared_prefix=None):
+        self.kernel, self.partition_tokens, self.work_items = args.kernel, args.partition_tokens, args.work_items
+        self.pool_pieces, self.pool_shift = args.pool_pieces, args.pool_shift
+        self.shared_prefix = args.shared_prefix if shared_prefix is None else shared_prefix
+        self.append = args.append
+
+
+def also_entry(cid, shared_prefix, args, dev):
+    """A compact record of another decode workload measured in the same process."""
+    import torch
+    from workloads import make_workload
+    wl = make_workload(cid)
+    print(f"[bench] also: config {cid}{' shared prefix' if shared_prefix else ''}: {wl.name}", file=sys.stderr,
+          flush=True)
+    cache, values = build_decode_cache(wl, dev)
+    o = DecodeOpts(args, shared_prefix=shared_prefix)
+    r = time_decode(wl, values, cache, o, args.steps, args.warmup, dev)
+    key = f"config {cid}"
+    prof = profiled_traffic(key) if not shared_prefix and o.kernel in (0, 2) else None
+    entry = {"workload": wl.name, "config_id": cid, "shared_prefix": wl.shared_prefix if shared_prefix else 0,
+             "dtype": wl.kv_dtype, "us_per_step": round(r["ms_per_step"] * 1e3, 2), "value": round(r["kv_gbs"], 2),
+             "unit": "GB/s", "pct_of_peak_hbm": round(100.0 * r["kv_gbs"] / PEAK_HBM_GBS, 2),
+             "kv_bytes": r["ab"]["kv"],
+             "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(r["achieved"] / PEAK_HBM_GBS, 4),
+                          "kernel": "decode split-K kernel" + (" (prefix pass + own rows)" if shared_prefix else ""),
+                          "avg_launch_us": round(r["split_avg_ms"] * 1e3, 2),
+                          "traffic": prof[0] if prof else None, "traffic_source": prof[1] if prof else None},
+             **r["step_stats"]}
+    del cache, values
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return entry
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode path here is single-GPU by design "
+              f"(--gpus {args.gpus} requested); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.extend:
+        run_extend(args)
+        return
+    import torch
+    from workloads import make_window_workload, make_workload
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    over = {"kv_dtype": args.kv} if args.kv else {}
+    wl = make_window_workload() if args.window else make_workload(args.config, seed=args.seed, **over)
+    print(f"[bench] {'window' if args.window else 'config %d' % args.config}: {wl.name}; blocks {wl.num_blocks}, "
+          f"attended tokens {int(wl.attend_lens.sum())}", file=sys.stderr, flush=True)
+    if args.shared_prefix and not wl.shared_prefix:
+        raise SystemExit("--shared-prefix needs a workload with a shared prefix (config 4)")
+    cache, values = build_decode_cache(wl, dev)
+    o = DecodeOpts(args)
+    r = time_decode(wl, values, cache, o, args.steps, args.warmup, dev, load_clock=not args.no_clocks)
+    print(f"[bench] timed {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    prefix = wl.shared_prefix if args.shared_prefix else 0
+    ab, ms_per_step, kv_gbs, achieved = r["ab"], r["ms_per_step"], r["kv_gbs"], r["achieved"]
     prof = (profiled_traffic(workload_key(args)) if args.kernel in (0, 2) and not args.work_items
             and not args.pool_pieces and not args.shared_prefix else None)
     traffic = prof[0] if prof else None
-    achieved = ab["split_kernel"] / (split_avg_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(kv_gbs, 2),
@@ -568,25 +754,36 @@ def main():
                    "attended_tokens": int(wl.attend_lens.sum()), "kv_bytes": ab["kv"],
                    "kernel": ["auto", "fma", "mfma"][args.kernel], "partition_tokens": args.partition_tokens or "auto",
                    "work_items": args.work_items or "auto", "pool_pieces": args.pool_pieces,
-                   "shared_prefix": prefix, "parallelism": "single GPU"},
+                   "shared_prefix": prefix, "append": args.append, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      # with a shared prefix: the prefix pass and the own-rows decode together, over the
                      # same unique bytes as the plain decode (the prefix counted once in both)
                      "kernel": "decode split-K kernel" + (" (prefix pass + own rows)" if prefix else ""),
-                     "avg_launch_us": round(split_avg_ms * 1e3, 2),
-                     "median_launch_us": round(split_ms[len(split_ms) // 2] * 1e3, 2),
+                     "avg_launch_us": round(r["split_avg_ms"] * 1e3, 2),
+                     "median_launch_us": round(r["split_median_ms"] * 1e3, 2),
                      "algorithmic_bytes_per_launch": ab["split_kernel"],
                      "traffic_source": prof[1] if prof else None},
-        **step_stats,
-        "env": environment(),
+        **r["step_stats"],
+        "env": environment(r["clocks"]),
     }
-    if args.calibrate:
-        result["calibration"] = calibrate_copy(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = (cpu_baseline_window(wl, values, args.cpu_seconds) if wl.window
                                   else cpu_baseline(wl, values, args.cpu_seconds))
+    del cache, values
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_calibrate:
+        cal = calibrate_copy(dev)
+        cal["kv_read_pct_of_read_GBs"] = round(100.0 * kv_gbs / cal["read_GBs"], 2)
+        cal["split_kernel_pct_of_read_GBs"] = round(100.0 * achieved / cal["read_GBs"], 2)
+        result["calibration"] = cal
+    default_run = (not args.window and args.config == 3 and not args.kv and args.seed is None and not args.kernel
+                   and not args.work_items and not args.pool_pieces and not args.shared_prefix
+                   and not args.partition_tokens and args.append == "fold")
+    if default_run and not args.no_also:
+        result["also"] = [also_entry(cid, sp, args, dev) for cid, sp in ((2, False), (4, False), (4, True), (5, False))]
     print(json.dumps(result), flush=True)
 
 

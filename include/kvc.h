@@ -226,7 +226,10 @@ kvc_status kvc_check_shared_prefix(const kvc_cache* cache, int32_t batch, const 
 
 /* Reserve (as kvc_reserve_host) and write: copies every copy-on-write block
  * (all layers, K and V, fp8 / int8 scales) then stores the new rows of every layer in
- * their slots.  k_new / v_new: device [num_layers][T][num_kv_heads][head_dim]
+ * their slots.  With k_new and v_new both NULL (and at most one new token per
+ * sequence) only the reservation and the copies are done: the rows are
+ * written later, one layer at a time, by kvc_decode_attention (opts k_new /
+ * v_new) -- the decode step with its append folded in.  k_new / v_new: device [num_layers][T][num_kv_heads][head_dim]
  * in in_dtype, T = sum(n_new), rows sequence by sequence in call order,
  * positions ascending.  in_dtype must equal kv_dtype, except that an fp8 or int8 cache
  * takes f32, f16 or bf16 rows and quantises them (rule above).  Requires
@@ -289,6 +292,15 @@ typedef struct kvc_decode_opts {
   const int64_t* seq_ids;   /* host, optional, [batch]: the cache's ids of the batch's rows (the order of
                                kvc_export_tables).  With shared_prefix > 0 the decode first runs
                                kvc_check_shared_prefix on them and fails as it does; ignored otherwise. */
+  const void* k_new;        /* decode only, optional (both or neither): this layer's new K and V rows,  */
+  const void* v_new;        /* device [batch][num_kv_heads][head_dim] in q_dtype, written to position
+                               context_lens[b] - 1 of every sequence before the attention reads it: the
+                               append of a decode step whose slots kvc_append reserved without rows
+                               ("苦猿的大模型日记 · Day45" PART 02: add the new token's K/V to the cache, then
+                               attend).  With the matrix-core kernel, no pool and a 16-bit cache the walk
+                               itself writes them (the wave that reads a sequence's last block writes its
+                               newest row first); otherwise an append kernel (with the fp8 / int8 scale
+                               rule) runs first.  A length or block id outside the arrays skips the write. */
 } kvc_decode_opts;
 
 /* Workspace bytes kvc_decode_attention needs for this shape (the split
@@ -432,6 +444,12 @@ kvc_status kvc_sched_get_stats(const kvc_sched* sched, kvc_sched_stats* out);
  * plain copy kernel of known size, used to calibrate HBM byte counters and
  * achievable bandwidth.  Not part of the method. */
 kvc_status kvc_stream_copy(void* dst, const void* src, size_t bytes, kvc_stream_t stream);
+/* Streaming read of `bytes` (multiple of 16) from src on `stream`, every byte
+ * once with non-temporal loads: the achievable HBM read rate that a decode's
+ * KV read can be compared with.  Each wave stores the xor of what it read to
+ * sink[(wave index) % sink_words] (device, sink_words >= 1 words), so the
+ * reads cannot be dropped.  Not part of the method. */
+kvc_status kvc_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, kvc_stream_t stream);
 
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* kvc_last_error(void);

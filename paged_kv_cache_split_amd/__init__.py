@@ -9,5 +9,5 @@ been built (``python paged_kv_cache_split_amd/build.py``).
 """
 from ._binding import (BF16, F16, F32, FP8, INT8, KVCache, KvcError, Scheduler, bytes_per_token,  # noqa: F401
                        decode_workspace_bytes, extend_workspace_bytes, lib, pool_bytes, scale_bytes,
-                       scratch_bytes, stream_copy)
+                       scratch_bytes, stream_copy, stream_read)
 from ._binding import LIB_PATH, SYMBOLS  # noqa: F401

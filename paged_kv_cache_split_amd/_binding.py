@@ -35,7 +35,7 @@ SYMBOLS = [
     "kvc_get_table", "kvc_stats", "kvc_check_shared_prefix", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
     "kvc_decode_attention", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_sched_create",
     "kvc_sched_destroy", "kvc_sched_submit", "kvc_sched_plan", "kvc_sched_commit", "kvc_sched_get_stats",
-    "kvc_stream_copy", "kvc_last_error",
+    "kvc_stream_copy", "kvc_stream_read", "kvc_last_error",
 ]
 
 
@@ -69,7 +69,8 @@ class KvcDecodeOpts(ctypes.Structure):
                 ("pool_pieces", ctypes.c_int32), ("pool_shift", ctypes.c_int32),
                 ("split_start", ctypes.c_void_p), ("split_end", ctypes.c_void_p), ("window", ctypes.c_int32),
                 ("tiles_per_wave", ctypes.c_int32), ("shared_prefix", ctypes.c_int32),
-                ("seq_ids", ctypes.POINTER(ctypes.c_int64))]
+                ("seq_ids", ctypes.POINTER(ctypes.c_int64)), ("k_new", ctypes.c_void_p),
+                ("v_new", ctypes.c_void_p)]
 
 
 _i32, _i64, _sz, _vp, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -109,6 +110,7 @@ _sig = {
     "kvc_sched_commit": (ctypes.c_int, [_vp, _P64, _i32, _P32]),
     "kvc_sched_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(KvcSchedStats)]),
     "kvc_stream_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+    "kvc_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _sz, _vp]),
     "kvc_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sig.items():
@@ -195,6 +197,14 @@ def stream_copy(dst, src, nbytes=None, stream=None):
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
     _check(_lib.kvc_stream_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), nbytes,
                                 _stream_ptr(stream)), "kvc_stream_copy")
+
+
+def stream_read(src, sink, nbytes=None, stream=None):
+    """Plain streaming read of ``nbytes`` (default: all of src) -- the read-rate
+    calibration kernel; sink: a device int32/uint32 tensor the waves write to."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(_lib.kvc_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                sink.numel(), _stream_ptr(stream)), "kvc_stream_read")
 
 
 # -- the cache ----------------------------------------------------------------
@@ -319,11 +329,18 @@ class KVCache:
                    "kvc_set_scratch")
 
     def append(self, seq_ids, k_new, v_new, n_new=None, stream=None):
-        """k_new / v_new: device tensors [num_layers, T, Hkv, D] (or [T, Hkv, D] for one layer)."""
+        """k_new / v_new: device tensors [num_layers, T, Hkv, D] (or [T, Hkv, D] for one layer).
+        Both None: reserve the slots (and copy shared blocks) only; the decode
+        then writes each sequence's newest row (``decode(..., k_new=, v_new=)``)."""
         ids, pids = _i64_array(seq_ids)
         nn, pnn = (None, None) if n_new is None else _i32_array(n_new)
         total = len(ids) if n_new is None else int(np.sum(nn))
         active = len(ids) if n_new is None else int(np.count_nonzero(nn))
+        if k_new is None and v_new is None:
+            self._ensure_scratch(active, total)
+            _check(_lib.kvc_append(self._h, len(ids), pids, pnn, None, None, BF16, _stream_ptr(stream)),
+                   "kvc_append")
+            return
         for t in (k_new, v_new):
             expect = self.num_layers * total * self.num_kv_heads * self.head_dim
             if not t.is_contiguous() or t.numel() != expect or not t.is_cuda:
@@ -349,12 +366,14 @@ class KVCache:
 
     def decode(self, q, block_table, context_lens, max_context_len, scale, layer=0, out=None, workspace=None,
                partition_tokens=0, kernel=0, work_items=0, pool_pieces=0, pool_shift=0, split_events=None,
-               stream=None, window=0, shared_prefix=0, seq_ids=None):
+               stream=None, window=0, shared_prefix=0, seq_ids=None, k_new=None, v_new=None):
         """Decode attention for one layer.  q: [B, Hq, D] device tensor.
         ``window`` > 0: each token sees at most that many rows ending at its own.
         ``shared_prefix`` > 0: the first that many tokens of every sequence are one
         shared prefix, attended once for the batch (the cascade split);
-        ``seq_ids`` (the batch's sequence ids) has the library check that first."""
+        ``seq_ids`` (the batch's sequence ids) has the library check that first.
+        ``k_new`` / ``v_new``: this layer's new rows [B, Hkv, D] (q's dtype), written
+        to each sequence's newest position before it is attended."""
         import torch
         B, Hq, D = q.shape
         if not q.is_contiguous():
@@ -365,6 +384,13 @@ class KVCache:
             ids_arr, opts.seq_ids = _i64_array(seq_ids)
             if len(ids_arr) != B:
                 raise ValueError("seq_ids must name one sequence per row of q")
+        if (k_new is None) != (v_new is None):
+            raise ValueError("k_new and v_new go together")
+        if k_new is not None:
+            for t in (k_new, v_new):
+                if not t.is_contiguous() or t.numel() != B * self.num_kv_heads * D or t.dtype != q.dtype:
+                    raise ValueError("k_new / v_new must be contiguous [B, Hkv, D] tensors in q's dtype")
+            opts.k_new, opts.v_new = k_new.data_ptr(), v_new.data_ptr()
         if split_events is not None:
             opts.split_start = split_events[0].cuda_event
             opts.split_end = split_events[1].cuda_event

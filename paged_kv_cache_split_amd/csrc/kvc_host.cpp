@@ -733,9 +733,14 @@ kvc_status kvc_append(kvc_cache* c, int32_t batch, const int64_t* seq_ids, const
   kvc_status st = check_device_ready(c);
   if (st != KVC_OK) return st;
   const kvc_dtype kv = c->cfg.kv_dtype;
-  if (!valid_dtype(in_dtype)) return fail(KVC_E_INVALID, "unknown in_dtype");
-  if (is_quantised(kv) ? is_quantised(in_dtype) : in_dtype != kv)
-    return fail(KVC_E_UNSUPPORTED, "append rows of dtype %d into a cache of dtype %d", (int)in_dtype, (int)kv);
+  // No rows at all: reserve the slots (and copy shared blocks) only; a
+  // decode call writes each sequence's newest row (kvc_decode_opts.k_new).
+  const bool rows_later = !k_new && !v_new;
+  if (!rows_later) {
+    if (!valid_dtype(in_dtype)) return fail(KVC_E_INVALID, "unknown in_dtype");
+    if (is_quantised(kv) ? is_quantised(in_dtype) : in_dtype != kv)
+      return fail(KVC_E_UNSUPPORTED, "append rows of dtype %d into a cache of dtype %d", (int)in_dtype, (int)kv);
+  }
   if (batch < 0) return fail(KVC_E_INVALID, "batch must be >= 0");
   int64_t total = 0, seg_bound = 0;
   int32_t active = 0;
@@ -747,7 +752,11 @@ kvc_status kvc_append(kvc_cache* c, int32_t batch, const int64_t* seq_ids, const
     // n rows starting anywhere inside a 16-token block span at most (n + 30) / 16 blocks
     if (n > 0) seg_bound += ((int64_t)n + 2 * kDeviceBlockSize - 2) / kDeviceBlockSize;
   }
-  if (total > 0 && (!k_new || !v_new)) return fail(KVC_E_INVALID, "k_new / v_new are NULL");
+  if (total > 0 && !rows_later && (!k_new || !v_new)) return fail(KVC_E_INVALID, "one of k_new / v_new is NULL");
+  if (rows_later)
+    for (int32_t i = 0; i < batch; ++i)
+      if (n_new && n_new[i] > 1)
+        return fail(KVC_E_INVALID, "an append without rows reserves at most one token per sequence");
   if (total > INT32_MAX) return fail(KVC_E_INVALID, "too many rows in one append");
   size_t need = kvc_scratch_bytes(active, total);
   if (!c->cfg.dev_scratch || c->cfg.dev_scratch_bytes < need)
@@ -791,6 +800,7 @@ kvc_status kvc_append(kvc_cache* c, int32_t batch, const int64_t* seq_ids, const
                                            (int32_t)plan.cow.size(), s);
     if (e != hipSuccess) return fail(KVC_E_HIP, "copy-on-write launch: %s", hipGetErrorString(e));
   }
+  if (rows_later) return ok();
   hipError_t e;
   if (inline_plan) {
     kvc::InlineSegments segs;
@@ -933,12 +943,15 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
       if (pst != KVC_OK) return pst;
     }
   }
+  const void* k_new = opts ? opts->k_new : nullptr;
+  const void* v_new = opts ? opts->v_new : nullptr;
+  if (!k_new != !v_new) return fail(KVC_E_INVALID, "opts: k_new and v_new must both be set or both be NULL");
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   hipError_t e = kvc::launch_decode(c->pool(), layer, plan, q, q_dtype, nullptr, batch, block_table,
                                     max_blocks_per_seq, context_lens, max_context_len, batch, num_heads, scale, out,
-                                    workspace,
+                                    workspace, k_new, v_new,
                                     opts ? static_cast<hipEvent_t>(opts->split_start) : nullptr,
                                     opts ? static_cast<hipEvent_t>(opts->split_end) : nullptr,
                                     static_cast<hipStream_t>(stream));
@@ -981,7 +994,7 @@ kvc_status kvc_extend_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
     return fail(KVC_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   hipError_t e = kvc::launch_decode(c->pool(), layer, plan, q, q_dtype, query_start, total_query, block_table,
                                     max_blocks_per_seq, context_lens, max_context_len, batch, num_heads, scale, out,
-                                    workspace,
+                                    workspace, nullptr, nullptr,
                                     opts ? static_cast<hipEvent_t>(opts->split_start) : nullptr,
                                     opts ? static_cast<hipEvent_t>(opts->split_end) : nullptr,
                                     static_cast<hipStream_t>(stream));
@@ -995,6 +1008,16 @@ kvc_status kvc_stream_copy(void* dst, const void* src, size_t bytes, kvc_stream_
   if (bytes == 0) return ok();
   hipError_t e = kvc::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVC_E_HIP, "copy launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvc_status kvc_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, kvc_stream_t stream) {
+  if (!src || !sink) return fail(KVC_E_INVALID, "NULL pointer");
+  if (bytes % 16 != 0) return fail(KVC_E_INVALID, "bytes must be a multiple of 16");
+  if (sink_words < 1) return fail(KVC_E_INVALID, "sink_words must be >= 1");
+  if (bytes == 0) return ok();
+  hipError_t e = kvc::launch_stream_read(src, bytes, sink, sink_words, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVC_E_HIP, "read launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -181,14 +181,23 @@ struct InlineSegments {
 hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, const InlineSegments* segs_inline,
                          int32_t num_segments, const void* k_new, const void* v_new, kvc_dtype in_dtype,
                          int64_t total_rows, hipStream_t stream);
+// Whether the decode walk writes the step's newest rows itself: the static
+// matrix-core walk over a 16-bit cache (a tile's one reader writes it); other
+// plans run an append kernel first.
+inline bool decode_folds_append(const DecodePlan& p, kvc_dtype kv) {
+  return p.kernel == 2 && p.tile_groups == 0 && p.pool_pieces == 0 && (kv == KVC_F16 || kv == KVC_BF16);
+}
 // q_start / total_q: several query tokens per sequence (plan.tile_groups > 0);
-// NULL / ignored for decode.
+// NULL / ignored for decode.  k_new / v_new (decode only, NULL = none): this
+// layer's new rows [batch][num_kv_heads][head_dim] in q_dtype, written to
+// position context_lens[b] - 1 of every sequence before it is attended.
 hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q,
                          kvc_dtype q_dtype, const int32_t* q_start, int32_t total_q, const int32_t* block_table,
                          int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len, int32_t batch,
-                         int32_t num_heads, float scale, void* out, void* workspace, hipEvent_t ev_start,
-                         hipEvent_t ev_end, hipStream_t stream);
+                         int32_t num_heads, float scale, void* out, void* workspace, const void* k_new,
+                         const void* v_new, hipEvent_t ev_start, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream);
 
 // Shared by the host sources (defined in kvc_host.cpp).
 kvc_status host_fail(kvc_status st, const char* msg);   // records msg as the thread's last error

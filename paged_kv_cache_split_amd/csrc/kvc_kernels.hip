@@ -247,6 +247,26 @@ struct SegFromArgs {
   InlineSegments v;
   __device__ __forceinline__ AppendSegment get(int i) const { return v.s[i]; }
 };
+// The newest row of sequence i (position context_lens[i] - 1, the one a decode
+// step appends) from its block-table row: row i of the append input goes to
+// that slot.  A length or block id outside the arrays gives an empty segment
+// (no write).
+struct SegFromTable {
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int32_t max_blocks, num_blocks;
+  __device__ __forceinline__ AppendSegment get(int i) const {
+    const int n = context_lens[i];
+    AppendSegment s{0, 0, 0, i};
+    if (n < 1 || n > max_blocks * kBS) return s;
+    const int blk = block_table[(int64_t)i * max_blocks + (n - 1) / kBS];
+    if (blk < 0 || blk >= num_blocks) return s;
+    s.block = blk;
+    s.offset = (n - 1) % kBS;
+    s.count = 1;
+    return s;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Append (reshape-and-cache) for f32 / f16 / bf16 caches: a plain copy of
@@ -300,6 +320,7 @@ __global__ __launch_bounds__(64) void append_quant_kernel(PoolDesc p, SEGS segs,
     else return int8_encode(x);
   };
   const AppendSegment sg = segs.get(blockIdx.x);
+  if (sg.count <= 0) return;
   const int h = blockIdx.y;
   const int layer = blockIdx.z >> 1;
   const bool is_v = blockIdx.z & 1;
@@ -399,6 +420,12 @@ struct DecodeArgs {
   const float* pre_acc;
   const float* pre_m;
   const float* pre_l;
+  // decode with the step's append folded in (16-bit caches, static split):
+  // this layer's new rows [batch][num_kv_heads][D] in the cache dtype; the row
+  // of sequence b goes to position context_lens[b] - 1 before it is attended
+  // (NULL: the rows are already in the pool)
+  const char* k_new;
+  const char* v_new;
 };
 
 template <kvc_dtype QT>
@@ -690,6 +717,13 @@ __device__ __forceinline__ void load_block(KvBlock<KV, D>& blk, const char* kt, 
     if constexpr (is_byte_code(KV)) blk.v[dd] = load_stream<uint32_t>(vt + voff + dd * 16 * kBS * E);
     else blk.v[dd] = load_stream<u32x2>(vt + voff + dd * 16 * kBS * E);
   }
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maximum)
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Max over the lanes l, l^16, l^32, l^48 (the four row groups of a wave)
@@ -1433,6 +1467,39 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
     if (xp == seg_end) finish();
   };
 
+  // The step's append folded into the walk: the wave whose main chunk holds a
+  // sequence's last block writes that sequence's newest row of this KV head
+  // (each (block, head) tile is read by exactly one wave, so no other wave
+  // reads it) before it loads any tile.  Its own later loads of that tile
+  // then see the stores: a work-group-scope fence orders them (on gfx950
+  // that takes no wait; a CU keeps one work-group's accesses in order).
+  if (!POOL && a.k_new) {
+    constexpr int X = 8;                          // 16-bit elements per 16-byte chunk
+    bool wrote = false;
+    for (int bb = b; bb < a.batch; ++bb) {
+      const int sb = start_of(bb), eb = start_of(bb + 1);
+      if (sb >= xb_main) break;
+      if (eb <= sb || eb - 1 < xa || eb - 1 >= xb_main) continue;   // last block in another chunk
+      const int pos = seq_len(bb) - 1;
+      const int blk = ((const_i32_kptr)(a.block_table + (int64_t)bb * a.max_blocks))[pos / kBS];
+      if (blk < 0 || blk >= a.num_blocks) continue;                 // a bad table entry: no write
+      const int off = pos % kBS;
+      const int64_t t = (int64_t)blk * block_stride + head_off;
+      // the pools are written only here, by the tile's one reader
+      char* kt = const_cast<char*>(a.k) + t;
+      char* vt = const_cast<char*>(a.v) + t;
+      const int64_t src = ((int64_t)bb * a.num_kv_heads + g) * D * 2;
+      if (lane < D / X)
+        *reinterpret_cast<u32x4*>(kt + ((int64_t)lane * kBS + off) * 16) =
+            *reinterpret_cast<const u32x4*>(a.k_new + src + lane * 16);
+#pragma unroll
+      for (int d = lane; d < D; d += 64)
+        *reinterpret_cast<uint16_t*>(vt + ((int64_t)d * kBS + off) * 2) =
+            *reinterpret_cast<const uint16_t*>(a.v_new + src + d * 2);
+      wrote = true;
+    }
+    if (wrote) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  }
   record_range(xa, xb_main, c);
   load_q(q, b);
   begin(xa);
@@ -1602,12 +1669,6 @@ __device__ __forceinline__ int flash_pieces(int nsteps, int split_steps) {
 // waves with a barrier.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(uintptr_t)lds_wave_base, 16, 0, 0);
-}
-// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maximum)
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 // s_barrier with no fence: the callers order their own LDS and memory traffic
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -2267,6 +2328,29 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(u32x4* __restrict__ ds
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Plain streaming read (calibration): every 16-byte chunk of src read once
+// with non-temporal loads, four per thread in flight; each wave writes the
+// xor of its chunks to one word of sink, so no load is dead.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                          uint32_t* __restrict__ sink, int64_t sink_words) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i), b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride), d = __builtin_nontemporal_load(src + i + 3 * stride);
+    const u32x4 x = a ^ b ^ c ^ d;
+    acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+  if ((threadIdx.x & 63) == 0) sink[((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) % sink_words] = acc;
+}
+
 template <kvc_dtype KV, kvc_dtype QT, int D>
 hipError_t launch_fma(const DecodeArgs& a, int G, dim3 grid, hipStream_t s) {
   if (G <= 1) hipLaunchKernelGGL((decode_fma_kernel<KV, QT, D, 1>), grid, dim3(64), 0, s, a);
@@ -2428,6 +2512,24 @@ hipError_t launch_append_from(const PoolDesc& pool, const SEGS& segs, int32_t nu
   return hipGetLastError();
 }
 
+// The newest row of each of `batch` sequences of one layer, read from the
+// block table: the append of a decode step whose bookkeeping is already done.
+hipError_t launch_append_newest(const PoolDesc& pool, int32_t layer, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* context_lens, int32_t batch, const void* k_new, const void* v_new,
+                                kvc_dtype in_dtype, hipStream_t stream) {
+  PoolDesc one = pool;
+  const int64_t layer_bytes = (int64_t)pool.num_blocks * pool.num_kv_heads * tile_bytes(pool);
+  one.k = pool.k + layer * layer_bytes;
+  one.v = pool.v + layer * layer_bytes;
+  if (pool.k_scale) {
+    one.k_scale = pool.k_scale + (int64_t)layer * pool.num_blocks * pool.num_kv_heads;
+    one.v_scale = pool.v_scale + (int64_t)layer * pool.num_blocks * pool.num_kv_heads;
+  }
+  one.num_layers = 1;
+  const SegFromTable segs{block_table, context_lens, max_blocks, pool.num_blocks};
+  return launch_append_from(one, segs, batch, k_new, v_new, in_dtype, batch, stream);
+}
+
 hipError_t launch_append(const PoolDesc& pool, const AppendSegment* segs_dev, const InlineSegments* segs_inline,
                          int32_t num_segments, const void* k_new, const void* v_new, kvc_dtype in_dtype,
                          int64_t total_rows, hipStream_t stream) {
@@ -2480,9 +2582,22 @@ hipError_t launch_cascade_typed(const DecodeArgs& a, const DecodePlan& plan, int
 hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& plan, const void* q, kvc_dtype q_dtype,
                          const int32_t* q_start, int32_t total_q, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* context_lens, int32_t max_context_len, int32_t batch, int32_t num_heads,
-                         float scale, void* out, void* workspace, hipEvent_t ev_start, hipEvent_t ev_end,
-                         hipStream_t stream) {
+                         float scale, void* out, void* workspace, const void* k_new, const void* v_new,
+                         hipEvent_t ev_start, hipEvent_t ev_end, hipStream_t stream) {
   DecodeArgs a;
+  // The step's newest rows: written by the static matrix-core walk itself
+  // (16-bit caches), else by an append kernel launched first.
+  a.k_new = a.v_new = nullptr;
+  if (k_new) {
+    if (decode_folds_append(plan, pool.dtype)) {
+      a.k_new = static_cast<const char*>(k_new);
+      a.v_new = static_cast<const char*>(v_new);
+    } else {
+      hipError_t e = launch_append_newest(pool, layer, block_table, max_blocks, context_lens, batch, k_new, v_new,
+                                          q_dtype, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
   const int64_t tb = tile_bytes(pool);
   const int64_t layer_bytes = (int64_t)pool.num_blocks * pool.num_kv_heads * tb;
   a.q = q;
@@ -2566,6 +2681,16 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
   }
   (void)q_dtype;
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  int64_t blocks = (n16 + 4 * 256 - 1) / (4 * 256);
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const u32x4*>(src),
+                     n16, sink, (int64_t)sink_words);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {

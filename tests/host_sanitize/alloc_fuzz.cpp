@@ -29,7 +29,7 @@ hipError_t launch_append(const PoolDesc&, const AppendSegment*, const InlineSegm
 }
 hipError_t launch_decode(const PoolDesc&, int32_t, const DecodePlan&, const void*, kvc_dtype, const int32_t*, int32_t,
                          const int32_t*, int32_t, const int32_t*, int32_t, int32_t, int32_t, float, void*, void*,
-                         hipEvent_t, hipEvent_t, hipStream_t) {
+                         const void*, const void*, hipEvent_t, hipEvent_t, hipStream_t) {
   return hipErrorNotSupported;
 }
 hipError_t launch_stream_copy(void*, const void*, size_t, hipStream_t) { return hipErrorNotSupported; }

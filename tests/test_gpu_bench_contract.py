@@ -1,7 +1,8 @@
 """bench.py's output line on the GPU: one JSON object with every field the
 benchmark contract names, numbers that agree with each other, and the
 oracle's CPU rate beside the GPU's.  A few short steps of the default
-workload (the 70B-shaped GQA layer) and of one several-token workload."""
+workload (the 70B-shaped GQA layer, with the other decode workloads under
+"also") and of one several-token workload."""
 import json
 import os
 import subprocess
@@ -20,7 +21,7 @@ ROOFLINE_FIELDS = {"bound", "achieved", "peak", "unit", "frac", "traffic"}
 
 def _bench(*args):
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
-                       timeout=110, cwd=ROOT)
+                       timeout=280, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1, r.stdout
@@ -48,6 +49,16 @@ def test_default_decode_line():
     cpu = res["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["cores"] >= 1 and cpu["value"] > 0
     assert cpu["sample"]
+    # the copy kernel's bandwidth on the same box, and the clocks seen under load
+    assert res["calibration"]["copy_read_plus_write_GBs"] > 0
+    assert "clocks" in res["env"]
+    # the other decode workloads of the same process
+    also = res["also"]
+    assert [(a["config_id"], bool(a["shared_prefix"])) for a in also] == [(2, False), (4, False), (4, True),
+                                                                          (5, False)]
+    for a in also:
+        assert a["value"] == pytest.approx(a["kv_bytes"] / (a["us_per_step"] * 1e-6) / 1e9, rel=2e-3)
+        assert 0 < a["roofline"]["frac"] < 1 and 0 < a["roofline"]["avg_launch_us"] < a["us_per_step"]
 
 
 def test_several_token_line():

@@ -227,6 +227,20 @@ def test_stream_copy_calibration_kernel():
     assert torch.equal(src, dst)
 
 
+def test_stream_read_calibration_kernel():
+    # every 16-byte chunk read once: the xor of what the waves store equals
+    # the xor of every word of the source (no two waves share a sink word here)
+    from paged_kv_cache_split_amd import stream_read
+    for n in (1 << 20, (1 << 22) + 48):
+        src = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+        sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+        stream_read(src, sink)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "int8", "f32"])
 def test_multi_layer_pool_and_cow(kv):
     # three layers share one block id space: appends write every layer, a
