@@ -334,6 +334,29 @@ kvc_status kvc_decode_attention(kvc_cache* cache, int32_t layer, const void* q, 
                                 float scale, void* out, void* workspace, size_t workspace_bytes,
                                 const kvc_decode_opts* opts, kvc_stream_t stream);
 
+/* Bytes of the static decode workspace kvc_decode_attention_static uses. */
+#define KVC_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* kvc_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation): the partials live in a static device
+ * array of KVC_STATIC_SCRATCH_BYTES (32 MiB) that the library's code object
+ * holds on each GPU it runs on until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine); it
+ * resolves the array's device address on its first call on a device.
+ * Arguments, options, checks and results are those of kvc_decode_attention,
+ * bit for bit; a shape whose kvc_decode_workspace_bytes exceeds
+ * KVC_STATIC_SCRATCH_BYTES gives KVC_E_WORKSPACE and launches nothing.  Every
+ * call on one GPU uses that GPU's one array: calls that overlap on one GPU
+ * (two streams, two threads) race and give undefined results; order them.
+ * Whatever a call needs zeroed (the pool's ticket counters) it zeroes itself
+ * on its stream. */
+kvc_status kvc_decode_attention_static(kvc_cache* cache, int32_t layer, const void* q, kvc_dtype q_dtype,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       float scale, void* out, const kvc_decode_opts* opts, kvc_stream_t stream);
+
 /* ---- several new query tokens per sequence --------------------------------- */
 
 /* Attention of several new tokens per sequence over the paged cache: the

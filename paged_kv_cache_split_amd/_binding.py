@@ -24,6 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, E_INVALID, E_UNSUPPORTED, E_NO_BLOCKS, E_NO_SEQ, E_SEQ_EXISTS, E_HIP, E_WORKSPACE = range(8)
 STATUS_NAMES = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_NO_BLOCKS", 4: "E_NO_SEQ",
                 5: "E_SEQ_EXISTS", 6: "E_HIP", 7: "E_WORKSPACE"}
+STATIC_SCRATCH_BYTES = 32 << 20   # KVC_STATIC_SCRATCH_BYTES
 # dtypes (kvc_dtype)
 F32, F16, BF16, FP8, INT8 = 0, 1, 2, 3, 4
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8, "int8": INT8}
@@ -33,7 +34,7 @@ SYMBOLS = [
     "kvc_set_scratch", "kvc_add_seq", "kvc_fork", "kvc_free_seq", "kvc_truncate", "kvc_truncate_many", "kvc_evict",
     "kvc_reserve_host",
     "kvc_get_table", "kvc_stats", "kvc_check_shared_prefix", "kvc_append", "kvc_export_tables", "kvc_decode_workspace_bytes",
-    "kvc_decode_attention", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_sched_create",
+    "kvc_decode_attention", "kvc_decode_attention_static", "kvc_extend_workspace_bytes", "kvc_extend_attention", "kvc_sched_create",
     "kvc_sched_destroy", "kvc_sched_submit", "kvc_sched_plan", "kvc_sched_commit", "kvc_sched_get_stats",
     "kvc_stream_copy", "kvc_stream_read", "kvc_last_error",
 ]
@@ -99,6 +100,8 @@ _sig = {
     "kvc_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
     "kvc_decode_attention": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f, _vp, _vp, _sz, ctypes.POINTER(KvcDecodeOpts), _vp]),
+    "kvc_decode_attention_static": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _vp, _i32, _i32, _i32,
+                                                   _i32, _i32, _i32, _f, _vp, ctypes.POINTER(KvcDecodeOpts), _vp]),
     "kvc_extend_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(KvcDecodeOpts)]),
     "kvc_extend_attention": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp, _sz,
@@ -406,6 +409,31 @@ class KVCache:
             ctypes.c_void_p(context_lens.data_ptr()), int(max_context_len), B, Hq, self.num_kv_heads, D,
             self.block_size, float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
             workspace.numel(), ctypes.byref(opts), _stream_ptr(stream)), "kvc_decode_attention")
+        return out
+
+    def decode_static(self, q, block_table, context_lens, max_context_len, scale, layer=0, out=None,
+                      partition_tokens=0, kernel=0, work_items=0, pool_pieces=0, pool_shift=0, stream=None, window=0,
+                      shared_prefix=0, k_new=None, v_new=None):
+        """decode() through kvc_decode_attention_static: no workspace, the
+        library's static one (calls on one GPU must not overlap)."""
+        import torch
+        B, Hq, D = q.shape
+        if not q.is_contiguous():
+            raise ValueError("q must be contiguous")
+        opts = KvcDecodeOpts(int(partition_tokens), int(kernel), int(work_items), int(pool_pieces), int(pool_shift),
+                             None, None, int(window), 0, int(shared_prefix))
+        if (k_new is None) != (v_new is None):
+            raise ValueError("k_new and v_new go together")
+        if k_new is not None:
+            opts.k_new, opts.v_new = k_new.data_ptr(), v_new.data_ptr()
+        if out is None:
+            out = torch.empty_like(q)
+        _check(_lib.kvc_decode_attention_static(
+            self._h, int(layer), ctypes.c_void_p(q.data_ptr()), _dtype_code(q.dtype),
+            ctypes.c_void_p(block_table.data_ptr()), int(block_table.shape[1]),
+            ctypes.c_void_p(context_lens.data_ptr()), int(max_context_len), B, Hq, self.num_kv_heads, D,
+            self.block_size, float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.byref(opts), _stream_ptr(stream)),
+            "kvc_decode_attention_static")
         return out
 
     def extend(self, q, query_start, max_query_len, block_table, context_lens, max_context_len, scale, layer=0,

@@ -959,6 +959,28 @@ kvc_status kvc_decode_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   return ok();
 }
 
+kvc_status kvc_decode_attention_static(kvc_cache* c, int32_t layer, const void* q, kvc_dtype q_dtype,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       float scale, void* out, const kvc_decode_opts* opts, kvc_stream_t stream) {
+  // The workspace is the library's static array of the current device;
+  // kvc_decode_attention makes every check, the size this plan needs against
+  // the array's included, before it launches anything.
+  void* ws = nullptr;
+  hipError_t e = kvc::static_scratch(&ws);
+  if (e != hipSuccess) return fail(KVC_E_HIP, "static workspace: %s", hipGetErrorString(e));
+  kvc_status st = kvc_decode_attention(c, layer, q, q_dtype, block_table, max_blocks_per_seq, context_lens,
+                                       max_context_len, batch, num_heads, num_kv_heads, head_dim, block_size, scale,
+                                       out, ws, KVC_STATIC_SCRATCH_BYTES, opts, stream);
+  if (st == KVC_E_WORKSPACE) {
+    const std::string why = g_last_error;
+    return fail(KVC_E_WORKSPACE, "%s: beyond the static workspace (%u bytes); use kvc_decode_attention with a "
+                "workspace of its own", why.c_str(), (unsigned)KVC_STATIC_SCRATCH_BYTES);
+  }
+  return st;
+}
+
 size_t kvc_extend_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_query_len, int32_t max_context_len, const kvc_decode_opts* opts) {
   if (batch < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || num_heads % num_kv_heads != 0) return 0;

@@ -198,6 +198,9 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
                          const void* v_new, hipEvent_t ev_start, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream);
+// Device address of the current device's static decode workspace
+// (KVC_STATIC_SCRATCH_BYTES bytes), resolved on the first call per device.
+hipError_t static_scratch(void** ptr);
 
 // Shared by the host sources (defined in kvc_host.cpp).
 kvc_status host_fail(kvc_status st, const char* msg);   // records msg as the thread's last error

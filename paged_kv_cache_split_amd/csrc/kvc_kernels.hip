@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kvc_internal.h"
@@ -2467,6 +2468,37 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
 }
 
 }  // namespace
+
+// The decode workspace of the allocation-free entry point: one array per
+// device, part of the library's code object (loaded with it, held until the
+// process ends).  Host code never passes `scratch` itself to a kernel -- on
+// the host the name stands for a host-side shadow -- but the device address
+// hipGetSymbolAddress returns for the current device, resolved once per
+// device below.
+static __device__ __align__(256) char scratch[KVC_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_copy_blocks(const PoolDesc& pool, const CowPair* pairs_dev, int32_t num_pairs, hipStream_t stream) {
   if (num_pairs <= 0) return hipSuccess;
