@@ -738,6 +738,16 @@ __device__ __forceinline__ float max_over_row_groups(float x) {
   return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
+// The P^T operand of a pair of weights as a bf16 hi part and a bf16 lo part:
+// hi = the top 16 bits of each weight (truncation; one byte permute packs the
+// pair), lo = the exact remainder w - hi rounded to bf16, so hi + lo is w to
+// ~2^-16 relative.
+__device__ __forceinline__ void split_bf16x2(float w0, float w1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t b0 = __float_as_uint(w0), b1 = __float_as_uint(w1);
+  hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+  lo = pack_bf16x2(w0 - __uint_as_float(b0 & 0xFFFF0000u), w1 - __uint_as_float(b1 & 0xFFFF0000u));
+}
+
 __device__ __forceinline__ float sum_over_row_groups(float x) {
   const uint32_t xb = __float_as_uint(x);
   const auto p16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
@@ -970,7 +980,7 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
   }
   l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
   // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
-  // ~2^-17 relative), so rounding the weights to 16 bits costs no accuracy
+  // ~2^-16 relative), so rounding the weights to 16 bits costs no accuracy
   // when the weighted values cancel.
   u32x2 pb, pl;
   if constexpr (KV == KVC_F16) {
@@ -983,10 +993,11 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
 #pragma unroll
       for (int e = 0; e < 4; ++e) pv[e] *= vsc;
     }
-    pb[0] = pack_bf16x2(pv[0], pv[1]);
-    pb[1] = pack_bf16x2(pv[2], pv[3]);
-    pl[0] = pack_bf16x2(pv[0] - bf16_lo(pb[0]), pv[1] - bf16_hi(pb[0]));
-    pl[1] = pack_bf16x2(pv[2] - bf16_lo(pb[1]), pv[3] - bf16_hi(pb[1]));
+    uint32_t h0, l0, h1, l1;
+    split_bf16x2(pv[0], pv[1], h0, l0);
+    split_bf16x2(pv[2], pv[3], h1, l1);
+    pb[0] = h0; pl[0] = l0;
+    pb[1] = h1; pl[1] = l1;
   }
 #pragma unroll
   for (int dd = 0; dd < NDD; ++dd) {
@@ -1967,8 +1978,14 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
           pb[i] = pack_f16x2(w[2 * i], w[2 * i + 1]);
           if constexpr (KVC_FLASH_P_LO) pl[i] = pack_f16x2(w[2 * i] - f16_lo(pb[i]), w[2 * i + 1] - f16_hi(pb[i]));
         } else {
-          pb[i] = pack_bf16x2(w[2 * i], w[2 * i + 1]);
-          if constexpr (KVC_FLASH_P_LO) pl[i] = pack_bf16x2(w[2 * i] - bf16_lo(pb[i]), w[2 * i + 1] - bf16_hi(pb[i]));
+          if constexpr (KVC_FLASH_P_LO) {
+            uint32_t hi, lo;
+            split_bf16x2(w[2 * i], w[2 * i + 1], hi, lo);
+            pb[i] = hi;
+            pl[i] = lo;
+          } else {
+            pb[i] = pack_bf16x2(w[2 * i], w[2 * i + 1]);
+          }
         }
       }
 #pragma unroll
