@@ -12,7 +12,10 @@ for many waves under random interleavings and asserts what the kernel relies
 on: every block is walked exactly once, by the process cursor, with the chunk id
 the merge expects; no pending range is overwritten; every query is loaded
 before its segment starts; the per-sequence records name exactly the chunks
-holding the sequence.  The GPU parity tests check the kernel itself.
+holding the sequence; and every partial slot the merge reads for a sequence
+(slots b + c for its recorded chunks c) is written by the same call, exactly
+once, while a sequence held by one chunk gets its output written by the walk
+and nothing read by the merge.  The GPU parity tests check the kernel itself.
 """
 import random
 
@@ -38,7 +41,7 @@ class Geo:
         ln = r1 - rm
         return rm + (j * ln + s.KP - 1) // s.KP, rm + ((j + 1) * ln + s.KP - 1) // s.KP, ww * (s.KP + 1) + 1 + j
 
-def run(seq_blocks, W_req, PF, pool_pieces, shift, rng, min_piece_turns=2):
+def run(seq_blocks, W_req, PF, pool_pieces, shift, rng, min_piece_turns=2, plant_whole_tail=False):
     TURN = PF + 1
     seq_start = [0]
     for nbk in seq_blocks: seq_start.append(seq_start[-1] + nbk)
@@ -50,6 +53,8 @@ def run(seq_blocks, W_req, PF, pool_pieces, shift, rng, min_piece_turns=2):
     counter = [0]
     processed = {}   # block -> chunk id
     seginfo = {}
+    partials = {}    # (sequence, chunk id) -> times the walk wrote that partial slot
+    outputs = {}     # sequence -> times the walk wrote its output directly
     def seq_holding(x):
         lo, hi = 0, batch - 1
         while lo < hi:
@@ -86,6 +91,13 @@ def run(seq_blocks, W_req, PF, pool_pieces, shift, rng, min_piece_turns=2):
                     assert bb not in seginfo
                     seginfo[bb] = (cc, geo.chunk_of_block(seq_start[bb + 1] - 1) - cc + 1)
         def finish():
+            # the segment's result: the output when it is the whole sequence,
+            # else the partial of (sequence, chunk)
+            if (plant_whole_tail or P['x0'] == P['sb']) and P['seg_end'] == P['eb']:
+                outputs[P['b']] = outputs.get(P['b'], 0) + 1
+            else:
+                key = (P['b'], P['c'])
+                partials[key] = partials.get(key, 0) + 1
             if P['proc_last']:
                 if not P['p_valid']: return
                 P['p_valid'] = False
@@ -153,6 +165,15 @@ def run(seq_blocks, W_req, PF, pool_pieces, shift, rng, min_piece_turns=2):
         c0, cnt = seginfo[b]
         chunks = sorted({processed[y] for y in range(seq_start[b], seq_start[b + 1])})
         assert chunks == list(range(c0, c0 + cnt)), (b, chunks, c0, cnt)
+        # what the merge reads for b was written by this call, once
+        if cnt <= 1:
+            assert outputs.get(b) == 1 and not any(k[0] == b for k in partials), (b, outputs.get(b))
+        else:
+            assert b not in outputs, ("a split sequence's output written by the walk", b)
+            for c in range(c0, c0 + cnt):
+                assert partials.get((b, c)) == 1, ("merge reads an unwritten or twice-written slot", b, c)
+    assert all(v == 1 for v in partials.values())
+    assert sum(1 for b in range(batch) if seq_blocks[b]) == len({k[0] for k in partials} | set(outputs))
     return KP
 
 
@@ -180,3 +201,28 @@ def test_planted_short_piece_is_caught():
         for _ in range(300):
             run([rng.randint(20, 300) for _ in range(6)], rng.choice([2, 4, 8]), 4, rng.choice([4, 8]), 1, rng,
                 min_piece_turns=0)
+
+
+@pytest.mark.parametrize("W,KP", [(1, 1), (2, 1), (1, 3), (3, 1)])
+def test_one_byte_ring_single_wave_pool(W, KP):
+    # the one-byte decode's deeper ring (PF 6, turns of 7 blocks) with a
+    # single wave or a single pool piece per wave: the wave's own pool piece
+    # comes back through its own ticket, read a turn late; tickets arrive in
+    # random order relative to the other waves' progress
+    rng = random.Random(100 * W + KP)
+    engaged = 0
+    for _ in range(150):
+        nb = rng.randint(1, 8)
+        seq_blocks = [rng.choice([0, 1, rng.randint(1, 40), rng.randint(60, 500)]) for _ in range(nb)]
+        engaged += bool(run(seq_blocks, W, 6, KP, rng.choice([1, 2]), rng))
+    assert engaged > 20
+
+
+def test_planted_unwritten_merge_slot_is_caught():
+    # a walk that takes a split sequence's last segment for the whole
+    # sequence writes the output there instead of its partial, so the merge
+    # would read a slot this call never wrote: the check must fail
+    rng = random.Random(3)
+    with pytest.raises(AssertionError, match="unwritten|written by the walk"):
+        for _ in range(50):
+            run([rng.randint(30, 200) for _ in range(3)], 4, 6, 0, 1, rng, plant_whole_tail=True)
