@@ -7,8 +7,9 @@
 // iteration, running sequences are preempted and recomputed later
 // ("苦猿的大模型日记 · Day45" PART 05 lists waiting, preemption, dropping the cache
 // and recomputing among what an engine does instead of failing); the
-// allocator's all-or-nothing KVC_E_NO_BLOCKS ("大模型推理加速核心KV Cache 复用机制与
-// 内存布局优化" §三, "OOM triggers preemption") is what the plan avoids.
+// allocator's all-or-nothing KVC_E_NO_BLOCKS (the out-of-blocks case of
+// "大模型推理加速核心KV Cache 复用机制与内存布局优化" §三, which hands the decision to
+// the scheduler) is what the plan avoids.
 //
 // Token accounting.  A request has a prompt of P tokens and produces up to M
 // tokens.  Its K/V rows enter the cache in position order: the prompt in

@@ -33,6 +33,8 @@ hipError_t launch_decode(const PoolDesc&, int32_t, const DecodePlan&, const void
   return hipErrorNotSupported;
 }
 hipError_t launch_stream_copy(void*, const void*, size_t, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_stream_read(const void*, size_t, uint32_t*, size_t, hipStream_t) { return hipErrorNotSupported; }
+hipError_t static_scratch(void**) { return hipErrorNotSupported; }
 }  // namespace kvc
 
 namespace {
