@@ -21,9 +21,10 @@ Modules and the passages each follows (pages are cited by title and section):
   nearest-even encode, written from the format definition.
 * ``fp8_policy`` -- the per-(block, KV head) scale rule used when fp8 KV is
   written.  Parity unpinned by the pages (they name FP8/E4M3 KV but give no
-  scale rule); pinned only by self-consistency invariants.
+  scale rule): the rule is a reading, whose rendering here is pinned by
+  invariants and by hand-worked codes and scales.
 * ``int8_policy`` -- the same kind of scale rule for a symmetric int8 code
   (round half to even, clamp to +-127).  Parity unpinned by the pages (they
-  list INT8 KV quantisation but give no scheme); pinned only by invariants.
+  list INT8 KV quantisation but give no scheme): a reading, pinned like fp8's.
 * ``sizing`` -- the KV bytes-per-token formula and pool sizes.
 """

@@ -19,6 +19,10 @@ For each write of ``c`` new rows into one (block, KV head) that already holds
 4. each new value x is stored as ``enc(x / s_new)``; if s_new == 0 every new
    value is zero and is stored as ``enc(x)`` (the signed zero code).
 
+The rule is a reading; this code's rendering of it (with the store model's
+split of a write into per-block runs) is pinned by codes and scales worked out
+by hand from the four steps above (tests/quant_literals.py).
+
 ``enc`` is E4M3FN round-to-nearest-even with saturation (``oracle.e4m3``).
 The dequantised value of a stored code is ``dec(code) * scale``.  The float32
 steps are written with NumPy float32 scalars so they round exactly as the

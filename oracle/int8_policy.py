@@ -23,6 +23,10 @@ For each write of ``c`` new rows into one (block, KV head) that already holds
 [-127, 127]; the code is stored as a two's-complement byte.  The value of a
 stored code is ``c * scale``.  The float32 steps use NumPy float32 scalars so
 they round exactly as the device's IEEE float32 arithmetic does.
+
+The rule is a reading; this code's rendering of it (with the store model's
+split of a write into per-block runs) is pinned by codes and scales worked out
+by hand from the steps above (tests/quant_literals.py).
 """
 from __future__ import annotations
 

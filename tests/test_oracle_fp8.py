@@ -2,8 +2,9 @@
 
 The codec is pinned to the OCP format table (golden fixture) and to torch's
 float8_e4m3fn dtype, an independent implementation of the same format.  The
-scale rule has no source on the pages ("parity unpinned"); it is checked only
-against its own stated invariants.
+scale rule has no source on the pages ("parity unpinned" by them); here it is
+checked against its own stated invariants, and test_oracle_quant_append.py pins
+its rendering to codes and scales worked out by hand.
 """
 import json
 import math
@@ -70,7 +71,8 @@ def test_encode_saturates_instead_of_nan():
     assert e4m3.encode_array(np.float32([1e9, -1e9])).tolist() == [0x7E, 0xFE]
 
 
-# -- scale rule (parity unpinned: invariants only) ------------------------------
+# -- scale rule (a reading, unpinned by the pages: invariants here; hand-worked
+#    codes and scales in test_oracle_quant_append.py) --------------------------
 
 def test_fresh_block_scale_and_error_bound():
     rng = np.random.default_rng(1)
@@ -123,7 +125,8 @@ def test_all_zero_rows_store_zero_codes():
     assert np.all(codes == 0x80)
 
 
-# -- int8 scale rule (parity unpinned by the pages: invariants only) -------------
+# -- int8 scale rule (a reading, unpinned by the pages: invariants here; hand-worked
+#    codes and scales in test_oracle_quant_append.py) --------------------------
 
 from oracle import int8_policy  # noqa: E402
 
