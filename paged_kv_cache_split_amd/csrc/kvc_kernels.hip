@@ -727,15 +727,27 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Max over the lanes l, l^16, l^32, l^48 (the four row groups of a wave)
-// with the gfx950 row-swap permutes: no LDS round trip.
+// max(a, b) of raw scores, which are finite or -inf (masked), never NaN: the
+// median of (a, b, +inf) is one instruction, where fmaxf adds a NaN-quieting
+// instruction per operand the compiler cannot prove already quiet (matrix-core
+// results, lane permutes).
+// (+inf goes through an empty asm so that the compiler does not fold the
+// median back into fmaxf and its quieting instructions.)
+__device__ __forceinline__ float score_max(float a, float b) {
+  float inf = __builtin_huge_valf();
+  asm("" : "+s"(inf));
+  return __builtin_amdgcn_fmed3f(a, b, inf);
+}
+
+// Max of raw scores over the lanes l, l^16, l^32, l^48 (the four row groups
+// of a wave) with the gfx950 row-swap permutes: no LDS round trip.
 __device__ __forceinline__ float max_over_row_groups(float x) {
   const uint32_t xb = __float_as_uint(x);
   const auto p16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
-  const float y = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const float y = score_max(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
   const uint32_t yb = __float_as_uint(y);
   const auto p32 = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
-  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+  return score_max(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
 // The P^T operand of a pair of weights as a bf16 hi part and a bf16 lo part:
@@ -955,7 +967,7 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
   }
   // the scale is positive, so the max of the raw scores, scaled, is the max
   // of the scaled scores; exp2(s * qk - m) is one fma
-  const float mx = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * qk;
+  const float mx = max_over_row_groups(score_max(score_max(sv[0], sv[1]), score_max(sv[2], sv[3]))) * qk;
   const bool grow = mx > m + kRescaleThreshold;
   if (__any(grow)) {
     const float mnew = grow ? mx : m;
