@@ -637,9 +637,21 @@ __global__ __launch_bounds__(64) void decode_fma_kernel(DecodeArgs a) {
 // Softmax runs on the score tile: a lane's 4 values plus two cross-group
 // shuffles give the per-head block max.
 // ---------------------------------------------------------------------------
+// The 16-row walks (decode, several tokens by row split) take the scores of
+// int8 caches on the f16 matrix cores: a K code c becomes the f16 value
+// 1152 + c with one byte permute per pair (f16 0x64XX is 1024 + XX, and
+// XX = c ^ 0x80 = c + 128), and the +1152 comes back out of the scores as a
+// per-column constant (1152 times the sum of the column's f16 query).  The
+// products with V stay bf16: a bias there would have to come back out of a
+// sum whose weights the matrix cores see rounded to 16 bits (and tiny ones as
+// f16 subnormals), and 1152 times those roundings is far above the result's
+// tolerance.
+constexpr bool qk_f16(kvc_dtype kv) { return kv == KVC_F16 || kv == KVC_INT8; }
+constexpr float kI8Bias = 1152.0f;
+
 template <kvc_dtype KV>
 __device__ __forceinline__ floatx4 mfma_qk(const u32x4& a, const u32x4& b, floatx4 c) {
-  if constexpr (KV == KVC_F16)
+  if constexpr (qk_f16(KV))
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
@@ -669,6 +681,13 @@ template <bool HI>
 __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
   constexpr int sh = HI ? 16 : 0;
   return pack_bf16x2((float)(int8_t)(w >> sh), (float)(int8_t)(w >> (sh + 8)));
+}
+
+// Four int8 codes (x = the code dword with every sign bit flipped, c + 128 as
+// unsigned bytes) -> two dwords of f16 pairs 1152 + c: byte k of the pair's
+// lane goes to the low byte of its 16-bit half, 0x64 to the high byte.
+__device__ __forceinline__ uint32_t i8x2_to_f16x2_biased(uint32_t x, bool hi) {
+  return __builtin_amdgcn_perm(0x64646464u, x, hi ? 0x04030402u : 0x04010400u);
 }
 
 template <kvc_dtype KV, bool HI>
@@ -767,6 +786,50 @@ __device__ __forceinline__ float sum_over_row_groups(float x) {
   const uint32_t yb = __float_as_uint(y);
   const auto p32 = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
   return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
+// int8 caches on the f16 matrix cores: the query operands of N column tiles
+// (q[N * NQK], bf16 as loaded) become f16 values q * 2^-e, with e >= 0 the
+// smallest exponent that keeps every query value of the wave below 2^15 (0
+// unless some |q| >= 2^15); kb[t] gets tile t's column bias, 1152 times the
+// sum of the column's f16 values over its four lane groups.  Returns 2^e,
+// which the score scale takes back.  Every lane of the wave takes part.
+template <int N, int NQK>
+__device__ __forceinline__ float int8_queries(u32x4* q, float* kb) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N * NQK; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(q[i][j])), __builtin_fabsf(bf16_hi(q[i][j]))));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  amax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(amax)));
+  // floor(log2(amax)) from the exponent field (amax >= 2^15 is a normal float)
+  const int e = amax >= 32768.0f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 14 : 0;
+  const float down = __builtin_ldexpf(1.0f, -e);
+#pragma unroll
+  for (int t = 0; t < N; ++t) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NQK; ++kk) {
+      u32x4& w = q[t * NQK + kk];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // values below f16's normal range become 0, so that the bias counts
+        // exactly what the matrix cores multiply whether or not they keep
+        // f16 subnormals
+        float f0 = bf16_lo(w[j]) * down, f1 = bf16_hi(w[j]) * down;
+        f0 = __builtin_fabsf(f0) < 0x1p-14f ? 0.0f : f0;
+        f1 = __builtin_fabsf(f1) < 0x1p-14f ? 0.0f : f1;
+        const uint32_t h = pack_f16x2(f0, f1);
+        sum += f16_lo(h) + f16_hi(h);
+        w[j] = h;
+      }
+    }
+    kb[t] = kI8Bias * sum_over_row_groups(sum);
+  }
+  return __builtin_ldexpf(1.0f, e);
 }
 
 // The reference max only moves when a block's max exceeds it by more than
@@ -927,6 +990,25 @@ struct BlockOps {
 
 template <kvc_dtype KV, int D>
 __device__ __forceinline__ void convert_codes(const KvBlock<KV, D>& cur, BlockOps<KV, D>& ops) {
+  if constexpr (KV == KVC_INT8) {
+    // K: biased f16 (1152 + c), a sign flip per dword and a byte permute per
+    // pair; V: bf16
+#pragma unroll
+    for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t x = cur.k[c2][j] ^ 0x80808080u;
+        ops.k[2 * c2 + (j >> 1)][2 * (j & 1)] = i8x2_to_f16x2_biased(x, false);
+        ops.k[2 * c2 + (j >> 1)][2 * (j & 1) + 1] = i8x2_to_f16x2_biased(x, true);
+      }
+    }
+#pragma unroll
+    for (int dd = 0; dd < D / 16; ++dd) {
+      ops.v[dd][0] = code2_to_bf16x2<KV, false>(cur.v[dd]);
+      ops.v[dd][1] = code2_to_bf16x2<KV, true>(cur.v[dd]);
+    }
+    return;
+  }
 #pragma unroll
   for (int c2 = 0; c2 < KvBlock<KV, D>::NK; ++c2) {
     ops.k[2 * c2][0] = code2_to_bf16x2<KV, false>(cur.k[c2][0]);
@@ -954,7 +1036,7 @@ __device__ __forceinline__ void convert_codes(const KvBlock<KV, D>& cur, BlockOp
 template <kvc_dtype KV, int D>
 __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, const u32x4* q, floatx4* acc,
                                           float& m, float& l, float qk, float vsc, bool edge, int t0, int ncol,
-                                          int col_lo) {
+                                          int col_lo, float kb = 0.0f) {
   constexpr int NQK = D / 32, NDD = D / 16;
   floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -967,7 +1049,10 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
   }
   // the scale is positive, so the max of the raw scores, scaled, is the max
   // of the scaled scores; exp2(s * qk - m) is one fma
-  const float mx = max_over_row_groups(score_max(score_max(sv[0], sv[1]), score_max(sv[2], sv[3]))) * qk;
+  // (int8: kb = the column's score bias 1152 * sum of its f16 query)
+  float mraw = max_over_row_groups(score_max(score_max(sv[0], sv[1]), score_max(sv[2], sv[3])));
+  if constexpr (KV == KVC_INT8) mraw -= kb;
+  const float mx = mraw * qk;
   const bool grow = mx > m + kRescaleThreshold;
   if (__any(grow)) {
     const float mnew = grow ? mx : m;
@@ -978,9 +1063,11 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
     for (int dd = 0; dd < NDD; ++dd) acc[dd] *= alpha;
     m = mnew;
   }
+  // exp2(s * qk - m), with int8's score bias taken out of the same fma
+  const float moff = KV == KVC_INT8 ? __builtin_fmaf(kb, qk, m) : m;
   float pv[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -m));
+  for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk, -moff));
   if (edge) {
     // Masked rows weigh 0 (forced: with m still -inf, or a zero one-byte
     // scale, the exponent above is NaN).  Scores of finite values are finite,
@@ -991,6 +1078,10 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
       if (sv[e] == kNegInf) pv[e] = 0.0f;
   }
   l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+  if constexpr (is_byte_code(KV)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+  }
   // P^T operand as a 16-bit hi part plus a 16-bit lo part (P = hi + lo to
   // ~2^-16 relative), so rounding the weights to 16 bits costs no accuracy
   // when the weighted values cancel.
@@ -1001,10 +1092,6 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
     pl[0] = pack_f16x2(pv[0] - f16_lo(pb[0]), pv[1] - f16_hi(pb[0]));
     pl[1] = pack_f16x2(pv[2] - f16_lo(pb[1]), pv[3] - f16_hi(pb[1]));
   } else {
-    if constexpr (is_byte_code(KV)) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pv[e] *= vsc;
-    }
     uint32_t h0, l0, h1, l1;
     split_bf16x2(pv[0], pv[1], h0, l0);
     split_bf16x2(pv[2], pv[3], h1, l1);
@@ -1170,6 +1257,13 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
         m[t] = kNegInf;
         l[t] = 0.0f;
       }
+      // int8 caches: column score biases and the score scale with the
+      // queries' 2^e (see int8_queries)
+      float kb[TPW];
+      float qk_seg = a.qk_scale;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) kb[t] = 0.0f;
+      if constexpr (KV == KVC_INT8) qk_seg *= int8_queries<TPW, NQK>(&qv[0][0], kb);
 
       if (cnt > 0) {
         // Physical block of local block j (scalar load).  Every prefetch is
@@ -1186,7 +1280,7 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
           const int blk_row = (tb + i) * kBS;          // the block's first row
           const int t0 = blk_row + 4 * r;              // this lane's first row
           if (blk_row + kBS > n) zero_rows_past_end<KV, D>(cur, n, t0);
-          float qk = a.qk_scale;
+          float qk = qk_seg;
           float vsc = 1.0f;
           BlockOps<KV, D> conv;                        // one-byte codes: converted once, for every tile
           if constexpr (is_byte_code(KV)) {
@@ -1204,7 +1298,7 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
             // of the sequence, or before the window's start (a wave-uniform
             // test): they are masked there.
             const bool edge = blk_row + kBS > n_lo[t] || blk_row < lo_hi[t];
-            tile_step<KV, D>(kop, vop, qv[t], acc[t], m[t], l[t], qk, vsc, edge, t0, ncol[t], col_lo[t]);
+            tile_step<KV, D>(kop, vop, qv[t], acc[t], m[t], l[t], qk, vsc, edge, t0, ncol[t], col_lo[t], kb[t]);
           }
         };
 
@@ -1360,6 +1454,9 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
   u32x4 q[NQK], q_next[NQK];
   floatx4 acc[NDD];
   float m = kNegInf, l = 0.0f;
+  // int8 caches: the column's score bias and the score scale with the
+  // query's 2^e (see int8_queries)
+  float kb = 0.0f, qk_seg = a.qk_scale;
   // Wave-uniform flags, one word (scalar registers are the scarce resource here).
   // The next range [na, nb) with id nc (its first block in sequence nbf) is
   // named by the prefetch cursor's ticket, entered by that cursor (F_NEXT
@@ -1412,6 +1509,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
     for (int dd = 0; dd < NDD; ++dd) acc[dd] = floatx4{0.f, 0.f, 0.f, 0.f};
     m = kNegInf;
     l = 0.0f;
+    if constexpr (KV == KVC_INT8) qk_seg = a.qk_scale * int8_queries<1, NQK>(q, &kb);
     // the query needed after this segment: the next segment's, or the next
     // range's first when that range is known
     bool want;
@@ -1474,7 +1572,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
     const int blk_row = (row0 + xp) * kBS;         // the block's first row
     const int t0 = blk_row + 4 * r;               // this lane's first row
     if (blk_row + kBS > n) zero_rows_past_end<KV, D>(cur, n, t0);
-    float qk = a.qk_scale;
+    float qk = qk_seg;
     float vsc = 1.0f;
     BlockOps<KV, D> conv;
     if constexpr (is_byte_code(KV)) {
@@ -1485,7 +1583,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
     const u32x4* kop = is_byte_code(KV) ? conv.k : cur.k;
     const u32x2* vop = is_byte_code(KV) ? conv.v : reinterpret_cast<const u32x2*>(cur.v);
     const bool edge = blk_row + kBS > n || blk_row < lo_hi;
-    tile_step<KV, D>(kop, vop, q, acc, m, l, qk, vsc, edge, t0, n, lo_hi);
+    tile_step<KV, D>(kop, vop, q, acc, m, l, qk, vsc, edge, t0, n, lo_hi, kb);
     ++xp;
     --left;
     if (xp == seg_end) finish();
