@@ -324,8 +324,11 @@ constexpr int32_t kMaxQueryTokens = 4096;
 // kernel without a row split by default (enough column tiles to fill the chip).
 constexpr int32_t kFlashMinQueryTokens = 64;
 // Cutting its rows: about this many waves in all, pieces of at least this many
-// steps (two blocks each), at most this many pieces per column tile.
-constexpr int64_t kFlashWaves = 8192;
+// steps (two blocks each), at most this many pieces per column tile.  (The
+// 2048-token prompt, kernel / step us: no cut 59 / 71, 4096 waves 35-37 /
+// 55-57, 8192 37 / 60, 16384 40 / 68: longer pieces leave fewer partials to
+// write and merge, shorter ones balance the causal tail.)
+constexpr int64_t kFlashWaves = 4096;
 constexpr int64_t kFlashMinSteps = 4;
 constexpr int64_t kFlashMaxPieces = 64;
 constexpr int32_t kFlashWavesPerGroup = 4;   // column tiles (waves) per work-group
