@@ -171,12 +171,13 @@ def profiled_traffic(key):
     """HBM bytes per split-kernel launch from a committed rocprofv3 summary
     (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy kernel's counts)
     of the workload `key`, or None when no summary was taken on the current
-    kernel source."""
+    sources (the kernels, and the host code that plans their launches)."""
     import glob
     import hashlib
-    src = os.path.join(ROOT, "paged_kv_cache_split_amd", "csrc", "kvc_kernels.hip")
+    csrc = os.path.join(ROOT, "paged_kv_cache_split_amd", "csrc")
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                      for f in ("kvc_kernels.hip", "kvc_host.cpp"))).hexdigest()
     except OSError:
         return None
     for fn in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):

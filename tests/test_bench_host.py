@@ -48,19 +48,23 @@ def test_window_bytes_cover_only_the_rows_inside_each_window():
     assert ab["tables"] == 4 * 64 * ((16385 + 15) // 16 - 12289 // 16) + 4 * 64
 
 
-def test_profiled_traffic_needs_the_current_kernel_source(tmp_path, monkeypatch):
+def test_profiled_traffic_needs_the_current_sources(tmp_path, monkeypatch):
     src_dir = tmp_path / "paged_kv_cache_split_amd" / "csrc"
     src_dir.mkdir(parents=True)
     (src_dir / "kvc_kernels.hip").write_bytes(b"// kernel source A\n")
+    (src_dir / "kvc_host.cpp").write_bytes(b"// host source A\n")
     prof = tmp_path / "profiles"
     prof.mkdir()
     import hashlib
-    sha_a = hashlib.sha256(b"// kernel source A\n").hexdigest()
+    sha_a = hashlib.sha256(b"// kernel source A\n// host source A\n").hexdigest()
     rec = {"workload_key": "config 3", "kernel_source_sha256": sha_a, "traffic_bytes_per_launch": 123}
     (prof / "k.md").write_text("# summary\n\n```\n" + json.dumps(rec) + "\n```\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.profiled_traffic("config 3") == (123, os.path.join("profiles", "k.md"))
     assert bench.profiled_traffic("config 4") is None
+    (src_dir / "kvc_host.cpp").write_bytes(b"// host source B\n")      # the launch planning changed since
+    assert bench.profiled_traffic("config 3") is None
+    (src_dir / "kvc_host.cpp").write_bytes(b"// host source A\n")
     (src_dir / "kvc_kernels.hip").write_bytes(b"// kernel source B\n")   # the kernel changed since
     assert bench.profiled_traffic("config 3") is None
 
