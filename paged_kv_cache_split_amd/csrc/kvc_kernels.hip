@@ -2457,26 +2457,37 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(u32x4* __restrict__ ds
 }
 
 // Plain streaming read (calibration): every 16-byte chunk of src read once
-// with non-temporal loads, four per thread in flight; each wave writes the
-// xor of its chunks to one word of sink, so no load is dead.
+// with non-temporal loads.  Each wave reads its own contiguous run, eight
+// 1 KiB wave loads in flight at a time (the decode's tiles are contiguous
+// runs too); each wave writes the xor of its chunks to one word of sink, so
+// no load is dead.
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                           uint32_t* __restrict__ sink, int64_t sink_words) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  // wave w's run: [r0, r1), cut in whole 64-chunk wave loads where possible
+  const int64_t per = ((n16 + waves - 1) / waves + 63) / 64 * 64;
+  const int64_t r0 = w * per, r1 = r0 + per < n16 ? r0 + per : n16;
   uint32_t acc = 0;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i), b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride), d = __builtin_nontemporal_load(src + i + 3 * stride);
-    const u32x4 x = a ^ b ^ c ^ d;
+  constexpr int U = 8;
+  int64_t i = r0 + lane;
+  for (; i + (U - 1) * 64 < r1; i += U * 64) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 64);
+    u32x4 x = v[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) x ^= v[u];
     acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
   }
-  for (; i < n16; i += stride) {
+  for (; i < r1; i += 64) {
     const u32x4 a = __builtin_nontemporal_load(src + i);
     acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
-  if ((threadIdx.x & 63) == 0) sink[((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) % sink_words] = acc;
+  if (lane == 0) sink[w % sink_words] = acc;
 }
 
 template <kvc_dtype KV, kvc_dtype QT, int D>
@@ -2844,8 +2855,8 @@ hipError_t launch_decode(const PoolDesc& pool, int32_t layer, const DecodePlan& 
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream) {
   const int64_t n16 = (int64_t)(bytes / 16);
-  int64_t blocks = (n16 + 4 * 256 - 1) / (4 * 256);
-  if (blocks > 256 * 16) blocks = 256 * 16;
+  int64_t blocks = (n16 + 8 * 256 - 1) / (8 * 256);
+  if (blocks > 256 * 8) blocks = 256 * 8;   // 8 work-groups of 4 waves per CU: one resident round
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const u32x4*>(src),
                      n16, sink, (int64_t)sink_words);
