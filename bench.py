@@ -222,8 +222,11 @@ def cpu_baseline(wl, values, budget_s):
         done_bytes += 2 * (lens[b] + 1) * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
         if wall > budget_s:
             break
+    all_bytes = sum(2 * (n + 1) * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype] for n in lens)
     return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
             "kind": "oracle",
+            # the whole step (every sequence) at the sample's rate, beside the GPU's us_per_step
+            "us_per_step": round(wall * all_bytes / done_bytes * 1e6, 1),
             "sample": f"{n_seq} of {wl.batch} sequences of the same workload ({done_bytes / 1e9:.3f} GB of KV, "
                       f"fp64 NumPy, {wall:.1f} s wall), one decode step each; "
                       f"os.cpu_count()={os.cpu_count()}"}
@@ -253,8 +256,11 @@ def cpu_baseline_window(wl, values, budget_s):
         done_bytes += 2 * (keep + 1) * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
         if wall > budget_s:
             break
+    all_bytes = sum(2 * min(int(n) + 1, wl.window) * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
+                    for n in wl.context_lens)
     return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
             "kind": "oracle",
+            "us_per_step": round(wall * all_bytes / done_bytes * 1e6, 1),
             "sample": f"{n_seq} of {wl.batch} sequences of the same workload ({done_bytes / 1e9:.3f} GB of KV in "
                       f"their windows, fp64 NumPy, {wall:.1f} s wall); os.cpu_count()={os.cpu_count()}"}
 
@@ -304,8 +310,11 @@ def cpu_baseline_extend(wl, values, budget_s):
         done_flops += 4 * wl.head_dim * wl.num_heads * (ql * (n - ql) + ql * (ql + 1) // 2)
         if wall > budget_s:
             break
+    all_flops = sum(4 * wl.head_dim * wl.num_heads * (int(ql) * int(L) + int(ql) * (int(ql) + 1) // 2)
+                    for ql, L in zip(wl.q_lens, lens))
     return {"value": round(done_flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": max(1, round(cpu / wall)),
             "kind": "oracle",
+            "us_per_step": round(wall * all_flops / done_flops * 1e6, 1),
             "sample": f"{n_seq} of {wl.batch} sequences of the same workload, fp64 NumPy, {wall:.1f} s wall; "
                       f"os.cpu_count()={os.cpu_count()}"}
 
