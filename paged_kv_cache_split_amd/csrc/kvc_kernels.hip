@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -87,6 +88,11 @@ constexpr int kBS = 16;                       // tokens per block (device work)
 #endif
 #ifndef KVC_PREFETCH_T4
 #define KVC_PREFETCH_T4 1
+#endif
+// Decode walk: at most this many finished segments per wave kept in LDS until
+// the wave's end (fewer when LDS is short; 0 writes every result at once).
+#ifndef KVC_STAGE_SLOTS
+#define KVC_STAGE_SLOTS 4
 #endif
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -427,6 +433,9 @@ struct DecodeArgs {
   // (NULL: the rows are already in the pool)
   const char* k_new;
   const char* v_new;
+  // decode walk: segments whose results are kept in LDS until the wave's end
+  // (slots of dynamic LDS after the scan; 0 = every result written at once)
+  int32_t stage_slots;
 };
 
 template <kvc_dtype QT>
@@ -1108,12 +1117,11 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
 // Output of one column tile: the normalised rows (out, in the 16-bit dtype of
 // q) or the partial (m, l, acc) at partial row rr.
 template <kvc_dtype KV, int D>
-__device__ __forceinline__ void write_out(const DecodeArgs& a, int64_t out_row, int h, int r, const floatx4* acc,
-                                          float lt) {
+__device__ __forceinline__ void write_out_row(const DecodeArgs& a, int64_t row, int r, const floatx4* acc, float lt) {
   const float inv = 1.0f / lt;
 #pragma unroll
   for (int dd = 0; dd < D / 16; ++dd) {
-    const int64_t o = (out_row * a.num_heads + h) * D + 16 * dd + 4 * r;
+    const int64_t o = row * D + 16 * dd + 4 * r;
     u32x2 wv;
     if constexpr (KV == KVC_F16) {
       wv[0] = pack_f16x2(acc[dd][0] * inv, acc[dd][1] * inv);
@@ -1124,6 +1132,12 @@ __device__ __forceinline__ void write_out(const DecodeArgs& a, int64_t out_row, 
     }
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = wv;
   }
+}
+
+template <kvc_dtype KV, int D>
+__device__ __forceinline__ void write_out(const DecodeArgs& a, int64_t out_row, int h, int r, const floatx4* acc,
+                                          float lt) {
+  write_out_row<KV, D>(a, out_row * a.num_heads + h, r, acc, lt);
 }
 
 template <int D>
@@ -1174,6 +1188,36 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
   int xa, xb, rm_unused;
   geo.wave_range(w, xa, xb, rm_unused);
   const int c = w;
+  // The chunk holding a sequence's first block records which chunks hold the
+  // sequence (for the merge), one sequence per lane, before any tile load:
+  // a store issued later would hold up the next load's wait (below).
+  if (g == 0 && threadIdx.x < 64 && blockIdx.z == gridDim.z - 1) {
+    int b0 = seq_holding(seq_start, a.batch, xa);
+    if (seq_start[b0] < xa) ++b0;               // it began in an earlier chunk
+    for (int bb = b0 + lane; bb < a.batch; bb += 64) {
+      const int s0 = seq_start[bb], s1 = seq_start[bb + 1];
+      if (s0 >= xb) break;
+      if (s1 > s0) {
+        a.ws_seginfo[2 * bb] = c;
+        a.ws_seginfo[2 * bb + 1] = geo.chunk_of_block(s1 - 1) - c + 1;
+      }
+    }
+  }
+  // Results of segments before the wave's last are kept in this wave's LDS
+  // slots (after the scan) and written after the walk: vector memory
+  // operations complete in issue order, so a store in the middle of the walk
+  // would hold up the next tile load's wait until the memory system
+  // acknowledged it, which under the walk's read stream takes microseconds.
+  // Per tile of a slot: the accumulator, then (m, l, destination) per lane;
+  // a destination is a partial row (>= 0), an output row r as -2 - r, or -1.
+  constexpr int TSLOT = NDD * 64 * 16 + 64 * 16;
+  char* stage = reinterpret_cast<char*>(seq_start + a.batch + 1);
+  stage += ((16 - ((uintptr_t)stage & 15)) & 15) + (threadIdx.x >> 6) * (16 + a.stage_slots * TPW * TSLOT);
+  int staged = 0;
+  auto flush_tile = [&](int64_t dst, const floatx4* ac, float mm, float lt) {
+    if (dst >= 0) write_partial<D>(a, dst, r, ac, mm, lt);
+    else if (dst <= -2) write_out_row<KV, D>(a, -2 - dst, r, ac, lt);
+  };
   {
     int b = seq_holding(seq_start, a.batch, xa);
     // Everything below that indexes memory is wave-uniform (scalar registers),
@@ -1187,11 +1231,6 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
       const int first = x - sb;                   // first block of this segment in the sequence's list
       const int count = seg_end - x;              // blocks in this segment
       const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
-      if (first == 0 && g == 0 && threadIdx.x == 0 && blockIdx.z == gridDim.z - 1) {
-        // the chunk holding a sequence's first block records which chunks hold it
-        a.ws_seginfo[2 * b] = c;
-        a.ws_seginfo[2 * b + 1] = geo.chunk_of_block(eb - 1) - c + 1;
-      }
       const int ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
       if (ct0 * 16 >= ql * G) {                   // no column of this sequence in the wave's tiles
         x = seg_end;
@@ -1343,24 +1382,51 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
         }
       }
       const bool whole = x == sb && seg_end == eb;   // the whole sequence is in this segment
+      const bool stage_it = seg_end < xb && staged < a.stage_slots;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        if (!active[t]) continue;
-        // l over the head's four lane groups
-        const float lt = sum_over_row_groups(l[t]);
-        if (!head_ok[t]) continue;
-        const int h = g * G + hh[t];
-        if (whole) {
-          write_out<KV, D>(a, q_row[t], h, r, acc[t], lt);
-        } else {
+        int64_t dst = -1;
+        float lt = 0.0f;
+        if (active[t]) {
+          // l over the head's four lane groups
+          lt = sum_over_row_groups(l[t]);
+          const int h = g * G + hh[t];
           // partial of (sequence b, chunk c) for this column: slot b + c is
           // unique, since every segment boundary advances the sequence, the
           // chunk, or both; one set of slots per query token index
-          const int tok = q_row[t] - q0;
-          write_partial<D>(a, ((int64_t)tok * a.num_heads + h) * slots + b + c, r, acc[t], m[t], lt);
+          if (head_ok[t])
+            dst = whole ? -2 - ((int64_t)q_row[t] * a.num_heads + h)
+                        : ((int64_t)(q_row[t] - q0) * a.num_heads + h) * slots + b + c;
+        }
+        if (stage_it) {
+          char* sl = stage + (staged * TPW + t) * TSLOT;
+#pragma unroll
+          for (int dd = 0; dd < NDD; ++dd) *reinterpret_cast<floatx4*>(sl + (dd * 64 + lane) * 16) = acc[t][dd];
+          *reinterpret_cast<u32x4*>(sl + NDD * 1024 + lane * 16) =
+              u32x4{__builtin_bit_cast(uint32_t, m[t]), __builtin_bit_cast(uint32_t, lt), (uint32_t)dst,
+                    (uint32_t)(dst >> 32)};
+        } else {
+          flush_tile(dst, acc[t], m[t], lt);
         }
       }
+      if (stage_it) ++staged;
       x = seg_end;
+    }
+  }
+  // the results kept in LDS, now that no load waits behind their stores
+  for (int sidx = 0; sidx < staged; ++sidx) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const char* sl = stage + (sidx * TPW + t) * TSLOT;
+      floatx4 ac[NDD];
+#pragma unroll
+      for (int dd = 0; dd < NDD; ++dd) ac[dd] = *reinterpret_cast<const floatx4*>(sl + (dd * 64 + lane) * 16);
+      const u32x4 e = *reinterpret_cast<const u32x4*>(sl + NDD * 1024 + lane * 16);
+      // (the elements go through scalars: hipcc's __builtin_bit_cast of a
+      // vector element reads element 0 whichever element is named)
+      const uint32_t em = e[0], el = e[1], dlo = e[2], dhi = e[3];
+      const int64_t dst = (int64_t)(((uint64_t)dhi << 32) | dlo);
+      flush_tile(dst, ac, __builtin_bit_cast(float, em), __builtin_bit_cast(float, el));
     }
   }
 }
@@ -1384,6 +1450,12 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
 // outlast two turns, which the pool's size test below guarantees; then the
 // prefetch cursor is also never more than one range ahead of the process
 // cursor, so one pending range is handed between them.
+// Bytes of one LDS slot holding a finished segment of the decode walk: the
+// accumulator (D/16 four-float registers per lane), m and l per lane, and the
+// segment's sequence, chunk and kind.
+template <int D>
+constexpr int stage_slot_bytes() { return (D / 16) * 64 * 16 + 64 * 8 + 16; }
+
 template <kvc_dtype KV, int D, int PF, bool POOL>
 __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_start) {
   constexpr int TURN = PF + 1;
@@ -1468,6 +1540,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
   constexpr int F_PEND = 8;   // the prefetch cursor has entered a range the process cursor has not
   constexpr int F_LAST = 16;  // the process cursor's segment is its range's last
   constexpr int F_WHOLE = 32; // the segment is its sequence's whole list
+  constexpr int F_STAGED = 256; // bits 8 and up: segments kept in LDS so far
   int flags = KP != 0 ? F_MORE : 0;
   int na = 0, nb = 0, nc = 0, nbf = 0;
 
@@ -1524,12 +1597,37 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
     }
     if (want) load_q(q_next, nb_q);
   };
-  // after the segment's last block: write it out, move to the next segment
+  // The results of segments before the wave's last go to LDS slots and are
+  // written out after the walk: vector memory operations complete in issue
+  // order, so a store issued in the middle of the walk would hold up every
+  // later tile load's wait until the memory system acknowledged it, which
+  // under the walk's own read stream takes several microseconds.
+  char* stage = reinterpret_cast<char*>(seq_start + a.batch + 1);
+  stage += (16 - ((uintptr_t)stage & 15)) & 15;
+  constexpr int SSLOT = stage_slot_bytes<D>();
+  auto write_result = [&](int bb, int cc, bool whole, const floatx4* ac, float mm, float lt) {
+    if (head_ok) {
+      if (whole) write_out<KV, D>(a, bb, h, r, ac, lt);
+      else write_partial<D>(a, (int64_t)h * slots + bb + cc, r, ac, mm, lt);
+    }
+  };
+  // after the segment's last block: write it out (or keep it in LDS), move
+  // to the next segment
   auto finish = [&]() {
     const float lt = sum_over_row_groups(l);
-    if (head_ok) {
-      if (flags & F_WHOLE) write_out<KV, D>(a, b, h, r, acc, lt);
-      else write_partial<D>(a, (int64_t)h * slots + b + c, r, acc, m, lt);
+    const bool final_write = (flags & F_LAST) && (!POOL || !(flags & F_PEND));
+    const int ns = flags / F_STAGED;
+    if (!POOL && !final_write && ns < a.stage_slots) {
+      char* sl = stage + ns * SSLOT;
+#pragma unroll
+      for (int dd = 0; dd < NDD; ++dd) *reinterpret_cast<floatx4*>(sl + (dd * 64 + lane) * 16) = acc[dd];
+      *reinterpret_cast<floatx2*>(sl + NDD * 1024 + lane * 8) = floatx2{m, lt};
+      if (lane == 0)
+        *reinterpret_cast<u32x4*>(sl + NDD * 1024 + 512) =
+            u32x4{(uint32_t)b, (uint32_t)c, (flags & F_WHOLE) ? 1u : 0u, 0u};
+      flags += F_STAGED;
+    } else {
+      write_result(b, c, (flags & F_WHOLE) != 0, acc, m, lt);
     }
     if (flags & F_LAST) {
       if (!POOL || !(flags & F_PEND)) return;  // the wave's last range is done
@@ -1675,6 +1773,22 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
     ph_next = next_phys();
     fetch(buf[(j + PF) % TURN], ph);
     process(buf[j]);
+  }
+  // the results kept in LDS, now that no load waits behind their stores
+  if constexpr (!POOL) {
+    const int ns = flags / F_STAGED;
+    for (int sidx = 0; sidx < ns; ++sidx) {
+      const char* sl = stage + sidx * SSLOT;
+      const u32x4 meta = *reinterpret_cast<const u32x4*>(sl + NDD * 1024 + 512);
+      const int bb = __builtin_amdgcn_readfirstlane((int)meta[0]);
+      const int cc = __builtin_amdgcn_readfirstlane((int)meta[1]);
+      const bool whole = __builtin_amdgcn_readfirstlane((int)meta[2]) != 0;
+      floatx4 ac[NDD];
+#pragma unroll
+      for (int dd = 0; dd < NDD; ++dd) ac[dd] = *reinterpret_cast<const floatx4*>(sl + (dd * 64 + lane) * 16);
+      const floatx2 ml = *reinterpret_cast<const floatx2*>(sl + NDD * 1024 + lane * 8);
+      write_result(bb, cc, whole, ac, ml[0], ml[1]);
+    }
   }
 }
 
@@ -2563,8 +2677,18 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
         if (D == 64) hipLaunchKernelGGL((decode_stream_kernel<KV, 64, KVC_STREAM_PF, true>), grid, dim3(64), scan_lds, s, a);
         else hipLaunchKernelGGL((decode_stream_kernel<KV, 128, KVC_STREAM_PF, true>), grid, dim3(64), scan_lds, s, a);
       } else {
-        if (D == 64) hipLaunchKernelGGL((decode_stream_kernel<KV, 64, KVC_STREAM_PF, false>), grid, dim3(64), scan_lds, s, a);
-        else hipLaunchKernelGGL((decode_stream_kernel<KV, 128, KVC_STREAM_PF, false>), grid, dim3(64), scan_lds, s, a);
+        // LDS slots for the walk's results before each wave's last, within
+        // the share of a CU's 160 KiB that each resident work-group (one wave)
+        // may take without lowering the waves resident per CU
+        DecodeArgs as = a;
+        const int64_t waves = (int64_t)a.work_items * a.num_kv_heads;
+        const int64_t per_cu = std::max<int64_t>(4, (waves + 255) / 256);
+        const int64_t budget = 163840 / per_cu - (int64_t)scan_lds - 16;
+        const int sslot = D == 64 ? stage_slot_bytes<64>() : stage_slot_bytes<128>();
+        as.stage_slots = (int32_t)std::max<int64_t>(0, std::min<int64_t>(KVC_STAGE_SLOTS, budget / sslot));
+        const size_t lds = scan_lds + (as.stage_slots > 0 ? 16 + (size_t)as.stage_slots * sslot : 0);
+        if (D == 64) hipLaunchKernelGGL((decode_stream_kernel<KV, 64, KVC_STREAM_PF, false>), grid, dim3(64), lds, s, as);
+        else hipLaunchKernelGGL((decode_stream_kernel<KV, 128, KVC_STREAM_PF, false>), grid, dim3(64), lds, s, as);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
@@ -2575,23 +2699,41 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
     }
     dim3 grid(a.work_items, a.num_kv_heads, tile_groups);
     dim3 block(64 * a.waves_per_group);
+    // LDS slots for each wave's results before its last segment, within the
+    // share of a CU's 160 KiB that each resident work-group may take (and
+    // 64 KiB per work-group)
+    DecodeArgs as = a;
+    {
+      const int tpw = std::max(1, std::min(4, tiles_per_wave));
+      const int64_t wpg = std::max(1, a.waves_per_group);
+      const int64_t waves = (int64_t)a.work_items * a.num_kv_heads * tile_groups * wpg;
+      const int64_t per_cu = std::max<int64_t>(4, (waves + 255) / 256);
+      const int64_t group = std::min<int64_t>(65536, 163840 * wpg / per_cu);
+      const int64_t per_wave = (group - (int64_t)scan_lds - 16) / wpg - 16;
+      const int64_t tslot = (int64_t)(D / 16) * 64 * 16 + 64 * 16;
+      as.stage_slots = (int32_t)std::max<int64_t>(0, std::min<int64_t>(KVC_STAGE_SLOTS, per_wave / (tpw * tslot)));
+    }
+    const size_t lds = scan_lds + 16 +
+                       (size_t)std::max(1, a.waves_per_group) *
+                           (16 + (size_t)as.stage_slots * std::max(1, std::min(4, tiles_per_wave)) *
+                                     ((size_t)(D / 16) * 64 * 16 + 64 * 16));
     // several tiles per wave leave fewer registers for the prefetch ring
     switch (tiles_per_wave) {
       case 1:
-        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, PF, 1>), grid, block, scan_lds, s, a);
-        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, PF, 1>), grid, block, scan_lds, s, a);
+        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, PF, 1>), grid, block, lds, s, as);
+        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, PF, 1>), grid, block, lds, s, as);
         break;
       case 2:
-        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T2, 2>), grid, block, scan_lds, s, a);
-        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T2, 2>), grid, block, scan_lds, s, a);
+        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T2, 2>), grid, block, lds, s, as);
+        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T2, 2>), grid, block, lds, s, as);
         break;
       case 3:
-        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T3, 3>), grid, block, scan_lds, s, a);
-        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T3, 3>), grid, block, scan_lds, s, a);
+        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T3, 3>), grid, block, lds, s, as);
+        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T3, 3>), grid, block, lds, s, as);
         break;
       default:
-        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T4, 4>), grid, block, scan_lds, s, a);
-        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T4, 4>), grid, block, scan_lds, s, a);
+        if (D == 64) hipLaunchKernelGGL((extend_mfma_kernel<KV, 64, KVC_PREFETCH_T4, 4>), grid, block, lds, s, as);
+        else hipLaunchKernelGGL((extend_mfma_kernel<KV, 128, KVC_PREFETCH_T4, 4>), grid, block, lds, s, as);
         break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
