@@ -219,6 +219,16 @@ __device__ __forceinline__ int attend_len(const int32_t* context_lens, int b, in
   return n < cap ? n : cap;
 }
 
+// The same for a wave-uniform b, read with a scalar load: a vector load whose
+// result is needed at once makes the wave wait for every vector load issued
+// before it (they complete in issue order), i.e. for the tiles in flight.
+__device__ __forceinline__ int attend_len_s(const int32_t* context_lens, int b, int max_ctx, int max_blocks) {
+  int n = ((const_i32_kptr)context_lens)[b];
+  n = n < max_ctx ? n : max_ctx;
+  int cap = max_blocks * kBS;
+  return n < cap ? n : cap;
+}
+
 // ---------------------------------------------------------------------------
 // Copy-on-write: copy whole blocks (every layer, head, K and V, fp8 scales).
 // grid (num_pairs, num_layers), 256 threads.
@@ -1230,7 +1240,7 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
       const int seg_end = eb < xb ? eb : xb;
       const int first = x - sb;                   // first block of this segment in the sequence's list
       const int count = seg_end - x;              // blocks in this segment
-      const int n = __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, b, a.max_ctx, a.max_blocks));
+      const int n = __builtin_amdgcn_readfirstlane(attend_len_s(a.context_lens, b, a.max_ctx, a.max_blocks));
       const int ql = __builtin_amdgcn_readfirstlane(query_len(a, b, n));
       if (ct0 * 16 >= ql * G) {                   // no column of this sequence in the wave's tiles
         x = seg_end;
@@ -1489,7 +1499,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
   const int win = a.window;
 
   auto seq_len = [&](int bb) -> int {
-    return __builtin_amdgcn_readfirstlane(attend_len(a.context_lens, bb, a.max_ctx, a.max_blocks));
+    return __builtin_amdgcn_readfirstlane(attend_len_s(a.context_lens, bb, a.max_ctx, a.max_blocks));
   };
   auto start_of = [&](int bb) -> int { return __builtin_amdgcn_readfirstlane(seq_start[bb]); };
   // Block-table row of sequence bb indexed by list position: entry x is the
