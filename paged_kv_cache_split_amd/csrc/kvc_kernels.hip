@@ -311,7 +311,27 @@ __global__ __launch_bounds__(64) void append_copy_kernel(PoolDesc p, SEGS segs, 
     u32x4 val = *reinterpret_cast<const u32x4*>(ksrc + r * row_bytes + c * 16);
     *reinterpret_cast<u32x4*>(kt + ((int64_t)c * kBS + sg.offset + r) * 16) = val;
   }
-  // V: element (r, d) -> tile[d][offset + r]
+  // V: element (r, d) -> tile[d][offset + r].  A whole block of 16-bit rows
+  // (a prompt or a long chunk) goes one dim per lane: the lane gathers the
+  // dim's 16 values (each row's values are read by consecutive lanes) and
+  // writes the tile row's 32 bytes at once, so the wave's stores are 2 KiB
+  // contiguous instead of 2 bytes every 32.
+  if constexpr (EBYTES == 2) {
+    if (sg.count == kBS && sg.offset == 0) {
+      for (int d = threadIdx.x; d < D; d += 64) {
+        uint32_t w[kBS / 2];
+#pragma unroll
+        for (int r = 0; r < kBS; r += 2) {
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(vsrc + r * row_bytes + (int64_t)d * 2);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(vsrc + (r + 1) * row_bytes + (int64_t)d * 2);
+          w[r / 2] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(vt + (int64_t)d * kBS * 2) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(vt + (int64_t)d * kBS * 2 + 16) = u32x4{w[4], w[5], w[6], w[7]};
+      }
+      return;
+    }
+  }
   for (int i = threadIdx.x; i < sg.count * D; i += 64) {
     int r = i / D, d = i % D;
     const char* s = vsrc + r * row_bytes + (int64_t)d * EBYTES;
