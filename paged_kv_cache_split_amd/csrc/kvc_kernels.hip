@@ -1089,11 +1089,17 @@ __device__ __forceinline__ void tile_step(const u32x4* kop, const u32x2* vop, co
   // the scale is positive, so the max of the raw scores, scaled, is the max
   // of the scaled scores; exp2(s * qk - m) is one fma
   // (int8: kb = the column's score bias 1152 * sum of its f16 query)
-  float mraw = max_over_row_groups(score_max(score_max(sv[0], sv[1]), score_max(sv[2], sv[3])));
-  if constexpr (KV == KVC_INT8) mraw -= kb;
-  const float mx = mraw * qk;
-  const bool grow = mx > m + kRescaleThreshold;
-  if (__any(grow)) {
+  // The column's reference max moves only when one of its 16 scores passes
+  // it by the threshold, so each lane first tests its own 4: only when some
+  // lane's do is the column max (over the four lanes holding the column)
+  // formed.  The outcome is the same as testing the column max every block.
+  float lraw = score_max(score_max(sv[0], sv[1]), score_max(sv[2], sv[3]));
+  if constexpr (KV == KVC_INT8) lraw -= kb;
+  if (__any(lraw * qk > m + kRescaleThreshold)) {
+    float mraw = max_over_row_groups(score_max(score_max(sv[0], sv[1]), score_max(sv[2], sv[3])));
+    if constexpr (KV == KVC_INT8) mraw -= kb;
+    const float mx = mraw * qk;
+    const bool grow = mx > m + kRescaleThreshold;
     const float mnew = grow ? mx : m;
     // (a column that has seen no row yet keeps m = -inf: alpha 1, not NaN)
     const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
