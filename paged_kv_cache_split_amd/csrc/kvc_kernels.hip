@@ -2193,15 +2193,17 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
       m1 = fmaxf(m1, s[8 + e]);
     }
     // (-inf * 0 is NaN: fmaxf keeps the other operand, and a column with no
-    // visible row in the step keeps its reference)
+    // visible row in the step keeps its reference). Both halves of the wave
+    // hold the same column and reference, so the column's max exceeds the
+    // reference exactly when one half's does: the swap is needed only then.
     float mx = fmaxf(m0 * qk0, m1 * qk1);
-    {
-      const uint32_t xb = __float_as_uint(mx);
-      const auto p32 = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
-      mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
-    }
-    const bool grow = mx > m + kRescaleThreshold;
-    if (__any(grow)) {
+    if (__any(mx > m + kRescaleThreshold)) {
+      {
+        const uint32_t xb = __float_as_uint(mx);
+        const auto p32 = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+        mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+      }
+      const bool grow = mx > m + kRescaleThreshold;
       const float mnew = grow ? mx : m;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
       l *= alpha;
