@@ -97,7 +97,8 @@ typedef enum kvc_dtype {
 
 typedef struct kvc_config {
   int32_t num_layers;     /* >= 1 */
-  int32_t num_kv_heads;   /* >= 1 */
+  int32_t num_kv_heads;   /* >= 1; one block of one layer, num_kv_heads x block_size x head_dim x dtype
+                             bytes, below 4 GiB (else KVC_E_UNSUPPORTED) */
   int32_t head_dim;       /* 64 or 128 */
   int32_t block_size;     /* tokens per block; device work needs 16, bookkeeping accepts 1..256 */
   int32_t num_blocks;     /* physical blocks in the pool, >= 1 */

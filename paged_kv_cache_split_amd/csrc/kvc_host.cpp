@@ -515,6 +515,12 @@ kvc_status kvc_create(const kvc_config* cfg, kvc_cache** out) {
   if (!valid_dtype(cfg->kv_dtype)) return fail(KVC_E_INVALID, "unknown kv_dtype %d", (int)cfg->kv_dtype);
   if ((int64_t)cfg->num_blocks * cfg->block_size > INT32_MAX)
     return fail(KVC_E_INVALID, "num_blocks * block_size must fit int32 slot numbers");
+  // the kernels form a block's offset as a 32 x 32-bit product of its id and
+  // the bytes of one block of one layer (all KV heads)
+  if ((int64_t)cfg->num_kv_heads * cfg->block_size * cfg->head_dim * (int64_t)kvc::dtype_bytes(cfg->kv_dtype) >
+      (int64_t)UINT32_MAX)
+    return fail(KVC_E_UNSUPPORTED, "one block of one layer (num_kv_heads * block_size * head_dim * dtype bytes) "
+                                   "must be below 4 GiB");
   kvc_cache* c = new (std::nothrow) kvc_cache();
   if (!c) return fail(KVC_E_INVALID, "out of host memory");
   c->cfg = *cfg;

@@ -2282,7 +2282,11 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   auto dma_stage = [&](int stg, Ids id) {
     char* base = lds + stg * SBYTES;
     // the two blocks' tiles of this head (wave-uniform offsets)
-    const int64_t o0 = (int64_t)id.p0 * block_stride + head_off, o1 = (int64_t)id.p1 * block_stride + head_off;
+    // (block ids are clamped to 0 .. num_blocks - 1, and one block of one
+    // layer is below 4 GiB: a 32 x 32-bit product)
+    const uint32_t bs32 = (uint32_t)block_stride;
+    const int64_t o0 = (int64_t)((uint64_t)(uint32_t)id.p0 * bs32) + head_off;
+    const int64_t o1 = (int64_t)((uint64_t)(uint32_t)id.p1 * bs32) + head_off;
 #pragma unroll
     for (int i = 0; i < PERD; ++i) {
       const int L = i * NT + tid;
@@ -2315,14 +2319,16 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
       for (int j = 0; j < NSTAGE - 1; ++j)
         if (s_begin + j < s_end) dma_stage(j, ids_of(s_begin + j));
       Ids idn = ids_of(s_begin + NSTAGE - 1);
-      for (int st = s_begin; st < s_end; ++st) {
-        const int i = st - s_begin, buf = i % NSTAGE;
+      // stage of step st, and the stage that takes the loads of st + NSTAGE - 1
+      int buf = 0, lbuf = NSTAGE - 1;
+      for (int st = s_begin; st < s_end;
+           ++st, buf = (buf + 1 == NSTAGE ? 0 : buf + 1), lbuf = (lbuf + 1 == NSTAGE ? 0 : lbuf + 1)) {
         const int ahead = min(s_end - 1 - st, NSTAGE - 2);   // later steps whose loads are in flight
         if (NSTAGE > 3 && ahead >= 2) vm_wait<(NSTAGE > 3 ? 2 : 1) * PERD>();
         else if (ahead >= 1) vm_wait<PERD>();
         else vm_wait<0>();
         wg_barrier();
-        if (st + NSTAGE - 1 < s_end) dma_stage((i + NSTAGE - 1) % NSTAGE, idn);
+        if (st + NSTAGE - 1 < s_end) dma_stage(lbuf, idn);
         idn = ids_of(st + NSTAGE);
         const int k0 = (jb0 + 2 * st) * kBS;
         if (tile_ok && k0 < w_hi && k0 + 2 * kBS > w_lo) {

@@ -198,6 +198,20 @@ def test_create_rejects_bad_configs(field, value, status):
     assert len(B.lib().kvc_last_error()) > 0
 
 
+def test_create_bounds_one_block_of_one_layer_below_4_gib():
+    # the kernels form a block's byte offset as a 32 x 32-bit product:
+    # num_kv_heads * block_size * head_dim * dtype bytes must stay below 2^32
+    # (16 * 64 * 2 bytes per KV head here)
+    h = ctypes.c_void_p()
+    cfg = _cfg(num_kv_heads=1 << 21)
+    assert B.lib().kvc_create(ctypes.byref(cfg), ctypes.byref(h)) == B.E_UNSUPPORTED
+    assert not h.value
+    cfg = _cfg(num_kv_heads=(1 << 21) - 1)
+    assert B.lib().kvc_create(ctypes.byref(cfg), ctypes.byref(h)) == B.OK
+    assert h.value
+    B.lib().kvc_destroy(h)
+
+
 def test_create_rejects_bad_free_order():
     h = ctypes.c_void_p()
     order = (ctypes.c_int32 * 8)(0, 1, 2, 3, 4, 5, 6, 6)
