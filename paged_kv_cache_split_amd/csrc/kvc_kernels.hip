@@ -210,6 +210,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ int clamp_block(int b, int num_blocks) {
   return (b < 0 || b >= num_blocks) ? 0 : b;
 }
+// x * y for x, y in 0 .. 2^32 - 1 (a clamped block id times the bytes of one
+// block of one layer, below 4 GiB, or times the KV head count): one 32 x
+// 32-bit product instead of a signed 64-bit one
+__device__ __forceinline__ int64_t mul_u32(int x, int64_t y) {
+  return (int64_t)((uint64_t)(uint32_t)x * (uint32_t)y);
+}
 
 // Tokens to attend for sequence b, clamped so every access stays in bounds.
 __device__ __forceinline__ int attend_len(const int32_t* context_lens, int b, int max_ctx, int max_blocks) {
@@ -1382,11 +1388,11 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
         // unrolling.
         KvBlock<KV, D> buf[PF + 1];
         auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
-          const int64_t o = (int64_t)ph * block_stride + head_off;
+          const int64_t o = mul_u32(ph, block_stride) + head_off;
           load_block<KV, D>(dst, a.k + o, a.v + o, koff, voff);
           if constexpr (is_byte_code(KV)) {
-            dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
-            dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
+            dst.ks = ((const_f32_kptr)a.k_scale)[mul_u32(ph, a.num_kv_heads) + g];
+            dst.vs = ((const_f32_kptr)a.v_scale)[mul_u32(ph, a.num_kv_heads) + g];
           }
         };
 #pragma unroll
@@ -1761,11 +1767,11 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
   begin(xa);
   KvBlock<KV, D> buf[TURN];
   auto fetch = [&](KvBlock<KV, D>& dst, int ph) {
-    const int64_t o = (int64_t)ph * block_stride + head_off;
+    const int64_t o = mul_u32(ph, block_stride) + head_off;
     load_block<KV, D>(dst, a.k + o, a.v + o, koff, voff);
     if constexpr (is_byte_code(KV)) {
-      dst.ks = ((const_f32_kptr)a.k_scale)[(int64_t)ph * a.num_kv_heads + g];
-      dst.vs = ((const_f32_kptr)a.v_scale)[(int64_t)ph * a.num_kv_heads + g];
+      dst.ks = ((const_f32_kptr)a.k_scale)[mul_u32(ph, a.num_kv_heads) + g];
+      dst.vs = ((const_f32_kptr)a.v_scale)[mul_u32(ph, a.num_kv_heads) + g];
     }
   };
 #pragma unroll
@@ -2075,14 +2081,14 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
       const bool is_v = c >= 2 * CHB;
       const int cc = is_v ? c - 2 * CHB : c;
       const int blk = cc / CHB, r16 = cc - blk * CHB;
-      const char* base = (is_v ? a.v : a.k) + (int64_t)(blk ? id.p1 : id.p0) * block_stride + head_off;
+      const char* base = (is_v ? a.v : a.k) + mul_u32(blk ? id.p1 : id.p0, block_stride) + head_off;
       r.w[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)(is_v ? r16 : k_piece(r16)) * 16);
     }
     if constexpr (is_byte_code(KV)) {
-      r.ks0 = ((const_f32_kptr)a.k_scale)[(int64_t)id.p0 * a.num_kv_heads + g];
-      r.ks1 = ((const_f32_kptr)a.k_scale)[(int64_t)id.p1 * a.num_kv_heads + g];
-      r.vs0 = ((const_f32_kptr)a.v_scale)[(int64_t)id.p0 * a.num_kv_heads + g];
-      r.vs1 = ((const_f32_kptr)a.v_scale)[(int64_t)id.p1 * a.num_kv_heads + g];
+      r.ks0 = ((const_f32_kptr)a.k_scale)[mul_u32(id.p0, a.num_kv_heads) + g];
+      r.ks1 = ((const_f32_kptr)a.k_scale)[mul_u32(id.p1, a.num_kv_heads) + g];
+      r.vs0 = ((const_f32_kptr)a.v_scale)[mul_u32(id.p0, a.num_kv_heads) + g];
+      r.vs1 = ((const_f32_kptr)a.v_scale)[mul_u32(id.p1, a.num_kv_heads) + g];
     }
   };
   // Store one step's pieces into LDS buffer buf.  K row of block blk, token t
@@ -2282,11 +2288,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   auto dma_stage = [&](int stg, Ids id) {
     char* base = lds + stg * SBYTES;
     // the two blocks' tiles of this head (wave-uniform offsets)
-    // (block ids are clamped to 0 .. num_blocks - 1, and one block of one
-    // layer is below 4 GiB: a 32 x 32-bit product)
-    const uint32_t bs32 = (uint32_t)block_stride;
-    const int64_t o0 = (int64_t)((uint64_t)(uint32_t)id.p0 * bs32) + head_off;
-    const int64_t o1 = (int64_t)((uint64_t)(uint32_t)id.p1 * bs32) + head_off;
+    const int64_t o0 = mul_u32(id.p0, block_stride) + head_off, o1 = mul_u32(id.p1, block_stride) + head_off;
 #pragma unroll
     for (int i = 0; i < PERD; ++i) {
       const int L = i * NT + tid;
