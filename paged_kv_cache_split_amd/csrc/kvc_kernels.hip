@@ -54,6 +54,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // decode kernel writes.
 typedef const int32_t __attribute__((address_space(4)))* const_i32_kptr;
 typedef const float __attribute__((address_space(4)))* const_f32_kptr;
+// p[i] for 0 <= i < 2^30 through a 32-bit byte offset, which the scalar load
+// takes as its offset register (no 64-bit index arithmetic)
+__device__ __forceinline__ int32_t ld_u32_index(const_i32_kptr p, int i) {
+  typedef const char __attribute__((address_space(4)))* const_c_kptr;
+  return *(const_i32_kptr)((const_c_kptr)p + ((uint32_t)i << 2));
+}
 
 constexpr int kBS = 16;                       // tokens per block (device work)
 
@@ -208,7 +214,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ int clamp_block(int b, int num_blocks) {
-  return (b < 0 || b >= num_blocks) ? 0 : b;
+  // (num_blocks >= 1: one unsigned compare tests both ends)
+  return (uint32_t)b < (uint32_t)num_blocks ? b : 0;
 }
 // x * y for x, y in 0 .. 2^32 - 1 (a clamped block id times the bytes of one
 // block of one layer, below 4 GiB, or times the KV head count): one 32 x
@@ -1353,7 +1360,7 @@ __device__ __forceinline__ void attend_extend(const DecodeArgs& a, int* seq_star
         const const_i32_kptr row = (const_i32_kptr)(a.block_table + (int64_t)b * a.max_blocks + tb);
         auto phys_of = [&](int j) -> int {
           j = j < cnt ? j : cnt - 1;
-          return clamp_block(row[j], a.num_blocks);
+          return clamp_block(ld_u32_index(row, j), a.num_blocks);
         };
 
         auto process = [&](KvBlock<KV, D>& cur, int i) {
@@ -1702,7 +1709,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs& a, int* seq_star
         ebf = start_of(bf + 1);
         rowf = row_of(bf, seq_len(bf));
       }
-      ph_last = clamp_block(rowf[xf], a.num_blocks);
+      ph_last = clamp_block(ld_u32_index(rowf, xf), a.num_blocks);
       ++xf;
       ++left;
     }
@@ -2062,7 +2069,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
     int p0, p1;
   };
   auto phys = [&](int j) -> int {   // table block j, or block jb0 past the end (its rows are all masked)
-    return clamp_block(row[j < jb1 ? j : jb0], a.num_blocks);
+    return clamp_block(ld_u32_index(row, j < jb1 ? j : jb0), a.num_blocks);
   };
   auto ids_of = [&](int st) -> Ids {
     st = st < s_end ? st : s_end - 1;
