@@ -327,14 +327,22 @@ constexpr int32_t kFlashMinQueryTokens = 64;
 // steps (two blocks each), at most this many pieces per column tile.  (The
 // 2048-token prompt, kernel / step us: no cut 59 / 71, 4096 waves 35-37 /
 // 55-57, 8192 37 / 60, 16384 40 / 68: longer pieces leave fewer partials to
-// write and merge, shorter ones balance the causal tail.)
+// write and merge, shorter ones balance the causal tail.)  With 16-bit codes
+// and head_dim 64 the kernel holds three waves per SIMD, so one round is 3072
+// waves (same prompt: 2048 waves 54 us, 3072 32, 4096 34, 6144 37).
 constexpr int64_t kFlashWaves = 4096;
+constexpr int64_t kFlashWaves16D64 = 3072;
+int64_t flash_waves_target(int kv, int32_t head_dim) {
+  return ((kv == KVC_F16 || kv == KVC_BF16) && head_dim == 64) ? kFlashWaves16D64 : kFlashWaves;
+}
 constexpr int64_t kFlashMinSteps = 4;
 constexpr int64_t kFlashMaxPieces = 64;
 constexpr int32_t kFlashWavesPerGroup = 4;   // column tiles (waves) per work-group
 
-bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t max_q, int32_t max_context_len,
-                 int kv, const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
+// kv: the cache's dtype, or -1 when unknown (a workspace query: the plan then
+// takes the largest cut any dtype takes)
+bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_q,
+                 int32_t max_context_len, int kv, const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
   if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2 && opts->kernel != 3) ||
                opts->window < 0 || opts->tiles_per_wave < 0 || opts->tiles_per_wave > 4))
     return false;
@@ -363,8 +371,9 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
     // diagonal's far end do not run alone; about kFlashWaves waves in all.
     const int64_t waves = (int64_t)batch * num_kv_heads * plan->tile_groups * kFlashWavesPerGroup;
     const int64_t max_steps = ((int64_t)(max_context_len + 15) / 16 + 1) / 2 + 1;
-    if (waves < kFlashWaves / 2 && max_steps > kFlashMinSteps) {
-      int64_t S = std::max<int64_t>(kFlashMinSteps, (max_steps * waves + kFlashWaves - 1) / kFlashWaves);
+    const int64_t target = flash_waves_target(kv, head_dim);
+    if (waves < target / 2 && max_steps > kFlashMinSteps) {
+      int64_t S = std::max<int64_t>(kFlashMinSteps, (max_steps * waves + target - 1) / target);
       int64_t pieces = (max_steps + S - 1) / S;
       const int64_t cap = std::min<int64_t>(kFlashMaxPieces, 65535 / plan->tile_groups);
       if (pieces > cap) {
@@ -994,7 +1003,7 @@ size_t kvc_extend_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
                                   int32_t max_query_len, int32_t max_context_len, const kvc_decode_opts* opts) {
   if (batch < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || num_heads % num_kv_heads != 0) return 0;
   kvc::DecodePlan p;
-  if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len, max_context_len, -1, opts, &p)) return 0;
+  if (!plan_extend(batch, num_heads, num_kv_heads, head_dim, max_query_len, max_context_len, -1, opts, &p)) return 0;
   return workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, p);
 }
 
@@ -1017,7 +1026,7 @@ kvc_status kvc_extend_attention(kvc_cache* c, int32_t layer, const void* q, kvc_
   const kvc_dtype kv = c->cfg.kv_dtype;
   if (kv == KVC_F32) return fail(KVC_E_UNSUPPORTED, "several query tokens need a 16-bit or fp8 cache");
   kvc::DecodePlan plan;
-  if (!plan_extend(batch, num_heads, num_kv_heads, max_query_len,
+  if (!plan_extend(batch, num_heads, num_kv_heads, head_dim, max_query_len,
                    std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size), (int)kv, opts, &plan))
     return fail(KVC_E_INVALID, "opts: kernel must be 0, 2 or 3, work_items >= 0, window >= 0");
   size_t need = workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, plan);
