@@ -235,6 +235,28 @@ def test_device_calls_on_bookkeeping_only_cache_fail_cleanly():
     assert st == B.E_INVALID
 
 
+def test_attention_refuses_block_lists_of_2_30_entries():
+    # the kernels read the block table through 32-bit byte offsets, so a call
+    # whose batch x blocks per sequence reaches 2^30 is refused before anything
+    # runs (the pools and arrays below are placeholders that nothing reads)
+    lib = B.lib()
+    buf = (ctypes.c_char * 64)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    cfg = _cfg(num_blocks=8, k_pool=p, v_pool=p)
+    h = ctypes.c_void_p()
+    assert lib.kvc_create(ctypes.byref(cfg), ctypes.byref(h)) == B.OK
+    try:
+        def call(max_blocks, max_ctx):
+            return lib.kvc_decode_attention(h, 0, p, B.F16, p, max_blocks, p, max_ctx, 8192, 4, 2, 64, 16, 0.1, p,
+                                            p, 64, None, None)
+        assert call(1 << 17, 1 << 21) == B.E_UNSUPPORTED            # 8192 x 2^17 = 2^30 blocks
+        assert b"2^30" in lib.kvc_last_error()
+        assert call(1 << 27, (1 << 21) - 16) == B.E_WORKSPACE       # 8192 x (2^17 - 1): the length bounds it
+        assert call((1 << 17) - 1, 1 << 30) == B.E_WORKSPACE        # ... or the table does
+    finally:
+        lib.kvc_destroy(h)
+
+
 def test_workspace_sizes():
     # FMA kernel: nothing when one partition holds every sequence, else rows * (D + 2) floats
     assert kvc.decode_workspace_bytes(4, 8, 2, 64, 200, partition_tokens=256, kernel=1) == 0
