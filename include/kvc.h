@@ -323,8 +323,9 @@ size_t kvc_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_
  *  workspace:    device, kvc_decode_workspace_bytes() bytes
  * Checks: num_heads % num_kv_heads == 0 and num_heads / num_kv_heads <= 16,
  * num_kv_heads / head_dim / block_size equal the cache's, block_size 16,
- * batch <= 8192, batch x ceil(min(max_context_len, max_blocks_per_seq x
- * block_size) / 16) < 2^30 (else KVC_E_UNSUPPORTED).
+ * batch <= 8192, max_blocks_per_seq x block_size <= 2^31 - 1 and
+ * batch x ceil(min(max_context_len, max_blocks_per_seq x block_size) / 16) < 2^30
+ * (else KVC_E_UNSUPPORTED).
  * Device-side values are clamped so every access stays inside the arrays the
  * arguments describe: a length above max_context_len or max_blocks_per_seq *
  * block_size is cut to it, a block id outside [0, num_blocks) reads block 0

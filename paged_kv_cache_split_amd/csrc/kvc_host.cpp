@@ -920,6 +920,9 @@ kvc_status check_attention_args(const kvc_cache* c, int32_t layer, const void* q
   // the scale must not flip the order of the scores
   if (!(scale >= 0.0f) || scale > 3.0e38f) return fail(KVC_E_INVALID, "scale must be finite and >= 0");
   if (batch > kvc::kMaxBatch) return fail(KVC_E_UNSUPPORTED, "batch %d > %d", batch, kvc::kMaxBatch);
+  // the kernels cap a length at max_blocks_per_seq x block_size in 32 bits
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    return fail(KVC_E_UNSUPPORTED, "max_blocks_per_seq * block_size must fit int32");
   // the kernels read the block table through 32-bit byte offsets: every list
   // position of a head's blocks (at most batch x blocks per sequence) < 2^30
   const int64_t per_seq = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size);

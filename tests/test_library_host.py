@@ -251,8 +251,9 @@ def test_attention_refuses_block_lists_of_2_30_entries():
                                             p, 64, None, None)
         assert call(1 << 17, 1 << 21) == B.E_UNSUPPORTED            # 8192 x 2^17 = 2^30 blocks
         assert b"2^30" in lib.kvc_last_error()
-        assert call(1 << 27, (1 << 21) - 16) == B.E_WORKSPACE       # 8192 x (2^17 - 1): the length bounds it
+        assert call((1 << 27) - 1, (1 << 21) - 16) == B.E_WORKSPACE  # 8192 x (2^17 - 1): the length bounds it
         assert call((1 << 17) - 1, 1 << 30) == B.E_WORKSPACE        # ... or the table does
+        assert call(1 << 27, 16) == B.E_UNSUPPORTED                 # 2^27 x 16 tokens overflow int32
     finally:
         lib.kvc_destroy(h)
 
