@@ -368,7 +368,7 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
     plan->work_items = 1;
     // Too few tiles to fill the chip (a single prompt): each group's steps of
     // two blocks are cut into pieces, so the groups holding the causal
-    // diagonal's far end do not run alone; about kFlashWaves waves in all.
+    // diagonal's far end do not run alone; about flash_waves_target() waves in all.
     const int64_t waves = (int64_t)batch * num_kv_heads * plan->tile_groups * kFlashWavesPerGroup;
     const int64_t max_steps = ((int64_t)(max_context_len + 15) / 16 + 1) / 2 + 1;
     const int64_t target = flash_waves_target(kv, head_dim);
