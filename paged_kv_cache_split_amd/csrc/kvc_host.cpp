@@ -338,9 +338,15 @@ int64_t flash_waves_target(int kv, int32_t head_dim) {
 constexpr int64_t kFlashMinSteps = 4;
 constexpr int64_t kFlashMaxPieces = 64;
 constexpr int32_t kFlashWavesPerGroup = 4;   // column tiles (waves) per work-group
+// 16-bit caches at head_dim 128: eight, each step's staged K/V shared by twice
+// the tiles at the same two waves per SIMD (chunk workload 406-409 us against
+// 411-416); at head_dim 64 a group of eight would leave two waves per SIMD
+// instead of three (the prompt took 40 us against 32)
+int32_t flash_waves_per_group(int kv, int32_t head_dim) {
+  return ((kv == KVC_F16 || kv == KVC_BF16) && head_dim == 128) ? 8 : kFlashWavesPerGroup;
+}
 
-// kv: the cache's dtype, or -1 when unknown (a workspace query: the plan then
-// takes the largest cut any dtype takes)
+// kv: the cache's dtype, or -1 for a one-byte cache's plan (the largest cut)
 bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_q,
                  int32_t max_context_len, int kv, const kvc_decode_opts* opts, kvc::DecodePlan* plan) {
   if (opts && (opts->work_items < 0 || (opts->kernel != 0 && opts->kernel != 2 && opts->kernel != 3) ||
@@ -360,16 +366,17 @@ bool plan_extend(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   plan->max_pieces = 1;
   if (plan->kernel == 3) {
     // one wave per 32 (token, head) columns, every row its columns see, four
-    // column tiles per work-group sharing the K/V steps; groups of tiles on
-    // grid.z (work_items and tiles_per_wave do not apply)
+    // or eight column tiles per work-group sharing the K/V steps; groups of
+    // tiles on grid.z (work_items and tiles_per_wave do not apply)
+    const int32_t wpg = flash_waves_per_group(kv, head_dim);
     plan->tiles_per_wave = 1;
-    plan->waves_per_group = kFlashWavesPerGroup;
-    plan->tile_groups = ((max_q * G + 31) / 32 + kFlashWavesPerGroup - 1) / kFlashWavesPerGroup;
+    plan->waves_per_group = wpg;
+    plan->tile_groups = ((max_q * G + 31) / 32 + wpg - 1) / wpg;
     plan->work_items = 1;
     // Too few tiles to fill the chip (a single prompt): each group's steps of
     // two blocks are cut into pieces, so the groups holding the causal
     // diagonal's far end do not run alone; about flash_waves_target() waves in all.
-    const int64_t waves = (int64_t)batch * num_kv_heads * plan->tile_groups * kFlashWavesPerGroup;
+    const int64_t waves = (int64_t)batch * num_kv_heads * plan->tile_groups * wpg;
     const int64_t max_steps = ((int64_t)(max_context_len + 15) / 16 + 1) / 2 + 1;
     const int64_t target = flash_waves_target(kv, head_dim);
     if (waves < target / 2 && max_steps > kFlashMinSteps) {
@@ -1010,9 +1017,15 @@ kvc_status kvc_decode_attention_static(kvc_cache* c, int32_t layer, const void* 
 size_t kvc_extend_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_query_len, int32_t max_context_len, const kvc_decode_opts* opts) {
   if (batch < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || num_heads % num_kv_heads != 0) return 0;
-  kvc::DecodePlan p;
-  if (!plan_extend(batch, num_heads, num_kv_heads, head_dim, max_query_len, max_context_len, -1, opts, &p)) return 0;
-  return workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, p);
+  // the plan depends on the cache's dtype (work-group size, cut): the larger
+  // of the 16-bit plan and the one-byte one
+  size_t need = 0;
+  for (int kv : {(int)KVC_BF16, -1}) {
+    kvc::DecodePlan p;
+    if (!plan_extend(batch, num_heads, num_kv_heads, head_dim, max_query_len, max_context_len, kv, opts, &p)) return 0;
+    need = std::max(need, workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, p));
+  }
+  return need;
 }
 
 kvc_status kvc_extend_attention(kvc_cache* c, int32_t layer, const void* q, kvc_dtype q_dtype,

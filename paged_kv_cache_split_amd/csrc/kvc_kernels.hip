@@ -1995,7 +1995,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   constexpr int NSTAGE = DMA ? KVC_FLASH_STAGES : 2, SBYTES = DMA ? STAGE_D : STAGE, KOFF = DMA ? KBYTES_D : KBYTES;
   static_assert(NSTAGE == 2 || NSTAGE == 3 || NSTAGE == 4, "2 to 4 stages");
   constexpr int PERD = STAGE_D / (16 * NT);           // loads per thread and step, straight to LDS
-  static_assert(STAGE_D % (16 * NT) == 0 && (32 * CR) % NT == 0, "whole loads per stage, K and V apart");
+  static_assert(STAGE_D % (16 * NT) == 0 && (32 * CR) % 64 == 0, "whole loads per stage, K and V per wave");
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * SBYTES];
   // global pieces of one step: 16 bytes each, both blocks, K then V
   constexpr int CHB = is_byte_code(KV) ? D : 2 * D;   // 16-byte pieces per (block, head) tile
@@ -2300,7 +2300,7 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
     for (int i = 0; i < PERD; ++i) {
       const int L = i * NT + tid;
       const char* src;
-      if (i * NT < 32 * CR) {                     // K: score row r, position pos
+      if (L < 32 * CR) {                          // K: score row r, position pos (wave-uniform)
         const int r = L / CR, pos = L % CR;
         const int dg = pos ^ ksw<CR>(r), rr = r & 15;
         const int tkn = (rr & 3) | ((rr & 4) << 1) | ((rr & 8) >> 1);   // rho(rr)
@@ -2695,10 +2695,20 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int D, int kernel, bool merg
   if constexpr (KV != KVC_F32) {
     if (kernel == 3) {   // several tokens, one wave per 32 columns (and piece of their rows)
       if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
-      // tile_groups: work-groups of waves_per_group (4) column tiles per sequence and head
+      // tile_groups: work-groups of waves_per_group column tiles per sequence
+      // and head; eight only for 16-bit caches at head_dim 128 (their stages
+      // shared by twice the tiles, at the same two waves per SIMD)
       dim3 grid(a.num_kv_heads, a.batch, tile_groups * a.max_pieces);
-      if (D == 64) hipLaunchKernelGGL((extend_flash_kernel<KV, 64, 4>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((extend_flash_kernel<KV, 128, 4>), grid, dim3(256), 0, s, a);
+      if (a.waves_per_group == 8) {
+        if constexpr (is_byte_code(KV)) return hipErrorInvalidValue;
+        else if (D == 128) hipLaunchKernelGGL((extend_flash_kernel<KV, 128, 8>), grid, dim3(512), 0, s, a);
+        else return hipErrorInvalidValue;
+      } else if (a.waves_per_group == 4) {
+        if (D == 64) hipLaunchKernelGGL((extend_flash_kernel<KV, 64, 4>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((extend_flash_kernel<KV, 128, 4>), grid, dim3(256), 0, s, a);
+      } else {
+        return hipErrorInvalidValue;
+      }
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
       if (a.max_pieces > 1 && !a.partials_only) {
