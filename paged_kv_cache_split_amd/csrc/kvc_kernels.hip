@@ -1992,7 +1992,8 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
   constexpr bool DMA = KVC_FLASH_DMA && !is_byte_code(KV);
   constexpr int RK = 2 * D, CR = RK / 16;             // K row bytes, 16-byte chunks per row
   constexpr int KBYTES_D = 32 * RK, STAGE_D = KBYTES_D + D * 64;
-  constexpr int NSTAGE = DMA ? KVC_FLASH_STAGES : 2, SBYTES = DMA ? STAGE_D : STAGE, KOFF = DMA ? KBYTES_D : KBYTES;
+  // (eight waves: two steps per barrier, in two halves of two stages)
+  constexpr int NSTAGE = DMA ? (WT == 8 ? 4 : KVC_FLASH_STAGES) : 2, SBYTES = DMA ? STAGE_D : STAGE, KOFF = DMA ? KBYTES_D : KBYTES;
   static_assert(NSTAGE == 2 || NSTAGE == 3 || NSTAGE == 4, "2 to 4 stages");
   constexpr int PERD = STAGE_D / (16 * NT);           // loads per thread and step, straight to LDS
   static_assert(STAGE_D % (16 * NT) == 0 && (32 * CR) % 64 == 0, "whole loads per stage, K and V per wave");
@@ -2316,7 +2317,39 @@ __global__ __launch_bounds__(64 * WT) void extend_flash_kernel(DecodeArgs a) {
     }
   };
 
-  if constexpr (DMA) {
+  if constexpr (DMA && WT == 8) {
+    // Eight waves wait at a barrier for the slowest of them, so they meet at
+    // one every two steps (chunk workload 395-398 us against 403-407; with
+    // four waves it measured the same either way): stages 0-1 and 2-3 take
+    // turns, and the loads of the next two steps go out right after the
+    // barrier that tells every wave is done with the two before.
+    if (s_end > s_begin) {
+      const Staged none{};
+      dma_stage(0, ids_of(s_begin));
+      if (s_begin + 1 < s_end) dma_stage(1, ids_of(s_begin + 1));
+      Ids n0 = ids_of(s_begin + 2), n1 = ids_of(s_begin + 3);
+      int hb = 0;   // first stage of the current two steps (0 or 2)
+      for (int s0 = s_begin; s0 < s_end; s0 += 2, hb ^= 2) {
+        vm_wait<0>();   // this wave's loads of steps s0 and s0 + 1
+        wg_barrier();
+        if (s0 + 2 < s_end) dma_stage(hb ^ 2, n0);
+        if (s0 + 3 < s_end) dma_stage((hb ^ 2) + 1, n1);
+        n0 = ids_of(s0 + 4);
+        n1 = ids_of(s0 + 5);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int st = s0 + j;
+          if (st < s_end) {
+            const int k0 = (jb0 + 2 * st) * kBS;
+            if (tile_ok && k0 < w_hi && k0 + 2 * kBS > w_lo) {
+              if (k0 + 2 * kBS > n_lo || k0 < lo_hi) step(std::true_type{}, hb + j, k0, none);
+              else step(std::false_type{}, hb + j, k0, none);
+            }
+          }
+        }
+      }
+    }
+  } else if constexpr (DMA) {
     // NSTAGE stages: step st's tiles were requested NSTAGE - 1 steps earlier.
     // At the head of step st every wave waits for its own loads of st (those
     // of the steps after it may stay in flight), then the barrier makes all
