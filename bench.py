@@ -167,11 +167,13 @@ def workload_key(args):
     return f"config {args.config}" + (f" kv {args.kv}" if args.kv else "")
 
 
-def profiled_traffic(key):
+def profiled_traffic(key, combined=False):
     """HBM bytes per split-kernel launch from a committed rocprofv3 summary
     (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy kernel's counts)
     of the workload `key`, or None when no summary was taken on the current
-    sources (the kernels, and the host code that plans their launches)."""
+    sources (the kernels, and the host code that plans their launches).
+    combined: the sum over every kernel the summary records for `key` (the
+    shared-prefix decode times its prefix pass and its split kernel as one)."""
     import glob
     import hashlib
     csrc = os.path.join(ROOT, "paged_kv_cache_split_amd", "csrc")
@@ -180,6 +182,7 @@ def profiled_traffic(key):
                                       for f in ("kvc_kernels.hip", "kvc_host.cpp"))).hexdigest()
     except OSError:
         return None
+    total, source = 0, None
     for fn in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         text = open(fn).read()
         for line in text.splitlines():
@@ -189,8 +192,11 @@ def profiled_traffic(key):
                 except ValueError:
                     continue
                 if rec.get("workload_key") == key and rec.get("kernel_source_sha256") == sha:
-                    return rec["traffic_bytes_per_launch"], os.path.relpath(fn, ROOT)
-    return None
+                    if not combined:
+                        return rec["traffic_bytes_per_launch"], os.path.relpath(fn, ROOT)
+                    total += rec["traffic_bytes_per_launch"]
+                    source = os.path.relpath(fn, ROOT)
+    return (total, source) if source else None
 
 
 def cpu_baseline(wl, values, budget_s):
@@ -697,7 +703,8 @@ def also_entry(cid, shared_prefix, args, dev):
     o = DecodeOpts(args, shared_prefix=shared_prefix)
     r = time_decode(wl, values, cache, o, args.steps, args.warmup, dev)
     key = f"config {cid}"
-    prof = profiled_traffic(key) if not shared_prefix and o.kernel in (0, 2) else None
+    prof = ((profiled_traffic(key + " shared prefix", combined=True) if shared_prefix else profiled_traffic(key))
+            if o.kernel in (0, 2) else None)
     entry = {"workload": wl.name, "config_id": cid, "shared_prefix": wl.shared_prefix if shared_prefix else 0,
              "dtype": wl.kv_dtype, "us_per_step": round(r["ms_per_step"] * 1e3, 2), "value": round(r["kv_gbs"], 2),
              "unit": "GB/s", "pct_of_peak_hbm": round(100.0 * r["kv_gbs"] / PEAK_HBM_GBS, 2),
@@ -740,8 +747,10 @@ def main():
     print(f"[bench] timed {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
     prefix = wl.shared_prefix if args.shared_prefix else 0
     ab, ms_per_step, kv_gbs, achieved = r["ab"], r["ms_per_step"], r["kv_gbs"], r["achieved"]
-    prof = (profiled_traffic(workload_key(args)) if args.kernel in (0, 2) and not args.work_items
-            and not args.pool_pieces and not args.shared_prefix else None)
+    prof = None
+    if args.kernel in (0, 2) and not args.work_items and not args.pool_pieces:
+        prof = (profiled_traffic(workload_key(args) + " shared prefix", combined=True) if args.shared_prefix
+                else profiled_traffic(workload_key(args)))
     traffic = prof[0] if prof else None
     result = {
         "metric": METRIC,

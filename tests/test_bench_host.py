@@ -76,3 +76,29 @@ def test_more_than_one_gpu_is_refused(n):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_profiled_traffic_matches_sources_and_sums_a_shared_prefix(tmp_path, monkeypatch):
+    # summaries count only for the sources they were taken on; the
+    # shared-prefix decode times its prefix pass and split kernel as one, so
+    # its traffic is the sum of both kernels' records
+    import hashlib
+    csrc = tmp_path / "paged_kv_cache_split_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "kvc_kernels.hip").write_bytes(b"kernels")
+    (csrc / "kvc_host.cpp").write_bytes(b"host")
+    sha = hashlib.sha256(b"kernelshost").hexdigest()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    recs = [{"kernel": "a", "workload_key": "config 4 shared prefix", "kernel_source_sha256": sha,
+             "traffic_bytes_per_launch": 100},
+            {"kernel": "b", "workload_key": "config 4 shared prefix", "kernel_source_sha256": sha,
+             "traffic_bytes_per_launch": 23},
+            {"kernel": "b", "workload_key": "config 3", "kernel_source_sha256": "0" * 64,
+             "traffic_bytes_per_launch": 7}]
+    (prof / "x.md").write_text("# x\n\n```\n" + "\n".join(json.dumps(r) for r in recs) + "\n```\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.profiled_traffic("config 4 shared prefix", combined=True) == (123, os.path.join("profiles", "x.md"))
+    assert bench.profiled_traffic("config 4 shared prefix") == (100, os.path.join("profiles", "x.md"))
+    assert bench.profiled_traffic("config 3") is None          # taken on other sources
+    assert bench.profiled_traffic("config 2", combined=True) is None
